@@ -1,0 +1,483 @@
+"""Pins for the float64 oracle against facts the pages and the mathematics fix.
+
+Each check is written so that a plausible slip in the oracle (a dropped term,
+a wrong sign, a swapped precision, a transposed operand) fails at least one
+of them; tests/test_oracle_mutations.py plants such slips and confirms it.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import mpq_oracle as O
+import mpq_synth as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def small_problem(seed=0, n=12, r=9, K=4, d=1, power=0.5):
+    g = rng(seed)
+    Q, _ = np.linalg.qr(g.standard_normal((n, n)))
+    V = Q[:, :r]
+    s = np.arange(1, r + 1, dtype=float) ** -power
+    w = g.standard_normal(n)
+    E = np.arange(K, dtype=float).reshape(K, 1) if d == 1 else g.standard_normal((K, d))
+    return w, s, V, E
+
+
+# ----------------------------------------------------------------------------
+# denoiser (key design 1): T1, T5
+# ----------------------------------------------------------------------------
+
+def check_denoiser_limits():
+    """T1 + T5: normalisation, the hard (gamma -> inf) and flat (gamma -> 0)
+    limits, and the closed form for a binary codebook {-a, +a}."""
+    g = rng(1)
+    C = g.standard_normal((7, 3))
+    r = g.standard_normal(12)
+    _, _, q = O.denoise(r, 0.7, C, 3, return_q=True)
+    assert np.allclose(q.sum(1), 1.0, atol=1e-14)
+    # gamma -> inf: one-hot at the nearest codeword (brute force), zero variance
+    xh, v, q = O.denoise(r, 1e9, C, 3, return_q=True)
+    for b in range(4):
+        dists = [sum((C[k, j] - r[3 * b + j]) ** 2 for j in range(3)) for k in range(7)]
+        k = dists.index(min(dists))
+        assert q[b, k] > 1 - 1e-12
+        assert np.allclose(xh[3 * b:3 * b + 3], C[k], atol=1e-9)
+        assert v[b] < 1e-9
+    # gamma -> 0: posterior = prior (uniform): mean of codewords, total variance
+    xh, v, _ = O.denoise(r, 1e-14, C, 3)
+    mean = C.mean(0)
+    tv = ((C - mean) ** 2).sum(1).mean()
+    assert np.allclose(xh.reshape(4, 3), mean[None, :], atol=1e-9)
+    assert np.allclose(v, tv, rtol=1e-9)
+    # binary codebook: x_hat = a tanh(gamma a r), var = a^2 - x_hat^2
+    a = 0.8
+    Cb = np.array([[-a], [a]])
+    r1 = np.linspace(-2, 2, 9)
+    for gam in (0.3, 2.0, 11.0):
+        xh, v, _ = O.denoise(r1, gam, Cb, 1)
+        ref = a * np.tanh(gam * a * r1)
+        assert np.allclose(xh, ref, rtol=1e-12, atol=1e-14)
+        assert np.allclose(v, a * a - ref * ref, rtol=1e-10, atol=1e-14)
+    # asymmetric binary codebook {c0, c1}: q(c1) = sigmoid(gamma (c1-c0)(r - (c0+c1)/2))
+    c0, c1 = -0.3, 1.1
+    Cb = np.array([[c0], [c1]])
+    for gam in (0.5, 4.0):
+        xh, v, _ = O.denoise(r1, gam, Cb, 1)
+        p1 = 1.0 / (1.0 + np.exp(-gam * (c1 - c0) * (r1 - 0.5 * (c0 + c1))))
+        assert np.allclose(xh, c0 + p1 * (c1 - c0), rtol=1e-12)
+        assert np.allclose(v, p1 * (1 - p1) * (c1 - c0) ** 2, rtol=1e-10, atol=1e-15)
+
+
+def check_denoiser_gaussian_limit():
+    """A fine uniform grid over a wide range approximates a flat prior: the
+    posterior becomes N(r, 1/gamma) per coordinate (mean r, variance 1/gamma)."""
+    h = 0.01
+    C = (np.arange(-1000, 1001) * h).reshape(-1, 1)
+    r = np.array([0.123, -1.77, 2.5])
+    gam = 4.0
+    xh, v, _ = O.denoise(r, gam, C, 1)
+    assert np.allclose(xh, r, atol=1e-9)
+    assert np.allclose(v, 1.0 / gam, rtol=1e-6)
+    # 2-d version: trace of covariance = d / gamma
+    g2 = np.array(list(itertools.product(np.arange(-120, 121) * 0.05, repeat=2)))
+    xh, v, _ = O.denoise(np.array([0.31, -0.42]), 9.0, g2, 2)
+    assert np.allclose(xh, [0.31, -0.42], atol=1e-9)
+    assert abs(v[0] - 2.0 / 9.0) < 1e-6
+
+
+def test_denoiser_limits():
+    check_denoiser_limits()
+
+
+def test_denoiser_gaussian_limit():
+    check_denoiser_gaussian_limit()
+
+
+def test_map_is_nearest_under_uniform_prior():
+    g = rng(2)
+    C = g.standard_normal((50, 8))
+    r = g.standard_normal(8 * 20)
+    for gam in (0.01, 1.0, 300.0):
+        mc = O.map_codes(r, gam, C, 8)
+        for b in range(20):
+            best = min(range(50), key=lambda k: (sum((C[k, j] - r[8 * b + j]) ** 2 for j in range(8)), k))
+            assert mc[b] == best
+    # ties go to the lowest index
+    C2 = np.array([[1.0], [-1.0], [1.0]])
+    assert list(O.map_codes(np.array([0.0, 2.0]), 1.0, C2, 1)) == [0, 0]
+    assert list(O.nearest_codeword(np.array([0.0, 2.0]), C2, 1)) == [0, 0]
+
+
+# ----------------------------------------------------------------------------
+# linear module and M-step: T2, T3
+# ----------------------------------------------------------------------------
+
+def dense_T(s, V):
+    return np.diag(s) @ V.T
+
+
+def check_linear_module_dense(n=12, r=9, seed=3):
+    """T3: the rank-space solve equals the dense LMMSE / ridge solve and
+    eta2 = n / tr Sigma2 with Sigma2 = (beta T^T T + gamma2 I)^-1 (numpy.linalg)."""
+    w, s, V, _ = small_problem(seed, n, r)
+    g = rng(seed + 100)
+    r2 = g.standard_normal(n)
+    beta, gamma2 = 37.0, 2.5
+    T = dense_T(s, V)
+    ytil = T @ w
+    lin = O.linear_module(r2, gamma2, beta, ytil, s, V)
+    A = beta * T.T @ T + gamma2 * np.eye(n)
+    xh = np.linalg.solve(A, beta * T.T @ ytil + gamma2 * r2)
+    Sig = np.linalg.inv(A)
+    assert np.allclose(lin["xhat2"], xh, rtol=1e-11, atol=1e-12)
+    assert np.isclose(lin["eta2"], n / np.trace(Sig), rtol=1e-12)
+    # extrinsic back: gamma1' = eta2 - gamma2, r1' removes the gamma2 r2 share
+    assert np.isclose(lin["gamma1"], n / np.trace(Sig) - gamma2, rtol=1e-11)
+    assert np.allclose(lin["gamma1"] * lin["r1"], n / np.trace(Sig) * xh - gamma2 * r2, rtol=1e-10)
+    # u is the rank-space residual at r2
+    assert np.allclose(lin["u"], ytil - T @ r2, rtol=1e-12, atol=1e-13)
+
+
+def check_beta_dense(n=12, r=9, seed=4):
+    """T2: the printed M-step equals [||y~ - T x_hat2||^2 + tr(T Sigma2 T^T)] / r
+    evaluated densely (the EM update of a Gaussian noise precision)."""
+    w, s, V, _ = small_problem(seed, n, r)
+    g = rng(seed + 7)
+    r2 = g.standard_normal(n)
+    beta, gamma2 = 12.0, 0.8
+    T = dense_T(s, V)
+    ytil = T @ w
+    lin = O.linear_module(r2, gamma2, beta, ytil, s, V)
+    A = beta * T.T @ T + gamma2 * np.eye(n)
+    Sig = np.linalg.inv(A)
+    xh = Sig @ (beta * T.T @ ytil + gamma2 * r2)
+    res = ytil - T @ xh
+    inv_beta = (res @ res + np.trace(T @ Sig @ T.T)) / r
+    assert np.isclose(O.beta_em(lin["u"], s, beta, gamma2), 1.0 / inv_beta, rtol=1e-12)
+    # damping is a convex combination in the precision domain
+    assert O.damp_beta(2.0, 6.0, 0.5) == 4.0
+    assert O.damp_beta(2.0, 6.0, 1.0) == 6.0
+    assert O.damp_beta(2.0, 6.0, 0.25) == 3.0
+
+
+def test_linear_module_matches_dense_solve():
+    for n, r in ((12, 9), (10, 10), (7, 3)):
+        check_linear_module_dense(n, r)
+
+
+def test_beta_mstep_matches_dense_em():
+    for n, r in ((12, 9), (9, 9)):
+        check_beta_dense(n, r)
+
+
+# ----------------------------------------------------------------------------
+# the message passing itself with a Gaussian prior: T4
+# ----------------------------------------------------------------------------
+
+def check_gaussian_prior_fixed_point(n=12, r=9, seed=5):
+    """T4: with a Gaussian prior N(mu, sigma^2 I) in the denoiser slot (test
+    only) expectation propagation is exact, so VAMP's fixed point is the
+    ridge solution (beta T^T T + sigma^-2 I)^-1 (beta T^T y~ + sigma^-2 mu),
+    the two posterior means agree and eta1 = eta2."""
+    w, s, V, _ = small_problem(seed, n, r)
+    g = rng(seed + 11)
+    mu = g.standard_normal(n)
+    sig2 = 0.37
+    beta = 5.0
+    T = dense_T(s, V)
+    ytil = T @ w
+
+    def gauss_denoiser(r1, gamma1):
+        prec = gamma1 + 1.0 / sig2
+        return (gamma1 * r1 + mu / sig2) / prec, np.full(n, 1.0 / prec)
+
+    C = np.arange(4, dtype=float).reshape(4, 1)
+    st = O.vamp(w, s, V, C, 1, 6, 0.5, 1.0, beta0=beta, denoiser=gauss_denoiser,
+                fixed_beta=True, record=True)
+    ridge = np.linalg.solve(beta * T.T @ T + np.eye(n) / sig2, beta * T.T @ ytil + mu / sig2)
+    last = st["history"][-1]
+    assert np.allclose(last["xhat2"], ridge, rtol=1e-10, atol=1e-12)
+    assert np.allclose(last["xhat1"], ridge, rtol=1e-10, atol=1e-12)
+    assert np.isclose(last["eta1"], last["eta2"], rtol=1e-10)
+    assert st["fallbacks"] == 0
+
+
+def test_gaussian_prior_vamp_reaches_ridge():
+    for n, r in ((12, 9), (8, 8)):
+        check_gaussian_prior_fixed_point(n, r)
+
+
+# ----------------------------------------------------------------------------
+# CD: T6, T7, T9
+# ----------------------------------------------------------------------------
+
+def brute_cd(codes, w, s, V, C, d, n_cd):
+    """Independent CD: every candidate is scored by the full objective."""
+    codes = list(codes)
+    B = len(codes)
+
+    def full(cs):
+        return O.objective(w, C[np.array(cs)].reshape(-1), s, V)
+
+    changes = []
+    for _ in range(n_cd):
+        ch = 0
+        for b in range(B):
+            cur = full(codes)
+            vals = []
+            for k in range(C.shape[0]):
+                trial = list(codes)
+                trial[b] = k
+                vals.append(full(trial))
+            k = int(np.argmin(vals))
+            if vals[k] < cur:
+                if k != codes[b]:
+                    ch += 1
+                codes[b] = k
+        changes.append(ch)
+        if ch == 0:
+            break
+    return codes, changes
+
+
+def check_cd_properties(seed=6, n=16, r=16, d=2, K=9):
+    """T6: the Mahalanobis form picks the same codeword as F_b; each accepted
+    move lowers the objective by exactly -dF; recomputing u from scratch
+    matches the carried residual."""
+    g = rng(seed)
+    Q, _ = np.linalg.qr(g.standard_normal((n, n)))
+    V = Q[:, :r]
+    s = np.arange(1, r + 1, dtype=float) ** -0.6
+    w = g.standard_normal(n)
+    C = g.standard_normal((K, d))
+    codes = O.nearest_codeword(w, C, d)
+    x = C[codes].reshape(-1)
+    u = O.rank_target(w - x, s, V)
+    for b in range(n // d):
+        sl = slice(b * d, (b + 1) * d)
+        Tb = s[:, None] * V[sl, :].T
+        gb = Tb.T @ u
+        G = Tb.T @ Tb
+        D = C - x[sl]
+        dF = 0.5 * np.einsum("kj,jl,kl->k", D, G, D) - D @ gb
+        mu = x[sl] + np.linalg.solve(G, gb)
+        maha = 0.5 * np.einsum("kj,jl,kl->k", C - mu, G, C - mu)
+        assert np.argmin(dF) == np.argmin(maha)
+        assert np.allclose(dF - dF.min(), maha - maha.min(), atol=1e-10)
+        k = int(np.argmin(dF))
+        before = O.objective(w, x, s, V)
+        if dF[k] < 0:
+            x[sl] = C[k]
+            u = u - Tb @ D[k]
+            after = O.objective(w, x, s, V)
+            assert np.isclose(after - before, dF[k], rtol=1e-9, atol=1e-12)
+            assert np.allclose(u, O.rank_target(w - x, s, V), atol=1e-12)
+
+
+def test_cd_properties():
+    for seed in range(4):
+        check_cd_properties(seed)
+
+
+def check_cd_bruteforce():
+    """T7 (i): T_vamp = 0 gives MAP(w) = RTN followed by CD; it equals an
+    independent CD that scores candidates by the full objective."""
+    for seed in range(3):
+        w, s, V, _ = small_problem(seed + 20, n=10, r=10)
+        E = np.arange(4, dtype=np.float32).reshape(4, 1)
+        a, o = 0.7, -1.05
+        C = O.row_codewords(E, a, o)
+        res = O.solve_row(w, s, V, E, a, o, 1, 0, 5, 0.5)
+        rtn = O.nearest_codeword(w, C, 1)
+        assert list(res["map_codes"]) == list(rtn)
+        ref_codes, ref_changes = brute_cd(rtn, w, s, V, C, 1, 5)
+        assert list(res["codes"]) == list(ref_codes)
+        assert res["cd_changes"][:len(ref_changes)] == ref_changes
+
+
+def test_cd_matches_bruteforce_objective_cd():
+    check_cd_bruteforce()
+
+
+def test_cd_gibbs_zero_temperature_limit():
+    """T7 (ii): the Gibbs block conditional p(c_b | rest) ~ exp(-beta F_b(c))
+    at beta = 1e12 puts all its mass on the CD choice."""
+    w, s, V, _ = small_problem(31, n=8, r=8)
+    C = O.row_codewords(np.arange(4, dtype=float).reshape(4, 1), 0.6, -0.9)
+    codes = list(O.nearest_codeword(w, C, 1))
+    for b in range(8):
+        F = []
+        for k in range(4):
+            t = list(codes)
+            t[b] = k
+            F.append(O.objective(w, C[np.array(t)].reshape(-1), s, V))
+        F = np.array(F)
+        logits = -1e12 * F
+        p = np.exp(logits - logits.max())
+        p /= p.sum()
+        new, _ = O.block_cd(codes, w, s, V, C, 1, 1)
+        # one sweep: the first block's choice is the conditional argmax
+        if b == 0:
+            assert int(np.argmax(p)) == new[0] or F[new[0]] == F.min()
+        codes[b] = int(np.argmin(F))
+
+
+def test_tiny_rows_exhaustive():
+    """T9: n = 8, 2-bit scalar (4^8 assignments): CD ends at a blockwise local
+    minimum (checked when it stopped on a no-change sweep) no worse than its
+    MAP start; the gap to the global minimum is reported, not asserted."""
+    gaps = []
+    for seed in range(6):
+        w, s, V, _ = small_problem(seed + 40, n=8, r=8)
+        E = np.arange(4, dtype=float).reshape(4, 1)
+        lo, hi = w.min(), w.max()
+        a = (hi - lo) / 3
+        o = -a * np.round(-lo / a)
+        C = O.row_codewords(E, a, o)
+        res = O.solve_row(w, s, V, E, a, o, 1, 8, 50, 0.5)
+        f_final = res["objective"]
+        f_map = O.codes_objective(w, res["map_codes"], C, 1, s, V)
+        assert f_final <= f_map + 1e-15
+        if res["cd_changes"][-1] == 0 or 0 in res["cd_changes"]:
+            for b in range(8):
+                for k in range(4):
+                    t = np.array(res["codes"])
+                    t[b] = k
+                    assert O.codes_objective(w, t, C, 1, s, V) >= f_final - 1e-14
+        allc = np.array(list(itertools.product(range(4), repeat=8)))
+        X = C[allc][..., 0]                      # 65536 x 8
+        Tm = dense_T(s, V)
+        Ev = 0.5 * (((w[None, :] - X) @ Tm.T) ** 2).sum(1)
+        gaps.append(f_final - Ev.min())
+        assert Ev.min() <= f_final + 1e-14
+    assert min(gaps) >= -1e-14
+
+
+# ----------------------------------------------------------------------------
+# the page's worked example: T8
+# ----------------------------------------------------------------------------
+
+def load_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split()
+            vals[k] = float(v)
+    return vals
+
+
+def worked_example_instance():
+    A = -math.sqrt(0.2)
+    Bc = math.sqrt(0.22)
+    p = 10 * math.sqrt(0.2) + math.sqrt(0.6)
+    q = -(10 * math.sqrt(0.22) - 0.6)
+    T = np.array([[1.0, 0.0], [10.0, 1.0]])
+    U, sv, Vt = np.linalg.svd(T)
+    return np.array([A, Bc, p, q]).reshape(4, 1), sv, Vt.T
+
+
+def test_worked_example_values():
+    """T8: the explainer's greedy-vs-deferred example (errors only)."""
+    gold = load_golden("worked_example.txt")
+    C, s, V = worked_example_instance()
+    w = np.zeros(2)
+
+    def F(k1, k2):
+        return O.objective(w, np.array([C[k1, 0], C[k2, 0]]), s, V)
+
+    def block1_alone(k):  # error of block 1 when block 2 exactly compensates
+        x1 = C[k, 0]
+        return 0.5 * x1 * x1
+
+    assert np.isclose(block1_alone(0), gold["block1_alone_A"], atol=1e-12)
+    assert np.isclose(block1_alone(1), gold["block1_alone_B"], atol=1e-12)
+    assert np.isclose(min(F(0, k) for k in range(4)) - block1_alone(0), gold["best_block2_after_A"], atol=1e-12)
+    assert np.isclose(min(F(1, k) for k in range(4)) - block1_alone(1), gold["best_block2_after_B"], atol=1e-12)
+    # greedy: commit block 1 by its own error, then the best block 2
+    k1 = int(np.argmin([block1_alone(k) for k in range(4)]))
+    greedy = min(F(k1, k) for k in range(4))
+    assert k1 == 0 and np.isclose(greedy, gold["greedy_total"], atol=1e-12)
+    allF = [F(i, j) for i in range(4) for j in range(4)]
+    assert np.isclose(min(allF), gold["deferred_total"], atol=1e-12)
+
+
+def check_worked_example_mpq():
+    """MPQ (VAMP -> MAP -> CD) ends at the deferred 0.29, below greedy 0.40."""
+    gold = load_golden("worked_example.txt")
+    C, s, V = worked_example_instance()
+    w = np.zeros(2)
+    for T_vamp in (8, 16):
+        res = O.solve_row(w, s, V, C, 1.0, 0.0, 1, T_vamp, 3, 0.5)
+        assert np.isclose(res["objective"], gold["deferred_total"], atol=1e-12)
+        assert list(res["codes"]) == [1, 3]
+
+
+def test_worked_example_mpq_reaches_deferred_optimum():
+    check_worked_example_mpq()
+
+
+# ----------------------------------------------------------------------------
+# metamorphic relations: T11
+# ----------------------------------------------------------------------------
+
+def test_scale_invariance():
+    """T11 (a, b): W and the codebook scaled by 2^k leave codes unchanged and
+    scale gamma and beta by 2^-2k; s scaled by 2^k scales beta by 2^-2k."""
+    L = S.make_layer("t", 4, 32, seed=7, d=1, bits=3, T_vamp=6)
+    for i in range(2):
+        base = O.solve_row(L.W[i], L.s, L.V, L.E, L.a[i], L.o[i], 1, 6, 3, 0.5)
+        sc = O.solve_row(4.0 * L.W[i], L.s, L.V, L.E, 4.0 * L.a[i], 4.0 * L.o[i], 1, 6, 3, 0.5)
+        assert list(base["codes"]) == list(sc["codes"])
+        assert np.allclose(sc["gamma1_tr"], base["gamma1_tr"] / 16.0, rtol=1e-12)
+        assert np.allclose(sc["beta_tr"], base["beta_tr"] / 16.0, rtol=1e-12)
+        s2 = O.solve_row(L.W[i], 2.0 * L.s, L.V, L.E, L.a[i], L.o[i], 1, 6, 3, 0.5)
+        assert list(base["codes"]) == list(s2["codes"])
+        assert np.allclose(s2["beta_tr"], base["beta_tr"] / 4.0, rtol=1e-12)
+        assert np.allclose(s2["gamma1_tr"], base["gamma1_tr"], rtol=1e-12)
+
+
+def test_hyperparameter_special_cases():
+    """T11 (d): n_cd = 0 returns the MAP codes; T_vamp = 0 starts CD from RTN."""
+    L = S.make_layer("t", 3, 24, seed=8, d=1, bits=3)
+    i = 1
+    C = O.row_codewords(L.E, L.a[i], L.o[i])
+    r0 = O.solve_row(L.W[i], L.s, L.V, L.E, L.a[i], L.o[i], 1, 5, 0, 0.5)
+    assert list(r0["codes"]) == list(r0["map_codes"])
+    r1 = O.solve_row(L.W[i], L.s, L.V, L.E, L.a[i], L.o[i], 1, 0, 0, 0.5)
+    assert list(r1["codes"]) == list(O.nearest_codeword(L.W[i], C, 1))
+    assert len(r1["beta_tr"]) == 1 and len(r1["gamma2_tr"]) == 0
+
+
+def test_frozen_row():
+    """G2: a row already on its grid returns the RTN codes and objective 0."""
+    w = np.array([-1.0, -0.75, 0.5, 0.0], dtype=np.float32)
+    E = np.arange(8, dtype=np.float32).reshape(8, 1)
+    s = np.ones(4, dtype=np.float32)
+    V = np.eye(4, dtype=np.float32)
+    res = O.solve_row(w, s, V, E, 0.25, -1.0, 1, 4, 3, 0.5)
+    assert res["frozen"] and res["objective"] == 0.0
+    assert list(res["codes"]) == [0, 1, 6, 4]
+
+
+def test_mpq_beats_rtn_on_c1_rows():
+    """Sanity on the small workload: MPQ never ends above RTN + CD's start."""
+    L = S.make_config("c1")
+    better = 0
+    for i in range(6):
+        res = O.solve_row(L.W[i], L.s, L.V, L.E, L.a[i], L.o[i], 1, 8, 3, 0.5)
+        C = O.row_codewords(L.E, L.a[i], L.o[i])
+        f_rtn = O.codes_objective(L.W[i], res["rtn_codes"], C, 1, L.s, L.V)
+        better += res["objective"] < f_rtn
+        assert res["objective"] <= O.codes_objective(L.W[i], res["map_codes"], C, 1, L.s, L.V) + 1e-15
+    assert better == 6
