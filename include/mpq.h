@@ -1,0 +1,166 @@
+/*
+ * mpq.h -- C ABI of the MPQ layer solver for AMD Instinct MI355X (gfx950).
+ *
+ * MPQ ("MPQ: A Message-Passing View of Post-Training Quantization",
+ * papernotes.org summary, section "Method") quantizes every output row w of a
+ * layer to a product codebook C_1 x ... x C_B (B = n / d blocks of d
+ * consecutive weights) by minimising 1/2 ||T (w - w_hat)||^2, T = diag(s) V^T.
+ * Stage 1 runs T_vamp iterations of rank-space VAMP (blockwise discrete
+ * denoiser -> Gaussian linear module -> empirical-Bayes beta M-step with
+ * damping); stage 2 takes the marginal-MAP codeword per block and refines it
+ * by exact block coordinate descent (at most n_cd sweeps).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Shapes: m rows, row length n, rank r (1 <= r <= n), block size d
+ *    (d = 1 or d = 8, n % d == 0), K codewords per block.
+ *  - Device buffers are float32/int32, row-major, allocated and owned by the
+ *    caller (W: m x n, s: r, V: n x r with orthonormal columns, row_scale and
+ *    row_offset: m).  The library never allocates device memory: all scratch
+ *    lives in the caller's `workspace` of at least mpq_workspace_bytes(...)
+ *    bytes (256-byte aligned).
+ *  - The base codebook `cb` is a HOST pointer, K x d float32 row-major; row
+ *    i's codewords are  c = row_scale[i] * e + row_offset[i]  for e in cb.
+ *    It is read before the call returns.  d = 1: 2 <= K <= 64, any values.
+ *    d = 8: 1 <= K <= 65536 and every entry and every half squared norm
+ *    ||e||^2 / 2 must be exactly representable in bfloat16 (true for the
+ *    half-integer E8 lattice points); otherwise MPQ_EUNSUPPORTED.
+ *  - row_scale[i] must be > 0.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream); calls return after enqueueing.  Outputs are valid once the
+ *    stream reaches that point.  Calls that share one workspace must not
+ *    overlap.
+ *  - Errors: 0 on success, a negative MPQ_E* code otherwise.  Arguments are
+ *    validated before anything is enqueued; on error nothing is launched
+ *    and no output is touched.  Nothing throws across the ABI.
+ *  - Results are deterministic: the same inputs give bitwise-identical
+ *    outputs (fixed-order reductions, no atomics on floating point).
+ */
+#ifndef MPQ_H
+#define MPQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MPQ_OK               0
+#define MPQ_ENULL           -1   /* a required pointer is NULL */
+#define MPQ_ESHAPE          -2   /* m < 0, n < 1, r < 1, r > n, n % d != 0, K out of range */
+#define MPQ_EPARAM          -3   /* T_vamp < 0, n_cd < 0, damping not in (0, 1] */
+#define MPQ_EUNSUPPORTED    -4   /* d not in {1, 8}, or a d = 8 codebook not exact in bfloat16 */
+#define MPQ_EWORKSPACE      -5   /* workspace NULL, misaligned or smaller than required */
+#define MPQ_EHIP            -6   /* a HIP runtime call failed */
+
+/* Optional controls (pass NULL for defaults; zero-initialise unused fields). */
+typedef struct {
+  float beta0;            /* > 0: initial inverse temperature for every row;
+                             <= 0: beta^0 = r / ||T (w - w_rtn)||^2 (the M-step at
+                             the round-to-nearest point with zero variance) */
+  uint32_t flags;         /* MPQ_F_FIXED_BETA: skip the beta M-step (beta stays beta^0)
+                             MPQ_F_PROFILE: time kernel groups with HIP events on
+                             `stream` (the call then waits for its own work) */
+  uint32_t prof_mask;     /* with MPQ_F_PROFILE: bit k times category k (MPQ_PROF_*) */
+  double* prof_ms;        /* host, MPQ_PROF_COUNT entries: milliseconds are ADDED */
+  int64_t* prof_launches; /* host, MPQ_PROF_COUNT entries: kernel launches ADDED */
+} mpq_options;
+
+#define MPQ_F_FIXED_BETA 1u
+#define MPQ_F_PROFILE    2u
+
+/* Profiling categories (kernel groups). */
+#define MPQ_PROF_PROLOGUE  0  /* rank-space projection, RTN, beta^0 */
+#define MPQ_PROF_DENOISE   1  /* blockwise discrete denoiser */
+#define MPQ_PROF_EXTRINSIC 2  /* denoiser -> linear extrinsic update */
+#define MPQ_PROF_LINEAR1   3  /* linear module GEMM 1 (P = R2 VS, u, z, M-step terms) */
+#define MPQ_PROF_BETA      4  /* beta M-step, eta2, gamma1' */
+#define MPQ_PROF_LINEAR2   5  /* linear module GEMM 2 (r1' = r2 + c V z) */
+#define MPQ_PROF_MAP       6  /* marginal MAP */
+#define MPQ_PROF_CD_GEMM   7  /* CD residual / gradient GEMMs */
+#define MPQ_PROF_CD_SEARCH 8  /* CD candidate search and moves */
+#define MPQ_PROF_OTHER     9  /* traces, copies, factor preparation */
+#define MPQ_PROF_COUNT    10
+
+/* Bytes of device workspace needed by every entry point for these shapes. */
+size_t mpq_workspace_bytes(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d);
+
+/* Human-readable text for a status code (static storage). */
+const char* mpq_strerror(int status);
+
+/*
+ * Full layer solve: prologue, T_vamp VAMP iterations, marginal MAP, n_cd CD
+ * sweeps.  Passages: the papernotes.org MPQ summary -- flowchart and key
+ * designs 1 (denoiser, rank-space linear module), 2 (beta M-step, damping),
+ * 3 (marginal MAP, exact block CD) and the hyper-parameter paragraph
+ * (gamma1^0 = 1 / MSE(w, w_rtn), S_CD sweeps with early stop).
+ *
+ * Outputs (device, caller-owned):
+ *   codes      m x (n/d) int32: index into cb of each block's final codeword.
+ *   beta_tr    m x (T_vamp+1): beta^0 .. beta^T          (may be NULL)
+ *   gamma1_tr  m x (T_vamp+1): gamma1^0 .. gamma1^T      (may be NULL)
+ *   gamma2_tr  m x T_vamp    : gamma2^0 .. gamma2^{T-1}  (may be NULL)
+ *   cd_changes m x n_cd int32: blocks changed in each CD sweep (may be NULL)
+ * A row whose round-to-nearest point already has zero objective keeps its
+ * RTN codes and reports +inf traces and zero changes.
+ */
+int mpq_quantize_layer(const float* W, int64_t m, int64_t n,
+                       const float* s, const float* V, int64_t r,
+                       const float* cb, int64_t K, int64_t d,
+                       const float* row_scale, const float* row_offset,
+                       int T_vamp, int n_cd, float damping, const mpq_options* opt,
+                       int32_t* codes, float* beta_tr, float* gamma1_tr, float* gamma2_tr,
+                       int32_t* cd_changes, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Step-level entry points.  They expose each stage of the solve on caller
+ * state so that a single stage can be compared with the oracle on the
+ * oracle's own inputs.  Every one of them prepares the rank-space factors
+ * and codebook tables in `workspace` from (s, V, cb) before running.
+ */
+
+/* Prologue (hyper-parameter paragraph; beta^0 as in mpq_options):
+ * ytil = s * (V^T w) (m x r), rtn_codes (m x n/d), gamma1 = 1/MSE(w, w_rtn),
+ * beta = beta^0 (m each). */
+int mpq_prologue(const float* W, int64_t m, int64_t n, const float* s, const float* V, int64_t r,
+                 const float* cb, int64_t K, int64_t d, const float* row_scale, const float* row_offset,
+                 const mpq_options* opt, float* ytil, int32_t* rtn_codes, float* gamma1, float* beta,
+                 void* workspace, size_t ws_bytes, void* stream);
+
+/* Blockwise discrete denoiser (key design 1): for every block, the posterior
+ * q_b(c) ~ exp(-gamma1/2 ||c - r1_b||^2) over the row's codewords, its mean
+ * xhat1 (m x n) and the trace of its covariance per block, vtrace (m x n/d). */
+int mpq_denoise(const float* R1, const float* gamma1, int64_t m, int64_t n,
+                const float* cb, int64_t K, int64_t d, const float* row_scale, const float* row_offset,
+                float* xhat1, float* vtrace, void* workspace, size_t ws_bytes, void* stream);
+
+/* One VAMP iteration (key designs 1 and 2) in place on (R1, gamma1, beta):
+ * denoise -> extrinsic (r2, gamma2) -> linear module -> beta M-step with
+ * damping -> extrinsic (r1', gamma1').  Optional outputs (may be NULL):
+ * xhat1 (m x n), eta1 (m), gamma2 (m), r2 (m x n), fallback (m int32: 1
+ * when eta1 <= gamma1 and the posterior was passed through). */
+int mpq_vamp_step(float* R1, float* gamma1, float* beta, const float* ytil, int64_t m, int64_t n,
+                  const float* s, const float* V, int64_t r, const float* cb, int64_t K, int64_t d,
+                  const float* row_scale, const float* row_offset, float damping, const mpq_options* opt,
+                  float* xhat1, float* eta1, float* gamma2, float* r2, int32_t* fallback,
+                  void* workspace, size_t ws_bytes, void* stream);
+
+/* Marginal MAP (key design 3): codes[i, b] = argmax_c q_b(c) at (R1, gamma1);
+ * under the uniform prior this is the nearest codeword (ties: lowest index). */
+int mpq_map(const float* R1, const float* gamma1, int64_t m, int64_t n,
+            const float* cb, int64_t K, int64_t d, const float* row_scale, const float* row_offset,
+            int32_t* codes, void* workspace, size_t ws_bytes, void* stream);
+
+/* Exact block coordinate descent (key design 3) from `codes` (updated in
+ * place): at most n_cd sweeps over the blocks in ascending order, each block
+ * moved to the codeword minimising 1/2 ||u - T_b (c - x_b)||^2 when that is
+ * a strict improvement.  cd_changes (m x n_cd, may be NULL) counts moves. */
+int mpq_cd(const float* W, int64_t m, int64_t n, const float* s, const float* V, int64_t r,
+           const float* cb, int64_t K, int64_t d, const float* row_scale, const float* row_offset,
+           int n_cd, int32_t* codes, int32_t* cd_changes, void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MPQ_H */

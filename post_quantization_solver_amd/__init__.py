@@ -1,0 +1,11 @@
+"""MPQ post-training-quantization layer solver for AMD Instinct MI355X.
+
+The solver (rank-space VAMP with a blockwise discrete denoiser and an
+empirical-Bayes inverse temperature, then marginal MAP and exact block
+coordinate descent) runs in hand-written HIP kernels for gfx950 behind the
+C ABI of include/mpq.h (libmpq.so).  This package is the thin binding.
+"""
+from .binding import (  # noqa: F401
+    EXPORTS, LIB_PATH, MPQError, PROF_NAMES, Profile, STATUS, cd, denoise, load_library, map_codes, prologue,
+    quantize_layer, vamp_step, workspace_bytes,
+)

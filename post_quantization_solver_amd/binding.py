@@ -1,0 +1,291 @@
+"""ctypes binding of libmpq.so (the C ABI in include/mpq.h).
+
+Argument marshalling only: every step of the solve runs in the library's HIP
+kernels.  Tensors are torch tensors on the GPU (float32 / int32, contiguous);
+the base codebook is a CPU float32 tensor or numpy array.  Work is enqueued on
+torch's current stream.  If the library is missing or fails to load, every
+call raises -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmpq.so")
+
+STATUS = {
+    0: "MPQ_OK", -1: "MPQ_ENULL", -2: "MPQ_ESHAPE", -3: "MPQ_EPARAM",
+    -4: "MPQ_EUNSUPPORTED", -5: "MPQ_EWORKSPACE", -6: "MPQ_EHIP",
+}
+F_FIXED_BETA = 1
+
+EXPORTS = ("mpq_workspace_bytes", "mpq_strerror", "mpq_quantize_layer", "mpq_prologue", "mpq_denoise",
+           "mpq_vamp_step", "mpq_map", "mpq_cd")
+
+
+class MPQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {STATUS.get(status, status)} ({_strerror(status)})")
+
+
+F_PROFILE = 2
+PROF_NAMES = ("prologue", "denoise", "extrinsic", "linear1", "beta", "linear2", "map", "cd_gemm", "cd_search",
+              "other")
+PROF_COUNT = len(PROF_NAMES)
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("beta0", ctypes.c_float), ("flags", ctypes.c_uint32), ("prof_mask", ctypes.c_uint32),
+                ("prof_ms", ctypes.POINTER(ctypes.c_double)), ("prof_launches", ctypes.POINTER(ctypes.c_int64))]
+
+
+class Profile:
+    """Host accumulators for the library's per-category event timing."""
+
+    def __init__(self, categories=PROF_NAMES):
+        self.ms = (ctypes.c_double * PROF_COUNT)()
+        self.launches = (ctypes.c_int64 * PROF_COUNT)()
+        self.mask = 0
+        for c in categories:
+            self.mask |= 1 << PROF_NAMES.index(c)
+
+    def as_dict(self):
+        return {nm: (float(self.ms[k]), int(self.launches[k])) for k, nm in enumerate(PROF_NAMES)
+                if self.mask >> k & 1}
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmpq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m post_quantization_solver_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    F = ctypes.c_float
+    SZ = ctypes.c_size_t
+    OPT = ctypes.POINTER(Options)
+    lib.mpq_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
+    lib.mpq_workspace_bytes.restype = SZ
+    lib.mpq_strerror.argtypes = [I]
+    lib.mpq_strerror.restype = ctypes.c_char_p
+    lib.mpq_quantize_layer.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, I, I, F, OPT,
+                                       P, P, P, P, P, P, SZ, P]
+    lib.mpq_prologue.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, OPT, P, P, P, P, P, SZ, P]
+    lib.mpq_denoise.argtypes = [P, P, I64, I64, P, I64, I64, P, P, P, P, P, SZ, P]
+    lib.mpq_vamp_step.argtypes = [P, P, P, P, I64, I64, P, P, I64, P, I64, I64, P, P, F, OPT,
+                                  P, P, P, P, P, P, SZ, P]
+    lib.mpq_map.argtypes = [P, P, I64, I64, P, I64, I64, P, P, P, P, SZ, P]
+    lib.mpq_cd.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, I, P, P, P, SZ, P]
+    for name in EXPORTS[2:]:
+        getattr(lib, name).restype = I
+    _lib = lib
+    return lib
+
+
+def _strerror(status: int) -> str:
+    try:
+        return load_library().mpq_strerror(int(status)).decode()
+    except Exception:  # noqa: BLE001 - only used to decorate an error message
+        return "?"
+
+
+def workspace_bytes(m, n, r, K, d) -> int:
+    return int(load_library().mpq_workspace_bytes(m, n, r, K, d))
+
+
+# ---------------------------------------------------------------- helpers
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, dtype, name, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _host_codebook(cb):
+    arr = cb.detach().cpu().numpy() if hasattr(cb, "detach") else np.asarray(cb)
+    arr = np.ascontiguousarray(arr, dtype=np.float32)
+    if arr.ndim != 2:
+        raise ValueError("codebook must be K x d")
+    return arr
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _workspace(m, n, r, K, d, device):
+    import torch
+    nb = workspace_bytes(m, n, r, K, d)
+    if nb == 0:
+        raise MPQError(-2, "mpq_workspace_bytes")
+    return torch.empty(nb, dtype=torch.uint8, device=device)
+
+
+def _opts(beta0=None, fixed_beta=False, profile=None):
+    flags = (F_FIXED_BETA if fixed_beta else 0) | (F_PROFILE if profile is not None else 0)
+    o = Options(float(beta0) if beta0 else 0.0, flags, profile.mask if profile is not None else 0,
+                profile.ms if profile is not None else None, profile.launches if profile is not None else None)
+    return ctypes.byref(o), o
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise MPQError(rc, what)
+
+
+# ---------------------------------------------------------------- entry points
+
+def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, damping=0.5, beta0=None,
+                   fixed_beta=False, workspace=None, traces=True, profile=None, outputs=None):
+    """Full MPQ solve of one layer (mpq_quantize_layer).
+
+    Returns dict(codes, beta_tr, gamma1_tr, gamma2_tr, cd_changes) of device
+    tensors.  `profile` (a Profile) turns on the library's event timing;
+    `outputs` (a dict from a previous call) reuses its output tensors.
+    """
+    import torch
+    m, n = W.shape
+    r = s.shape[0]
+    E = _host_codebook(cb)
+    K, d = E.shape
+    dev = W.device
+    _dev(W, torch.float32, "W")
+    _dev(s, torch.float32, "s", (r,))
+    _dev(V, torch.float32, "V", (n, r))
+    _dev(row_scale, torch.float32, "row_scale", (m,))
+    _dev(row_offset, torch.float32, "row_offset", (m,))
+    if outputs is not None:
+        codes, bt, g1, g2, ch = (outputs[k] for k in ("codes", "beta_tr", "gamma1_tr", "gamma2_tr", "cd_changes"))
+    else:
+        codes = torch.empty((m, n // d if d else 0), dtype=torch.int32, device=dev)
+        bt = torch.empty((m, T_vamp + 1), dtype=torch.float32, device=dev) if traces else None
+        g1 = torch.empty((m, T_vamp + 1), dtype=torch.float32, device=dev) if traces else None
+        g2 = torch.empty((m, T_vamp), dtype=torch.float32, device=dev) if traces and T_vamp > 0 else None
+        ch = torch.zeros((m, n_cd), dtype=torch.int32, device=dev) if traces and n_cd > 0 else None
+    ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
+    op, _keep = _opts(beta0, fixed_beta, profile)
+    rc = load_library().mpq_quantize_layer(
+        _ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d, _ptr(row_scale),
+        _ptr(row_offset), int(T_vamp), int(n_cd), float(damping), op, _ptr(codes), _ptr(bt), _ptr(g1), _ptr(g2),
+        _ptr(ch), _ptr(ws), ws.numel(), _stream())
+    _check(rc, "mpq_quantize_layer")
+    return dict(codes=codes, beta_tr=bt, gamma1_tr=g1, gamma2_tr=g2, cd_changes=ch)
+
+
+def prologue(W, s, V, cb, row_scale, row_offset, beta0=None, workspace=None):
+    import torch
+    m, n = W.shape
+    r = s.shape[0]
+    E = _host_codebook(cb)
+    K, d = E.shape
+    dev = W.device
+    ytil = torch.empty((m, r), dtype=torch.float32, device=dev)
+    rtn = torch.empty((m, n // d), dtype=torch.int32, device=dev)
+    gamma1 = torch.empty(m, dtype=torch.float32, device=dev)
+    beta = torch.empty(m, dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
+    op, _keep = _opts(beta0)
+    rc = load_library().mpq_prologue(_ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d,
+                                     _ptr(row_scale), _ptr(row_offset), op, _ptr(ytil), _ptr(rtn), _ptr(gamma1),
+                                     _ptr(beta), _ptr(ws), ws.numel(), _stream())
+    _check(rc, "mpq_prologue")
+    return dict(ytil=ytil, rtn_codes=rtn, gamma1=gamma1, beta=beta)
+
+
+def denoise(R1, gamma1, cb, row_scale, row_offset, workspace=None):
+    import torch
+    m, n = R1.shape
+    E = _host_codebook(cb)
+    K, d = E.shape
+    dev = R1.device
+    _dev(R1, torch.float32, "R1")
+    _dev(gamma1, torch.float32, "gamma1", (m,))
+    xhat = torch.empty_like(R1)
+    vtr = torch.empty((m, n // d), dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else _workspace(m, n, n, K, d, dev)
+    rc = load_library().mpq_denoise(_ptr(R1), _ptr(gamma1), m, n, E.ctypes.data_as(ctypes.c_void_p), K, d,
+                                    _ptr(row_scale), _ptr(row_offset), _ptr(xhat), _ptr(vtr), _ptr(ws), ws.numel(),
+                                    _stream())
+    _check(rc, "mpq_denoise")
+    return xhat, vtr
+
+
+def vamp_step(R1, gamma1, beta, ytil, s, V, cb, row_scale, row_offset, damping=0.5, fixed_beta=False,
+              workspace=None):
+    """One VAMP iteration in place on (R1, gamma1, beta); returns the diagnostics."""
+    import torch
+    m, n = R1.shape
+    r = s.shape[0]
+    E = _host_codebook(cb)
+    K, d = E.shape
+    dev = R1.device
+    for t, nm in ((R1, "R1"), (gamma1, "gamma1"), (beta, "beta"), (ytil, "ytil")):
+        _dev(t, torch.float32, nm)
+    xhat = torch.empty_like(R1)
+    r2 = torch.empty_like(R1)
+    eta1 = torch.empty(m, dtype=torch.float32, device=dev)
+    gamma2 = torch.empty(m, dtype=torch.float32, device=dev)
+    fb = torch.empty(m, dtype=torch.int32, device=dev)
+    ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
+    op, _keep = _opts(None, fixed_beta)
+    rc = load_library().mpq_vamp_step(_ptr(R1), _ptr(gamma1), _ptr(beta), _ptr(ytil), m, n, _ptr(s), _ptr(V), r,
+                                      E.ctypes.data_as(ctypes.c_void_p), K, d, _ptr(row_scale), _ptr(row_offset),
+                                      float(damping), op, _ptr(xhat), _ptr(eta1), _ptr(gamma2), _ptr(r2), _ptr(fb),
+                                      _ptr(ws), ws.numel(), _stream())
+    _check(rc, "mpq_vamp_step")
+    return dict(xhat1=xhat, eta1=eta1, gamma2=gamma2, r2=r2, fallback=fb)
+
+
+def map_codes(R1, gamma1, cb, row_scale, row_offset, workspace=None):
+    import torch
+    m, n = R1.shape
+    E = _host_codebook(cb)
+    K, d = E.shape
+    codes = torch.empty((m, n // d), dtype=torch.int32, device=R1.device)
+    ws = workspace if workspace is not None else _workspace(m, n, n, K, d, R1.device)
+    rc = load_library().mpq_map(_ptr(R1), _ptr(gamma1), m, n, E.ctypes.data_as(ctypes.c_void_p), K, d,
+                                _ptr(row_scale), _ptr(row_offset), _ptr(codes), _ptr(ws), ws.numel(), _stream())
+    _check(rc, "mpq_map")
+    return codes
+
+
+def cd(W, s, V, cb, row_scale, row_offset, codes, n_cd=3, workspace=None):
+    """Block CD from `codes` (a device int32 tensor, updated in place)."""
+    import torch
+    m, n = W.shape
+    r = s.shape[0]
+    E = _host_codebook(cb)
+    K, d = E.shape
+    _dev(codes, torch.int32, "codes", (m, n // d))
+    ch = torch.zeros((m, max(n_cd, 1)), dtype=torch.int32, device=W.device)
+    ws = workspace if workspace is not None else _workspace(m, n, r, K, d, W.device)
+    rc = load_library().mpq_cd(_ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d,
+                               _ptr(row_scale), _ptr(row_offset), int(n_cd), _ptr(codes), _ptr(ch), _ptr(ws),
+                               ws.numel(), _stream())
+    _check(rc, "mpq_cd")
+    return codes, ch[:, :n_cd]

@@ -1,0 +1,639 @@
+// Host orchestration and the C ABI declared in include/mpq.h.
+//
+// Every entry point validates its arguments on the host, carves the caller's
+// workspace, uploads the codebook tables and then enqueues kernels on the
+// caller's stream.  Nothing is allocated and no state outlives a call.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+#include <algorithm>
+#include <vector>
+
+#include "../../include/mpq.h"
+#include "internal.h"
+
+namespace mpq {
+// launchers defined in the kernel files
+hipError_t launch_denoise_scalar(const float*, const float*, int64_t, int64_t, const CbTables&, const float*,
+                                 const float*, float*, float*, hipStream_t);
+hipError_t launch_nearest_scalar(const float*, int64_t, int64_t, const CbTables&, const float*, const float*,
+                                 int32_t*, hipStream_t);
+hipError_t launch_denoise_lattice(const float*, const float*, int64_t, int64_t, const CbTables&, const float*,
+                                  const float*, float*, float*, hipStream_t);
+hipError_t launch_nearest_lattice(const float*, int64_t, int64_t, const CbTables&, const float*, const float*,
+                                  int32_t*, hipStream_t);
+hipError_t launch_beta_lin(int64_t, const float*, const float*, float*, float*, hipStream_t);
+hipError_t launch_fill_i32(int32_t*, int64_t, int32_t, hipStream_t);
+hipError_t launch_cd_lattice_block(int64_t, int64_t, int64_t, int, int, float*, const float*, const CbTables&,
+                                   const float*, int32_t*, float*, int32_t*, float*, int32_t*, hipStream_t);
+int cd_lattice_slices(int Kpad);
+hipError_t launch_record_i32(const int32_t* src, int64_t m, int32_t* dst, int64_t ld, int64_t col, hipStream_t st);
+}  // namespace mpq
+
+using namespace mpq;
+
+namespace {
+
+constexpr int KD = 256;          // CD tile width (columns)
+constexpr int LAT_CHUNK = 128;   // lattice codebook padding granularity
+constexpr size_t ALIGN = 256;
+
+#define MPQ_TRY(x)                       \
+  do {                                   \
+    hipError_t e_ = (x);                 \
+    if (e_ != hipSuccess) return MPQ_EHIP; \
+  } while (0)
+
+// Run a launch expression; with profiling on for `cat`, bracket it with
+// events recorded on the call's stream.
+#define TIMED(c, cat, expr)                                         \
+  do {                                                              \
+    if ((c).timed(cat)) {                                           \
+      Prof::Ev ev_{nullptr, nullptr, (cat)};                        \
+      MPQ_TRY(hipEventCreate(&ev_.a));                              \
+      if (hipEventCreate(&ev_.b) != hipSuccess) {                   \
+        hipEventDestroy(ev_.a);                                     \
+        return MPQ_EHIP;                                            \
+      }                                                             \
+      (c).prof.evs.push_back(ev_);                                  \
+      MPQ_TRY(hipEventRecord(ev_.a, (c).st));                       \
+      MPQ_TRY(expr);                                                \
+      MPQ_TRY(hipEventRecord(ev_.b, (c).st));                       \
+    } else {                                                        \
+      MPQ_TRY(expr);                                                \
+    }                                                               \
+  } while (0)
+
+struct Layout {
+  int64_t m, n, r, K, d, B;
+  int Kpad, ncoltiles, ntiles, nslices;
+  size_t off[32];
+  size_t total;
+};
+
+enum Region {
+  R_VS, R_VST, R_YTIL, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI,
+  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_COUNT
+};
+
+size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
+  Layout L;
+  L.m = m; L.n = n; L.r = r; L.K = K; L.d = d;
+  L.B = n / d;
+  L.Kpad = d == 8 ? (int)((K + LAT_CHUNK - 1) / LAT_CHUNK * LAT_CHUNK) : (int)K;
+  L.ncoltiles = gemm_col_tiles((int)std::max(r, n));
+  L.ntiles = (int)((n + KD - 1) / KD);
+  L.nslices = d == 8 ? cd_lattice_slices(L.Kpad) : 0;
+  size_t sz[R_COUNT];
+  const size_t f = sizeof(float);
+  sz[R_VS] = (size_t)n * r * f;
+  sz[R_VST] = (size_t)n * r * f;
+  sz[R_YTIL] = (size_t)m * r * f;
+  sz[R_R1] = (size_t)m * n * f;
+  sz[R_R2] = (size_t)m * n * f;
+  sz[R_X1] = (size_t)m * n * f;
+  sz[R_Z] = (size_t)m * r * f;
+  sz[R_VBLK] = (size_t)m * L.B * f;
+  sz[R_ROWS] = (size_t)8 * m * f;
+  sz[R_PART] = (size_t)m * L.ncoltiles * f;
+  sz[R_GT] = (size_t)m * KD * f;
+  sz[R_DELTA] = (size_t)m * KD * f;
+  sz[R_HD] = (size_t)L.ntiles * KD * KD * f;
+  sz[R_PS] = (size_t)std::max(L.nslices, 1) * m * f;
+  sz[R_PI] = (size_t)std::max(L.nslices, 1) * m * sizeof(int32_t);
+  sz[R_CHG] = (size_t)m * sizeof(int32_t);
+  sz[R_CODES] = (size_t)m * L.B * sizeof(int32_t);
+  sz[R_LEVELS] = 64 * f;
+  sz[R_QK] = d == 8 ? (size_t)L.Kpad * 16 * sizeof(uint32_t) : 0;
+  sz[R_PV] = d == 8 ? (size_t)L.Kpad * 8 * sizeof(uint32_t) : 0;
+  sz[R_E32] = (size_t)(d == 8 ? L.Kpad : 64) * 8 * f;
+  size_t o = 0;
+  for (int k = 0; k < R_COUNT; ++k) {
+    L.off[k] = o;
+    o += round_up(std::max(sz[k], (size_t)ALIGN));
+  }
+  L.total = o;
+  return L;
+}
+
+// Opt-in event timing of kernel groups (MPQ_F_PROFILE).
+struct Prof {
+  struct Ev {
+    hipEvent_t a, b;
+    int cat;
+  };
+  bool on = false;
+  uint32_t mask = 0;
+  double* ms = nullptr;
+  int64_t* launches = nullptr;
+  std::vector<Ev> evs;
+  ~Prof() {
+    for (auto& e : evs) {
+      hipEventDestroy(e.a);
+      hipEventDestroy(e.b);
+    }
+  }
+};
+
+struct Ctx {
+  Layout L;
+  char* ws;
+  hipStream_t st;
+  CbTables cb;
+  Prof prof;
+  bool timed(int cat) const { return prof.on && (prof.mask >> cat & 1u); }
+  float* p(Region k) const { return reinterpret_cast<float*>(ws + L.off[k]); }
+  int32_t* pi(Region k) const { return reinterpret_cast<int32_t*>(ws + L.off[k]); }
+  float* rowv(int k) const { return p(R_ROWS) + (size_t)k * L.m; }
+  float* gamma1() const { return rowv(0); }
+  float* beta() const { return rowv(1); }
+  float* gamma2() const { return rowv(2); }
+  float* eta1() const { return rowv(3); }
+  float* coef() const { return rowv(4); }
+  float* betalin() const { return rowv(5); }
+  float* rowsq() const { return rowv(6); }
+};
+
+bool bf16_exact(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  return std::isfinite(x) && (u & 0xffffu) == 0;
+}
+
+uint16_t bf16_bits(float x) {  // exact values only
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  return (uint16_t)(u >> 16);
+}
+
+void split3_host(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
+  auto rne = [](float v) -> uint16_t {
+    uint32_t u;
+    memcpy(&u, &v, 4);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+  };
+  auto back = [](uint16_t b) -> float {
+    uint32_t u = (uint32_t)b << 16;
+    float v;
+    memcpy(&v, &u, 4);
+    return v;
+  };
+  h = rne(x);
+  float r1 = x - back(h);
+  m = rne(r1);
+  float r2 = r1 - back(m);
+  l = rne(r2);
+}
+
+int check_codebook(const float* cb, int64_t K, int64_t d) {
+  if (d != 1 && d != 8) return MPQ_EUNSUPPORTED;
+  if (d == 1) {
+    if (K < 2 || K > 64) return MPQ_ESHAPE;
+    for (int64_t k = 0; k < K; ++k)
+      if (!std::isfinite(cb[k])) return MPQ_EPARAM;
+    return MPQ_OK;
+  }
+  if (K < 1 || K > 65536) return MPQ_ESHAPE;
+  for (int64_t k = 0; k < K; ++k) {
+    float h = 0.f;
+    for (int q = 0; q < 8; ++q) {
+      float v = cb[k * 8 + q];
+      if (!bf16_exact(v)) return MPQ_EUNSUPPORTED;
+      h += v * v;
+    }
+    if (!bf16_exact(0.5f * h)) return MPQ_EUNSUPPORTED;
+  }
+  return MPQ_OK;
+}
+
+int check_shapes(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
+  if (d != 1 && d != 8) return MPQ_EUNSUPPORTED;
+  if (m < 0 || n < 1 || r < 1 || r > n || n % d != 0) return MPQ_ESHAPE;
+  if (d == 1 && (K < 2 || K > 64)) return MPQ_ESHAPE;
+  if (d == 8 && (K < 1 || K > 65536)) return MPQ_ESHAPE;
+  if (m > ((int64_t)1 << 23) || n > ((int64_t)1 << 20)) return MPQ_ESHAPE;
+  return MPQ_OK;
+}
+
+int check_ws(const Layout& L, void* ws, size_t bytes) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0 || bytes < L.total) return MPQ_EWORKSPACE;
+  return MPQ_OK;
+}
+
+// Upload the codebook tables into the workspace (host -> device, then wait
+// for the copy so the staging buffer can be released).
+int upload_codebook(Ctx& c, const float* cb) {
+  const Layout& L = c.L;
+  c.cb.K = (int)L.K;
+  c.cb.d = (int)L.d;
+  c.cb.Kpad = L.Kpad;
+  c.cb.levels = c.p(R_LEVELS);
+  c.cb.e32 = c.p(R_E32);
+  c.cb.qk_keys = reinterpret_cast<const uint32_t*>(c.p(R_QK));
+  c.cb.pv_ops = reinterpret_cast<const uint32_t*>(c.p(R_PV));
+  if (L.d == 1) {
+    std::vector<float> lv(64, 0.f);
+    for (int64_t k = 0; k < L.K; ++k) lv[k] = cb[k];
+    MPQ_TRY(hipMemcpyAsync(c.p(R_LEVELS), lv.data(), 64 * sizeof(float), hipMemcpyHostToDevice, c.st));
+    MPQ_TRY(hipMemcpyAsync(c.p(R_E32), lv.data(), 64 * sizeof(float), hipMemcpyHostToDevice, c.st));
+    MPQ_TRY(hipStreamSynchronize(c.st));
+    return MPQ_OK;
+  }
+  const int Kp = L.Kpad;
+  std::vector<float> e32((size_t)Kp * 8, 0.f);
+  std::vector<uint16_t> qk((size_t)Kp * 32, 0);   // (Kp/16) subtiles x 64 lanes x 8 bf16
+  std::vector<uint16_t> pv((size_t)Kp * 16, 0);   // (Kp/32) steps x 64 lanes x 8 bf16
+  std::vector<float> nrm(Kp, 0.f);
+  const uint16_t neg1 = bf16_bits(-1.f);
+  const uint16_t big = bf16_bits(-1.2676506e30f);  // -2^100 for padding codewords
+  for (int c0 = 0; c0 < Kp; ++c0) {
+    float h = 0.f;
+    if (c0 < L.K) {
+      for (int q = 0; q < 8; ++q) {
+        e32[(size_t)c0 * 8 + q] = cb[(size_t)c0 * 8 + q];
+        h += cb[(size_t)c0 * 8 + q] * cb[(size_t)c0 * 8 + q];
+      }
+      nrm[c0] = h;
+    }
+    // QK key fragment: subtile c0 / 16, lane (i = c0 % 16, g)
+    const int stl = c0 / 16, ci = c0 % 16;
+    for (int g = 0; g < 4; ++g) {
+      uint16_t* w = &qk[(((size_t)stl * 64) + g * 16 + ci) * 8];
+      if (g < 3) {
+        for (int q = 0; q < 8; ++q) w[q] = c0 < L.K ? bf16_bits(cb[(size_t)c0 * 8 + q]) : 0;
+      } else {
+        uint16_t mh = c0 < L.K ? bf16_bits(-0.5f * h) : big;
+        w[0] = mh; w[1] = mh; w[2] = mh;
+        w[3] = neg1; w[4] = neg1; w[5] = neg1;
+        w[6] = 0; w[7] = 0;
+      }
+    }
+  }
+  // PV fragment: step s (32 codewords), lane (i = output column, g), slot t
+  // <-> codeword 32 s + (t < 4 ? 4 g + t : 16 + 4 g + t - 4); columns
+  // 0..7 e, 8..10 ||e||^2 as hi/mid/lo bf16, 11 the constant 1.
+  for (int s = 0; s < Kp / 32; ++s) {
+    for (int g = 0; g < 4; ++g) {
+      for (int i = 0; i < 16; ++i) {
+        uint16_t* w = &pv[(((size_t)s * 64) + g * 16 + i) * 8];
+        for (int tt = 0; tt < 8; ++tt) {
+          int cw = 32 * s + (tt < 4 ? 4 * g + tt : 16 + 4 * g + tt - 4);
+          uint16_t val = 0;
+          if (cw < L.K) {
+            if (i < 8) {
+              val = bf16_bits(cb[(size_t)cw * 8 + i]);
+            } else if (i <= 10) {
+              uint16_t hh, mm, ll;
+              split3_host(nrm[cw], hh, mm, ll);
+              val = i == 8 ? hh : (i == 9 ? mm : ll);
+            } else if (i == 11) {
+              val = bf16_bits(1.f);
+            }
+          }
+          w[tt] = val;
+        }
+      }
+    }
+  }
+  MPQ_TRY(hipMemcpyAsync(c.p(R_E32), e32.data(), e32.size() * sizeof(float), hipMemcpyHostToDevice, c.st));
+  MPQ_TRY(hipMemcpyAsync(c.p(R_QK), qk.data(), qk.size() * sizeof(uint16_t), hipMemcpyHostToDevice, c.st));
+  MPQ_TRY(hipMemcpyAsync(c.p(R_PV), pv.data(), pv.size() * sizeof(uint16_t), hipMemcpyHostToDevice, c.st));
+  MPQ_TRY(hipStreamSynchronize(c.st));
+  return MPQ_OK;
+}
+
+GemmArgs gemm(int M, int N, int K, const float* A, int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda;
+  g.B = B; g.ldb = ldb;
+  g.C = C; g.ldc = ldc;
+  g.batch = 1;
+  return g;
+}
+
+hipError_t nearest(const Ctx& c, const float* R, int32_t* codes, const float* a, const float* o) {
+  if (c.L.d == 1) return launch_nearest_scalar(R, c.L.m, c.L.n, c.cb, a, o, codes, c.st);
+  return launch_nearest_lattice(R, c.L.m, c.L.n, c.cb, a, o, codes, c.st);
+}
+
+hipError_t denoise(const Ctx& c, const float* R1, const float* gamma1, const float* a, const float* o, float* xhat,
+                   float* vblk) {
+  if (c.L.d == 1) return launch_denoise_scalar(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.st);
+  return launch_denoise_lattice(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.st);
+}
+
+int prepare_factors(Ctx& c, const float* V, const float* s) {
+  TIMED(c, MPQ_PROF_OTHER, launch_scale_columns(V, s, c.L.n, c.L.r, c.p(R_VS), c.p(R_VST), c.st));
+  return MPQ_OK;
+}
+
+// Collect profiling results (waits for the call's last event).
+int finish(Ctx& c, int rc) {
+  if (rc != MPQ_OK || !c.prof.on || c.prof.evs.empty()) return rc;
+  MPQ_TRY(hipEventSynchronize(c.prof.evs.back().b));
+  for (auto& e : c.prof.evs) {
+    float ms = 0.f;
+    MPQ_TRY(hipEventElapsedTime(&ms, e.a, e.b));
+    if (c.prof.ms) c.prof.ms[e.cat] += ms;
+    if (c.prof.launches) c.prof.launches[e.cat] += 1;
+  }
+  return rc;
+}
+
+// ytil = W VS, RTN codes, gamma1^0, beta^0.
+int run_prologue(Ctx& c, const float* W, const float* a, const float* o, const mpq_options* opt, float* ytil,
+                 int32_t* rtn, float* gamma1, float* beta) {
+  const Layout& L = c.L;
+  TIMED(c, MPQ_PROF_PROLOGUE,
+        launch_gemm(EPI_STORE, gemm((int)L.m, (int)L.r, (int)L.n, W, L.n, c.p(R_VST), L.n, ytil, L.r), c.st));
+  TIMED(c, MPQ_PROF_PROLOGUE, nearest(c, W, rtn, a, o));
+  TIMED(c, MPQ_PROF_PROLOGUE, launch_gather(rtn, L.m, L.n, c.cb, a, o, W, nullptr, c.p(R_X1), c.rowsq(), c.st));
+  GemmArgs g = gemm((int)L.m, (int)L.r, (int)L.n, c.p(R_X1), L.n, c.p(R_VST), L.n, nullptr, 0);
+  g.partial = c.p(R_PART);
+  g.ldp = gemm_col_tiles((int)L.r);
+  TIMED(c, MPQ_PROF_PROLOGUE, launch_gemm(EPI_ROWSUMSQ, g, c.st));
+  float b0 = (opt && opt->beta0 > 0.f) ? opt->beta0 : 0.f;
+  TIMED(c, MPQ_PROF_PROLOGUE, launch_prologue_finish(L.m, L.n, L.r, c.rowsq(), c.p(R_PART), gemm_col_tiles((int)L.r), b0, gamma1, beta,
+                                 nullptr, c.st));
+  return MPQ_OK;
+}
+
+// One VAMP iteration on (R1, gamma1, beta).  gamma2_rec (optional) receives
+// gamma2 as the extrinsic step produced it.
+int run_iteration(Ctx& c, float* R1, float* gamma1, float* beta, const float* ytil, const float* s, const float* a,
+                  const float* o, float damping, int fixed_beta, float* xhat_out, float* eta1_out,
+                  float* gamma2_out, float* r2_out, int32_t* fallback_out, float* trace_g2, int64_t ld_g2,
+                  int64_t col) {
+  const Layout& L = c.L;
+  float* X1 = c.p(R_X1);
+  float* R2 = c.p(R_R2);
+  TIMED(c, MPQ_PROF_DENOISE, denoise(c, R1, gamma1, a, o, X1, c.p(R_VBLK)));
+  if (xhat_out) TIMED(c, MPQ_PROF_OTHER, launch_copy_rows_f(X1, xhat_out, L.m * L.n, c.st));
+  TIMED(c, MPQ_PROF_EXTRINSIC,
+        launch_extrinsic(R1, X1, c.p(R_VBLK), L.m, L.n, L.B, a, gamma1, R2, c.gamma2(),
+                         eta1_out ? eta1_out : c.eta1(), fallback_out, c.st));
+  if (gamma2_out) TIMED(c, MPQ_PROF_OTHER, launch_copy_rows_f(c.gamma2(), gamma2_out, L.m, c.st));
+  if (trace_g2) TIMED(c, MPQ_PROF_OTHER, launch_record(c.gamma2(), L.m, trace_g2, ld_g2, col, c.st));
+  if (r2_out) TIMED(c, MPQ_PROF_OTHER, launch_copy_rows_f(R2, r2_out, L.m * L.n, c.st));
+  TIMED(c, MPQ_PROF_EXTRINSIC, launch_beta_lin(L.m, gamma1, beta, c.betalin(), c.gamma2(), c.st));
+  GemmArgs g1 = gemm((int)L.m, (int)L.r, (int)L.n, R2, L.n, c.p(R_VST), L.n, c.p(R_Z), L.r);
+  g1.X = ytil; g1.ldx = L.r;
+  g1.s = s;
+  g1.rowa = c.betalin();
+  g1.rowb = c.gamma2();
+  g1.partial = c.p(R_PART);
+  g1.ldp = gemm_col_tiles((int)L.r);
+  TIMED(c, MPQ_PROF_LINEAR1, launch_gemm(EPI_LINEAR1, g1, c.st));
+  TIMED(c, MPQ_PROF_BETA, launch_beta(L.m, L.n, L.r, s, c.p(R_PART), gemm_col_tiles((int)L.r), c.gamma2(), damping, fixed_beta, beta,
+                      gamma1, c.coef(), c.st));
+  GemmArgs g2 = gemm((int)L.m, (int)L.n, (int)L.r, c.p(R_Z), L.r, c.p(R_VS), L.r, R1, L.n);
+  g2.X = R2; g2.ldx = L.n;
+  g2.rowa = c.coef();
+  TIMED(c, MPQ_PROF_LINEAR2, launch_gemm(EPI_AXPY_ROW, g2, c.st));
+  return MPQ_OK;
+}
+
+// n_cd sweeps of exact block CD from `codes` (workspace or caller buffer).
+int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int32_t* codes, int32_t* cd_changes) {
+  const Layout& L = c.L;
+  if (n_cd <= 0 || L.m == 0) return MPQ_OK;
+  float* X = c.p(R_R2);     // codeword values (scalar CD keeps them current)
+  float* D = c.p(R_X1);     // W - X
+  float* U = c.p(R_Z);      // rank-space residual
+  float* Gt = c.p(R_GT);
+  float* Dl = c.p(R_DELTA);
+  float* Hd = c.p(R_HD);
+  int32_t* chg = c.pi(R_CHG);
+  TIMED(c, MPQ_PROF_CD_GEMM, launch_gather(codes, L.m, L.n, c.cb, a, o, W, X, D, nullptr, c.st));
+  TIMED(c, MPQ_PROF_CD_GEMM,
+        launch_gemm(EPI_STORE, gemm((int)L.m, (int)L.r, (int)L.n, D, L.n, c.p(R_VST), L.n, U, L.r), c.st));
+  // diagonal tiles of H = VS VS^T
+  const int full = (int)(L.n / KD);
+  if (full > 0) {
+    GemmArgs h = gemm(KD, KD, (int)L.r, c.p(R_VS), L.r, c.p(R_VS), L.r, Hd, KD);
+    h.batch = full;
+    h.sA = (int64_t)KD * L.r;
+    h.sB = (int64_t)KD * L.r;
+    h.sC = (int64_t)KD * KD;
+    TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm(EPI_STORE, h, c.st));
+  }
+  const int rem = (int)(L.n - (int64_t)full * KD);
+  if (rem > 0) {
+    const float* vs = c.p(R_VS) + (int64_t)full * KD * L.r;
+    TIMED(c, MPQ_PROF_CD_GEMM,
+          launch_gemm(EPI_STORE, gemm(rem, rem, (int)L.r, vs, L.r, vs, L.r, Hd + (int64_t)full * KD * KD, rem),
+                      c.st));
+  }
+  for (int sw = 0; sw < n_cd; ++sw) {
+    TIMED(c, MPQ_PROF_OTHER, launch_fill_i32(chg, L.m, 0, c.st));
+    for (int tl = 0; tl < L.ntiles; ++tl) {
+      const int64_t j0 = (int64_t)tl * KD;
+      const int kw = (int)std::min<int64_t>(KD, L.n - j0);
+      const float* Ht = Hd + (int64_t)tl * KD * KD;
+      TIMED(c, MPQ_PROF_CD_GEMM,
+            launch_gemm(EPI_STORE, gemm((int)L.m, kw, (int)L.r, U, L.r, c.p(R_VS) + j0 * L.r, L.r, Gt, kw), c.st));
+      if (L.d == 1) {
+        TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_scalar_tile(L.m, L.n, j0, kw, Gt, Ht, c.cb, a, o, codes, X, Dl, chg, c.st));
+      } else {
+        for (int bl = 0; bl < kw / 8; ++bl) {
+          TIMED(c, MPQ_PROF_CD_SEARCH,
+                launch_cd_lattice_block(L.m, L.n, j0 / 8 + bl, bl, kw, Gt, Ht, c.cb, a, codes, Dl, chg, c.p(R_PS),
+                                        c.pi(R_PI), c.st));
+        }
+      }
+      TIMED(c, MPQ_PROF_CD_GEMM,
+            launch_gemm(EPI_SUB_INPLACE, gemm((int)L.m, (int)L.r, kw, Dl, kw, c.p(R_VST) + j0, L.n, U, L.r), c.st));
+    }
+    if (cd_changes) TIMED(c, MPQ_PROF_OTHER, launch_record_i32(chg, L.m, cd_changes, n_cd, sw, c.st));
+  }
+  return MPQ_OK;
+}
+
+// The whole layer: prologue, T_vamp iterations, marginal MAP, CD.
+int solve_layer(Ctx& c, const float* W, const float* s, const float* V, const float* row_scale,
+                const float* row_offset, int T_vamp, int n_cd, float damping, const mpq_options* opt, int32_t* codes,
+                float* beta_tr, float* gamma1_tr, float* gamma2_tr, int32_t* cd_changes) {
+  int rc = prepare_factors(c, V, s);
+  if (rc) return rc;
+  const Layout& L = c.L;
+  const int fixed = (opt && (opt->flags & MPQ_F_FIXED_BETA)) ? 1 : 0;
+  float* R1 = c.p(R_R1);
+  rc = run_prologue(c, W, row_scale, row_offset, opt, c.p(R_YTIL), c.pi(R_CODES), c.gamma1(), c.beta());
+  if (rc) return rc;
+  TIMED(c, MPQ_PROF_OTHER, launch_copy_rows_f(W, R1, L.m * L.n, c.st));
+  for (int t = 0; t < T_vamp; ++t) {
+    TIMED(c, MPQ_PROF_OTHER, launch_record(c.beta(), L.m, beta_tr, T_vamp + 1, t, c.st));
+    TIMED(c, MPQ_PROF_OTHER, launch_record(c.gamma1(), L.m, gamma1_tr, T_vamp + 1, t, c.st));
+    rc = run_iteration(c, R1, c.gamma1(), c.beta(), c.p(R_YTIL), s, row_scale, row_offset, damping, fixed, nullptr,
+                       nullptr, nullptr, nullptr, nullptr, gamma2_tr, T_vamp, t);
+    if (rc) return rc;
+  }
+  TIMED(c, MPQ_PROF_OTHER, launch_record(c.beta(), L.m, beta_tr, T_vamp + 1, T_vamp, c.st));
+  TIMED(c, MPQ_PROF_OTHER, launch_record(c.gamma1(), L.m, gamma1_tr, T_vamp + 1, T_vamp, c.st));
+  // marginal MAP at (r1^T, gamma1^T); frozen rows keep r1 = w, i.e. their RTN codes
+  TIMED(c, MPQ_PROF_MAP, nearest(c, R1, codes, row_scale, row_offset));
+  return run_cd(c, W, row_scale, row_offset, n_cd, codes, cd_changes);
+}
+
+int begin(Ctx& c, int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, const float* cb, void* ws, size_t bytes,
+          void* stream, const mpq_options* opt = nullptr) {
+  if (opt && (opt->flags & MPQ_F_PROFILE)) {
+    c.prof.on = true;
+    c.prof.mask = opt->prof_mask;
+    c.prof.ms = opt->prof_ms;
+    c.prof.launches = opt->prof_launches;
+  }
+  int rc = check_shapes(m, n, r, K, d);
+  if (rc) return rc;
+  if (!cb) return MPQ_ENULL;
+  rc = check_codebook(cb, K, d);
+  if (rc) return rc;
+  c.L = make_layout(m, n, r, K, d);
+  rc = check_ws(c.L, ws, bytes);
+  if (rc) return rc;
+  c.ws = static_cast<char*>(ws);
+  c.st = static_cast<hipStream_t>(stream);
+  return MPQ_OK;
+}
+
+}  // namespace
+
+namespace mpq {
+__global__ void record_i32_kernel(const int32_t* __restrict__ src, int64_t m, int32_t* __restrict__ dst, int64_t ld,
+                                  int64_t col) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < m) dst[i * ld + col] = src[i];
+}
+hipError_t launch_record_i32(const int32_t* src, int64_t m, int32_t* dst, int64_t ld, int64_t col, hipStream_t st) {
+  if (m <= 0 || !dst) return hipSuccess;
+  hipLaunchKernelGGL(record_i32_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, src, m, dst, ld, col);
+  return hipGetLastError();
+}
+}  // namespace mpq
+
+extern "C" {
+
+size_t mpq_workspace_bytes(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
+  if (check_shapes(m, n, r, K, d) != MPQ_OK) return 0;
+  return make_layout(m, n, r, K, d).total;
+}
+
+const char* mpq_strerror(int status) {
+  switch (status) {
+    case MPQ_OK: return "ok";
+    case MPQ_ENULL: return "a required pointer is NULL";
+    case MPQ_ESHAPE: return "invalid shape (m, n, r, K, d)";
+    case MPQ_EPARAM: return "invalid parameter (T_vamp, n_cd, damping or a non-finite codebook entry)";
+    case MPQ_EUNSUPPORTED: return "unsupported codebook (d must be 1 or 8; d = 8 entries must be exact in bfloat16)";
+    case MPQ_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case MPQ_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int mpq_quantize_layer(const float* W, int64_t m, int64_t n, const float* s, const float* V, int64_t r,
+                       const float* cb, int64_t K, int64_t d, const float* row_scale, const float* row_offset,
+                       int T_vamp, int n_cd, float damping, const mpq_options* opt, int32_t* codes, float* beta_tr,
+                       float* gamma1_tr, float* gamma2_tr, int32_t* cd_changes, void* workspace, size_t ws_bytes,
+                       void* stream) {
+  if (T_vamp < 0 || n_cd < 0 || !(damping > 0.f && damping <= 1.f)) return MPQ_EPARAM;
+  int rc = check_shapes(m, n, r, K, d);
+  if (rc) return rc;
+  if (m == 0) return MPQ_OK;
+  if (!W || !s || !V || !row_scale || !row_offset || !codes) return MPQ_ENULL;
+  Ctx c;
+  rc = begin(c, m, n, r, K, d, cb, workspace, ws_bytes, stream, opt);
+  if (rc) return rc;
+  rc = upload_codebook(c, cb);
+  if (rc) return rc;
+  return finish(c, solve_layer(c, W, s, V, row_scale, row_offset, T_vamp, n_cd, damping, opt, codes, beta_tr,
+                               gamma1_tr, gamma2_tr, cd_changes));
+}
+
+int mpq_prologue(const float* W, int64_t m, int64_t n, const float* s, const float* V, int64_t r, const float* cb,
+                 int64_t K, int64_t d, const float* row_scale, const float* row_offset, const mpq_options* opt,
+                 float* ytil, int32_t* rtn_codes, float* gamma1, float* beta, void* workspace, size_t ws_bytes,
+                 void* stream) {
+  int rc = check_shapes(m, n, r, K, d);
+  if (rc) return rc;
+  if (m == 0) return MPQ_OK;
+  if (!W || !s || !V || !row_scale || !row_offset || !ytil || !rtn_codes || !gamma1 || !beta) return MPQ_ENULL;
+  Ctx c;
+  rc = begin(c, m, n, r, K, d, cb, workspace, ws_bytes, stream, opt);
+  if (rc) return rc;
+  if ((rc = upload_codebook(c, cb))) return rc;
+  if ((rc = prepare_factors(c, V, s))) return rc;
+  return finish(c, run_prologue(c, W, row_scale, row_offset, opt, ytil, rtn_codes, gamma1, beta));
+}
+
+int mpq_denoise(const float* R1, const float* gamma1, int64_t m, int64_t n, const float* cb, int64_t K, int64_t d,
+                const float* row_scale, const float* row_offset, float* xhat1, float* vtrace, void* workspace,
+                size_t ws_bytes, void* stream) {
+  int rc = check_shapes(m, n, n, K, d);
+  if (rc) return rc;
+  if (m == 0) return MPQ_OK;
+  if (!R1 || !gamma1 || !row_scale || !row_offset || !xhat1 || !vtrace) return MPQ_ENULL;
+  Ctx c;
+  rc = begin(c, m, n, 1, K, d, cb, workspace, ws_bytes, stream);
+  if (rc) return rc;
+  if ((rc = upload_codebook(c, cb))) return rc;
+  MPQ_TRY(denoise(c, R1, gamma1, row_scale, row_offset, xhat1, vtrace));
+  return MPQ_OK;
+}
+
+int mpq_vamp_step(float* R1, float* gamma1, float* beta, const float* ytil, int64_t m, int64_t n, const float* s,
+                  const float* V, int64_t r, const float* cb, int64_t K, int64_t d, const float* row_scale,
+                  const float* row_offset, float damping, const mpq_options* opt, float* xhat1, float* eta1,
+                  float* gamma2, float* r2, int32_t* fallback, void* workspace, size_t ws_bytes, void* stream) {
+  if (!(damping > 0.f && damping <= 1.f)) return MPQ_EPARAM;
+  int rc = check_shapes(m, n, r, K, d);
+  if (rc) return rc;
+  if (m == 0) return MPQ_OK;
+  if (!R1 || !gamma1 || !beta || !ytil || !s || !V || !row_scale || !row_offset) return MPQ_ENULL;
+  Ctx c;
+  rc = begin(c, m, n, r, K, d, cb, workspace, ws_bytes, stream, opt);
+  if (rc) return rc;
+  if ((rc = upload_codebook(c, cb))) return rc;
+  if ((rc = prepare_factors(c, V, s))) return rc;
+  const int fixed = (opt && (opt->flags & MPQ_F_FIXED_BETA)) ? 1 : 0;
+  return finish(c, run_iteration(c, R1, gamma1, beta, ytil, s, row_scale, row_offset, damping, fixed, xhat1, eta1,
+                                 gamma2, r2, fallback, nullptr, 0, 0));
+}
+
+int mpq_map(const float* R1, const float* gamma1, int64_t m, int64_t n, const float* cb, int64_t K, int64_t d,
+            const float* row_scale, const float* row_offset, int32_t* codes, void* workspace, size_t ws_bytes,
+            void* stream) {
+  int rc = check_shapes(m, n, n, K, d);
+  if (rc) return rc;
+  if (m == 0) return MPQ_OK;
+  if (!R1 || !gamma1 || !row_scale || !row_offset || !codes) return MPQ_ENULL;
+  Ctx c;
+  rc = begin(c, m, n, 1, K, d, cb, workspace, ws_bytes, stream);
+  if (rc) return rc;
+  if ((rc = upload_codebook(c, cb))) return rc;
+  MPQ_TRY(nearest(c, R1, codes, row_scale, row_offset));
+  return MPQ_OK;
+}
+
+int mpq_cd(const float* W, int64_t m, int64_t n, const float* s, const float* V, int64_t r, const float* cb, int64_t K,
+           int64_t d, const float* row_scale, const float* row_offset, int n_cd, int32_t* codes, int32_t* cd_changes,
+           void* workspace, size_t ws_bytes, void* stream) {
+  if (n_cd < 0) return MPQ_EPARAM;
+  int rc = check_shapes(m, n, r, K, d);
+  if (rc) return rc;
+  if (m == 0) return MPQ_OK;
+  if (!W || !s || !V || !row_scale || !row_offset || !codes) return MPQ_ENULL;
+  Ctx c;
+  rc = begin(c, m, n, r, K, d, cb, workspace, ws_bytes, stream);
+  if (rc) return rc;
+  if ((rc = upload_codebook(c, cb))) return rc;
+  if ((rc = prepare_factors(c, V, s))) return rc;
+  return run_cd(c, W, row_scale, row_offset, n_cd, codes, cd_changes);
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Exact block coordinate descent (d = 1), tiled.
+//
+// The residual u = y~ - T x lives in rank space (m x r).  For a tile of kd
+// consecutive columns the solver forms the tile gradient g = T_tile^T u with
+// one GEMM, runs the exact sequential CD over the tile's columns on g (after a
+// move delta at column j, g_j' -= H[j][j'] delta with H = T^T T restricted to
+// the tile), and then applies u -= T_tile Delta with a second GEMM.  In exact
+// arithmetic this is the plain per-block sweep: the tile only batches the
+// residual updates.
+//
+// This kernel: one wave per row; the tile's gradient, codes and codeword
+// values sit in registers (lane l, slot s <-> column s*64 + l).
+#include <math.h>
+#include "mpq_device.h"
+#include "internal.h"
+
+namespace mpq {
+
+template <int SLOTS>
+__global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t n, int64_t j0, int kd,
+                                                             const float* __restrict__ G, const float* __restrict__ Ht,
+                                                             const float* __restrict__ levels, int K,
+                                                             const float* __restrict__ a, const float* __restrict__ o,
+                                                             int32_t* __restrict__ codes, float* __restrict__ X,
+                                                             float* __restrict__ Delta, int32_t* __restrict__ changes) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= m) return;
+  const float ai = a[i], oi = o[i];
+  const float cl = lane < K ? fmaf(ai, levels[lane], oi) : 0.f;
+
+  float g[SLOTS], x[SLOTS], dl[SLOTS];
+  int cd[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    int jj = s * 64 + lane;
+    bool in = jj < kd;
+    g[s] = in ? G[i * kd + jj] : 0.f;
+    x[s] = in ? X[i * n + j0 + jj] : 0.f;
+    cd[s] = in ? codes[i * n + j0 + jj] : 0;
+    dl[s] = 0.f;
+  }
+  int moved = 0;
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    for (int jl = 0; jl < 64; ++jl) {
+      const int jj = s * 64 + jl;
+      if (jj >= kd) break;
+      const float gj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g[s]), jl));
+      const float xj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[s]), jl));
+      const float hjj = Ht[(int64_t)jj * kd + jj];
+      // dF(c) = 1/2 H_jj (c - x_j)^2 - (c - x_j) g_j over the row's levels
+      float dlt = cl - xj;
+      float f = lane < K ? (0.5f * hjj * dlt - gj) * dlt : INFINITY;
+      int k = lane;
+#pragma unroll
+      for (int msk = 1; msk < 64; msk <<= 1) {
+        float fo = shfl_xor_f(f, msk);
+        int ko = shfl_xor_i(k, msk);
+        if (fo < f || (fo == f && ko < k)) { f = fo; k = ko; }
+      }
+      if (f < 0.f) {  // strict improvement only (uniform across the wave)
+        const float cnew = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), k));
+        const float dstar = cnew - xj;
+        if (lane == jl) { x[s] = cnew; cd[s] = k; dl[s] = dstar; }
+        ++moved;
+        const float* hrow = Ht + (int64_t)jj * kd;
+#pragma unroll
+        for (int s2 = 0; s2 < SLOTS; ++s2) {
+          int jc = s2 * 64 + lane;
+          if (jc < kd) g[s2] -= hrow[jc] * dstar;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    int jj = s * 64 + lane;
+    if (jj < kd) {
+      X[i * n + j0 + jj] = x[s];
+      codes[i * n + j0 + jj] = cd[s];
+      Delta[i * kd + jj] = dl[s];
+    }
+  }
+  if (lane == 0) changes[i] += moved;
+}
+
+hipError_t launch_cd_scalar_tile(int64_t m, int64_t n, int64_t j0, int kd, const float* G, const float* Ht,
+                                 const CbTables& cb, const float* a, const float* o, int32_t* codes, float* X,
+                                 float* Delta, int32_t* changes, hipStream_t st) {
+  if (m <= 0) return hipSuccess;
+  dim3 grid((unsigned)((m + 3) / 4));
+  if (kd <= 64)
+    hipLaunchKernelGGL((cd_scalar_tile_kernel<1>), grid, dim3(256), 0, st, m, n, j0, kd, G, Ht, cb.levels, cb.K, a, o,
+                       codes, X, Delta, changes);
+  else if (kd <= 128)
+    hipLaunchKernelGGL((cd_scalar_tile_kernel<2>), grid, dim3(256), 0, st, m, n, j0, kd, G, Ht, cb.levels, cb.K, a, o,
+                       codes, X, Delta, changes);
+  else if (kd <= 256)
+    hipLaunchKernelGGL((cd_scalar_tile_kernel<4>), grid, dim3(256), 0, st, m, n, j0, kd, G, Ht, cb.levels, cb.K, a, o,
+                       codes, X, Delta, changes);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace mpq

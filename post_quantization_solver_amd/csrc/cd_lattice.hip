@@ -1,0 +1,239 @@
+// Exact block coordinate descent for d = 8 codebooks.
+//
+// Within a tile of kd columns the tile gradient g = T_tile^T u (m x kd) is
+// kept current by the update kernel (g_b' -= H[b'][b] delta after a move at
+// block b).  For block b of the tile and row i with current codeword
+// x_b = a e_x + o, the change of the objective for candidate c = a e + o is
+//     dF(e) = 1/2 a^2 (e - e_x)^T G (e - e_x) - a (e - e_x)^T g_b,  G = H_bb,
+// i.e. up to a constant in e:
+//     score(e) = a^2 t(e) - e . q,   t(e) = e^T G e / 2,   q = a (a G e_x + g_b).
+// cd_score_kernel evaluates score(e) for every codeword with one bf16 MFMA per
+// 16 x 16 (codeword x row) tile -- key slots [e | e | e | t terms], query
+// slots [-q hi | -q mid | -q lo | a^2 terms], all products exact -- and keeps
+// the per-row argmin (ties: lowest index) of its codeword slice.
+// cd_update_kernel reduces the slices in order, re-evaluates dF of the winner
+// exactly in float32 and moves the block only on a strict decrease.
+#include <math.h>
+#include "mpq_device.h"
+#include "internal.h"
+
+namespace mpq {
+
+constexpr int CDL_ROWS_WAVE = 64;            // 4 row subtiles per wave
+constexpr int CDL_ROWS_WG = 4 * CDL_ROWS_WAVE;
+constexpr int CDL_CW_WG = 1024;              // codewords per workgroup slice
+
+__device__ __forceinline__ v4u pack8(const uint32_t (&w)[8]) {
+  v4u r;
+  r.x = pack2(w[0], w[1]);
+  r.y = pack2(w[2], w[3]);
+  r.z = pack2(w[4], w[5]);
+  r.w = pack2(w[6], w[7]);
+  return r;
+}
+
+// grid: (slices, row groups).  part_s / part_i: [slices][m].
+__global__ __launch_bounds__(256) void cd_score_kernel(int64_t m, int64_t n, int64_t b, int bl, int kd,
+                                                       const float* __restrict__ Gt, const float* __restrict__ Ht,
+                                                       const uint32_t* __restrict__ keys,
+                                                       const float* __restrict__ e32, int K, int Kpad,
+                                                       const float* __restrict__ a, const int32_t* __restrict__ codes,
+                                                       float* __restrict__ part_s, int32_t* __restrict__ part_i) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds_key[(CDL_CW_WG / 16) * 64 * 4];
+  __shared__ float Gb[64];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int64_t B = n / 8;
+  const int cw_base = blockIdx.x * CDL_CW_WG;
+  const int ncw = min(CDL_CW_WG, Kpad - cw_base);
+  const int64_t row_base = (int64_t)blockIdx.y * CDL_ROWS_WG + wave * CDL_ROWS_WAVE;
+
+  if (t < 64) Gb[t] = Ht[(int64_t)(8 * bl + (t >> 3)) * kd + 8 * bl + (t & 7)];
+  __syncthreads();
+
+  // key fragments of this slice: lanes g < 3 copy e, lanes g = 3 carry t(e) terms
+  for (int f = t; f < (ncw / 16) * 64; f += 256) {
+    const int st = f >> 6, ln = f & 63, gi = ln >> 4, ci = ln & 15;
+    const int cw = cw_base + st * 16 + ci;
+    v4u w;
+    if (gi < 3) {
+      w = reinterpret_cast<const v4u*>(keys)[(int64_t)(cw_base / 16 + st) * 64 + ln];
+    } else {
+      float tq;
+      if (cw < K) {
+        const float* e = e32 + (int64_t)cw * 8;
+        float acc = 0.f;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          float rowv = 0.f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) rowv = fmaf(Gb[p * 8 + q], e[q], rowv);
+          acc = fmaf(e[p], rowv, acc);
+        }
+        tq = 0.5f * acc;
+      } else {
+        tq = 1.2676506e30f;  // 2^100: padding never wins
+      }
+      uint32_t h, mm, l;
+      split3_bf16(tq, h, mm, l);
+      uint32_t ww[8] = {h, mm, l, h, mm, h, 0u, 0u};
+      w = pack8(ww);
+    }
+    reinterpret_cast<v4u*>(lds_key)[f] = w;
+  }
+  __syncthreads();
+
+  // row queries: lane (j, g) of subtile q serves row row_base + 16 q + j
+  v4u qop[4];
+  float best[4];
+  int bidx[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t i = row_base + q * 16 + j;
+    float qv[8];
+    float A = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qv[k] = 0.f;
+    if (i < m) {
+      const float ai = a[i];
+      const float* ex = e32 + (int64_t)codes[i * B + b] * 8;
+      const float* gb = Gt + i * kd + 8 * bl;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        float ge = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ge = fmaf(Gb[p * 8 + k], ex[k], ge);
+        qv[p] = -ai * fmaf(ai, ge, gb[p]);
+      }
+      A = ai * ai;
+    }
+    uint32_t w[8];
+    if (g < 3) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        uint32_t h, mm, l;
+        split3_bf16(qv[k], h, mm, l);
+        w[k] = g == 0 ? h : (g == 1 ? mm : l);
+      }
+    } else {
+      uint32_t h, mm, l;
+      split3_bf16(A, h, mm, l);
+      w[0] = h; w[1] = h; w[2] = h; w[3] = mm; w[4] = mm; w[5] = l; w[6] = 0; w[7] = 0;
+    }
+    qop[q] = pack8(w);
+    best[q] = INFINITY;
+    bidx[q] = 0x7fffffff;
+  }
+
+  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+  const v4u* kq = reinterpret_cast<const v4u*>(lds_key);
+#pragma unroll 2
+  for (int st = 0; st < ncw / 16; ++st) {
+    const v4u k0 = kq[st * 64 + lane];
+    const int cw0 = cw_base + st * 16 + 4 * g;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v4f s = mfma_bf16_16x16x32(k0, qop[q], zero4);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (s[v] < best[q]) { best[q] = s[v]; bidx[q] = cw0 + v; }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float bv = best[q];
+    int bi = bidx[q];
+#pragma unroll
+    for (int msk = 16; msk <= 32; msk <<= 1) {
+      float ov = shfl_xor_f(bv, msk);
+      int oi = shfl_xor_i(bi, msk);
+      if (ov < bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    const int64_t i = row_base + q * 16 + j;
+    if (g == 0 && i < m) {
+      part_s[(int64_t)blockIdx.x * m + i] = bv;
+      part_i[(int64_t)blockIdx.x * m + i] = bi;
+    }
+  }
+}
+
+// One wave per row.
+__global__ __launch_bounds__(256) void cd_update_kernel(int64_t m, int64_t n, int64_t b, int bl, int kd, int nslices,
+                                                        float* __restrict__ Gt, const float* __restrict__ Ht,
+                                                        const float* __restrict__ e32, const float* __restrict__ a,
+                                                        const float* __restrict__ part_s,
+                                                        const int32_t* __restrict__ part_i,
+                                                        int32_t* __restrict__ codes, float* __restrict__ Delta,
+                                                        int32_t* __restrict__ changes) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= m) return;
+  const int64_t B = n / 8;
+  float bv = INFINITY;
+  int bi = 0x7fffffff;
+  for (int sl = 0; sl < nslices; ++sl) {
+    float v = part_s[(int64_t)sl * m + i];
+    int id = part_i[(int64_t)sl * m + i];
+    if (v < bv || (v == bv && id < bi)) { bv = v; bi = id; }
+  }
+  const int cx = codes[i * B + b];
+  float* dl = Delta + i * kd + 8 * bl;
+  bool accept = false;
+  float dlt[8];
+  if (bi != cx) {
+    const float ai = a[i];
+    const float* gb = Gt + i * kd + 8 * bl;
+    const float* en = e32 + (int64_t)bi * 8;
+    const float* eo = e32 + (int64_t)cx * 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dlt[k] = ai * (en[k] - eo[k]);
+    float f = 0.f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      float gd = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) gd = fmaf(Ht[(int64_t)(8 * bl + p) * kd + 8 * bl + k], dlt[k], gd);
+      f = fmaf(dlt[p], 0.5f * gd - gb[p], f);
+    }
+    accept = f < 0.f;
+  }
+  if (!accept) {
+    if (lane < 8) dl[lane] = 0.f;
+    return;
+  }
+  if (lane < 8) dl[lane] = dlt[lane];
+  if (lane == 0) {
+    codes[i * B + b] = bi;
+    changes[i] += 1;
+  }
+  // g_j -= sum_k H[j][8 bl + k] delta_k for every column j of the tile
+  for (int jc = lane; jc < kd; jc += 64) {
+    const float* hr = Ht + (int64_t)jc * kd + 8 * bl;
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s = fmaf(hr[k], dlt[k], s);
+    Gt[i * kd + jc] -= s;
+  }
+}
+
+hipError_t launch_cd_lattice_block(int64_t m, int64_t n, int64_t b, int bl, int kd, float* Gt, const float* Ht,
+                                   const CbTables& cb, const float* a, int32_t* codes, float* Delta,
+                                   int32_t* changes, float* part_s, int32_t* part_i, hipStream_t st) {
+  if (m <= 0) return hipSuccess;
+  const int nslices = (cb.Kpad + CDL_CW_WG - 1) / CDL_CW_WG;
+  dim3 g1((unsigned)nslices, (unsigned)((m + CDL_ROWS_WG - 1) / CDL_ROWS_WG));
+  hipLaunchKernelGGL(cd_score_kernel, g1, dim3(256), 0, st, m, n, b, bl, kd, Gt, Ht, cb.qk_keys, cb.e32, cb.K,
+                     cb.Kpad, a, codes, part_s, part_i);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(cd_update_kernel, dim3((unsigned)((m + 3) / 4)), dim3(256), 0, st, m, n, b, bl, kd, nslices, Gt,
+                     Ht, cb.e32, a, part_s, part_i, codes, Delta, changes);
+  return hipGetLastError();
+}
+
+int cd_lattice_slices(int Kpad) { return (Kpad + CDL_CW_WG - 1) / CDL_CW_WG; }
+
+}  // namespace mpq

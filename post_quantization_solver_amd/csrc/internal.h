@@ -1,0 +1,80 @@
+// Host-side declarations shared by the MPQ launchers (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace mpq {
+
+// ---------------------------------------------------------------- GEMM ----
+// C[M x N] (+)= A[M x K] * B[N x K]^T in float32 on the fp32 MFMA units.
+enum GemmEpi : int {
+  EPI_STORE = 0,        // C = acc
+  EPI_ROWSUMSQ = 1,     // partial[i][tile] = sum over the tile's columns of acc^2
+  EPI_LINEAR1 = 2,      // u = X - acc; C = beta u / (beta s^2 + gamma2);
+                        // partial[i][tile] = sum (gamma2 u / (beta s^2 + gamma2))^2
+  EPI_AXPY_ROW = 3,     // C = X + rowa[i] * acc
+  EPI_SUB_INPLACE = 4,  // C -= acc
+};
+
+struct GemmArgs {
+  int M, N, K;
+  const float* A; int64_t lda; int64_t sA;   // sA/sB/sC: batch strides (blockIdx.z)
+  const float* B; int64_t ldb; int64_t sB;
+  float* C; int64_t ldc; int64_t sC;
+  const float* X; int64_t ldx;
+  const float* s;
+  const float* rowa;
+  const float* rowb;
+  float* partial; int64_t ldp;
+  int batch;
+};
+
+constexpr int GEMM_BM = 128, GEMM_BN = 128;
+inline int gemm_col_tiles(int N) { return (N + GEMM_BN - 1) / GEMM_BN; }
+hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t st);
+
+// ------------------------------------------------------------ codebook ----
+// Device tables derived from the host codebook.
+struct CbTables {
+  int K, d;
+  int Kpad;                 // K rounded up to the lattice chunk size (d = 8)
+  const float* levels;      // d = 1: K base levels
+  const uint32_t* qk_keys;  // d = 8: QK operand fragments, Kpad/16 subtiles x 64 lanes x 4 words
+  const uint32_t* pv_ops;   // d = 8: PV operand fragments, Kpad/32 steps x 64 lanes x 4 words
+  const float* e32;         // d = 8: base codewords as float32, Kpad x 8
+};
+
+// ----------------------------------------------------------- kernels ----
+hipError_t launch_scale_columns(const float* V, const float* s, int64_t n, int64_t r, float* VS, float* VSt, hipStream_t st);
+
+// X = codewords of codes; optionally D = W - X and per-row sum of D^2.
+hipError_t launch_gather(const int32_t* codes, int64_t m, int64_t n, const CbTables& cb,
+                         const float* a, const float* o, const float* W, float* X, float* D,
+                         float* rowsq, hipStream_t st);
+
+// Prologue per-row finish: gamma1 = 1/mse, beta0 from partial sums, frozen flags.
+hipError_t launch_prologue_finish(int64_t m, int64_t n, int64_t r, const float* rowsq, const float* partial,
+                                  int nparts, float beta0_override, float* gamma1, float* beta,
+                                  float* beta_work, hipStream_t st);
+
+// Extrinsic denoiser -> linear: eta1 from the block variances, gamma2, r2.
+hipError_t launch_extrinsic(const float* R1, const float* xhat, const float* vblk, int64_t m, int64_t n, int64_t B,
+                            const float* a, const float* gamma1, float* R2, float* gamma2, float* eta1,
+                            int32_t* fallback, hipStream_t st);
+
+// beta M-step + linear-side extrinsic precision.
+hipError_t launch_beta(int64_t m, int64_t n, int64_t r, const float* s, const float* partial, int nparts,
+                       const float* gamma2, float damping, int fixed_beta, float* beta, float* gamma1,
+                       float* coef, hipStream_t st);
+
+// Trace / state bookkeeping.
+hipError_t launch_record(const float* src, int64_t m, float* dst, int64_t ld, int64_t col, hipStream_t st);
+hipError_t launch_copy_rows_f(const float* src, float* dst, int64_t count, hipStream_t st);
+
+// CD (scalar grids): one tile of kd columns starting at column j0.
+hipError_t launch_cd_scalar_tile(int64_t m, int64_t n, int64_t j0, int kd, const float* G, const float* Ht,
+                                 const CbTables& cb, const float* a, const float* o, int32_t* codes,
+                                 float* X, float* Delta, int32_t* changes, hipStream_t st);
+
+}  // namespace mpq

@@ -1,0 +1,362 @@
+// Lattice-codebook (d = 8) kernels on the bf16 matrix cores.
+//
+// A query is one (row i, block b): r' = (r1_b - o_i) / a_i in codebook units
+// and kappa = gamma1_i a_i^2.  Up to a per-query constant the denoiser's
+// log-weights are  kappa (e . r' - ||e||^2 / 2),  so scoring a query against
+// the whole codebook is a matrix product with the codebook (single-head
+// attention with head size 8: keys = values = codewords).
+//
+// Scores are formed exactly in float32 with one v_mfma_f32_16x16x32_bf16 per
+// 16 x 16 (codeword x query) tile: codeword entries and ||e||^2/2 are exact in
+// bfloat16 (checked on the host), and each float32 query coefficient enters as
+// three bfloat16 terms (hi + mid + lo), so every product is exact and only the
+// float32 accumulation rounds.  K-slots of one tile:
+//     key   : [ e (8) | e (8) | e (8) | -h, -h, -h, -1, -1, -1, 0, 0 ]
+//     query : [ (k'r')hi | (k'r')mid | (k'r')lo | k'hi, k'mid, k'lo, Mhi, Mmid, Mlo, 0, 0 ]
+// with h = ||e||^2 / 2, k' = kappa log2(e) and M the running log2 shift, giving
+//     S'(e) = k' (e . r' - h) - M      (log2 domain, already shifted).
+// The softmax is online: M only moves when a score exceeds it by more than
+// 8 (log2), so p = 2^S' stays in (0, 2^8] without per-tile rescaling.
+// The weighted sums  sum p e, sum p ||e||^2, sum p  come from a second MFMA
+// against [e | ||e||^2 (hi, mid, lo) | 1], with p split into bf16 hi + lo.
+#include <math.h>
+#include "mpq_device.h"
+#include "internal.h"
+
+namespace mpq {
+
+constexpr int LAT_WAVES = 4;
+constexpr int LAT_QSUB = 4;                      // 16-query subtiles per wave
+constexpr int LAT_QW = 16 * LAT_QSUB;            // queries per wave
+constexpr int LAT_QWG = LAT_QW * LAT_WAVES;      // queries per workgroup
+constexpr int LAT_CH = 128;                      // codewords per LDS chunk
+constexpr int LAT_KEY_WORDS = (LAT_CH / 16) * 64 * 4;   // uint32 per chunk (QK fragments)
+constexpr int LAT_PV_WORDS = (LAT_CH / 32) * 64 * 4;    // uint32 per chunk (PV fragments)
+constexpr float LAT_SLACK = 8.0f;                // lazy-shift window (log2 units)
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct QueryInfo {
+  int64_t i, b;
+  bool valid;
+};
+
+__device__ __forceinline__ QueryInfo query_of(int64_t Q, int64_t total, int64_t B) {
+  QueryInfo q;
+  q.valid = Q < total;
+  q.i = q.valid ? Q / B : 0;
+  q.b = q.valid ? Q - q.i * B : 0;
+  return q;
+}
+
+// Copy one chunk of codebook fragments (keys and optionally PV operands) into LDS.
+template <bool PV>
+__device__ __forceinline__ void load_chunk(uint32_t* __restrict__ lds_key, uint32_t* __restrict__ lds_pv,
+                                           const uint32_t* __restrict__ keys, const uint32_t* __restrict__ pv,
+                                           int64_t chunk, int t) {
+  const v4u* src = reinterpret_cast<const v4u*>(keys + chunk * LAT_KEY_WORDS);
+  v4u* dst = reinterpret_cast<v4u*>(lds_key);
+  for (int k = t; k < LAT_KEY_WORDS / 4; k += 256) dst[k] = src[k];
+  if (PV) {
+    const v4u* s2 = reinterpret_cast<const v4u*>(pv + chunk * LAT_PV_WORDS);
+    v4u* d2 = reinterpret_cast<v4u*>(lds_pv);
+    for (int k = t; k < LAT_PV_WORDS / 4; k += 256) d2[k] = s2[k];
+  }
+}
+
+// Build the lane's query operand.  Lane (j, g): group g = 0, 1, 2 carries the
+// hi / mid / lo bf16 terms of qv[0..7]; group 3 carries [k hi, mid, lo, M hi, mid, lo, 0, 0].
+__device__ __forceinline__ v4u make_query(const float (&qv)[8], float kap, float M, int g) {
+  uint32_t w[8];
+  if (g < 3) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t h, m, l;
+      split3_bf16(qv[k], h, m, l);
+      w[k] = g == 0 ? h : (g == 1 ? m : l);
+    }
+  } else {
+    uint32_t kh, km, kl, mh, mm, ml;
+    split3_bf16(kap, kh, km, kl);
+    split3_bf16(M, mh, mm, ml);
+    w[0] = kh; w[1] = km; w[2] = kl; w[3] = mh; w[4] = mm; w[5] = ml; w[6] = 0; w[7] = 0;
+  }
+  v4u r;
+  r.x = pack2(w[0], w[1]);
+  r.y = pack2(w[2], w[3]);
+  r.z = pack2(w[4], w[5]);
+  r.w = pack2(w[6], w[7]);
+  return r;
+}
+
+__device__ __forceinline__ float max8(const v4f& a, const v4f& b) {
+  return fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
+}
+
+// p -> (hi, lo) bfloat16 pair words.  hi truncates p to its top 16 bits; lo
+// rounds the exact remainder p - hi to bfloat16.
+__device__ __forceinline__ void split_p(float p0, float p1, uint32_t& hw, uint32_t& lw) {
+  uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+  hw = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+  float l0 = p0 - __uint_as_float(b0 & 0xffff0000u);
+  float l1 = p1 - __uint_as_float(b1 & 0xffff0000u);
+  lw = pack2(f2bf_bits(l0), f2bf_bits(l1));
+}
+
+__global__ __launch_bounds__(256) void denoise_lattice_kernel(
+    const float* __restrict__ R1, const float* __restrict__ gamma1, int64_t m, int64_t n,
+    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ pvops, const float* __restrict__ e32,
+    int Kpad, const float* __restrict__ a, const float* __restrict__ o, float* __restrict__ xhat,
+    float* __restrict__ vblk) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds_key[2][LAT_KEY_WORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_pv[2][LAT_PV_WORDS];
+  __shared__ float fin[LAT_QWG][13];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int64_t B = n / 8;
+  const int64_t total = m * B;
+  const int64_t qbase = (int64_t)blockIdx.x * LAT_QWG + wave * LAT_QW;
+
+  // ---- per-query setup (each of the 4 lanes of a query computes the same values)
+  v4u qop[LAT_QSUB];
+  float kap[LAT_QSUB], Mq[LAT_QSUB], qv[LAT_QSUB][8];
+  const float h0 = 0.5f * (e32[0] * e32[0] + e32[1] * e32[1] + e32[2] * e32[2] + e32[3] * e32[3] +
+                           e32[4] * e32[4] + e32[5] * e32[5] + e32[6] * e32[6] + e32[7] * e32[7]);
+#pragma unroll
+  for (int q = 0; q < LAT_QSUB; ++q) {
+    QueryInfo qi = query_of(qbase + q * 16 + j, total, B);
+    float k2 = 0.f;
+    float rp[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) rp[k] = 0.f;
+    if (qi.valid) {
+      float gm = gamma1[qi.i];
+      if (isfinite(gm)) {
+        float ai = a[qi.i], oi = o[qi.i];
+        const float* rr = R1 + qi.i * n + qi.b * 8;
+        float inva = 1.f / ai;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rp[k] = (rr[k] - oi) * inva;
+        k2 = gm * ai * ai * LOG2E;
+      }
+    }
+    // initial shift: the score of codeword 0, a lower bound of the maximum
+    float s0 = -h0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s0 = fmaf(e32[k], rp[k], s0);
+    kap[q] = k2;
+    Mq[q] = k2 * s0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qv[q][k] = k2 * rp[k];
+    qop[q] = make_query(qv[q], k2, Mq[q], g);
+  }
+
+  // acc: this chunk's sums (the MFMAs accumulate at most 2 * LAT_CH / 32
+  // products into it); tot: running total, updated by one float32 add per
+  // chunk so long accumulations round to nearest at every step.
+  v4f acc[LAT_QSUB], tot[LAT_QSUB];
+#pragma unroll
+  for (int q = 0; q < LAT_QSUB; ++q) {
+    acc[q] = (v4f){0.f, 0.f, 0.f, 0.f};
+    tot[q] = (v4f){0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int nchunks = Kpad / LAT_CH;
+  load_chunk<true>(lds_key[0], lds_pv[0], keys, pvops, 0, t);
+  __syncthreads();
+  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < nchunks; ++c) {
+    const int cur = c & 1;
+    if (c + 1 < nchunks) load_chunk<true>(lds_key[cur ^ 1], lds_pv[cur ^ 1], keys, pvops, c + 1, t);
+    const v4u* kq = reinterpret_cast<const v4u*>(lds_key[cur]);
+    const v4u* pq = reinterpret_cast<const v4u*>(lds_pv[cur]);
+#pragma unroll 1
+    for (int st = 0; st < LAT_CH / 32; ++st) {
+      const v4u k0 = kq[(2 * st) * 64 + lane];
+      const v4u k1 = kq[(2 * st + 1) * 64 + lane];
+      const v4u pv = pq[st * 64 + lane];
+#pragma unroll
+      for (int q = 0; q < LAT_QSUB; ++q) {
+        v4f s0 = mfma_bf16_16x16x32(k0, qop[q], zero4);
+        v4f s1 = mfma_bf16_16x16x32(k1, qop[q], zero4);
+        float lm = max8(s0, s1);
+        if (__builtin_amdgcn_ballot_w64(lm > LAT_SLACK)) {
+          // move the shift of every query whose scores exceed the window
+          float mx = fmaxf(lm, shfl_xor_f(lm, 16));
+          mx = fmaxf(mx, shfl_xor_f(mx, 32));
+          float dM = mx > LAT_SLACK ? mx : 0.f;
+          if (dM > 0.f) {
+            Mq[q] += dM;
+            float f = __builtin_amdgcn_exp2f(-dM);
+            acc[q] *= f;
+            tot[q] *= f;
+          }
+          qop[q] = make_query(qv[q], kap[q], Mq[q], g);
+          s0 = mfma_bf16_16x16x32(k0, qop[q], zero4);
+          s1 = mfma_bf16_16x16x32(k1, qop[q], zero4);
+        }
+        float p[8];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          p[v] = __builtin_amdgcn_exp2f(s0[v]);
+          p[4 + v] = __builtin_amdgcn_exp2f(s1[v]);
+        }
+        uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+        split_p(p[0], p[1], h0, l0);
+        split_p(p[2], p[3], h1, l1);
+        split_p(p[4], p[5], h2, l2);
+        split_p(p[6], p[7], h3, l3);
+        v4u hi = {h0, h1, h2, h3};
+        v4u lo = {l0, l1, l2, l3};
+        acc[q] = mfma_bf16_16x16x32(pv, hi, acc[q]);
+        acc[q] = mfma_bf16_16x16x32(pv, lo, acc[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < LAT_QSUB; ++q) {
+      tot[q] += acc[q];
+      acc[q] = zero4;
+    }
+    __syncthreads();
+  }
+
+  // ---- finish: lane (j, g) holds columns 4g..4g+3 of query j's sums:
+  // 0..7 sum p e, 8..10 sum p ||e||^2 (hi, mid, lo), 11 sum p.
+#pragma unroll
+  for (int q = 0; q < LAT_QSUB; ++q) {
+    const int ql = wave * LAT_QW + q * 16 + j;
+    if (g < 3) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) fin[ql][4 * g + v] = tot[q][v];
+    }
+  }
+  __syncthreads();
+  {
+    const int ql = t;  // one thread per query of the workgroup
+    const int64_t Q = (int64_t)blockIdx.x * LAT_QWG + ql;
+    QueryInfo qi = query_of(Q, total, B);
+    if (qi.valid) {
+      float gm = gamma1[qi.i];
+      float* xo = xhat + qi.i * n + qi.b * 8;
+      if (!isfinite(gm)) {
+        const float* rr = R1 + qi.i * n + qi.b * 8;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) xo[k] = rr[k];
+        vblk[qi.i * B + qi.b] = 0.f;
+      } else {
+        float ai = a[qi.i], oi = o[qi.i];
+        float z = fin[ql][11];
+        float invz = 1.f / z;
+        float m2 = (fin[ql][8] + fin[ql][9] + fin[ql][10]) * invz;
+        float nx = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          float mk = fin[ql][k] * invz;
+          nx = fmaf(mk, mk, nx);
+          xo[k] = fmaf(ai, mk, oi);
+        }
+        vblk[qi.i * B + qi.b] = fmaxf(m2 - nx, 0.f) * ai * ai;
+      }
+    }
+  }
+}
+
+// Nearest codeword per block (argmax of e . r' - ||e||^2/2; ties to the
+// lowest index), used for round-to-nearest and for the marginal MAP.
+__global__ __launch_bounds__(256) void nearest_lattice_kernel(const float* __restrict__ R, int64_t m, int64_t n,
+                                                              const uint32_t* __restrict__ keys, int Kpad,
+                                                              const float* __restrict__ a,
+                                                              const float* __restrict__ o,
+                                                              int32_t* __restrict__ codes) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds_key[2][LAT_KEY_WORDS];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int64_t B = n / 8;
+  const int64_t total = m * B;
+  const int64_t qbase = (int64_t)blockIdx.x * LAT_QWG + wave * LAT_QW;
+
+  v4u qop[LAT_QSUB];
+#pragma unroll
+  for (int q = 0; q < LAT_QSUB; ++q) {
+    QueryInfo qi = query_of(qbase + q * 16 + j, total, B);
+    float rp[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) rp[k] = 0.f;
+    if (qi.valid) {
+      float ai = a[qi.i], oi = o[qi.i];
+      const float* rr = R + qi.i * n + qi.b * 8;
+      float inva = 1.f / ai;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rp[k] = (rr[k] - oi) * inva;
+    }
+    qop[q] = make_query(rp, 1.f, 0.f, g);
+  }
+  float best[LAT_QSUB];
+  int bidx[LAT_QSUB];
+#pragma unroll
+  for (int q = 0; q < LAT_QSUB; ++q) { best[q] = -INFINITY; bidx[q] = 0x7fffffff; }
+
+  const int nchunks = Kpad / LAT_CH;
+  load_chunk<false>(lds_key[0], nullptr, keys, nullptr, 0, t);
+  __syncthreads();
+  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < nchunks; ++c) {
+    const int cur = c & 1;
+    if (c + 1 < nchunks) load_chunk<false>(lds_key[cur ^ 1], nullptr, keys, nullptr, c + 1, t);
+    const v4u* kq = reinterpret_cast<const v4u*>(lds_key[cur]);
+#pragma unroll 1
+    for (int st = 0; st < LAT_CH / 16; ++st) {
+      const v4u k0 = kq[st * 64 + lane];
+      const int cw0 = c * LAT_CH + st * 16 + 4 * g;
+#pragma unroll
+      for (int q = 0; q < LAT_QSUB; ++q) {
+        v4f s = mfma_bf16_16x16x32(k0, qop[q], zero4);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if (s[v] > best[q]) { best[q] = s[v]; bidx[q] = cw0 + v; }
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < LAT_QSUB; ++q) {
+    float bv = best[q];
+    int bi = bidx[q];
+#pragma unroll
+    for (int msk = 16; msk <= 32; msk <<= 1) {
+      float ov = shfl_xor_f(bv, msk);
+      int oi = shfl_xor_i(bi, msk);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    QueryInfo qi = query_of(qbase + q * 16 + j, total, B);
+    if (g == 0 && qi.valid) codes[qi.i * B + qi.b] = bi;
+  }
+}
+
+hipError_t launch_denoise_lattice(const float* R1, const float* gamma1, int64_t m, int64_t n, const CbTables& cb,
+                                  const float* a, const float* o, float* xhat, float* vblk, hipStream_t st) {
+  int64_t total = m * (n / 8);
+  if (total <= 0) return hipSuccess;
+  dim3 grid((unsigned)((total + LAT_QWG - 1) / LAT_QWG));
+  hipLaunchKernelGGL(denoise_lattice_kernel, grid, dim3(256), 0, st, R1, gamma1, m, n, cb.qk_keys, cb.pv_ops, cb.e32,
+                     cb.Kpad, a, o, xhat, vblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_nearest_lattice(const float* R, int64_t m, int64_t n, const CbTables& cb, const float* a,
+                                  const float* o, int32_t* codes, hipStream_t st) {
+  int64_t total = m * (n / 8);
+  if (total <= 0) return hipSuccess;
+  dim3 grid((unsigned)((total + LAT_QWG - 1) / LAT_QWG));
+  hipLaunchKernelGGL(nearest_lattice_kernel, grid, dim3(256), 0, st, R, m, n, cb.qk_keys, cb.Kpad, a, o, codes);
+  return hipGetLastError();
+}
+
+}  // namespace mpq

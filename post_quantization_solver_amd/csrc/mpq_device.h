@@ -1,0 +1,44 @@
+// Device-side helpers shared by the MPQ kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+#define MPQ_WAVE 64
+
+// float -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f2bf_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf_bits2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Split a float32 into three bfloat16 terms whose sum reproduces it to
+// about 2^-24 relative (each term rounds the remainder of the previous).
+__device__ __forceinline__ void split3_bf16(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
+  h = f2bf_bits(x);
+  float r1 = x - bf_bits2f(h);
+  m = f2bf_bits(r1);
+  float r2 = r1 - bf_bits2f(m);
+  l = f2bf_bits(r2);
+}
+
+__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return (lo16 & 0xffffu) | (hi16 << 16); }
+
+// Cross-lane helpers (full wave64).
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+__device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// MFMA wrappers.  16x16 output layout (all dtypes): lane l holds rows
+// 4*(l/16) + v (v = 0..3) of column l % 16.
+__device__ __forceinline__ v4f mfma_f32_16x16x4(float a, float b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(v4u a, v4u b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}

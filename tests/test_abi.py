@@ -1,0 +1,83 @@
+"""Host-side checks of the C ABI: the library loads, exports everything the
+header declares, sizes workspaces and rejects bad arguments before touching
+the GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import post_quantization_solver_amd as mpq
+import mpq_synth as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mpq.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mpq.LIB_PATH):
+        from post_quantization_solver_amd import build
+        build.build()
+    return mpq.load_library()
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mpq_\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(mpq.EXPORTS)
+    for nm in names:
+        assert hasattr(lib, nm), nm
+
+
+def test_workspace_sizes(lib):
+    assert mpq.workspace_bytes(64, 256, 256, 8, 1) > 0
+    big = mpq.workspace_bytes(4096, 14336, 14336, 65536, 8)
+    assert 2e9 < big < 8e9
+    assert mpq.workspace_bytes(4, 10, 11, 8, 1) == 0       # r > n
+    assert mpq.workspace_bytes(4, 12, 12, 8, 8) == 0       # n % d
+    assert mpq.workspace_bytes(4, 16, 16, 8, 3) == 0       # d unsupported
+    assert mpq.workspace_bytes(4, 16, 16, 65, 1) == 0      # K > 64 for scalar grids
+
+
+FAKE = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+
+
+def call_layer(lib, m=4, n=16, r=16, K=8, d=1, T=2, ncd=1, rho=0.5, cb=None, ws_bytes=1 << 30, W=FAKE, ws=FAKE):
+    E = np.arange(K * d, dtype=np.float32).reshape(K, d) if cb is None else cb
+    return lib.mpq_quantize_layer(W, m, n, FAKE, FAKE, r, E.ctypes.data_as(ctypes.c_void_p), K, d, FAKE, FAKE, T,
+                                  ncd, rho, None, FAKE, None, None, None, None, ws, ws_bytes, None)
+
+
+def test_argument_validation(lib):
+    assert call_layer(lib, T=-1) == -3
+    assert call_layer(lib, ncd=-2) == -3
+    assert call_layer(lib, rho=0.0) == -3
+    assert call_layer(lib, rho=1.5) == -3
+    assert call_layer(lib, rho=float("nan")) == -3
+    assert call_layer(lib, d=3, n=18, r=18) == -4
+    assert call_layer(lib, d=8, n=12, r=12) == -2
+    assert call_layer(lib, r=17) == -2
+    assert call_layer(lib, m=-1) == -2
+    assert call_layer(lib, W=None) == -1
+    assert call_layer(lib, m=0) == 0                       # nothing to do
+    # d = 8 codebook not exact in bfloat16
+    bad = S.e8_codebook(256) * np.float32(1.1)
+    assert call_layer(lib, d=8, K=256, cb=bad) == -4
+    # workspace too small or misaligned
+    good = S.e8_codebook(256)
+    assert call_layer(lib, d=8, K=256, cb=good, ws_bytes=1024) == -5
+    assert call_layer(lib, d=8, K=256, cb=good, ws=ctypes.c_void_p((1 << 20) + 4)) == -5
+    assert call_layer(lib, d=8, K=256, cb=good, ws=None) == -5
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.mpq_strerror(code).decode()
+    with pytest.raises(mpq.MPQError):
+        mpq.binding._check(-3, "x")

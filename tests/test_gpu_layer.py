@@ -1,0 +1,113 @@
+"""End-to-end parity of mpq_quantize_layer with the oracle on small layers
+(all rows), plus edge cases: ragged shapes, r < n, padded lattice codebooks,
+frozen rows, T_vamp = 0, n_cd = 0, m = 0, determinism."""
+import numpy as np
+import pytest
+
+import mpq_synth as S
+from oracle import mpq_oracle as O
+from parity_helpers import SOFT_RTOL, OBJ_RTOL, CODE_FRAC, dev, host, layer_tensors, compare_layer
+from oracle_pool import solve_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(L, T_vamp=None, n_cd=None):
+    import torch
+    import post_quantization_solver_amd as mpq
+    T = layer_tensors(L)
+    out = mpq.quantize_layer(T["W"], T["s"], T["V"], L.E, T["a"], T["o"],
+                             T_vamp=L.T_vamp if T_vamp is None else T_vamp,
+                             n_cd=L.n_cd if n_cd is None else n_cd, damping=L.damping)
+    torch.cuda.synchronize()
+    return {k: (host(v) if v is not None else None) for k, v in out.items()}
+
+
+CASES = {
+    "c1": lambda: S.make_config("c1"),
+    "ragged_scalar": lambda: S.make_layer("ragged_scalar", 37, 200, seed=21, d=1, bits=4, power=0.6, r=150, T_vamp=6),
+    "scalar_k2": lambda: S.make_layer("scalar_k2", 9, 40, seed=22, d=1, bits=1, power=0.5, T_vamp=5),
+    "scalar_k64": lambda: S.make_layer("scalar_k64", 9, 72, seed=23, d=1, bits=6, power=0.5, T_vamp=5),
+    "lattice_small": lambda: S.make_layer("lattice_small", 24, 136, seed=24, d=8, power=0.6, T_vamp=6),
+    "lattice_k1000_r": lambda: S.make_layer("lattice_k1000_r", 20, 64, seed=25, d=8, K=1000, power=0.5, r=60,
+                                            T_vamp=5),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layer_parity(name):
+    L = CASES[name]()
+    rows = np.arange(L.m)
+    print(f"[layer] {name} m={L.m} n={L.n} r={L.r} K={L.K} d={L.d} T={L.T_vamp}", flush=True)
+    gpu = run_gpu(L)
+    refs = solve_rows(L, rows)
+    summ = compare_layer(L, rows, gpu, refs)
+    print(f"  codes {summ['code_agreement']:.5f} rows-equal {summ['rows_codes_equal']}/{summ['n_rows']} "
+          f"obj {summ['obj_rel_max']:.2e} traces {summ['trace_rel_max']}", flush=True)
+    assert summ["code_agreement"] >= CODE_FRAC
+    assert summ["obj_rel_max"] < OBJ_RTOL
+    for key, v in summ["trace_rel_max"].items():
+        assert v < SOFT_RTOL, (key, v)
+
+
+def test_special_cases():
+    L = S.make_layer("sp", 12, 48, seed=31, d=1, bits=3, T_vamp=4)
+    rows = np.arange(L.m)
+    # T_vamp = 0: RTN then CD
+    g0 = run_gpu(L, T_vamp=0)
+    r0 = solve_rows(L, rows, T_vamp=0)
+    assert (g0["codes"] == np.stack([r["codes"] for r in r0])).mean() >= CODE_FRAC
+    # n_cd = 0: MAP codes
+    g1 = run_gpu(L, n_cd=0)
+    r1 = solve_rows(L, rows, n_cd=0)
+    assert (g1["codes"] == np.stack([r["map_codes"] for r in r1])).mean() >= CODE_FRAC
+    assert g1["cd_changes"] is None
+
+
+def test_frozen_rows_and_empty():
+    import torch
+    import post_quantization_solver_amd as mpq
+    L = S.make_layer("fz", 6, 32, seed=32, d=1, bits=3, T_vamp=4)
+    W = L.W.copy()
+    # row 2 exactly on a grid with an exactly representable scale and offset
+    a = L.a.copy()
+    o = L.o.copy()
+    a[2], o[2] = 0.25, -1.0
+    W[2] = (np.arange(32) % 8) * 0.25 - 1.0
+    L2 = S.Layer("fz", W, L.s, L.V, L.E, a, o, 1, 4, 3, 0.5)
+    g = run_gpu(L2)
+    assert np.all(g["codes"][2] == np.arange(32) % 8)
+    assert np.all(np.isinf(g["beta_tr"][2])) and np.all(np.isinf(g["gamma1_tr"][2]))
+    assert np.all(g["cd_changes"][2] == 0)
+    assert np.all(np.isfinite(g["beta_tr"][[0, 1, 3, 4, 5]]))
+    ref = solve_rows(L2, [2])[0]
+    assert ref["frozen"] and list(ref["codes"]) == list(g["codes"][2])
+    # m = 0 is a no-op
+    T = layer_tensors(L2)
+    out = mpq.quantize_layer(T["W"][:0], T["s"], T["V"], L.E, T["a"][:0], T["o"][:0], T_vamp=2, n_cd=1)
+    assert out["codes"].shape == (0, 32)
+
+
+def test_deterministic_and_row_independent():
+    L = S.make_layer("det", 16, 64, seed=33, d=8, K=4096, power=0.6, T_vamp=4)
+    g1 = run_gpu(L)
+    g2 = run_gpu(L)
+    for k in ("codes", "beta_tr", "gamma1_tr", "gamma2_tr", "cd_changes"):
+        assert np.array_equal(g1[k], g2[k]), k
+    # solving a permuted batch permutes the outputs bitwise
+    perm = np.random.default_rng(0).permutation(L.m)
+    Lp = S.Layer("perm", L.W[perm], L.s, L.V, L.E, L.a[perm], L.o[perm], L.d, L.T_vamp, L.n_cd, L.damping)
+    gp = run_gpu(Lp)
+    for k in ("codes", "beta_tr", "gamma1_tr"):
+        assert np.array_equal(gp[k], g1[k][perm]), k
+
+
+def test_scale_metamorphic():
+    """W and codebook scale x4: identical codes; beta and gamma scale by 1/16."""
+    L = S.make_layer("scl", 16, 96, seed=34, d=1, bits=3, T_vamp=6)
+    Ls = S.Layer("scl4", L.W * 4, L.s, L.V, L.E, L.a * 4, L.o * 4, 1, 6, 3, 0.5)
+    g = run_gpu(L)
+    gs = run_gpu(Ls)
+    assert np.array_equal(g["codes"], gs["codes"])
+    assert np.allclose(gs["beta_tr"], g["beta_tr"] / 16, rtol=1e-5)
+    assert np.allclose(gs["gamma1_tr"], g["gamma1_tr"] / 16, rtol=1e-5)

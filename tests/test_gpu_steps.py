@@ -1,0 +1,158 @@
+"""Teacher-forced parity of each stage of the solve: the GPU runs one stage on
+the oracle's own state and its outputs are compared with the oracle's.
+
+Tolerances: soft quantities 1e-4 relative (per row vector, per scalar), codes
+>= 99.9 % of blocks, objectives 1e-5 relative.
+"""
+import numpy as np
+import pytest
+
+import mpq_synth as S
+from oracle import mpq_oracle as O
+from parity_helpers import SOFT_RTOL, OBJ_RTOL, CODE_FRAC, dev, host, layer_tensors, rel_vec, rel_scalar
+from oracle_pool import solve_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def layers():
+    return {
+        "scalar3": S.make_config("c1"),
+        "ragged4": S.make_layer("ragged4", 37, 200, seed=11, d=1, bits=4, power=0.6, r=150, T_vamp=5),
+        "lattice": S.make_layer("lattice", 24, 136, seed=12, d=8, power=0.6, T_vamp=4),
+        "lattice_k1000": S.make_layer("lattice_k1000", 20, 64, seed=13, d=8, K=1000, power=0.5, r=60, T_vamp=4),
+    }
+
+
+_CACHE = {}
+
+
+def oracle_runs(name):
+    if name not in _CACHE:
+        L = layers()[name]
+        rows = np.arange(L.m)
+        _CACHE[name] = (L, rows, solve_rows(L, rows, record=True))
+    return _CACHE[name]
+
+
+NAMES = ["scalar3", "ragged4", "lattice", "lattice_k1000"]
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_prologue(name):
+    import post_quantization_solver_amd as mpq
+    L, rows, refs = oracle_runs(name)
+    T = layer_tensors(L)
+    print(f"[prologue] {name} m={L.m} n={L.n} r={L.r} K={L.K} d={L.d}", flush=True)
+    out = mpq.prologue(T["W"], T["s"], T["V"], L.E, T["a"], T["o"])
+    ytil = host(out["ytil"])
+    rtn = host(out["rtn_codes"])
+    g1 = host(out["gamma1"])
+    b0 = host(out["beta"])
+    worst_y = max(rel_vec(ytil[i], O.rank_target(L.W[i], L.s, L.V)) for i in rows)
+    agree = float(np.mean([np.mean(rtn[i] == refs[k]["rtn_codes"]) for k, i in enumerate(rows)]))
+    wg = max(rel_scalar(g1[i], refs[k]["gamma1_tr"][0]) for k, i in enumerate(rows))
+    wb = max(rel_scalar(b0[i], refs[k]["beta_tr"][0]) for k, i in enumerate(rows))
+    print(f"  ytil {worst_y:.2e} rtn agree {agree:.5f} gamma1 {wg:.2e} beta {wb:.2e}", flush=True)
+    assert worst_y < 1e-5
+    assert agree >= CODE_FRAC
+    assert wg < SOFT_RTOL and wb < SOFT_RTOL
+
+
+@pytest.mark.parametrize("name", NAMES)
+@pytest.mark.parametrize("t", [0, 2])
+def test_denoise(name, t):
+    import post_quantization_solver_amd as mpq
+    L, rows, refs = oracle_runs(name)
+    T = layer_tensors(L)
+    R1 = np.stack([r["history"][t]["r1"] for r in refs]).astype(np.float32)
+    g1 = np.array([r["history"][t]["gamma1"] for r in refs], dtype=np.float32)
+    print(f"[denoise] {name} t={t}", flush=True)
+    xh, vt = mpq.denoise(dev(R1), dev(g1), L.E, T["a"], T["o"])
+    xh, vt = host(xh), host(vt)
+    wx, wv = 0.0, 0.0
+    for k, i in enumerate(rows):
+        C = O.row_codewords(L.E, L.a[i], L.o[i])
+        xr, vr, _ = O.denoise(R1[k].astype(np.float64), float(g1[k]), C, L.d)
+        wx = max(wx, rel_vec(xh[k], xr))
+        wv = max(wv, rel_scalar(vt[k].astype(np.float64).sum(), vr.sum()))
+    print(f"  xhat1 {wx:.2e}  sum v {wv:.2e}", flush=True)
+    assert wx < SOFT_RTOL and wv < SOFT_RTOL
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_vamp_step(name):
+    import post_quantization_solver_amd as mpq
+    L, rows, refs = oracle_runs(name)
+    T = layer_tensors(L)
+    ytil = np.stack([O.rank_target(L.W[i], L.s, L.V) for i in rows]).astype(np.float32)
+    worst = {}
+    for t in range(L.T_vamp):
+        h = [r["history"][t] for r in refs]
+        R1 = dev(np.stack([x["r1"] for x in h]).astype(np.float32))
+        g1 = dev(np.array([x["gamma1"] for x in h], dtype=np.float32))
+        bt = dev(np.array([x["beta"] for x in h], dtype=np.float32))
+        print(f"[vamp_step] {name} t={t}", flush=True)
+        out = mpq.vamp_step(R1, g1, bt, dev(ytil), T["s"], T["V"], L.E, T["a"], T["o"], damping=L.damping)
+        r1n, g1n, btn = host(R1), host(g1), host(bt)
+        eta1, g2, fb = host(out["eta1"]), host(out["gamma2"]), host(out["fallback"])
+        xh, r2 = host(out["xhat1"]), host(out["r2"])
+        for k in range(len(rows)):
+            nxt = refs[k]["history"][t + 1] if t + 1 < L.T_vamp else None
+            r1_ref = nxt["r1"] if nxt else refs[k]["r1_final"]
+            g1_ref = refs[k]["gamma1_tr"][t + 1]
+            b_ref = refs[k]["beta_tr"][t + 1]
+            # gamma2 = eta1 - gamma1 and r2 (which divides by gamma2) are
+            # compared relative to the subtraction's operands: errors scaled
+            # by cond = eta1 / gamma2 (1 when the posterior is passed through)
+            cond = max(1.0, h[k]["eta1"] / h[k]["gamma2"])
+            errs = dict(xhat1=rel_vec(xh[k], h[k]["xhat1"]), eta1=rel_scalar(eta1[k], h[k]["eta1"]),
+                        gamma2=rel_scalar(g2[k], h[k]["gamma2"]) / cond, r2=rel_vec(r2[k], h[k]["r2"]) / cond,
+                        gamma2_raw=rel_scalar(g2[k], h[k]["gamma2"]), r2_raw=rel_vec(r2[k], h[k]["r2"]),
+                        r1=rel_vec(r1n[k], r1_ref), gamma1=rel_scalar(g1n[k], g1_ref), beta=rel_scalar(btn[k], b_ref),
+                        fallback=float(bool(fb[k]) != bool(h[k]["fell_back"])))
+            for key, v in errs.items():
+                worst[key] = max(worst.get(key, 0.0), v)
+    print("  worst:", {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
+    assert worst["fallback"] == 0.0
+    for key in ("xhat1", "eta1", "gamma2", "r2", "r1", "gamma1", "beta"):
+        assert worst[key] < SOFT_RTOL, (key, worst[key])
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_map(name):
+    import post_quantization_solver_amd as mpq
+    L, rows, refs = oracle_runs(name)
+    T = layer_tensors(L)
+    R1 = np.stack([r["r1_final"] for r in refs]).astype(np.float32)
+    g1 = np.array([r["gamma1_tr"][-1] for r in refs], dtype=np.float32)
+    codes = host(mpq.map_codes(dev(R1), dev(g1), L.E, T["a"], T["o"]))
+    ref = np.stack([O.map_codes(R1[k].astype(np.float64), float(g1[k]), O.row_codewords(L.E, L.a[i], L.o[i]), L.d)
+                    for k, i in enumerate(rows)])
+    agree = float((codes == ref).mean())
+    print(f"[map] {name} agreement {agree:.5f}", flush=True)
+    assert agree >= CODE_FRAC
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_cd(name):
+    import torch
+    import post_quantization_solver_amd as mpq
+    L, rows, refs = oracle_runs(name)
+    T = layer_tensors(L)
+    start = np.stack([r["map_codes"] for r in refs]).astype(np.int32)
+    codes = dev(start)
+    codes, ch = mpq.cd(T["W"], T["s"], T["V"], L.E, T["a"], T["o"], codes, n_cd=L.n_cd)
+    torch.cuda.synchronize()
+    codes, ch = host(codes), host(ch)
+    ref = np.stack([r["codes"] for r in refs])
+    agree = float((codes == ref).mean())
+    f_gpu = np.array([O.codes_objective(L.W[i], codes[k], O.row_codewords(L.E, L.a[i], L.o[i]), L.d, L.s, L.V)
+                      for k, i in enumerate(rows)])
+    f_ref = np.array([r["objective"] for r in refs])
+    obj = float(np.max(np.abs(f_gpu - f_ref) / f_ref))
+    ch_ref = np.array([r["cd_changes"] for r in refs])
+    print(f"[cd] {name} agreement {agree:.5f} objective {obj:.2e} changes gpu {ch.sum(0)} ref {ch_ref.sum(0)}",
+          flush=True)
+    assert agree >= CODE_FRAC
+    assert obj < OBJ_RTOL
