@@ -1,0 +1,180 @@
+"""Benchmark: one MPQ layer solve per step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config c5] [--cpu-rows R | --no-cpu]
+
+A step is one full mpq_quantize_layer call (prologue, T_vamp VAMP
+iterations, marginal MAP, 3 CD sweeps) on a seeded synthetic layer whose
+inputs are already resident in HBM.  The default workload is the 2-bit E8
+lattice layer 4096 x 14336 (Llama-3-8B MLP-down shape), T_vamp = 16.
+
+Prints ONE JSON line: throughput in weights quantized per second, the
+roofline of the dominant kernel (timed with HIP events on the library's
+stream inside the timed region) and the float64 oracle's throughput on a
+bounded sample of rows of the same layer, run on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "weights quantized/sec per layer (T_vamp=16 + 3 CD sweeps), % of MFMA/HBM peak"
+
+# MI355X published peaks
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+# Transcendental issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz at a
+# quarter of the fp32 VALU rate -> 9.83e12 exp/s.
+EXP_RATE = 256 * 4 * 16 * 2.4e9 / 4
+LATTICE_FLOP_PER_EVAL = 36     # 2*8 (distance contraction) + 2*10 (weighted moments)
+SCALAR_FLOP_PER_EVAL = 8       # distance, scaled logit, three moment updates
+
+WORKLOADS = {
+    "c1": "3-bit scalar toy layer 64x256, T_vamp=8, 3 CD sweeps",
+    "c2": "3-bit scalar Llama-3.2-1B attention projection 2048x2048 (Laplace + 1% outlier columns), T_vamp=16, 3 CD",
+    "c3": "4-bit scalar Llama-3.2-1B MLP-down 2048x8192, T_vamp=16, 3 CD",
+    "c4": "2-bit E8 lattice Llama-3-8B attention projection 4096x4096, T_vamp=16, 3 CD",
+    "c5": "2-bit E8 lattice Llama-3-8B MLP-down 4096x14336 (Student-t rows), T_vamp=16, 3 CD",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def dominant_roofline(L, prof, steps):
+    """Roofline entry for the kernel group with the largest time."""
+    m, n, r, K, d = L.m, L.n, L.r, L.K, L.d
+    best = max(prof, key=lambda k: prof[k][0])
+    ms, launches = prof[best]
+    per_launch_s = ms / max(launches, 1) / 1e3
+    if best == "denoise":
+        evals = m * (n // d) * K
+        if d == 8:
+            flops = evals * LATTICE_FLOP_PER_EVAL
+            peak = LATTICE_FLOP_PER_EVAL * EXP_RATE / 1e12
+        else:
+            flops = evals * SCALAR_FLOP_PER_EVAL
+            peak = SCALAR_FLOP_PER_EVAL * EXP_RATE / 1e12
+        achieved = flops / per_launch_s / 1e12
+        return dict(kernel="denoise", bound="alu", achieved=achieved, peak=peak, unit="TFLOP/s",
+                    frac=achieved / peak, traffic=None, launches=launches, avg_ms=ms / max(launches, 1))
+    if best in ("linear1", "linear2"):
+        flops = 2.0 * m * n * r
+        achieved = flops / per_launch_s / 1e12
+        return dict(kernel=best, bound="mfma", achieved=achieved, peak=PEAK_FP32_MFMA_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / PEAK_FP32_MFMA_TFLOPS, traffic=None, launches=launches,
+                    avg_ms=ms / max(launches, 1))
+    return dict(kernel=best, bound="alu", achieved=None, peak=None, unit="TFLOP/s", frac=None, traffic=None,
+                launches=launches, avg_ms=ms / max(launches, 1))
+
+
+def cpu_baseline(L, rows_count, gpu_codes):
+    """Time the float64 oracle on `rows_count` rows of the layer, one worker
+    process per row (each solves its row through the whole pipeline)."""
+    import numpy as np
+    import mpq_synth as S
+    from oracle import mpq_oracle as O
+    from oracle.pool import solve_rows
+    rows = S.parity_rows(L.m, rows_count)
+    t0 = time.perf_counter()
+    res = solve_rows(L, rows, max_workers=len(rows))
+    wall = time.perf_counter() - t0
+    agree = float(np.mean([np.mean(gpu_codes[i] == r["codes"]) for i, r in zip(rows, res)]))
+    obj_rel = max(abs(O.codes_objective(L.W[i], gpu_codes[i], O.row_codewords(L.E, L.a[i], L.o[i]), L.d, L.s, L.V)
+                      - r["objective"]) / r["objective"] for i, r in zip(rows, res))
+    value = len(rows) * L.n / wall
+    return dict(value=value, unit="weights/s", cores=len(rows), kind="oracle",
+                sample=f"{len(rows)} rows (every {max(L.m // len(rows), 1)}-th) of the same layer through the "
+                       f"whole pipeline, one single-threaded float64 NumPy worker per row; wall {wall:.1f} s",
+                parity=dict(rows=len(rows), code_agreement=agree, obj_rel_max=obj_rel))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="c5", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-rows", type=int, default=0, help="oracle rows for the CPU baseline (0: host cores, <=16)")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the MPQ layer solve is single-GPU here "
+              "(rows would shard across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mpq_synth as S
+    import post_quantization_solver_amd as mpq
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    mpq.load_library()
+    t0 = time.perf_counter()
+    L = S.make_config(args.config, device=dev)
+    log(f"[bench] {args.config}: m={L.m} n={L.n} r={L.r} K={L.K} d={L.d} T={L.T_vamp} S={L.n_cd} "
+        f"inputs in {time.perf_counter() - t0:.1f} s")
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
+    W, s, V, a, o = t(L.W), t(L.s), t(L.V), t(L.a), t(L.o)
+    ws = torch.empty(mpq.workspace_bytes(L.m, L.n, L.r, L.K, L.d), dtype=torch.uint8, device=dev)
+    kw = dict(T_vamp=L.T_vamp, n_cd=L.n_cd, damping=L.damping, workspace=ws)
+    out = None
+    for k in range(args.warmup):
+        out = mpq.quantize_layer(W, s, V, L.E, a, o, outputs=out, **kw)
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {k + 1}/{args.warmup} done")
+
+    # timed region: K steps; the dominant kernel groups are event-timed on the library's stream
+    prof = mpq.Profile(("denoise", "linear1", "linear2", "cd_search", "cd_gemm"))
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        out = mpq.quantize_layer(W, s, V, L.E, a, o, outputs=out, profile=prof, **kw)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = L.m * L.n / (ms_per_step / 1e3)
+    timed_prof = prof.as_dict()
+    log(f"[bench] {args.steps} steps: {ms_per_step:.1f} ms/step, {value / 1e6:.3f} M weights/s")
+
+    # one extra profiled step with every kernel group for the time split
+    full = mpq.Profile()
+    out = mpq.quantize_layer(W, s, V, L.E, a, o, outputs=out, profile=full, **kw)
+    torch.cuda.synchronize()
+    split = {k: round(v[0], 3) for k, v in full.as_dict().items()}
+    log(f"[bench] kernel ms per step: {split}")
+    roof = dominant_roofline(L, {k: v for k, v in timed_prof.items() if k in ("denoise", "linear1", "linear2")},
+                             args.steps)
+    codes = out["codes"].cpu().numpy()
+
+    cpu = None
+    if not args.no_cpu:
+        rows = args.cpu_rows or max(1, min(16, os.cpu_count() or 1))
+        log(f"[bench] oracle baseline on {rows} rows ...")
+        cpu = cpu_baseline(L, rows, codes)
+        log(f"[bench] oracle {cpu['value']:.1f} weights/s; parity on its rows {cpu['parity']}")
+
+    line = dict(metric=METRIC, value=value, unit="weights/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+                ms_per_step=ms_per_step, higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
+                data="synthetic",
+                config=dict(workload=f"{args.config}: {WORKLOADS[args.config]}", m=L.m, n=L.n, r=L.r, K=L.K,
+                            d=L.d, T_vamp=L.T_vamp, n_cd=L.n_cd, damping=L.damping),
+                roofline=dict(bound=roof["bound"], achieved=roof["achieved"], peak=roof["peak"], unit=roof["unit"],
+                              frac=roof["frac"], traffic=roof["traffic"], kernel=roof["kernel"],
+                              avg_launch_ms=roof["avg_ms"], launches=roof["launches"]),
+                kernel_ms_per_step=split, cpu_baseline=cpu)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

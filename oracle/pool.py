@@ -1,0 +1,80 @@
+"""Run the float64 oracle over many rows in worker processes.
+
+TEST INFRASTRUCTURE ONLY (used by tests/ and by bench.py's CPU-baseline leg).
+Workers are started with the 'spawn' method, import only numpy and the
+oracle, and never touch the GPU.  Layer arrays are written once to .npy files
+and memory-mapped by every worker, so large factors are not pickled per job;
+each worker promotes them to float64 once.  BLAS runs single-threaded in each
+worker.
+"""
+from __future__ import annotations
+
+import multiprocessing as mp
+import os
+import shutil
+import sys
+import tempfile
+from concurrent.futures import ProcessPoolExecutor
+
+import numpy as np
+
+_ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+_CACHE = {}
+_THREAD_VARS = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+
+
+def _load(path):
+    if path not in _CACHE:
+        _CACHE.clear()
+        arrs = {k: np.load(os.path.join(path, k + ".npy"), mmap_mode="r") for k in ("W", "s", "V", "E", "a", "o")}
+        _CACHE[path] = dict(W=arrs["W"], a=arrs["a"], o=arrs["o"], s=np.asarray(arrs["s"], np.float64),
+                            V=np.asarray(arrs["V"], np.float64), E=np.asarray(arrs["E"]))
+    return _CACHE[path]
+
+
+def _solve(job):
+    if _ROOT not in sys.path:
+        sys.path.insert(0, _ROOT)
+    from oracle import mpq_oracle as O
+    path, i, d, T, S, rho, record = job
+    A = _load(path)
+    w = np.asarray(A["W"][i], np.float64)
+    a, o = float(A["a"][i]), float(A["o"][i])
+    res = O.solve_row(w, A["s"], A["V"], A["E"], a, o, d, T, S, rho, record=record)
+    C = O.row_codewords(A["E"], a, o)
+    res["map_objective"] = O.codes_objective(w, res["map_codes"], C, d, A["s"], A["V"])
+    res["rtn_objective"] = O.codes_objective(w, res["rtn_codes"], C, d, A["s"], A["V"])
+    res["row"] = int(i)
+    return res
+
+
+def default_workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def solve_rows(L, rows, T_vamp=None, n_cd=None, record=False, max_workers=None):
+    """Oracle results for the given rows of a layer (attributes W, s, V, E, a,
+    o, d, T_vamp, n_cd, damping), in row order."""
+    T = L.T_vamp if T_vamp is None else T_vamp
+    S = L.n_cd if n_cd is None else n_cd
+    rows = [int(i) for i in rows]
+    tmp = tempfile.mkdtemp(prefix="mpq_oracle_")
+    try:
+        for k in ("W", "s", "V", "E", "a", "o"):
+            np.save(os.path.join(tmp, k + ".npy"), np.ascontiguousarray(getattr(L, k)))
+        jobs = [(tmp, i, L.d, T, S, L.damping, record) for i in rows]
+        nw = min(max_workers or default_workers(), len(jobs))
+        saved = {k: os.environ.get(k) for k in _THREAD_VARS}
+        for k in _THREAD_VARS:
+            os.environ[k] = "1"
+        try:
+            with ProcessPoolExecutor(max_workers=max(nw, 1), mp_context=mp.get_context("spawn")) as ex:
+                return list(ex.map(_solve, jobs))
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)

@@ -21,6 +21,9 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
     # packed fp32 VALU forms stay off on this target
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA sources/results in ordinary VGPRs: no accumulator-register copies
+    # between the matrix cores and the VALU work that consumes their results
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -19,7 +19,7 @@ hipError_t launch_denoise_scalar(const float*, const float*, int64_t, int64_t, c
 hipError_t launch_nearest_scalar(const float*, int64_t, int64_t, const CbTables&, const float*, const float*,
                                  int32_t*, hipStream_t);
 hipError_t launch_denoise_lattice(const float*, const float*, int64_t, int64_t, const CbTables&, const float*,
-                                  const float*, float*, float*, hipStream_t);
+                                  const float*, float*, float*, int32_t*, hipStream_t);
 hipError_t launch_nearest_lattice(const float*, int64_t, int64_t, const CbTables&, const float*, const float*,
                                   int32_t*, hipStream_t);
 hipError_t launch_beta_lin(int64_t, const float*, const float*, float*, float*, hipStream_t);
@@ -73,7 +73,7 @@ struct Layout {
 
 enum Region {
   R_VS, R_VST, R_YTIL, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI,
-  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_COUNT
+  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_COUNT
 };
 
 size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -109,6 +109,7 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
   sz[R_QK] = d == 8 ? (size_t)L.Kpad * 16 * sizeof(uint32_t) : 0;
   sz[R_PV] = d == 8 ? (size_t)L.Kpad * 8 * sizeof(uint32_t) : 0;
   sz[R_E32] = (size_t)(d == 8 ? L.Kpad : 64) * 8 * f;
+  sz[R_FLAG] = d == 8 ? (size_t)(64 + m * L.B) * sizeof(int32_t) : 0;
   size_t o = 0;
   for (int k = 0; k < R_COUNT; ++k) {
     L.off[k] = o;
@@ -215,6 +216,7 @@ int check_shapes(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
   if (d == 1 && (K < 2 || K > 64)) return MPQ_ESHAPE;
   if (d == 8 && (K < 1 || K > 65536)) return MPQ_ESHAPE;
   if (m > ((int64_t)1 << 23) || n > ((int64_t)1 << 20)) return MPQ_ESHAPE;
+  if (m * (n / d) > (int64_t)0x7fffff00) return MPQ_ESHAPE;   // block indices fit int32
   return MPQ_OK;
 }
 
@@ -324,7 +326,7 @@ hipError_t nearest(const Ctx& c, const float* R, int32_t* codes, const float* a,
 hipError_t denoise(const Ctx& c, const float* R1, const float* gamma1, const float* a, const float* o, float* xhat,
                    float* vblk) {
   if (c.L.d == 1) return launch_denoise_scalar(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.st);
-  return launch_denoise_lattice(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.st);
+  return launch_denoise_lattice(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.pi(R_FLAG), c.st);
 }
 
 int prepare_factors(Ctx& c, const float* V, const float* s) {

@@ -25,6 +25,8 @@
 
 namespace mpq {
 
+hipError_t launch_fill_i32(int32_t* dst, int64_t count, int32_t v, hipStream_t st);
+
 constexpr int LAT_WAVES = 4;
 constexpr int LAT_QSUB = 4;                      // 16-query subtiles per wave
 constexpr int LAT_QW = 16 * LAT_QSUB;            // queries per wave
@@ -99,14 +101,27 @@ __device__ __forceinline__ void split_p(float p0, float p1, uint32_t& hw, uint32
   hw = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
   float l0 = p0 - __uint_as_float(b0 & 0xffff0000u);
   float l1 = p1 - __uint_as_float(b1 & 0xffff0000u);
-  lw = pack2(f2bf_bits(l0), f2bf_bits(l1));
+  lw = f2bf_pack(l0, l1);
 }
 
+// Two variants share this body.
+//  FAST (ONLINE = false): every query of the grid, with the fixed shift
+//    M = k' ||r'||^2 / 2, an upper bound of k' (e . r' - h) for ANY codebook
+//    (equality iff e = r'), so S'(e) = -k' ||e - r'||^2 / 2 <= 0 and no
+//    running maximum is needed.  A query whose total weight sum_p falls
+//    below 2^-90 (every codeword far away: its weights would lose precision
+//    in the float32 subnormal range) is appended to `flag_list` instead of
+//    being written.
+//  ONLINE (ONLINE = true): the queries listed in flag_list, with the lazy
+//    online maximum described above; exact for any query.
+// Each query's result depends only on its own inputs, so the order of the
+// list does not change any output bit.
+template <bool ONLINE>
 __global__ __launch_bounds__(256) void denoise_lattice_kernel(
     const float* __restrict__ R1, const float* __restrict__ gamma1, int64_t m, int64_t n,
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ pvops, const float* __restrict__ e32,
     int Kpad, const float* __restrict__ a, const float* __restrict__ o, float* __restrict__ xhat,
-    float* __restrict__ vblk) {
+    float* __restrict__ vblk, int32_t* __restrict__ flag_list, int32_t* __restrict__ flag_count) {
   __shared__ __attribute__((aligned(16))) uint32_t lds_key[2][LAT_KEY_WORDS];
   __shared__ __attribute__((aligned(16))) uint32_t lds_pv[2][LAT_PV_WORDS];
   __shared__ float fin[LAT_QWG][13];
@@ -117,17 +132,33 @@ __global__ __launch_bounds__(256) void denoise_lattice_kernel(
   const int j = lane & 15;
   const int g = lane >> 4;
   const int64_t B = n / 8;
-  const int64_t total = m * B;
+  const int64_t total = ONLINE ? (int64_t)(*flag_count) : m * B;
+  if ((int64_t)blockIdx.x * LAT_QWG >= total) return;   // uniform per workgroup
   const int64_t qbase = (int64_t)blockIdx.x * LAT_QWG + wave * LAT_QW;
+
+  // query index -> (row, block); ONLINE reads it from the flag list
+  auto resolve = [&](int64_t slot) -> QueryInfo {
+    if (!ONLINE) return query_of(slot, total, B);
+    QueryInfo qi;
+    qi.valid = slot < total;
+    int64_t Q = qi.valid ? (int64_t)flag_list[slot] : 0;
+    qi.i = Q / B;
+    qi.b = Q - qi.i * B;
+    return qi;
+  };
 
   // ---- per-query setup (each of the 4 lanes of a query computes the same values)
   v4u qop[LAT_QSUB];
-  float kap[LAT_QSUB], Mq[LAT_QSUB], qv[LAT_QSUB][8];
-  const float h0 = 0.5f * (e32[0] * e32[0] + e32[1] * e32[1] + e32[2] * e32[2] + e32[3] * e32[3] +
-                           e32[4] * e32[4] + e32[5] * e32[5] + e32[6] * e32[6] + e32[7] * e32[7]);
+  float kap[LAT_QSUB], Mq[LAT_QSUB], qv[ONLINE ? LAT_QSUB : 1][8];
+  float h0 = 0.f;
+  if (ONLINE) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) h0 = fmaf(e32[k], e32[k], h0);
+    h0 *= 0.5f;
+  }
 #pragma unroll
   for (int q = 0; q < LAT_QSUB; ++q) {
-    QueryInfo qi = query_of(qbase + q * 16 + j, total, B);
+    QueryInfo qi = resolve(qbase + q * 16 + j);
     float k2 = 0.f;
     float rp[8];
 #pragma unroll
@@ -143,15 +174,29 @@ __global__ __launch_bounds__(256) void denoise_lattice_kernel(
         k2 = gm * ai * ai * LOG2E;
       }
     }
-    // initial shift: the score of codeword 0, a lower bound of the maximum
-    float s0 = -h0;
+    float sref;
+    if (ONLINE) {
+      // initial shift: the score of codeword 0, a lower bound of the maximum
+      sref = -h0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) s0 = fmaf(e32[k], rp[k], s0);
+      for (int k = 0; k < 8; ++k) sref = fmaf(e32[k], rp[k], sref);
+    } else {
+      // ||r'||^2 / 2, the upper bound of e . r' - ||e||^2 / 2
+      sref = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sref = fmaf(rp[k], rp[k], sref);
+      sref *= 0.5f;
+    }
     kap[q] = k2;
-    Mq[q] = k2 * s0;
+    Mq[q] = k2 * sref;
+    float qq[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) qv[q][k] = k2 * rp[k];
-    qop[q] = make_query(qv[q], k2, Mq[q], g);
+    for (int k = 0; k < 8; ++k) qq[k] = k2 * rp[k];
+    if (ONLINE) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qv[ONLINE ? q : 0][k] = qq[k];
+    }
+    qop[q] = make_query(qq, k2, Mq[q], g);
   }
 
   // acc: this chunk's sums (the MFMAs accumulate at most 2 * LAT_CH / 32
@@ -182,21 +227,23 @@ __global__ __launch_bounds__(256) void denoise_lattice_kernel(
       for (int q = 0; q < LAT_QSUB; ++q) {
         v4f s0 = mfma_bf16_16x16x32(k0, qop[q], zero4);
         v4f s1 = mfma_bf16_16x16x32(k1, qop[q], zero4);
-        float lm = max8(s0, s1);
-        if (__builtin_amdgcn_ballot_w64(lm > LAT_SLACK)) {
-          // move the shift of every query whose scores exceed the window
-          float mx = fmaxf(lm, shfl_xor_f(lm, 16));
-          mx = fmaxf(mx, shfl_xor_f(mx, 32));
-          float dM = mx > LAT_SLACK ? mx : 0.f;
-          if (dM > 0.f) {
-            Mq[q] += dM;
-            float f = __builtin_amdgcn_exp2f(-dM);
-            acc[q] *= f;
-            tot[q] *= f;
+        if (ONLINE) {
+          float lm = max8(s0, s1);
+          if (__builtin_amdgcn_ballot_w64(lm > LAT_SLACK)) {
+            // move the shift of every query whose scores exceed the window
+            float mx = fmaxf(lm, shfl_xor_f(lm, 16));
+            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            float dM = mx > LAT_SLACK ? mx : 0.f;
+            if (dM > 0.f) {
+              Mq[q] += dM;
+              float f = __builtin_amdgcn_exp2f(-dM);
+              acc[q] *= f;
+              tot[q] *= f;
+            }
+            qop[q] = make_query(qv[ONLINE ? q : 0], kap[q], Mq[q], g);
+            s0 = mfma_bf16_16x16x32(k0, qop[q], zero4);
+            s1 = mfma_bf16_16x16x32(k1, qop[q], zero4);
           }
-          qop[q] = make_query(qv[q], kap[q], Mq[q], g);
-          s0 = mfma_bf16_16x16x32(k0, qop[q], zero4);
-          s1 = mfma_bf16_16x16x32(k1, qop[q], zero4);
         }
         float p[8];
 #pragma unroll
@@ -204,13 +251,13 @@ __global__ __launch_bounds__(256) void denoise_lattice_kernel(
           p[v] = __builtin_amdgcn_exp2f(s0[v]);
           p[4 + v] = __builtin_amdgcn_exp2f(s1[v]);
         }
-        uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-        split_p(p[0], p[1], h0, l0);
-        split_p(p[2], p[3], h1, l1);
-        split_p(p[4], p[5], h2, l2);
-        split_p(p[6], p[7], h3, l3);
-        v4u hi = {h0, h1, h2, h3};
-        v4u lo = {l0, l1, l2, l3};
+        uint32_t h0w, h1w, h2w, h3w, l0w, l1w, l2w, l3w;
+        split_p(p[0], p[1], h0w, l0w);
+        split_p(p[2], p[3], h1w, l1w);
+        split_p(p[4], p[5], h2w, l2w);
+        split_p(p[6], p[7], h3w, l3w);
+        v4u hi = {h0w, h1w, h2w, h3w};
+        v4u lo = {l0w, l1w, l2w, l3w};
         acc[q] = mfma_bf16_16x16x32(pv, hi, acc[q]);
         acc[q] = mfma_bf16_16x16x32(pv, lo, acc[q]);
       }
@@ -236,19 +283,22 @@ __global__ __launch_bounds__(256) void denoise_lattice_kernel(
   __syncthreads();
   {
     const int ql = t;  // one thread per query of the workgroup
-    const int64_t Q = (int64_t)blockIdx.x * LAT_QWG + ql;
-    QueryInfo qi = query_of(Q, total, B);
+    const int64_t slot = (int64_t)blockIdx.x * LAT_QWG + ql;
+    QueryInfo qi = resolve(slot);
     if (qi.valid) {
       float gm = gamma1[qi.i];
       float* xo = xhat + qi.i * n + qi.b * 8;
+      float z = fin[ql][11];
       if (!isfinite(gm)) {
         const float* rr = R1 + qi.i * n + qi.b * 8;
 #pragma unroll
         for (int k = 0; k < 8; ++k) xo[k] = rr[k];
         vblk[qi.i * B + qi.b] = 0.f;
+      } else if (!ONLINE && !(z >= 0x1p-90f)) {
+        int pos = atomicAdd(flag_count, 1);
+        flag_list[pos] = (int32_t)slot;
       } else {
         float ai = a[qi.i], oi = o[qi.i];
-        float z = fin[ql][11];
         float invz = 1.f / z;
         float m2 = (fin[ql][8] + fin[ql][9] + fin[ql][10]) * invz;
         float nx = 0.f;
@@ -340,13 +390,24 @@ __global__ __launch_bounds__(256) void nearest_lattice_kernel(const float* __res
   }
 }
 
+// flag: two int32 words of scratch (count) followed by room for m * n / 8 query indices.
 hipError_t launch_denoise_lattice(const float* R1, const float* gamma1, int64_t m, int64_t n, const CbTables& cb,
-                                  const float* a, const float* o, float* xhat, float* vblk, hipStream_t st) {
+                                  const float* a, const float* o, float* xhat, float* vblk, int32_t* flag,
+                                  hipStream_t st) {
   int64_t total = m * (n / 8);
   if (total <= 0) return hipSuccess;
+  int32_t* count = flag;
+  int32_t* list = flag + 64;
+  hipError_t e = launch_fill_i32(count, 1, 0, st);
+  if (e != hipSuccess) return e;
   dim3 grid((unsigned)((total + LAT_QWG - 1) / LAT_QWG));
-  hipLaunchKernelGGL(denoise_lattice_kernel, grid, dim3(256), 0, st, R1, gamma1, m, n, cb.qk_keys, cb.pv_ops, cb.e32,
-                     cb.Kpad, a, o, xhat, vblk);
+  hipLaunchKernelGGL((denoise_lattice_kernel<false>), grid, dim3(256), 0, st, R1, gamma1, m, n, cb.qk_keys, cb.pv_ops,
+                     cb.e32, cb.Kpad, a, o, xhat, vblk, list, count);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // flagged queries: the exact online-maximum pass; surplus workgroups exit at once
+  hipLaunchKernelGGL((denoise_lattice_kernel<true>), grid, dim3(256), 0, st, R1, gamma1, m, n, cb.qk_keys, cb.pv_ops,
+                     cb.e32, cb.Kpad, a, o, xhat, vblk, list, count);
   return hipGetLastError();
 }
 

@@ -10,11 +10,16 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 #define MPQ_WAVE 64
 
-// float -> bfloat16 bits, round to nearest even (finite inputs).
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// float -> bfloat16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t f2bf_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x);
+}
+// Two floats -> packed bfloat16 pair (x in the low half), round to nearest even.
+__device__ __forceinline__ uint32_t f2bf_pack(float x, float y) {
+  v2bf v = {(__bf16)x, (__bf16)y};
+  return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ float bf_bits2f(uint32_t b) { return __uint_as_float(b << 16); }
 

@@ -10,7 +10,7 @@ import pytest
 import mpq_synth as S
 from oracle import mpq_oracle as O
 from parity_helpers import SOFT_RTOL, OBJ_RTOL, CODE_FRAC, dev, host, layer_tensors, rel_vec, rel_scalar
-from oracle_pool import solve_rows
+from oracle.pool import solve_rows
 
 pytestmark = pytest.mark.gpu
 
