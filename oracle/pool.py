@@ -32,6 +32,24 @@ def _load(path):
     return _CACHE[path]
 
 
+def _stage(job):
+    """MAP or CD of one row from a given state (kind 'map': r1, gamma1;
+    kind 'cd': start codes)."""
+    if _ROOT not in sys.path:
+        sys.path.insert(0, _ROOT)
+    from oracle import mpq_oracle as O
+    path, i, d, S, kind, state = job
+    A = _load(path)
+    w = np.asarray(A["W"][i], np.float64)
+    a, o = float(A["a"][i]), float(A["o"][i])
+    C = O.row_codewords(A["E"], a, o)
+    if kind == "map":
+        r1, gamma1 = state
+        return O.map_codes(np.asarray(r1, np.float64), float(gamma1), C, d)
+    codes, changes = O.block_cd(np.asarray(state, np.int64), w, A["s"], A["V"], C, d, S)
+    return dict(codes=codes, changes=changes, objective=O.codes_objective(w, codes, C, d, A["s"], A["V"]))
+
+
 def _solve(job):
     if _ROOT not in sys.path:
         sys.path.insert(0, _ROOT)
@@ -52,24 +70,19 @@ def default_workers() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def solve_rows(L, rows, T_vamp=None, n_cd=None, record=False, max_workers=None):
-    """Oracle results for the given rows of a layer (attributes W, s, V, E, a,
-    o, d, T_vamp, n_cd, damping), in row order."""
-    T = L.T_vamp if T_vamp is None else T_vamp
-    S = L.n_cd if n_cd is None else n_cd
-    rows = [int(i) for i in rows]
+def _run(L, fn, make_jobs, max_workers):
     tmp = tempfile.mkdtemp(prefix="mpq_oracle_")
     try:
         for k in ("W", "s", "V", "E", "a", "o"):
             np.save(os.path.join(tmp, k + ".npy"), np.ascontiguousarray(getattr(L, k)))
-        jobs = [(tmp, i, L.d, T, S, L.damping, record) for i in rows]
+        jobs = make_jobs(tmp)
         nw = min(max_workers or default_workers(), len(jobs))
         saved = {k: os.environ.get(k) for k in _THREAD_VARS}
         for k in _THREAD_VARS:
             os.environ[k] = "1"
         try:
             with ProcessPoolExecutor(max_workers=max(nw, 1), mp_context=mp.get_context("spawn")) as ex:
-                return list(ex.map(_solve, jobs))
+                return list(ex.map(fn, jobs))
         finally:
             for k, v in saved.items():
                 if v is None:
@@ -78,3 +91,27 @@ def solve_rows(L, rows, T_vamp=None, n_cd=None, record=False, max_workers=None):
                     os.environ[k] = v
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
+
+
+def solve_rows(L, rows, T_vamp=None, n_cd=None, record=False, max_workers=None):
+    """Oracle results for the given rows of a layer (attributes W, s, V, E, a,
+    o, d, T_vamp, n_cd, damping), in row order."""
+    T = L.T_vamp if T_vamp is None else T_vamp
+    S = L.n_cd if n_cd is None else n_cd
+    rows = [int(i) for i in rows]
+    return _run(L, _solve, lambda tmp: [(tmp, i, L.d, T, S, L.damping, record) for i in rows], max_workers)
+
+
+def map_rows(L, rows, r1, gamma1, max_workers=None):
+    """Oracle marginal-MAP codes of `rows` at the given (r1[k], gamma1[k])."""
+    rows = [int(i) for i in rows]
+    return _run(L, _stage, lambda tmp: [(tmp, i, L.d, 0, "map", (r1[k], gamma1[k])) for k, i in enumerate(rows)],
+                max_workers)
+
+
+def cd_rows(L, rows, start_codes, n_cd=None, max_workers=None):
+    """Oracle block CD of `rows` from start_codes[k]."""
+    S = L.n_cd if n_cd is None else n_cd
+    rows = [int(i) for i in rows]
+    return _run(L, _stage, lambda tmp: [(tmp, i, L.d, S, "cd", start_codes[k]) for k, i in enumerate(rows)],
+                max_workers)

@@ -24,9 +24,6 @@ hipError_t launch_nearest_lattice(const float*, int64_t, int64_t, const CbTables
                                   int32_t*, hipStream_t);
 hipError_t launch_beta_lin(int64_t, const float*, const float*, float*, float*, hipStream_t);
 hipError_t launch_fill_i32(int32_t*, int64_t, int32_t, hipStream_t);
-hipError_t launch_cd_lattice_block(int64_t, int64_t, int64_t, int, int, float*, const float*, const CbTables&,
-                                   const float*, int32_t*, float*, int32_t*, float*, int32_t*, hipStream_t);
-int cd_lattice_slices(int Kpad);
 hipError_t launch_record_i32(const int32_t* src, int64_t m, int32_t* dst, int64_t ld, int64_t col, hipStream_t st);
 }  // namespace mpq
 
@@ -73,7 +70,7 @@ struct Layout {
 
 enum Region {
   R_VS, R_VST, R_YTIL, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI,
-  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_COUNT
+  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_COUNT
 };
 
 size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -98,11 +95,12 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
   sz[R_VBLK] = (size_t)m * L.B * f;
   sz[R_ROWS] = (size_t)8 * m * f;
   sz[R_PART] = (size_t)m * L.ncoltiles * f;
-  sz[R_GT] = (size_t)m * KD * f;
-  sz[R_DELTA] = (size_t)m * KD * f;
-  sz[R_HD] = (size_t)L.ntiles * KD * KD * f;
-  sz[R_PS] = (size_t)std::max(L.nslices, 1) * m * f;
-  sz[R_PI] = (size_t)std::max(L.nslices, 1) * m * sizeof(int32_t);
+  const size_t f64 = sizeof(double);
+  sz[R_GT] = (size_t)m * KD * f64;
+  sz[R_DELTA] = (size_t)m * KD * f64;
+  sz[R_HD] = (size_t)L.ntiles * KD * KD * f64;
+  sz[R_PS] = (size_t)2 * std::max(L.nslices, 1) * m * f;
+  sz[R_PI] = (size_t)2 * std::max(L.nslices, 1) * m * sizeof(int32_t);
   sz[R_CHG] = (size_t)m * sizeof(int32_t);
   sz[R_CODES] = (size_t)m * L.B * sizeof(int32_t);
   sz[R_LEVELS] = 64 * f;
@@ -110,6 +108,8 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
   sz[R_PV] = d == 8 ? (size_t)L.Kpad * 8 * sizeof(uint32_t) : 0;
   sz[R_E32] = (size_t)(d == 8 ? L.Kpad : 64) * 8 * f;
   sz[R_FLAG] = d == 8 ? (size_t)(64 + m * L.B) * sizeof(int32_t) : 0;
+  sz[R_U64] = (size_t)m * r * f64;
+  sz[R_D64] = (size_t)m * n * f64;
   size_t o = 0;
   for (int k = 0; k < R_COUNT; ++k) {
     L.off[k] = o;
@@ -400,47 +400,62 @@ int run_iteration(Ctx& c, float* R1, float* gamma1, float* beta, const float* yt
   return MPQ_OK;
 }
 
+Gemm64Args gemm64(int M, int N, int K, const void* A, int64_t lda, const float* B, int64_t ldb, double* C,
+                  int64_t ldc) {
+  Gemm64Args g;
+  memset(&g, 0, sizeof(g));
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda;
+  g.B = B; g.ldb = ldb;
+  g.C = C; g.ldc = ldc;
+  g.batch = 1;
+  return g;
+}
+
 // n_cd sweeps of exact block CD from `codes` (workspace or caller buffer).
+// The residual U = (W - X) V diag(s), the tile gradients, the diagonal tiles
+// of H and the moves are float64.
 int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int32_t* codes, int32_t* cd_changes) {
   const Layout& L = c.L;
   if (n_cd <= 0 || L.m == 0) return MPQ_OK;
-  float* X = c.p(R_R2);     // codeword values (scalar CD keeps them current)
-  float* D = c.p(R_X1);     // W - X
-  float* U = c.p(R_Z);      // rank-space residual
-  float* Gt = c.p(R_GT);
-  float* Dl = c.p(R_DELTA);
-  float* Hd = c.p(R_HD);
+  double* D = reinterpret_cast<double*>(c.p(R_D64));   // W - X
+  double* U = reinterpret_cast<double*>(c.p(R_U64));   // rank-space residual
+  double* Gt = reinterpret_cast<double*>(c.p(R_GT));
+  double* Dl = reinterpret_cast<double*>(c.p(R_DELTA));
+  double* Hd = reinterpret_cast<double*>(c.p(R_HD));
   int32_t* chg = c.pi(R_CHG);
-  TIMED(c, MPQ_PROF_CD_GEMM, launch_gather(codes, L.m, L.n, c.cb, a, o, W, X, D, nullptr, c.st));
+  TIMED(c, MPQ_PROF_CD_GEMM, launch_gather(codes, L.m, L.n, c.cb, a, o, W, nullptr, nullptr, nullptr, c.st, D));
   TIMED(c, MPQ_PROF_CD_GEMM,
-        launch_gemm(EPI_STORE, gemm((int)L.m, (int)L.r, (int)L.n, D, L.n, c.p(R_VST), L.n, U, L.r), c.st));
+        launch_gemm64(EPI_STORE, true, gemm64((int)L.m, (int)L.r, (int)L.n, D, L.n, c.p(R_VST), L.n, U, L.r), c.st));
   // diagonal tiles of H = VS VS^T
   const int full = (int)(L.n / KD);
   if (full > 0) {
-    GemmArgs h = gemm(KD, KD, (int)L.r, c.p(R_VS), L.r, c.p(R_VS), L.r, Hd, KD);
+    Gemm64Args h = gemm64(KD, KD, (int)L.r, c.p(R_VS), L.r, c.p(R_VS), L.r, Hd, KD);
     h.batch = full;
     h.sA = (int64_t)KD * L.r;
     h.sB = (int64_t)KD * L.r;
     h.sC = (int64_t)KD * KD;
-    TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm(EPI_STORE, h, c.st));
+    TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_STORE, false, h, c.st));
   }
   const int rem = (int)(L.n - (int64_t)full * KD);
   if (rem > 0) {
     const float* vs = c.p(R_VS) + (int64_t)full * KD * L.r;
     TIMED(c, MPQ_PROF_CD_GEMM,
-          launch_gemm(EPI_STORE, gemm(rem, rem, (int)L.r, vs, L.r, vs, L.r, Hd + (int64_t)full * KD * KD, rem),
-                      c.st));
+          launch_gemm64(EPI_STORE, false, gemm64(rem, rem, (int)L.r, vs, L.r, vs, L.r, Hd + (int64_t)full * KD * KD,
+                                                 rem), c.st));
   }
   for (int sw = 0; sw < n_cd; ++sw) {
     TIMED(c, MPQ_PROF_OTHER, launch_fill_i32(chg, L.m, 0, c.st));
     for (int tl = 0; tl < L.ntiles; ++tl) {
       const int64_t j0 = (int64_t)tl * KD;
       const int kw = (int)std::min<int64_t>(KD, L.n - j0);
-      const float* Ht = Hd + (int64_t)tl * KD * KD;
+      const double* Ht = Hd + (int64_t)tl * KD * KD;
       TIMED(c, MPQ_PROF_CD_GEMM,
-            launch_gemm(EPI_STORE, gemm((int)L.m, kw, (int)L.r, U, L.r, c.p(R_VS) + j0 * L.r, L.r, Gt, kw), c.st));
+            launch_gemm64(EPI_STORE, true, gemm64((int)L.m, kw, (int)L.r, U, L.r, c.p(R_VS) + j0 * L.r, L.r, Gt, kw),
+                          c.st));
       if (L.d == 1) {
-        TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_scalar_tile(L.m, L.n, j0, kw, Gt, Ht, c.cb, a, o, codes, X, Dl, chg, c.st));
+        TIMED(c, MPQ_PROF_CD_SEARCH,
+              launch_cd_scalar_tile(L.m, L.n, j0, kw, Gt, Ht, c.cb, a, o, codes, nullptr, Dl, chg, c.st));
       } else {
         for (int bl = 0; bl < kw / 8; ++bl) {
           TIMED(c, MPQ_PROF_CD_SEARCH,
@@ -449,7 +464,8 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
         }
       }
       TIMED(c, MPQ_PROF_CD_GEMM,
-            launch_gemm(EPI_SUB_INPLACE, gemm((int)L.m, (int)L.r, kw, Dl, kw, c.p(R_VST) + j0, L.n, U, L.r), c.st));
+            launch_gemm64(EPI_SUB_INPLACE, true, gemm64((int)L.m, (int)L.r, kw, Dl, kw, c.p(R_VST) + j0, L.n, U, L.r),
+                          c.st));
     }
     if (cd_changes) TIMED(c, MPQ_PROF_OTHER, launch_record_i32(chg, L.m, cd_changes, n_cd, sw, c.st));
   }

@@ -9,36 +9,50 @@
 // residual updates.
 //
 // This kernel: one wave per row; the tile's gradient, codes and codeword
-// values sit in registers (lane l, slot s <-> column s*64 + l).
+// values sit in registers (lane l, slot s <-> column s*64 + l).  The residual,
+// gradient, H tile and moves are float64 so that the integer decisions
+// depend on float32 rounding as little as possible.
 #include <math.h>
 #include "mpq_device.h"
 #include "internal.h"
 
 namespace mpq {
 
+// Uniform read of lane `l`'s double (two 32-bit readlanes).
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  int2 p = __builtin_bit_cast(int2, v);
+  p.x = __builtin_amdgcn_readlane(p.x, l);
+  p.y = __builtin_amdgcn_readlane(p.y, l);
+  return __builtin_bit_cast(double, p);
+}
+
+// CD decisions use float64 state (tile gradient g, tile of H, moves) and
+// float64 codeword values c = a e + o:
+// dF(c) = 1/2 H_jj (c - x_j)^2 - (c - x_j) g_j.
 template <int SLOTS>
 __global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t n, int64_t j0, int kd,
-                                                             const float* __restrict__ G, const float* __restrict__ Ht,
+                                                             const double* __restrict__ G,
+                                                             const double* __restrict__ Ht,
                                                              const float* __restrict__ levels, int K,
                                                              const float* __restrict__ a, const float* __restrict__ o,
                                                              int32_t* __restrict__ codes, float* __restrict__ X,
-                                                             float* __restrict__ Delta, int32_t* __restrict__ changes) {
+                                                             double* __restrict__ Delta, int32_t* __restrict__ changes) {
   const int lane = threadIdx.x & 63;
   const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= m) return;
-  const float ai = a[i], oi = o[i];
-  const float cl = lane < K ? fmaf(ai, levels[lane], oi) : 0.f;
+  const double ai = a[i], oi = o[i];
+  const double cl = lane < K ? ai * (double)levels[lane] + oi : 0.0;
 
-  float g[SLOTS], x[SLOTS], dl[SLOTS];
+  double g[SLOTS], dl[SLOTS], x[SLOTS];
   int cd[SLOTS];
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     int jj = s * 64 + lane;
     bool in = jj < kd;
-    g[s] = in ? G[i * kd + jj] : 0.f;
-    x[s] = in ? X[i * n + j0 + jj] : 0.f;
+    g[s] = in ? G[i * kd + jj] : 0.0;
     cd[s] = in ? codes[i * n + j0 + jj] : 0;
-    dl[s] = 0.f;
+    x[s] = in ? ai * (double)levels[cd[s]] + oi : 0.0;
+    dl[s] = 0.0;
   }
   int moved = 0;
 #pragma unroll
@@ -46,25 +60,24 @@ __global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t 
     for (int jl = 0; jl < 64; ++jl) {
       const int jj = s * 64 + jl;
       if (jj >= kd) break;
-      const float gj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g[s]), jl));
-      const float xj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[s]), jl));
-      const float hjj = Ht[(int64_t)jj * kd + jj];
-      // dF(c) = 1/2 H_jj (c - x_j)^2 - (c - x_j) g_j over the row's levels
-      float dlt = cl - xj;
-      float f = lane < K ? (0.5f * hjj * dlt - gj) * dlt : INFINITY;
+      const double gj = readlane_d(g[s], jl);
+      const double xj = readlane_d(x[s], jl);
+      const double hjj = Ht[(int64_t)jj * kd + jj];
+      const double dlt = cl - xj;
+      double f = lane < K ? (0.5 * hjj * dlt - gj) * dlt : INFINITY;
       int k = lane;
 #pragma unroll
       for (int msk = 1; msk < 64; msk <<= 1) {
-        float fo = shfl_xor_f(f, msk);
+        double fo = __shfl_xor(f, msk, 64);
         int ko = shfl_xor_i(k, msk);
         if (fo < f || (fo == f && ko < k)) { f = fo; k = ko; }
       }
-      if (f < 0.f) {  // strict improvement only (uniform across the wave)
-        const float cnew = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), k));
-        const float dstar = cnew - xj;
+      if (f < 0.0) {  // strict improvement only (uniform across the wave)
+        const double cnew = readlane_d(cl, k);
+        const double dstar = cnew - xj;
         if (lane == jl) { x[s] = cnew; cd[s] = k; dl[s] = dstar; }
         ++moved;
-        const float* hrow = Ht + (int64_t)jj * kd;
+        const double* hrow = Ht + (int64_t)jj * kd;
 #pragma unroll
         for (int s2 = 0; s2 < SLOTS; ++s2) {
           int jc = s2 * 64 + lane;
@@ -77,7 +90,6 @@ __global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t 
   for (int s = 0; s < SLOTS; ++s) {
     int jj = s * 64 + lane;
     if (jj < kd) {
-      X[i * n + j0 + jj] = x[s];
       codes[i * n + j0 + jj] = cd[s];
       Delta[i * kd + jj] = dl[s];
     }
@@ -85,9 +97,9 @@ __global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t 
   if (lane == 0) changes[i] += moved;
 }
 
-hipError_t launch_cd_scalar_tile(int64_t m, int64_t n, int64_t j0, int kd, const float* G, const float* Ht,
+hipError_t launch_cd_scalar_tile(int64_t m, int64_t n, int64_t j0, int kd, const double* G, const double* Ht,
                                  const CbTables& cb, const float* a, const float* o, int32_t* codes, float* X,
-                                 float* Delta, int32_t* changes, hipStream_t st) {
+                                 double* Delta, int32_t* changes, hipStream_t st) {
   if (m <= 0) return hipSuccess;
   dim3 grid((unsigned)((m + 3) / 4));
   if (kd <= 64)

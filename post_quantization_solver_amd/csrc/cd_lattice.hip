@@ -11,8 +11,10 @@
 // 16 x 16 (codeword x row) tile -- key slots [e | e | e | t terms], query
 // slots [-q hi | -q mid | -q lo | a^2 terms], all products exact -- and keeps
 // the per-row argmin (ties: lowest index) of its codeword slice.
-// cd_update_kernel reduces the slices in order, re-evaluates dF of the winner
-// exactly in float32 and moves the block only on a strict decrease.
+// cd_update_kernel merges the slices' two best candidates in order,
+// re-evaluates dF of both finalists exactly in float64 (the tile gradient,
+// H and the residual are float64) and moves the block only on a strict
+// decrease.
 #include <math.h>
 #include "mpq_device.h"
 #include "internal.h"
@@ -32,14 +34,42 @@ __device__ __forceinline__ v4u pack8(const uint32_t (&w)[8]) {
   return r;
 }
 
-// grid: (slices, row groups).  part_s / part_i: [slices][m].
+// (score, index) pairs ordered by score, ties to the lower index.
+struct Cand {
+  float v;
+  int i;
+};
+__device__ __forceinline__ bool cand_less(float v1, int i1, float v2, int i2) {
+  return v1 < v2 || (v1 == v2 && i1 < i2);
+}
+// Merge two sorted top-2 lists (a1 <= a2, c1 <= c2) into the top 2 of the four.
+__device__ __forceinline__ void merge_top2(Cand& a1, Cand& a2, Cand c1, Cand c2) {
+  if (cand_less(c1.v, c1.i, a1.v, a1.i)) {
+    Cand sec = cand_less(a1.v, a1.i, c2.v, c2.i) ? a1 : c2;
+    a1 = c1;
+    a2 = sec;
+  } else if (cand_less(c1.v, c1.i, a2.v, a2.i)) {
+    a2 = c1;
+  }
+}
+__device__ __forceinline__ Cand shfl_cand(Cand c, int mask) {
+  Cand o;
+  o.v = shfl_xor_f(c.v, mask);
+  o.i = shfl_xor_i(c.i, mask);
+  return o;
+}
+
+// grid: (slices, row groups).  part_s / part_i: [2][slices][m] (best, second).
+// The float32 scores only rank candidates; the update kernel re-evaluates the
+// two best of every slice exactly in float64.
 __global__ __launch_bounds__(256) void cd_score_kernel(int64_t m, int64_t n, int64_t b, int bl, int kd,
-                                                       const float* __restrict__ Gt, const float* __restrict__ Ht,
+                                                       const double* __restrict__ Gt, const double* __restrict__ Ht,
                                                        const uint32_t* __restrict__ keys,
                                                        const float* __restrict__ e32, int K, int Kpad,
                                                        const float* __restrict__ a, const int32_t* __restrict__ codes,
                                                        float* __restrict__ part_s, int32_t* __restrict__ part_i) {
   __shared__ __attribute__((aligned(16))) uint32_t lds_key[(CDL_CW_WG / 16) * 64 * 4];
+  __shared__ double Gd[64];
   __shared__ float Gb[64];
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -50,8 +80,13 @@ __global__ __launch_bounds__(256) void cd_score_kernel(int64_t m, int64_t n, int
   const int cw_base = blockIdx.x * CDL_CW_WG;
   const int ncw = min(CDL_CW_WG, Kpad - cw_base);
   const int64_t row_base = (int64_t)blockIdx.y * CDL_ROWS_WG + wave * CDL_ROWS_WAVE;
+  const int nsl = gridDim.x;
 
-  if (t < 64) Gb[t] = Ht[(int64_t)(8 * bl + (t >> 3)) * kd + 8 * bl + (t & 7)];
+  if (t < 64) {
+    double h = Ht[(int64_t)(8 * bl + (t >> 3)) * kd + 8 * bl + (t & 7)];
+    Gd[t] = h;
+    Gb[t] = (float)h;
+  }
   __syncthreads();
 
   // key fragments of this slice: lanes g < 3 copy e, lanes g = 3 carry t(e) terms
@@ -98,17 +133,17 @@ __global__ __launch_bounds__(256) void cd_score_kernel(int64_t m, int64_t n, int
 #pragma unroll
     for (int k = 0; k < 8; ++k) qv[k] = 0.f;
     if (i < m) {
-      const float ai = a[i];
+      const double ai = a[i];
       const float* ex = e32 + (int64_t)codes[i * B + b] * 8;
-      const float* gb = Gt + i * kd + 8 * bl;
+      const double* gb = Gt + i * kd + 8 * bl;
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
-        float ge = 0.f;
+        double ge = 0.0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) ge = fmaf(Gb[p * 8 + k], ex[k], ge);
-        qv[p] = -ai * fmaf(ai, ge, gb[p]);
+        for (int k = 0; k < 8; ++k) ge = fma(Gd[p * 8 + k], (double)ex[k], ge);
+        qv[p] = (float)(-ai * fma(ai, ge, gb[p]));
       }
-      A = ai * ai;
+      A = (float)(ai * ai);
     }
     uint32_t w[8];
     if (g < 3) {
@@ -136,91 +171,113 @@ __global__ __launch_bounds__(256) void cd_score_kernel(int64_t m, int64_t n, int
     const int cw0 = cw_base + st * 16 + 4 * g;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      v4f s = mfma_bf16_16x16x32(k0, qop[q], zero4);
+      v4f sc = mfma_bf16_16x16x32(k0, qop[q], zero4);
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        if (s[v] < best[q]) { best[q] = s[v]; bidx[q] = cw0 + v; }
+        if (sc[v] < best[q]) { best[q] = sc[v]; bidx[q] = cw0 + v; }
     }
   }
+  // top 2 of the row's four lane-bests (lanes j, j+16, j+32, j+48)
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    float bv = best[q];
-    int bi = bidx[q];
+    Cand c1 = {best[q], bidx[q]};
+    Cand c2 = {INFINITY, 0x7fffffff};
 #pragma unroll
     for (int msk = 16; msk <= 32; msk <<= 1) {
-      float ov = shfl_xor_f(bv, msk);
-      int oi = shfl_xor_i(bi, msk);
-      if (ov < bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      Cand o1 = shfl_cand(c1, msk), o2 = shfl_cand(c2, msk);
+      merge_top2(c1, c2, o1, o2);
     }
     const int64_t i = row_base + q * 16 + j;
     if (g == 0 && i < m) {
-      part_s[(int64_t)blockIdx.x * m + i] = bv;
-      part_i[(int64_t)blockIdx.x * m + i] = bi;
+      part_s[(int64_t)blockIdx.x * m + i] = c1.v;
+      part_i[(int64_t)blockIdx.x * m + i] = c1.i;
+      part_s[((int64_t)nsl + blockIdx.x) * m + i] = c2.v;
+      part_i[((int64_t)nsl + blockIdx.x) * m + i] = c2.i;
     }
   }
 }
 
-// One wave per row.
+// Exact float64 change of the objective for moving block (8 coords) from
+// base codeword ex to en (row scale ai): dF = 1/2 d^T G d - d^T g, d = a (en - ex).
+__device__ __forceinline__ double move_gain(const double* __restrict__ Ht, int kd, int bl,
+                                            const double* __restrict__ gb, const float* en, const float* ex,
+                                            double ai, double (&dlt)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) dlt[k] = ai * ((double)en[k] - (double)ex[k]);
+  double f = 0.0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    double gd = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) gd = fma(Ht[(int64_t)(8 * bl + p) * kd + 8 * bl + k], dlt[k], gd);
+    f = fma(dlt[p], 0.5 * gd - gb[p], f);
+  }
+  return f;
+}
+
+// One wave per row: merge the slices' top-2 lists in order, re-score the two
+// finalists in float64 and move on a strict decrease.
 __global__ __launch_bounds__(256) void cd_update_kernel(int64_t m, int64_t n, int64_t b, int bl, int kd, int nslices,
-                                                        float* __restrict__ Gt, const float* __restrict__ Ht,
+                                                        double* __restrict__ Gt, const double* __restrict__ Ht,
                                                         const float* __restrict__ e32, const float* __restrict__ a,
                                                         const float* __restrict__ part_s,
                                                         const int32_t* __restrict__ part_i,
-                                                        int32_t* __restrict__ codes, float* __restrict__ Delta,
+                                                        int32_t* __restrict__ codes, double* __restrict__ Delta,
                                                         int32_t* __restrict__ changes) {
   const int lane = threadIdx.x & 63;
   const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= m) return;
   const int64_t B = n / 8;
-  float bv = INFINITY;
-  int bi = 0x7fffffff;
+  Cand c1 = {INFINITY, 0x7fffffff}, c2 = {INFINITY, 0x7fffffff};
   for (int sl = 0; sl < nslices; ++sl) {
-    float v = part_s[(int64_t)sl * m + i];
-    int id = part_i[(int64_t)sl * m + i];
-    if (v < bv || (v == bv && id < bi)) { bv = v; bi = id; }
+    Cand o1 = {part_s[(int64_t)sl * m + i], part_i[(int64_t)sl * m + i]};
+    Cand o2 = {part_s[((int64_t)nslices + sl) * m + i], part_i[((int64_t)nslices + sl) * m + i]};
+    merge_top2(c1, c2, o1, o2);
   }
   const int cx = codes[i * B + b];
-  float* dl = Delta + i * kd + 8 * bl;
-  bool accept = false;
-  float dlt[8];
-  if (bi != cx) {
-    const float ai = a[i];
-    const float* gb = Gt + i * kd + 8 * bl;
-    const float* en = e32 + (int64_t)bi * 8;
-    const float* eo = e32 + (int64_t)cx * 8;
+  double* dl = Delta + i * kd + 8 * bl;
+  const double* gb = Gt + i * kd + 8 * bl;
+  const double ai = a[i];
+  const float* ex = e32 + (int64_t)cx * 8;
+  double bestF = 0.0;
+  int bestk = cx;
+  double dlt[8], tmp[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) dlt[k] = ai * (en[k] - eo[k]);
-    float f = 0.f;
+  for (int k = 0; k < 8; ++k) dlt[k] = 0.0;
+  const int cands[2] = {c1.i, c2.i};
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      float gd = 0.f;
+  for (int c = 0; c < 2; ++c) {
+    const int k2 = cands[c];
+    if (k2 == 0x7fffffff || k2 == cx) continue;
+    double f = move_gain(Ht, kd, bl, gb, e32 + (int64_t)k2 * 8, ex, ai, tmp);
+    if (f < bestF || (f == bestF && bestk != cx && k2 < bestk)) {
+      bestF = f;
+      bestk = k2;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) gd = fmaf(Ht[(int64_t)(8 * bl + p) * kd + 8 * bl + k], dlt[k], gd);
-      f = fmaf(dlt[p], 0.5f * gd - gb[p], f);
+      for (int k = 0; k < 8; ++k) dlt[k] = tmp[k];
     }
-    accept = f < 0.f;
   }
-  if (!accept) {
-    if (lane < 8) dl[lane] = 0.f;
+  if (bestk == cx) {
+    if (lane < 8) dl[lane] = 0.0;
     return;
   }
   if (lane < 8) dl[lane] = dlt[lane];
   if (lane == 0) {
-    codes[i * B + b] = bi;
+    codes[i * B + b] = bestk;
     changes[i] += 1;
   }
   // g_j -= sum_k H[j][8 bl + k] delta_k for every column j of the tile
   for (int jc = lane; jc < kd; jc += 64) {
-    const float* hr = Ht + (int64_t)jc * kd + 8 * bl;
-    float s = 0.f;
+    const double* hr = Ht + (int64_t)jc * kd + 8 * bl;
+    double sacc = 0.0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) s = fmaf(hr[k], dlt[k], s);
-    Gt[i * kd + jc] -= s;
+    for (int k = 0; k < 8; ++k) sacc = fma(hr[k], dlt[k], sacc);
+    Gt[i * kd + jc] -= sacc;
   }
 }
 
-hipError_t launch_cd_lattice_block(int64_t m, int64_t n, int64_t b, int bl, int kd, float* Gt, const float* Ht,
-                                   const CbTables& cb, const float* a, int32_t* codes, float* Delta,
+hipError_t launch_cd_lattice_block(int64_t m, int64_t n, int64_t b, int bl, int kd, double* Gt, const double* Ht,
+                                   const CbTables& cb, const float* a, int32_t* codes, double* Delta,
                                    int32_t* changes, float* part_s, int32_t* part_i, hipStream_t st) {
   if (m <= 0) return hipSuccess;
   const int nslices = (cb.Kpad + CDL_CW_WG - 1) / CDL_CW_WG;

@@ -1,0 +1,157 @@
+// Float64 GEMM on the CDNA4 fp64 matrix cores, for the coordinate-descent
+// state (rank-space residual, tile gradients and the diagonal tiles of H):
+//
+//   C[M x N] (=, -=) A[M x K] * B[N x K]^T,   A float64 or float32,
+//   B float32 (widened exactly on load), C float64.
+//
+// CD decides integer codes from small differences of these quantities, so
+// they are kept in float64.  Same tiling as the float32 kernel: 256 threads
+// per 128 x 128 tile, K in LDS slices of 16 (double-buffered), each wave a
+// 64 x 64 block of 4 x 4 v_mfma_f64_16x16x4_f64 accumulators; lane (i, g)
+// feeds k = 4g + kk to MFMA step kk.  Unlike the float32 form, this MFMA
+// returns rows g + 4v (v = 0..3) of column i in lane (i, g).
+#include "mpq_device.h"
+#include "internal.h"
+
+namespace mpq {
+
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+constexpr int BK64 = 16;
+constexpr int LDS64 = BK64 + 2;  // doubles per LDS row
+
+template <typename T, bool VEC>
+__device__ __forceinline__ void load_tile64(const T* __restrict__ P, int64_t ld, int rows, int K, int row0, int k0,
+                                            int t, double (&reg)[2][4]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int rr = row0 + (t >> 2) + h * 64;
+    int kk = k0 + (t & 3) * 4;
+    const T* src = P + (int64_t)rr * ld + kk;
+    if (VEC && rr < rows && kk < K) {
+      if (sizeof(T) == 8) {
+        const double2* s2 = reinterpret_cast<const double2*>(src);
+        double2 a = s2[0], b = s2[1];
+        reg[h][0] = a.x; reg[h][1] = a.y; reg[h][2] = b.x; reg[h][3] = b.y;
+      } else {
+        float4 a = *reinterpret_cast<const float4*>(src);
+        reg[h][0] = a.x; reg[h][1] = a.y; reg[h][2] = a.z; reg[h][3] = a.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) reg[h][q] = (rr < rows && kk + q < K) ? (double)src[q] : 0.0;
+    }
+  }
+}
+
+__device__ __forceinline__ void store_tile64(double* lds, int t, const double (&reg)[2][4]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int rr = (t >> 2) + h * 64;
+    double* d = lds + rr * LDS64 + (t & 3) * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[q] = reg[h][q];
+  }
+}
+
+template <typename TA, int EPI, bool VEC>
+__global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
+  __shared__ double As[2][GEMM_BM * LDS64];
+  __shared__ double Bs[2][GEMM_BN * LDS64];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wr = (wave >> 1) * 64;
+  const int wc = (wave & 1) * 64;
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+  const int row0 = blockIdx.y * GEMM_BM;
+  const int col0 = blockIdx.x * GEMM_BN;
+  const int z = blockIdx.z;
+  const TA* A = reinterpret_cast<const TA*>(g.A) + (int64_t)z * g.sA;
+  const float* B = g.B + (int64_t)z * g.sB;
+  double* C = g.C + (int64_t)z * g.sC;
+
+  v4d acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (v4d){0.0, 0.0, 0.0, 0.0};
+
+  const int nk = (g.K + BK64 - 1) / BK64;
+  double ra[2][4], rb[2][4];
+  load_tile64<TA, VEC>(A, g.lda, g.M, g.K, row0, 0, t, ra);
+  load_tile64<float, VEC>(B, g.ldb, g.N, g.K, col0, 0, t, rb);
+  store_tile64(As[0], t, ra);
+  store_tile64(Bs[0], t, rb);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) {
+      load_tile64<TA, VEC>(A, g.lda, g.M, g.K, row0, (kt + 1) * BK64, t, ra);
+      load_tile64<float, VEC>(B, g.ldb, g.N, g.K, col0, (kt + 1) * BK64, t, rb);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      double af[4], bf[4];
+#pragma unroll
+      for (int si = 0; si < 4; ++si) af[si] = As[cur][(wr + si * 16 + li) * LDS64 + lg * 4 + kk];
+#pragma unroll
+      for (int sj = 0; sj < 4; ++sj) bf[sj] = Bs[cur][(wc + sj * 16 + li) * LDS64 + lg * 4 + kk];
+#pragma unroll
+      for (int si = 0; si < 4; ++si)
+#pragma unroll
+        for (int sj = 0; sj < 4; ++sj)
+          acc[si][sj] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[si], bf[sj], acc[si][sj], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      store_tile64(As[cur ^ 1], t, ra);
+      store_tile64(Bs[cur ^ 1], t, rb);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int si = 0; si < 4; ++si)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      // v_mfma_f64_16x16x4_f64 output: lane l holds rows l/16 + 4 v of column l % 16
+      const int row = row0 + wr + si * 16 + lg + 4 * v;
+      if (row >= g.M) continue;
+#pragma unroll
+      for (int sj = 0; sj < 4; ++sj) {
+        const int col = col0 + wc + sj * 16 + li;
+        if (col >= g.N) continue;
+        double* cp = C + (int64_t)row * g.ldc + col;
+        if (EPI == EPI_STORE)
+          *cp = acc[si][sj][v];
+        else
+          *cp = *cp - acc[si][sj][v];
+      }
+    }
+}
+
+template <typename TA, int EPI>
+static hipError_t launch64(const Gemm64Args& g, hipStream_t st) {
+  dim3 grid(gemm_col_tiles(g.N), (g.M + GEMM_BM - 1) / GEMM_BM, g.batch > 0 ? g.batch : 1);
+  const size_t ea = sizeof(TA);
+  bool vec = (g.K % 4 == 0) && (g.lda % 4 == 0) && (g.ldb % 4 == 0) && (g.sA % 4 == 0) && (g.sB % 4 == 0) &&
+             ((reinterpret_cast<uintptr_t>(g.A) % (4 * ea)) == 0) && ((reinterpret_cast<uintptr_t>(g.B) & 15) == 0);
+  if (vec)
+    hipLaunchKernelGGL((gemm64_nt_kernel<TA, EPI, true>), grid, dim3(256), 0, st, g);
+  else
+    hipLaunchKernelGGL((gemm64_nt_kernel<TA, EPI, false>), grid, dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm64(int epi, bool a_is_f64, const Gemm64Args& g, hipStream_t st) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (a_is_f64) {
+    if (epi == EPI_STORE) return launch64<double, EPI_STORE>(g, st);
+    if (epi == EPI_SUB_INPLACE) return launch64<double, EPI_SUB_INPLACE>(g, st);
+  } else {
+    if (epi == EPI_STORE) return launch64<float, EPI_STORE>(g, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mpq

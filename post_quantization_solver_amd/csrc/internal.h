@@ -34,6 +34,17 @@ constexpr int GEMM_BM = 128, GEMM_BN = 128;
 inline int gemm_col_tiles(int N) { return (N + GEMM_BN - 1) / GEMM_BN; }
 hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t st);
 
+// Float64 variant for the CD state: C (float64) = / -= A (float64 or float32)
+// * B (float32)^T on the fp64 matrix cores.  Epilogues EPI_STORE, EPI_SUB_INPLACE.
+struct Gemm64Args {
+  int M, N, K;
+  const void* A; int64_t lda; int64_t sA;
+  const float* B; int64_t ldb; int64_t sB;
+  double* C; int64_t ldc; int64_t sC;
+  int batch;
+};
+hipError_t launch_gemm64(int epi, bool a_is_f64, const Gemm64Args& g, hipStream_t st);
+
 // ------------------------------------------------------------ codebook ----
 // Device tables derived from the host codebook.
 struct CbTables {
@@ -48,10 +59,11 @@ struct CbTables {
 // ----------------------------------------------------------- kernels ----
 hipError_t launch_scale_columns(const float* V, const float* s, int64_t n, int64_t r, float* VS, float* VSt, hipStream_t st);
 
-// X = codewords of codes; optionally D = W - X and per-row sum of D^2.
+// X = codewords of codes; optionally D = W - X (float32 and/or float64) and
+// the per-row sum of D^2.
 hipError_t launch_gather(const int32_t* codes, int64_t m, int64_t n, const CbTables& cb,
                          const float* a, const float* o, const float* W, float* X, float* D,
-                         float* rowsq, hipStream_t st);
+                         float* rowsq, hipStream_t st, double* D64 = nullptr);
 
 // Prologue per-row finish: gamma1 = 1/mse, beta0 from partial sums, frozen flags.
 hipError_t launch_prologue_finish(int64_t m, int64_t n, int64_t r, const float* rowsq, const float* partial,
@@ -73,8 +85,13 @@ hipError_t launch_record(const float* src, int64_t m, float* dst, int64_t ld, in
 hipError_t launch_copy_rows_f(const float* src, float* dst, int64_t count, hipStream_t st);
 
 // CD (scalar grids): one tile of kd columns starting at column j0.
-hipError_t launch_cd_scalar_tile(int64_t m, int64_t n, int64_t j0, int kd, const float* G, const float* Ht,
+hipError_t launch_cd_scalar_tile(int64_t m, int64_t n, int64_t j0, int kd, const double* G, const double* Ht,
                                  const CbTables& cb, const float* a, const float* o, int32_t* codes,
-                                 float* X, float* Delta, int32_t* changes, hipStream_t st);
+                                 float* X, double* Delta, int32_t* changes, hipStream_t st);
+// CD (d = 8): one block of a tile (scoring over codeword slices, then the move).
+hipError_t launch_cd_lattice_block(int64_t m, int64_t n, int64_t b, int bl, int kd, double* Gt, const double* Ht,
+                                   const CbTables& cb, const float* a, int32_t* codes, double* Delta,
+                                   int32_t* changes, float* part_s, int32_t* part_i, hipStream_t st);
+int cd_lattice_slices(int Kpad);
 
 }  // namespace mpq

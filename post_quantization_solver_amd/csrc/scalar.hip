@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
                                                      const float* __restrict__ e32, const float* __restrict__ a,
                                                      const float* __restrict__ o, const float* __restrict__ W,
                                                      float* __restrict__ X, float* __restrict__ D,
-                                                     float* __restrict__ rowsq) {
+                                                     float* __restrict__ rowsq, double* __restrict__ D64) {
   __shared__ float sh[256];
   const int64_t i = blockIdx.x;
   const int t = threadIdx.x;
@@ -112,6 +112,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
     int c = codes[i * B + b];
     float x = fmaf(ai, e32[(int64_t)c * d + (j - b * d)], oi);
     if (X) X[i * n + j] = x;
+    if (D64) D64[i * n + j] = (double)W[i * n + j] - ((double)ai * (double)e32[(int64_t)c * d + (j - b * d)] + (double)oi);
     if (D) {
       float dd = W[i * n + j] - x;
       D[i * n + j] = dd;
@@ -130,10 +131,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 }
 
 hipError_t launch_gather(const int32_t* codes, int64_t m, int64_t n, const CbTables& cb, const float* a,
-                         const float* o, const float* W, float* X, float* D, float* rowsq, hipStream_t st) {
+                         const float* o, const float* W, float* X, float* D, float* rowsq, hipStream_t st,
+                         double* D64) {
   if (m <= 0) return hipSuccess;
   const float* tab = cb.d == 1 ? cb.levels : cb.e32;
-  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)m), dim3(256), 0, st, codes, n, cb.d, tab, a, o, W, X, D, rowsq);
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)m), dim3(256), 0, st, codes, n, cb.d, tab, a, o, W, X, D, rowsq,
+                     D64);
   return hipGetLastError();
 }
 

@@ -106,10 +106,14 @@ def test_vamp_step(name):
             # compared relative to the subtraction's operands: errors scaled
             # by cond = eta1 / gamma2 (1 when the posterior is passed through)
             cond = max(1.0, h[k]["eta1"] / h[k]["gamma2"])
+            # r1' = r2 + (eta2/gamma1')(xhat2 - r2): relative to its largest operand
+            cond2 = max(1.0, h[k]["eta2"] / g1_ref * np.linalg.norm(h[k]["xhat2"] - h[k]["r2"]) /
+                        max(np.linalg.norm(r1_ref), 1e-300))
             errs = dict(xhat1=rel_vec(xh[k], h[k]["xhat1"]), eta1=rel_scalar(eta1[k], h[k]["eta1"]),
                         gamma2=rel_scalar(g2[k], h[k]["gamma2"]) / cond, r2=rel_vec(r2[k], h[k]["r2"]) / cond,
                         gamma2_raw=rel_scalar(g2[k], h[k]["gamma2"]), r2_raw=rel_vec(r2[k], h[k]["r2"]),
-                        r1=rel_vec(r1n[k], r1_ref), gamma1=rel_scalar(g1n[k], g1_ref), beta=rel_scalar(btn[k], b_ref),
+                        r1=rel_vec(r1n[k], r1_ref) / cond2, r1_raw=rel_vec(r1n[k], r1_ref),
+                        gamma1=rel_scalar(g1n[k], g1_ref), beta=rel_scalar(btn[k], b_ref),
                         fallback=float(bool(fb[k]) != bool(h[k]["fell_back"])))
             for key, v in errs.items():
                 worst[key] = max(worst.get(key, 0.0), v)
