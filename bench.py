@@ -29,9 +29,9 @@ METRIC = "weights quantized/sec per layer (T_vamp=16 + 3 CD sweeps), % of MFMA/H
 # MI355X published peaks
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-# Transcendental issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz at a
-# quarter of the fp32 VALU rate -> 9.83e12 exp/s.
-EXP_RATE = 256 * 4 * 16 * 2.4e9 / 4
+# Transcendental issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz at half
+# the fp32 VALU rate on gfx950 -> 19.66e12 exp/s (a throughput probe reads 18.4e12).
+EXP_RATE = 256 * 4 * 16 * 2.4e9 / 2
 LATTICE_FLOP_PER_EVAL = 36     # 2*8 (distance contraction) + 2*10 (weighted moments)
 SCALAR_FLOP_PER_EVAL = 8       # distance, scaled logit, three moment updates
 
@@ -75,6 +75,23 @@ def dominant_roofline(L, prof, steps):
                 launches=launches, avg_ms=ms / max(launches, 1))
 
 
+def measured_traffic(config, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or
+    None when there is none or the kernel's sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"counters_{config}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get("kernels", {}).get(kernel)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return rec["hbm_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
 def cpu_baseline(L, rows_count, gpu_codes):
     """Time the float64 oracle on `rows_count` rows of the layer, one worker
     process per row (each solves its row through the whole pipeline)."""
@@ -96,6 +113,25 @@ def cpu_baseline(L, rows_count, gpu_codes):
                 parity=dict(rows=len(rows), code_agreement=agree, obj_rel_max=obj_rel))
 
 
+def load_or_make(S, name, dev, cache):
+    """The named workload; with `cache`, arrays are saved there once and reloaded."""
+    import numpy as np
+    fields = ("W", "s", "V", "E", "a", "o")
+    path = os.path.join(cache, name) if cache else ""
+    if path and all(os.path.exists(os.path.join(path, f + ".npy")) for f in fields):
+        ref = S.make_config("c1")  # only for the scalar metadata of the Layer record
+        arr = {f: np.load(os.path.join(path, f + ".npy")) for f in fields}
+        spec = S.configs._SPECS[name]
+        return S.Layer(name, arr["W"], arr["s"], arr["V"], arr["E"], arr["a"], arr["o"], spec["d"],
+                       spec.get("T_vamp", 16), ref.n_cd, ref.damping)
+    L = S.make_config(name, device=dev)
+    if path:
+        os.makedirs(path, exist_ok=True)
+        for f in fields:
+            np.save(os.path.join(path, f + ".npy"), getattr(L, f))
+    return L
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,7 +140,21 @@ def main():
     ap.add_argument("--config", default="c5", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle rows for the CPU baseline (0: host cores, <=16)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cache", default="", help="directory for the generated inputs (reused when present)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 times), the reference kernel for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_calibration} MiB 5 times")
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the MPQ layer solve is single-GPU here "
               "(rows would shard across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
@@ -121,7 +171,7 @@ def main():
     dev = torch.device("cuda:0")
     mpq.load_library()
     t0 = time.perf_counter()
-    L = S.make_config(args.config, device=dev)
+    L = load_or_make(S, args.config, dev, args.cache)
     log(f"[bench] {args.config}: m={L.m} n={L.n} r={L.r} K={L.K} d={L.d} T={L.T_vamp} S={L.n_cd} "
         f"inputs in {time.perf_counter() - t0:.1f} s")
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
@@ -155,6 +205,7 @@ def main():
     log(f"[bench] kernel ms per step: {split}")
     roof = dominant_roofline(L, {k: v for k, v in timed_prof.items() if k in ("denoise", "linear1", "linear2")},
                              args.steps)
+    roof["traffic"] = measured_traffic(args.config, roof["kernel"])
     codes = out["codes"].cpu().numpy()
 
     cpu = None
