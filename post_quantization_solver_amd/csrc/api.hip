@@ -32,6 +32,7 @@ using namespace mpq;
 namespace {
 
 constexpr int KD = 256;          // CD tile width (columns)
+constexpr int MAX_SPLITK = 16;   // K chunks for the CD tile-gradient GEMM
 constexpr int LAT_CHUNK = 128;   // lattice codebook padding granularity
 constexpr size_t ALIGN = 256;
 
@@ -70,7 +71,7 @@ struct Layout {
 
 enum Region {
   R_VS, R_VST, R_YTIL, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI,
-  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_COUNT
+  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_SPLIT, R_COUNT
 };
 
 size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -110,6 +111,7 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
   sz[R_FLAG] = d == 8 ? (size_t)(64 + m * L.B) * sizeof(int32_t) : 0;
   sz[R_U64] = (size_t)m * r * f64;
   sz[R_D64] = (size_t)m * n * f64;
+  sz[R_SPLIT] = (size_t)MAX_SPLITK * m * KD * f64;
   size_t o = 0;
   for (int k = 0; k < R_COUNT; ++k) {
     L.off[k] = o;
@@ -450,9 +452,20 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
       const int64_t j0 = (int64_t)tl * KD;
       const int kw = (int)std::min<int64_t>(KD, L.n - j0);
       const double* Ht = Hd + (int64_t)tl * KD * KD;
-      TIMED(c, MPQ_PROF_CD_GEMM,
-            launch_gemm64(EPI_STORE, true, gemm64((int)L.m, kw, (int)L.r, U, L.r, c.p(R_VS) + j0 * L.r, L.r, Gt, kw),
-                          c.st));
+      {
+        // the tile gradient has few output tiles and a long K (= r): split K
+        // until the launch has about 512 workgroups
+        const int64_t out_tiles = (int64_t)gemm_col_tiles(kw) * ((L.m + GEMM_BM - 1) / GEMM_BM);
+        int splits = (int)std::min<int64_t>(MAX_SPLITK, std::max<int64_t>(1, 512 / std::max<int64_t>(out_tiles, 1)));
+        splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, L.r / 256));
+        Gemm64Args gg = gemm64((int)L.m, kw, (int)L.r, U, L.r, c.p(R_VS) + j0 * L.r, L.r, Gt, kw);
+        if (splits > 1) {
+          TIMED(c, MPQ_PROF_CD_GEMM,
+                launch_gemm64_splitk(EPI_STORE, gg, splits, reinterpret_cast<double*>(c.p(R_SPLIT)), c.st));
+        } else {
+          TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_STORE, true, gg, c.st));
+        }
+      }
       if (L.d == 1) {
         TIMED(c, MPQ_PROF_CD_SEARCH,
               launch_cd_scalar_tile(L.m, L.n, j0, kw, Gt, Ht, c.cb, a, o, codes, nullptr, Dl, chg, c.st));

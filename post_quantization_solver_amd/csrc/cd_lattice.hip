@@ -228,10 +228,22 @@ __global__ __launch_bounds__(256) void cd_update_kernel(int64_t m, int64_t n, in
   const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= m) return;
   const int64_t B = n / 8;
+  // top 2 over all slices: lane l takes slice l (of each group of 64), then a
+  // butterfly merge; the top two of a totally ordered set do not depend on
+  // the merge order
   Cand c1 = {INFINITY, 0x7fffffff}, c2 = {INFINITY, 0x7fffffff};
-  for (int sl = 0; sl < nslices; ++sl) {
-    Cand o1 = {part_s[(int64_t)sl * m + i], part_i[(int64_t)sl * m + i]};
-    Cand o2 = {part_s[((int64_t)nslices + sl) * m + i], part_i[((int64_t)nslices + sl) * m + i]};
+  for (int base = 0; base < nslices; base += 64) {
+    const int sl = base + lane;
+    Cand o1 = {INFINITY, 0x7fffffff}, o2 = {INFINITY, 0x7fffffff};
+    if (sl < nslices) {
+      o1 = {part_s[(int64_t)sl * m + i], part_i[(int64_t)sl * m + i]};
+      o2 = {part_s[((int64_t)nslices + sl) * m + i], part_i[((int64_t)nslices + sl) * m + i]};
+    }
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) {
+      Cand p1 = shfl_cand(o1, msk), p2 = shfl_cand(o2, msk);
+      merge_top2(o1, o2, p1, p2);
+    }
     merge_top2(c1, c2, o1, o2);
   }
   const int cx = codes[i * B + b];

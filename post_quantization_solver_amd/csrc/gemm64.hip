@@ -68,8 +68,13 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
   const int row0 = blockIdx.y * GEMM_BM;
   const int col0 = blockIdx.x * GEMM_BN;
   const int z = blockIdx.z;
-  const TA* A = reinterpret_cast<const TA*>(g.A) + (int64_t)z * g.sA;
-  const float* B = g.B + (int64_t)z * g.sB;
+  // split K: chunk z covers k in [z * kchunk, min(K, (z+1) * kchunk)) and
+  // writes its partial product to slice z of C (stride sC); otherwise z is the batch
+  const bool split = g.ksplit > 1;
+  const int kbeg = split ? z * g.kchunk : 0;
+  const int Kz = split ? min(g.K - kbeg, g.kchunk) : g.K;
+  const TA* A = reinterpret_cast<const TA*>(g.A) + (split ? (int64_t)kbeg : (int64_t)z * g.sA);
+  const float* B = g.B + (split ? (int64_t)kbeg : (int64_t)z * g.sB);
   double* C = g.C + (int64_t)z * g.sC;
 
   v4d acc[4][4];
@@ -78,18 +83,18 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (v4d){0.0, 0.0, 0.0, 0.0};
 
-  const int nk = (g.K + BK64 - 1) / BK64;
+  const int nk = (Kz + BK64 - 1) / BK64;
   double ra[2][4], rb[2][4];
-  load_tile64<TA, VEC>(A, g.lda, g.M, g.K, row0, 0, t, ra);
-  load_tile64<float, VEC>(B, g.ldb, g.N, g.K, col0, 0, t, rb);
+  load_tile64<TA, VEC>(A, g.lda, g.M, Kz, row0, 0, t, ra);
+  load_tile64<float, VEC>(B, g.ldb, g.N, Kz, col0, 0, t, rb);
   store_tile64(As[0], t, ra);
   store_tile64(Bs[0], t, rb);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) {
-      load_tile64<TA, VEC>(A, g.lda, g.M, g.K, row0, (kt + 1) * BK64, t, ra);
-      load_tile64<float, VEC>(B, g.ldb, g.N, g.K, col0, (kt + 1) * BK64, t, rb);
+      load_tile64<TA, VEC>(A, g.lda, g.M, Kz, row0, (kt + 1) * BK64, t, ra);
+      load_tile64<float, VEC>(B, g.ldb, g.N, Kz, col0, (kt + 1) * BK64, t, rb);
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -130,16 +135,59 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
     }
 }
 
+// Sum of the split-K slices in slice order: C[i][j] (=, -=) sum_z P[z][i][j].
+template <int EPI>
+__global__ void splitk_reduce_kernel(const double* __restrict__ P, int64_t slice, int splits, int M, int N,
+                                     double* __restrict__ C, int64_t ldc) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= (int64_t)M * N) return;
+  int64_t i = k / N, j = k - i * N;
+  double acc = 0.0;
+  for (int z = 0; z < splits; ++z) acc += P[(int64_t)z * slice + k];
+  double* cp = C + i * ldc + j;
+  if (EPI == EPI_STORE)
+    *cp = acc;
+  else
+    *cp = *cp - acc;
+}
+
 template <typename TA, int EPI>
 static hipError_t launch64(const Gemm64Args& g, hipStream_t st) {
   dim3 grid(gemm_col_tiles(g.N), (g.M + GEMM_BM - 1) / GEMM_BM, g.batch > 0 ? g.batch : 1);
+  if (g.ksplit > 1) grid.z = g.ksplit;
   const size_t ea = sizeof(TA);
   bool vec = (g.K % 4 == 0) && (g.lda % 4 == 0) && (g.ldb % 4 == 0) && (g.sA % 4 == 0) && (g.sB % 4 == 0) &&
              ((reinterpret_cast<uintptr_t>(g.A) % (4 * ea)) == 0) && ((reinterpret_cast<uintptr_t>(g.B) & 15) == 0);
+  if (g.ksplit > 1) vec = vec && (g.kchunk % 4 == 0);
   if (vec)
     hipLaunchKernelGGL((gemm64_nt_kernel<TA, EPI, true>), grid, dim3(256), 0, st, g);
   else
     hipLaunchKernelGGL((gemm64_nt_kernel<TA, EPI, false>), grid, dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+// C (=, -=) A B^T with K split into `splits` chunks written to `part`
+// (splits x M x N doubles) and summed in a fixed order: fills the GPU when
+// M x N has few tiles and K is long.
+hipError_t launch_gemm64_splitk(int epi, const Gemm64Args& g0, int splits, double* part, hipStream_t st) {
+  if (g0.M <= 0 || g0.N <= 0) return hipSuccess;
+  Gemm64Args g = g0;
+  g.batch = 1;
+  g.ksplit = splits;
+  g.kchunk = ((g0.K + splits - 1) / splits + 15) / 16 * 16;
+  g.C = part;
+  g.ldc = g0.N;
+  g.sC = (int64_t)g0.M * g0.N;
+  hipError_t e = launch64<double, EPI_STORE>(g, st);
+  if (e != hipSuccess) return e;
+  int64_t total = (int64_t)g0.M * g0.N;
+  dim3 grid((unsigned)((total + 255) / 256));
+  if (epi == EPI_STORE)
+    hipLaunchKernelGGL((splitk_reduce_kernel<EPI_STORE>), grid, dim3(256), 0, st, part, g.sC, splits, g0.M, g0.N,
+                       g0.C, g0.ldc);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<EPI_SUB_INPLACE>), grid, dim3(256), 0, st, part, g.sC, splits, g0.M,
+                       g0.N, g0.C, g0.ldc);
   return hipGetLastError();
 }
 

@@ -42,8 +42,11 @@ struct Gemm64Args {
   const float* B; int64_t ldb; int64_t sB;
   double* C; int64_t ldc; int64_t sC;
   int batch;
+  int ksplit, kchunk;   // split-K (set by launch_gemm64_splitk)
 };
 hipError_t launch_gemm64(int epi, bool a_is_f64, const Gemm64Args& g, hipStream_t st);
+// A float64, split K into `splits` chunks through `part` (splits * M * N doubles).
+hipError_t launch_gemm64_splitk(int epi, const Gemm64Args& g, int splits, double* part, hipStream_t st);
 
 // ------------------------------------------------------------ codebook ----
 // Device tables derived from the host codebook.
