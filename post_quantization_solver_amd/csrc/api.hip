@@ -71,7 +71,7 @@ struct Layout {
 
 enum Region {
   R_VS, R_VST, R_YTIL, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI,
-  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_SPLIT, R_COUNT
+  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_SPLIT, R_TKEY, R_QF, R_COUNT
 };
 
 size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -112,6 +112,8 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
   sz[R_U64] = (size_t)m * r * f64;
   sz[R_D64] = (size_t)m * n * f64;
   sz[R_SPLIT] = (size_t)MAX_SPLITK * m * KD * f64;
+  sz[R_TKEY] = d == 8 ? (size_t)(KD / 8) * L.Kpad * 4 * sizeof(uint32_t) : 0;
+  sz[R_QF] = d == 8 ? (size_t)m * 16 * sizeof(uint32_t) : 0;
   size_t o = 0;
   for (int k = 0; k < R_COUNT; ++k) {
     L.off[k] = o;
@@ -470,10 +472,12 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
         TIMED(c, MPQ_PROF_CD_SEARCH,
               launch_cd_scalar_tile(L.m, L.n, j0, kw, Gt, Ht, c.cb, a, o, codes, nullptr, Dl, chg, c.st));
       } else {
+        uint32_t* tk = reinterpret_cast<uint32_t*>(c.p(R_TKEY));
+        TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_lattice_tkeys(kw / 8, kw, Ht, c.cb, tk, c.st));
         for (int bl = 0; bl < kw / 8; ++bl) {
           TIMED(c, MPQ_PROF_CD_SEARCH,
-                launch_cd_lattice_block(L.m, L.n, j0 / 8 + bl, bl, kw, Gt, Ht, c.cb, a, codes, Dl, chg, c.p(R_PS),
-                                        c.pi(R_PI), c.st));
+                launch_cd_lattice_block(L.m, L.n, j0 / 8 + bl, bl, kw, Gt, Ht, tk, c.cb, a, codes, Dl, chg,
+                                        c.p(R_PS), c.pi(R_PI), reinterpret_cast<uint32_t*>(c.p(R_QF)), c.st));
         }
       }
       TIMED(c, MPQ_PROF_CD_GEMM,

@@ -92,9 +92,15 @@ hipError_t launch_cd_scalar_tile(int64_t m, int64_t n, int64_t j0, int kd, const
                                  const CbTables& cb, const float* a, const float* o, int32_t* codes,
                                  float* X, double* Delta, int32_t* changes, hipStream_t st);
 // CD (d = 8): one block of a tile (scoring over codeword slices, then the move).
+// tk: the tile's score-key table, nb blocks x Kpad x 4 words (written by
+// launch_cd_lattice_tkeys once per tile); qf: m x 16 words of per-row query
+// fragments, passed from each block's update to the next block's scoring.
+hipError_t launch_cd_lattice_tkeys(int nb, int kd, const double* Ht, const CbTables& cb, uint32_t* tk,
+                                   hipStream_t st);
 hipError_t launch_cd_lattice_block(int64_t m, int64_t n, int64_t b, int bl, int kd, double* Gt, const double* Ht,
-                                   const CbTables& cb, const float* a, int32_t* codes, double* Delta,
-                                   int32_t* changes, float* part_s, int32_t* part_i, hipStream_t st);
+                                   const uint32_t* tk, const CbTables& cb, const float* a, int32_t* codes,
+                                   double* Delta, int32_t* changes, float* part_s, int32_t* part_i, uint32_t* qf,
+                                   hipStream_t st);
 int cd_lattice_slices(int Kpad);
 
 }  // namespace mpq

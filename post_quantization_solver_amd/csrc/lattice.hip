@@ -19,6 +19,8 @@
 // 8 (log2), so p = 2^S' stays in (0, 2^8] without per-tile rescaling.
 // The weighted sums  sum p e, sum p ||e||^2, sum p  come from a second MFMA
 // against [e | ||e||^2 (hi, mid, lo) | 1], with p split into bf16 hi + lo.
+// Both MFMAs see the same rounded weights hi + lo, so the normalized sums are
+// weighted means with weights within about 2^-17 of p.
 #include <math.h>
 #include "mpq_device.h"
 #include "internal.h"
@@ -94,13 +96,27 @@ __device__ __forceinline__ float max8(const v4f& a, const v4f& b) {
   return fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
 }
 
-// p -> (hi, lo) bfloat16 pair words.  hi truncates p to its top 16 bits; lo
-// rounds the exact remainder p - hi to bfloat16.
-__device__ __forceinline__ void split_p(float p0, float p1, uint32_t& hw, uint32_t& lw) {
-  uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
-  hw = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-  float l0 = p0 - __uint_as_float(b0 & 0xffff0000u);
-  float l1 = p1 - __uint_as_float(b1 & 0xffff0000u);
+// The bf16 pairs (-1, 0) and (0, -1) as 32-bit words held in VGPRs.  They
+// are moved in as literals: the compiler would otherwise encode (-1, 0) as the
+// inline constant -1.0, which v_dot2c_f32_bf16 does not read as that pair.
+struct DotMasks {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ DotMasks dot_masks() {
+  DotMasks d;
+  asm volatile("v_mov_b32 %0, 0xbf80" : "=v"(d.lo));
+  asm volatile("v_mov_b32 %0, 0xbf800000" : "=v"(d.hi));
+  return d;
+}
+
+// p -> (hi, lo) bfloat16 pair words: hi rounds p to nearest bfloat16 and lo
+// rounds the remainder p - hi, which is exact in float32 and is formed by one
+// v_dot2_f32_bf16 each ((-1) hi + 0 + p).  p = hi + lo to about 2^-17.
+__device__ __forceinline__ void split_p(float p0, float p1, const DotMasks& dm, uint32_t& hw, uint32_t& lw) {
+  const v2bf h = {(__bf16)p0, (__bf16)p1};
+  const float l0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(v2bf, dm.lo), p0, false);
+  const float l1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(v2bf, dm.hi), p1, false);
+  hw = __builtin_bit_cast(uint32_t, h);
   lw = f2bf_pack(l0, l1);
 }
 
@@ -209,6 +225,7 @@ __global__ __launch_bounds__(256) void denoise_lattice_kernel(
     tot[q] = (v4f){0.f, 0.f, 0.f, 0.f};
   }
 
+  const DotMasks dm = dot_masks();
   const int nchunks = Kpad / LAT_CH;
   load_chunk<true>(lds_key[0], lds_pv[0], keys, pvops, 0, t);
   __syncthreads();
@@ -252,10 +269,10 @@ __global__ __launch_bounds__(256) void denoise_lattice_kernel(
           p[4 + v] = __builtin_amdgcn_exp2f(s1[v]);
         }
         uint32_t h0w, h1w, h2w, h3w, l0w, l1w, l2w, l3w;
-        split_p(p[0], p[1], h0w, l0w);
-        split_p(p[2], p[3], h1w, l1w);
-        split_p(p[4], p[5], h2w, l2w);
-        split_p(p[6], p[7], h3w, l3w);
+        split_p(p[0], p[1], dm, h0w, l0w);
+        split_p(p[2], p[3], dm, h1w, l1w);
+        split_p(p[4], p[5], dm, h2w, l2w);
+        split_p(p[6], p[7], dm, h3w, l3w);
         v4u hi = {h0w, h1w, h2w, h3w};
         v4u lo = {l0w, l1w, l2w, l3w};
         acc[q] = mfma_bf16_16x16x32(pv, hi, acc[q]);

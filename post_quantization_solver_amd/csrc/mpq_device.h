@@ -38,6 +38,12 @@ __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return
 // Cross-lane helpers (full wave64).
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 __device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, 64); }
+__device__ __forceinline__ uint32_t shfl_i(uint32_t v, int src) { return (uint32_t)__shfl((int)v, src, 64); }
+__device__ __forceinline__ double shfl_d(double v, int src) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = shfl_i((uint32_t)u, src), hi = shfl_i((uint32_t)(u >> 32), src);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
 
 // MFMA wrappers.  16x16 output layout (all dtypes): lane l holds rows
 // 4*(l/16) + v (v = 0..3) of column l % 16.
