@@ -67,6 +67,32 @@ __device__ __forceinline__ void load_chunk(uint32_t* __restrict__ lds_key, uint3
   }
 }
 
+// Register-staged copy of one chunk (keys and PV operands): fetch_chunk
+// issues the global loads, store_chunk writes them to LDS later, so the load
+// latency overlaps the scoring of the previous chunk.
+constexpr int LAT_KEY_V4 = LAT_KEY_WORDS / 4 / 256;   // v4u per thread
+constexpr int LAT_PV_V4 = LAT_PV_WORDS / 4 / 256;
+static_assert(LAT_KEY_WORDS % 1024 == 0 && LAT_PV_WORDS % 1024 == 0, "chunk not a multiple of the workgroup");
+struct ChunkRegs {
+  v4u k[LAT_KEY_V4], p[LAT_PV_V4];
+};
+__device__ __forceinline__ void fetch_chunk(ChunkRegs& r, const uint32_t* __restrict__ keys,
+                                            const uint32_t* __restrict__ pv, int64_t chunk, int t) {
+  const v4u* sk = reinterpret_cast<const v4u*>(keys + chunk * LAT_KEY_WORDS);
+  const v4u* sp = reinterpret_cast<const v4u*>(pv + chunk * LAT_PV_WORDS);
+#pragma unroll
+  for (int k = 0; k < LAT_KEY_V4; ++k) r.k[k] = sk[t + 256 * k];
+#pragma unroll
+  for (int k = 0; k < LAT_PV_V4; ++k) r.p[k] = sp[t + 256 * k];
+}
+__device__ __forceinline__ void store_chunk(uint32_t* __restrict__ lds_key, uint32_t* __restrict__ lds_pv,
+                                            const ChunkRegs& r, int t) {
+#pragma unroll
+  for (int k = 0; k < LAT_KEY_V4; ++k) reinterpret_cast<v4u*>(lds_key)[t + 256 * k] = r.k[k];
+#pragma unroll
+  for (int k = 0; k < LAT_PV_V4; ++k) reinterpret_cast<v4u*>(lds_pv)[t + 256 * k] = r.p[k];
+}
+
 // Build the lane's query operand.  Lane (j, g): group g = 0, 1, 2 carries the
 // hi / mid / lo bf16 terms of qv[0..7]; group 3 carries [k hi, mid, lo, M hi, mid, lo, 0, 0].
 __device__ __forceinline__ v4u make_query(const float (&qv)[8], float kap, float M, int g) {
@@ -133,14 +159,23 @@ __device__ __forceinline__ void split_p(float p0, float p1, const DotMasks& dm, 
 // Each query's result depends only on its own inputs, so the order of the
 // list does not change any output bit.
 template <bool ONLINE>
-__global__ __launch_bounds__(256) void denoise_lattice_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 : 5))) void denoise_lattice_kernel(
     const float* __restrict__ R1, const float* __restrict__ gamma1, int64_t m, int64_t n,
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ pvops, const float* __restrict__ e32,
     int Kpad, const float* __restrict__ a, const float* __restrict__ o, float* __restrict__ xhat,
     float* __restrict__ vblk, int32_t* __restrict__ flag_list, int32_t* __restrict__ flag_count) {
-  __shared__ __attribute__((aligned(16))) uint32_t lds_key[2][LAT_KEY_WORDS];
-  __shared__ __attribute__((aligned(16))) uint32_t lds_pv[2][LAT_PV_WORDS];
-  __shared__ float fin[LAT_QWG][13];
+  // codebook chunks (double-buffered) while scoring; per-query sums after
+  union Smem {
+    struct {
+      uint32_t key[2][LAT_KEY_WORDS];
+      uint32_t pv[2][LAT_PV_WORDS];
+    } ch;
+    float fin[LAT_QWG][13];
+  };
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  auto& lds_key = sm.ch.key;
+  auto& lds_pv = sm.ch.pv;
+  auto& fin = sm.fin;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -216,8 +251,9 @@ __global__ __launch_bounds__(256) void denoise_lattice_kernel(
   }
 
   // acc: this chunk's sums (the MFMAs accumulate at most 2 * LAT_CH / 32
-  // products into it); tot: running total, updated by one float32 add per
-  // chunk so long accumulations round to nearest at every step.
+  // products into it, starting from zero at the chunk's first step); tot:
+  // running total, updated by one float32 add per chunk so long
+  // accumulations round to nearest at every step.
   v4f acc[LAT_QSUB], tot[LAT_QSUB];
 #pragma unroll
   for (int q = 0; q < LAT_QSUB; ++q) {
@@ -227,15 +263,17 @@ __global__ __launch_bounds__(256) void denoise_lattice_kernel(
 
   const DotMasks dm = dot_masks();
   const int nchunks = Kpad / LAT_CH;
-  load_chunk<true>(lds_key[0], lds_pv[0], keys, pvops, 0, t);
+  ChunkRegs pre;
+  fetch_chunk(pre, keys, pvops, 0, t);
+  store_chunk(lds_key[0], lds_pv[0], pre, t);
   __syncthreads();
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
   for (int c = 0; c < nchunks; ++c) {
     const int cur = c & 1;
-    if (c + 1 < nchunks) load_chunk<true>(lds_key[cur ^ 1], lds_pv[cur ^ 1], keys, pvops, c + 1, t);
+    if (c + 1 < nchunks) fetch_chunk(pre, keys, pvops, c + 1, t);
     const v4u* kq = reinterpret_cast<const v4u*>(lds_key[cur]);
     const v4u* pq = reinterpret_cast<const v4u*>(lds_pv[cur]);
-#pragma unroll 1
+#pragma unroll
     for (int st = 0; st < LAT_CH / 32; ++st) {
       const v4u k0 = kq[(2 * st) * 64 + lane];
       const v4u k1 = kq[(2 * st + 1) * 64 + lane];
@@ -275,15 +313,14 @@ __global__ __launch_bounds__(256) void denoise_lattice_kernel(
         split_p(p[6], p[7], dm, h3w, l3w);
         v4u hi = {h0w, h1w, h2w, h3w};
         v4u lo = {l0w, l1w, l2w, l3w};
-        acc[q] = mfma_bf16_16x16x32(pv, hi, acc[q]);
+        acc[q] = mfma_bf16_16x16x32(pv, hi, st == 0 ? zero4 : acc[q]);
         acc[q] = mfma_bf16_16x16x32(pv, lo, acc[q]);
       }
     }
 #pragma unroll
-    for (int q = 0; q < LAT_QSUB; ++q) {
-      tot[q] += acc[q];
-      acc[q] = zero4;
-    }
+    for (int q = 0; q < LAT_QSUB; ++q) tot[q] += acc[q];
+    // the other buffer was last read in chunk c - 1, before the previous barrier
+    if (c + 1 < nchunks) store_chunk(lds_key[cur ^ 1], lds_pv[cur ^ 1], pre, t);
     __syncthreads();
   }
 
