@@ -28,11 +28,13 @@ METRIC = "weights quantized/sec per layer (T_vamp=16 + 3 CD sweeps), % of MFMA/H
 
 # MI355X published peaks
 PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 # Transcendental issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz at half
 # the fp32 VALU rate on gfx950 -> 19.66e12 exp/s (a throughput probe reads 18.4e12).
 EXP_RATE = 256 * 4 * 16 * 2.4e9 / 2
 LATTICE_FLOP_PER_EVAL = 36     # 2*8 (distance contraction) + 2*10 (weighted moments)
+LATTICE_MFMA_FLOP_PER_EVAL = 128   # bf16 MFMA flops the lattice denoiser issues per eval
 SCALAR_FLOP_PER_EVAL = 8       # distance, scaled logit, three moment updates
 
 WORKLOADS = {
@@ -63,8 +65,15 @@ def dominant_roofline(L, prof, steps):
             flops = evals * SCALAR_FLOP_PER_EVAL
             peak = SCALAR_FLOP_PER_EVAL * EXP_RATE / 1e12
         achieved = flops / per_launch_s / 1e12
-        return dict(kernel="denoise", bound="alu", achieved=achieved, peak=peak, unit="TFLOP/s",
-                    frac=achieved / peak, traffic=None, launches=launches, avg_ms=ms / max(launches, 1))
+        out = dict(kernel="denoise", bound="alu", achieved=achieved, peak=peak, unit="TFLOP/s",
+                   frac=achieved / peak, traffic=None, launches=launches, avg_ms=ms / max(launches, 1))
+        if d == 8:
+            # the same launch against the bf16 matrix cores: per 16 queries x 32 codewords
+            # it issues two score and two weighted-sum 16x16x32 MFMAs (128 flops per eval)
+            mf = evals * LATTICE_MFMA_FLOP_PER_EVAL / per_launch_s / 1e12
+            out["secondary"] = dict(bound="mfma", achieved=mf, peak=PEAK_BF16_MFMA_TFLOPS, unit="TFLOP/s",
+                                    frac=mf / PEAK_BF16_MFMA_TFLOPS)
+        return out
     if best in ("linear1", "linear2"):
         flops = 2.0 * m * n * r
         achieved = flops / per_launch_s / 1e12
@@ -141,6 +150,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle rows for the CPU baseline (0: host cores, <=16)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cache", default="", help="directory for the generated inputs (reused when present)")
+    ap.add_argument("--n-cd", type=int, default=None,
+                    help="CD sweeps (default: the workload's 3); 0 runs only the prologue, VAMP and MAP, e.g. for "
+                         "counter passes over the VAMP kernels")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), the reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -172,6 +184,8 @@ def main():
     mpq.load_library()
     t0 = time.perf_counter()
     L = load_or_make(S, args.config, dev, args.cache)
+    if args.n_cd is not None:
+        L.n_cd = args.n_cd
     log(f"[bench] {args.config}: m={L.m} n={L.n} r={L.r} K={L.K} d={L.d} T={L.T_vamp} S={L.n_cd} "
         f"inputs in {time.perf_counter() - t0:.1f} s")
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
@@ -222,7 +236,8 @@ def main():
                             d=L.d, T_vamp=L.T_vamp, n_cd=L.n_cd, damping=L.damping),
                 roofline=dict(bound=roof["bound"], achieved=roof["achieved"], peak=roof["peak"], unit=roof["unit"],
                               frac=roof["frac"], traffic=roof["traffic"], kernel=roof["kernel"],
-                              avg_launch_ms=roof["avg_ms"], launches=roof["launches"]),
+                              avg_launch_ms=roof["avg_ms"], launches=roof["launches"],
+                              **({"secondary": roof["secondary"]} if "secondary" in roof else {})),
                 kernel_ms_per_step=split, cpu_baseline=cpu)
     print(json.dumps(line), flush=True)
 

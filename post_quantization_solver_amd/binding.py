@@ -34,7 +34,7 @@ class MPQError(RuntimeError):
 
 F_PROFILE = 2
 PROF_NAMES = ("prologue", "denoise", "extrinsic", "linear1", "beta", "linear2", "map", "cd_gemm", "cd_search",
-              "other")
+              "other", "denoise_exact")
 PROF_COUNT = len(PROF_NAMES)
 
 

@@ -20,6 +20,8 @@ hipError_t launch_nearest_scalar(const float*, int64_t, int64_t, const CbTables&
                                  int32_t*, hipStream_t);
 hipError_t launch_denoise_lattice(const float*, const float*, int64_t, int64_t, const CbTables&, const float*,
                                   const float*, float*, float*, int32_t*, hipStream_t);
+hipError_t launch_denoise_lattice_exact(const float*, const float*, int64_t, int64_t, const CbTables&,
+                                        const float*, const float*, float*, float*, int32_t*, hipStream_t);
 hipError_t launch_nearest_lattice(const float*, int64_t, int64_t, const CbTables&, const float*, const float*,
                                   int32_t*, hipStream_t);
 hipError_t launch_beta_lin(int64_t, const float*, const float*, float*, float*, hipStream_t);
@@ -327,10 +329,16 @@ hipError_t nearest(const Ctx& c, const float* R, int32_t* codes, const float* a,
   return launch_nearest_lattice(R, c.L.m, c.L.n, c.cb, a, o, codes, c.st);
 }
 
-hipError_t denoise(const Ctx& c, const float* R1, const float* gamma1, const float* a, const float* o, float* xhat,
-                   float* vblk) {
-  if (c.L.d == 1) return launch_denoise_scalar(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.st);
-  return launch_denoise_lattice(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.pi(R_FLAG), c.st);
+int denoise(Ctx& c, const float* R1, const float* gamma1, const float* a, const float* o, float* xhat, float* vblk) {
+  if (c.L.d == 1) {
+    TIMED(c, MPQ_PROF_DENOISE, launch_denoise_scalar(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.st));
+    return MPQ_OK;
+  }
+  TIMED(c, MPQ_PROF_DENOISE,
+        launch_denoise_lattice(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.pi(R_FLAG), c.st));
+  TIMED(c, MPQ_PROF_DENOISE_EXACT,
+        launch_denoise_lattice_exact(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.pi(R_FLAG), c.st));
+  return MPQ_OK;
 }
 
 int prepare_factors(Ctx& c, const float* V, const float* s) {
@@ -378,7 +386,8 @@ int run_iteration(Ctx& c, float* R1, float* gamma1, float* beta, const float* yt
   const Layout& L = c.L;
   float* X1 = c.p(R_X1);
   float* R2 = c.p(R_R2);
-  TIMED(c, MPQ_PROF_DENOISE, denoise(c, R1, gamma1, a, o, X1, c.p(R_VBLK)));
+  int rc = denoise(c, R1, gamma1, a, o, X1, c.p(R_VBLK));
+  if (rc) return rc;
   if (xhat_out) TIMED(c, MPQ_PROF_OTHER, launch_copy_rows_f(X1, xhat_out, L.m * L.n, c.st));
   TIMED(c, MPQ_PROF_EXTRINSIC,
         launch_extrinsic(R1, X1, c.p(R_VBLK), L.m, L.n, L.B, a, gamma1, R2, c.gamma2(),
@@ -617,8 +626,7 @@ int mpq_denoise(const float* R1, const float* gamma1, int64_t m, int64_t n, cons
   rc = begin(c, m, n, 1, K, d, cb, workspace, ws_bytes, stream);
   if (rc) return rc;
   if ((rc = upload_codebook(c, cb))) return rc;
-  MPQ_TRY(denoise(c, R1, gamma1, row_scale, row_offset, xhat1, vtrace));
-  return MPQ_OK;
+  return denoise(c, R1, gamma1, row_scale, row_offset, xhat1, vtrace);
 }
 
 int mpq_vamp_step(float* R1, float* gamma1, float* beta, const float* ytil, int64_t m, int64_t n, const float* s,

@@ -444,7 +444,9 @@ __global__ __launch_bounds__(256) void nearest_lattice_kernel(const float* __res
   }
 }
 
-// flag: two int32 words of scratch (count) followed by room for m * n / 8 query indices.
+// flag: 64 int32 words of scratch (count first) followed by room for
+// m * n / 8 query indices.  The fast pass scores every query and lists those
+// it cannot resolve; launch_denoise_lattice_exact redoes the listed ones.
 hipError_t launch_denoise_lattice(const float* R1, const float* gamma1, int64_t m, int64_t n, const CbTables& cb,
                                   const float* a, const float* o, float* xhat, float* vblk, int32_t* flag,
                                   hipStream_t st) {
@@ -457,11 +459,19 @@ hipError_t launch_denoise_lattice(const float* R1, const float* gamma1, int64_t 
   dim3 grid((unsigned)((total + LAT_QWG - 1) / LAT_QWG));
   hipLaunchKernelGGL((denoise_lattice_kernel<false>), grid, dim3(256), 0, st, R1, gamma1, m, n, cb.qk_keys, cb.pv_ops,
                      cb.e32, cb.Kpad, a, o, xhat, vblk, list, count);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // flagged queries: the exact online-maximum pass; surplus workgroups exit at once
+  return hipGetLastError();
+}
+
+// The flagged queries with the exact online-maximum pass; the grid covers
+// every query and surplus workgroups exit at once.
+hipError_t launch_denoise_lattice_exact(const float* R1, const float* gamma1, int64_t m, int64_t n,
+                                        const CbTables& cb, const float* a, const float* o, float* xhat, float* vblk,
+                                        int32_t* flag, hipStream_t st) {
+  int64_t total = m * (n / 8);
+  if (total <= 0) return hipSuccess;
+  dim3 grid((unsigned)((total + LAT_QWG - 1) / LAT_QWG));
   hipLaunchKernelGGL((denoise_lattice_kernel<true>), grid, dim3(256), 0, st, R1, gamma1, m, n, cb.qk_keys, cb.pv_ops,
-                     cb.e32, cb.Kpad, a, o, xhat, vblk, list, count);
+                     cb.e32, cb.Kpad, a, o, xhat, vblk, flag + 64, flag);
   return hipGetLastError();
 }
 
