@@ -1,25 +1,37 @@
-// Float32 GEMM on the CDNA4 fp32 matrix cores with the MPQ epilogues fused.
+// Float32 GEMM with the MPQ epilogues fused, on the bf16 matrix cores.
 //
 //   C[M x N] = A[M x K] * B[N x K]^T      (both operands K-contiguous)
 //
 // Every product in the solver is written in this "NT" form by keeping both
 // VS = V diag(s) (n x r) and its transpose in the workspace, so a single
-// kernel covers the rank-space projections of the linear module, the
-// prologue, and the CD gradient / residual updates.
+// kernel covers the rank-space projections of the linear module and the
+// prologue.
+//
+// Precision: each float32 operand is split exactly into three bfloat16 terms
+// x = h + m + l (h rounds x, m rounds x - h, l rounds x - h - m; the
+// remainders are formed exactly with v_dot2_f32_bf16), and the product keeps
+// the six cross terms down to 2^-16 relative, hh + hm + mh + hl + lh + mm,
+// accumulated in float32 by the MFMA: a float32-accurate product at the bf16
+// matrix-core rate (six bf16 products cost 96 cycles per 16 x 16 x 32 block
+// against 256 for the same block on v_mfma_f32_16x16x4_f32).
 //
 // Tiling: 256 threads (4 waves) per 128 x 128 tile, K staged through LDS in
-// slices of 16 (double-buffered).  Each wave owns a 64 x 64 sub-tile made of
-// 4 x 4 v_mfma_f32_16x16x4_f32 accumulators.  Within a K slice lane (i, g)
-// (i = lane % 16, g = lane / 16) reads A[i][4g .. 4g+3] and B[j][4g .. 4g+3]
-// as one 16-byte LDS load; MFMA step kk consumes component kk, so the four
-// steps together cover all 16 k of the slice.
+// slices of 16 (double-buffered; the split happens once, when a slice is
+// written to LDS).  Each wave owns a 64 x 64 sub-tile of 4 x 4
+// v_mfma_f32_16x16x32_bf16 accumulators.  An MFMA's 32 K-slots carry two
+// products over the same 16 k: lanes g = 0, 1 (slots 0..15) one term pair,
+// lanes g = 2, 3 (slots 16..31) another, k = 8 (g & 1) + 0..7 in both halves:
+//     MFMA 1: A [h | m] x B [h | h]  ->  hh + mh
+//     MFMA 2: A [h | m] x B [m | m]  ->  hm + mm
+//     MFMA 3: A [h | l] x B [l | h]  ->  hl + lh
+// LDS layout per operand and buffer: [term][k half][row][8 bf16], so a
+// fragment is one conflict-free 16-byte read per lane.
 #include "mpq_device.h"
 #include "internal.h"
 
 namespace mpq {
 
 constexpr int BK = 16;
-constexpr int LDS_STRIDE = BK + 4;  // floats per LDS row (padding against bank conflicts)
 
 template <bool VEC>
 __device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t ld, int rows, int K,
@@ -44,18 +56,42 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t l
   }
 }
 
-__device__ __forceinline__ void store_tile(float* lds, int t, const float4 (&reg)[2]) {
+// LDS words (uint32) of one operand slice: 3 terms x 2 k halves x 128 rows x 4 words
+constexpr int SPLIT_WORDS = 3 * 2 * 128 * 4;
+
+__device__ __forceinline__ int split_word(int term, int khalf, int row) { return ((term * 2 + khalf) * 128 + row) * 4; }
+
+// Split the thread's two float4 (rows t/4 and t/4 + 64, k quad t % 4) into
+// the three bf16 terms and write them to one LDS slice.
+__device__ __forceinline__ void store_split(uint32_t* lds, int t, const float4 (&reg)[2], const DotMasks& dm) {
+  const int q = t & 3;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    int rr = (t >> 2) + h * 64;
-    *reinterpret_cast<float4*>(lds + rr * LDS_STRIDE + (t & 3) * 4) = reg[h];
+    const int rr = (t >> 2) + h * 64;
+    const float x[4] = {reg[h].x, reg[h].y, reg[h].z, reg[h].w};
+    uint32_t th[2], tm[2], tl[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      th[p] = f2bf_pack(x[2 * p], x[2 * p + 1]);
+      const float r0 = sub_bf16_lo(x[2 * p], th[p], dm), r1 = sub_bf16_hi(x[2 * p + 1], th[p], dm);
+      tm[p] = f2bf_pack(r0, r1);
+      tl[p] = f2bf_pack(sub_bf16_lo(r0, tm[p], dm), sub_bf16_hi(r1, tm[p], dm));
+    }
+    const int off = (q & 1) * 2;
+    *reinterpret_cast<uint2*>(lds + split_word(0, q >> 1, rr) + off) = make_uint2(th[0], th[1]);
+    *reinterpret_cast<uint2*>(lds + split_word(1, q >> 1, rr) + off) = make_uint2(tm[0], tm[1]);
+    *reinterpret_cast<uint2*>(lds + split_word(2, q >> 1, rr) + off) = make_uint2(tl[0], tl[1]);
   }
+}
+
+__device__ __forceinline__ v4u split_frag(const uint32_t* lds, int term, int khalf, int row) {
+  return *reinterpret_cast<const v4u*>(lds + split_word(term, khalf, row));
 }
 
 template <int EPI, bool VEC>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) float As[2][GEMM_BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) float Bs[2][GEMM_BN * LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint32_t As[2][SPLIT_WORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t Bs[2][SPLIT_WORDS];
   __shared__ float red[2][GEMM_BM];
 
   const int t = threadIdx.x;
@@ -82,39 +118,47 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
+  const DotMasks dm = dot_masks();
   const int nk = (g.K + BK - 1) / BK;
   float4 ra[2], rb[2];
   load_tile<VEC>(A, g.lda, g.M, g.K, row0, 0, t, ra);
   load_tile<VEC>(B, g.ldb, g.N, g.K, col0, 0, t, rb);
-  store_tile(As[0], t, ra);
-  store_tile(Bs[0], t, rb);
+  store_split(As[0], t, ra, dm);
+  store_split(Bs[0], t, rb, dm);
   __syncthreads();
 
+  // the lane's terms: A [h | m], A [h | l]; B h, m, [l | h]
+  const int kh = lg & 1;
+  const int ta1 = lg < 2 ? 0 : 1, ta3 = lg < 2 ? 0 : 2, tb3 = lg < 2 ? 2 : 0;
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) {
       load_tile<VEC>(A, g.lda, g.M, g.K, row0, (kt + 1) * BK, t, ra);
       load_tile<VEC>(B, g.ldb, g.N, g.K, col0, (kt + 1) * BK, t, rb);
     }
-    float4 af[4], bf[4];
+    v4u b1[4], b2[4], b3[4];
 #pragma unroll
-    for (int si = 0; si < 4; ++si)
-      af[si] = *reinterpret_cast<const float4*>(&As[cur][(wr + si * 16 + li) * LDS_STRIDE + lg * 4]);
+    for (int sj = 0; sj < 4; ++sj) {
+      const int rowb = wc + sj * 16 + li;
+      b1[sj] = split_frag(Bs[cur], 0, kh, rowb);
+      b2[sj] = split_frag(Bs[cur], 1, kh, rowb);
+      b3[sj] = split_frag(Bs[cur], tb3, kh, rowb);
+    }
 #pragma unroll
-    for (int sj = 0; sj < 4; ++sj)
-      bf[sj] = *reinterpret_cast<const float4*>(&Bs[cur][(wc + sj * 16 + li) * LDS_STRIDE + lg * 4]);
-#pragma unroll
-    for (int si = 0; si < 4; ++si)
+    for (int si = 0; si < 4; ++si) {
+      const int rowa = wr + si * 16 + li;
+      const v4u a12 = split_frag(As[cur], ta1, kh, rowa);
+      const v4u a3 = split_frag(As[cur], ta3, kh, rowa);
 #pragma unroll
       for (int sj = 0; sj < 4; ++sj) {
-        acc[si][sj] = mfma_f32_16x16x4(af[si].x, bf[sj].x, acc[si][sj]);
-        acc[si][sj] = mfma_f32_16x16x4(af[si].y, bf[sj].y, acc[si][sj]);
-        acc[si][sj] = mfma_f32_16x16x4(af[si].z, bf[sj].z, acc[si][sj]);
-        acc[si][sj] = mfma_f32_16x16x4(af[si].w, bf[sj].w, acc[si][sj]);
+        acc[si][sj] = mfma_bf16_16x16x32(a12, b1[sj], acc[si][sj]);
+        acc[si][sj] = mfma_bf16_16x16x32(a12, b2[sj], acc[si][sj]);
+        acc[si][sj] = mfma_bf16_16x16x32(a3, b3[sj], acc[si][sj]);
       }
+    }
     if (kt + 1 < nk) {
-      store_tile(As[cur ^ 1], t, ra);
-      store_tile(Bs[cur ^ 1], t, rb);
+      store_split(As[cur ^ 1], t, ra, dm);
+      store_split(Bs[cur ^ 1], t, rb, dm);
     }
     __syncthreads();
   }

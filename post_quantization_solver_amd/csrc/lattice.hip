@@ -122,28 +122,12 @@ __device__ __forceinline__ float max8(const v4f& a, const v4f& b) {
   return fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
 }
 
-// The bf16 pairs (-1, 0) and (0, -1) as 32-bit words held in VGPRs.  They
-// are moved in as literals: the compiler would otherwise encode (-1, 0) as the
-// inline constant -1.0, which v_dot2c_f32_bf16 does not read as that pair.
-struct DotMasks {
-  uint32_t lo, hi;
-};
-__device__ __forceinline__ DotMasks dot_masks() {
-  DotMasks d;
-  asm volatile("v_mov_b32 %0, 0xbf80" : "=v"(d.lo));
-  asm volatile("v_mov_b32 %0, 0xbf800000" : "=v"(d.hi));
-  return d;
-}
-
 // p -> (hi, lo) bfloat16 pair words: hi rounds p to nearest bfloat16 and lo
 // rounds the remainder p - hi, which is exact in float32 and is formed by one
 // v_dot2_f32_bf16 each ((-1) hi + 0 + p).  p = hi + lo to about 2^-17.
 __device__ __forceinline__ void split_p(float p0, float p1, const DotMasks& dm, uint32_t& hw, uint32_t& lw) {
-  const v2bf h = {(__bf16)p0, (__bf16)p1};
-  const float l0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(v2bf, dm.lo), p0, false);
-  const float l1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(v2bf, dm.hi), p1, false);
-  hw = __builtin_bit_cast(uint32_t, h);
-  lw = f2bf_pack(l0, l1);
+  hw = f2bf_pack(p0, p1);
+  lw = f2bf_pack(sub_bf16_lo(p0, hw, dm), sub_bf16_hi(p1, hw, dm));
 }
 
 // Two variants share this body.

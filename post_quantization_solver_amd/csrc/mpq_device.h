@@ -53,3 +53,24 @@ __device__ __forceinline__ v4f mfma_f32_16x16x4(float a, float b, v4f c) {
 __device__ __forceinline__ v4f mfma_bf16_16x16x32(v4u a, v4u b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
+
+// The bf16 pairs (-1, 0) and (0, -1) as 32-bit words held in VGPRs.  They are
+// moved in as literals: the compiler would otherwise encode (-1, 0) as the
+// inline constant -1.0, which v_dot2c_f32_bf16 does not read as that pair.
+struct DotMasks {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ DotMasks dot_masks() {
+  DotMasks d;
+  asm volatile("v_mov_b32 %0, 0xbf80" : "=v"(d.lo));
+  asm volatile("v_mov_b32 %0, 0xbf800000" : "=v"(d.hi));
+  return d;
+}
+// x - (element 0 or 1 of the bf16 pair h), exact whenever the difference is a
+// float32 (h rounded from x): one v_dot2_f32_bf16 with the pair (-1, 0) / (0, -1).
+__device__ __forceinline__ float sub_bf16_lo(float x, uint32_t h, const DotMasks& dm) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, h), __builtin_bit_cast(v2bf, dm.lo), x, false);
+}
+__device__ __forceinline__ float sub_bf16_hi(float x, uint32_t h, const DotMasks& dm) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, h), __builtin_bit_cast(v2bf, dm.hi), x, false);
+}
