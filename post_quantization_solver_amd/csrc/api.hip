@@ -73,7 +73,7 @@ struct Layout {
 
 enum Region {
   R_VS, R_VST, R_YTIL, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI,
-  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_SPLIT, R_TKEY, R_QF, R_COUNT
+  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_SPLIT, R_TKEY, R_QF, R_VSP, R_VSTP, R_R2P, R_ZP, R_COUNT
 };
 
 size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -116,6 +116,11 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
   sz[R_SPLIT] = (size_t)MAX_SPLITK * m * KD * f64;
   sz[R_TKEY] = d == 8 ? (size_t)(KD / 8) * L.Kpad * 4 * sizeof(uint32_t) : 0;
   sz[R_QF] = d == 8 ? (size_t)m * 16 * sizeof(uint32_t) : 0;
+  // pre-split GEMM operands of the linear module (bf16 term tiles)
+  sz[R_VSP] = packed_split_words(n, r) * sizeof(uint32_t);
+  sz[R_VSTP] = packed_split_words(r, n) * sizeof(uint32_t);
+  sz[R_R2P] = packed_split_words(m, n) * sizeof(uint32_t);
+  sz[R_ZP] = packed_split_words(m, r) * sizeof(uint32_t);
   size_t o = 0;
   for (int k = 0; k < R_COUNT; ++k) {
     L.off[k] = o;
@@ -341,8 +346,16 @@ int denoise(Ctx& c, const float* R1, const float* gamma1, const float* a, const 
   return MPQ_OK;
 }
 
-int prepare_factors(Ctx& c, const float* V, const float* s) {
+uint32_t* packed(const Ctx& c, Region k) { return reinterpret_cast<uint32_t*>(c.p(k)); }
+
+// VS = V diag(s) and its transpose; with `split`, also their bf16-term tiles
+// for the linear module's GEMMs.
+int prepare_factors(Ctx& c, const float* V, const float* s, bool split = false) {
   TIMED(c, MPQ_PROF_OTHER, launch_scale_columns(V, s, c.L.n, c.L.r, c.p(R_VS), c.p(R_VST), c.st));
+  if (split) {
+    TIMED(c, MPQ_PROF_OTHER, launch_pack_split(c.p(R_VS), c.L.n, c.L.r, c.L.r, packed(c, R_VSP), c.st));
+    TIMED(c, MPQ_PROF_OTHER, launch_pack_split(c.p(R_VST), c.L.r, c.L.n, c.L.n, packed(c, R_VSTP), c.st));
+  }
   return MPQ_OK;
 }
 
@@ -396,7 +409,10 @@ int run_iteration(Ctx& c, float* R1, float* gamma1, float* beta, const float* yt
   if (trace_g2) TIMED(c, MPQ_PROF_OTHER, launch_record(c.gamma2(), L.m, trace_g2, ld_g2, col, c.st));
   if (r2_out) TIMED(c, MPQ_PROF_OTHER, launch_copy_rows_f(R2, r2_out, L.m * L.n, c.st));
   TIMED(c, MPQ_PROF_EXTRINSIC, launch_beta_lin(L.m, gamma1, beta, c.betalin(), c.gamma2(), c.st));
+  TIMED(c, MPQ_PROF_OTHER, launch_pack_split(R2, L.m, L.n, L.n, packed(c, R_R2P), c.st));
   GemmArgs g1 = gemm((int)L.m, (int)L.r, (int)L.n, R2, L.n, c.p(R_VST), L.n, c.p(R_Z), L.r);
+  g1.Ap = packed(c, R_R2P);
+  g1.Bp = packed(c, R_VSTP);
   g1.X = ytil; g1.ldx = L.r;
   g1.s = s;
   g1.rowa = c.betalin();
@@ -406,7 +422,10 @@ int run_iteration(Ctx& c, float* R1, float* gamma1, float* beta, const float* yt
   TIMED(c, MPQ_PROF_LINEAR1, launch_gemm(EPI_LINEAR1, g1, c.st));
   TIMED(c, MPQ_PROF_BETA, launch_beta(L.m, L.n, L.r, s, c.p(R_PART), gemm_col_tiles((int)L.r), c.gamma2(), damping, fixed_beta, beta,
                       gamma1, c.coef(), c.st));
+  TIMED(c, MPQ_PROF_OTHER, launch_pack_split(c.p(R_Z), L.m, L.r, L.r, packed(c, R_ZP), c.st));
   GemmArgs g2 = gemm((int)L.m, (int)L.n, (int)L.r, c.p(R_Z), L.r, c.p(R_VS), L.r, R1, L.n);
+  g2.Ap = packed(c, R_ZP);
+  g2.Bp = packed(c, R_VSP);
   g2.X = R2; g2.ldx = L.n;
   g2.rowa = c.coef();
   TIMED(c, MPQ_PROF_LINEAR2, launch_gemm(EPI_AXPY_ROW, g2, c.st));
@@ -502,7 +521,7 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
 int solve_layer(Ctx& c, const float* W, const float* s, const float* V, const float* row_scale,
                 const float* row_offset, int T_vamp, int n_cd, float damping, const mpq_options* opt, int32_t* codes,
                 float* beta_tr, float* gamma1_tr, float* gamma2_tr, int32_t* cd_changes) {
-  int rc = prepare_factors(c, V, s);
+  int rc = prepare_factors(c, V, s, T_vamp > 0);
   if (rc) return rc;
   const Layout& L = c.L;
   const int fixed = (opt && (opt->flags & MPQ_F_FIXED_BETA)) ? 1 : 0;
@@ -642,7 +661,7 @@ int mpq_vamp_step(float* R1, float* gamma1, float* beta, const float* ytil, int6
   rc = begin(c, m, n, r, K, d, cb, workspace, ws_bytes, stream, opt);
   if (rc) return rc;
   if ((rc = upload_codebook(c, cb))) return rc;
-  if ((rc = prepare_factors(c, V, s))) return rc;
+  if ((rc = prepare_factors(c, V, s, true))) return rc;
   const int fixed = (opt && (opt->flags & MPQ_F_FIXED_BETA)) ? 1 : 0;
   return finish(c, run_iteration(c, R1, gamma1, beta, ytil, s, row_scale, row_offset, damping, fixed, xhat1, eta1,
                                  gamma2, r2, fallback, nullptr, 0, 0));

@@ -61,6 +61,15 @@ constexpr int SPLIT_WORDS = 3 * 2 * 128 * 4;
 
 __device__ __forceinline__ int split_word(int term, int khalf, int row) { return ((term * 2 + khalf) * 128 + row) * 4; }
 
+// Two floats -> their three bf16 terms as packed pairs (h, m, l).
+__device__ __forceinline__ void split_pair(float x0, float x1, const DotMasks& dm, uint32_t& th, uint32_t& tm,
+                                           uint32_t& tl) {
+  th = f2bf_pack(x0, x1);
+  const float r0 = sub_bf16_lo(x0, th, dm), r1 = sub_bf16_hi(x1, th, dm);
+  tm = f2bf_pack(r0, r1);
+  tl = f2bf_pack(sub_bf16_lo(r0, tm, dm), sub_bf16_hi(r1, tm, dm));
+}
+
 // Split the thread's two float4 (rows t/4 and t/4 + 64, k quad t % 4) into
 // the three bf16 terms and write them to one LDS slice.
 __device__ __forceinline__ void store_split(uint32_t* lds, int t, const float4 (&reg)[2], const DotMasks& dm) {
@@ -71,12 +80,7 @@ __device__ __forceinline__ void store_split(uint32_t* lds, int t, const float4 (
     const float x[4] = {reg[h].x, reg[h].y, reg[h].z, reg[h].w};
     uint32_t th[2], tm[2], tl[2];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      th[p] = f2bf_pack(x[2 * p], x[2 * p + 1]);
-      const float r0 = sub_bf16_lo(x[2 * p], th[p], dm), r1 = sub_bf16_hi(x[2 * p + 1], th[p], dm);
-      tm[p] = f2bf_pack(r0, r1);
-      tl[p] = f2bf_pack(sub_bf16_lo(r0, tm[p], dm), sub_bf16_hi(r1, tm[p], dm));
-    }
+    for (int p = 0; p < 2; ++p) split_pair(x[2 * p], x[2 * p + 1], dm, th[p], tm[p], tl[p]);
     const int off = (q & 1) * 2;
     *reinterpret_cast<uint2*>(lds + split_word(0, q >> 1, rr) + off) = make_uint2(th[0], th[1]);
     *reinterpret_cast<uint2*>(lds + split_word(1, q >> 1, rr) + off) = make_uint2(tm[0], tm[1]);
@@ -88,8 +92,56 @@ __device__ __forceinline__ v4u split_frag(const uint32_t* lds, int term, int kha
   return *reinterpret_cast<const v4u*>(lds + split_word(term, khalf, row));
 }
 
-template <int EPI, bool VEC>
-__global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g) {
+// Pre-split ("packed") operands: for every 128-row x 16-k tile, one block of
+// SPLIT_WORDS words laid out exactly as the LDS slice (term, k half, row, 8
+// bf16), tiles ordered [row tile][k tile], zero outside the matrix.  A slice
+// then reaches LDS as three coalesced 16-byte copies per thread.
+__global__ __launch_bounds__(256) void pack_split_kernel(const float* __restrict__ X, int rows, int K, int64_t ld,
+                                                         int nks, uint32_t* __restrict__ out) {
+  const int t = threadIdx.x;
+  const int ks = blockIdx.x, rt = blockIdx.y;
+  const int r = t >> 1, kh = t & 1;
+  const int64_t row = (int64_t)rt * 128 + r;
+  const int k0 = ks * 16 + kh * 8;
+  float x[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) x[q] = (row < rows && k0 + q < K) ? X[row * ld + k0 + q] : 0.f;
+  const DotMasks dm = dot_masks();
+  uint32_t th[4], tm[4], tl[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) split_pair(x[2 * p], x[2 * p + 1], dm, th[p], tm[p], tl[p]);
+  uint32_t* blk = out + ((int64_t)rt * nks + ks) * SPLIT_WORDS;
+  *reinterpret_cast<v4u*>(blk + split_word(0, kh, r)) = (v4u){th[0], th[1], th[2], th[3]};
+  *reinterpret_cast<v4u*>(blk + split_word(1, kh, r)) = (v4u){tm[0], tm[1], tm[2], tm[3]};
+  *reinterpret_cast<v4u*>(blk + split_word(2, kh, r)) = (v4u){tl[0], tl[1], tl[2], tl[3]};
+}
+
+size_t packed_split_words(int64_t rows, int64_t K) {
+  return (size_t)((rows + 127) / 128) * (size_t)((K + 15) / 16) * SPLIT_WORDS;
+}
+
+hipError_t launch_pack_split(const float* X, int64_t rows, int64_t K, int64_t ld, uint32_t* out, hipStream_t st) {
+  if (rows <= 0 || K <= 0) return hipSuccess;
+  const int nks = (int)((K + 15) / 16);
+  hipLaunchKernelGGL(pack_split_kernel, dim3((unsigned)nks, (unsigned)((rows + 127) / 128)), dim3(256), 0, st, X,
+                     (int)rows, (int)K, ld, nks, out);
+  return hipGetLastError();
+}
+
+// Copy of one packed slice (3 x 16 bytes per thread) between global and LDS.
+__device__ __forceinline__ void load_packed(const uint32_t* __restrict__ blk, int t, v4u (&reg)[3]) {
+#pragma unroll
+  for (int j = 0; j < 3; ++j) reg[j] = reinterpret_cast<const v4u*>(blk)[t + 256 * j];
+}
+__device__ __forceinline__ void store_packed(uint32_t* lds, int t, const v4u (&reg)[3]) {
+#pragma unroll
+  for (int j = 0; j < 3; ++j) reinterpret_cast<v4u*>(lds)[t + 256 * j] = reg[j];
+}
+
+// PACKED: both operands come pre-split (g.Ap, g.Bp); otherwise they are float32
+// (g.A, g.B) and split on the way to LDS.
+template <int EPI, bool VEC, bool PACKED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void gemm_nt_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint32_t As[2][SPLIT_WORDS];
   __shared__ __attribute__((aligned(16))) uint32_t Bs[2][SPLIT_WORDS];
   __shared__ float red[2][GEMM_BM];
@@ -121,10 +173,20 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g) {
   const DotMasks dm = dot_masks();
   const int nk = (g.K + BK - 1) / BK;
   float4 ra[2], rb[2];
-  load_tile<VEC>(A, g.lda, g.M, g.K, row0, 0, t, ra);
-  load_tile<VEC>(B, g.ldb, g.N, g.K, col0, 0, t, rb);
-  store_split(As[0], t, ra, dm);
-  store_split(Bs[0], t, rb, dm);
+  v4u pa[3], pb[3];
+  const uint32_t* Ap = PACKED ? g.Ap + (int64_t)tile_m * nk * SPLIT_WORDS : nullptr;
+  const uint32_t* Bp = PACKED ? g.Bp + (int64_t)tile_n * nk * SPLIT_WORDS : nullptr;
+  if (PACKED) {
+    load_packed(Ap, t, pa);
+    load_packed(Bp, t, pb);
+    store_packed(As[0], t, pa);
+    store_packed(Bs[0], t, pb);
+  } else {
+    load_tile<VEC>(A, g.lda, g.M, g.K, row0, 0, t, ra);
+    load_tile<VEC>(B, g.ldb, g.N, g.K, col0, 0, t, rb);
+    store_split(As[0], t, ra, dm);
+    store_split(Bs[0], t, rb, dm);
+  }
   __syncthreads();
 
   // the lane's terms: A [h | m], A [h | l]; B h, m, [l | h]
@@ -133,32 +195,42 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g) {
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) {
-      load_tile<VEC>(A, g.lda, g.M, g.K, row0, (kt + 1) * BK, t, ra);
-      load_tile<VEC>(B, g.ldb, g.N, g.K, col0, (kt + 1) * BK, t, rb);
+      if (PACKED) {
+        load_packed(Ap + (int64_t)(kt + 1) * SPLIT_WORDS, t, pa);
+        load_packed(Bp + (int64_t)(kt + 1) * SPLIT_WORDS, t, pb);
+      } else {
+        load_tile<VEC>(A, g.lda, g.M, g.K, row0, (kt + 1) * BK, t, ra);
+        load_tile<VEC>(B, g.ldb, g.N, g.K, col0, (kt + 1) * BK, t, rb);
+      }
     }
-    v4u b1[4], b2[4], b3[4];
-#pragma unroll
-    for (int sj = 0; sj < 4; ++sj) {
-      const int rowb = wc + sj * 16 + li;
-      b1[sj] = split_frag(Bs[cur], 0, kh, rowb);
-      b2[sj] = split_frag(Bs[cur], 1, kh, rowb);
-      b3[sj] = split_frag(Bs[cur], tb3, kh, rowb);
-    }
+    v4u a12[4], a3[4];
 #pragma unroll
     for (int si = 0; si < 4; ++si) {
       const int rowa = wr + si * 16 + li;
-      const v4u a12 = split_frag(As[cur], ta1, kh, rowa);
-      const v4u a3 = split_frag(As[cur], ta3, kh, rowa);
+      a12[si] = split_frag(As[cur], ta1, kh, rowa);
+      a3[si] = split_frag(As[cur], ta3, kh, rowa);
+    }
 #pragma unroll
-      for (int sj = 0; sj < 4; ++sj) {
-        acc[si][sj] = mfma_bf16_16x16x32(a12, b1[sj], acc[si][sj]);
-        acc[si][sj] = mfma_bf16_16x16x32(a12, b2[sj], acc[si][sj]);
-        acc[si][sj] = mfma_bf16_16x16x32(a3, b3[sj], acc[si][sj]);
+    for (int sj = 0; sj < 4; ++sj) {
+      const int rowb = wc + sj * 16 + li;
+      const v4u b1 = split_frag(Bs[cur], 0, kh, rowb);
+      const v4u b2 = split_frag(Bs[cur], 1, kh, rowb);
+      const v4u b3 = split_frag(Bs[cur], tb3, kh, rowb);
+#pragma unroll
+      for (int si = 0; si < 4; ++si) {
+        acc[si][sj] = mfma_bf16_16x16x32(a12[si], b1, acc[si][sj]);
+        acc[si][sj] = mfma_bf16_16x16x32(a12[si], b2, acc[si][sj]);
+        acc[si][sj] = mfma_bf16_16x16x32(a3[si], b3, acc[si][sj]);
       }
     }
     if (kt + 1 < nk) {
-      store_split(As[cur ^ 1], t, ra, dm);
-      store_split(Bs[cur ^ 1], t, rb, dm);
+      if (PACKED) {
+        store_packed(As[cur ^ 1], t, pa);
+        store_packed(Bs[cur ^ 1], t, pb);
+      } else {
+        store_split(As[cur ^ 1], t, ra, dm);
+        store_split(Bs[cur ^ 1], t, rb, dm);
+      }
     }
     __syncthreads();
   }
@@ -252,13 +324,18 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g) {
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& g, hipStream_t st) {
   dim3 grid(gemm_col_tiles(g.N), (g.M + GEMM_BM - 1) / GEMM_BM, g.batch > 0 ? g.batch : 1);
+  if (g.Ap && g.Bp) {
+    if (g.batch > 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_nt_kernel<EPI, true, true>), grid, dim3(256), 0, st, g);
+    return hipGetLastError();
+  }
   bool vec = (g.K % 4 == 0) && (g.lda % 4 == 0) && (g.ldb % 4 == 0) &&
              ((reinterpret_cast<uintptr_t>(g.A) & 15) == 0) && ((reinterpret_cast<uintptr_t>(g.B) & 15) == 0) &&
              (g.sA % 4 == 0) && (g.sB % 4 == 0);
   if (vec)
-    hipLaunchKernelGGL((gemm_nt_kernel<EPI, true>), grid, dim3(256), 0, st, g);
+    hipLaunchKernelGGL((gemm_nt_kernel<EPI, true, false>), grid, dim3(256), 0, st, g);
   else
-    hipLaunchKernelGGL((gemm_nt_kernel<EPI, false>), grid, dim3(256), 0, st, g);
+    hipLaunchKernelGGL((gemm_nt_kernel<EPI, false, false>), grid, dim3(256), 0, st, g);
   return hipGetLastError();
 }
 

@@ -28,11 +28,19 @@ struct GemmArgs {
   const float* rowb;
   float* partial; int64_t ldp;
   int batch;
+  // optional pre-split operands (launch_pack_split layout, same M/N/K); when
+  // both are set they replace A and B
+  const uint32_t* Ap;
+  const uint32_t* Bp;
 };
 
 constexpr int GEMM_BM = 128, GEMM_BN = 128;
 inline int gemm_col_tiles(int N) { return (N + GEMM_BN - 1) / GEMM_BN; }
 hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t st);
+// X (rows x K, leading dimension ld) -> its three bf16 terms in the GEMM's
+// packed tile layout (packed_split_words(rows, K) uint32 words).
+size_t packed_split_words(int64_t rows, int64_t K);
+hipError_t launch_pack_split(const float* X, int64_t rows, int64_t K, int64_t ld, uint32_t* out, hipStream_t st);
 
 // Float64 variant for the CD state: C (float64) = / -= A (float64 or float32)
 // * B (float32)^T on the fp64 matrix cores.  Epilogues EPI_STORE, EPI_SUB_INPLACE.
