@@ -102,12 +102,10 @@ __global__ __launch_bounds__(256) void cd_tkeys_kernel(int kd, const double* __r
 // per-row constant.  G is the block's 8 x 8 diagonal of H, e_x the current
 // codeword, g the block's gradient (lane p < 8 passes g[p]).  Called by a whole
 // wave; lanes 0..15 write the 16 words of qf[i].
-__device__ __forceinline__ void cd_query_row(int lane, int64_t i, int64_t b, int bl, int kd, double gp,
-                                             const double* __restrict__ Ht, const float* __restrict__ e32,
-                                             double ai, const int32_t* __restrict__ codes, int64_t B,
-                                             uint32_t* __restrict__ qf) {
+__device__ __forceinline__ void cd_query_row(int lane, int64_t i, int bl, int kd, double gp,
+                                             const double* __restrict__ Ht, const float* __restrict__ ex,
+                                             double ai, uint32_t* __restrict__ qf) {
   const int p = lane & 7;
-  const float* ex = e32 + (int64_t)codes[i * B + b] * 8;
   const double* hr = Ht + (int64_t)(8 * bl + p) * kd + 8 * bl;
   double ge = 0.0;
 #pragma unroll
@@ -143,7 +141,7 @@ __global__ __launch_bounds__(256) void cd_query_kernel(int64_t m, int64_t n, int
   const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= m) return;
   const double gp = Gt[i * kd + 8 * bl + (lane & 7)];
-  cd_query_row(lane, i, b, bl, kd, gp, Ht, e32, (double)a[i], codes, n / 8, qf);
+  cd_query_row(lane, i, bl, kd, gp, Ht, e32 + (int64_t)codes[i * (n / 8) + b] * 8, (double)a[i], qf);
 }
 
 // A score with its 2 low mantissa bits replaced by the codeword's position v
@@ -153,7 +151,7 @@ __device__ __forceinline__ float tag2(float x, uint32_t v) {
   return __uint_as_float((__float_as_uint(x) & 0xfffffffcu) | v);
 }
 
-// grid: (slices, row groups).  part_s / part_i: [2][slices][m] (best, second).
+// grid: (slices, row groups).  part_s / part_i: [m][slices][2] (best, second).
 // The float32 scores only rank candidates; the update kernel re-evaluates the
 // two best of every slice exactly in float64.
 __global__ __launch_bounds__(256) void cd_score_kernel(int64_t m, int bl, const uint32_t* __restrict__ keys,
@@ -222,34 +220,26 @@ __global__ __launch_bounds__(256) void cd_score_kernel(int64_t m, int bl, const 
     }
     const int64_t i = row_base + q * 16 + j;
     if (g == 0 && i < m) {
-      part_s[(int64_t)blockIdx.x * m + i] = c1.v;
-      part_i[(int64_t)blockIdx.x * m + i] = c1.i;
-      part_s[((int64_t)nsl + blockIdx.x) * m + i] = c2.v;
-      part_i[((int64_t)nsl + blockIdx.x) * m + i] = c2.i;
+      reinterpret_cast<float2*>(part_s)[i * nsl + blockIdx.x] = make_float2(c1.v, c2.v);
+      reinterpret_cast<int2*>(part_i)[i * nsl + blockIdx.x] = make_int2(c1.i, c2.i);
     }
   }
 }
 
-// Exact float64 change of the objective for moving block (8 coords) from
-// base codeword ex to en (row scale ai): dF = 1/2 d^T G d - d^T g, d = a (en - ex).
-__device__ __forceinline__ double move_gain(const double* __restrict__ Ht, int kd, int bl,
-                                            const double* __restrict__ gb, const float* en, const float* ex,
-                                            double ai, double (&dlt)[8]) {
+// Sum over the wave, fixed butterfly order (the same value in every lane).
+__device__ __forceinline__ double wave_sum_d(double x) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) dlt[k] = ai * ((double)en[k] - (double)ex[k]);
-  double f = 0.0;
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    double gd = 0.0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) gd = fma(Ht[(int64_t)(8 * bl + p) * kd + 8 * bl + k], dlt[k], gd);
-    f = fma(dlt[p], 0.5 * gd - gb[p], f);
-  }
-  return f;
+  for (int msk = 1; msk < 64; msk <<= 1) x += __shfl_xor(x, msk, 64);
+  return x;
 }
 
-// One wave per row: merge the slices' top-2 lists in order, re-score the two
-// finalists in float64 and move on a strict decrease.
+// One wave per row: merge the slices' top-2 lists, re-score the two
+// finalists exactly in float64 and move on a strict decrease; then update
+// the tile gradient and write the next block's query fragments.  Loads that
+// do not depend on the merge are issued first.  Lane l = 8 p + k holds
+// H[8 bl + p][8 bl + k] of the block's diagonal, so the exact change
+//   dF(c) = 1/2 d^T G d - d^T g,   d = a (e_c - e_x)
+// is one product per lane and a wave sum.
 __global__ __launch_bounds__(256) void cd_update_kernel(int64_t m, int64_t n, int64_t b, int bl, int kd, int nslices,
                                                         double* __restrict__ Gt, const double* __restrict__ Ht,
                                                         const float* __restrict__ e32, const float* __restrict__ a,
@@ -261,16 +251,46 @@ __global__ __launch_bounds__(256) void cd_update_kernel(int64_t m, int64_t n, in
   const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= m) return;
   const int64_t B = n / 8;
-  // top 2 over all slices: lane l takes slice l (of each group of 64), then a
-  // butterfly merge; the top two of a totally ordered set do not depend on
-  // the merge order
+  const int p = lane >> 3, k = lane & 7;
+  const int c0 = 8 * (bl + 1);          // the next block's first column in the tile
+  const bool has_next = c0 < kd;
+
+  // independent loads
+  const int cx = codes[i * B + b];
+  const int cn = has_next ? codes[i * B + b + 1] : 0;
+  const double ai = a[i];
+  const double hpk = Ht[(int64_t)(8 * bl + p) * kd + 8 * bl + k];
+  const double gpp = Gt[i * kd + 8 * bl + p];
+  const double gnext = has_next ? Gt[i * kd + c0 + k] : 0.0;
+  Cand o[2][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int sl = 64 * r + lane;
+    o[r][0] = o[r][1] = Cand{INFINITY, 0x7fffffff};
+    if (sl < nslices) {
+      const float2 sv = reinterpret_cast<const float2*>(part_s)[i * nslices + sl];
+      const int2 iv = reinterpret_cast<const int2*>(part_i)[i * nslices + sl];
+      o[r][0] = {sv.x, iv.x};
+      o[r][1] = {sv.y, iv.y};
+    }
+  }
+  // top 2 over all slices (lane butterfly; the top two of a totally ordered
+  // set do not depend on the merge order)
   Cand c1 = {INFINITY, 0x7fffffff}, c2 = {INFINITY, 0x7fffffff};
   for (int base = 0; base < nslices; base += 64) {
-    const int sl = base + lane;
-    Cand o1 = {INFINITY, 0x7fffffff}, o2 = {INFINITY, 0x7fffffff};
-    if (sl < nslices) {
-      o1 = {part_s[(int64_t)sl * m + i], part_i[(int64_t)sl * m + i]};
-      o2 = {part_s[((int64_t)nslices + sl) * m + i], part_i[((int64_t)nslices + sl) * m + i]};
+    Cand o1, o2;
+    if (base < 128) {
+      o1 = o[base >> 6][0];
+      o2 = o[base >> 6][1];
+    } else {
+      const int sl = base + lane;
+      o1 = o2 = Cand{INFINITY, 0x7fffffff};
+      if (sl < nslices) {
+        const float2 sv = reinterpret_cast<const float2*>(part_s)[i * nslices + sl];
+        const int2 iv = reinterpret_cast<const int2*>(part_i)[i * nslices + sl];
+        o1 = {sv.x, iv.x};
+        o2 = {sv.y, iv.y};
+      }
     }
 #pragma unroll
     for (int msk = 1; msk < 64; msk <<= 1) {
@@ -279,54 +299,54 @@ __global__ __launch_bounds__(256) void cd_update_kernel(int64_t m, int64_t n, in
     }
     merge_top2(c1, c2, o1, o2);
   }
-  const int cx = codes[i * B + b];
-  double* dl = Delta + i * kd + 8 * bl;
-  const double* gb = Gt + i * kd + 8 * bl;
-  const double ai = a[i];
+
   const float* ex = e32 + (int64_t)cx * 8;
   double bestF = 0.0;
   int bestk = cx;
-  double dlt[8], tmp[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) dlt[k] = 0.0;
   const int cands[2] = {c1.i, c2.i};
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int k2 = cands[c];
-    if (k2 == 0x7fffffff || k2 == cx) continue;
-    double f = move_gain(Ht, kd, bl, gb, e32 + (int64_t)k2 * 8, ex, ai, tmp);
+    if (k2 == 0x7fffffff || k2 == cx) continue;   // uniform over the wave
+    const float* en = e32 + (int64_t)k2 * 8;
+    const double dp = ai * ((double)en[p] - (double)ex[p]);
+    const double dk = ai * ((double)en[k] - (double)ex[k]);
+    double term = dp * (0.5 * hpk * dk);
+    if (k == 0) term -= dp * gpp;
+    const double f = wave_sum_d(term);
     if (f < bestF || (f == bestF && bestk != cx && k2 < bestk)) {
       bestF = f;
       bestk = k2;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) dlt[k] = tmp[k];
     }
   }
   const bool moved = bestk != cx;   // uniform over the wave
-  if (lane < 8) dl[lane] = moved ? dlt[lane] : 0.0;
+  double dl[8];
+  const float* eb = e32 + (int64_t)bestk * 8;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dl[q] = moved ? ai * ((double)eb[q] - (double)ex[q]) : 0.0;
+  if (lane < 8) Delta[i * kd + 8 * bl + lane] = dl[lane];
   if (moved && lane == 0) {
     codes[i * B + b] = bestk;
     changes[i] += 1;
   }
-  // g_j -= sum_k H[j][8 bl + k] delta_k for every column j of the tile; the
-  // lanes owning the next block's columns keep their new values
-  const int c0 = 8 * (bl + 1);
+  // g_j -= sum_q H[j][8 bl + q] delta_q for every column j of the tile, read
+  // as H[8 bl + q][j] (the diagonal tile is symmetric) so the loads coalesce;
+  // the lanes owning the next block's columns keep their new values
   double gk = 0.0;
   if (moved) {
     for (int jc = lane; jc < kd; jc += 64) {
-      const double* hr = Ht + (int64_t)jc * kd + 8 * bl;
       double sacc = 0.0;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) sacc = fma(hr[k], dlt[k], sacc);
+      for (int q = 0; q < 8; ++q) sacc = fma(Ht[(int64_t)(8 * bl + q) * kd + jc], dl[q], sacc);
       const double nv = Gt[i * kd + jc] - sacc;
       Gt[i * kd + jc] = nv;
       if (jc >= c0 && jc < c0 + 8) gk = nv;
     }
   }
   // the next block's query fragments
-  if (c0 < kd) {
-    const double gp = moved ? shfl_d(gk, (c0 & 63) + (lane & 7)) : Gt[i * kd + c0 + (lane & 7)];
-    cd_query_row(lane, i, b + 1, bl + 1, kd, gp, Ht, e32, ai, codes, B, qf);
+  if (has_next) {
+    const double gp = moved ? shfl_d(gk, (c0 & 63) + k) : gnext;
+    cd_query_row(lane, i, bl + 1, kd, gp, Ht, e32 + (int64_t)cn * 8, ai, qf);
   }
 }
 

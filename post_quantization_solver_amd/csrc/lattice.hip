@@ -22,6 +22,7 @@
 // Both MFMAs see the same rounded weights hi + lo, so the normalized sums are
 // weighted means with weights within about 2^-17 of p.
 #include <math.h>
+#include <algorithm>
 #include "mpq_device.h"
 #include "internal.h"
 
@@ -161,6 +162,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
   auto& lds_pv = sm.ch.pv;
   auto& fin = sm.fin;
 
+  // queries per wave: 4 subtiles of 16 in the fast pass; the exact pass
+  // takes 1 (its few queries spread over more waves, so a pass lasts less)
+  constexpr int QS = ONLINE ? 1 : LAT_QSUB;
+  constexpr int QW = 16 * QS;
+  constexpr int QWG = QW * LAT_WAVES;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -168,8 +174,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
   const int g = lane >> 4;
   const int64_t B = n / 8;
   const int64_t total = ONLINE ? (int64_t)(*flag_count) : m * B;
-  if ((int64_t)blockIdx.x * LAT_QWG >= total) return;   // uniform per workgroup
-  const int64_t qbase = (int64_t)blockIdx.x * LAT_QWG + wave * LAT_QW;
+  // FAST: one workgroup per 256 queries.  ONLINE: the grid strides over the
+  // flagged list (its length is only known on the device).
+  const int64_t vstride = ONLINE ? (int64_t)gridDim.x : total;
+  for (int64_t vb = blockIdx.x; vb * QWG < total; vb += vstride) {   // uniform per workgroup
+  const int64_t qbase = vb * QWG + wave * QW;
 
   // query index -> (row, block); ONLINE reads it from the flag list
   auto resolve = [&](int64_t slot) -> QueryInfo {
@@ -183,8 +192,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
   };
 
   // ---- per-query setup (each of the 4 lanes of a query computes the same values)
-  v4u qop[LAT_QSUB];
-  float kap[LAT_QSUB], Mq[LAT_QSUB], qv[ONLINE ? LAT_QSUB : 1][8];
+  v4u qop[QS];
+  float kap[QS], Mq[QS], qv[ONLINE ? QS : 1][8];
   float h0 = 0.f;
   if (ONLINE) {
 #pragma unroll
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
     h0 *= 0.5f;
   }
 #pragma unroll
-  for (int q = 0; q < LAT_QSUB; ++q) {
+  for (int q = 0; q < QS; ++q) {
     QueryInfo qi = resolve(qbase + q * 16 + j);
     float k2 = 0.f;
     float rp[8];
@@ -238,9 +247,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
   // products into it, starting from zero at the chunk's first step); tot:
   // running total, updated by one float32 add per chunk so long
   // accumulations round to nearest at every step.
-  v4f acc[LAT_QSUB], tot[LAT_QSUB];
+  v4f acc[QS], tot[QS];
 #pragma unroll
-  for (int q = 0; q < LAT_QSUB; ++q) {
+  for (int q = 0; q < QS; ++q) {
     acc[q] = (v4f){0.f, 0.f, 0.f, 0.f};
     tot[q] = (v4f){0.f, 0.f, 0.f, 0.f};
   }
@@ -263,7 +272,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
       const v4u k1 = kq[(2 * st + 1) * 64 + lane];
       const v4u pv = pq[st * 64 + lane];
 #pragma unroll
-      for (int q = 0; q < LAT_QSUB; ++q) {
+      for (int q = 0; q < QS; ++q) {
         v4f s0 = mfma_bf16_16x16x32(k0, qop[q], zero4);
         v4f s1 = mfma_bf16_16x16x32(k1, qop[q], zero4);
         if (ONLINE) {
@@ -302,7 +311,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
       }
     }
 #pragma unroll
-    for (int q = 0; q < LAT_QSUB; ++q) tot[q] += acc[q];
+    for (int q = 0; q < QS; ++q) tot[q] += acc[q];
     // the other buffer was last read in chunk c - 1, before the previous barrier
     if (c + 1 < nchunks) store_chunk(lds_key[cur ^ 1], lds_pv[cur ^ 1], pre, t);
     __syncthreads();
@@ -311,17 +320,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
   // ---- finish: lane (j, g) holds columns 4g..4g+3 of query j's sums:
   // 0..7 sum p e, 8..10 sum p ||e||^2 (hi, mid, lo), 11 sum p.
 #pragma unroll
-  for (int q = 0; q < LAT_QSUB; ++q) {
-    const int ql = wave * LAT_QW + q * 16 + j;
+  for (int q = 0; q < QS; ++q) {
+    const int ql = wave * QW + q * 16 + j;
     if (g < 3) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) fin[ql][4 * g + v] = tot[q][v];
     }
   }
   __syncthreads();
-  {
+  if (t < QWG) {
     const int ql = t;  // one thread per query of the workgroup
-    const int64_t slot = (int64_t)blockIdx.x * LAT_QWG + ql;
+    const int64_t slot = vb * QWG + ql;
     QueryInfo qi = resolve(slot);
     if (qi.valid) {
       float gm = gamma1[qi.i];
@@ -349,6 +358,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
         vblk[qi.i * B + qi.b] = fmaxf(m2 - nx, 0.f) * ai * ai;
       }
     }
+  }
+  __syncthreads();   // the next query group reuses the LDS
   }
 }
 
@@ -446,14 +457,16 @@ hipError_t launch_denoise_lattice(const float* R1, const float* gamma1, int64_t 
   return hipGetLastError();
 }
 
-// The flagged queries with the exact online-maximum pass; the grid covers
-// every query and surplus workgroups exit at once.
+// The flagged queries with the exact online-maximum pass: a grid of at most
+// LAT_EXACT_WGS workgroups strides over the list (surplus ones exit at once).
+constexpr int64_t LAT_EXACT_WGS = 1024;
 hipError_t launch_denoise_lattice_exact(const float* R1, const float* gamma1, int64_t m, int64_t n,
                                         const CbTables& cb, const float* a, const float* o, float* xhat, float* vblk,
                                         int32_t* flag, hipStream_t st) {
   int64_t total = m * (n / 8);
   if (total <= 0) return hipSuccess;
-  dim3 grid((unsigned)((total + LAT_QWG - 1) / LAT_QWG));
+  const int64_t qwg = 16 * LAT_WAVES;   // queries per workgroup of the exact pass
+  dim3 grid((unsigned)std::min<int64_t>((total + qwg - 1) / qwg, LAT_EXACT_WGS));
   hipLaunchKernelGGL((denoise_lattice_kernel<true>), grid, dim3(256), 0, st, R1, gamma1, m, n, cb.qk_keys, cb.pv_ops,
                      cb.e32, cb.Kpad, a, o, xhat, vblk, flag + 64, flag);
   return hipGetLastError();
