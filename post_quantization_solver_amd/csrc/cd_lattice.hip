@@ -201,9 +201,14 @@ __global__ __launch_bounds__(256) void cd_score_kernel(int64_t m, int bl, const 
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       v4f sc = mfma_bf16_16x16x32(k0, qop[q], zero4);
-      float nb = fminf(fminf(best[q], tag2(sc[0], 0u)), fminf(tag2(sc[1], 1u), fminf(tag2(sc[2], 2u), tag2(sc[3], 3u))));
-      bst[q] = nb < best[q] ? st : bst[q];
-      best[q] = nb;
+      // IEEE minimum (v_minimum3_f32): the scores are finite, so it needs no
+      // NaN quieting of its operands
+      const float m4 = __builtin_elementwise_minimum(
+          __builtin_elementwise_minimum(__builtin_elementwise_minimum(tag2(sc[0], 0u), tag2(sc[1], 1u)),
+                                        tag2(sc[2], 2u)),
+          tag2(sc[3], 3u));
+      bst[q] = m4 < best[q] ? st : bst[q];
+      best[q] = __builtin_elementwise_minimum(best[q], m4);
     }
   }
   // top 2 of the row's four lane-bests (lanes j, j+16, j+32, j+48)
