@@ -35,6 +35,9 @@ namespace {
 
 constexpr int KD = 256;          // CD tile width (columns)
 constexpr int MAX_SPLITK = 16;   // K chunks for the CD tile-gradient GEMM
+constexpr int CD_GROUPS_MAX = 2; // CD row groups run on streams of their own
+// row groups for the CD sweeps: two for layers of at least 1024 rows
+int cd_groups(int64_t m) { return m >= 1024 ? CD_GROUPS_MAX : 1; }
 constexpr int LAT_CHUNK = 128;   // lattice codebook padding granularity
 constexpr size_t ALIGN = 256;
 
@@ -52,7 +55,7 @@ constexpr size_t ALIGN = 256;
       Prof::Ev ev_{nullptr, nullptr, (cat)};                        \
       MPQ_TRY(hipEventCreate(&ev_.a));                              \
       if (hipEventCreate(&ev_.b) != hipSuccess) {                   \
-        hipEventDestroy(ev_.a);                                     \
+        (void)hipEventDestroy(ev_.a);                               \
         return MPQ_EHIP;                                            \
       }                                                             \
       (c).prof.evs.push_back(ev_);                                  \
@@ -113,8 +116,9 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
   sz[R_FLAG] = d == 8 ? (size_t)(64 + m * L.B) * sizeof(int32_t) : 0;
   sz[R_U64] = (size_t)m * r * f64;
   sz[R_D64] = (size_t)m * n * f64;
-  sz[R_SPLIT] = (size_t)MAX_SPLITK * m * KD * f64;
-  sz[R_TKEY] = d == 8 ? (size_t)(KD / 8) * L.Kpad * 4 * sizeof(uint32_t) : 0;
+  const int G = cd_groups(m);
+  sz[R_SPLIT] = (size_t)MAX_SPLITK * G * ((m + G - 1) / G) * KD * f64;
+  sz[R_TKEY] = d == 8 ? (size_t)G * (KD / 8) * L.Kpad * 4 * sizeof(uint32_t) : 0;
   sz[R_QF] = d == 8 ? (size_t)m * 16 * sizeof(uint32_t) : 0;
   // pre-split GEMM operands of the linear module (bf16 term tiles)
   sz[R_VSP] = packed_split_words(n, r) * sizeof(uint32_t);
@@ -143,8 +147,8 @@ struct Prof {
   std::vector<Ev> evs;
   ~Prof() {
     for (auto& e : evs) {
-      hipEventDestroy(e.a);
-      hipEventDestroy(e.b);
+      (void)hipEventDestroy(e.a);
+      (void)hipEventDestroy(e.b);
     }
   }
 };
@@ -362,9 +366,9 @@ int prepare_factors(Ctx& c, const float* V, const float* s, bool split = false) 
 // Collect profiling results (waits for the call's last event).
 int finish(Ctx& c, int rc) {
   if (rc != MPQ_OK || !c.prof.on || c.prof.evs.empty()) return rc;
-  MPQ_TRY(hipEventSynchronize(c.prof.evs.back().b));
   for (auto& e : c.prof.evs) {
     float ms = 0.f;
+    MPQ_TRY(hipEventSynchronize(e.b));   // events may sit on several streams
     MPQ_TRY(hipEventElapsedTime(&ms, e.a, e.b));
     if (c.prof.ms) c.prof.ms[e.cat] += ms;
     if (c.prof.launches) c.prof.launches[e.cat] += 1;
@@ -476,45 +480,131 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
           launch_gemm64(EPI_STORE, false, gemm64(rem, rem, (int)L.r, vs, L.r, vs, L.r, Hd + (int64_t)full * KD * KD,
                                                  rem), c.st));
   }
-  for (int sw = 0; sw < n_cd; ++sw) {
-    TIMED(c, MPQ_PROF_OTHER, launch_fill_i32(chg, L.m, 0, c.st));
-    for (int tl = 0; tl < L.ntiles; ++tl) {
-      const int64_t j0 = (int64_t)tl * KD;
-      const int kw = (int)std::min<int64_t>(KD, L.n - j0);
-      const double* Ht = Hd + (int64_t)tl * KD * KD;
-      {
-        // the tile gradient has few output tiles and a long K (= r): split K
-        // until the launch has about 512 workgroups
-        const int64_t out_tiles = (int64_t)gemm_col_tiles(kw) * ((L.m + GEMM_BM - 1) / GEMM_BM);
-        int splits = (int)std::min<int64_t>(MAX_SPLITK, std::max<int64_t>(1, 512 / std::max<int64_t>(out_tiles, 1)));
-        splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, L.r / 256));
-        Gemm64Args gg = gemm64((int)L.m, kw, (int)L.r, U, L.r, c.p(R_VS) + j0 * L.r, L.r, Gt, kw);
-        if (splits > 1) {
-          TIMED(c, MPQ_PROF_CD_GEMM,
-                launch_gemm64_splitk(EPI_STORE, gg, splits, reinterpret_cast<double*>(c.p(R_SPLIT)), c.st));
-        } else {
-          TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_STORE, true, gg, c.st));
-        }
-      }
-      if (L.d == 1) {
-        TIMED(c, MPQ_PROF_CD_SEARCH,
-              launch_cd_scalar_tile(L.m, L.n, j0, kw, Gt, Ht, c.cb, a, o, codes, nullptr, Dl, chg, c.st));
-      } else {
-        uint32_t* tk = reinterpret_cast<uint32_t*>(c.p(R_TKEY));
-        TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_lattice_tkeys(kw / 8, kw, Ht, c.cb, tk, c.st));
-        for (int bl = 0; bl < kw / 8; ++bl) {
-          TIMED(c, MPQ_PROF_CD_SEARCH,
-                launch_cd_lattice_block(L.m, L.n, j0 / 8 + bl, bl, kw, Gt, Ht, tk, c.cb, a, codes, Dl, chg,
-                                        c.p(R_PS), c.pi(R_PI), reinterpret_cast<uint32_t*>(c.p(R_QF)), c.st));
-        }
-      }
-      TIMED(c, MPQ_PROF_CD_GEMM,
-            launch_gemm64(EPI_SUB_INPLACE, true, gemm64((int)L.m, (int)L.r, kw, Dl, kw, c.p(R_VST) + j0, L.n, U, L.r),
-                          c.st));
+  // The sweeps: rows are independent problems, so large layers split them
+  // into row groups, each on a stream of its own (forked from and joined to
+  // the caller's stream).  The enqueue order interleaves the groups block by
+  // block, so one group's moves and launch gaps overlap the other's scoring.
+  const int G = cd_groups(L.m);
+  const int64_t mg_max = (L.m + G - 1) / G;
+  hipStream_t parent = c.st;
+  hipStream_t gs[CD_GROUPS_MAX];
+  hipEvent_t gev[CD_GROUPS_MAX + 1];
+  int nstreams = 0, nevents = 0;
+  auto release = [&]() {
+    for (int k = 0; k < nstreams; ++k) (void)hipStreamDestroy(gs[k]);
+    for (int k = 0; k < nevents; ++k) (void)hipEventDestroy(gev[k]);
+    c.st = parent;
+  };
+  if (G > 1) {
+    if (hipEventCreateWithFlags(&gev[0], hipEventDisableTiming) != hipSuccess) return MPQ_EHIP;
+    nevents = 1;
+    if (hipEventRecord(gev[0], parent) != hipSuccess) { release(); return MPQ_EHIP; }
+    for (int g = 0; g < G; ++g) {
+      if (hipStreamCreateWithFlags(&gs[g], hipStreamNonBlocking) != hipSuccess) { release(); return MPQ_EHIP; }
+      ++nstreams;
+      if (hipStreamWaitEvent(gs[g], gev[0], 0) != hipSuccess) { release(); return MPQ_EHIP; }
     }
-    if (cd_changes) TIMED(c, MPQ_PROF_OTHER, launch_record_i32(chg, L.m, cd_changes, n_cd, sw, c.st));
+  } else {
+    gs[0] = parent;
   }
-  return MPQ_OK;
+  struct Group {
+    int64_t r0, mg;
+    double *Gt, *Dl, *U, *part;
+    int32_t *codes, *chg, *changes, *pi;
+    float* ps;
+    const float *a, *o;
+    uint32_t *qf, *tk;
+  } grp[CD_GROUPS_MAX];
+  for (int g = 0; g < G; ++g) {
+    Group& q = grp[g];
+    q.r0 = g * mg_max;
+    q.mg = std::max<int64_t>(0, std::min<int64_t>(mg_max, L.m - q.r0));
+    q.Gt = Gt + q.r0 * KD;
+    q.Dl = Dl + q.r0 * KD;
+    q.U = U + q.r0 * L.r;
+    q.part = reinterpret_cast<double*>(c.p(R_SPLIT)) + (int64_t)g * MAX_SPLITK * mg_max * KD;
+    q.codes = codes + q.r0 * L.B;
+    q.chg = chg + q.r0;
+    q.changes = cd_changes ? cd_changes + q.r0 * n_cd : nullptr;
+    q.ps = c.p(R_PS) + q.r0 * 2 * std::max(L.nslices, 1);
+    q.pi = c.pi(R_PI) + q.r0 * 2 * std::max(L.nslices, 1);
+    q.a = a + q.r0;
+    q.o = o + q.r0;
+    q.qf = reinterpret_cast<uint32_t*>(c.p(R_QF)) + q.r0 * 16;
+    q.tk = reinterpret_cast<uint32_t*>(c.p(R_TKEY)) + (int64_t)g * (KD / 8) * L.Kpad * 4;
+  }
+  int rc = MPQ_OK;
+  auto body = [&]() -> int {
+    for (int sw = 0; sw < n_cd; ++sw) {
+      for (int g = 0; g < G; ++g) {
+        c.st = gs[g];
+        TIMED(c, MPQ_PROF_OTHER, launch_fill_i32(grp[g].chg, grp[g].mg, 0, c.st));
+      }
+      for (int tl = 0; tl < L.ntiles; ++tl) {
+        const int64_t j0 = (int64_t)tl * KD;
+        const int kw = (int)std::min<int64_t>(KD, L.n - j0);
+        const double* Ht = Hd + (int64_t)tl * KD * KD;
+        for (int g = 0; g < G; ++g) {
+          const Group& q = grp[g];
+          if (q.mg == 0) continue;
+          c.st = gs[g];
+          // the tile gradient has few output tiles and a long K (= r): split K
+          // until the launch has about 512 workgroups
+          const int64_t out_tiles = (int64_t)gemm_col_tiles(kw) * ((q.mg + GEMM_BM - 1) / GEMM_BM);
+          int splits = (int)std::min<int64_t>(MAX_SPLITK, std::max<int64_t>(1, 512 / std::max<int64_t>(out_tiles, 1)));
+          splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, L.r / 256));
+          Gemm64Args gg = gemm64((int)q.mg, kw, (int)L.r, q.U, L.r, c.p(R_VS) + j0 * L.r, L.r, q.Gt, kw);
+          if (splits > 1) {
+            TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64_splitk(EPI_STORE, gg, splits, q.part, c.st));
+          } else {
+            TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_STORE, true, gg, c.st));
+          }
+          if (L.d == 1) {
+            TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_scalar_tile(q.mg, L.n, j0, kw, q.Gt, Ht, c.cb, q.a, q.o, q.codes,
+                                                               nullptr, q.Dl, q.chg, c.st));
+          } else {
+            TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_lattice_tkeys(kw / 8, kw, Ht, c.cb, q.tk, c.st));
+          }
+        }
+        if (L.d == 8) {
+          for (int bl = 0; bl < kw / 8; ++bl) {
+            for (int g = 0; g < G; ++g) {
+              const Group& q = grp[g];
+              if (q.mg == 0) continue;
+              c.st = gs[g];
+              TIMED(c, MPQ_PROF_CD_SEARCH,
+                    launch_cd_lattice_block(q.mg, L.n, j0 / 8 + bl, bl, kw, q.Gt, Ht, q.tk, c.cb, q.a, q.codes, q.Dl,
+                                            q.chg, q.ps, q.pi, q.qf, c.st));
+            }
+          }
+        }
+        for (int g = 0; g < G; ++g) {
+          const Group& q = grp[g];
+          if (q.mg == 0) continue;
+          c.st = gs[g];
+          TIMED(c, MPQ_PROF_CD_GEMM,
+                launch_gemm64(EPI_SUB_INPLACE, true,
+                              gemm64((int)q.mg, (int)L.r, kw, q.Dl, kw, c.p(R_VST) + j0, L.n, q.U, L.r), c.st));
+        }
+      }
+      for (int g = 0; g < G; ++g) {
+        c.st = gs[g];
+        if (grp[g].changes)
+          TIMED(c, MPQ_PROF_OTHER, launch_record_i32(grp[g].chg, grp[g].mg, grp[g].changes, n_cd, sw, c.st));
+      }
+    }
+    return MPQ_OK;
+  };
+  rc = body();
+  if (rc == MPQ_OK && G > 1) {
+    for (int g = 0; g < G && rc == MPQ_OK; ++g) {
+      if (hipEventCreateWithFlags(&gev[nevents], hipEventDisableTiming) != hipSuccess) { rc = MPQ_EHIP; break; }
+      hipEvent_t e = gev[nevents++];
+      if (hipEventRecord(e, gs[g]) != hipSuccess || hipStreamWaitEvent(parent, e, 0) != hipSuccess) rc = MPQ_EHIP;
+    }
+  }
+  release();
+  return rc;
 }
 
 // The whole layer: prologue, T_vamp iterations, marginal MAP, CD.

@@ -102,14 +102,9 @@ __global__ __launch_bounds__(256) void cd_tkeys_kernel(int kd, const double* __r
 // per-row constant.  G is the block's 8 x 8 diagonal of H, e_x the current
 // codeword, g the block's gradient (lane p < 8 passes g[p]).  Called by a whole
 // wave; lanes 0..15 write the 16 words of qf[i].
-__device__ __forceinline__ void cd_query_row(int lane, int64_t i, int bl, int kd, double gp,
-                                             const double* __restrict__ Ht, const float* __restrict__ ex,
-                                             double ai, uint32_t* __restrict__ qf) {
-  const int p = lane & 7;
-  const double* hr = Ht + (int64_t)(8 * bl + p) * kd + 8 * bl;
-  double ge = 0.0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) ge = fma(hr[k], (double)ex[k], ge);
+// The writer: lane p (= lane & 7) passes ge = (G e_x)[p] and g[p].
+__device__ __forceinline__ void cd_query_write(int lane, int64_t i, double ge, double gp, double ai,
+                                               uint32_t* __restrict__ qf) {
   const float qv = (float)(-ai * fma(ai, ge, gp));
   uint32_t h, mm, l;
   split3_bf16(qv, h, mm, l);
@@ -128,6 +123,17 @@ __device__ __forceinline__ void cd_query_row(int lane, int64_t i, int bl, int kd
     word = pack2(aw[2 * w], aw[2 * w + 1]);
   }
   if (lane < 16) qf[i * 16 + lane] = word;
+}
+
+__device__ __forceinline__ void cd_query_row(int lane, int64_t i, int bl, int kd, double gp,
+                                             const double* __restrict__ Ht, const float* __restrict__ ex,
+                                             double ai, uint32_t* __restrict__ qf) {
+  const int p = lane & 7;
+  const double* hr = Ht + (int64_t)(8 * bl + p) * kd + 8 * bl;
+  double ge = 0.0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ge = fma(hr[k], (double)ex[k], ge);
+  cd_query_write(lane, i, ge, gp, ai, qf);
 }
 
 // Query fragments for the first block of a tile (later blocks get theirs from
@@ -240,11 +246,15 @@ __device__ __forceinline__ double wave_sum_d(double x) {
 
 // One wave per row: merge the slices' top-2 lists, re-score the two
 // finalists exactly in float64 and move on a strict decrease; then update
-// the tile gradient and write the next block's query fragments.  Loads that
-// do not depend on the merge are issued first.  Lane l = 8 p + k holds
+// the tile gradient and write the next block's query fragments.  Everything
+// that does not depend on the merge (current and next codewords, the H
+// entries of the gradient update and of the next query, the gradient) is
+// loaded first, so a row costs two dependent memory round trips: the
+// candidates, then the finalists' codewords.  Lane l = 8 p + k holds
 // H[8 bl + p][8 bl + k] of the block's diagonal, so the exact change
 //   dF(c) = 1/2 d^T G d - d^T g,   d = a (e_c - e_x)
 // is one product per lane and a wave sum.
+constexpr int CD_COLS_LANE = 4;   // tile columns per lane in the gradient update (tile width <= 256)
 __global__ __launch_bounds__(256) void cd_update_kernel(int64_t m, int64_t n, int64_t b, int bl, int kd, int nslices,
                                                         double* __restrict__ Gt, const double* __restrict__ Ht,
                                                         const float* __restrict__ e32, const float* __restrict__ a,
@@ -260,13 +270,35 @@ __global__ __launch_bounds__(256) void cd_update_kernel(int64_t m, int64_t n, in
   const int c0 = 8 * (bl + 1);          // the next block's first column in the tile
   const bool has_next = c0 < kd;
 
-  // independent loads
+  // ---- loads that do not depend on the merge
   const int cx = codes[i * B + b];
   const int cn = has_next ? codes[i * B + b + 1] : 0;
   const double ai = a[i];
   const double hpk = Ht[(int64_t)(8 * bl + p) * kd + 8 * bl + k];
   const double gpp = Gt[i * kd + 8 * bl + p];
   const double gnext = has_next ? Gt[i * kd + c0 + k] : 0.0;
+  const float exp_ = e32[(int64_t)cx * 8 + p], exk = e32[(int64_t)cx * 8 + k];
+  float exq[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) exq[q] = e32[(int64_t)cx * 8 + q];
+  // gradient update operands: column jc = lane + 64 u of the tile, rows 8 bl + q of
+  // H's diagonal tile (symmetric, read as H[8 bl + q][jc] so the loads coalesce)
+  double gcol[CD_COLS_LANE], hcol[CD_COLS_LANE][8];
+#pragma unroll
+  for (int u = 0; u < CD_COLS_LANE; ++u) {
+    const int jc = lane + 64 * u;
+    gcol[u] = jc < kd ? Gt[i * kd + jc] : 0.0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) hcol[u][q] = jc < kd ? Ht[(int64_t)(8 * bl + q) * kd + jc] : 0.0;
+  }
+  // next block's query operands (lane k of each group of 8 builds q[k])
+  double hnext[8];
+  float exn[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    hnext[q] = has_next ? Ht[(int64_t)(c0 + k) * kd + c0 + q] : 0.0;
+    exn[q] = e32[(int64_t)cn * 8 + q];
+  }
   Cand o[2][2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -279,8 +311,9 @@ __global__ __launch_bounds__(256) void cd_update_kernel(int64_t m, int64_t n, in
       o[r][1] = {sv.y, iv.y};
     }
   }
-  // top 2 over all slices (lane butterfly; the top two of a totally ordered
-  // set do not depend on the merge order)
+
+  // ---- top 2 over all slices (lane butterfly; the top two of a totally
+  // ordered set do not depend on the merge order)
   Cand c1 = {INFINITY, 0x7fffffff}, c2 = {INFINITY, 0x7fffffff};
   for (int base = 0; base < nslices; base += 64) {
     Cand o1, o2;
@@ -305,53 +338,71 @@ __global__ __launch_bounds__(256) void cd_update_kernel(int64_t m, int64_t n, in
     merge_top2(c1, c2, o1, o2);
   }
 
-  const float* ex = e32 + (int64_t)cx * 8;
-  double bestF = 0.0;
-  int bestk = cx;
+  // ---- the finalists' codewords, then the exact re-scoring
   const int cands[2] = {c1.i, c2.i};
+  float ec[2][8], ecp[2], eck[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const bool ok = cands[c] != 0x7fffffff;
+    const int64_t base_c = ok ? (int64_t)cands[c] * 8 : 0;
+    ecp[c] = e32[base_c + p];
+    eck[c] = e32[base_c + k];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ec[c][q] = e32[base_c + q];
+  }
+  double bestF = 0.0;
+  int bestk = cx, bestc = -1;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int k2 = cands[c];
     if (k2 == 0x7fffffff || k2 == cx) continue;   // uniform over the wave
-    const float* en = e32 + (int64_t)k2 * 8;
-    const double dp = ai * ((double)en[p] - (double)ex[p]);
-    const double dk = ai * ((double)en[k] - (double)ex[k]);
+    const double dp = ai * ((double)ecp[c] - (double)exp_);
+    const double dk = ai * ((double)eck[c] - (double)exk);
     double term = dp * (0.5 * hpk * dk);
     if (k == 0) term -= dp * gpp;
     const double f = wave_sum_d(term);
     if (f < bestF || (f == bestF && bestk != cx && k2 < bestk)) {
       bestF = f;
       bestk = k2;
+      bestc = c;
     }
   }
   const bool moved = bestk != cx;   // uniform over the wave
   double dl[8];
-  const float* eb = e32 + (int64_t)bestk * 8;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dl[q] = moved ? ai * ((double)eb[q] - (double)ex[q]) : 0.0;
+  for (int q = 0; q < 8; ++q) {
+    const float eb = bestc == 1 ? ec[1][q] : ec[0][q];
+    dl[q] = moved ? ai * ((double)eb - (double)exq[q]) : 0.0;
+  }
   if (lane < 8) Delta[i * kd + 8 * bl + lane] = dl[lane];
   if (moved && lane == 0) {
     codes[i * B + b] = bestk;
     changes[i] += 1;
   }
-  // g_j -= sum_q H[j][8 bl + q] delta_q for every column j of the tile, read
-  // as H[8 bl + q][j] (the diagonal tile is symmetric) so the loads coalesce;
-  // the lanes owning the next block's columns keep their new values
+  // g_j -= sum_q H[j][8 bl + q] delta_q for every column j of the tile; the
+  // lanes owning the next block's columns keep their new values
   double gk = 0.0;
   if (moved) {
-    for (int jc = lane; jc < kd; jc += 64) {
-      double sacc = 0.0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) sacc = fma(Ht[(int64_t)(8 * bl + q) * kd + jc], dl[q], sacc);
-      const double nv = Gt[i * kd + jc] - sacc;
-      Gt[i * kd + jc] = nv;
-      if (jc >= c0 && jc < c0 + 8) gk = nv;
+    for (int u = 0; u < CD_COLS_LANE; ++u) {
+      const int jc = lane + 64 * u;
+      if (jc < kd) {
+        double sacc = 0.0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sacc = fma(hcol[u][q], dl[q], sacc);
+        const double nv = gcol[u] - sacc;
+        Gt[i * kd + jc] = nv;
+        if (jc >= c0 && jc < c0 + 8) gk = nv;
+      }
     }
   }
-  // the next block's query fragments
+  // ---- the next block's query fragments
   if (has_next) {
     const double gp = moved ? shfl_d(gk, (c0 & 63) + k) : gnext;
-    cd_query_row(lane, i, bl + 1, kd, gp, Ht, e32 + (int64_t)cn * 8, ai, qf);
+    double ge = 0.0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ge = fma(hnext[q], (double)exn[q], ge);
+    cd_query_write(lane, i, ge, gp, ai, qf);
   }
 }
 

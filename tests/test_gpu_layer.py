@@ -111,3 +111,20 @@ def test_scale_metamorphic():
     assert np.array_equal(g["codes"], gs["codes"])
     assert np.allclose(gs["beta_tr"], g["beta_tr"] / 16, rtol=1e-5)
     assert np.allclose(gs["gamma1_tr"], g["gamma1_tr"] / 16, rtol=1e-5)
+
+
+def test_cd_row_groups_on_streams():
+    """Layers of >= 1024 rows run their CD sweeps as two row groups on streams
+    of their own; each row's result must equal solving its group alone (both
+    halves use the same kernels and split counts), for the lattice and the
+    scalar CD."""
+    for d, extra in ((8, dict(K=1000, r=60)), (1, dict(bits=3))):
+        L = S.make_layer("grp", 1024, 64, seed=35, d=d, power=0.6, T_vamp=3, **extra)
+        full = run_gpu(L)
+        for lo, hi in ((0, 512), (512, 1024)):
+            Lh = S.Layer("half", np.ascontiguousarray(L.W[lo:hi]), L.s, L.V, L.E, L.a[lo:hi], L.o[lo:hi], L.d,
+                         L.T_vamp, L.n_cd, L.damping)
+            part = run_gpu(Lh)
+            for k in ("codes", "cd_changes", "beta_tr", "gamma1_tr"):
+                assert np.array_equal(part[k], full[k][lo:hi]), (d, lo, k)
+        assert full["cd_changes"].sum() > 0
