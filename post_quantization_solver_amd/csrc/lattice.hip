@@ -174,10 +174,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
   const int g = lane >> 4;
   const int64_t B = n / 8;
   const int64_t total = ONLINE ? (int64_t)(*flag_count) : m * B;
-  // FAST: one workgroup per 256 queries.  ONLINE: the grid strides over the
-  // flagged list (its length is only known on the device).
-  const int64_t vstride = ONLINE ? (int64_t)gridDim.x : total;
-  for (int64_t vb = blockIdx.x; vb * QWG < total; vb += vstride) {   // uniform per workgroup
+  // one group of QWG queries (uniform per workgroup)
+  auto group = [&](const int64_t vb) {
   const int64_t qbase = vb * QWG + wave * QW;
 
   // query index -> (row, block); ONLINE reads it from the flag list
@@ -359,7 +357,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
       }
     }
   }
-  __syncthreads();   // the next query group reuses the LDS
+  };
+  // FAST: one workgroup per QWG queries.  ONLINE: the grid strides over the
+  // flagged list (its length is only known on the device).
+  if (ONLINE) {
+    for (int64_t vb = blockIdx.x; vb * QWG < total; vb += gridDim.x) {
+      group(vb);
+      __syncthreads();   // the next query group reuses the LDS
+    }
+  } else if ((int64_t)blockIdx.x * QWG < total) {
+    group((int64_t)blockIdx.x);
   }
 }
 
