@@ -35,6 +35,12 @@ Readings where the pages are silent (each also listed in the design doc):
       ascending b by CD.
   R9  CD accepts strict improvements only; argmin / argmax ties go to the
       lowest codeword index.
+  A1  anchored prior (hyper-parameter paragraph: anchor scale tau = 0.2;
+      tau -> infinity is the unanchored limit; the form is not printed):
+      rho_b(c) proportional to exp(-||c - w_b||^2 / (2 tau^2 a^2)), a Gaussian
+      anchor at the row's own weights whose width is tau codebook units
+      (a = the row's codebook scale).  It enters the denoiser and the MAP as a
+      per-block log-prior; CD minimises the layer objective alone.
   G1  (guard) the denoiser's variance sum is floored at
       n * (1e-12 * a)^2, a = the row's codebook scale; it never binds on
       continuous data.
@@ -94,27 +100,49 @@ def nearest_codeword(x, C, d):
 
 def block_logits(r1b, gamma1, C, log_prior=None):
     """log q_b(c) up to a constant: log rho_b(c) - gamma1/2 ||c - r1_b||^2
-    (key design 1, the blockwise discrete denoiser)."""
+    (key design 1, the blockwise discrete denoiser).  log_prior: one value
+    per codeword (K), or one row per block (nb x K)."""
     L = -0.5 * gamma1 * sq_dist(r1b, C)
     if log_prior is not None:
-        L = L + np.asarray(log_prior, dtype=np.float64)[None, :]
+        lp = np.asarray(log_prior, dtype=np.float64)
+        L = L + (lp[None, :] if lp.ndim == 1 else lp)
     return L
 
 
-def denoise(r1, gamma1, C, d, log_prior=None, return_q=False):
+def anchor_log_prior(wb, lam, C):
+    """Reading A1: log rho_b(c) = -lam/2 ||c - w_b||^2 for the blocks wb (nb x d),
+    lam = 1 / (tau a)^2."""
+    return -0.5 * float(lam) * sq_dist(wb, C)
+
+
+def anchor_lambda(tau, a):
+    """Precision of the anchored prior (reading A1): 1 / (tau a)^2; 0 when unanchored."""
+    if tau is None or not np.isfinite(tau) or tau <= 0:
+        return 0.0
+    return 1.0 / (float(tau) * float(a)) ** 2
+
+
+def denoise(r1, gamma1, C, d, log_prior=None, return_q=False, anchor=None):
     """Blockwise discrete denoiser (key design 1).
 
     For every block: q_b(c) = softmax_c of the block logits, posterior mean
     x_hat1_b = sum_c q_b(c) c and the trace of the posterior covariance
-    v_b = sum_c q_b(c) ||c - x_hat1_b||^2.  Returns (x_hat1, v, q or None).
+    v_b = sum_c q_b(c) ||c - x_hat1_b||^2.  anchor = (w, lam) adds the
+    anchored prior of reading A1.  Returns (x_hat1, v, q or None).
     """
     R = _blocks(r1, d)
     B, K = R.shape[0], C.shape[0]
+    Wb = _blocks(anchor[0], d) if anchor is not None else None
     xhat = np.empty_like(R)
     v = np.empty(B)
     q_all = np.empty((B, K)) if return_q else None
     for b0, b1 in _chunks(B, K, d):
-        L = block_logits(R[b0:b1], gamma1, C, log_prior)
+        lp = log_prior
+        if anchor is not None and anchor[1] > 0:
+            lp = anchor_log_prior(Wb[b0:b1], anchor[1], C)
+            if log_prior is not None:
+                lp = lp + np.asarray(log_prior, dtype=np.float64)[None, :]
+        L = block_logits(R[b0:b1], gamma1, C, lp)
         L = L - L.max(axis=1, keepdims=True)
         q = np.exp(L)
         q /= q.sum(axis=1, keepdims=True)
@@ -198,7 +226,7 @@ def vamp_init(w, s, V, C, d):
 
 
 def vamp(w, s, V, C, d, T_vamp, damping, a_scale, beta0=None, denoiser=None,
-         fixed_beta=False, record=False):
+         fixed_beta=False, record=False, anchor_tau=None):
     """T_vamp iterations of rank-space VAMP with the beta M-step.
 
     `denoiser(r1, gamma1) -> (x_hat1, v_blocks)` defaults to the discrete
@@ -213,7 +241,8 @@ def vamp(w, s, V, C, d, T_vamp, damping, a_scale, beta0=None, denoiser=None,
     if beta0 is not None:
         beta = float(beta0)
     if denoiser is None:
-        denoiser = lambda r, g: denoise(r, g, C, d)[:2]  # noqa: E731
+        anchor = (w, anchor_lambda(anchor_tau, a_scale))
+        denoiser = lambda r, g: denoise(r, g, C, d, anchor=anchor)[:2]  # noqa: E731
     r1 = w.copy()
     tr_beta, tr_g1, tr_g2, tr_eta1 = [beta], [gamma1], [], []
     hist = []
@@ -247,14 +276,21 @@ def vamp(w, s, V, C, d, T_vamp, damping, a_scale, beta0=None, denoiser=None,
 # stage 2: hard decisions
 # ----------------------------------------------------------------------------
 
-def map_codes(r1, gamma1, C, d, log_prior=None):
+def map_codes(r1, gamma1, C, d, log_prior=None, anchor=None):
     """Marginal MAP projection (key design 3): x_b^(0) = argmax_c q_b(c)
-    evaluated at (r1^T, gamma1^T); ties to the lowest index."""
+    evaluated at (r1^T, gamma1^T); ties to the lowest index.  anchor = (w, lam)
+    adds the anchored prior of reading A1."""
     R = _blocks(r1, d)
     B, K = R.shape[0], C.shape[0]
+    Wb = _blocks(anchor[0], d) if anchor is not None else None
     out = np.empty(B, dtype=np.int64)
     for b0, b1 in _chunks(B, K, d):
-        out[b0:b1] = np.argmax(block_logits(R[b0:b1], gamma1, C, log_prior), axis=1)
+        lp = log_prior
+        if anchor is not None and anchor[1] > 0:
+            lp = anchor_log_prior(Wb[b0:b1], anchor[1], C)
+            if log_prior is not None:
+                lp = lp + np.asarray(log_prior, dtype=np.float64)[None, :]
+        out[b0:b1] = np.argmax(block_logits(R[b0:b1], gamma1, C, lp), axis=1)
     return out
 
 
@@ -312,8 +348,9 @@ def codes_objective(w, codes, C, d, s, V):
 # the whole row
 # ----------------------------------------------------------------------------
 
-def solve_row(w, s, V, E, a, o, d, T_vamp, n_cd, damping, beta0=None, record=False):
+def solve_row(w, s, V, E, a, o, d, T_vamp, n_cd, damping, beta0=None, record=False, anchor_tau=None):
     """MPQ on one row: VAMP (T_vamp iterations) -> marginal MAP -> block CD.
+    anchor_tau: the anchored prior of reading A1 (None: uniform prior).
 
     Returns dict(codes, objective, beta_tr, gamma1_tr, gamma2_tr, eta1_tr,
     cd_changes, fallbacks, map_codes, rtn_codes, frozen[, history]).
@@ -328,8 +365,8 @@ def solve_row(w, s, V, E, a, o, d, T_vamp, n_cd, damping, beta0=None, record=Fal
                     gamma1_tr=np.full(T_vamp + 1, inf), gamma2_tr=np.full(T_vamp, inf),
                     eta1_tr=np.full(T_vamp, inf), cd_changes=[0] * n_cd, fallbacks=0,
                     map_codes=rtn, rtn_codes=rtn, frozen=True, history=[])
-    st = vamp(w, s, V, C, d, T_vamp, damping, a, beta0=beta0, record=record)
-    mc = map_codes(st["r1"], st["gamma1"], C, d)
+    st = vamp(w, s, V, C, d, T_vamp, damping, a, beta0=beta0, record=record, anchor_tau=anchor_tau)
+    mc = map_codes(st["r1"], st["gamma1"], C, d, anchor=(w, anchor_lambda(anchor_tau, a)))
     codes, changes = block_cd(mc, w, s, V, C, d, n_cd)
     changes = list(changes) + [0] * (n_cd - len(changes))
     out = dict(codes=codes, objective=codes_objective(w, codes, C, d, s, V),

@@ -54,11 +54,11 @@ def _solve(job):
     if _ROOT not in sys.path:
         sys.path.insert(0, _ROOT)
     from oracle import mpq_oracle as O
-    path, i, d, T, S, rho, record = job
+    path, i, d, T, S, rho, record, tau = job
     A = _load(path)
     w = np.asarray(A["W"][i], np.float64)
     a, o = float(A["a"][i]), float(A["o"][i])
-    res = O.solve_row(w, A["s"], A["V"], A["E"], a, o, d, T, S, rho, record=record)
+    res = O.solve_row(w, A["s"], A["V"], A["E"], a, o, d, T, S, rho, record=record, anchor_tau=tau)
     C = O.row_codewords(A["E"], a, o)
     res["map_objective"] = O.codes_objective(w, res["map_codes"], C, d, A["s"], A["V"])
     res["rtn_objective"] = O.codes_objective(w, res["rtn_codes"], C, d, A["s"], A["V"])
@@ -93,13 +93,14 @@ def _run(L, fn, make_jobs, max_workers):
         shutil.rmtree(tmp, ignore_errors=True)
 
 
-def solve_rows(L, rows, T_vamp=None, n_cd=None, record=False, max_workers=None):
+def solve_rows(L, rows, T_vamp=None, n_cd=None, record=False, max_workers=None, anchor_tau=None):
     """Oracle results for the given rows of a layer (attributes W, s, V, E, a,
-    o, d, T_vamp, n_cd, damping), in row order."""
+    o, d, T_vamp, n_cd, damping), in row order; anchor_tau: the anchored prior."""
     T = L.T_vamp if T_vamp is None else T_vamp
     S = L.n_cd if n_cd is None else n_cd
     rows = [int(i) for i in rows]
-    return _run(L, _solve, lambda tmp: [(tmp, i, L.d, T, S, L.damping, record) for i in rows], max_workers)
+    return _run(L, _solve, lambda tmp: [(tmp, i, L.d, T, S, L.damping, record, anchor_tau) for i in rows],
+                max_workers)
 
 
 def map_rows(L, rows, r1, gamma1, max_workers=None):

@@ -7,11 +7,11 @@ from oracle import mpq_oracle as O
 import test_oracle_pins as P
 
 _orig = {k: getattr(O, k) for k in ("denoise", "extrinsic_denoiser_to_linear", "linear_module",
-                                     "beta_em", "block_cd", "rank_target", "block_logits")}
+                                     "beta_em", "block_cd", "rank_target", "block_logits", "anchor_log_prior")}
 
 
-def denoise_var_about_r(r1, gamma1, C, d, log_prior=None, return_q=False):
-    xh, v, q = _orig["denoise"](r1, gamma1, C, d, log_prior, True)
+def denoise_var_about_r(r1, gamma1, C, d, log_prior=None, return_q=False, anchor=None):
+    xh, v, q = _orig["denoise"](r1, gamma1, C, d, log_prior, True, anchor)
     R = np.asarray(r1, float).reshape(-1, d)
     v = np.einsum("bk,bk->b", q, O.sq_dist(R, C))
     return xh, v, (q if return_q else None)
@@ -103,6 +103,14 @@ def cd_sign(codes, w, s, V, C, d, n_cd):
     return codes, changes
 
 
+def anchor_wrong_sign(wb, lam, C):
+    return -_orig["anchor_log_prior"](wb, lam, C)
+
+
+def anchor_no_half(wb, lam, C):
+    return 2.0 * _orig["anchor_log_prior"](wb, lam, C)
+
+
 def rank_target_transposed(w, s, V):
     return np.asarray(s, float) * (np.asarray(V, float) @ np.asarray(w, float))
 
@@ -120,6 +128,8 @@ MUTATIONS = [
     ("beta_em", beta_not_squared, [P.check_beta_dense]),
     ("block_cd", cd_sign, [P.check_cd_bruteforce, P.check_worked_example_mpq]),
     ("rank_target", rank_target_transposed, [P.check_worked_example_mpq, P.check_cd_bruteforce]),
+    ("anchor_log_prior", anchor_wrong_sign, [P.check_anchor_prior]),
+    ("anchor_log_prior", anchor_no_half, [P.check_anchor_prior]),
 ]
 
 

@@ -470,6 +470,62 @@ def test_frozen_row():
     assert list(res["codes"]) == [0, 1, 6, 4]
 
 
+# ----------------------------------------------------------------------------
+# anchored prior (reading A1: hyper-parameter paragraph, tau = 0.2; tau -> inf
+# is the unanchored limit)
+# ----------------------------------------------------------------------------
+
+def check_anchor_prior(seed=11, nb=40, d=2, K=24):
+    """Completing the square: a Gaussian anchor of precision lam at w turns
+    the block posterior at (r, gamma) into the unanchored one at
+    ((gamma r + lam w) / (gamma + lam), gamma + lam) -- the same softmax,
+    derived independently of how the oracle adds the log-prior.  Also the
+    limits lam = 0 (uniform prior) and lam -> inf (the codeword nearest w)."""
+    g = rng(seed)
+    C = g.standard_normal((K, d))
+    r = g.standard_normal(nb * d) * 1.3
+    w = g.standard_normal(nb * d)
+    for gamma, lam in ((0.7, 2.5), (4.0, 0.3), (1e-3, 9.0)):
+        xa, va, _ = O.denoise(r, gamma, C, d, anchor=(w, lam))
+        reff = (gamma * r + lam * w) / (gamma + lam)
+        xu, vu, _ = O.denoise(reff, gamma + lam, C, d)
+        assert np.allclose(xa, xu, rtol=1e-10, atol=1e-12)
+        assert np.allclose(va, vu, rtol=1e-10, atol=1e-12)
+        ma = O.map_codes(r, gamma, C, d, anchor=(w, lam))
+        assert np.array_equal(ma, O.nearest_codeword(reff, C, d))
+    x0, v0, _ = O.denoise(r, 2.0, C, d, anchor=(w, 0.0))
+    xu, vu, _ = O.denoise(r, 2.0, C, d)
+    assert np.array_equal(x0, xu) and np.array_equal(v0, vu)
+    xs, _, _ = O.denoise(r, 2.0, C, d, anchor=(w, 1e6))
+    near_w = O.nearest_codeword(w, C, d)
+    assert np.allclose(xs, C[near_w].reshape(-1), atol=1e-6)
+    assert np.array_equal(O.map_codes(r, 2.0, C, d, anchor=(w, 1e6)), near_w)
+    assert O.anchor_lambda(0.2, 0.5) == pytest.approx(100.0)
+    assert O.anchor_lambda(None, 0.5) == 0.0
+
+
+def test_anchor_prior():
+    check_anchor_prior()
+
+
+def test_anchor_whole_row_limits():
+    """tau = None and a huge tau give the unanchored solve; with T_vamp = 0 the
+    anchored MAP (centred at w, like the cavity) is round to nearest; at the
+    pages' tau = 0.2 CD only lowers the objective from the MAP point."""
+    L = S.make_layer("anc", 2, 32, seed=12, d=1, bits=3, T_vamp=4)
+    i = 0
+    C = O.row_codewords(L.E, L.a[i], L.o[i])
+    t0 = O.solve_row(L.W[i], L.s, L.V, L.E, L.a[i], L.o[i], 1, 0, 0, 0.5, anchor_tau=0.05)
+    assert list(t0["map_codes"]) == list(O.nearest_codeword(L.W[i], C, 1))
+    t2 = O.solve_row(L.W[i], L.s, L.V, L.E, L.a[i], L.o[i], 1, 4, 3, 0.5, anchor_tau=0.2)
+    f_map = O.codes_objective(L.W[i], t2["map_codes"], C, 1, L.s, L.V)
+    assert np.isfinite(t2["objective"]) and t2["objective"] <= f_map + 1e-15
+    base = O.solve_row(L.W[i], L.s, L.V, L.E, L.a[i], L.o[i], 1, 4, 3, 0.5)
+    loose = O.solve_row(L.W[i], L.s, L.V, L.E, L.a[i], L.o[i], 1, 4, 3, 0.5, anchor_tau=1e9)
+    assert list(base["codes"]) == list(loose["codes"])
+    assert np.allclose(base["gamma1_tr"], loose["gamma1_tr"], rtol=1e-9)
+
+
 def test_mpq_beats_rtn_on_c1_rows():
     """Sanity on the small workload: MPQ never ends above RTN + CD's start."""
     L = S.make_config("c1")
