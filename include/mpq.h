@@ -65,6 +65,14 @@ typedef struct {
   uint32_t prof_mask;     /* with MPQ_F_PROFILE: bit k times category k (MPQ_PROF_*) */
   double* prof_ms;        /* host, MPQ_PROF_COUNT entries: milliseconds are ADDED */
   int64_t* prof_launches; /* host, MPQ_PROF_COUNT entries: kernel launches ADDED */
+  float anchor_tau;       /* > 0: anchored codebook prior of scale tau (the hyper-
+                             parameter paragraph's anchor, default there 0.2; the
+                             form is not printed -- read here as
+                             rho_b(c) ~ exp(-||c - w_b||^2 / (2 tau^2 a_i^2)), a_i
+                             the row's codebook scale), used by the denoiser and
+                             the marginal MAP; <= 0 (or NaN): uniform prior */
+  const float* anchor_w;  /* device, m x n: the weights w the prior is anchored at,
+                             for mpq_vamp_step (mpq_quantize_layer anchors at its W) */
 } mpq_options;
 
 #define MPQ_F_FIXED_BETA 1u
@@ -140,7 +148,9 @@ int mpq_denoise(const float* R1, const float* gamma1, int64_t m, int64_t n,
  * denoise -> extrinsic (r2, gamma2) -> linear module -> beta M-step with
  * damping -> extrinsic (r1', gamma1').  Optional outputs (may be NULL):
  * xhat1 (m x n), eta1 (m), gamma2 (m), r2 (m x n), fallback (m int32: 1
- * when eta1 <= gamma1 and the posterior was passed through). */
+ * when eta1 <= gamma1 and the posterior was passed through).  With
+ * opt->anchor_tau > 0, opt->anchor_w must point to the weights (else MPQ_ENULL)
+ * and xhat1 is the anchored posterior's mean. */
 int mpq_vamp_step(float* R1, float* gamma1, float* beta, const float* ytil, int64_t m, int64_t n,
                   const float* s, const float* V, int64_t r, const float* cb, int64_t K, int64_t d,
                   const float* row_scale, const float* row_offset, float damping, const mpq_options* opt,

@@ -40,7 +40,8 @@ PROF_COUNT = len(PROF_NAMES)
 
 class Options(ctypes.Structure):
     _fields_ = [("beta0", ctypes.c_float), ("flags", ctypes.c_uint32), ("prof_mask", ctypes.c_uint32),
-                ("prof_ms", ctypes.POINTER(ctypes.c_double)), ("prof_launches", ctypes.POINTER(ctypes.c_int64))]
+                ("prof_ms", ctypes.POINTER(ctypes.c_double)), ("prof_launches", ctypes.POINTER(ctypes.c_int64)),
+                ("anchor_tau", ctypes.c_float), ("anchor_w", ctypes.c_void_p)]
 
 
 class Profile:
@@ -146,10 +147,11 @@ def _workspace(m, n, r, K, d, device):
     return torch.empty(nb, dtype=torch.uint8, device=device)
 
 
-def _opts(beta0=None, fixed_beta=False, profile=None):
+def _opts(beta0=None, fixed_beta=False, profile=None, anchor_tau=None, anchor_w=None):
     flags = (F_FIXED_BETA if fixed_beta else 0) | (F_PROFILE if profile is not None else 0)
     o = Options(float(beta0) if beta0 else 0.0, flags, profile.mask if profile is not None else 0,
-                profile.ms if profile is not None else None, profile.launches if profile is not None else None)
+                profile.ms if profile is not None else None, profile.launches if profile is not None else None,
+                float(anchor_tau) if anchor_tau else 0.0, anchor_w.data_ptr() if anchor_w is not None else None)
     return ctypes.byref(o), o
 
 
@@ -161,12 +163,13 @@ def _check(rc, what):
 # ---------------------------------------------------------------- entry points
 
 def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, damping=0.5, beta0=None,
-                   fixed_beta=False, workspace=None, traces=True, profile=None, outputs=None):
+                   fixed_beta=False, workspace=None, traces=True, profile=None, outputs=None, anchor_tau=None):
     """Full MPQ solve of one layer (mpq_quantize_layer).
 
     Returns dict(codes, beta_tr, gamma1_tr, gamma2_tr, cd_changes) of device
     tensors.  `profile` (a Profile) turns on the library's event timing;
-    `outputs` (a dict from a previous call) reuses its output tensors.
+    `outputs` (a dict from a previous call) reuses its output tensors;
+    `anchor_tau` > 0 selects the anchored codebook prior (None: uniform).
     """
     import torch
     m, n = W.shape
@@ -188,7 +191,7 @@ def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, dampin
         g2 = torch.empty((m, T_vamp), dtype=torch.float32, device=dev) if traces and T_vamp > 0 else None
         ch = torch.zeros((m, n_cd), dtype=torch.int32, device=dev) if traces and n_cd > 0 else None
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
-    op, _keep = _opts(beta0, fixed_beta, profile)
+    op, _keep = _opts(beta0, fixed_beta, profile, anchor_tau)
     rc = load_library().mpq_quantize_layer(
         _ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d, _ptr(row_scale),
         _ptr(row_offset), int(T_vamp), int(n_cd), float(damping), op, _ptr(codes), _ptr(bt), _ptr(g1), _ptr(g2),
@@ -236,8 +239,9 @@ def denoise(R1, gamma1, cb, row_scale, row_offset, workspace=None):
 
 
 def vamp_step(R1, gamma1, beta, ytil, s, V, cb, row_scale, row_offset, damping=0.5, fixed_beta=False,
-              workspace=None):
-    """One VAMP iteration in place on (R1, gamma1, beta); returns the diagnostics."""
+              workspace=None, anchor_tau=None, W=None):
+    """One VAMP iteration in place on (R1, gamma1, beta); returns the diagnostics.
+    With `anchor_tau` > 0 the prior is anchored at the weights `W`."""
     import torch
     m, n = R1.shape
     r = s.shape[0]
@@ -252,7 +256,9 @@ def vamp_step(R1, gamma1, beta, ytil, s, V, cb, row_scale, row_offset, damping=0
     gamma2 = torch.empty(m, dtype=torch.float32, device=dev)
     fb = torch.empty(m, dtype=torch.int32, device=dev)
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
-    op, _keep = _opts(None, fixed_beta)
+    if anchor_tau:
+        _dev(W, torch.float32, "W", (m, n))
+    op, _keep = _opts(None, fixed_beta, None, anchor_tau, W)
     rc = load_library().mpq_vamp_step(_ptr(R1), _ptr(gamma1), _ptr(beta), _ptr(ytil), m, n, _ptr(s), _ptr(V), r,
                                       E.ctypes.data_as(ctypes.c_void_p), K, d, _ptr(row_scale), _ptr(row_offset),
                                       float(damping), op, _ptr(xhat), _ptr(eta1), _ptr(gamma2), _ptr(r2), _ptr(fb),

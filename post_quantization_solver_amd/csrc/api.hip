@@ -76,7 +76,7 @@ struct Layout {
 
 enum Region {
   R_VS, R_VST, R_YTIL, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI,
-  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_SPLIT, R_TKEY, R_QF, R_VSP, R_VSTP, R_R2P, R_ZP, R_COUNT
+  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_SPLIT, R_TKEY, R_QF, R_VSP, R_VSTP, R_R2P, R_ZP, R_ANCH, R_COUNT
 };
 
 size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -125,6 +125,7 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
   sz[R_VSTP] = packed_split_words(r, n) * sizeof(uint32_t);
   sz[R_R2P] = packed_split_words(m, n) * sizeof(uint32_t);
   sz[R_ZP] = packed_split_words(m, r) * sizeof(uint32_t);
+  sz[R_ANCH] = (size_t)m * n * f;   // anchored-prior cavity mean
   size_t o = 0;
   for (int k = 0; k < R_COUNT; ++k) {
     L.off[k] = o;
@@ -170,6 +171,11 @@ struct Ctx {
   float* coef() const { return rowv(4); }
   float* betalin() const { return rowv(5); }
   float* rowsq() const { return rowv(6); }
+  float* gamma_anchor() const { return rowv(7); }
+  // anchored codebook prior (mpq_options.anchor_tau > 0) and its weights
+  float anchor_tau = 0.f;
+  const float* anchor_w = nullptr;
+  bool anchored() const { return anchor_tau > 0.f; }
 };
 
 bool bf16_exact(float x) {
@@ -403,7 +409,17 @@ int run_iteration(Ctx& c, float* R1, float* gamma1, float* beta, const float* yt
   const Layout& L = c.L;
   float* X1 = c.p(R_X1);
   float* R2 = c.p(R_R2);
-  int rc = denoise(c, R1, gamma1, a, o, X1, c.p(R_VBLK));
+  // the denoiser's cavity: (r1, gamma1), or with the anchored prior the
+  // completed-square (r_eff, gamma1 + lam)
+  const float* Rd = R1;
+  const float* gd = gamma1;
+  if (c.anchored()) {
+    TIMED(c, MPQ_PROF_OTHER, launch_anchor(R1, c.anchor_w, gamma1, a, c.anchor_tau, L.m, L.n, c.p(R_ANCH),
+                                           c.gamma_anchor(), c.st));
+    Rd = c.p(R_ANCH);
+    gd = c.gamma_anchor();
+  }
+  int rc = denoise(c, Rd, gd, a, o, X1, c.p(R_VBLK));
   if (rc) return rc;
   if (xhat_out) TIMED(c, MPQ_PROF_OTHER, launch_copy_rows_f(X1, xhat_out, L.m * L.n, c.st));
   TIMED(c, MPQ_PROF_EXTRINSIC,
@@ -614,6 +630,7 @@ int solve_layer(Ctx& c, const float* W, const float* s, const float* V, const fl
   int rc = prepare_factors(c, V, s, T_vamp > 0);
   if (rc) return rc;
   const Layout& L = c.L;
+  c.anchor_w = W;
   const int fixed = (opt && (opt->flags & MPQ_F_FIXED_BETA)) ? 1 : 0;
   float* R1 = c.p(R_R1);
   rc = run_prologue(c, W, row_scale, row_offset, opt, c.p(R_YTIL), c.pi(R_CODES), c.gamma1(), c.beta());
@@ -628,8 +645,15 @@ int solve_layer(Ctx& c, const float* W, const float* s, const float* V, const fl
   }
   TIMED(c, MPQ_PROF_OTHER, launch_record(c.beta(), L.m, beta_tr, T_vamp + 1, T_vamp, c.st));
   TIMED(c, MPQ_PROF_OTHER, launch_record(c.gamma1(), L.m, gamma1_tr, T_vamp + 1, T_vamp, c.st));
-  // marginal MAP at (r1^T, gamma1^T); frozen rows keep r1 = w, i.e. their RTN codes
-  TIMED(c, MPQ_PROF_MAP, nearest(c, R1, codes, row_scale, row_offset));
+  // marginal MAP at (r1^T, gamma1^T); frozen rows keep r1 = w, i.e. their RTN
+  // codes.  With the anchored prior the argmax is the codeword nearest r_eff.
+  const float* Rm = R1;
+  if (c.anchored()) {
+    TIMED(c, MPQ_PROF_MAP, launch_anchor(R1, W, c.gamma1(), row_scale, c.anchor_tau, L.m, L.n, c.p(R_ANCH),
+                                         c.gamma_anchor(), c.st));
+    Rm = c.p(R_ANCH);
+  }
+  TIMED(c, MPQ_PROF_MAP, nearest(c, Rm, codes, row_scale, row_offset));
   return run_cd(c, W, row_scale, row_offset, n_cd, codes, cd_changes);
 }
 
@@ -640,6 +664,10 @@ int begin(Ctx& c, int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, const f
     c.prof.mask = opt->prof_mask;
     c.prof.ms = opt->prof_ms;
     c.prof.launches = opt->prof_launches;
+  }
+  if (opt && opt->anchor_tau > 0.f && std::isfinite(opt->anchor_tau)) {
+    c.anchor_tau = opt->anchor_tau;
+    c.anchor_w = opt->anchor_w;
   }
   int rc = check_shapes(m, n, r, K, d);
   if (rc) return rc;
@@ -751,6 +779,7 @@ int mpq_vamp_step(float* R1, float* gamma1, float* beta, const float* ytil, int6
   rc = begin(c, m, n, r, K, d, cb, workspace, ws_bytes, stream, opt);
   if (rc) return rc;
   if ((rc = upload_codebook(c, cb))) return rc;
+  if (c.anchored() && !c.anchor_w) return MPQ_ENULL;
   if ((rc = prepare_factors(c, V, s, true))) return rc;
   const int fixed = (opt && (opt->flags & MPQ_F_FIXED_BETA)) ? 1 : 0;
   return finish(c, run_iteration(c, R1, gamma1, beta, ytil, s, row_scale, row_offset, damping, fixed, xhat1, eta1,

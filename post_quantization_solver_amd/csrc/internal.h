@@ -91,6 +91,11 @@ hipError_t launch_beta(int64_t m, int64_t n, int64_t r, const float* s, const fl
                        const float* gamma2, float damping, int fixed_beta, float* beta, float* gamma1,
                        float* coef, hipStream_t st);
 
+// Anchored prior: Reff = (gamma R + lam W) / (gamma + lam), geff = gamma + lam
+// per row, lam = 1 / (tau a_i)^2.
+hipError_t launch_anchor(const float* R, const float* W, const float* gamma, const float* a, float tau, int64_t m,
+                         int64_t n, float* Reff, float* geff, hipStream_t st);
+
 // Trace / state bookkeeping.
 hipError_t launch_record(const float* src, int64_t m, float* dst, int64_t ld, int64_t col, hipStream_t st);
 hipError_t launch_copy_rows_f(const float* src, float* dst, int64_t count, hipStream_t st);

@@ -258,4 +258,42 @@ hipError_t launch_fill_i32(int32_t* dst, int64_t count, int32_t v, hipStream_t s
   return hipGetLastError();
 }
 
+// Anchored prior (the hyper-parameter paragraph's anchor scale tau; its form
+// is not printed, read as a Gaussian anchor of precision lam = 1 / (tau a_i)^2
+// at the row's weights).  Completing the square, the block posterior
+//   q_b(c) ~ exp(-lam/2 ||c - w_b||^2 - gamma/2 ||c - r_b||^2)
+// is the uniform-prior one at r_eff = (gamma r + lam w) / (gamma + lam) with
+// precision gamma + lam, so the denoiser and the MAP run unchanged on
+// (Reff, geff).  Rows with infinite precision keep r (frozen rows).
+__global__ void anchor_kernel(const float* __restrict__ R, const float* __restrict__ W,
+                              const float* __restrict__ gamma, const float* __restrict__ a, float tau, int64_t m,
+                              int64_t n, float* __restrict__ Reff, float* __restrict__ geff) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= m * n) return;
+  const int64_t i = k / n;
+  const float g = gamma[i];
+  const float ta = tau * a[i];
+  const float lam = 1.f / (ta * ta);
+  float out;
+  if (!isfinite(g)) {
+    out = R[k];
+  } else if (!isfinite(lam)) {
+    out = W[k];
+  } else {
+    const float inv = 1.f / (g + lam);
+    out = fmaf(g * inv, R[k], lam * inv * W[k]);
+  }
+  Reff[k] = out;
+  if (k - i * n == 0) geff[i] = isfinite(g) ? g + lam : g;
+}
+
+hipError_t launch_anchor(const float* R, const float* W, const float* gamma, const float* a, float tau, int64_t m,
+                         int64_t n, float* Reff, float* geff, hipStream_t st) {
+  const int64_t total = m * n;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(anchor_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, R, W, gamma, a, tau, m, n,
+                     Reff, geff);
+  return hipGetLastError();
+}
+
 }  // namespace mpq
