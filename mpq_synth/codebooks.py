@@ -59,17 +59,23 @@ def e8_codebook(K: int = 65536) -> np.ndarray:
     return np.ascontiguousarray(pts[order][:K].astype(np.float32))
 
 
-def scalar_grid(W: np.ndarray, bits: int):
-    """Min-Max per-row uniform grid.
+def scalar_grid(W: np.ndarray, bits: int, group: int = 0):
+    """Min-Max uniform grid per row, or per group of `group` consecutive columns.
 
-    Returns (E, a, o): E = arange(2^bits) as (K, 1) float32, and per-row
-    float32 a (scale) and o (= -scale * zero_point).  A constant row gets
-    scale 1 so its grid stays well defined.
+    Returns (E, a, o): E = arange(2^bits) as (K, 1) float32, and float32 a
+    (scale) and o (= -scale * zero_point), shape (m,) per row or (m, G) per
+    group.  A constant row or group gets scale 1 so its grid stays well defined.
     """
     K = 1 << bits
     W64 = np.asarray(W, dtype=np.float64)
-    lo = W64.min(1)
-    hi = W64.max(1)
+    if group:
+        m, n = W64.shape
+        G = (n + group - 1) // group
+        lo = np.stack([W64[:, k * group:(k + 1) * group].min(1) for k in range(G)], axis=1)
+        hi = np.stack([W64[:, k * group:(k + 1) * group].max(1) for k in range(G)], axis=1)
+    else:
+        lo = W64.min(1)
+        hi = W64.max(1)
     scale = (hi - lo) / (K - 1)
     scale = np.where(scale > 0, scale, 1.0)
     zero = np.round(-lo / scale)  # numpy rounds half to even

@@ -32,13 +32,14 @@ class Layer:
     s: np.ndarray          # r float32 (singular values)
     V: np.ndarray          # n x r float32, orthonormal columns
     E: np.ndarray          # K x d float32 base codebook
-    a: np.ndarray          # m float32 per-row codebook scale
-    o: np.ndarray          # m float32 per-row codebook offset
+    a: np.ndarray          # m float32 per-row codebook scale (m x G with group-wise grids)
+    o: np.ndarray          # m float32 per-row codebook offset (m x G with group-wise grids)
     d: int
     T_vamp: int
     n_cd: int
     damping: float
     meta: dict = field(default_factory=dict)
+    group: int = 0         # > 0: grids per group of this many columns (a, o are m x G)
 
     @property
     def m(self):
@@ -103,9 +104,10 @@ def draw_weights(rng, m, n, dist, outlier_frac=0.0, outlier_factor=8.0, outlier_
 
 def make_layer(name, m, n, *, seed, dist="normal", d=1, bits=3, K=None, power=0.5,
                lead=0, r=None, T_vamp=16, n_cd=3, damping=0.5, outlier_frac=0.0,
-               device=None, W=None, s=None, V=None):
-    """General seeded layer.  d = 1 -> Min-Max scalar grid with 2^bits levels;
-    d = 8 -> the first K points of E8 (K defaults to 65536)."""
+               device=None, W=None, s=None, V=None, group=0):
+    """General seeded layer.  d = 1 -> Min-Max scalar grid with 2^bits levels
+    (per row, or per group of `group` columns); d = 8 -> the first K points of
+    E8 (K defaults to 65536)."""
     ss = np.random.SeedSequence(seed)
     w_ss, v_ss, o_ss = ss.spawn(3)
     r = n if r is None else r
@@ -117,15 +119,17 @@ def make_layer(name, m, n, *, seed, dist="normal", d=1, bits=3, K=None, power=0.
     if s is None:
         s = spectrum(r, power, lead)
     if d == 1:
-        E, a, o = scalar_grid(W, bits)
+        E, a, o = scalar_grid(W, bits, group)
     elif d == 8:
         E = e8_codebook(65536 if K is None else K)
         raw_rms = float(np.sqrt((E.astype(np.float64) ** 2).mean()))
         a, o = lattice_row_scale(W, raw_rms)
     else:
         raise ValueError("d must be 1 or 8")
+    if group and d != 1:
+        raise ValueError("group-wise grids are generated for scalar codebooks")
     return Layer(name, W, s, V, E, a, o, d, T_vamp, n_cd, damping,
-                 meta=dict(seed=seed, dist=dist, power=power, lead=lead))
+                 meta=dict(seed=seed, dist=dist, power=power, lead=lead), group=int(group))
 
 
 _SPECS = {

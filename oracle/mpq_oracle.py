@@ -41,6 +41,10 @@ Readings where the pages are silent (each also listed in the design doc):
       anchor at the row's own weights whose width is tau codebook units
       (a = the row's codebook scale).  It enters the denoiser and the MAP as a
       per-block log-prior; CD minimises the layer objective alone.
+  A2  group-wise grids (hyper-parameter paragraph: scalar grids with group
+      size 128): the codebook of block b is a_k e + o_k for the column group k
+      of g consecutive weights that holds the block (g a multiple of d); a
+      row's blocks keep their own group's codewords in every stage.
   G1  (guard) the denoiser's variance sum is floored at
       n * (1e-12 * a)^2, a = the row's codebook scale; it never binds on
       continuous data.
@@ -65,6 +69,42 @@ def row_codewords(E, a, o):
     return float(a) * np.asarray(E, dtype=np.float64) + float(o)
 
 
+class GroupedCodebook:
+    """Reading A2: codewords a_k e + o_k of consecutive column groups of g
+    weights (the last group may be shorter).  Stage functions given one of
+    these in place of a K x d codebook run group by group."""
+
+    def __init__(self, E, a, o, n, d, g):
+        a = np.atleast_1d(np.asarray(a, np.float64))
+        o = np.atleast_1d(np.asarray(o, np.float64))
+        if g <= 0 or g % d:
+            raise ValueError("group size must be a positive multiple of d")
+        self.d, self.g, self.n = d, g, n
+        self.groups = [(c0, min(n, c0 + g), row_codewords(E, a[k], o[k])) for k, c0 in enumerate(range(0, n, g))]
+        if len(self.groups) != a.shape[0] or len(self.groups) != o.shape[0]:
+            raise ValueError("one (a, o) per group")
+        self.scale = float(np.max(np.abs(a)))
+
+    def block_codebooks(self):
+        """The codebook of every block, in block order."""
+        out = []
+        for c0, c1, C in self.groups:
+            out += [C] * ((c1 - c0) // self.d)
+        return out
+
+    def decode(self, codes):
+        """The weights x of the given block codes."""
+        Cb = self.block_codebooks()
+        return np.concatenate([Cb[b][k] for b, k in enumerate(np.asarray(codes))])
+
+
+def decode(C, codes, d):
+    """x for the block codes under C (K x d codebook or GroupedCodebook)."""
+    if isinstance(C, GroupedCodebook):
+        return C.decode(codes)
+    return C[np.asarray(codes)].reshape(-1)
+
+
 def _blocks(x, d):
     return np.asarray(x, dtype=np.float64).reshape(-1, d)
 
@@ -86,6 +126,8 @@ def sq_dist(Xb, C):
 
 def nearest_codeword(x, C, d):
     """Per-block argmin_c ||x_b - c||^2, ties to the lowest index (round to nearest)."""
+    if isinstance(C, GroupedCodebook):
+        return np.concatenate([nearest_codeword(np.asarray(x)[c0:c1], Cg, d) for c0, c1, Cg in C.groups])
     Xb = _blocks(x, d)
     B, K = Xb.shape[0], C.shape[0]
     out = np.empty(B, dtype=np.int64)
@@ -130,6 +172,11 @@ def denoise(r1, gamma1, C, d, log_prior=None, return_q=False, anchor=None):
     v_b = sum_c q_b(c) ||c - x_hat1_b||^2.  anchor = (w, lam) adds the
     anchored prior of reading A1.  Returns (x_hat1, v, q or None).
     """
+    if isinstance(C, GroupedCodebook):
+        parts = [denoise(np.asarray(r1)[c0:c1], gamma1, Cg, d, log_prior, False,
+                         None if anchor is None else (np.asarray(anchor[0])[c0:c1], anchor[1]))
+                 for c0, c1, Cg in C.groups]
+        return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]), None
     R = _blocks(r1, d)
     B, K = R.shape[0], C.shape[0]
     Wb = _blocks(anchor[0], d) if anchor is not None else None
@@ -216,7 +263,7 @@ def vamp_init(w, s, V, C, d):
     Returns (rtn_codes, gamma1_0, beta_0, mse, ||T (w - w_rtn)||^2)."""
     w = np.asarray(w, np.float64)
     codes = nearest_codeword(w, C, d)
-    w_rtn = C[codes].reshape(-1)
+    w_rtn = decode(C, codes, d)
     mse = float(np.mean((w - w_rtn) ** 2))
     res = rank_target(w - w_rtn, s, V)
     nrm2 = float(res @ res)
@@ -280,6 +327,10 @@ def map_codes(r1, gamma1, C, d, log_prior=None, anchor=None):
     """Marginal MAP projection (key design 3): x_b^(0) = argmax_c q_b(c)
     evaluated at (r1^T, gamma1^T); ties to the lowest index.  anchor = (w, lam)
     adds the anchored prior of reading A1."""
+    if isinstance(C, GroupedCodebook):
+        return np.concatenate([map_codes(np.asarray(r1)[c0:c1], gamma1, Cg, d, log_prior,
+                                         None if anchor is None else (np.asarray(anchor[0])[c0:c1], anchor[1]))
+                               for c0, c1, Cg in C.groups])
     R = _blocks(r1, d)
     B, K = R.shape[0], C.shape[0]
     Wb = _blocks(anchor[0], d) if anchor is not None else None
@@ -308,9 +359,10 @@ def block_cd(codes, w, s, V, C, d, n_cd):
     s = np.asarray(s, np.float64)
     V = np.asarray(V, np.float64)
     codes = np.array(codes, dtype=np.int64)
-    x = C[codes].reshape(-1).copy()
+    x = decode(C, codes, d).copy()
     u = rank_target(np.asarray(w, np.float64) - x, s, V)
     B = x.shape[0] // d
+    Cb = C.block_codebooks() if isinstance(C, GroupedCodebook) else [C] * B
     changes = []
     for _ in range(n_cd):
         changed = 0
@@ -319,13 +371,13 @@ def block_cd(codes, w, s, V, C, d, n_cd):
             Tb = s[:, None] * V[sl, :].T          # r x d
             g = Tb.T @ u
             G = Tb.T @ Tb
-            D = C - x[sl][None, :]                # K x d : c - x_b
+            D = Cb[b] - x[sl][None, :]            # K x d : c - x_b
             dF = 0.5 * np.einsum("kj,kj->k", D @ G, D) - D @ g
             k = int(np.argmin(dF))
             if dF[k] < 0.0:
                 delta = D[k]
                 u = u - Tb @ delta
-                x[sl] = C[k]
+                x[sl] = Cb[b][k]
                 codes[b] = k
                 changed += 1
         changes.append(changed)
@@ -341,22 +393,29 @@ def objective(w, x, s, V):
 
 
 def codes_objective(w, codes, C, d, s, V):
-    return objective(w, C[np.asarray(codes)].reshape(-1), s, V)
+    return objective(w, decode(C, codes, d), s, V)
 
 
 # ----------------------------------------------------------------------------
 # the whole row
 # ----------------------------------------------------------------------------
 
-def solve_row(w, s, V, E, a, o, d, T_vamp, n_cd, damping, beta0=None, record=False, anchor_tau=None):
+def solve_row(w, s, V, E, a, o, d, T_vamp, n_cd, damping, beta0=None, record=False, anchor_tau=None, group=0):
     """MPQ on one row: VAMP (T_vamp iterations) -> marginal MAP -> block CD.
     anchor_tau: the anchored prior of reading A1 (None: uniform prior).
+    group > 0: group-wise grids of reading A2 (a, o hold one value per group).
 
     Returns dict(codes, objective, beta_tr, gamma1_tr, gamma2_tr, eta1_tr,
     cd_changes, fallbacks, map_codes, rtn_codes, frozen[, history]).
     """
     w = np.asarray(w, np.float64)
-    C = row_codewords(E, a, o)
+    if group:
+        if anchor_tau is not None and np.isfinite(anchor_tau) and anchor_tau > 0:
+            raise ValueError("the anchored prior (A1) is defined for one codebook scale per row")
+        C = GroupedCodebook(E, a, o, w.shape[0], d, group)
+        a = C.scale   # the variance floor's scale (G1) and, per group, no anchor scale
+    else:
+        C = row_codewords(E, a, o)
     B = w.shape[0] // d
     rtn, gamma1_0, beta_0, mse, nrm2 = vamp_init(w, s, V, C, d)
     if mse == 0.0 or nrm2 == 0.0:   # G2: the RTN point already has zero objective

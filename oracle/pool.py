@@ -38,11 +38,14 @@ def _stage(job):
     if _ROOT not in sys.path:
         sys.path.insert(0, _ROOT)
     from oracle import mpq_oracle as O
-    path, i, d, S, kind, state = job
+    path, i, d, S, kind, state, group = job
     A = _load(path)
     w = np.asarray(A["W"][i], np.float64)
-    a, o = float(A["a"][i]), float(A["o"][i])
-    C = O.row_codewords(A["E"], a, o)
+    if group:
+        C = O.GroupedCodebook(A["E"], np.asarray(A["a"][i], np.float64), np.asarray(A["o"][i], np.float64),
+                              w.shape[0], d, group)
+    else:
+        C = O.row_codewords(A["E"], float(A["a"][i]), float(A["o"][i]))
     if kind == "map":
         r1, gamma1 = state
         return O.map_codes(np.asarray(r1, np.float64), float(gamma1), C, d)
@@ -54,12 +57,16 @@ def _solve(job):
     if _ROOT not in sys.path:
         sys.path.insert(0, _ROOT)
     from oracle import mpq_oracle as O
-    path, i, d, T, S, rho, record, tau = job
+    path, i, d, T, S, rho, record, tau, group = job
     A = _load(path)
     w = np.asarray(A["W"][i], np.float64)
-    a, o = float(A["a"][i]), float(A["o"][i])
-    res = O.solve_row(w, A["s"], A["V"], A["E"], a, o, d, T, S, rho, record=record, anchor_tau=tau)
-    C = O.row_codewords(A["E"], a, o)
+    if group:
+        a, o = np.asarray(A["a"][i], np.float64), np.asarray(A["o"][i], np.float64)
+        C = O.GroupedCodebook(A["E"], a, o, w.shape[0], d, group)
+    else:
+        a, o = float(A["a"][i]), float(A["o"][i])
+        C = O.row_codewords(A["E"], a, o)
+    res = O.solve_row(w, A["s"], A["V"], A["E"], a, o, d, T, S, rho, record=record, anchor_tau=tau, group=group)
     res["map_objective"] = O.codes_objective(w, res["map_codes"], C, d, A["s"], A["V"])
     res["rtn_objective"] = O.codes_objective(w, res["rtn_codes"], C, d, A["s"], A["V"])
     res["row"] = int(i)
@@ -99,14 +106,16 @@ def solve_rows(L, rows, T_vamp=None, n_cd=None, record=False, max_workers=None, 
     T = L.T_vamp if T_vamp is None else T_vamp
     S = L.n_cd if n_cd is None else n_cd
     rows = [int(i) for i in rows]
-    return _run(L, _solve, lambda tmp: [(tmp, i, L.d, T, S, L.damping, record, anchor_tau) for i in rows],
+    group = getattr(L, "group", 0)
+    return _run(L, _solve, lambda tmp: [(tmp, i, L.d, T, S, L.damping, record, anchor_tau, group) for i in rows],
                 max_workers)
 
 
 def map_rows(L, rows, r1, gamma1, max_workers=None):
     """Oracle marginal-MAP codes of `rows` at the given (r1[k], gamma1[k])."""
     rows = [int(i) for i in rows]
-    return _run(L, _stage, lambda tmp: [(tmp, i, L.d, 0, "map", (r1[k], gamma1[k])) for k, i in enumerate(rows)],
+    g = getattr(L, "group", 0)
+    return _run(L, _stage, lambda tmp: [(tmp, i, L.d, 0, "map", (r1[k], gamma1[k]), g) for k, i in enumerate(rows)],
                 max_workers)
 
 
@@ -114,5 +123,6 @@ def cd_rows(L, rows, start_codes, n_cd=None, max_workers=None):
     """Oracle block CD of `rows` from start_codes[k]."""
     S = L.n_cd if n_cd is None else n_cd
     rows = [int(i) for i in rows]
-    return _run(L, _stage, lambda tmp: [(tmp, i, L.d, S, "cd", start_codes[k]) for k, i in enumerate(rows)],
+    g = getattr(L, "group", 0)
+    return _run(L, _stage, lambda tmp: [(tmp, i, L.d, S, "cd", start_codes[k], g) for k, i in enumerate(rows)],
                 max_workers)

@@ -111,6 +111,13 @@ def anchor_no_half(wb, lam, C):
     return 2.0 * _orig["anchor_log_prior"](wb, lam, C)
 
 
+def grouped_blocks_reversed(self):
+    out = []
+    for c0, c1, C in reversed(self.groups):
+        out += [C] * ((c1 - c0) // self.d)
+    return out
+
+
 def rank_target_transposed(w, s, V):
     return np.asarray(s, float) * (np.asarray(V, float) @ np.asarray(w, float))
 
@@ -130,6 +137,7 @@ MUTATIONS = [
     ("rank_target", rank_target_transposed, [P.check_worked_example_mpq, P.check_cd_bruteforce]),
     ("anchor_log_prior", anchor_wrong_sign, [P.check_anchor_prior]),
     ("anchor_log_prior", anchor_no_half, [P.check_anchor_prior]),
+    ("GroupedCodebook.block_codebooks", grouped_blocks_reversed, [P.check_grouped_local_minimum]),
 ]
 
 
@@ -137,7 +145,11 @@ MUTATIONS = [
 def test_pins_catch_mutation(monkeypatch, name, fn, checks):
     for chk in checks:
         chk()  # clean oracle passes
-    monkeypatch.setattr(O, name, fn)
+    if "." in name:
+        cls, attr = name.split(".")
+        monkeypatch.setattr(getattr(O, cls), attr, fn)
+    else:
+        monkeypatch.setattr(O, name, fn)
     caught = 0
     for chk in checks:
         try:

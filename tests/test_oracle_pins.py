@@ -526,6 +526,63 @@ def test_anchor_whole_row_limits():
     assert np.allclose(base["gamma1_tr"], loose["gamma1_tr"], rtol=1e-9)
 
 
+# ----------------------------------------------------------------------------
+# group-wise grids (reading A2: hyper-parameter paragraph, group size 128 for
+# scalar grids)
+# ----------------------------------------------------------------------------
+
+def _grouped_problem(seed=13, n=12, r=10, g=4, K=4):
+    w, s, V, _ = small_problem(seed, n=n, r=r, K=K)
+    E = np.arange(K, dtype=float).reshape(K, 1)
+    G = n // g
+    lo = np.array([w[k * g:(k + 1) * g].min() for k in range(G)])
+    hi = np.array([w[k * g:(k + 1) * g].max() for k in range(G)])
+    a = (hi - lo) / (K - 1)
+    o = lo.copy()
+    return w, s, V, E, a, o, g
+
+
+def check_grouped_identical_groups():
+    """Groups that all carry the row's grid reproduce the per-row solve exactly."""
+    w, s, V, E, _, _, g = _grouped_problem()
+    a0, o0 = 0.37, -0.61
+    G = w.shape[0] // g
+    base = O.solve_row(w, s, V, E, a0, o0, 1, 4, 3, 0.5)
+    grp = O.solve_row(w, s, V, E, np.full(G, a0), np.full(G, o0), 1, 4, 3, 0.5, group=g)
+    assert list(base["codes"]) == list(grp["codes"])
+    assert base["objective"] == grp["objective"]
+    assert np.array_equal(base["gamma1_tr"], grp["gamma1_tr"])
+
+
+def check_grouped_local_minimum():
+    """With distinct group grids: round to nearest uses each group's own grid,
+    every final weight lies on its group's grid, and no single-block change to
+    a codeword of the block's own grid lowers the objective (CD's fixed point)."""
+    w, s, V, E, a, o, g = _grouped_problem()
+    res = O.solve_row(w, s, V, E, a, o, 1, 4, 6, 0.5, group=g)
+    grids = [a[k] * E[:, 0] + o[k] for k in range(len(a))]
+    for j, k in enumerate(res["rtn_codes"]):
+        grid = grids[j // g]
+        assert k == int(np.argmin(np.abs(grid - w[j])))
+    x = np.array([grids[j // g][k] for j, k in enumerate(res["codes"])])
+    f0 = O.objective(w, x, s, V)
+    assert abs(f0 - res["objective"]) <= 1e-12 * max(1.0, f0)
+    if res["cd_changes"][-1] == 0:   # converged within the sweeps
+        for j in range(len(x)):
+            for c in grids[j // g]:
+                y = x.copy()
+                y[j] = c
+                assert O.objective(w, y, s, V) >= f0 - 1e-12 * max(1.0, f0)
+
+
+def test_grouped_identical_groups():
+    check_grouped_identical_groups()
+
+
+def test_grouped_local_minimum():
+    check_grouped_local_minimum()
+
+
 def test_mpq_beats_rtn_on_c1_rows():
     """Sanity on the small workload: MPQ never ends above RTN + CD's start."""
     L = S.make_config("c1")
