@@ -16,7 +16,8 @@
  *    (d = 1 or d = 8, n % d == 0), K codewords per block.
  *  - Device buffers are float32/int32, row-major, allocated and owned by the
  *    caller (W: m x n, s: r, V: n x r with orthonormal columns, row_scale and
- *    row_offset: m).  The library never allocates device memory: all scratch
+ *    row_offset: m, or m x ceil(n / g) with column groups, see
+ *    mpq_options.group).  The library never allocates device memory: all scratch
  *    lives in the caller's `workspace` of at least mpq_workspace_bytes(...)
  *    bytes (256-byte aligned).
  *  - The base codebook `cb` is a HOST pointer, K x d float32 row-major; row
@@ -25,7 +26,7 @@
  *    d = 8: 1 <= K <= 65536 and every entry and every half squared norm
  *    ||e||^2 / 2 must be exactly representable in bfloat16 (true for the
  *    half-integer E8 lattice points); otherwise MPQ_EUNSUPPORTED.
- *  - row_scale[i] must be > 0.
+ *  - row_scale[i] must be > 0 (every entry, with column groups).
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default
  *    stream); calls return after enqueueing.  Outputs are valid once the
  *    stream reaches that point.  Calls that share one workspace must not
@@ -49,8 +50,9 @@ extern "C" {
 #define MPQ_OK               0
 #define MPQ_ENULL           -1   /* a required pointer is NULL */
 #define MPQ_ESHAPE          -2   /* m < 0, n < 1, r < 1, r > n, n % d != 0, K out of range */
-#define MPQ_EPARAM          -3   /* T_vamp < 0, n_cd < 0, damping not in (0, 1] */
-#define MPQ_EUNSUPPORTED    -4   /* d not in {1, 8}, or a d = 8 codebook not exact in bfloat16 */
+#define MPQ_EPARAM          -3   /* T_vamp < 0, n_cd < 0, damping not in (0, 1], group < 0 */
+#define MPQ_EUNSUPPORTED    -4   /* d not in {1, 8}, a d = 8 codebook not exact in bfloat16, or
+                                    column groups with d = 8 or the anchored prior */
 #define MPQ_EWORKSPACE      -5   /* workspace NULL, misaligned or smaller than required */
 #define MPQ_EHIP            -6   /* a HIP runtime call failed */
 
@@ -72,7 +74,19 @@ typedef struct {
                              the row's codebook scale), used by the denoiser and
                              the marginal MAP; <= 0 (or NaN): uniform prior */
   const float* anchor_w;  /* device, m x n: the weights w the prior is anchored at,
-                             for mpq_vamp_step (mpq_quantize_layer anchors at its W) */
+                             for mpq_vamp_step, mpq_denoise and mpq_map
+                             (mpq_quantize_layer anchors at its W; mpq_cd has no
+                             prior) */
+  int64_t group;          /* > 0: group-wise scalar grids (the hyper-parameter
+                             paragraph's scalar runs use groups of 128): each run of
+                             g = group consecutive columns of a row has its own
+                             affine, so row_scale and row_offset are m x G,
+                             G = ceil(n / g), and column j of row i uses entry
+                             [i][j / g] (the last group may be shorter).  Needs
+                             d = 1 and the uniform prior (else MPQ_EUNSUPPORTED);
+                             the denoiser's variance floor then uses the row's
+                             largest scale.  0: one affine per row; < 0:
+                             MPQ_EPARAM */
 } mpq_options;
 
 #define MPQ_F_FIXED_BETA 1u
@@ -142,7 +156,8 @@ int mpq_prologue(const float* W, int64_t m, int64_t n, const float* s, const flo
  * xhat1 (m x n) and the trace of its covariance per block, vtrace (m x n/d). */
 int mpq_denoise(const float* R1, const float* gamma1, int64_t m, int64_t n,
                 const float* cb, int64_t K, int64_t d, const float* row_scale, const float* row_offset,
-                float* xhat1, float* vtrace, void* workspace, size_t ws_bytes, void* stream);
+                const mpq_options* opt, float* xhat1, float* vtrace, void* workspace, size_t ws_bytes,
+                void* stream);
 
 /* One VAMP iteration (key designs 1 and 2) in place on (R1, gamma1, beta):
  * denoise -> extrinsic (r2, gamma2) -> linear module -> beta M-step with
@@ -158,10 +173,12 @@ int mpq_vamp_step(float* R1, float* gamma1, float* beta, const float* ytil, int6
                   void* workspace, size_t ws_bytes, void* stream);
 
 /* Marginal MAP (key design 3): codes[i, b] = argmax_c q_b(c) at (R1, gamma1);
- * under the uniform prior this is the nearest codeword (ties: lowest index). */
+ * under the uniform prior this is the nearest codeword (ties: lowest index),
+ * under the anchored prior the codeword nearest the completed-square mean
+ * (gamma1 r1 + lam w) / (gamma1 + lam). */
 int mpq_map(const float* R1, const float* gamma1, int64_t m, int64_t n,
             const float* cb, int64_t K, int64_t d, const float* row_scale, const float* row_offset,
-            int32_t* codes, void* workspace, size_t ws_bytes, void* stream);
+            const mpq_options* opt, int32_t* codes, void* workspace, size_t ws_bytes, void* stream);
 
 /* Exact block coordinate descent (key design 3) from `codes` (updated in
  * place): at most n_cd sweeps over the blocks in ascending order, each block
@@ -169,7 +186,8 @@ int mpq_map(const float* R1, const float* gamma1, int64_t m, int64_t n,
  * a strict improvement.  cd_changes (m x n_cd, may be NULL) counts moves. */
 int mpq_cd(const float* W, int64_t m, int64_t n, const float* s, const float* V, int64_t r,
            const float* cb, int64_t K, int64_t d, const float* row_scale, const float* row_offset,
-           int n_cd, int32_t* codes, int32_t* cd_changes, void* workspace, size_t ws_bytes, void* stream);
+           int n_cd, const mpq_options* opt, int32_t* codes, int32_t* cd_changes, void* workspace,
+           size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -142,13 +142,16 @@ _SPECS = {
 }
 
 
-def make_config(name: str, device=None) -> Layer:
-    """One of the five named workloads (seed 1000 + index)."""
+def make_config(name: str, device=None, group: int = 0) -> Layer:
+    """One of the five named workloads (seed 1000 + index); `group` > 0 gives
+    a scalar workload group-wise grids of that many columns (same weights)."""
     idx = CONFIG_NAMES.index(name) + 1
     spec = dict(_SPECS[name])
     m = spec.pop("m")
     n = spec.pop("n")
-    return make_layer(name, m, n, seed=1000 + idx, device=device, n_cd=3, damping=0.5, **spec)
+    L = make_layer(name if not group else f"{name}_g{group}", m, n, seed=1000 + idx, device=device, n_cd=3,
+                   damping=0.5, group=group, **spec)
+    return L
 
 
 def parity_rows(m: int, count: int = 64) -> np.ndarray:

@@ -41,7 +41,7 @@ PROF_COUNT = len(PROF_NAMES)
 class Options(ctypes.Structure):
     _fields_ = [("beta0", ctypes.c_float), ("flags", ctypes.c_uint32), ("prof_mask", ctypes.c_uint32),
                 ("prof_ms", ctypes.POINTER(ctypes.c_double)), ("prof_launches", ctypes.POINTER(ctypes.c_int64)),
-                ("anchor_tau", ctypes.c_float), ("anchor_w", ctypes.c_void_p)]
+                ("anchor_tau", ctypes.c_float), ("anchor_w", ctypes.c_void_p), ("group", ctypes.c_int64)]
 
 
 class Profile:
@@ -83,11 +83,11 @@ def load_library(path: str = LIB_PATH):
     lib.mpq_quantize_layer.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, I, I, F, OPT,
                                        P, P, P, P, P, P, SZ, P]
     lib.mpq_prologue.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, OPT, P, P, P, P, P, SZ, P]
-    lib.mpq_denoise.argtypes = [P, P, I64, I64, P, I64, I64, P, P, P, P, P, SZ, P]
+    lib.mpq_denoise.argtypes = [P, P, I64, I64, P, I64, I64, P, P, OPT, P, P, P, SZ, P]
     lib.mpq_vamp_step.argtypes = [P, P, P, P, I64, I64, P, P, I64, P, I64, I64, P, P, F, OPT,
                                   P, P, P, P, P, P, SZ, P]
-    lib.mpq_map.argtypes = [P, P, I64, I64, P, I64, I64, P, P, P, P, SZ, P]
-    lib.mpq_cd.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, I, P, P, P, SZ, P]
+    lib.mpq_map.argtypes = [P, P, I64, I64, P, I64, I64, P, P, OPT, P, P, SZ, P]
+    lib.mpq_cd.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, I, OPT, P, P, P, SZ, P]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -147,12 +147,24 @@ def _workspace(m, n, r, K, d, device):
     return torch.empty(nb, dtype=torch.uint8, device=device)
 
 
-def _opts(beta0=None, fixed_beta=False, profile=None, anchor_tau=None, anchor_w=None):
+def _opts(beta0=None, fixed_beta=False, profile=None, anchor_tau=None, anchor_w=None, group=None):
     flags = (F_FIXED_BETA if fixed_beta else 0) | (F_PROFILE if profile is not None else 0)
     o = Options(float(beta0) if beta0 else 0.0, flags, profile.mask if profile is not None else 0,
                 profile.ms if profile is not None else None, profile.launches if profile is not None else None,
-                float(anchor_tau) if anchor_tau else 0.0, anchor_w.data_ptr() if anchor_w is not None else None)
+                float(anchor_tau) if anchor_tau else 0.0, anchor_w.data_ptr() if anchor_w is not None else None,
+                int(group) if group else 0)
     return ctypes.byref(o), o
+
+
+def _affine(row_scale, row_offset, m, n, group):
+    """Check the per-row (m,) or per-group (m, ceil(n / group)) affine tensors."""
+    import torch
+    G = 1 if not group or group >= n else -(-n // group)
+    for t, nm in ((row_scale, "row_scale"), (row_offset, "row_offset")):
+        _dev(t, torch.float32, nm)
+        if t.numel() != m * G or t.dim() not in (1, 2) or t.shape[0] != m:
+            raise ValueError(f"{nm} has shape {tuple(t.shape)}, expected ({m},) or ({m}, {G})"
+                             if G == 1 else f"{nm} has shape {tuple(t.shape)}, expected ({m}, {G})")
 
 
 def _check(rc, what):
@@ -163,13 +175,16 @@ def _check(rc, what):
 # ---------------------------------------------------------------- entry points
 
 def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, damping=0.5, beta0=None,
-                   fixed_beta=False, workspace=None, traces=True, profile=None, outputs=None, anchor_tau=None):
+                   fixed_beta=False, workspace=None, traces=True, profile=None, outputs=None, anchor_tau=None,
+                   group=None):
     """Full MPQ solve of one layer (mpq_quantize_layer).
 
     Returns dict(codes, beta_tr, gamma1_tr, gamma2_tr, cd_changes) of device
     tensors.  `profile` (a Profile) turns on the library's event timing;
     `outputs` (a dict from a previous call) reuses its output tensors;
-    `anchor_tau` > 0 selects the anchored codebook prior (None: uniform).
+    `anchor_tau` > 0 selects the anchored codebook prior (None: uniform);
+    `group` > 0 gives every `group` consecutive columns their own affine
+    (row_scale and row_offset then m x ceil(n / group)).
     """
     import torch
     m, n = W.shape
@@ -180,8 +195,7 @@ def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, dampin
     _dev(W, torch.float32, "W")
     _dev(s, torch.float32, "s", (r,))
     _dev(V, torch.float32, "V", (n, r))
-    _dev(row_scale, torch.float32, "row_scale", (m,))
-    _dev(row_offset, torch.float32, "row_offset", (m,))
+    _affine(row_scale, row_offset, m, n, group)
     if outputs is not None:
         codes, bt, g1, g2, ch = (outputs[k] for k in ("codes", "beta_tr", "gamma1_tr", "gamma2_tr", "cd_changes"))
     else:
@@ -191,7 +205,7 @@ def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, dampin
         g2 = torch.empty((m, T_vamp), dtype=torch.float32, device=dev) if traces and T_vamp > 0 else None
         ch = torch.zeros((m, n_cd), dtype=torch.int32, device=dev) if traces and n_cd > 0 else None
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
-    op, _keep = _opts(beta0, fixed_beta, profile, anchor_tau)
+    op, _keep = _opts(beta0, fixed_beta, profile, anchor_tau, None, group)
     rc = load_library().mpq_quantize_layer(
         _ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d, _ptr(row_scale),
         _ptr(row_offset), int(T_vamp), int(n_cd), float(damping), op, _ptr(codes), _ptr(bt), _ptr(g1), _ptr(g2),
@@ -200,7 +214,7 @@ def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, dampin
     return dict(codes=codes, beta_tr=bt, gamma1_tr=g1, gamma2_tr=g2, cd_changes=ch)
 
 
-def prologue(W, s, V, cb, row_scale, row_offset, beta0=None, workspace=None):
+def prologue(W, s, V, cb, row_scale, row_offset, beta0=None, workspace=None, group=None):
     import torch
     m, n = W.shape
     r = s.shape[0]
@@ -211,8 +225,9 @@ def prologue(W, s, V, cb, row_scale, row_offset, beta0=None, workspace=None):
     rtn = torch.empty((m, n // d), dtype=torch.int32, device=dev)
     gamma1 = torch.empty(m, dtype=torch.float32, device=dev)
     beta = torch.empty(m, dtype=torch.float32, device=dev)
+    _affine(row_scale, row_offset, m, n, group)
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
-    op, _keep = _opts(beta0)
+    op, _keep = _opts(beta0, group=group)
     rc = load_library().mpq_prologue(_ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d,
                                      _ptr(row_scale), _ptr(row_offset), op, _ptr(ytil), _ptr(rtn), _ptr(gamma1),
                                      _ptr(beta), _ptr(ws), ws.numel(), _stream())
@@ -220,7 +235,8 @@ def prologue(W, s, V, cb, row_scale, row_offset, beta0=None, workspace=None):
     return dict(ytil=ytil, rtn_codes=rtn, gamma1=gamma1, beta=beta)
 
 
-def denoise(R1, gamma1, cb, row_scale, row_offset, workspace=None):
+def denoise(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=None, W=None, group=None):
+    """Blockwise denoiser (mpq_denoise): (xhat1, per-block variance trace)."""
     import torch
     m, n = R1.shape
     E = _host_codebook(cb)
@@ -228,18 +244,22 @@ def denoise(R1, gamma1, cb, row_scale, row_offset, workspace=None):
     dev = R1.device
     _dev(R1, torch.float32, "R1")
     _dev(gamma1, torch.float32, "gamma1", (m,))
+    _affine(row_scale, row_offset, m, n, group)
+    if anchor_tau:
+        _dev(W, torch.float32, "W", (m, n))
     xhat = torch.empty_like(R1)
     vtr = torch.empty((m, n // d), dtype=torch.float32, device=dev)
     ws = workspace if workspace is not None else _workspace(m, n, n, K, d, dev)
+    op, _keep = _opts(anchor_tau=anchor_tau, anchor_w=W, group=group)
     rc = load_library().mpq_denoise(_ptr(R1), _ptr(gamma1), m, n, E.ctypes.data_as(ctypes.c_void_p), K, d,
-                                    _ptr(row_scale), _ptr(row_offset), _ptr(xhat), _ptr(vtr), _ptr(ws), ws.numel(),
-                                    _stream())
+                                    _ptr(row_scale), _ptr(row_offset), op, _ptr(xhat), _ptr(vtr), _ptr(ws),
+                                    ws.numel(), _stream())
     _check(rc, "mpq_denoise")
     return xhat, vtr
 
 
 def vamp_step(R1, gamma1, beta, ytil, s, V, cb, row_scale, row_offset, damping=0.5, fixed_beta=False,
-              workspace=None, anchor_tau=None, W=None):
+              workspace=None, anchor_tau=None, W=None, group=None):
     """One VAMP iteration in place on (R1, gamma1, beta); returns the diagnostics.
     With `anchor_tau` > 0 the prior is anchored at the weights `W`."""
     import torch
@@ -256,9 +276,10 @@ def vamp_step(R1, gamma1, beta, ytil, s, V, cb, row_scale, row_offset, damping=0
     gamma2 = torch.empty(m, dtype=torch.float32, device=dev)
     fb = torch.empty(m, dtype=torch.int32, device=dev)
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
+    _affine(row_scale, row_offset, m, n, group)
     if anchor_tau:
         _dev(W, torch.float32, "W", (m, n))
-    op, _keep = _opts(None, fixed_beta, None, anchor_tau, W)
+    op, _keep = _opts(None, fixed_beta, None, anchor_tau, W, group)
     rc = load_library().mpq_vamp_step(_ptr(R1), _ptr(gamma1), _ptr(beta), _ptr(ytil), m, n, _ptr(s), _ptr(V), r,
                                       E.ctypes.data_as(ctypes.c_void_p), K, d, _ptr(row_scale), _ptr(row_offset),
                                       float(damping), op, _ptr(xhat), _ptr(eta1), _ptr(gamma2), _ptr(r2), _ptr(fb),
@@ -267,20 +288,27 @@ def vamp_step(R1, gamma1, beta, ytil, s, V, cb, row_scale, row_offset, damping=0
     return dict(xhat1=xhat, eta1=eta1, gamma2=gamma2, r2=r2, fallback=fb)
 
 
-def map_codes(R1, gamma1, cb, row_scale, row_offset, workspace=None):
+def map_codes(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=None, W=None, group=None):
+    """Marginal MAP codes (mpq_map)."""
     import torch
     m, n = R1.shape
     E = _host_codebook(cb)
     K, d = E.shape
+    _dev(R1, torch.float32, "R1")
+    _dev(gamma1, torch.float32, "gamma1", (m,))
+    _affine(row_scale, row_offset, m, n, group)
+    if anchor_tau:
+        _dev(W, torch.float32, "W", (m, n))
     codes = torch.empty((m, n // d), dtype=torch.int32, device=R1.device)
     ws = workspace if workspace is not None else _workspace(m, n, n, K, d, R1.device)
+    op, _keep = _opts(anchor_tau=anchor_tau, anchor_w=W, group=group)
     rc = load_library().mpq_map(_ptr(R1), _ptr(gamma1), m, n, E.ctypes.data_as(ctypes.c_void_p), K, d,
-                                _ptr(row_scale), _ptr(row_offset), _ptr(codes), _ptr(ws), ws.numel(), _stream())
+                                _ptr(row_scale), _ptr(row_offset), op, _ptr(codes), _ptr(ws), ws.numel(), _stream())
     _check(rc, "mpq_map")
     return codes
 
 
-def cd(W, s, V, cb, row_scale, row_offset, codes, n_cd=3, workspace=None):
+def cd(W, s, V, cb, row_scale, row_offset, codes, n_cd=3, workspace=None, group=None):
     """Block CD from `codes` (a device int32 tensor, updated in place)."""
     import torch
     m, n = W.shape
@@ -288,10 +316,12 @@ def cd(W, s, V, cb, row_scale, row_offset, codes, n_cd=3, workspace=None):
     E = _host_codebook(cb)
     K, d = E.shape
     _dev(codes, torch.int32, "codes", (m, n // d))
+    _affine(row_scale, row_offset, m, n, group)
     ch = torch.zeros((m, max(n_cd, 1)), dtype=torch.int32, device=W.device)
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, W.device)
+    op, _keep = _opts(group=group)
     rc = load_library().mpq_cd(_ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d,
-                               _ptr(row_scale), _ptr(row_offset), int(n_cd), _ptr(codes), _ptr(ch), _ptr(ws),
+                               _ptr(row_scale), _ptr(row_offset), int(n_cd), op, _ptr(codes), _ptr(ch), _ptr(ws),
                                ws.numel(), _stream())
     _check(rc, "mpq_cd")
     return codes, ch[:, :n_cd]

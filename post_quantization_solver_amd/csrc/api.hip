@@ -423,7 +423,7 @@ int run_iteration(Ctx& c, float* R1, float* gamma1, float* beta, const float* yt
   if (rc) return rc;
   if (xhat_out) TIMED(c, MPQ_PROF_OTHER, launch_copy_rows_f(X1, xhat_out, L.m * L.n, c.st));
   TIMED(c, MPQ_PROF_EXTRINSIC,
-        launch_extrinsic(R1, X1, c.p(R_VBLK), L.m, L.n, L.B, a, gamma1, R2, c.gamma2(),
+        launch_extrinsic(R1, X1, c.p(R_VBLK), L.m, L.n, L.B, a, c.cb.G, gamma1, R2, c.gamma2(),
                          eta1_out ? eta1_out : c.eta1(), fallback_out, c.st));
   if (gamma2_out) TIMED(c, MPQ_PROF_OTHER, launch_copy_rows_f(c.gamma2(), gamma2_out, L.m, c.st));
   if (trace_g2) TIMED(c, MPQ_PROF_OTHER, launch_record(c.gamma2(), L.m, trace_g2, ld_g2, col, c.st));
@@ -544,8 +544,8 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
     q.changes = cd_changes ? cd_changes + q.r0 * n_cd : nullptr;
     q.ps = c.p(R_PS) + q.r0 * 2 * std::max(L.nslices, 1);
     q.pi = c.pi(R_PI) + q.r0 * 2 * std::max(L.nslices, 1);
-    q.a = a + q.r0;
-    q.o = o + q.r0;
+    q.a = a + q.r0 * c.cb.G;
+    q.o = o + q.r0 * c.cb.G;
     q.qf = reinterpret_cast<uint32_t*>(c.p(R_QF)) + q.r0 * 16;
     q.tk = reinterpret_cast<uint32_t*>(c.p(R_TKEY)) + (int64_t)g * (KD / 8) * L.Kpad * 4;
   }
@@ -674,6 +674,18 @@ int begin(Ctx& c, int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, const f
   if (!cb) return MPQ_ENULL;
   rc = check_codebook(cb, K, d);
   if (rc) return rc;
+  // affine groups: one (a, o) per group of `group` columns (d = 1, uniform
+  // prior only), else one per row
+  c.cb.gs = (int)n;
+  c.cb.G = 1;
+  if (opt && opt->group != 0) {
+    if (opt->group < 0) return MPQ_EPARAM;
+    if (d != 1 || c.anchored()) return MPQ_EUNSUPPORTED;
+    if (opt->group < n) {
+      c.cb.gs = (int)opt->group;
+      c.cb.G = (int)((n + opt->group - 1) / opt->group);
+    }
+  }
   c.L = make_layout(m, n, r, K, d);
   rc = check_ws(c.L, ws, bytes);
   if (rc) return rc;
@@ -710,7 +722,9 @@ const char* mpq_strerror(int status) {
     case MPQ_ENULL: return "a required pointer is NULL";
     case MPQ_ESHAPE: return "invalid shape (m, n, r, K, d)";
     case MPQ_EPARAM: return "invalid parameter (T_vamp, n_cd, damping or a non-finite codebook entry)";
-    case MPQ_EUNSUPPORTED: return "unsupported codebook (d must be 1 or 8; d = 8 entries must be exact in bfloat16)";
+    case MPQ_EUNSUPPORTED:
+      return "unsupported codebook (d must be 1 or 8; d = 8 entries must be exact in bfloat16; column groups need "
+             "d = 1 and the uniform prior)";
     case MPQ_EWORKSPACE: return "workspace missing, misaligned or too small";
     case MPQ_EHIP: return "HIP runtime error";
   }
@@ -753,17 +767,26 @@ int mpq_prologue(const float* W, int64_t m, int64_t n, const float* s, const flo
 }
 
 int mpq_denoise(const float* R1, const float* gamma1, int64_t m, int64_t n, const float* cb, int64_t K, int64_t d,
-                const float* row_scale, const float* row_offset, float* xhat1, float* vtrace, void* workspace,
-                size_t ws_bytes, void* stream) {
+                const float* row_scale, const float* row_offset, const mpq_options* opt, float* xhat1, float* vtrace,
+                void* workspace, size_t ws_bytes, void* stream) {
   int rc = check_shapes(m, n, n, K, d);
   if (rc) return rc;
   if (m == 0) return MPQ_OK;
   if (!R1 || !gamma1 || !row_scale || !row_offset || !xhat1 || !vtrace) return MPQ_ENULL;
   Ctx c;
-  rc = begin(c, m, n, 1, K, d, cb, workspace, ws_bytes, stream);
+  rc = begin(c, m, n, 1, K, d, cb, workspace, ws_bytes, stream, opt);
   if (rc) return rc;
+  if (c.anchored() && !c.anchor_w) return MPQ_ENULL;
   if ((rc = upload_codebook(c, cb))) return rc;
-  return denoise(c, R1, gamma1, row_scale, row_offset, xhat1, vtrace);
+  const float* Rd = R1;
+  const float* gd = gamma1;
+  if (c.anchored()) {
+    TIMED(c, MPQ_PROF_OTHER, launch_anchor(R1, c.anchor_w, gamma1, row_scale, c.anchor_tau, m, n, c.p(R_ANCH),
+                                           c.gamma_anchor(), c.st));
+    Rd = c.p(R_ANCH);
+    gd = c.gamma_anchor();
+  }
+  return finish(c, denoise(c, Rd, gd, row_scale, row_offset, xhat1, vtrace));
 }
 
 int mpq_vamp_step(float* R1, float* gamma1, float* beta, const float* ytil, int64_t m, int64_t n, const float* s,
@@ -778,8 +801,8 @@ int mpq_vamp_step(float* R1, float* gamma1, float* beta, const float* ytil, int6
   Ctx c;
   rc = begin(c, m, n, r, K, d, cb, workspace, ws_bytes, stream, opt);
   if (rc) return rc;
-  if ((rc = upload_codebook(c, cb))) return rc;
   if (c.anchored() && !c.anchor_w) return MPQ_ENULL;
+  if ((rc = upload_codebook(c, cb))) return rc;
   if ((rc = prepare_factors(c, V, s, true))) return rc;
   const int fixed = (opt && (opt->flags & MPQ_F_FIXED_BETA)) ? 1 : 0;
   return finish(c, run_iteration(c, R1, gamma1, beta, ytil, s, row_scale, row_offset, damping, fixed, xhat1, eta1,
@@ -787,34 +810,41 @@ int mpq_vamp_step(float* R1, float* gamma1, float* beta, const float* ytil, int6
 }
 
 int mpq_map(const float* R1, const float* gamma1, int64_t m, int64_t n, const float* cb, int64_t K, int64_t d,
-            const float* row_scale, const float* row_offset, int32_t* codes, void* workspace, size_t ws_bytes,
-            void* stream) {
+            const float* row_scale, const float* row_offset, const mpq_options* opt, int32_t* codes, void* workspace,
+            size_t ws_bytes, void* stream) {
   int rc = check_shapes(m, n, n, K, d);
   if (rc) return rc;
   if (m == 0) return MPQ_OK;
   if (!R1 || !gamma1 || !row_scale || !row_offset || !codes) return MPQ_ENULL;
   Ctx c;
-  rc = begin(c, m, n, 1, K, d, cb, workspace, ws_bytes, stream);
+  rc = begin(c, m, n, 1, K, d, cb, workspace, ws_bytes, stream, opt);
   if (rc) return rc;
+  if (c.anchored() && !c.anchor_w) return MPQ_ENULL;
   if ((rc = upload_codebook(c, cb))) return rc;
-  MPQ_TRY(nearest(c, R1, codes, row_scale, row_offset));
-  return MPQ_OK;
+  const float* Rm = R1;
+  if (c.anchored()) {
+    TIMED(c, MPQ_PROF_MAP, launch_anchor(R1, c.anchor_w, gamma1, row_scale, c.anchor_tau, m, n, c.p(R_ANCH),
+                                         c.gamma_anchor(), c.st));
+    Rm = c.p(R_ANCH);
+  }
+  TIMED(c, MPQ_PROF_MAP, nearest(c, Rm, codes, row_scale, row_offset));
+  return finish(c, MPQ_OK);
 }
 
 int mpq_cd(const float* W, int64_t m, int64_t n, const float* s, const float* V, int64_t r, const float* cb, int64_t K,
-           int64_t d, const float* row_scale, const float* row_offset, int n_cd, int32_t* codes, int32_t* cd_changes,
-           void* workspace, size_t ws_bytes, void* stream) {
+           int64_t d, const float* row_scale, const float* row_offset, int n_cd, const mpq_options* opt,
+           int32_t* codes, int32_t* cd_changes, void* workspace, size_t ws_bytes, void* stream) {
   if (n_cd < 0) return MPQ_EPARAM;
   int rc = check_shapes(m, n, r, K, d);
   if (rc) return rc;
   if (m == 0) return MPQ_OK;
   if (!W || !s || !V || !row_scale || !row_offset || !codes) return MPQ_ENULL;
   Ctx c;
-  rc = begin(c, m, n, r, K, d, cb, workspace, ws_bytes, stream);
+  rc = begin(c, m, n, r, K, d, cb, workspace, ws_bytes, stream, opt);
   if (rc) return rc;
   if ((rc = upload_codebook(c, cb))) return rc;
   if ((rc = prepare_factors(c, V, s))) return rc;
-  return run_cd(c, W, row_scale, row_offset, n_cd, codes, cd_changes);
+  return finish(c, run_cd(c, W, row_scale, row_offset, n_cd, codes, cd_changes));
 }
 
 }  // extern "C"

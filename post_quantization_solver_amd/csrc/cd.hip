@@ -35,13 +35,17 @@ __global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t 
                                                              const double* __restrict__ Ht,
                                                              const float* __restrict__ levels, int K,
                                                              const float* __restrict__ a, const float* __restrict__ o,
+                                                             int gs, int ng,
                                                              int32_t* __restrict__ codes, float* __restrict__ X,
                                                              double* __restrict__ Delta, int32_t* __restrict__ changes) {
   const int lane = threadIdx.x & 63;
   const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= m) return;
-  const double ai = a[i], oi = o[i];
-  const double cl = lane < K ? ai * (double)levels[lane] + oi : 0.0;
+  // lane k holds level k of the current column's affine group; the group
+  // changes along the tile only with column groups (uniform across the wave)
+  const double lvk = lane < K ? (double)levels[lane] : 0.0;
+  int cur = (int)j0 / gs;
+  double cl = (double)a[i * ng + cur] * lvk + (double)o[i * ng + cur];
 
   double g[SLOTS], dl[SLOTS], x[SLOTS];
   int cd[SLOTS];
@@ -51,7 +55,8 @@ __global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t 
     bool in = jj < kd;
     g[s] = in ? G[i * kd + jj] : 0.0;
     cd[s] = in ? codes[i * n + j0 + jj] : 0;
-    x[s] = in ? ai * (double)levels[cd[s]] + oi : 0.0;
+    const int64_t ag = i * ng + (in ? (int)(j0 + jj) / gs : 0);
+    x[s] = in ? (double)a[ag] * (double)levels[cd[s]] + (double)o[ag] : 0.0;
     dl[s] = 0.0;
   }
   int moved = 0;
@@ -60,6 +65,11 @@ __global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t 
     for (int jl = 0; jl < 64; ++jl) {
       const int jj = s * 64 + jl;
       if (jj >= kd) break;
+      const int grp = (int)(j0 + jj) / gs;
+      if (grp != cur) {
+        cur = grp;
+        cl = (double)a[i * ng + cur] * lvk + (double)o[i * ng + cur];
+      }
       const double gj = readlane_d(g[s], jl);
       const double xj = readlane_d(x[s], jl);
       const double hjj = Ht[(int64_t)jj * kd + jj];
@@ -104,13 +114,13 @@ hipError_t launch_cd_scalar_tile(int64_t m, int64_t n, int64_t j0, int kd, const
   dim3 grid((unsigned)((m + 3) / 4));
   if (kd <= 64)
     hipLaunchKernelGGL((cd_scalar_tile_kernel<1>), grid, dim3(256), 0, st, m, n, j0, kd, G, Ht, cb.levels, cb.K, a, o,
-                       codes, X, Delta, changes);
+                       cb.gs, cb.G, codes, X, Delta, changes);
   else if (kd <= 128)
     hipLaunchKernelGGL((cd_scalar_tile_kernel<2>), grid, dim3(256), 0, st, m, n, j0, kd, G, Ht, cb.levels, cb.K, a, o,
-                       codes, X, Delta, changes);
+                       cb.gs, cb.G, codes, X, Delta, changes);
   else if (kd <= 256)
     hipLaunchKernelGGL((cd_scalar_tile_kernel<4>), grid, dim3(256), 0, st, m, n, j0, kd, G, Ht, cb.levels, cb.K, a, o,
-                       codes, X, Delta, changes);
+                       cb.gs, cb.G, codes, X, Delta, changes);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

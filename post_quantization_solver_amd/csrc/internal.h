@@ -65,6 +65,10 @@ struct CbTables {
   const uint32_t* qk_keys;  // d = 8: QK operand fragments, Kpad/16 subtiles x 64 lanes x 4 words
   const uint32_t* pv_ops;   // d = 8: PV operand fragments, Kpad/32 steps x 64 lanes x 4 words
   const float* e32;         // d = 8: base codewords as float32, Kpad x 8
+  // Per-row affine layout: column j of row i uses a[i * G + j / gs],
+  // o[i * G + j / gs] (one affine per row: gs = n, G = 1; column groups of
+  // gs weights only with d = 1).
+  int gs, G;
 };
 
 // ----------------------------------------------------------- kernels ----
@@ -82,8 +86,9 @@ hipError_t launch_prologue_finish(int64_t m, int64_t n, int64_t r, const float* 
                                   float* beta_work, hipStream_t st);
 
 // Extrinsic denoiser -> linear: eta1 from the block variances, gamma2, r2.
+// The variance floor uses the row's largest scale over its G affine groups.
 hipError_t launch_extrinsic(const float* R1, const float* xhat, const float* vblk, int64_t m, int64_t n, int64_t B,
-                            const float* a, const float* gamma1, float* R2, float* gamma2, float* eta1,
+                            const float* a, int G, const float* gamma1, float* R2, float* gamma2, float* eta1,
                             int32_t* fallback, hipStream_t st);
 
 // beta M-step + linear-side extrinsic precision.

@@ -25,6 +25,20 @@ __device__ __forceinline__ float block_sum(float x, float* sh) {
   return r;
 }
 
+__device__ __forceinline__ float block_max(float x, float* sh) {
+  const int t = threadIdx.x;
+  sh[t] = x;
+  __syncthreads();
+#pragma unroll
+  for (int w = ROW_THREADS / 2; w > 0; w >>= 1) {
+    if (t < w) sh[t] = fmaxf(sh[t], sh[t + w]);
+    __syncthreads();
+  }
+  float r = sh[0];
+  __syncthreads();
+  return r;
+}
+
 // VS = V diag(s) (n x r) and VSt = VS^T (r x n), via 32 x 32 LDS tiles.
 __global__ void scale_columns_kernel(const float* __restrict__ V, const float* __restrict__ s, int64_t n, int64_t r,
                                      float* __restrict__ VS, float* __restrict__ VSt) {
@@ -91,7 +105,7 @@ hipError_t launch_prologue_finish(int64_t m, int64_t n, int64_t r, const float* 
 // R2 may alias xhat (each element is read and written by the same thread).
 __global__ __launch_bounds__(ROW_THREADS) void extrinsic_kernel(
     const float* __restrict__ R1, const float* xhat, const float* __restrict__ vblk, int64_t n, int64_t B,
-    const float* __restrict__ a, const float* __restrict__ gamma1, float* R2, float* __restrict__ gamma2,
+    const float* __restrict__ a, int G, const float* __restrict__ gamma1, float* R2, float* __restrict__ gamma2,
     float* __restrict__ eta1_out, int32_t* __restrict__ fallback) {
   __shared__ float sh[ROW_THREADS];
   const int64_t i = blockIdx.x;
@@ -112,7 +126,9 @@ __global__ __launch_bounds__(ROW_THREADS) void extrinsic_kernel(
   float part = 0.f;
   for (int64_t b = t; b < B; b += ROW_THREADS) part += vblk[i * B + b];
   float vs = block_sum(part, sh);
-  const float ai = a[i];
+  float amax = 0.f;
+  for (int g = t; g < G; g += ROW_THREADS) amax = fmaxf(amax, a[i * G + g]);
+  const float ai = G == 1 ? a[i] : block_max(amax, sh);
   const float floor_v = (float)n * 1e-24f * ai * ai;
   const float eta1 = (float)n / fmaxf(vs, floor_v);
   const bool pass = eta1 > g1;
@@ -131,10 +147,10 @@ __global__ __launch_bounds__(ROW_THREADS) void extrinsic_kernel(
 }
 
 hipError_t launch_extrinsic(const float* R1, const float* xhat, const float* vblk, int64_t m, int64_t n, int64_t B,
-                            const float* a, const float* gamma1, float* R2, float* gamma2, float* eta1,
+                            const float* a, int G, const float* gamma1, float* R2, float* gamma2, float* eta1,
                             int32_t* fallback, hipStream_t st) {
   if (m <= 0) return hipSuccess;
-  hipLaunchKernelGGL(extrinsic_kernel, dim3((unsigned)m), dim3(ROW_THREADS), 0, st, R1, xhat, vblk, n, B, a, gamma1,
+  hipLaunchKernelGGL(extrinsic_kernel, dim3((unsigned)m), dim3(ROW_THREADS), 0, st, R1, xhat, vblk, n, B, a, G, gamma1,
                      R2, gamma2, eta1, fallback);
   return hipGetLastError();
 }

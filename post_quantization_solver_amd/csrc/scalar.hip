@@ -1,6 +1,8 @@
 // Scalar-grid (d = 1) kernels: the blockwise discrete denoiser, nearest
 // codeword (RTN / marginal MAP under the uniform prior) and codeword gather.
-// Row i's levels are c_k = a_i * e_k + o_i (fma, float32).
+// The levels of row i at column j are c_k = a * e_k + o (fma, float32) with
+// the affine (a, o) of the column's group: index i * G + j / gs (one affine
+// per row when gs = n).
 #include <math.h>
 #include "mpq_device.h"
 #include "internal.h"
@@ -18,7 +20,8 @@ __global__ __launch_bounds__(256) void denoise_scalar_kernel(const float* __rest
                                                              const float* __restrict__ gamma1, int64_t m, int64_t n,
                                                              const float* __restrict__ levels, int K,
                                                              const float* __restrict__ a, const float* __restrict__ o,
-                                                             float* __restrict__ xhat, float* __restrict__ vblk) {
+                                                             int gs, int G, float* __restrict__ xhat,
+                                                             float* __restrict__ vblk) {
   __shared__ float lv[MAXK_SCALAR];
   if (threadIdx.x < K) lv[threadIdx.x] = levels[threadIdx.x];
   __syncthreads();
@@ -32,7 +35,8 @@ __global__ __launch_bounds__(256) void denoise_scalar_kernel(const float* __rest
     vblk[i * n + j] = 0.f;
     return;
   }
-  const float ai = a[i], oi = o[i];
+  const int64_t ag = i * G + (int)j / gs;
+  const float ai = a[ag], oi = o[ag];
   float cs = fmaf(ai, lv[0], oi);
   float best = fabsf(cs - r);
   for (int k = 1; k < K; ++k) {
@@ -60,7 +64,7 @@ __global__ __launch_bounds__(256) void denoise_scalar_kernel(const float* __rest
 __global__ __launch_bounds__(256) void nearest_scalar_kernel(const float* __restrict__ R, int64_t m, int64_t n,
                                                              const float* __restrict__ levels, int K,
                                                              const float* __restrict__ a, const float* __restrict__ o,
-                                                             int32_t* __restrict__ codes) {
+                                                             int gs, int G, int32_t* __restrict__ codes) {
   __shared__ float lv[MAXK_SCALAR];
   if (threadIdx.x < K) lv[threadIdx.x] = levels[threadIdx.x];
   __syncthreads();
@@ -68,7 +72,8 @@ __global__ __launch_bounds__(256) void nearest_scalar_kernel(const float* __rest
   if (k0 >= m * n) return;
   const int64_t i = k0 / n, j = k0 - i * n;
   const float r = R[i * n + j];
-  const float ai = a[i], oi = o[i];
+  const int64_t ag = i * G + (int)j / gs;
+  const float ai = a[ag], oi = o[ag];
   float best = INFINITY;
   int bk = 0;
   for (int k = 0; k < K; ++k) {
@@ -82,15 +87,16 @@ __global__ __launch_bounds__(256) void nearest_scalar_kernel(const float* __rest
 hipError_t launch_denoise_scalar(const float* R1, const float* gamma1, int64_t m, int64_t n, const CbTables& cb,
                                  const float* a, const float* o, float* xhat, float* vblk, hipStream_t st) {
   dim3 grid((unsigned)((m * n + 255) / 256));
-  hipLaunchKernelGGL(denoise_scalar_kernel, grid, dim3(256), 0, st, R1, gamma1, m, n, cb.levels, cb.K, a, o, xhat,
-                     vblk);
+  hipLaunchKernelGGL(denoise_scalar_kernel, grid, dim3(256), 0, st, R1, gamma1, m, n, cb.levels, cb.K, a, o, cb.gs,
+                     cb.G, xhat, vblk);
   return hipGetLastError();
 }
 
 hipError_t launch_nearest_scalar(const float* R, int64_t m, int64_t n, const CbTables& cb, const float* a,
                                  const float* o, int32_t* codes, hipStream_t st) {
   dim3 grid((unsigned)((m * n + 255) / 256));
-  hipLaunchKernelGGL(nearest_scalar_kernel, grid, dim3(256), 0, st, R, m, n, cb.levels, cb.K, a, o, codes);
+  hipLaunchKernelGGL(nearest_scalar_kernel, grid, dim3(256), 0, st, R, m, n, cb.levels, cb.K, a, o, cb.gs, cb.G,
+                     codes);
   return hipGetLastError();
 }
 
@@ -98,16 +104,18 @@ hipError_t launch_nearest_scalar(const float* R, int64_t m, int64_t n, const CbT
 // workgroup per row, fixed-order reduction).
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ codes, int64_t n, int d,
                                                      const float* __restrict__ e32, const float* __restrict__ a,
-                                                     const float* __restrict__ o, const float* __restrict__ W,
+                                                     const float* __restrict__ o, int gs, int G,
+                                                     const float* __restrict__ W,
                                                      float* __restrict__ X, float* __restrict__ D,
                                                      float* __restrict__ rowsq, double* __restrict__ D64) {
   __shared__ float sh[256];
   const int64_t i = blockIdx.x;
   const int t = threadIdx.x;
-  const float ai = a[i], oi = o[i];
   const int64_t B = n / d;
   float acc = 0.f;
   for (int64_t j = t; j < n; j += 256) {
+    const int64_t ag = i * G + (int)j / gs;
+    const float ai = a[ag], oi = o[ag];
     int64_t b = j / d;
     int c = codes[i * B + b];
     float x = fmaf(ai, e32[(int64_t)c * d + (j - b * d)], oi);
@@ -135,8 +143,8 @@ hipError_t launch_gather(const int32_t* codes, int64_t m, int64_t n, const CbTab
                          double* D64) {
   if (m <= 0) return hipSuccess;
   const float* tab = cb.d == 1 ? cb.levels : cb.e32;
-  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)m), dim3(256), 0, st, codes, n, cb.d, tab, a, o, W, X, D, rowsq,
-                     D64);
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)m), dim3(256), 0, st, codes, n, cb.d, tab, a, o, cb.gs, cb.G, W, X, D,
+                     rowsq, D64);
   return hipGetLastError();
 }
 

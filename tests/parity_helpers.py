@@ -38,12 +38,20 @@ def rel_scalar(a, b):
     return abs(a - b) / abs(b) if b != 0 else abs(a - b)
 
 
+def row_codebook(L, i):
+    """The oracle's codebook of row i: its codewords, or its group-wise grids."""
+    from oracle import mpq_oracle as O
+    g = getattr(L, "group", 0)
+    if g:
+        return O.GroupedCodebook(L.E, L.a[i], L.o[i], L.n, L.d, g)
+    return O.row_codewords(L.E, L.a[i], L.o[i])
+
+
 def objectives(L, rows, codes):
     from oracle import mpq_oracle as O
     out = []
     for k, i in enumerate(rows):
-        C = O.row_codewords(L.E, L.a[i], L.o[i])
-        out.append(O.codes_objective(L.W[i], codes[k], C, L.d, L.s, L.V))
+        out.append(O.codes_objective(L.W[i], codes[k], row_codebook(L, i), L.d, L.s, L.V))
     return np.array(out)
 
 

@@ -48,10 +48,12 @@ def test_workspace_sizes(lib):
 FAKE = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
 
 
-def call_layer(lib, m=4, n=16, r=16, K=8, d=1, T=2, ncd=1, rho=0.5, cb=None, ws_bytes=1 << 30, W=FAKE, ws=FAKE):
+def call_layer(lib, m=4, n=16, r=16, K=8, d=1, T=2, ncd=1, rho=0.5, cb=None, ws_bytes=1 << 30, W=FAKE, ws=FAKE,
+               opt=None):
     E = np.arange(K * d, dtype=np.float32).reshape(K, d) if cb is None else cb
+    op = ctypes.byref(opt) if opt is not None else None
     return lib.mpq_quantize_layer(W, m, n, FAKE, FAKE, r, E.ctypes.data_as(ctypes.c_void_p), K, d, FAKE, FAKE, T,
-                                  ncd, rho, None, FAKE, None, None, None, None, ws, ws_bytes, None)
+                                  ncd, rho, op, FAKE, None, None, None, None, ws, ws_bytes, None)
 
 
 def test_argument_validation(lib):
@@ -74,6 +76,39 @@ def test_argument_validation(lib):
     assert call_layer(lib, d=8, K=256, cb=good, ws_bytes=1024) == -5
     assert call_layer(lib, d=8, K=256, cb=good, ws=ctypes.c_void_p((1 << 20) + 4)) == -5
     assert call_layer(lib, d=8, K=256, cb=good, ws=None) == -5
+
+
+def test_group_option_validation(lib):
+    Opt = mpq.binding.Options
+    assert call_layer(lib, opt=Opt(group=-1)) == -3
+    good = S.e8_codebook(256)
+    assert call_layer(lib, d=8, K=256, cb=good, opt=Opt(group=8)) == -4          # groups need d = 1
+    assert call_layer(lib, opt=Opt(group=8, anchor_tau=0.2)) == -4                # and the uniform prior
+    # an accepted group option reaches the workspace check
+    assert call_layer(lib, opt=Opt(group=8), ws_bytes=1024) == -5
+    assert call_layer(lib, opt=Opt(group=64), ws_bytes=1024) == -5                # group >= n: one per row
+    assert call_layer(lib, opt=Opt(group=0, anchor_tau=0.2), ws_bytes=1024) == -5
+
+
+def test_options_layout_matches_header(tmp_path):
+    """The ctypes mirror of mpq_options has the header's field offsets and size
+    (compiled with the host C compiler)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    Opt = mpq.binding.Options
+    names = [f[0] for f in Opt._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"mpq.h\"\nint main(void) {\n" +
+                   "".join(f'  printf("%zu\\n", offsetof(mpq_options, {nm}));\n' for nm in names) +
+                   '  printf("%zu\\n", sizeof(mpq_options));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    want = [getattr(Opt, nm).offset for nm in names] + [ctypes.sizeof(Opt)]
+    assert got == want
 
 
 def test_strerror(lib):

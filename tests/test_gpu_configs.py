@@ -1,4 +1,6 @@
-"""Parity on the five named workloads at full size (n, r, K as benchmarked).
+"""Parity on the five named workloads at full size (n, r, K as benchmarked),
+and on c3 with group-wise grids of 128 columns (the hyper-parameter
+paragraph's scalar setting).
 
 The GPU solves the whole layer in the configuration bench.py times; the
 float64 oracle solves a fixed sample of rows (every m/k-th row).  Rows are
@@ -27,17 +29,19 @@ import mpq_synth as S
 from oracle import mpq_oracle as O
 from oracle.pool import solve_rows, map_rows, cd_rows
 from parity_helpers import (SOFT_RTOL, OBJ_RTOL, CODE_FRAC, dev, host, layer_tensors, compare_layer, rel_vec,
-                            rel_scalar)
+                            rel_scalar, row_codebook)
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE = {"c1": 64, "c2": 16, "c3": 16, "c4": 8, "c5": 4}
+SAMPLE = {"c1": 64, "c2": 16, "c3": 16, "c4": 8, "c5": 4, "c3_g128": 16}
+CASES = {"c1": ("c1", 0), "c2": ("c2", 0), "c3": ("c3", 0), "c4": ("c4", 0), "c5": ("c5", 0),
+         "c3_g128": ("c3", 128)}
 E2E_TRACE_TOL = 1e-3
 
 
 def sublayer(L, rows):
-    return S.Layer(L.name + "_rows", np.ascontiguousarray(L.W[rows]), L.s, L.V, L.E, L.a[rows], L.o[rows], L.d,
-                   L.T_vamp, L.n_cd, L.damping)
+    return S.Layer(L.name + "_rows", np.ascontiguousarray(L.W[rows]), L.s, L.V, L.E, np.ascontiguousarray(L.a[rows]),
+                   np.ascontiguousarray(L.o[rows]), L.d, L.T_vamp, L.n_cd, L.damping, group=L.group)
 
 
 def teacher_forced_steps(mpq, L, Ts, refs, k_rows):
@@ -48,7 +52,8 @@ def teacher_forced_steps(mpq, L, Ts, refs, k_rows):
         R1 = dev(np.stack([x["r1"] for x in h]).astype(np.float32))
         g1 = dev(np.array([x["gamma1"] for x in h], dtype=np.float32))
         bt = dev(np.array([x["beta"] for x in h], dtype=np.float32))
-        o = mpq.vamp_step(R1, g1, bt, ytil, Ts["s"], Ts["V"], L.E, Ts["a"], Ts["o"], damping=L.damping)
+        o = mpq.vamp_step(R1, g1, bt, ytil, Ts["s"], Ts["V"], L.E, Ts["a"], Ts["o"], damping=L.damping,
+                          group=L.group)
         r1n, g1n, btn = host(R1), host(g1), host(bt)
         xh, eta1, g2, r2, fb = (host(o[k]) for k in ("xhat1", "eta1", "gamma2", "r2", "fallback"))
         for k in range(k_rows):
@@ -67,16 +72,17 @@ def teacher_forced_steps(mpq, L, Ts, refs, k_rows):
     return worst
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", list(CASES))
 def test_config_parity(name):
     import torch
     import post_quantization_solver_amd as mpq
     print(f"[config] {name}: generating inputs", flush=True)
-    L = S.make_config(name, device="cuda")
+    L = S.make_config(CASES[name][0], device="cuda", group=CASES[name][1])
+    g = L.group
     T = layer_tensors(L)
     print(f"[config] {name}: m={L.m} n={L.n} r={L.r} K={L.K} d={L.d} T={L.T_vamp} full solve on GPU", flush=True)
     out = mpq.quantize_layer(T["W"], T["s"], T["V"], L.E, T["a"], T["o"], T_vamp=L.T_vamp, n_cd=L.n_cd,
-                             damping=L.damping)
+                             damping=L.damping, group=g)
     torch.cuda.synchronize()
     gpu = {k: (host(v) if v is not None else None) for k, v in out.items()}
     del T, out
@@ -89,13 +95,13 @@ def test_config_parity(name):
 
     # GPU stages on the sampled rows alone (bitwise the same as in the full solve)
     print(f"[config] {name}: GPU stages on {k_rows} sampled rows", flush=True)
-    pro = mpq.prologue(Ts["W"], Ts["s"], Ts["V"], L.E, Ts["a"], Ts["o"])
+    pro = mpq.prologue(Ts["W"], Ts["s"], Ts["V"], L.E, Ts["a"], Ts["o"], group=g)
     R1 = Ts["W"].clone()
     g1, bt = pro["gamma1"], pro["beta"]
     for _ in range(L.T_vamp):
-        mpq.vamp_step(R1, g1, bt, pro["ytil"], Ts["s"], Ts["V"], L.E, Ts["a"], Ts["o"], damping=L.damping)
-    map_gpu = mpq.map_codes(R1, g1, L.E, Ts["a"], Ts["o"])
-    cd_gpu, _ = mpq.cd(Ts["W"], Ts["s"], Ts["V"], L.E, Ts["a"], Ts["o"], map_gpu.clone(), n_cd=L.n_cd)
+        mpq.vamp_step(R1, g1, bt, pro["ytil"], Ts["s"], Ts["V"], L.E, Ts["a"], Ts["o"], damping=L.damping, group=g)
+    map_gpu = mpq.map_codes(R1, g1, L.E, Ts["a"], Ts["o"], group=g)
+    cd_gpu, _ = mpq.cd(Ts["W"], Ts["s"], Ts["V"], L.E, Ts["a"], Ts["o"], map_gpu.clone(), n_cd=L.n_cd, group=g)
     torch.cuda.synchronize()
     r1_gpu, g1_gpu, map_gpu, cd_gpu = host(R1), host(g1), host(map_gpu), host(cd_gpu)
     same_as_full = bool(np.array_equal(cd_gpu, gpu["codes"][rows]))
@@ -106,8 +112,8 @@ def test_config_parity(name):
     cdr = cd_rows(L, rows, map_gpu)
     cd_ref = np.stack([r["codes"] for r in cdr])
     f_cd_ref = np.array([r["objective"] for r in cdr])
-    f_cd_gpu = np.array([O.codes_objective(Ls.W[k], cd_gpu[k], O.row_codewords(L.E, Ls.a[k], Ls.o[k]), L.d, L.s,
-                                           L.V) for k in range(k_rows)])
+    f_cd_gpu = np.array([O.codes_objective(Ls.W[k], cd_gpu[k], row_codebook(Ls, k), L.d, L.s, L.V)
+                         for k in range(k_rows)])
 
     report = {}
     report["step"] = {k: float(f"{v:.3g}") for k, v in teacher_forced_steps(mpq, L, Ts, refs, k_rows).items()}
@@ -121,7 +127,7 @@ def test_config_parity(name):
     report["e2e_rows_equal"] = f"{summ['rows_codes_equal']}/{k_rows}"
     report["e2e_obj_rel_max"] = summ["obj_rel_max"]
     report["e2e_obj_gpu_minus_oracle_mean"] = float(np.mean(
-        (np.array([O.codes_objective(L.W[i], gpu["codes"][i], O.row_codewords(L.E, L.a[i], L.o[i]), L.d, L.s, L.V)
+        (np.array([O.codes_objective(L.W[i], gpu["codes"][i], row_codebook(L, i), L.d, L.s, L.V)
                    for i in rows]) - np.array([r["objective"] for r in refs])) /
         np.array([r["objective"] for r in refs])))
     report["fallbacks"] = int(sum(r["fallbacks"] for r in refs))
