@@ -51,12 +51,22 @@ Readings where the pages are silent (each also listed in the design doc):
   G2  (guard) a row whose round-to-nearest point already has zero
       objective (zero RTN error, or an RTN error invisible to T) returns its
       RTN codes, objective 0 and +inf precision traces.
+  G3  sequential greedy comparator (the ablation's greedy baseline; the
+      explainer's worked example scores a block by its error when the later
+      blocks compensate exactly, and the MPQ summary's ablation table names
+      the greedy LDLQ baseline; no damping is printed): blocks in ascending
+      order, each committed to the codeword that minimises the objective with
+      the earlier blocks fixed and the later ones at their best continuous
+      values, on the damped H + delta I with delta = 0.01 mean(diag H) (the
+      damping customary for greedy solvers; it keeps a rank-deficient H
+      factorisable).  Its objective is reported on the undamped H.
 """
 from __future__ import annotations
 
 import numpy as np
 
 VAR_FLOOR_REL = 1e-24          # G1: per-coordinate variance floor, in units of a^2
+GREEDY_DAMP = 0.01             # G3: the greedy comparator's damping, relative to mean(diag H)
 _CHUNK_ELEMS = 1 << 22         # block chunking for memory only (blocks are independent)
 
 
@@ -384,6 +394,50 @@ def block_cd(codes, w, s, V, C, d, n_cd):
         if changed == 0:
             break
     return codes, changes
+
+
+def greedy_hessian(s, V, damp=GREEDY_DAMP):
+    """H + delta I with H = V diag(s^2) V^T and delta = damp * mean(diag H) (G3)."""
+    s = np.asarray(s, np.float64)
+    V = np.asarray(V, np.float64)
+    H = (V * (s * s)[None, :]) @ V.T
+    return H + (damp * float(np.mean(np.diag(H)))) * np.eye(H.shape[0])
+
+
+def sequential_greedy(w, s, V, C, d, damp=GREEDY_DAMP):
+    """Sequential greedy comparator (reading G3), block by block in ascending
+    order on f(e) = 1/2 e^T H e, H the damped greedy_hessian, e = w - x.
+
+    With the earlier blocks committed (e_<) and the later ones free, the
+    objective as a function of block b is, up to a constant,
+        1/2 (e_b - t_b)^T M_b (e_b - t_b),
+    where S = H[>=b, >=b], (t_b, t_>) = -S^{-1} H[>=b, <b] e_< is the best
+    continuous completion and M_b = ((S^{-1})[b, b])^{-1} the Schur complement
+    that leaves block b after eliminating the later blocks.  Block b takes the
+    codeword c minimising it at e_b = w_b - c (first argmin).  Returns codes.
+    """
+    w = np.asarray(w, np.float64)
+    n = w.shape[0]
+    B = n // d
+    H = greedy_hessian(s, V, damp)
+    Cb = C.block_codebooks() if isinstance(C, GroupedCodebook) else [C] * B
+    e = np.zeros(n)
+    codes = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        lo = b * d
+        S = H[lo:, lo:]
+        rhs = (H[lo:, :lo] @ e[:lo])[:, None]
+        unit = np.zeros((n - lo, d))
+        unit[:d, :] = np.eye(d)
+        X = np.linalg.solve(S, np.hstack([rhs, unit]))
+        t = -X[:d, 0]
+        M = np.linalg.inv(X[:d, 1:])
+        Eb = w[lo:lo + d][None, :] - Cb[b] - t[None, :]       # K x d : e_b(c) - t_b
+        cost = 0.5 * np.einsum("kj,kj->k", Eb @ M, Eb)
+        k = int(np.argmin(cost))
+        codes[b] = k
+        e[lo:lo + d] = w[lo:lo + d] - Cb[b][k]
+    return codes
 
 
 def objective(w, x, s, V):

@@ -33,8 +33,8 @@ def _load(path):
 
 
 def _stage(job):
-    """MAP or CD of one row from a given state (kind 'map': r1, gamma1;
-    kind 'cd': start codes)."""
+    """MAP, CD or the greedy comparator of one row (kind 'map': state = (r1,
+    gamma1); kind 'cd': state = start codes; kind 'greedy': no state)."""
     if _ROOT not in sys.path:
         sys.path.insert(0, _ROOT)
     from oracle import mpq_oracle as O
@@ -49,6 +49,9 @@ def _stage(job):
     if kind == "map":
         r1, gamma1 = state
         return O.map_codes(np.asarray(r1, np.float64), float(gamma1), C, d)
+    if kind == "greedy":
+        codes = O.sequential_greedy(w, A["s"], A["V"], C, d)
+        return dict(codes=codes, objective=O.codes_objective(w, codes, C, d, A["s"], A["V"]))
     codes, changes = O.block_cd(np.asarray(state, np.int64), w, A["s"], A["V"], C, d, S)
     return dict(codes=codes, changes=changes, objective=O.codes_objective(w, codes, C, d, A["s"], A["V"]))
 
@@ -126,3 +129,10 @@ def cd_rows(L, rows, start_codes, n_cd=None, max_workers=None):
     g = getattr(L, "group", 0)
     return _run(L, _stage, lambda tmp: [(tmp, i, L.d, S, "cd", start_codes[k], g) for k, i in enumerate(rows)],
                 max_workers)
+
+
+def greedy_rows(L, rows, max_workers=None):
+    """Oracle sequential-greedy codes (reading G3) of `rows`, with their objectives."""
+    rows = [int(i) for i in rows]
+    g = getattr(L, "group", 0)
+    return _run(L, _stage, lambda tmp: [(tmp, i, L.d, 0, "greedy", None, g) for i in rows], max_workers)

@@ -7,7 +7,8 @@ from oracle import mpq_oracle as O
 import test_oracle_pins as P
 
 _orig = {k: getattr(O, k) for k in ("denoise", "extrinsic_denoiser_to_linear", "linear_module",
-                                     "beta_em", "block_cd", "rank_target", "block_logits", "anchor_log_prior")}
+                                     "beta_em", "block_cd", "rank_target", "block_logits", "anchor_log_prior",
+                                     "greedy_hessian")}
 
 
 def denoise_var_about_r(r1, gamma1, C, d, log_prior=None, return_q=False, anchor=None):
@@ -118,6 +119,38 @@ def grouped_blocks_reversed(self):
     return out
 
 
+def greedy_undamped(s, V, damp=O.GREEDY_DAMP):
+    return _orig["greedy_hessian"](s, V, 0.0)
+
+
+def _greedy_slip(euclid=False, t_sign=-1.0):
+    def greedy(w, s, V, C, d, damp=O.GREEDY_DAMP):
+        w = np.asarray(w, float)
+        n = w.shape[0]
+        H = O.greedy_hessian(s, V, damp)
+        e = np.zeros(n)
+        codes = np.zeros(n // d, dtype=np.int64)
+        for b in range(n // d):
+            lo = b * d
+            unit = np.zeros((n - lo, d))
+            unit[:d] = np.eye(d)
+            X = np.linalg.solve(H[lo:, lo:], np.hstack([(H[lo:, :lo] @ e[:lo])[:, None], unit]))
+            t = t_sign * X[:d, 0]
+            M = np.eye(d) if euclid else np.linalg.inv(X[:d, 1:])
+            Eb = w[lo:lo + d][None, :] - C - t[None, :]
+            k = int(np.argmin(np.einsum("kj,kj->k", Eb @ M, Eb)))
+            codes[b] = k
+            e[lo:lo + d] = w[lo:lo + d] - C[k]
+        return codes
+    return greedy
+
+
+greedy_euclidean_metric = _greedy_slip(euclid=True)
+greedy_euclidean_metric.__name__ = "greedy_euclidean_metric"
+greedy_target_sign = _greedy_slip(t_sign=1.0)
+greedy_target_sign.__name__ = "greedy_target_sign"
+
+
 def rank_target_transposed(w, s, V):
     return np.asarray(s, float) * (np.asarray(V, float) @ np.asarray(w, float))
 
@@ -138,6 +171,9 @@ MUTATIONS = [
     ("anchor_log_prior", anchor_wrong_sign, [P.check_anchor_prior]),
     ("anchor_log_prior", anchor_no_half, [P.check_anchor_prior]),
     ("GroupedCodebook.block_codebooks", grouped_blocks_reversed, [P.check_grouped_local_minimum]),
+    ("greedy_hessian", greedy_undamped, [P.check_greedy_bruteforce]),
+    ("sequential_greedy", greedy_euclidean_metric, [P.check_greedy_bruteforce]),
+    ("sequential_greedy", greedy_target_sign, [P.check_greedy_bruteforce, P.check_greedy_worked_example]),
 ]
 
 

@@ -594,3 +594,88 @@ def test_mpq_beats_rtn_on_c1_rows():
         better += res["objective"] < f_rtn
         assert res["objective"] <= O.codes_objective(L.W[i], res["map_codes"], C, 1, L.s, L.V) + 1e-15
     assert better == 6
+
+
+# ----------------------------------------------------------------------------
+# sequential greedy comparator (reading G3)
+# ----------------------------------------------------------------------------
+
+def brute_greedy(w, s, V, C, d, damp):
+    """The greedy of G3 computed independently: for every block and candidate,
+    the later blocks' best continuous values come from a least-squares solve on
+    the stacked operator [T; sqrt(delta) I] (whose Gram matrix is H + delta I)."""
+    T = dense_T(s, V)
+    n = T.shape[1]
+    delta = damp * float(np.mean(np.diag(T.T @ T)))
+    A = np.vstack([T, math.sqrt(delta) * np.eye(n)])
+    e = np.zeros(n)
+    codes = []
+    for b in range(n // d):
+        hi = (b + 1) * d
+        best, bk = np.inf, -1
+        for k in range(C.shape[0]):
+            eb = e.copy()
+            eb[b * d:hi] = w[b * d:hi] - C[k]
+            r0 = A[:, :hi] @ eb[:hi]
+            if hi < n:
+                z = np.linalg.lstsq(A[:, hi:], -r0, rcond=None)[0]
+                r0 = r0 + A[:, hi:] @ z
+            cost = 0.5 * float(r0 @ r0)
+            if bk < 0 or cost < best - 1e-12 * abs(best):
+                best, bk = cost, k
+        codes.append(bk)
+        e[b * d:(b + 1) * d] = w[b * d:(b + 1) * d] - C[bk]
+    return np.array(codes)
+
+
+def check_greedy_bruteforce():
+    for seed, n, r, d, K, damp, pw in ((21, 6, 6, 1, 5, 0.0, 0.5), (22, 6, 4, 1, 5, 0.01, 0.5),
+                                       (23, 8, 8, 2, 6, 0.0, 0.5), (24, 8, 5, 2, 6, 0.01, 0.5),
+                                       (25, 8, 8, 2, 6, 0.3, 0.5), (26, 12, 12, 4, 24, 0.0, 2.0),
+                                       (27, 12, 9, 4, 24, 0.01, 2.0)):
+        w, s, V, _ = small_problem(seed, n=n, r=r, d=d, power=pw)
+        C = rng(seed + 100).standard_normal((K, d))
+        got = O.sequential_greedy(w, s, V, C, d, damp=damp)
+        ref = brute_greedy(w, s, V, C, d, damp)
+        assert list(got) == list(ref), (seed, got, ref)
+
+
+def test_greedy_matches_least_squares_bruteforce():
+    check_greedy_bruteforce()
+
+
+def check_greedy_worked_example():
+    """The explainer's greedy commits block 1 by its own error with block 2
+    compensating (A, 0.10) and ends at the printed greedy total 0.40."""
+    gold = load_golden("worked_example.txt")
+    C, s, V = worked_example_instance()
+    w = np.zeros(2)
+    codes = O.sequential_greedy(w, s, V, C, 1, damp=0.0)
+    assert codes[0] == 0
+    assert np.isclose(O.codes_objective(w, codes, C, 1, s, V), gold["greedy_total"], atol=1e-12)
+
+
+def test_greedy_worked_example():
+    check_greedy_worked_example()
+
+
+def test_greedy_uncoupled_is_round_to_nearest():
+    """Diagonal H (V = I): no coupling, so the greedy is round to nearest (d = 1)."""
+    g = rng(31)
+    n = 10
+    w = g.standard_normal(n)
+    s = np.abs(g.standard_normal(n)) + 0.1
+    E = np.arange(6, dtype=float).reshape(6, 1) * 0.7 - 1.5
+    codes = O.sequential_greedy(w, s, np.eye(n), E, 1)
+    assert list(codes) == list(O.nearest_codeword(w, E, 1))
+
+
+def test_greedy_last_block_is_best_response():
+    """Undamped, the last block has no later blocks to compensate: its code is
+    the exact best response to the committed others (CD's block rule)."""
+    w, s, V, _ = small_problem(32, n=12, r=12, d=2)
+    C = rng(132).standard_normal((7, 2))
+    codes = O.sequential_greedy(w, s, V, C, 2, damp=0.0)
+    x = C[codes].reshape(-1)
+    f = [O.objective(w, np.concatenate([x[:-2], C[k]]), s, V) for k in range(7)]
+    assert int(np.argmin(f)) == codes[-1]
