@@ -59,7 +59,8 @@ Readings where the pages are silent (each also listed in the design doc):
       the earlier blocks fixed and the later ones at their best continuous
       values, on the damped H + delta I with delta = 0.01 mean(diag H) (the
       damping customary for greedy solvers; it keeps a rank-deficient H
-      factorisable).  Its objective is reported on the undamped H.
+      factorisable; delta = 1 if H = 0).  Its objective is reported on the
+      undamped H.
 """
 from __future__ import annotations
 
@@ -397,11 +398,14 @@ def block_cd(codes, w, s, V, C, d, n_cd):
 
 
 def greedy_hessian(s, V, damp=GREEDY_DAMP):
-    """H + delta I with H = V diag(s^2) V^T and delta = damp * mean(diag H) (G3)."""
+    """H + delta I with H = V diag(s^2) V^T and delta = damp * mean(diag H) (G3);
+    delta = 1 when H = 0 (every code then scores alike, and the greedy rounds
+    to nearest)."""
     s = np.asarray(s, np.float64)
     V = np.asarray(V, np.float64)
     H = (V * (s * s)[None, :]) @ V.T
-    return H + (damp * float(np.mean(np.diag(H)))) * np.eye(H.shape[0])
+    mean_diag = float(np.mean(np.diag(H)))
+    return H + (damp * mean_diag if mean_diag > 0 else 1.0) * np.eye(H.shape[0])
 
 
 def sequential_greedy(w, s, V, C, d, damp=GREEDY_DAMP):

@@ -670,6 +670,17 @@ def test_greedy_uncoupled_is_round_to_nearest():
     assert list(codes) == list(O.nearest_codeword(w, E, 1))
 
 
+def test_greedy_zero_operator_is_round_to_nearest():
+    """s = 0 (H = 0): the damping alone remains, so the greedy rounds to nearest."""
+    g = rng(33)
+    n = 8
+    w = g.standard_normal(n)
+    Q, _ = np.linalg.qr(g.standard_normal((n, n)))
+    E = np.arange(5, dtype=float).reshape(5, 1) * 0.6 - 1.2
+    codes = O.sequential_greedy(w, np.zeros(n), Q, E, 1)
+    assert list(codes) == list(O.nearest_codeword(w, E, 1))
+
+
 def test_greedy_last_block_is_best_response():
     """Undamped, the last block has no later blocks to compensate: its code is
     the exact best response to the committed others (CD's block rule)."""
