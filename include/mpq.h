@@ -87,6 +87,10 @@ typedef struct {
                              the denoiser's variance floor then uses the row's
                              largest scale.  0: one affine per row; < 0:
                              MPQ_EPARAM */
+  /* Diagnostics of mpq_quantize_layer (optional device outputs, NULL: none). */
+  int32_t* map_codes;     /* m x (n/d): the marginal-MAP codes CD starts from */
+  double* objective;      /* m: 1/2 ||T (w - w_hat)||^2 of the returned codes, as
+                             mpq_objective computes it */
 } mpq_options;
 
 #define MPQ_F_FIXED_BETA 1u
@@ -188,6 +192,35 @@ int mpq_cd(const float* W, int64_t m, int64_t n, const float* s, const float* V,
            const float* cb, int64_t K, int64_t d, const float* row_scale, const float* row_offset,
            int n_cd, const mpq_options* opt, int32_t* codes, int32_t* cd_changes, void* workspace,
            size_t ws_bytes, void* stream);
+
+/* Sequential greedy comparator, the greedy baseline of the ablation table of
+ * the papernotes.org MPQ summary (ablation section, Table 3), with the decision
+ * rule of the
+ * learnaivisually.com explainer's "Worked example": blocks in ascending order,
+ * each committed to the codeword that minimises the objective when the earlier
+ * blocks are fixed and the later ones compensate exactly (continuous values).
+ * The pages print no formula or damping; it runs on H + delta I with
+ * delta = 0.01 mean(diag H) (1 when H = 0), H = V diag(s^2) V^T, as
+ * nearest-plane decoding on the lower triangular Lam with
+ * H + delta I = Lam^T Lam (float64 Cholesky on the GPU).  codes: m x n/d
+ * int32 output.  Needs mpq_greedy_workspace_bytes(...) of workspace (it adds
+ * the n x n float64 factor to mpq_workspace_bytes).  Column groups as in
+ * mpq_options.group; the anchored prior does not apply. */
+size_t mpq_greedy_workspace_bytes(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d);
+int mpq_greedy(const float* W, int64_t m, int64_t n, const float* s, const float* V, int64_t r,
+               const float* cb, int64_t K, int64_t d, const float* row_scale, const float* row_offset,
+               const mpq_options* opt, int32_t* codes, void* workspace, size_t ws_bytes, void* stream);
+
+/* Layer objective of given codes (the problem statement of the summary's
+ * "Method" section): objective[i] = 1/2 ||diag(s) V^T (w_i - x_i)||^2 with x_i
+ * the weights of codes[i] (m x n/d int32, each in [0, K)), computed in float64
+ * (W - X formed in float64, the rank-space product on the fp64 matrix cores,
+ * a fixed-order row sum).  objective: device, m doubles.  Column groups as in
+ * mpq_options.group. */
+int mpq_objective(const float* W, int64_t m, int64_t n, const float* s, const float* V, int64_t r,
+                  const float* cb, int64_t K, int64_t d, const float* row_scale, const float* row_offset,
+                  const mpq_options* opt, const int32_t* codes, double* objective, void* workspace,
+                  size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -428,20 +428,27 @@ def sequential_greedy(w, s, V, C, d, damp=GREEDY_DAMP):
     e = np.zeros(n)
     codes = np.zeros(B, dtype=np.int64)
     for b in range(B):
-        lo = b * d
-        S = H[lo:, lo:]
-        rhs = (H[lo:, :lo] @ e[:lo])[:, None]
-        unit = np.zeros((n - lo, d))
-        unit[:d, :] = np.eye(d)
-        X = np.linalg.solve(S, np.hstack([rhs, unit]))
-        t = -X[:d, 0]
-        M = np.linalg.inv(X[:d, 1:])
-        Eb = w[lo:lo + d][None, :] - Cb[b] - t[None, :]       # K x d : e_b(c) - t_b
-        cost = 0.5 * np.einsum("kj,kj->k", Eb @ M, Eb)
-        k = int(np.argmin(cost))
+        k = int(np.argmin(greedy_block_costs(H, w, e, Cb[b], d, b)))
         codes[b] = k
-        e[lo:lo + d] = w[lo:lo + d] - Cb[b][k]
+        e[b * d:(b + 1) * d] = w[b * d:(b + 1) * d] - Cb[b][k]
     return codes
+
+
+def greedy_block_costs(H, w, e, Cb, d, b):
+    """The greedy's cost of every codeword of block b (sequential_greedy):
+    e holds the committed errors w - x of the blocks before b (the rest is
+    ignored), H the damped greedy_hessian, Cb the block's K x d codebook."""
+    n = w.shape[0]
+    lo = b * d
+    S = H[lo:, lo:]
+    rhs = (H[lo:, :lo] @ e[:lo])[:, None]
+    unit = np.zeros((n - lo, d))
+    unit[:d, :] = np.eye(d)
+    X = np.linalg.solve(S, np.hstack([rhs, unit]))
+    t = -X[:d, 0]
+    M = np.linalg.inv(X[:d, 1:])
+    Eb = np.asarray(w, np.float64)[lo:lo + d][None, :] - Cb - t[None, :]   # K x d : e_b(c) - t_b
+    return 0.5 * np.einsum("kj,kj->k", Eb @ M, Eb)
 
 
 def objective(w, x, s, V):

@@ -23,7 +23,7 @@ STATUS = {
 F_FIXED_BETA = 1
 
 EXPORTS = ("mpq_workspace_bytes", "mpq_strerror", "mpq_quantize_layer", "mpq_prologue", "mpq_denoise",
-           "mpq_vamp_step", "mpq_map", "mpq_cd")
+           "mpq_vamp_step", "mpq_map", "mpq_cd", "mpq_objective", "mpq_greedy", "mpq_greedy_workspace_bytes")
 
 
 class MPQError(RuntimeError):
@@ -41,7 +41,8 @@ PROF_COUNT = len(PROF_NAMES)
 class Options(ctypes.Structure):
     _fields_ = [("beta0", ctypes.c_float), ("flags", ctypes.c_uint32), ("prof_mask", ctypes.c_uint32),
                 ("prof_ms", ctypes.POINTER(ctypes.c_double)), ("prof_launches", ctypes.POINTER(ctypes.c_int64)),
-                ("anchor_tau", ctypes.c_float), ("anchor_w", ctypes.c_void_p), ("group", ctypes.c_int64)]
+                ("anchor_tau", ctypes.c_float), ("anchor_w", ctypes.c_void_p), ("group", ctypes.c_int64),
+                ("map_codes", ctypes.c_void_p), ("objective", ctypes.c_void_p)]
 
 
 class Profile:
@@ -88,7 +89,13 @@ def load_library(path: str = LIB_PATH):
                                   P, P, P, P, P, P, SZ, P]
     lib.mpq_map.argtypes = [P, P, I64, I64, P, I64, I64, P, P, OPT, P, P, SZ, P]
     lib.mpq_cd.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, I, OPT, P, P, P, SZ, P]
+    lib.mpq_objective.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, OPT, P, P, P, SZ, P]
+    lib.mpq_greedy.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, OPT, P, P, SZ, P]
+    lib.mpq_greedy_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
+    lib.mpq_greedy_workspace_bytes.restype = SZ
     for name in EXPORTS[2:]:
+        if name.endswith("_bytes"):
+            continue
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -103,6 +110,10 @@ def _strerror(status: int) -> str:
 
 def workspace_bytes(m, n, r, K, d) -> int:
     return int(load_library().mpq_workspace_bytes(m, n, r, K, d))
+
+
+def greedy_workspace_bytes(m, n, r, K, d) -> int:
+    return int(load_library().mpq_greedy_workspace_bytes(m, n, r, K, d))
 
 
 # ---------------------------------------------------------------- helpers
@@ -147,12 +158,14 @@ def _workspace(m, n, r, K, d, device):
     return torch.empty(nb, dtype=torch.uint8, device=device)
 
 
-def _opts(beta0=None, fixed_beta=False, profile=None, anchor_tau=None, anchor_w=None, group=None):
+def _opts(beta0=None, fixed_beta=False, profile=None, anchor_tau=None, anchor_w=None, group=None, map_codes=None,
+          objective=None):
     flags = (F_FIXED_BETA if fixed_beta else 0) | (F_PROFILE if profile is not None else 0)
     o = Options(float(beta0) if beta0 else 0.0, flags, profile.mask if profile is not None else 0,
                 profile.ms if profile is not None else None, profile.launches if profile is not None else None,
                 float(anchor_tau) if anchor_tau else 0.0, anchor_w.data_ptr() if anchor_w is not None else None,
-                int(group) if group else 0)
+                int(group) if group else 0, map_codes.data_ptr() if map_codes is not None else None,
+                objective.data_ptr() if objective is not None else None)
     return ctypes.byref(o), o
 
 
@@ -176,7 +189,7 @@ def _check(rc, what):
 
 def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, damping=0.5, beta0=None,
                    fixed_beta=False, workspace=None, traces=True, profile=None, outputs=None, anchor_tau=None,
-                   group=None):
+                   group=None, diagnostics=False):
     """Full MPQ solve of one layer (mpq_quantize_layer).
 
     Returns dict(codes, beta_tr, gamma1_tr, gamma2_tr, cd_changes) of device
@@ -184,7 +197,9 @@ def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, dampin
     `outputs` (a dict from a previous call) reuses its output tensors;
     `anchor_tau` > 0 selects the anchored codebook prior (None: uniform);
     `group` > 0 gives every `group` consecutive columns their own affine
-    (row_scale and row_offset then m x ceil(n / group)).
+    (row_scale and row_offset then m x ceil(n / group)); `diagnostics` adds
+    map_codes (the marginal-MAP codes CD starts from) and objective (float64,
+    per row) to the result.
     """
     import torch
     m, n = W.shape
@@ -205,13 +220,18 @@ def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, dampin
         g2 = torch.empty((m, T_vamp), dtype=torch.float32, device=dev) if traces and T_vamp > 0 else None
         ch = torch.zeros((m, n_cd), dtype=torch.int32, device=dev) if traces and n_cd > 0 else None
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
-    op, _keep = _opts(beta0, fixed_beta, profile, anchor_tau, None, group)
+    mc = torch.empty((m, n // d), dtype=torch.int32, device=dev) if diagnostics else None
+    obj = torch.empty(m, dtype=torch.float64, device=dev) if diagnostics else None
+    op, _keep = _opts(beta0, fixed_beta, profile, anchor_tau, None, group, mc, obj)
     rc = load_library().mpq_quantize_layer(
         _ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d, _ptr(row_scale),
         _ptr(row_offset), int(T_vamp), int(n_cd), float(damping), op, _ptr(codes), _ptr(bt), _ptr(g1), _ptr(g2),
         _ptr(ch), _ptr(ws), ws.numel(), _stream())
     _check(rc, "mpq_quantize_layer")
-    return dict(codes=codes, beta_tr=bt, gamma1_tr=g1, gamma2_tr=g2, cd_changes=ch)
+    out = dict(codes=codes, beta_tr=bt, gamma1_tr=g1, gamma2_tr=g2, cd_changes=ch)
+    if diagnostics:
+        out.update(map_codes=mc, objective=obj)
+    return out
 
 
 def prologue(W, s, V, cb, row_scale, row_offset, beta0=None, workspace=None, group=None):
@@ -325,3 +345,51 @@ def cd(W, s, V, cb, row_scale, row_offset, codes, n_cd=3, workspace=None, group=
                                ws.numel(), _stream())
     _check(rc, "mpq_cd")
     return codes, ch[:, :n_cd]
+
+
+def objective(W, s, V, cb, row_scale, row_offset, codes, workspace=None, group=None):
+    """Per-row float64 objective 1/2 ||diag(s) V^T (w - x)||^2 of `codes` (mpq_objective)."""
+    import torch
+    m, n = W.shape
+    r = s.shape[0]
+    E = _host_codebook(cb)
+    K, d = E.shape
+    _dev(W, torch.float32, "W")
+    _dev(s, torch.float32, "s", (r,))
+    _dev(V, torch.float32, "V", (n, r))
+    _dev(codes, torch.int32, "codes", (m, n // d))
+    _affine(row_scale, row_offset, m, n, group)
+    f = torch.empty(m, dtype=torch.float64, device=W.device)
+    ws = workspace if workspace is not None else _workspace(m, n, r, K, d, W.device)
+    op, _keep = _opts(group=group)
+    rc = load_library().mpq_objective(_ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d,
+                                      _ptr(row_scale), _ptr(row_offset), op, _ptr(codes), _ptr(f), _ptr(ws),
+                                      ws.numel(), _stream())
+    _check(rc, "mpq_objective")
+    return f
+
+
+def greedy(W, s, V, cb, row_scale, row_offset, workspace=None, group=None, profile=None):
+    """Sequential greedy comparator codes (mpq_greedy); the workspace must hold
+    greedy_workspace_bytes(...)."""
+    import torch
+    m, n = W.shape
+    r = s.shape[0]
+    E = _host_codebook(cb)
+    K, d = E.shape
+    _dev(W, torch.float32, "W")
+    _dev(s, torch.float32, "s", (r,))
+    _dev(V, torch.float32, "V", (n, r))
+    _affine(row_scale, row_offset, m, n, group)
+    codes = torch.empty((m, n // d), dtype=torch.int32, device=W.device)
+    if workspace is None:
+        nb = greedy_workspace_bytes(m, n, r, K, d)
+        if nb == 0:
+            raise MPQError(-2, "mpq_greedy_workspace_bytes")
+        workspace = torch.empty(nb, dtype=torch.uint8, device=W.device)
+    op, _keep = _opts(profile=profile, group=group)
+    rc = load_library().mpq_greedy(_ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d,
+                                   _ptr(row_scale), _ptr(row_offset), op, _ptr(codes), _ptr(workspace),
+                                   workspace.numel(), _stream())
+    _check(rc, "mpq_greedy")
+    return codes

@@ -27,6 +27,7 @@ hipError_t launch_nearest_lattice(const float*, int64_t, int64_t, const CbTables
 hipError_t launch_beta_lin(int64_t, const float*, const float*, float*, float*, hipStream_t);
 hipError_t launch_fill_i32(int32_t*, int64_t, int32_t, hipStream_t);
 hipError_t launch_record_i32(const int32_t* src, int64_t m, int32_t* dst, int64_t ld, int64_t col, hipStream_t st);
+hipError_t launch_fill_f64(double* dst, int64_t count, double v, hipStream_t st);
 }  // namespace mpq
 
 using namespace mpq;
@@ -70,18 +71,23 @@ constexpr size_t ALIGN = 256;
 struct Layout {
   int64_t m, n, r, K, d, B;
   int Kpad, ncoltiles, ntiles, nslices;
-  size_t off[32];
+  size_t off[48];   // >= R_COUNT (checked below)
   size_t total;
 };
 
 enum Region {
   R_VS, R_VST, R_YTIL, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI,
-  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_SPLIT, R_TKEY, R_QF, R_VSP, R_VSTP, R_R2P, R_ZP, R_ANCH, R_COUNT
+  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_SPLIT, R_TKEY, R_QF, R_VSP, R_VSTP, R_R2P, R_ZP, R_ANCH,
+  R_LAM, R_CTMP, R_GDIAG, R_COUNT
 };
+
+static_assert(R_COUNT <= (int)(sizeof(Layout::off) / sizeof(size_t)), "Layout::off holds every region");
 
 size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
-Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
+// greedy: also the regions of the sequential greedy comparator (the n x n
+// triangular factor and its scratch).
+Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, bool greedy = false) {
   Layout L;
   L.m = m; L.n = n; L.r = r; L.K = K; L.d = d;
   L.B = n / d;
@@ -126,6 +132,9 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
   sz[R_R2P] = packed_split_words(m, n) * sizeof(uint32_t);
   sz[R_ZP] = packed_split_words(m, r) * sizeof(uint32_t);
   sz[R_ANCH] = (size_t)m * n * f;   // anchored-prior cavity mean
+  sz[R_LAM] = greedy ? (size_t)n * n * f64 : 0;
+  sz[R_CTMP] = greedy ? chol_tmp_doubles(n) * f64 : 0;
+  sz[R_GDIAG] = greedy ? (size_t)KD * KD * f64 : 0;
   size_t o = 0;
   for (int k = 0; k < R_COUNT; ++k) {
     L.off[k] = o;
@@ -623,6 +632,67 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
   return rc;
 }
 
+// f[i] = 1/2 ||diag(s) V^T (w_i - x_i)||^2 of the codes' weights x, float64:
+// D = W - X (float64), U = D VS on the fp64 matrix cores, then a fixed-order
+// row sum.  Uses the CD residual regions of the workspace.
+int run_objective(Ctx& c, const float* W, const float* a, const float* o, const int32_t* codes, double* f) {
+  const Layout& L = c.L;
+  double* D = reinterpret_cast<double*>(c.p(R_D64));
+  double* U = reinterpret_cast<double*>(c.p(R_U64));
+  TIMED(c, MPQ_PROF_OTHER, launch_gather(codes, L.m, L.n, c.cb, a, o, W, nullptr, nullptr, nullptr, c.st, D));
+  TIMED(c, MPQ_PROF_OTHER,
+        launch_gemm64(EPI_STORE, true, gemm64((int)L.m, (int)L.r, (int)L.n, D, L.n, c.p(R_VST), L.n, U, L.r), c.st));
+  TIMED(c, MPQ_PROF_OTHER, launch_half_sumsq64(U, L.m, L.r, f, c.st));
+  return MPQ_OK;
+}
+
+// Sequential greedy comparator (G3 in the oracle): factor the damped H, then
+// commit the blocks in ascending order, tile by tile.
+constexpr double GREEDY_DAMP = 0.01;
+int run_greedy(Ctx& c, const float* W, const float* a, const float* o, int32_t* codes) {
+  const Layout& L = c.L;
+  double* Lam = reinterpret_cast<double*>(c.p(R_LAM));
+  double* Rt = reinterpret_cast<double*>(c.p(R_HD));
+  double* P = reinterpret_cast<double*>(c.p(R_D64));
+  double* En = reinterpret_cast<double*>(c.p(R_DELTA));
+  double* Gd = reinterpret_cast<double*>(c.p(R_GDIAG));
+  uint32_t* tk = reinterpret_cast<uint32_t*>(c.p(R_TKEY));
+  uint32_t* qf = reinterpret_cast<uint32_t*>(c.p(R_QF));
+  TIMED(c, MPQ_PROF_OTHER, launch_greedy_factor(c.p(R_VS), L.n, L.r, GREEDY_DAMP, Lam,
+                                                reinterpret_cast<double*>(c.p(R_CTMP)), c.st));
+  TIMED(c, MPQ_PROF_OTHER, launch_greedy_rtiles(Lam, L.n, KD, Rt, c.st));
+  TIMED(c, MPQ_PROF_OTHER, launch_fill_f64(P, L.m * L.n, 0.0, c.st));
+  for (int tl = 0; tl < L.ntiles; ++tl) {
+    const int64_t j0 = (int64_t)tl * KD;
+    const int kw = (int)std::min<int64_t>(KD, L.n - j0);
+    const double* Rtile = Rt + (int64_t)tl * KD * KD;
+    if (L.d == 1) {
+      TIMED(c, MPQ_PROF_CD_SEARCH,
+            launch_greedy_scalar_tile(L.m, L.n, j0, kw, P, Rtile, W, c.cb, a, o, codes, En, c.st));
+    } else {
+      TIMED(c, MPQ_PROF_CD_SEARCH, launch_greedy_gdiag(Lam, L.n, j0, kw, Gd, c.st));
+      TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_lattice_tkeys(kw / 8, kw, Gd, c.cb, tk, c.st));
+      TIMED(c, MPQ_PROF_CD_SEARCH, launch_greedy_query(L.m, L.n, j0, P, Lam, W, a, o, qf, c.st));
+      for (int bl = 0; bl < kw / 8; ++bl) {
+        TIMED(c, MPQ_PROF_CD_SEARCH,
+              launch_cd_lattice_score(L.m, bl, tk, c.cb, qf, c.p(R_PS), c.pi(R_PI), c.st));
+        TIMED(c, MPQ_PROF_CD_SEARCH,
+              launch_greedy_update(L.m, L.n, j0, j0 / 8 + bl, bl, kw, P, Lam, Rtile, W, c.cb, a, o, c.p(R_PS),
+                                   c.pi(R_PI), codes, En, qf, c.st));
+      }
+    }
+    const int64_t j1 = j0 + kw;
+    if (j1 < L.n) {
+      // P[:, j1:] -= (-E) Lam[j1:, j0:j1]^T
+      Gemm64Args g = gemm64((int)L.m, (int)(L.n - j1), kw, En, kw, nullptr, 0, P + j1, L.n);
+      g.B64 = Lam + j1 * L.n + j0;
+      g.ldb = L.n;
+      TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_SUB_INPLACE, true, g, c.st));
+    }
+  }
+  return MPQ_OK;
+}
+
 // The whole layer: prologue, T_vamp iterations, marginal MAP, CD.
 int solve_layer(Ctx& c, const float* W, const float* s, const float* V, const float* row_scale,
                 const float* row_offset, int T_vamp, int n_cd, float damping, const mpq_options* opt, int32_t* codes,
@@ -654,11 +724,15 @@ int solve_layer(Ctx& c, const float* W, const float* s, const float* V, const fl
     Rm = c.p(R_ANCH);
   }
   TIMED(c, MPQ_PROF_MAP, nearest(c, Rm, codes, row_scale, row_offset));
-  return run_cd(c, W, row_scale, row_offset, n_cd, codes, cd_changes);
+  if (opt && opt->map_codes) TIMED(c, MPQ_PROF_OTHER, launch_copy_i32(codes, opt->map_codes, L.m * L.B, c.st));
+  rc = run_cd(c, W, row_scale, row_offset, n_cd, codes, cd_changes);
+  if (rc) return rc;
+  if (opt && opt->objective) return run_objective(c, W, row_scale, row_offset, codes, opt->objective);
+  return MPQ_OK;
 }
 
 int begin(Ctx& c, int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, const float* cb, void* ws, size_t bytes,
-          void* stream, const mpq_options* opt = nullptr) {
+          void* stream, const mpq_options* opt = nullptr, bool greedy = false) {
   if (opt && (opt->flags & MPQ_F_PROFILE)) {
     c.prof.on = true;
     c.prof.mask = opt->prof_mask;
@@ -686,7 +760,7 @@ int begin(Ctx& c, int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, const f
       c.cb.G = (int)((n + opt->group - 1) / opt->group);
     }
   }
-  c.L = make_layout(m, n, r, K, d);
+  c.L = make_layout(m, n, r, K, d, greedy);
   rc = check_ws(c.L, ws, bytes);
   if (rc) return rc;
   c.ws = static_cast<char*>(ws);
@@ -714,6 +788,11 @@ extern "C" {
 size_t mpq_workspace_bytes(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
   if (check_shapes(m, n, r, K, d) != MPQ_OK) return 0;
   return make_layout(m, n, r, K, d).total;
+}
+
+size_t mpq_greedy_workspace_bytes(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d) {
+  if (check_shapes(m, n, r, K, d) != MPQ_OK) return 0;
+  return make_layout(m, n, r, K, d, true).total;
 }
 
 const char* mpq_strerror(int status) {
@@ -845,6 +924,36 @@ int mpq_cd(const float* W, int64_t m, int64_t n, const float* s, const float* V,
   if ((rc = upload_codebook(c, cb))) return rc;
   if ((rc = prepare_factors(c, V, s))) return rc;
   return finish(c, run_cd(c, W, row_scale, row_offset, n_cd, codes, cd_changes));
+}
+
+int mpq_greedy(const float* W, int64_t m, int64_t n, const float* s, const float* V, int64_t r, const float* cb,
+               int64_t K, int64_t d, const float* row_scale, const float* row_offset, const mpq_options* opt,
+               int32_t* codes, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_shapes(m, n, r, K, d);
+  if (rc) return rc;
+  if (m == 0) return MPQ_OK;
+  if (!W || !s || !V || !row_scale || !row_offset || !codes) return MPQ_ENULL;
+  Ctx c;
+  rc = begin(c, m, n, r, K, d, cb, workspace, ws_bytes, stream, opt, true);
+  if (rc) return rc;
+  if ((rc = upload_codebook(c, cb))) return rc;
+  if ((rc = prepare_factors(c, V, s))) return rc;
+  return finish(c, run_greedy(c, W, row_scale, row_offset, codes));
+}
+
+int mpq_objective(const float* W, int64_t m, int64_t n, const float* s, const float* V, int64_t r, const float* cb,
+                  int64_t K, int64_t d, const float* row_scale, const float* row_offset, const mpq_options* opt,
+                  const int32_t* codes, double* objective, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_shapes(m, n, r, K, d);
+  if (rc) return rc;
+  if (m == 0) return MPQ_OK;
+  if (!W || !s || !V || !row_scale || !row_offset || !codes || !objective) return MPQ_ENULL;
+  Ctx c;
+  rc = begin(c, m, n, r, K, d, cb, workspace, ws_bytes, stream, opt);
+  if (rc) return rc;
+  if ((rc = upload_codebook(c, cb))) return rc;
+  if ((rc = prepare_factors(c, V, s))) return rc;
+  return finish(c, run_objective(c, W, row_scale, row_offset, codes, objective));
 }
 
 }  // extern "C"

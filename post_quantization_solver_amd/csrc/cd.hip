@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t 
     g[s] = in ? G[i * kd + jj] : 0.0;
     cd[s] = in ? codes[i * n + j0 + jj] : 0;
     const int64_t ag = i * ng + (in ? (int)(j0 + jj) / gs : 0);
-    x[s] = in ? (double)a[ag] * (double)levels[cd[s]] + (double)o[ag] : 0.0;
+    x[s] = in ? (double)a[ag] * (double)levels[safe_code(cd[s], K)] + (double)o[ag] : 0.0;
     dl[s] = 0.0;
   }
   int moved = 0;

@@ -18,46 +18,13 @@
 #include <math.h>
 #include "mpq_device.h"
 #include "internal.h"
+#include "lattice_search.h"
 
 namespace mpq {
 
 constexpr int CDL_ROWS_WAVE = 64;            // 4 row subtiles per wave
 constexpr int CDL_ROWS_WG = 4 * CDL_ROWS_WAVE;
 constexpr int CDL_CW_WG = 512;               // codewords per workgroup slice
-
-__device__ __forceinline__ v4u pack8(const uint32_t (&w)[8]) {
-  v4u r;
-  r.x = pack2(w[0], w[1]);
-  r.y = pack2(w[2], w[3]);
-  r.z = pack2(w[4], w[5]);
-  r.w = pack2(w[6], w[7]);
-  return r;
-}
-
-// (score, index) pairs ordered by score, ties to the lower index.
-struct Cand {
-  float v;
-  int i;
-};
-__device__ __forceinline__ bool cand_less(float v1, int i1, float v2, int i2) {
-  return v1 < v2 || (v1 == v2 && i1 < i2);
-}
-// Merge two sorted top-2 lists (a1 <= a2, c1 <= c2) into the top 2 of the four.
-__device__ __forceinline__ void merge_top2(Cand& a1, Cand& a2, Cand c1, Cand c2) {
-  if (cand_less(c1.v, c1.i, a1.v, a1.i)) {
-    Cand sec = cand_less(a1.v, a1.i, c2.v, c2.i) ? a1 : c2;
-    a1 = c1;
-    a2 = sec;
-  } else if (cand_less(c1.v, c1.i, a2.v, a2.i)) {
-    a2 = c1;
-  }
-}
-__device__ __forceinline__ Cand shfl_cand(Cand c, int mask) {
-  Cand o;
-  o.v = shfl_xor_f(c.v, mask);
-  o.i = shfl_xor_i(c.i, mask);
-  return o;
-}
 
 // t fragments of one CD tile: for block bl of the tile and codeword cw, the
 // K-slots 24..31 of the score key, [t hi, mid, lo, hi, mid, hi, 0, 0] with
@@ -95,34 +62,13 @@ __global__ __launch_bounds__(256) void cd_tkeys_kernel(int kd, const double* __r
   tk[(int64_t)bl * Kpad + cw] = pack8(ww);
 }
 
-// Query fragments of row i for block b (tile block bl): the K-slots of the
-// score MFMA's query column, [q hi (8) | q mid (8) | q lo (8) | A hi, hi, hi,
-// mid, mid, lo, 0, 0] with q = -a (a G e_x + g) and A = a^2, so that with the
-// keys [e | e | e | t terms] the score is A t(e) + e . q, i.e. dF(e) up to a
-// per-row constant.  G is the block's 8 x 8 diagonal of H, e_x the current
-// codeword, g the block's gradient (lane p < 8 passes g[p]).  Called by a whole
-// wave; lanes 0..15 write the 16 words of qf[i].
-// The writer: lane p (= lane & 7) passes ge = (G e_x)[p] and g[p].
+// CD's query for block b: q = -a (a G e_x + g) (G the block's 8 x 8 diagonal
+// of H, e_x the current codeword, g the block's gradient), so the score is
+// dF(e) up to a per-row constant.  Lane p (= lane & 7) passes ge = (G e_x)[p]
+// and g[p].
 __device__ __forceinline__ void cd_query_write(int lane, int64_t i, double ge, double gp, double ai,
                                                uint32_t* __restrict__ qf) {
-  const float qv = (float)(-ai * fma(ai, ge, gp));
-  uint32_t h, mm, l;
-  split3_bf16(qv, h, mm, l);
-  // lane 8 sel + p holds part sel of q[p]; word w of group gi (< 3), written
-  // by lane 4 gi + w, packs part gi of q[2w] and q[2w + 1]
-  const int sel = (lane >> 3) & 3;
-  const uint32_t part = sel == 0 ? h : (sel == 1 ? mm : l);
-  const int gi = (lane >> 2) & 3, w = lane & 3;
-  const uint32_t lo = shfl_i(part, 8 * gi + 2 * w);
-  const uint32_t hi = shfl_i(part, 8 * gi + 2 * w + 1);
-  uint32_t word = pack2(lo, hi);
-  if (gi == 3) {
-    uint32_t ah, am, al;
-    split3_bf16((float)(ai * ai), ah, am, al);
-    const uint32_t aw[8] = {ah, ah, ah, am, am, al, 0u, 0u};
-    word = pack2(aw[2 * w], aw[2 * w + 1]);
-  }
-  if (lane < 16) qf[i * 16 + lane] = word;
+  query_write(lane, i, (float)(-ai * fma(ai, ge, gp)), ai, qf);
 }
 
 __device__ __forceinline__ void cd_query_row(int lane, int64_t i, int bl, int kd, double gp,
@@ -140,14 +86,15 @@ __device__ __forceinline__ void cd_query_row(int lane, int64_t i, int bl, int kd
 // the previous block's update).  One wave per row.
 __global__ __launch_bounds__(256) void cd_query_kernel(int64_t m, int64_t n, int64_t b, int bl, int kd,
                                                        const double* __restrict__ Gt, const double* __restrict__ Ht,
-                                                       const float* __restrict__ e32, const float* __restrict__ a,
+                                                       const float* __restrict__ e32, int K,
+                                                       const float* __restrict__ a,
                                                        const int32_t* __restrict__ codes,
                                                        uint32_t* __restrict__ qf) {
   const int lane = threadIdx.x & 63;
   const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= m) return;
   const double gp = Gt[i * kd + 8 * bl + (lane & 7)];
-  cd_query_row(lane, i, bl, kd, gp, Ht, e32 + (int64_t)codes[i * (n / 8) + b] * 8, (double)a[i], qf);
+  cd_query_row(lane, i, bl, kd, gp, Ht, e32 + (int64_t)safe_code(codes[i * (n / 8) + b], K) * 8, (double)a[i], qf);
 }
 
 // A score with its 2 low mantissa bits replaced by the codeword's position v
@@ -237,13 +184,6 @@ __global__ __launch_bounds__(256) void cd_score_kernel(int64_t m, int bl, const 
   }
 }
 
-// Sum over the wave, fixed butterfly order (the same value in every lane).
-__device__ __forceinline__ double wave_sum_d(double x) {
-#pragma unroll
-  for (int msk = 1; msk < 64; msk <<= 1) x += __shfl_xor(x, msk, 64);
-  return x;
-}
-
 // One wave per row: merge the slices' top-2 lists, re-score the two
 // finalists exactly in float64 and move on a strict decrease; then update
 // the tile gradient and write the next block's query fragments.  Everything
@@ -257,7 +197,8 @@ __device__ __forceinline__ double wave_sum_d(double x) {
 constexpr int CD_COLS_LANE = 4;   // tile columns per lane in the gradient update (tile width <= 256)
 __global__ __launch_bounds__(256) void cd_update_kernel(int64_t m, int64_t n, int64_t b, int bl, int kd, int nslices,
                                                         double* __restrict__ Gt, const double* __restrict__ Ht,
-                                                        const float* __restrict__ e32, const float* __restrict__ a,
+                                                        const float* __restrict__ e32, int K,
+                                                        const float* __restrict__ a,
                                                         const float* __restrict__ part_s,
                                                         const int32_t* __restrict__ part_i,
                                                         int32_t* __restrict__ codes, double* __restrict__ Delta,
@@ -272,15 +213,16 @@ __global__ __launch_bounds__(256) void cd_update_kernel(int64_t m, int64_t n, in
 
   // ---- loads that do not depend on the merge
   const int cx = codes[i * B + b];
-  const int cn = has_next ? codes[i * B + b + 1] : 0;
+  const int cn = has_next ? safe_code(codes[i * B + b + 1], K) : 0;
+  const int cxs = safe_code(cx, K);
   const double ai = a[i];
   const double hpk = Ht[(int64_t)(8 * bl + p) * kd + 8 * bl + k];
   const double gpp = Gt[i * kd + 8 * bl + p];
   const double gnext = has_next ? Gt[i * kd + c0 + k] : 0.0;
-  const float exp_ = e32[(int64_t)cx * 8 + p], exk = e32[(int64_t)cx * 8 + k];
+  const float exp_ = e32[(int64_t)cxs * 8 + p], exk = e32[(int64_t)cxs * 8 + k];
   float exq[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) exq[q] = e32[(int64_t)cx * 8 + q];
+  for (int q = 0; q < 8; ++q) exq[q] = e32[(int64_t)cxs * 8 + q];
   // gradient update operands: column jc = lane + 64 u of the tile, rows 8 bl + q of
   // H's diagonal tile (symmetric, read as H[8 bl + q][jc] so the loads coalesce)
   double gcol[CD_COLS_LANE], hcol[CD_COLS_LANE][8];
@@ -422,7 +364,8 @@ hipError_t launch_cd_lattice_block(int64_t m, int64_t n, int64_t b, int bl, int 
   if (m <= 0) return hipSuccess;
   const dim3 rows_grid((unsigned)((m + 3) / 4));
   if (bl == 0) {
-    hipLaunchKernelGGL(cd_query_kernel, rows_grid, dim3(256), 0, st, m, n, b, bl, kd, Gt, Ht, cb.e32, a, codes, qf);
+    hipLaunchKernelGGL(cd_query_kernel, rows_grid, dim3(256), 0, st, m, n, b, bl, kd, Gt, Ht, cb.e32, cb.K, a, codes,
+                       qf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -432,11 +375,21 @@ hipError_t launch_cd_lattice_block(int64_t m, int64_t n, int64_t b, int bl, int 
                      cb.Kpad, reinterpret_cast<const v4u*>(qf), part_s, part_i);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(cd_update_kernel, rows_grid, dim3(256), 0, st, m, n, b, bl, kd, nslices, Gt, Ht, cb.e32, a,
-                     part_s, part_i, codes, Delta, changes, qf);
+  hipLaunchKernelGGL(cd_update_kernel, rows_grid, dim3(256), 0, st, m, n, b, bl, kd, nslices, Gt, Ht, cb.e32, cb.K,
+                     a, part_s, part_i, codes, Delta, changes, qf);
   return hipGetLastError();
 }
 
 int cd_lattice_slices(int Kpad) { return (Kpad + CDL_CW_WG - 1) / CDL_CW_WG; }
+
+hipError_t launch_cd_lattice_score(int64_t m, int bl, const uint32_t* tk, const CbTables& cb, const uint32_t* qf,
+                                   float* part_s, int32_t* part_i, hipStream_t st) {
+  if (m <= 0) return hipSuccess;
+  const int nslices = cd_lattice_slices(cb.Kpad);
+  dim3 g1((unsigned)nslices, (unsigned)((m + CDL_ROWS_WG - 1) / CDL_ROWS_WG));
+  hipLaunchKernelGGL(cd_score_kernel, g1, dim3(256), 0, st, m, bl, cb.qk_keys, reinterpret_cast<const v4u*>(tk),
+                     cb.Kpad, reinterpret_cast<const v4u*>(qf), part_s, part_i);
+  return hipGetLastError();
+}
 
 }  // namespace mpq

@@ -1,8 +1,9 @@
 // Float64 GEMM on the CDNA4 fp64 matrix cores, for the coordinate-descent
 // state (rank-space residual, tile gradients and the diagonal tiles of H):
 //
-//   C[M x N] (=, -=) A[M x K] * B[N x K]^T,   A float64 or float32,
-//   B float32 (widened exactly on load), C float64.
+//   C[M x N] (=, -=) A[M x K] * B[N x K]^T,   A and B float64, or A float64
+//   and B float32, or both float32 (float32 widened exactly on load), C float64;
+//   optionally only the tiles that touch the lower triangle (col <= row).
 //
 // CD decides integer codes from small differences of these quantities, so
 // they are kept in float64.  Same tiling as the float32 kernel: 256 threads
@@ -54,7 +55,7 @@ __device__ __forceinline__ void store_tile64(double* lds, int t, const double (&
   }
 }
 
-template <typename TA, int EPI, bool VEC>
+template <typename TA, typename TB, int EPI, bool VEC>
 __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
   __shared__ double As[2][GEMM_BM * LDS64];
   __shared__ double Bs[2][GEMM_BN * LDS64];
@@ -67,6 +68,7 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
   const int lg = lane >> 4;
   const int row0 = blockIdx.y * GEMM_BM;
   const int col0 = blockIdx.x * GEMM_BN;
+  if (g.lower && col0 >= row0 + GEMM_BM) return;   // whole tile above the diagonal
   const int z = blockIdx.z;
   // split K: chunk z covers k in [z * kchunk, min(K, (z+1) * kchunk)) and
   // writes its partial product to slice z of C (stride sC); otherwise z is the batch
@@ -74,7 +76,9 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
   const int kbeg = split ? z * g.kchunk : 0;
   const int Kz = split ? min(g.K - kbeg, g.kchunk) : g.K;
   const TA* A = reinterpret_cast<const TA*>(g.A) + (split ? (int64_t)kbeg : (int64_t)z * g.sA);
-  const float* B = g.B + (split ? (int64_t)kbeg : (int64_t)z * g.sB);
+  const TB* B = reinterpret_cast<const TB*>(sizeof(TB) == 8 ? static_cast<const void*>(g.B64)
+                                                            : static_cast<const void*>(g.B)) +
+                (split ? (int64_t)kbeg : (int64_t)z * g.sB);
   double* C = g.C + (int64_t)z * g.sC;
 
   v4d acc[4][4];
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
   const int nk = (Kz + BK64 - 1) / BK64;
   double ra[2][4], rb[2][4];
   load_tile64<TA, VEC>(A, g.lda, g.M, Kz, row0, 0, t, ra);
-  load_tile64<float, VEC>(B, g.ldb, g.N, Kz, col0, 0, t, rb);
+  load_tile64<TB, VEC>(B, g.ldb, g.N, Kz, col0, 0, t, rb);
   store_tile64(As[0], t, ra);
   store_tile64(Bs[0], t, rb);
   __syncthreads();
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
     const int cur = kt & 1;
     if (kt + 1 < nk) {
       load_tile64<TA, VEC>(A, g.lda, g.M, Kz, row0, (kt + 1) * BK64, t, ra);
-      load_tile64<float, VEC>(B, g.ldb, g.N, Kz, col0, (kt + 1) * BK64, t, rb);
+      load_tile64<TB, VEC>(B, g.ldb, g.N, Kz, col0, (kt + 1) * BK64, t, rb);
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -151,18 +155,19 @@ __global__ void splitk_reduce_kernel(const double* __restrict__ P, int64_t slice
     *cp = *cp - acc;
 }
 
-template <typename TA, int EPI>
+template <typename TA, int EPI, typename TB = float>
 static hipError_t launch64(const Gemm64Args& g, hipStream_t st) {
   dim3 grid(gemm_col_tiles(g.N), (g.M + GEMM_BM - 1) / GEMM_BM, g.batch > 0 ? g.batch : 1);
   if (g.ksplit > 1) grid.z = g.ksplit;
-  const size_t ea = sizeof(TA);
+  const size_t ea = sizeof(TA), eb = sizeof(TB);
+  const void* bp = eb == 8 ? static_cast<const void*>(g.B64) : static_cast<const void*>(g.B);
   bool vec = (g.K % 4 == 0) && (g.lda % 4 == 0) && (g.ldb % 4 == 0) && (g.sA % 4 == 0) && (g.sB % 4 == 0) &&
-             ((reinterpret_cast<uintptr_t>(g.A) % (4 * ea)) == 0) && ((reinterpret_cast<uintptr_t>(g.B) & 15) == 0);
+             ((reinterpret_cast<uintptr_t>(g.A) % (4 * ea)) == 0) && ((reinterpret_cast<uintptr_t>(bp) % (4 * eb)) == 0);
   if (g.ksplit > 1) vec = vec && (g.kchunk % 4 == 0);
   if (vec)
-    hipLaunchKernelGGL((gemm64_nt_kernel<TA, EPI, true>), grid, dim3(256), 0, st, g);
+    hipLaunchKernelGGL((gemm64_nt_kernel<TA, TB, EPI, true>), grid, dim3(256), 0, st, g);
   else
-    hipLaunchKernelGGL((gemm64_nt_kernel<TA, EPI, false>), grid, dim3(256), 0, st, g);
+    hipLaunchKernelGGL((gemm64_nt_kernel<TA, TB, EPI, false>), grid, dim3(256), 0, st, g);
   return hipGetLastError();
 }
 
@@ -193,6 +198,12 @@ hipError_t launch_gemm64_splitk(int epi, const Gemm64Args& g0, int splits, doubl
 
 hipError_t launch_gemm64(int epi, bool a_is_f64, const Gemm64Args& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.B64) {
+    if (!a_is_f64 || g.ksplit > 1) return hipErrorInvalidValue;
+    if (epi == EPI_STORE) return launch64<double, EPI_STORE, double>(g, st);
+    if (epi == EPI_SUB_INPLACE) return launch64<double, EPI_SUB_INPLACE, double>(g, st);
+    return hipErrorInvalidValue;
+  }
   if (a_is_f64) {
     if (epi == EPI_STORE) return launch64<double, EPI_STORE>(g, st);
     if (epi == EPI_SUB_INPLACE) return launch64<double, EPI_SUB_INPLACE>(g, st);

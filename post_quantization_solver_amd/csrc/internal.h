@@ -51,6 +51,8 @@ struct Gemm64Args {
   double* C; int64_t ldc; int64_t sC;
   int batch;
   int ksplit, kchunk;   // split-K (set by launch_gemm64_splitk)
+  const double* B64;    // float64 B (with a float64 A) in place of B
+  int lower;            // only tiles with some col <= row (the rest of C untouched)
 };
 hipError_t launch_gemm64(int epi, bool a_is_f64, const Gemm64Args& g, hipStream_t st);
 // A float64, split K into `splits` chunks through `part` (splits * M * N doubles).
@@ -104,6 +106,9 @@ hipError_t launch_anchor(const float* R, const float* W, const float* gamma, con
 // Trace / state bookkeeping.
 hipError_t launch_record(const float* src, int64_t m, float* dst, int64_t ld, int64_t col, hipStream_t st);
 hipError_t launch_copy_rows_f(const float* src, float* dst, int64_t count, hipStream_t st);
+hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t count, hipStream_t st);
+// f[i] = 1/2 sum_l U[i][l]^2 (float64), U m x r.
+hipError_t launch_half_sumsq64(const double* U, int64_t m, int64_t r, double* f, hipStream_t st);
 
 // CD (scalar grids): one tile of kd columns starting at column j0.
 hipError_t launch_cd_scalar_tile(int64_t m, int64_t n, int64_t j0, int kd, const double* G, const double* Ht,
@@ -120,5 +125,27 @@ hipError_t launch_cd_lattice_block(int64_t m, int64_t n, int64_t b, int bl, int 
                                    double* Delta, int32_t* changes, float* part_s, int32_t* part_i, uint32_t* qf,
                                    hipStream_t st);
 int cd_lattice_slices(int Kpad);
+// The scoring pass alone (codeword slices x row groups -> part_s / part_i).
+hipError_t launch_cd_lattice_score(int64_t m, int bl, const uint32_t* tk, const CbTables& cb, const uint32_t* qf,
+                                   float* part_s, int32_t* part_i, hipStream_t st);
+
+// ------------------------------------------------ sequential greedy (G3) ----
+// Lam (n x n float64, lower) with H + delta I = Lam^T Lam from VS (n x r),
+// delta = damp * mean(diag H); tmp: chol_tmp_doubles(n) doubles.
+size_t chol_tmp_doubles(int64_t n);
+hipError_t launch_greedy_factor(const float* VS, int64_t n, int64_t r, double damp, double* Lam, double* tmp,
+                                hipStream_t st);
+// Transposed diagonal tiles of Lam (tile t at Rt + t kd kd, row stride = its width).
+hipError_t launch_greedy_rtiles(const double* Lam, int64_t n, int kd, double* Rt, hipStream_t st);
+hipError_t launch_greedy_scalar_tile(int64_t m, int64_t n, int64_t j0, int kw, double* P, const double* Rt,
+                                     const float* W, const CbTables& cb, const float* a, const float* o,
+                                     int32_t* codes, double* En, hipStream_t st);
+hipError_t launch_greedy_gdiag(const double* Lam, int64_t n, int64_t j0, int kw, double* Gt, hipStream_t st);
+hipError_t launch_greedy_query(int64_t m, int64_t n, int64_t j0, const double* P, const double* Lam, const float* W,
+                               const float* a, const float* o, uint32_t* qf, hipStream_t st);
+hipError_t launch_greedy_update(int64_t m, int64_t n, int64_t j0, int64_t b, int bl, int kw, double* P,
+                                const double* Lam, const double* Rt, const float* W, const CbTables& cb,
+                                const float* a, const float* o, const float* part_s, const int32_t* part_i,
+                                int32_t* codes, double* En, uint32_t* qf, hipStream_t st);
 
 }  // namespace mpq

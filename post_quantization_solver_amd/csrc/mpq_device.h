@@ -35,6 +35,11 @@ __device__ __forceinline__ void split3_bf16(float x, uint32_t& h, uint32_t& m, u
 
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return (lo16 & 0xffffu) | (hi16 << 16); }
 
+// A caller-supplied code used as a table index: codes outside [0, K) read
+// entry 0 instead (the kernels that read such codes make their rows NaN, so
+// nothing is decided from the stand-in).
+__device__ __forceinline__ int safe_code(int c, int K) { return (unsigned)c < (unsigned)K ? c : 0; }
+
 // Cross-lane helpers (full wave64).
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 __device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, 64); }

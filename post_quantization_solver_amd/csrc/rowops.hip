@@ -260,6 +260,62 @@ hipError_t launch_copy_rows_f(const float* src, float* dst, int64_t count, hipSt
   return hipGetLastError();
 }
 
+__global__ void copy_words_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst, int64_t count) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; k < count; k += stride) dst[k] = src[k];
+}
+
+hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t count, hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  int64_t blocks = (count + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(copy_words_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     reinterpret_cast<const uint32_t*>(src), reinterpret_cast<uint32_t*>(dst), count);
+  return hipGetLastError();
+}
+
+// f[i] = 1/2 sum_l U[i][l]^2 in float64 (one workgroup per row, fixed order):
+// the layer objective 1/2 ||T (w - x)||^2 from the rank-space residual.
+__global__ __launch_bounds__(ROW_THREADS) void half_sumsq64_kernel(const double* __restrict__ U, int64_t r,
+                                                                   double* __restrict__ f) {
+  __shared__ double sh[ROW_THREADS];
+  const int64_t i = blockIdx.x;
+  const int t = threadIdx.x;
+  double acc = 0.0;
+  for (int64_t l = t; l < r; l += ROW_THREADS) {
+    const double u = U[i * r + l];
+    acc = fma(u, u, acc);
+  }
+  sh[t] = acc;
+  __syncthreads();
+  for (int w = ROW_THREADS / 2; w > 0; w >>= 1) {
+    if (t < w) sh[t] += sh[t + w];
+    __syncthreads();
+  }
+  if (t == 0) f[i] = 0.5 * sh[0];
+}
+
+hipError_t launch_half_sumsq64(const double* U, int64_t m, int64_t r, double* f, hipStream_t st) {
+  if (m <= 0) return hipSuccess;
+  hipLaunchKernelGGL(half_sumsq64_kernel, dim3((unsigned)m), dim3(ROW_THREADS), 0, st, U, r, f);
+  return hipGetLastError();
+}
+
+__global__ void fill_f64_kernel(double* __restrict__ dst, int64_t count, double v) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; k < count; k += stride) dst[k] = v;
+}
+
+hipError_t launch_fill_f64(double* dst, int64_t count, double v, hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  int64_t blocks = (count + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_f64_kernel, dim3((unsigned)blocks), dim3(256), 0, st, dst, count, v);
+  return hipGetLastError();
+}
+
 __global__ void fill_i32_kernel(int32_t* __restrict__ dst, int64_t count, int32_t v) {
   int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t stride = (int64_t)gridDim.x * blockDim.x;

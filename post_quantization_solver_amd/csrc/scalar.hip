@@ -104,7 +104,7 @@ hipError_t launch_nearest_scalar(const float* R, int64_t m, int64_t n, const CbT
 // workgroup per row, fixed-order reduction).
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ codes, int64_t n, int d,
                                                      const float* __restrict__ e32, const float* __restrict__ a,
-                                                     const float* __restrict__ o, int gs, int G,
+                                                     const float* __restrict__ o, int gs, int G, int K,
                                                      const float* __restrict__ W,
                                                      float* __restrict__ X, float* __restrict__ D,
                                                      float* __restrict__ rowsq, double* __restrict__ D64) {
@@ -117,10 +117,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
     const int64_t ag = i * G + (int)j / gs;
     const float ai = a[ag], oi = o[ag];
     int64_t b = j / d;
-    int c = codes[i * B + b];
-    float x = fmaf(ai, e32[(int64_t)c * d + (j - b * d)], oi);
+    const int c = codes[i * B + b];
+    // a code outside [0, K) (caller input) gives a NaN weight
+    const float e = (unsigned)c < (unsigned)K ? e32[(int64_t)c * d + (j - b * d)] : __builtin_nanf("");
+    float x = fmaf(ai, e, oi);
     if (X) X[i * n + j] = x;
-    if (D64) D64[i * n + j] = (double)W[i * n + j] - ((double)ai * (double)e32[(int64_t)c * d + (j - b * d)] + (double)oi);
+    if (D64) D64[i * n + j] = (double)W[i * n + j] - ((double)ai * (double)e + (double)oi);
     if (D) {
       float dd = W[i * n + j] - x;
       D[i * n + j] = dd;
@@ -143,8 +145,8 @@ hipError_t launch_gather(const int32_t* codes, int64_t m, int64_t n, const CbTab
                          double* D64) {
   if (m <= 0) return hipSuccess;
   const float* tab = cb.d == 1 ? cb.levels : cb.e32;
-  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)m), dim3(256), 0, st, codes, n, cb.d, tab, a, o, cb.gs, cb.G, W, X, D,
-                     rowsq, D64);
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)m), dim3(256), 0, st, codes, n, cb.d, tab, a, o, cb.gs, cb.G, cb.K, W,
+                     X, D, rowsq, D64);
   return hipGetLastError();
 }
 

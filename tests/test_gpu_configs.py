@@ -143,3 +143,44 @@ def test_config_parity(name):
     assert report["cd_obj_rel"] < OBJ_RTOL
     for key, v in summ["trace_rel_max"].items():
         assert v < E2E_TRACE_TOL, ("end-to-end trace drift", key, v)
+
+
+GREEDY_SAMPLE = {"c2": (4, 8), "c4": (2, 4)}   # rows, blocks per row
+
+
+@pytest.mark.parametrize("name", list(GREEDY_SAMPLE))
+def test_config_greedy(name):
+    """The greedy comparator on the whole layer at full size; for sampled rows
+    and blocks, the GPU's code is the oracle's argmin of the greedy cost given
+    the GPU's own earlier codes (teacher-forced per block; a near-tie may pick
+    either codeword, so the chosen cost must be within 1e-6 of the minimum)."""
+    import torch
+    import post_quantization_solver_amd as mpq
+    L = S.make_config(name, device="cuda")
+    T = layer_tensors(L)
+    print(f"[greedy config] {name}: m={L.m} n={L.n} K={L.K} d={L.d}", flush=True)
+    codes = host(mpq.greedy(T["W"], T["s"], T["V"], L.E, T["a"], T["o"]))
+    torch.cuda.synchronize()
+    del T
+    torch.cuda.empty_cache()
+    nrow, nblk = GREEDY_SAMPLE[name]
+    rows = S.parity_rows(L.m, nrow)
+    B = L.n // L.d
+    blocks = sorted({B - 1, B - 2, B - 9, B - 64, B // 2, B // 4, 3, 0})[:max(nblk, 1) + 4]
+    H = O.greedy_hessian(L.s, L.V)
+    exact, worst = 0, 0.0
+    total = 0
+    for i in rows:
+        C = row_codebook(L, i)
+        x = O.decode(C, codes[i], L.d)
+        e = np.asarray(L.W[i], np.float64) - x
+        for b in blocks:
+            cost = O.greedy_block_costs(H, np.asarray(L.W[i], np.float64), e, C, L.d, b)
+            k = int(codes[i][b])
+            best = float(np.min(cost))
+            exact += int(k == int(np.argmin(cost)))
+            worst = max(worst, (cost[k] - best) / max(abs(best), 1e-300))
+            total += 1
+    print(f"  {name}: sampled blocks {total}, exact argmin {exact}, worst cost excess {worst:.2e}", flush=True)
+    assert worst < 1e-6
+    assert exact >= total - 1
