@@ -80,9 +80,22 @@ def rht_matrix(n: int, signs) -> np.ndarray:
 
 
 def rht_rows(A, signs) -> np.ndarray:
-    """Every row a of A mapped to U a."""
+    """Every row a of A mapped to U a.  Rows longer than 4096 use the Kronecker
+    form (Had_28 (x) Had_(2^k)) x = vec over (a, b) of Had_28 X Had_(2^k)^T,
+    X[a][b] = x[a 2^k + b], instead of forming U (the same product)."""
     A = np.asarray(A, np.float64)
-    return A @ rht_matrix(A.shape[1], signs).T
+    n = A.shape[1]
+    if n <= 4096:
+        return A @ rht_matrix(n, signs).T
+    Y = A * np.asarray(signs, np.float64)[None, :]
+    if n % 28 == 0 and (n // 28) & (n // 28 - 1) == 0:
+        P, S = paley2(13), hadamard(n // 28)
+        X = Y.reshape(-1, 28, n // 28)
+        out = np.einsum("ac,rcb->rab", P, X) @ S.T
+    else:
+        H = hadamard(n)
+        out = Y @ H.T
+    return out.reshape(A.shape) / np.sqrt(n)
 
 
 def gram(X) -> np.ndarray:

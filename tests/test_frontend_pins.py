@@ -84,6 +84,19 @@ def check_factor(n=24, N=60, r=24, seed=2):
         assert np.isclose(O.objective(w, x, s, V), 0.5 * np.sum((X @ (w - x)) ** 2), rtol=1e-10)
 
 
+def test_rht_kronecker_form_matches_matrix():
+    """The Kronecker evaluation used for long rows equals the dense U (n = 28 * 256 > 4096)."""
+    g = np.random.default_rng(5)
+    n = 28 * 256
+    signs = g.choice([-1.0, 1.0], size=n)
+    A = g.standard_normal((3, n))
+    dense = A @ F.rht_matrix(n, signs).T
+    assert np.allclose(F.rht_rows(A, signs), dense, atol=1e-10)
+    B = g.standard_normal((2, 8192))
+    s2 = g.choice([-1.0, 1.0], size=8192)
+    assert np.allclose(F.rht_rows(B, s2), B @ F.rht_matrix(8192, s2).T, atol=1e-10)
+
+
 def test_factor():
     check_factor()
     check_factor(r=10)
