@@ -55,6 +55,7 @@ extern "C" {
                                     column groups with d = 8 or the anchored prior */
 #define MPQ_EWORKSPACE      -5   /* workspace NULL, misaligned or smaller than required */
 #define MPQ_EHIP            -6   /* a HIP runtime call failed */
+#define MPQ_ESOLVER         -7   /* mpq_factor: rocSOLVER not loadable, or its eigensolver failed */
 
 /* Optional controls (pass NULL for defaults; zero-initialise unused fields). */
 typedef struct {
@@ -221,6 +222,49 @@ int mpq_objective(const float* W, int64_t m, int64_t n, const float* s, const fl
                   const float* cb, int64_t K, int64_t d, const float* row_scale, const float* row_offset,
                   const mpq_options* opt, const int32_t* codes, double* objective, void* workspace,
                   size_t ws_bytes, void* stream);
+
+/*
+ * Front end: calibration activations -> the solver's (s, V), and the random
+ * Hadamard transform (RHT) used as incoherence processing.  Passages: the
+ * papernotes.org MPQ summary ("Overall framework": the objective
+ * 1/2 (w - w_hat)^T H (w - w_hat) with the calibration Gram matrix, solved in
+ * the basis of its factorisation; the hyper-parameter paragraph: AWQ + RHT for
+ * scalar grids, RHT for the lattice) and the ai.info summary's main findings
+ * (conjugating H by an RHT keeps its eigenvalues).  The pages print no RHT
+ * construction (reading: Sylvester for n = 2^k, Paley type II order 28 (x)
+ * Sylvester for n = 28 * 2^k; signs are the caller's random +-1).
+ */
+
+/* Bytes of workspace mpq_gram needs for row length n (0 if n is out of range). */
+size_t mpq_gram_workspace_bytes(int64_t n);
+
+/* H = X^T X: X device float32 N x n (row-major, tokens by features), H device
+ * float64 n x n (full symmetric, overwritten).  Products are exact in float64
+ * and summed in float64 on the fp64 matrix cores, tokens in chunks of 4096.
+ * 1 <= n <= 65536, N >= 0 (N = 0 gives H = 0). */
+int mpq_gram(const float* X, int64_t N, int64_t n, double* H, void* workspace, size_t ws_bytes, void* stream);
+
+/* In place, every row a of A (device float32, rows x n) -> Had_n (signs * a) /
+ * sqrt(n) (signs: device float32, n entries of +-1).  Apply it to W's rows
+ * and to the activations' rows alike: W X^T is unchanged and H becomes
+ * U H U^T.  n = 2^k or 28 * 2^k, n <= 16384 (else MPQ_EUNSUPPORTED). */
+int mpq_rht(float* A, int64_t rows, int64_t n, const float* signs, void* stream);
+
+/* Bytes of workspace mpq_factor needs (0 if n is out of range or rocSOLVER
+ * cannot be loaded). */
+size_t mpq_factor_workspace_bytes(int64_t n);
+
+/* The r largest eigenpairs of the symmetric H (device float64 n x n,
+ * overwritten): s[l] = sqrt(max(lambda_l, 0)) in descending order (device
+ * float32, r) and V (device float32 n x r, unit eigenvectors in its columns;
+ * each column's sign is arbitrary -- the solver does not depend on it).
+ * rocSOLVER's divide-and-conquer eigensolver, loaded at the first call; its
+ * scratch comes from the workspace (the rocBLAS handle the call creates and
+ * destroys may hold small buffers of its own: the one exception to the
+ * no-allocation rule).  Waits for the stream (to read the solver's status).
+ * 1 <= r <= n <= 65536. */
+int mpq_factor(double* H, int64_t n, int64_t r, float* s, float* V, void* workspace, size_t ws_bytes,
+               void* stream);
 
 #ifdef __cplusplus
 }

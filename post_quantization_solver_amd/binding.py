@@ -18,12 +18,13 @@ LIB_PATH = os.path.join(HERE, "libmpq.so")
 
 STATUS = {
     0: "MPQ_OK", -1: "MPQ_ENULL", -2: "MPQ_ESHAPE", -3: "MPQ_EPARAM",
-    -4: "MPQ_EUNSUPPORTED", -5: "MPQ_EWORKSPACE", -6: "MPQ_EHIP",
+    -4: "MPQ_EUNSUPPORTED", -5: "MPQ_EWORKSPACE", -6: "MPQ_EHIP", -7: "MPQ_ESOLVER",
 }
 F_FIXED_BETA = 1
 
 EXPORTS = ("mpq_workspace_bytes", "mpq_strerror", "mpq_quantize_layer", "mpq_prologue", "mpq_denoise",
-           "mpq_vamp_step", "mpq_map", "mpq_cd", "mpq_objective", "mpq_greedy", "mpq_greedy_workspace_bytes")
+           "mpq_vamp_step", "mpq_map", "mpq_cd", "mpq_objective", "mpq_greedy", "mpq_greedy_workspace_bytes",
+           "mpq_gram_workspace_bytes", "mpq_gram", "mpq_rht", "mpq_factor_workspace_bytes", "mpq_factor")
 
 
 class MPQError(RuntimeError):
@@ -93,6 +94,13 @@ def load_library(path: str = LIB_PATH):
     lib.mpq_greedy.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, OPT, P, P, SZ, P]
     lib.mpq_greedy_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
     lib.mpq_greedy_workspace_bytes.restype = SZ
+    lib.mpq_gram_workspace_bytes.argtypes = [I64]
+    lib.mpq_gram_workspace_bytes.restype = SZ
+    lib.mpq_gram.argtypes = [P, I64, I64, P, P, SZ, P]
+    lib.mpq_rht.argtypes = [P, I64, I64, P, P]
+    lib.mpq_factor_workspace_bytes.argtypes = [I64]
+    lib.mpq_factor_workspace_bytes.restype = SZ
+    lib.mpq_factor.argtypes = [P, I64, I64, P, P, P, SZ, P]
     for name in EXPORTS[2:]:
         if name.endswith("_bytes"):
             continue
@@ -393,3 +401,61 @@ def greedy(W, s, V, cb, row_scale, row_offset, workspace=None, group=None, profi
                                    workspace.numel(), _stream())
     _check(rc, "mpq_greedy")
     return codes
+
+
+# ---------------------------------------------------------------- front end
+
+def gram(X, workspace=None):
+    """H = X^T X (float64 n x n) of the activations X (device float32 N x n)."""
+    import torch
+    _dev(X, torch.float32, "X")
+    N, n = X.shape
+    H = torch.empty((n, n), dtype=torch.float64, device=X.device)
+    if workspace is None:
+        nb = int(load_library().mpq_gram_workspace_bytes(n))
+        if nb == 0:
+            raise MPQError(-2, "mpq_gram_workspace_bytes")
+        workspace = torch.empty(nb, dtype=torch.uint8, device=X.device)
+    _check(load_library().mpq_gram(_ptr(X), N, n, _ptr(H), _ptr(workspace), workspace.numel(), _stream()),
+           "mpq_gram")
+    return H
+
+
+def rht(A, signs):
+    """Random Hadamard transform of every row of A (device float32, in place); returns A."""
+    import torch
+    _dev(A, torch.float32, "A")
+    rows, n = A.shape
+    _dev(signs, torch.float32, "signs", (n,))
+    _check(load_library().mpq_rht(_ptr(A), rows, n, _ptr(signs), _stream()), "mpq_rht")
+    return A
+
+
+def factor(H, r, workspace=None):
+    """(s, V) of the r largest eigenpairs of H (device float64 n x n, overwritten)."""
+    import torch
+    _dev(H, torch.float64, "H")
+    n = H.shape[0]
+    s = torch.empty(r, dtype=torch.float32, device=H.device)
+    V = torch.empty((n, r), dtype=torch.float32, device=H.device)
+    if workspace is None:
+        nb = int(load_library().mpq_factor_workspace_bytes(n))
+        if nb == 0:
+            raise MPQError(-7, "mpq_factor_workspace_bytes")
+        workspace = torch.empty(nb, dtype=torch.uint8, device=H.device)
+    _check(load_library().mpq_factor(_ptr(H), n, int(r), _ptr(s), _ptr(V), _ptr(workspace), workspace.numel(),
+                                     _stream()), "mpq_factor")
+    return s, V
+
+
+def frontend(X, W, r=None, signs=None):
+    """Activations X (N x n) and weights W (m x n) -> (W', s, V) for the solver:
+    with `signs` both are rotated by the RHT first (copies; the inputs are
+    left unchanged), then H = X'^T X' and its r largest modes (default r = n)."""
+    n = X.shape[1]
+    if signs is not None:
+        X = rht(X.clone(), signs)
+        W = rht(W.clone(), signs)
+    H = gram(X)
+    s, V = factor(H, n if r is None else r)
+    return W, s, V

@@ -27,7 +27,6 @@ hipError_t launch_nearest_lattice(const float*, int64_t, int64_t, const CbTables
 hipError_t launch_beta_lin(int64_t, const float*, const float*, float*, float*, hipStream_t);
 hipError_t launch_fill_i32(int32_t*, int64_t, int32_t, hipStream_t);
 hipError_t launch_record_i32(const int32_t* src, int64_t m, int32_t* dst, int64_t ld, int64_t col, hipStream_t st);
-hipError_t launch_fill_f64(double* dst, int64_t count, double v, hipStream_t st);
 }  // namespace mpq
 
 using namespace mpq;
@@ -806,6 +805,7 @@ const char* mpq_strerror(int status) {
              "d = 1 and the uniform prior)";
     case MPQ_EWORKSPACE: return "workspace missing, misaligned or too small";
     case MPQ_EHIP: return "HIP runtime error";
+    case MPQ_ESOLVER: return "the eigensolver (rocSOLVER) could not be loaded or did not converge";
   }
   return "unknown status";
 }
@@ -954,6 +954,73 @@ int mpq_objective(const float* W, int64_t m, int64_t n, const float* s, const fl
   if ((rc = upload_codebook(c, cb))) return rc;
   if ((rc = prepare_factors(c, V, s))) return rc;
   return finish(c, run_objective(c, W, row_scale, row_offset, codes, objective));
+}
+
+// ------------------------------------------------------------ front end
+
+constexpr int64_t FRONT_MAX_N = 65536;
+
+size_t mpq_gram_workspace_bytes(int64_t n) {
+  if (n < 1 || n > FRONT_MAX_N) return 0;
+  return std::max(gram_tmp_bytes(n), (size_t)ALIGN);
+}
+
+int mpq_gram(const float* X, int64_t N, int64_t n, double* H, void* workspace, size_t ws_bytes, void* stream) {
+  if (n < 1 || n > FRONT_MAX_N || N < 0) return MPQ_ESHAPE;
+  if ((N > 0 && !X) || !H) return MPQ_ENULL;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % ALIGN) != 0 || ws_bytes < mpq_gram_workspace_bytes(n))
+    return MPQ_EWORKSPACE;
+  MPQ_TRY(launch_gram(X, N, n, H, static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
+  return MPQ_OK;
+}
+
+int mpq_rht(float* A, int64_t rows, int64_t n, const float* signs, void* stream) {
+  int p28 = 0;
+  if (rows < 0) return MPQ_ESHAPE;
+  if (rht_shape(n, &p28) < 0) return MPQ_EUNSUPPORTED;
+  if (rows == 0) return MPQ_OK;
+  if (!A || !signs) return MPQ_ENULL;
+  MPQ_TRY(launch_rht(A, rows, n, signs, static_cast<hipStream_t>(stream)));
+  return MPQ_OK;
+}
+
+namespace {
+struct FactorLayout {
+  size_t d, e, info, scratch, total, scratch_bytes;
+};
+bool factor_layout(int64_t n, FactorLayout& F) {
+  const int64_t sb = factor_solver_bytes(n);
+  if (sb < 0) return false;
+  F.d = 0;
+  F.e = round_up((size_t)n * sizeof(double));
+  F.info = F.e + round_up((size_t)n * sizeof(double));
+  F.scratch = F.info + ALIGN;
+  F.scratch_bytes = (size_t)sb;
+  F.total = F.scratch + round_up(std::max<size_t>((size_t)sb, ALIGN));
+  return true;
+}
+}  // namespace
+
+size_t mpq_factor_workspace_bytes(int64_t n) {
+  if (n < 1 || n > FRONT_MAX_N) return 0;
+  FactorLayout F;
+  return factor_layout(n, F) ? F.total : 0;
+}
+
+int mpq_factor(double* H, int64_t n, int64_t r, float* s, float* V, void* workspace, size_t ws_bytes,
+               void* stream) {
+  if (n < 1 || n > FRONT_MAX_N || r < 1 || r > n) return MPQ_ESHAPE;
+  if (!H || !s || !V) return MPQ_ENULL;
+  FactorLayout F;
+  if (!factor_layout(n, F)) return MPQ_ESOLVER;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % ALIGN) != 0 || ws_bytes < F.total)
+    return MPQ_EWORKSPACE;
+  char* w = static_cast<char*>(workspace);
+  const int rc = run_factor(H, n, r, s, V, reinterpret_cast<double*>(w + F.d), reinterpret_cast<double*>(w + F.e),
+                            reinterpret_cast<int*>(w + F.info), w + F.scratch, F.scratch_bytes,
+                            static_cast<hipStream_t>(stream));
+  if (rc == -7 || rc == -8) return MPQ_ESOLVER;
+  return rc == 0 ? MPQ_OK : MPQ_EHIP;
 }
 
 }  // extern "C"

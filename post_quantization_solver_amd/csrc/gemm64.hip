@@ -209,6 +209,7 @@ hipError_t launch_gemm64(int epi, bool a_is_f64, const Gemm64Args& g, hipStream_
     if (epi == EPI_SUB_INPLACE) return launch64<double, EPI_SUB_INPLACE>(g, st);
   } else {
     if (epi == EPI_STORE) return launch64<float, EPI_STORE>(g, st);
+    if (epi == EPI_SUB_INPLACE) return launch64<float, EPI_SUB_INPLACE>(g, st);
   }
   return hipErrorInvalidValue;
 }

@@ -148,4 +148,14 @@ hipError_t launch_greedy_update(int64_t m, int64_t n, int64_t j0, int64_t b, int
                                 const float* a, const float* o, const float* part_s, const int32_t* part_i,
                                 int32_t* codes, double* En, uint32_t* qf, hipStream_t st);
 
+// ------------------------------------------------------------ front end ----
+size_t gram_tmp_bytes(int64_t n);
+hipError_t launch_gram(const float* X, int64_t N, int64_t n, double* H, float* tmp, hipStream_t st);
+int rht_shape(int64_t n, int* p28);
+hipError_t launch_rht(float* A, int64_t rows, int64_t n, const float* signs, hipStream_t st);
+int64_t factor_solver_bytes(int64_t n);
+int run_factor(double* H, int64_t n, int64_t r, float* s, float* V, double* D, double* E, int* info, void* scratch,
+               size_t scratch_bytes, hipStream_t st);
+hipError_t launch_fill_f64(double* dst, int64_t count, double v, hipStream_t st);
+
 }  // namespace mpq

@@ -90,6 +90,20 @@ def test_group_option_validation(lib):
     assert call_layer(lib, opt=Opt(group=0, anchor_tau=0.2), ws_bytes=1024) == -5
 
 
+def test_frontend_argument_validation(lib):
+    assert lib.mpq_rht(FAKE, 4, 12, FAKE, None) == -4          # n neither 2^k nor 28 * 2^k
+    assert lib.mpq_rht(FAKE, 4, 32768, FAKE, None) == -4       # longer than the LDS row
+    assert lib.mpq_rht(FAKE, -1, 16, FAKE, None) == -2
+    assert lib.mpq_rht(FAKE, 0, 16, FAKE, None) == 0
+    assert lib.mpq_rht(None, 2, 16, FAKE, None) == -1
+    assert lib.mpq_gram(FAKE, 10, 0, FAKE, FAKE, 1 << 30, None) == -2
+    assert lib.mpq_gram(FAKE, 10, 16, None, FAKE, 1 << 30, None) == -1
+    assert lib.mpq_gram(FAKE, 10, 16, FAKE, FAKE, 16, None) == -5
+    assert lib.mpq_factor(FAKE, 16, 17, FAKE, FAKE, FAKE, 1 << 30, None) == -2
+    assert lib.mpq_factor(None, 16, 4, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert lib.mpq_gram_workspace_bytes(0) == 0 and lib.mpq_gram_workspace_bytes(256) > 0
+
+
 def test_options_layout_matches_header(tmp_path):
     """The ctypes mirror of mpq_options has the header's field offsets and size
     (compiled with the host C compiler)."""
