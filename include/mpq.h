@@ -96,6 +96,7 @@ typedef struct {
 
 #define MPQ_F_FIXED_BETA 1u
 #define MPQ_F_PROFILE    2u
+#define MPQ_F_NO_E8DP    4u   /* d = 8: always use the codebook-scan denoiser (for A/B checks) */
 
 /* Profiling categories (kernel groups). */
 #define MPQ_PROF_PROLOGUE  0  /* rank-space projection, RTN, beta^0 */
@@ -114,8 +115,24 @@ typedef struct {
 /* Bytes of device workspace needed by every entry point for these shapes. */
 size_t mpq_workspace_bytes(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d);
 
+/* How the library treats a base codebook (host pointer, K x d):
+ * MPQ_CB_E8_PREFIX when d = 8 and cb is exactly the first K points of the E8
+ * lattice in ascending (||x||^2, x_1, .., x_8) order -- the blockwise denoiser
+ * then evaluates the posterior by a forward-backward pass over the 8
+ * coordinates (the Gaussian factorises over coordinates and the codebook is
+ * a finite automaton over them), 13 exponentials per coordinate instead of K
+ * per block; MPQ_CB_GENERIC otherwise (scan of the whole codebook on the
+ * matrix cores); a negative MPQ_E* code for invalid arguments. */
+#define MPQ_CB_GENERIC   0
+#define MPQ_CB_E8_PREFIX 1
+int mpq_codebook_kind(const float* cb, int64_t K, int64_t d);
+
 /* Human-readable text for a status code (static storage). */
 const char* mpq_strerror(int status);
+
+/* Name of the HIP error behind the calling thread's last MPQ_EHIP (static
+ * storage; "hipSuccess" if there was none). */
+const char* mpq_hip_error_name(void);
 
 /*
  * Full layer solve: prologue, T_vamp VAMP iterations, marginal MAP, n_cd CD

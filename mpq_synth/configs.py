@@ -104,10 +104,10 @@ def draw_weights(rng, m, n, dist, outlier_frac=0.0, outlier_factor=8.0, outlier_
 
 def make_layer(name, m, n, *, seed, dist="normal", d=1, bits=3, K=None, power=0.5,
                lead=0, r=None, T_vamp=16, n_cd=3, damping=0.5, outlier_frac=0.0,
-               device=None, W=None, s=None, V=None, group=0):
+               device=None, W=None, s=None, V=None, group=0, E=None):
     """General seeded layer.  d = 1 -> Min-Max scalar grid with 2^bits levels
     (per row, or per group of `group` columns); d = 8 -> the first K points of
-    E8 (K defaults to 65536)."""
+    E8 (K defaults to 65536), or the given K x 8 codebook E."""
     ss = np.random.SeedSequence(seed)
     w_ss, v_ss, o_ss = ss.spawn(3)
     r = n if r is None else r
@@ -121,7 +121,7 @@ def make_layer(name, m, n, *, seed, dist="normal", d=1, bits=3, K=None, power=0.
     if d == 1:
         E, a, o = scalar_grid(W, bits, group)
     elif d == 8:
-        E = e8_codebook(65536 if K is None else K)
+        E = e8_codebook(65536 if K is None else K) if E is None else np.ascontiguousarray(E, dtype=np.float32)
         raw_rms = float(np.sqrt((E.astype(np.float64) ** 2).mean()))
         a, o = lattice_row_scale(W, raw_rms)
     else:

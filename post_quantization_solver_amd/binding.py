@@ -24,16 +24,24 @@ F_FIXED_BETA = 1
 
 EXPORTS = ("mpq_workspace_bytes", "mpq_strerror", "mpq_quantize_layer", "mpq_prologue", "mpq_denoise",
            "mpq_vamp_step", "mpq_map", "mpq_cd", "mpq_objective", "mpq_greedy", "mpq_greedy_workspace_bytes",
-           "mpq_gram_workspace_bytes", "mpq_gram", "mpq_rht", "mpq_factor_workspace_bytes", "mpq_factor")
+           "mpq_gram_workspace_bytes", "mpq_gram", "mpq_rht", "mpq_factor_workspace_bytes", "mpq_factor",
+           "mpq_codebook_kind", "mpq_hip_error_name")
 
 
 class MPQError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
-        super().__init__(f"{what} failed: {STATUS.get(status, status)} ({_strerror(status)})")
+        detail = _strerror(status)
+        if status == -6:
+            try:
+                detail += ": " + load_library().mpq_hip_error_name().decode()
+            except Exception:  # noqa: BLE001 - only used to decorate an error message
+                pass
+        super().__init__(f"{what} failed: {STATUS.get(status, status)} ({detail})")
 
 
 F_PROFILE = 2
+F_NO_E8DP = 4
 PROF_NAMES = ("prologue", "denoise", "extrinsic", "linear1", "beta", "linear2", "map", "cd_gemm", "cd_search",
               "other", "denoise_exact")
 PROF_COUNT = len(PROF_NAMES)
@@ -71,6 +79,16 @@ def load_library(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m post_quantization_solver_amd.build`")
+    # The library registers its GPU code when it is loaded; with a GPU present,
+    # initialise the runtime first so that registration does not happen inside
+    # the loader (where the runtime's own start-up fails and every later launch
+    # from the library reports hipErrorNoDevice).
+    try:
+        import torch
+        if torch.cuda.is_available():
+            torch.cuda.init()
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
@@ -101,8 +119,11 @@ def load_library(path: str = LIB_PATH):
     lib.mpq_factor_workspace_bytes.argtypes = [I64]
     lib.mpq_factor_workspace_bytes.restype = SZ
     lib.mpq_factor.argtypes = [P, I64, I64, P, P, P, SZ, P]
+    lib.mpq_codebook_kind.argtypes = [P, I64, I64]
+    lib.mpq_hip_error_name.argtypes = []
+    lib.mpq_hip_error_name.restype = ctypes.c_char_p
     for name in EXPORTS[2:]:
-        if name.endswith("_bytes"):
+        if name.endswith("_bytes") or name == "mpq_hip_error_name":
             continue
         getattr(lib, name).restype = I
     _lib = lib
@@ -114,6 +135,16 @@ def _strerror(status: int) -> str:
         return load_library().mpq_strerror(int(status)).decode()
     except Exception:  # noqa: BLE001 - only used to decorate an error message
         return "?"
+
+
+def codebook_kind(cb) -> str:
+    """'e8_prefix' if the codebook is the first K points of E8 in (norm, lex)
+    order (the forward-backward denoiser applies), else 'generic'."""
+    E = _host_codebook(cb)
+    rc = load_library().mpq_codebook_kind(E.ctypes.data_as(ctypes.c_void_p), E.shape[0], E.shape[1])
+    if rc < 0:
+        raise MPQError(rc, "mpq_codebook_kind")
+    return "e8_prefix" if rc == 1 else "generic"
 
 
 def workspace_bytes(m, n, r, K, d) -> int:
@@ -167,8 +198,9 @@ def _workspace(m, n, r, K, d, device):
 
 
 def _opts(beta0=None, fixed_beta=False, profile=None, anchor_tau=None, anchor_w=None, group=None, map_codes=None,
-          objective=None):
-    flags = (F_FIXED_BETA if fixed_beta else 0) | (F_PROFILE if profile is not None else 0)
+          objective=None, scan_denoiser=False):
+    flags = ((F_FIXED_BETA if fixed_beta else 0) | (F_PROFILE if profile is not None else 0) |
+             (F_NO_E8DP if scan_denoiser else 0))
     o = Options(float(beta0) if beta0 else 0.0, flags, profile.mask if profile is not None else 0,
                 profile.ms if profile is not None else None, profile.launches if profile is not None else None,
                 float(anchor_tau) if anchor_tau else 0.0, anchor_w.data_ptr() if anchor_w is not None else None,
@@ -197,7 +229,7 @@ def _check(rc, what):
 
 def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, damping=0.5, beta0=None,
                    fixed_beta=False, workspace=None, traces=True, profile=None, outputs=None, anchor_tau=None,
-                   group=None, diagnostics=False):
+                   group=None, diagnostics=False, scan_denoiser=False):
     """Full MPQ solve of one layer (mpq_quantize_layer).
 
     Returns dict(codes, beta_tr, gamma1_tr, gamma2_tr, cd_changes) of device
@@ -230,7 +262,7 @@ def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, dampin
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
     mc = torch.empty((m, n // d), dtype=torch.int32, device=dev) if diagnostics else None
     obj = torch.empty(m, dtype=torch.float64, device=dev) if diagnostics else None
-    op, _keep = _opts(beta0, fixed_beta, profile, anchor_tau, None, group, mc, obj)
+    op, _keep = _opts(beta0, fixed_beta, profile, anchor_tau, None, group, mc, obj, scan_denoiser)
     rc = load_library().mpq_quantize_layer(
         _ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d, _ptr(row_scale),
         _ptr(row_offset), int(T_vamp), int(n_cd), float(damping), op, _ptr(codes), _ptr(bt), _ptr(g1), _ptr(g2),
@@ -263,8 +295,10 @@ def prologue(W, s, V, cb, row_scale, row_offset, beta0=None, workspace=None, gro
     return dict(ytil=ytil, rtn_codes=rtn, gamma1=gamma1, beta=beta)
 
 
-def denoise(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=None, W=None, group=None):
-    """Blockwise denoiser (mpq_denoise): (xhat1, per-block variance trace)."""
+def denoise(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=None, W=None, group=None,
+            scan_denoiser=False):
+    """Blockwise denoiser (mpq_denoise): (xhat1, per-block variance trace).
+    `scan_denoiser` forces the codebook-scan kernel for E8-prefix codebooks."""
     import torch
     m, n = R1.shape
     E = _host_codebook(cb)
@@ -278,7 +312,7 @@ def denoise(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=No
     xhat = torch.empty_like(R1)
     vtr = torch.empty((m, n // d), dtype=torch.float32, device=dev)
     ws = workspace if workspace is not None else _workspace(m, n, n, K, d, dev)
-    op, _keep = _opts(anchor_tau=anchor_tau, anchor_w=W, group=group)
+    op, _keep = _opts(anchor_tau=anchor_tau, anchor_w=W, group=group, scan_denoiser=scan_denoiser)
     rc = load_library().mpq_denoise(_ptr(R1), _ptr(gamma1), m, n, E.ctypes.data_as(ctypes.c_void_p), K, d,
                                     _ptr(row_scale), _ptr(row_offset), op, _ptr(xhat), _ptr(vtr), _ptr(ws),
                                     ws.numel(), _stream())

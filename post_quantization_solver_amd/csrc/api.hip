@@ -11,6 +11,7 @@
 
 #include "../../include/mpq.h"
 #include "internal.h"
+#include "e8dp.h"
 
 namespace mpq {
 // launchers defined in the kernel files
@@ -26,6 +27,12 @@ hipError_t launch_nearest_lattice(const float*, int64_t, int64_t, const CbTables
                                   int32_t*, hipStream_t);
 hipError_t launch_beta_lin(int64_t, const float*, const float*, float*, float*, hipStream_t);
 hipError_t launch_fill_i32(int32_t*, int64_t, int32_t, hipStream_t);
+bool e8_prefix_detect(const float* cb, int64_t K, E8Prefix& P);
+size_t e8_table_bytes();
+void e8_build_tables(const E8Prefix& P, int8_t* out);
+hipError_t launch_denoise_e8dp(const float* R1, const float* gamma1, int64_t m, int64_t n, const E8Prefix& P,
+                               const int8_t* tables, const float* a, const float* o, float* xhat, float* vblk,
+                               int32_t* flag, hipStream_t st);
 hipError_t launch_record_i32(const int32_t* src, int64_t m, int32_t* dst, int64_t ld, int64_t col, hipStream_t st);
 }  // namespace mpq
 
@@ -41,10 +48,16 @@ int cd_groups(int64_t m) { return m >= 1024 ? CD_GROUPS_MAX : 1; }
 constexpr int LAT_CHUNK = 128;   // lattice codebook padding granularity
 constexpr size_t ALIGN = 256;
 
+// The HIP error behind the last MPQ_EHIP of this thread (mpq_hip_error_name).
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
 #define MPQ_TRY(x)                       \
   do {                                   \
     hipError_t e_ = (x);                 \
-    if (e_ != hipSuccess) return MPQ_EHIP; \
+    if (e_ != hipSuccess) {              \
+      g_last_hip_error = e_;             \
+      return MPQ_EHIP;                   \
+    }                                    \
   } while (0)
 
 // Run a launch expression; with profiling on for `cat`, bracket it with
@@ -77,7 +90,7 @@ struct Layout {
 enum Region {
   R_VS, R_VST, R_YTIL, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI,
   R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_SPLIT, R_TKEY, R_QF, R_VSP, R_VSTP, R_R2P, R_ZP, R_ANCH,
-  R_LAM, R_CTMP, R_GDIAG, R_COUNT
+  R_LAM, R_CTMP, R_GDIAG, R_E8T, R_COUNT
 };
 
 static_assert(R_COUNT <= (int)(sizeof(Layout::off) / sizeof(size_t)), "Layout::off holds every region");
@@ -134,6 +147,7 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, bool g
   sz[R_LAM] = greedy ? (size_t)n * n * f64 : 0;
   sz[R_CTMP] = greedy ? chol_tmp_doubles(n) * f64 : 0;
   sz[R_GDIAG] = greedy ? (size_t)KD * KD * f64 : 0;
+  sz[R_E8T] = d == 8 ? e8_table_bytes() : 0;   // automaton tables of the E8 forward-backward denoiser
   size_t o = 0;
   for (int k = 0; k < R_COUNT; ++k) {
     L.off[k] = o;
@@ -184,6 +198,11 @@ struct Ctx {
   float anchor_tau = 0.f;
   const float* anchor_w = nullptr;
   bool anchored() const { return anchor_tau > 0.f; }
+  // d = 8 codebooks that are the first K points of E8 in (norm, lex) order:
+  // the denoiser runs the forward-backward pass over coordinates
+  bool e8dp = false;
+  bool e8dp_allowed = true;
+  E8Prefix e8p;
 };
 
 bool bf16_exact(float x) {
@@ -265,6 +284,7 @@ int upload_codebook(Ctx& c, const float* cb) {
   c.cb.e32 = c.p(R_E32);
   c.cb.qk_keys = reinterpret_cast<const uint32_t*>(c.p(R_QK));
   c.cb.pv_ops = reinterpret_cast<const uint32_t*>(c.p(R_PV));
+  c.e8dp = L.d == 8 && c.e8dp_allowed && e8_prefix_detect(cb, L.K, c.e8p);
   if (L.d == 1) {
     std::vector<float> lv(64, 0.f);
     for (int64_t k = 0; k < L.K; ++k) lv[k] = cb[k];
@@ -332,6 +352,12 @@ int upload_codebook(Ctx& c, const float* cb) {
   MPQ_TRY(hipMemcpyAsync(c.p(R_E32), e32.data(), e32.size() * sizeof(float), hipMemcpyHostToDevice, c.st));
   MPQ_TRY(hipMemcpyAsync(c.p(R_QK), qk.data(), qk.size() * sizeof(uint16_t), hipMemcpyHostToDevice, c.st));
   MPQ_TRY(hipMemcpyAsync(c.p(R_PV), pv.data(), pv.size() * sizeof(uint16_t), hipMemcpyHostToDevice, c.st));
+  std::vector<int8_t> e8t;
+  if (c.e8dp) {
+    e8t.resize(e8_table_bytes());
+    e8_build_tables(c.e8p, e8t.data());
+    MPQ_TRY(hipMemcpyAsync(c.p(R_E8T), e8t.data(), e8t.size(), hipMemcpyHostToDevice, c.st));
+  }
   MPQ_TRY(hipStreamSynchronize(c.st));
   return MPQ_OK;
 }
@@ -357,8 +383,14 @@ int denoise(Ctx& c, const float* R1, const float* gamma1, const float* a, const 
     TIMED(c, MPQ_PROF_DENOISE, launch_denoise_scalar(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.st));
     return MPQ_OK;
   }
-  TIMED(c, MPQ_PROF_DENOISE,
-        launch_denoise_lattice(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.pi(R_FLAG), c.st));
+  if (c.e8dp) {
+    TIMED(c, MPQ_PROF_DENOISE,
+          launch_denoise_e8dp(R1, gamma1, c.L.m, c.L.n, c.e8p, reinterpret_cast<const int8_t*>(c.p(R_E8T)), a, o,
+                              xhat, vblk, c.pi(R_FLAG), c.st));
+  } else {
+    TIMED(c, MPQ_PROF_DENOISE,
+          launch_denoise_lattice(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.pi(R_FLAG), c.st));
+  }
   TIMED(c, MPQ_PROF_DENOISE_EXACT,
         launch_denoise_lattice_exact(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.pi(R_FLAG), c.st));
   return MPQ_OK;
@@ -742,6 +774,7 @@ int begin(Ctx& c, int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, const f
     c.anchor_tau = opt->anchor_tau;
     c.anchor_w = opt->anchor_w;
   }
+  c.e8dp_allowed = !(opt && (opt->flags & MPQ_F_NO_E8DP));
   int rc = check_shapes(m, n, r, K, d);
   if (rc) return rc;
   if (!cb) return MPQ_ENULL;
@@ -793,6 +826,8 @@ size_t mpq_greedy_workspace_bytes(int64_t m, int64_t n, int64_t r, int64_t K, in
   if (check_shapes(m, n, r, K, d) != MPQ_OK) return 0;
   return make_layout(m, n, r, K, d, true).total;
 }
+
+const char* mpq_hip_error_name(void) { return hipGetErrorName(g_last_hip_error); }
 
 const char* mpq_strerror(int status) {
   switch (status) {
@@ -924,6 +959,14 @@ int mpq_cd(const float* W, int64_t m, int64_t n, const float* s, const float* V,
   if ((rc = upload_codebook(c, cb))) return rc;
   if ((rc = prepare_factors(c, V, s))) return rc;
   return finish(c, run_cd(c, W, row_scale, row_offset, n_cd, codes, cd_changes));
+}
+
+int mpq_codebook_kind(const float* cb, int64_t K, int64_t d) {
+  if (!cb) return MPQ_ENULL;
+  if (d != 1 && d != 8) return MPQ_EUNSUPPORTED;
+  if (K < 1 || K > (d == 1 ? 64 : 65536)) return MPQ_ESHAPE;
+  E8Prefix P;
+  return d == 8 && e8_prefix_detect(cb, K, P) ? MPQ_CB_E8_PREFIX : MPQ_CB_GENERIC;
 }
 
 int mpq_greedy(const float* W, int64_t m, int64_t n, const float* s, const float* V, int64_t r, const float* cb,

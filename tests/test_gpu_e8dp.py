@@ -1,0 +1,108 @@
+"""The forward-backward E8 denoiser (codebooks that are the first K points of
+E8 in (norm, lexicographic) order) against the oracle's scan of the whole
+codebook, and against the library's own codebook-scan kernel; codebooks that
+are not such a prefix keep the scan kernel.  Tolerances as for every
+denoiser test: x_hat and the per-row variance sum 1e-4 relative."""
+import numpy as np
+import pytest
+
+import mpq_synth as S
+from oracle import mpq_oracle as O
+from parity_helpers import SOFT_RTOL, dev, host, rel_vec, rel_scalar
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_denoise(R1, g1, E, a, o):
+    xs, vs = [], []
+    for k in range(R1.shape[0]):
+        C = O.row_codewords(E, a[k], o[k])
+        x, v, _ = O.denoise(R1[k].astype(np.float64), float(g1[k]), C, 8)
+        xs.append(x)
+        vs.append(v)
+    return np.stack(xs), np.stack(vs)
+
+
+def compare(R1, g1, E, a, o, **kw):
+    import post_quantization_solver_amd as mpq
+    xh, vt = mpq.denoise(dev(R1), dev(g1), E, dev(a), dev(o), **kw)
+    xh, vt = host(xh), host(vt)
+    xr, vr = oracle_denoise(R1, g1, E, a, o)
+    wx = max(rel_vec(xh[k], xr[k]) for k in range(R1.shape[0]))
+    wv = max(rel_scalar(vt[k].astype(np.float64).sum(), vr[k].sum()) for k in range(R1.shape[0]))
+    return wx, wv, xh, vt
+
+
+@pytest.mark.parametrize("K", [1, 240, 1000, 2401, 65536])
+@pytest.mark.parametrize("kappa", [0.05, 1.0, 30.0])
+def test_e8dp_denoiser(K, kappa):
+    import post_quantization_solver_amd as mpq
+    E = S.e8_codebook(K)
+    assert mpq.codebook_kind(E) == "e8_prefix"
+    g = np.random.default_rng(K + int(kappa * 100))
+    m, n = 6, 64
+    a = (0.3 + g.random(m)).astype(np.float32)
+    o = (0.1 * g.standard_normal(m)).astype(np.float32)
+    R1 = (g.standard_normal((m, n)) * 1.3 * a[:, None] + o[:, None]).astype(np.float32)
+    g1 = (kappa / a.astype(np.float64) ** 2).astype(np.float32)
+    wx, wv, xh, vt = compare(R1, g1, E, a, o)
+    print(f"[e8dp] K={K} kappa={kappa}: xhat {wx:.2e} sum v {wv:.2e}", flush=True)
+    assert wx < SOFT_RTOL and wv < SOFT_RTOL
+    # the codebook-scan kernel on the same inputs agrees too
+    wx2, wv2, xs, vs = compare(R1, g1, E, a, o, scan_denoiser=True)
+    assert wx2 < SOFT_RTOL and wv2 < SOFT_RTOL
+
+
+def test_e8dp_underflow_goes_to_exact_pass():
+    """Queries far outside the codebook with a sharp posterior: the normaliser
+    of the factorised pass underflows float64 and the exact pass takes over."""
+    E = S.e8_codebook(65536)
+    m, n = 2, 16
+    a = np.ones(m, np.float32)
+    o = np.zeros(m, np.float32)
+    R1 = np.zeros((m, n), np.float32)
+    R1[:, 0] = 10.0
+    R1[:, 9] = -9.0
+    g1 = np.full(m, 600.0, np.float32)
+    wx, wv, xh, vt = compare(R1, g1, E, a, o)
+    print(f"[e8dp underflow] xhat {wx:.2e} sum v {wv:.2e}", flush=True)
+    assert wx < SOFT_RTOL and wv < SOFT_RTOL
+
+
+def test_non_prefix_codebooks_use_the_scan():
+    import post_quantization_solver_amd as mpq
+    E = S.e8_codebook(1000)
+    shuffled = E[np.random.default_rng(3).permutation(1000)]
+    assert mpq.codebook_kind(shuffled) == "generic"
+    assert mpq.codebook_kind(np.delete(E, 10, axis=0)) == "generic"
+    g = np.random.default_rng(4)
+    m, n = 4, 64
+    a = np.full(m, 0.7, np.float32)
+    o = np.zeros(m, np.float32)
+    R1 = (g.standard_normal((m, n)) * 0.9).astype(np.float32)
+    g1 = np.full(m, 2.0, np.float32)
+    wx, wv, _, _ = compare(R1, g1, shuffled, a, o)
+    assert wx < SOFT_RTOL and wv < SOFT_RTOL
+
+
+def test_layer_with_and_without_e8dp():
+    """A whole lattice layer: the forward-backward path and the scan path both
+    match the oracle's codes (each teacher-forced stage is covered elsewhere)."""
+    import torch
+    import post_quantization_solver_amd as mpq
+    from oracle.pool import solve_rows
+    from parity_helpers import CODE_FRAC, layer_tensors, compare_layer
+    L = S.make_layer("e8dp_layer", 12, 128, seed=91, d=8, K=4096, power=0.6, T_vamp=6)
+    T = layer_tensors(L)
+    refs = solve_rows(L, np.arange(L.m))
+    for scan in (False, True):
+        out = mpq.quantize_layer(T["W"], T["s"], T["V"], L.E, T["a"], T["o"], T_vamp=L.T_vamp, n_cd=L.n_cd,
+                                 damping=L.damping, scan_denoiser=scan)
+        torch.cuda.synchronize()
+        gpu = {k: (host(v) if v is not None else None) for k, v in out.items()}
+        summ = compare_layer(L, np.arange(L.m), gpu, refs)
+        print(f"[e8dp layer] scan={scan}: codes {summ['code_agreement']:.5f} traces {summ['trace_rel_max']}",
+              flush=True)
+        assert summ["code_agreement"] >= CODE_FRAC
+        for key, v in summ["trace_rel_max"].items():
+            assert v < SOFT_RTOL, (key, v)

@@ -21,6 +21,8 @@ def layers():
         "ragged4": S.make_layer("ragged4", 37, 200, seed=11, d=1, bits=4, power=0.6, r=150, T_vamp=5),
         "lattice": S.make_layer("lattice", 24, 136, seed=12, d=8, power=0.6, T_vamp=4),
         "lattice_k1000": S.make_layer("lattice_k1000", 20, 64, seed=13, d=8, K=1000, power=0.5, r=60, T_vamp=4),
+        "lattice_shuffled": S.make_layer("lattice_shuffled", 16, 64, seed=14, d=8, power=0.5, r=60, T_vamp=4,
+                                         E=S.e8_codebook(3000)[np.random.default_rng(14).permutation(3000)]),
     }
 
 
@@ -35,7 +37,7 @@ def oracle_runs(name):
     return _CACHE[name]
 
 
-NAMES = ["scalar3", "ragged4", "lattice", "lattice_k1000"]
+NAMES = ["scalar3", "ragged4", "lattice", "lattice_k1000", "lattice_shuffled"]
 
 
 @pytest.mark.parametrize("name", NAMES)
