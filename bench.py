@@ -30,6 +30,7 @@ METRIC = "weights quantized/sec per layer (T_vamp=16 + 3 CD sweeps), % of MFMA/H
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+PEAK_FP64_VALU_TFLOPS = 78.6
 # Transcendental issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz at half
 # the fp32 VALU rate on gfx950 -> 19.66e12 exp/s (a throughput probe reads 18.4e12).
 EXP_RATE = 256 * 4 * 16 * 2.4e9 / 2
@@ -51,12 +52,25 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def mpq_e8dp_transitions(E):
+    import post_quantization_solver_amd as mpq
+    return mpq.binding.e8dp_transitions(E)
+
+
 def dominant_roofline(L, prof, steps):
     """Roofline entry for the kernel group with the largest time."""
     m, n, r, K, d = L.m, L.n, L.r, L.K, L.d
     best = max(prof, key=lambda k: prof[k][0])
     ms, launches = prof[best]
     per_launch_s = ms / max(launches, 1) / 1e3
+    if best == "denoise" and d == 8 and mpq_e8dp_transitions(L.E) > 0:
+        # forward-backward pass over the E8 automaton: 8 flops per transition
+        # per block, on the float64 vector units
+        flops = m * (n // d) * 8.0 * mpq_e8dp_transitions(L.E)
+        achieved = flops / per_launch_s / 1e12
+        return dict(kernel="denoise", bound="alu", achieved=achieved, peak=PEAK_FP64_VALU_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / PEAK_FP64_VALU_TFLOPS, traffic=None, launches=launches,
+                    avg_ms=ms / max(launches, 1), path="E8 forward-backward (float64)")
     if best == "denoise":
         evals = m * (n // d) * K
         if d == 8:
@@ -255,6 +269,7 @@ def main():
                 roofline=dict(bound=roof["bound"], achieved=roof["achieved"], peak=roof["peak"], unit=roof["unit"],
                               frac=roof["frac"], traffic=roof["traffic"], kernel=roof["kernel"],
                               avg_launch_ms=roof["avg_ms"], launches=roof["launches"],
+                              **({"path": roof["path"]} if "path" in roof else {}),
                               **({"secondary": roof["secondary"]} if "secondary" in roof else {})),
                 kernel_ms_per_step=split, cpu_baseline=cpu)
     print(json.dumps(line), flush=True)

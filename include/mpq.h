@@ -127,6 +127,11 @@ size_t mpq_workspace_bytes(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d
 #define MPQ_CB_E8_PREFIX 1
 int mpq_codebook_kind(const float* cb, int64_t K, int64_t d);
 
+/* For an MPQ_CB_E8_PREFIX codebook (K x 8, host): the number of valid
+ * transitions of its automaton over the 8 coordinates, the work unit of the
+ * forward-backward denoiser (8 flops each per block); 0 for other codebooks. */
+int64_t mpq_e8dp_transitions(const float* cb, int64_t K);
+
 /* Human-readable text for a status code (static storage). */
 const char* mpq_strerror(int status);
 

@@ -25,7 +25,7 @@ F_FIXED_BETA = 1
 EXPORTS = ("mpq_workspace_bytes", "mpq_strerror", "mpq_quantize_layer", "mpq_prologue", "mpq_denoise",
            "mpq_vamp_step", "mpq_map", "mpq_cd", "mpq_objective", "mpq_greedy", "mpq_greedy_workspace_bytes",
            "mpq_gram_workspace_bytes", "mpq_gram", "mpq_rht", "mpq_factor_workspace_bytes", "mpq_factor",
-           "mpq_codebook_kind", "mpq_hip_error_name")
+           "mpq_codebook_kind", "mpq_hip_error_name", "mpq_e8dp_transitions")
 
 
 class MPQError(RuntimeError):
@@ -120,10 +120,12 @@ def load_library(path: str = LIB_PATH):
     lib.mpq_factor_workspace_bytes.restype = SZ
     lib.mpq_factor.argtypes = [P, I64, I64, P, P, P, SZ, P]
     lib.mpq_codebook_kind.argtypes = [P, I64, I64]
+    lib.mpq_e8dp_transitions.argtypes = [P, I64]
+    lib.mpq_e8dp_transitions.restype = I64
     lib.mpq_hip_error_name.argtypes = []
     lib.mpq_hip_error_name.restype = ctypes.c_char_p
     for name in EXPORTS[2:]:
-        if name.endswith("_bytes") or name == "mpq_hip_error_name":
+        if name.endswith("_bytes") or name in ("mpq_hip_error_name", "mpq_e8dp_transitions"):
             continue
         getattr(lib, name).restype = I
     _lib = lib
@@ -145,6 +147,14 @@ def codebook_kind(cb) -> str:
     if rc < 0:
         raise MPQError(rc, "mpq_codebook_kind")
     return "e8_prefix" if rc == 1 else "generic"
+
+
+def e8dp_transitions(cb) -> int:
+    """Valid transitions of an E8-prefix codebook's automaton (0 otherwise)."""
+    E = _host_codebook(cb)
+    if E.shape[1] != 8:
+        return 0
+    return int(load_library().mpq_e8dp_transitions(E.ctypes.data_as(ctypes.c_void_p), E.shape[0]))
 
 
 def workspace_bytes(m, n, r, K, d) -> int:

@@ -28,6 +28,7 @@ hipError_t launch_nearest_lattice(const float*, int64_t, int64_t, const CbTables
 hipError_t launch_beta_lin(int64_t, const float*, const float*, float*, float*, hipStream_t);
 hipError_t launch_fill_i32(int32_t*, int64_t, int32_t, hipStream_t);
 bool e8_prefix_detect(const float* cb, int64_t K, E8Prefix& P);
+int64_t e8_transitions(const E8Prefix& P);
 size_t e8_table_bytes();
 void e8_build_tables(const E8Prefix& P, int8_t* out);
 hipError_t launch_denoise_e8dp(const float* R1, const float* gamma1, int64_t m, int64_t n, const E8Prefix& P,
@@ -967,6 +968,12 @@ int mpq_codebook_kind(const float* cb, int64_t K, int64_t d) {
   if (K < 1 || K > (d == 1 ? 64 : 65536)) return MPQ_ESHAPE;
   E8Prefix P;
   return d == 8 && e8_prefix_detect(cb, K, P) ? MPQ_CB_E8_PREFIX : MPQ_CB_GENERIC;
+}
+
+int64_t mpq_e8dp_transitions(const float* cb, int64_t K) {
+  E8Prefix P;
+  if (!cb || K < 1 || K > 65536 || !e8_prefix_detect(cb, K, P)) return 0;
+  return e8_transitions(P);
 }
 
 int mpq_greedy(const float* W, int64_t m, int64_t n, const float* s, const float* V, int64_t r, const float* cb,

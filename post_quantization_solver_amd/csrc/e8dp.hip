@@ -71,6 +71,17 @@ bool e8_prefix_detect(const float* cb, int64_t K, E8Prefix& P) {
   return (int64_t)(Bn[E8_INIT_I] + Bn[E8_INIT_H]) == K;
 }
 
+// Valid transitions (position, state, value) of the automaton: the work of one
+// query is 8 flops per transition (one FMA backward; product, sum and two FMAs
+// forward).
+int64_t e8_transitions(const E8Prefix& P) {
+  int64_t t = 0;
+  for (int p = 1; p <= 8; ++p)
+    for (int st = 0; st < E8_NS; ++st)
+      for (int k = 0; k < 7; ++k) t += e8_succ(st, p, k, P) >= 0;
+  return t;
+}
+
 // ------------------------------------------------------------ device side
 
 // Transition tables (uniform over queries): for position p (0-based) and
