@@ -29,11 +29,9 @@ hipError_t launch_beta_lin(int64_t, const float*, const float*, float*, float*, 
 hipError_t launch_fill_i32(int32_t*, int64_t, int32_t, hipStream_t);
 bool e8_prefix_detect(const float* cb, int64_t K, E8Prefix& P);
 int64_t e8_transitions(const E8Prefix& P);
-size_t e8_table_bytes();
-void e8_build_tables(const E8Prefix& P, int8_t* out);
 hipError_t launch_denoise_e8dp(const float* R1, const float* gamma1, int64_t m, int64_t n, const E8Prefix& P,
-                               const int8_t* tables, const float* a, const float* o, float* xhat, float* vblk,
-                               int32_t* flag, hipStream_t st);
+                               const float* a, const float* o, float* xhat, float* vblk, int32_t* flag,
+                               hipStream_t st);
 hipError_t launch_record_i32(const int32_t* src, int64_t m, int32_t* dst, int64_t ld, int64_t col, hipStream_t st);
 }  // namespace mpq
 
@@ -91,7 +89,7 @@ struct Layout {
 enum Region {
   R_VS, R_VST, R_YTIL, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI,
   R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_SPLIT, R_TKEY, R_QF, R_VSP, R_VSTP, R_R2P, R_ZP, R_ANCH,
-  R_LAM, R_CTMP, R_GDIAG, R_E8T, R_COUNT
+  R_LAM, R_CTMP, R_GDIAG, R_COUNT
 };
 
 static_assert(R_COUNT <= (int)(sizeof(Layout::off) / sizeof(size_t)), "Layout::off holds every region");
@@ -148,7 +146,6 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, bool g
   sz[R_LAM] = greedy ? (size_t)n * n * f64 : 0;
   sz[R_CTMP] = greedy ? chol_tmp_doubles(n) * f64 : 0;
   sz[R_GDIAG] = greedy ? (size_t)KD * KD * f64 : 0;
-  sz[R_E8T] = d == 8 ? e8_table_bytes() : 0;   // automaton tables of the E8 forward-backward denoiser
   size_t o = 0;
   for (int k = 0; k < R_COUNT; ++k) {
     L.off[k] = o;
@@ -353,12 +350,6 @@ int upload_codebook(Ctx& c, const float* cb) {
   MPQ_TRY(hipMemcpyAsync(c.p(R_E32), e32.data(), e32.size() * sizeof(float), hipMemcpyHostToDevice, c.st));
   MPQ_TRY(hipMemcpyAsync(c.p(R_QK), qk.data(), qk.size() * sizeof(uint16_t), hipMemcpyHostToDevice, c.st));
   MPQ_TRY(hipMemcpyAsync(c.p(R_PV), pv.data(), pv.size() * sizeof(uint16_t), hipMemcpyHostToDevice, c.st));
-  std::vector<int8_t> e8t;
-  if (c.e8dp) {
-    e8t.resize(e8_table_bytes());
-    e8_build_tables(c.e8p, e8t.data());
-    MPQ_TRY(hipMemcpyAsync(c.p(R_E8T), e8t.data(), e8t.size(), hipMemcpyHostToDevice, c.st));
-  }
   MPQ_TRY(hipStreamSynchronize(c.st));
   return MPQ_OK;
 }
@@ -386,8 +377,7 @@ int denoise(Ctx& c, const float* R1, const float* gamma1, const float* a, const 
   }
   if (c.e8dp) {
     TIMED(c, MPQ_PROF_DENOISE,
-          launch_denoise_e8dp(R1, gamma1, c.L.m, c.L.n, c.e8p, reinterpret_cast<const int8_t*>(c.p(R_E8T)), a, o,
-                              xhat, vblk, c.pi(R_FLAG), c.st));
+          launch_denoise_e8dp(R1, gamma1, c.L.m, c.L.n, c.e8p, a, o, xhat, vblk, c.pi(R_FLAG), c.st));
   } else {
     TIMED(c, MPQ_PROF_DENOISE,
           launch_denoise_lattice(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.pi(R_FLAG), c.st));

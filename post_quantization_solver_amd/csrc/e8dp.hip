@@ -6,16 +6,27 @@
 //   q(e) ~ prod_j g_j(e_j),   g_j(x) = exp(-kappa/2 (x - r'_j)^2 + sh_j),
 // and the codebook is the set of accepted paths of the automaton of e8dp.h.
 // So the normaliser Z, the means E[e_j] and E||e - r'||^2 are sums over the
-// automaton's paths: a backward pass gives the completion sums B_p(state), a
-// forward pass the prefix sums F_p(state), and for coordinate p
-//   sum_e q(e) e_p          = sum_state B_p(state) sum_{pred, x} F_{p-1}(pred) g_p(x) x
-//   sum_e q(e) (e_p - r'_p)^2 = same with (x - r'_p)^2.
+// automaton's paths: a forward pass gives the prefix sums F_p(state), a
+// backward pass the completion sums B_p(state), and for coordinate p
+//   sum_e q(e) e_p            = sum_state F_{p-1}(state) sum_x g_p(x) x B_p(succ(state, x))
+//   sum_e q(e) (e_p - r'_p)^2 = the same with (x - r'_p)^2.
 // 13 exponentials per coordinate instead of K per block, all in float64
 // (sh_j makes each coordinate's largest factor 1; a query whose Z still falls
-// below 1e-280 is handed to the exact attention pass).  One wave per query,
-// two automaton states per lane, the tables in LDS.
+// below 1e-280 is handed to the exact attention pass).
+//
+// Lane layout.  Integer and half-integer points never mix, so each class is
+// its own pass.  In the integer class the parity of the coordinate sum equals
+// that of the partial norm Q, so a state is (Q, t); in the half class it is
+// (s, Qi, t).  One query per 16-lane row (four per wave): lane j holds the
+// three lexicographic states t of Q = j (integer class) or of s = j / 8,
+// Qi = j % 8 (half class).  A value x moves Q by x^2 (Qi by (4x^2 - 1)/8, and
+// flips s or not depending on x and the parity of the position), the same
+// lane offset for every state, so each transition is one DPP row shift or
+// rotation of a register: the whole pass lives in registers, with only the
+// per-coordinate factors g in LDS.
 #include <math.h>
 #include <algorithm>
+#include <type_traits>
 #include <vector>
 #include "mpq_device.h"
 #include "internal.h"
@@ -71,58 +82,197 @@ bool e8_prefix_detect(const float* cb, int64_t K, E8Prefix& P) {
   return (int64_t)(Bn[E8_INIT_I] + Bn[E8_INIT_H]) == K;
 }
 
-// Valid transitions (position, state, value) of the automaton: the work of one
-// query is 8 flops per transition (one FMA backward; product, sum and two FMAs
-// forward).
+// Transitions (position, state, value) of the trimmed automaton: those on some
+// path from an initial state to an accepting one.  The algorithmic work of one
+// query is 8 flops per such transition (one multiply-add backward; product,
+// sum and two multiply-adds for the prefix sums and the moments).
 int64_t e8_transitions(const E8Prefix& P) {
+  std::vector<std::vector<char>> fw(9, std::vector<char>(E8_NS, 0)), bw(9, std::vector<char>(E8_NS, 0));
+  fw[0][E8_INIT_I] = fw[0][E8_INIT_H] = 1;
+  for (int p = 1; p <= 8; ++p)
+    for (int st = 0; st < E8_NS; ++st)
+      if (fw[p - 1][st])
+        for (int k = 0; k < 7; ++k) {
+          const int nx = e8_succ(st, p, k, P);
+          if (nx >= 0) fw[p][nx] = 1;
+        }
+  for (int st = 0; st < E8_NS; ++st) bw[8][st] = e8_accept(st, P);
+  for (int p = 8; p >= 1; --p)
+    for (int st = 0; st < E8_NS; ++st)
+      for (int k = 0; k < 7; ++k) {
+        const int nx = e8_succ(st, p, k, P);
+        if (nx >= 0 && bw[p][nx]) bw[p - 1][st] = 1;
+      }
   int64_t t = 0;
   for (int p = 1; p <= 8; ++p)
     for (int st = 0; st < E8_NS; ++st)
-      for (int k = 0; k < 7; ++k) t += e8_succ(st, p, k, P) >= 0;
+      for (int k = 0; k < 7; ++k) {
+        const int nx = e8_succ(st, p, k, P);
+        t += fw[p - 1][st] && nx >= 0 && bw[p][nx];
+      }
   return t;
 }
 
 // ------------------------------------------------------------ device side
 
-// Transition tables (uniform over queries): for position p (0-based) and
-// state st (E8_NS + 1 slots, the last a dummy state whose sums are 0), one
-// 8-byte word with the successors through value index k = 0..6 (byte k) and
-// one 16-byte word with the (up to two) predecessors (bytes 2k, 2k + 1);
-// missing ones, and the unused last bytes, name the dummy.
-constexpr int E8_SLOTS = E8_NS + 1;                      // + dummy
-constexpr int E8_SUCC_BYTES = 8 * E8_SLOTS * 8;
-constexpr int E8_PRED_BYTES = 8 * E8_SLOTS * 16;
-constexpr int E8_TABLE_BYTES = E8_SUCC_BYTES + E8_PRED_BYTES;
+constexpr int E8DP_WAVES = 4;   // waves per workgroup, four queries per wave
 
-size_t e8_table_bytes() { return E8_TABLE_BYTES; }
+// Per-query factors in LDS: c[p][k] = g_p of value index k (integer values
+// k - 3 for k < 7, half values (k - 7) - 5/2 for 7 <= k < 13) and c[p][13] =
+// r'_p.  The padding puts the four rows of a wave in different banks.
+struct E8RowCoef {
+  double c[8][16];
+  double pad[2];
+};
 
-void e8_build_tables(const E8Prefix& P, int8_t* out) {
-  uint8_t* succ = reinterpret_cast<uint8_t*>(out);
-  uint8_t* pred = succ + E8_SUCC_BYTES;
-  for (int p = 0; p < 8; ++p)
-    for (int st = 0; st < E8_SLOTS; ++st) {
-      uint8_t* sw = succ + (p * E8_SLOTS + st) * 8;
-      uint8_t* pw = pred + (p * E8_SLOTS + st) * 16;
-      for (int k = 0; k < 8; ++k) {
-        int nx = -1, pr[2] = {-1, -1}, np = 0;
-        if (st < E8_NS && k < 7) {
-          nx = e8_succ(st, p + 1, k, P);
-          np = e8_pred(st, p + 1, k, P, pr);
-        }
-        sw[k] = (uint8_t)(nx >= 0 ? nx : E8_NS);
-        for (int z = 0; z < 2; ++z) pw[2 * k + z] = (uint8_t)(z < np ? pr[z] : E8_NS);
-      }
-    }
+// DPP row operations on a float64 register (two 32-bit moves): row_shl:n
+// reads lane j + n, row_shr:n lane j - n (0 outside the 16-lane row),
+// row_ror:n lane (j - n) mod 16.  CTRL < 0 is the identity.
+template <int CTRL>
+__device__ __forceinline__ double row_read(double v) {
+  if constexpr (CTRL < 0) {
+    return v;
+  } else {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xf, 0xf, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, true);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+  }
 }
 
-constexpr int E8DP_WAVES = 4;
+constexpr int DPP_ROW_SHL = 0x100, DPP_ROW_SHR = 0x110, DPP_ROW_ROR = 0x120;
 
-struct E8WaveLds {
-  double B[9][E8_SLOTS];
-  double F[2][E8_SLOTS];
-  double g[8][14];   // 7 integer values, 6 half values, 0 (the missing 7th half value)
-  double rp[8];      // r' of the query
-};
+// Sum over the 16 lanes of a row, in every lane of it.
+__device__ __forceinline__ double row_sum(double v) {
+  v += row_read<DPP_ROW_ROR + 8>(v);
+  v += row_read<DPP_ROW_ROR + 4>(v);
+  v += row_read<DPP_ROW_ROR + 2>(v);
+  v += row_read<DPP_ROW_ROR + 1>(v);
+  return v;
+}
+
+template <int I, int N, class Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  if constexpr (I < N) {
+    fn(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(fn);
+  }
+}
+
+// Twice the value of index k in a class (integer k - 3, half (2k - 5)/2).
+constexpr int e8_twice_value(bool half, int k) { return half ? 2 * k - 5 : 2 * (k - 3); }
+// Half class: Qi moves by (u^2 - 1)/8 for u = 2x.
+constexpr int e8_qi_step(int k) { return ((2 * k - 5) * (2 * k - 5) - 1) / 8; }
+
+// DPP control that brings the state reached through value k at position p
+// (1-based) into the lane of its source state (backward) or the source state
+// into the lane of the state it reaches (forward).
+constexpr int e8_ctrl(bool half, int p, int k, bool fwd) {
+  if (!half) {
+    const int a2 = (k - 3) * (k - 3);
+    return a2 == 0 ? -1 : (fwd ? DPP_ROW_SHR : DPP_ROW_SHL) + a2;
+  }
+  const int u = 2 * k - 5, d = e8_qi_step(k);
+  // s flips when the coordinate sum (of 2x) mod 4 crosses the parity of p:
+  // for odd p when u = 3 mod 4, for even p when u = 1 mod 4
+  const bool flip = (p & 1) ? ((u & 3) == 3) : ((u & 3) == 1);
+  if (!flip) return d == 0 ? -1 : (fwd ? DPP_ROW_SHR : DPP_ROW_SHL) + d;
+  return DPP_ROW_ROR + ((fwd ? 8 + d : 8 - d) & 15);
+}
+
+// Keeps the factors of a pass from being held in registers until the next one.
+__device__ __forceinline__ void reload_barrier() { asm volatile("" ::: "memory"); }
+
+// One class: forward pass storing F_0..F_7, then the backward pass with the
+// moments of every coordinate accumulated per lane.  LCLASS: the codebook's
+// last point is in this class, so the lexicographic "equal" chain runs the
+// whole length (otherwise it ends after the first coordinate).
+template <bool HALF, bool LCLASS>
+__device__ __forceinline__ void e8_class_pass(const int j, const E8RowCoef& cf, const E8Prefix& P, double (&m1)[8],
+                                              double& m2, double& z) {
+  constexpr int NK = HALF ? 6 : 7;
+  constexpr int KO = HALF ? 7 : 0;
+  const int qi = j & 7;
+  // half class: a move of Qi by d stays inside the 6 valid slots of the lane's s block
+  const double mb1 = qi <= 4 ? 1.0 : 0.0, mb3 = qi <= 2 ? 1.0 : 0.0;
+  const double mf1 = qi >= 1 ? 1.0 : 0.0, mf3 = qi >= 3 ? 1.0 : 0.0;
+  double Fl[8], Fe[8], Fg[8];
+  Fl[0] = 0.0;
+  Fe[0] = j == 0 ? 1.0 : 0.0;
+  Fg[0] = 0.0;
+  static_for<1, 8>([&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = decltype(pc)::value, c = p - 1;
+    constexpr bool live = LCLASS || p == 1;
+    int l2 = P.L2[c];
+    asm volatile("" : "+s"(l2));   // per step: keeps the selectors below from living across passes
+    double nl = 0.0, ne = 0.0, ng = 0.0;
+    static_for<0, NK>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int CT = e8_ctrl(HALF, p, k, true);
+      double g = cf.c[c][KO + k];
+      if constexpr (HALF && e8_qi_step(k) == 1) g *= mf1;
+      if constexpr (HALF && e8_qi_step(k) == 3) g *= mf3;
+      nl = fma(g, row_read<CT>(Fl[c]), nl);
+      ng = fma(g, row_read<CT>(Fg[c]), ng);
+      if constexpr (live) {
+        const int ck = e8_cmp(e8_twice_value(HALF, k), l2);
+        const double w = g * row_read<CT>(Fe[c]);
+        nl = fma(w, ck == 0 ? 1.0 : 0.0, nl);
+        ne = fma(w, ck == 1 ? 1.0 : 0.0, ne);
+        ng = fma(w, ck == 2 ? 1.0 : 0.0, ng);
+      }
+    });
+    Fl[p] = nl;
+    Fe[p] = ne;
+    Fg[p] = ng;
+  });
+  reload_barrier();
+  double Bl, Be, Bg;
+  {
+    const int norm = HALF ? 2 * qi + 2 : j;
+    const bool valid = HALF ? (qi <= 5 && j < 8) : ((j & 1) == 0 && j <= 12);
+    Bl = valid && norm <= P.qlast ? 1.0 : 0.0;
+    Be = Bl;
+    Bg = valid && norm < P.qlast ? 1.0 : 0.0;
+  }
+  static_for<0, 8>([&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = 8 - decltype(pc)::value, c = p - 1;
+    constexpr bool live = LCLASS || p == 1;
+    int l2 = P.L2[c];
+    asm volatile("" : "+s"(l2));   // per step: keeps the selectors below from living across passes
+    const double rp = cf.c[c][13];
+    double nl = 0.0, ne = 0.0, ng = 0.0, a0 = 0.0, a1 = 0.0, a2 = 0.0;
+    static_for<0, NK>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int CT = e8_ctrl(HALF, p, k, false);
+      constexpr double x = 0.5 * e8_twice_value(HALF, k);
+      double g = cf.c[c][KO + k];
+      if constexpr (HALF && e8_qi_step(k) == 1) g *= mb1;
+      if constexpr (HALF && e8_qi_step(k) == 3) g *= mb3;
+      const double sl = row_read<CT>(Bl), sg = row_read<CT>(Bg);
+      nl = fma(g, sl, nl);
+      ng = fma(g, sg, ng);
+      double pk = fma(Fl[c], sl, Fg[c] * sg);
+      if constexpr (live) {
+        const int ck = e8_cmp(e8_twice_value(HALF, k), l2);
+        const double se = row_read<CT>(Be);
+        const double sel = fma(se, ck == 1 ? 1.0 : 0.0, fma(sg, ck == 2 ? 1.0 : 0.0, sl * (ck == 0 ? 1.0 : 0.0)));
+        pk = fma(Fe[c], sel, pk);
+        ne = fma(g, sel, ne);
+      }
+      const double gp = g * pk;
+      a0 += gp;
+      a1 = fma(x, gp, a1);
+      a2 = fma(x * x, gp, a2);
+    });
+    m1[c] += a1;
+    m2 += fma(rp * rp, a0, fma(-2.0 * rp, a1, a2));
+    if constexpr (p == 1) z += a0;
+    Bl = nl;
+    Be = ne;
+    Bg = ng;
+  });
+}
 
 // Wave-local ordering of LDS writes before other lanes of the wave read them.
 __device__ __forceinline__ void wave_sync() {
@@ -131,157 +281,99 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One wave per query, the waves of the grid striding over the queries; lane
-// l owns states l and l + 64 (the dummy included).
+// Four queries per wave, one per 16-lane row.
 __global__ __launch_bounds__(256) void e8dp_kernel(const float* __restrict__ R1, const float* __restrict__ gamma1,
                                                    int64_t m, int64_t n, const float* __restrict__ a,
-                                                   const float* __restrict__ o, E8Prefix P,
-                                                   const int8_t* __restrict__ tables, float* __restrict__ xhat,
+                                                   const float* __restrict__ o, E8Prefix P, float* __restrict__ xhat,
                                                    float* __restrict__ vblk, int32_t* __restrict__ flag_list,
                                                    int32_t* __restrict__ flag_count) {
-  __shared__ __attribute__((aligned(16))) int8_t T[E8_TABLE_BYTES];
-  __shared__ E8WaveLds lds_all[E8DP_WAVES];
-  for (int k = threadIdx.x; k < E8_TABLE_BYTES / 16; k += 256)
-    reinterpret_cast<int4*>(T)[k] = reinterpret_cast<const int4*>(tables)[k];
-  __syncthreads();
-  const uint2* succ = reinterpret_cast<const uint2*>(T);
-  const uint4* pred = reinterpret_cast<const uint4*>(T + E8_SUCC_BYTES);
+  __shared__ E8RowCoef coef[E8DP_WAVES * 4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  E8WaveLds& S = lds_all[wave];
+  const int row = lane >> 4, j = lane & 15;
+  E8RowCoef& cf = coef[wave * 4 + row];
   const int64_t B = n / 8;
   const int64_t total = m * B;
-  const int st0 = lane, st1 = lane + 64;
-  const bool has1 = st1 < E8_SLOTS;
-  // per-lane class constants: value of index k is k - c0 (integer) or k - 2.5 (half)
-  const double xoff0 = st0 < E8_NI ? 3.0 : 2.5, xoff1 = st1 < E8_NI ? 3.0 : 2.5;
-  const int goff0 = st0 < E8_NI ? 0 : 7, goff1 = st1 < E8_NI ? 0 : 7;
-  const double acc0 = (st0 < E8_NS && e8_accept(st0, P)) ? 1.0 : 0.0;
-  const double acc1 = (has1 && st1 < E8_NS && e8_accept(st1, P)) ? 1.0 : 0.0;
-  const double ini0 = (st0 == E8_INIT_I || st0 == E8_INIT_H) ? 1.0 : 0.0;
-  const double ini1 = (st1 == E8_INIT_I || st1 == E8_INIT_H) ? 1.0 : 0.0;
-  for (int64_t q = (int64_t)blockIdx.x * E8DP_WAVES + wave; q < total; q += (int64_t)gridDim.x * E8DP_WAVES) {
-    const int64_t i = q / B, b = q - i * B;
-    const double gm = (double)gamma1[i];
+  const bool lhalf = (P.L2[0] & 1) != 0;
+  const double xj = j < 7 ? (double)(j - 3) : (double)(j - 7) - 2.5;   // value of factor index j (j < 13)
+  {
+    const int64_t q = ((int64_t)blockIdx.x * E8DP_WAVES + wave) * 4 + row;
+    const bool active = q < total;
+    int64_t i = 0, b = 0;
+    double gm = 0.0, ai = 1.0, oi = 0.0;
+    if (active) {
+      i = q / B;
+      b = q - i * B;
+      gm = (double)gamma1[i];
+      ai = (double)a[i];
+      oi = (double)o[i];
+    }
+    const bool frozen = active && !isfinite(gm);   // frozen row: the cavity passes through
+    const double kap = active && !frozen ? gm * ai * ai : 0.0;
     const float* rq = R1 + i * n + b * 8;
+    const float rv = active && j < 8 ? rq[j] : 0.f;
+    if (j < 8) cf.c[j][13] = ((double)rv - oi) / ai;
+    wave_sync();
+    if (j < 13) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const double r = cf.c[c][13];
+        const double xb = fmin(fmax(rint(2.0 * r) * 0.5, -3.0), 3.0);   // nearest of the 13 values
+        const double d = xj - r, db = xb - r;
+        cf.c[c][j] = exp(-0.5 * kap * (d * d - db * db));
+      }
+    }
+    wave_sync();
+    double m1[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    double m2 = 0.0, z = 0.0;
+    if (lhalf) {
+      e8_class_pass<false, false>(j, cf, P, m1, m2, z);
+      reload_barrier();
+      e8_class_pass<true, true>(j, cf, P, m1, m2, z);
+    } else {
+      e8_class_pass<false, true>(j, cf, P, m1, m2, z);
+      reload_barrier();
+      e8_class_pass<true, false>(j, cf, P, m1, m2, z);
+    }
+    reload_barrier();
+    const double Z = row_sum(z);
+    const double M2 = row_sum(m2);
+    double mj = 0.0, sq = 0.0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const double mc = row_sum(m1[c]);
+      mj = j == c ? mc : mj;
+      const double dl = mc / Z - cf.c[c][13];
+      sq = fma(dl, dl, sq);
+    }
+    if (!active) return;
     float* xo = xhat + i * n + b * 8;
-    if (!isfinite(gm)) {   // frozen row: the cavity passes through (uniform over the wave)
-      if (lane < 8) xo[lane] = rq[lane];
-      if (lane == 0) vblk[i * B + b] = 0.f;
-      continue;
+    if (frozen) {
+      if (j < 8) xo[j] = rv;
+      if (j == 0) vblk[i * B + b] = 0.f;
+      return;
     }
-    const double ai = (double)a[i], oi = (double)o[i];
-    const double rl = lane < 8 ? ((double)rq[lane] - oi) / ai : 0.0;   // r'_lane
-    if (lane < 8) S.rp[lane] = rl;
-    wave_sync();
-    const double kap = gm * ai * ai;
-    // per-coordinate factors g_j(x) = exp(-kappa/2 (x - r'_j)^2 + sh_j), largest 1
-    for (int pk = lane; pk < 112; pk += 64) {
-      const int j = pk / 14, k = pk % 14;
-      double best = -INFINITY, lw = 0.0;
-#pragma unroll
-      for (int kk = 0; kk < 13; ++kk) {
-        const double x = kk < 7 ? (double)(kk - 3) : (double)(kk - 7) - 2.5;
-        const double d = x - S.rp[j];
-        const double l = -0.5 * kap * d * d;
-        best = fmax(best, l);
-        lw = kk == k ? l : lw;
-      }
-      S.g[j][k] = k < 13 ? exp(lw - best) : 0.0;
-    }
-    S.B[8][st0] = acc0;
-    if (has1) S.B[8][st1] = acc1;
-    wave_sync();
-    // backward: B_{p-1}(st) = sum_k g_p(k) B_p(succ)
-#pragma unroll 1
-    for (int p = 8; p >= 1; --p) {
-      const uint2 w0 = succ[(p - 1) * E8_SLOTS + st0];
-      const uint2 w1 = has1 ? succ[(p - 1) * E8_SLOTS + st1] : make_uint2(0u, 0u);
-      double a0 = 0.0, a1 = 0.0;
-#pragma unroll
-      for (int k = 0; k < 7; ++k) {
-        const uint32_t i0 = ((k < 4 ? w0.x : w0.y) >> (8 * (k & 3))) & 0xffu;
-        a0 = fma(S.g[p - 1][goff0 + k], S.B[p][i0], a0);
-        if (has1) {
-          const uint32_t i1 = ((k < 4 ? w1.x : w1.y) >> (8 * (k & 3))) & 0xffu;
-          a1 = fma(S.g[p - 1][goff1 + k], S.B[p][i1], a1);
-        }
-      }
-      S.B[p - 1][st0] = a0;
-      if (has1) S.B[p - 1][st1] = a1;
-      wave_sync();
-    }
-    const double Z = S.B[0][E8_INIT_I] + S.B[0][E8_INIT_H];
-    // forward with the moments
-    S.F[0][st0] = ini0;
-    if (has1) S.F[0][st1] = ini1;
-    wave_sync();
-    // lane j keeps sum_e q(e) e_j; every lane the sum of q(e) ||e - r'||^2
-    double m1 = 0.0, mom2 = 0.0;
-#pragma unroll 1
-    for (int p = 1; p <= 8; ++p) {
-      const int cur = (p - 1) & 1, nxt = p & 1;
-      const uint4 v0 = pred[(p - 1) * E8_SLOTS + st0];
-      const uint4 v1 = has1 ? pred[(p - 1) * E8_SLOTS + st1] : make_uint4(0u, 0u, 0u, 0u);
-      const double rpp = S.rp[p - 1];
-      double aF0 = 0.0, aG0 = 0.0, aH0 = 0.0, aF1 = 0.0, aG1 = 0.0, aH1 = 0.0;
-#pragma unroll
-      for (int k = 0; k < 7; ++k) {
-        const double x0 = (double)k - xoff0, d0 = x0 - rpp;
-        // bytes 2k, 2k + 1 of the 16-byte word: the two predecessors through k
-        const uint32_t h0 = ((k < 2 ? v0.x : k < 4 ? v0.y : k < 6 ? v0.z : v0.w) >> (16 * (k & 1))) & 0xffffu;
-        const double f0 = S.F[cur][h0 & 0xffu] + S.F[cur][h0 >> 8];
-        const double gf0 = S.g[p - 1][goff0 + k] * f0;
-        aF0 += gf0;
-        aG0 = fma(gf0, x0, aG0);
-        aH0 = fma(gf0, d0 * d0, aH0);
-        if (has1) {
-          const double x1 = (double)k - xoff1, d1 = x1 - rpp;
-          const uint32_t h1 = ((k < 2 ? v1.x : k < 4 ? v1.y : k < 6 ? v1.z : v1.w) >> (16 * (k & 1))) & 0xffffu;
-          const double f1 = S.F[cur][h1 & 0xffu] + S.F[cur][h1 >> 8];
-          const double gf1 = S.g[p - 1][goff1 + k] * f1;
-          aF1 += gf1;
-          aG1 = fma(gf1, x1, aG1);
-          aH1 = fma(gf1, d1 * d1, aH1);
-        }
-      }
-      S.F[nxt][st0] = aF0;
-      if (has1) S.F[nxt][st1] = aF1;
-      const double b0 = S.B[p][st0], b1 = has1 ? S.B[p][st1] : 0.0;
-      double c1 = fma(aG0, b0, aG1 * b1);
-#pragma unroll
-      for (int msk = 1; msk < 64; msk <<= 1) c1 += __shfl_xor(c1, msk, 64);
-      m1 = lane == p - 1 ? c1 : m1;
-      mom2 = fma(aH0, b0, fma(aH1, b1, mom2));
-      wave_sync();
-    }
-#pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) mom2 += __shfl_xor(mom2, msk, 64);
     if (!(Z > 1e-280) || !isfinite(Z)) {
-      if (lane == 0) flag_list[atomicAdd(flag_count, 1)] = (int32_t)q;
-      continue;
+      if (j == 0) flag_list[atomicAdd(flag_count, 1)] = (int32_t)q;
+      return;
     }
     const double iz = 1.0 / Z;
-    const double dl = lane < 8 ? m1 * iz - rl : 0.0;
-    double sq = dl * dl;
-#pragma unroll
-    for (int msk = 1; msk < 8; msk <<= 1) sq += __shfl_xor(sq, msk, 64);
-    if (lane < 8) xo[lane] = (float)fma(ai, m1 * iz, oi);
-    if (lane == 0) vblk[i * B + b] = (float)(fmax(mom2 * iz - sq, 0.0) * ai * ai);
+    if (j < 8) xo[j] = (float)fma(ai, mj * iz, oi);
+    if (j == 0) vblk[i * B + b] = (float)(fmax(M2 * iz - sq, 0.0) * ai * ai);
   }
 }
 
-constexpr int E8DP_GRID_MAX = 8192;   // workgroups (each wave then loops over queries)
-
 hipError_t launch_denoise_e8dp(const float* R1, const float* gamma1, int64_t m, int64_t n, const E8Prefix& P,
-                               const int8_t* tables, const float* a, const float* o, float* xhat, float* vblk,
-                               int32_t* flag, hipStream_t st) {
+                               const float* a, const float* o, float* xhat, float* vblk, int32_t* flag,
+                               hipStream_t st) {
   const int64_t total = m * (n / 8);
   if (total <= 0) return hipSuccess;
   hipError_t e = launch_fill_i32(flag, 1, 0, st);
   if (e != hipSuccess) return e;
-  const int64_t wgs = std::min<int64_t>((total + E8DP_WAVES - 1) / E8DP_WAVES, E8DP_GRID_MAX);
-  hipLaunchKernelGGL(e8dp_kernel, dim3((unsigned)wgs), dim3(256), 0, st, R1, gamma1, m, n, a, o, P, tables, xhat,
+  const int64_t per_wg = (int64_t)E8DP_WAVES * 4;
+  const int64_t wgs = (total + per_wg - 1) / per_wg;
+  if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(e8dp_kernel, dim3((unsigned)wgs), dim3(64 * E8DP_WAVES), 0, st, R1, gamma1, m, n, a, o, P, xhat,
                      vblk, flag + 64, flag);
   return hipGetLastError();
 }

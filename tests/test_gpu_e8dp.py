@@ -106,3 +106,28 @@ def test_layer_with_and_without_e8dp():
         assert summ["code_agreement"] >= CODE_FRAC
         for key, v in summ["trace_rel_max"].items():
             assert v < SOFT_RTOL, (key, v)
+
+
+@pytest.mark.parametrize("K", [2401, 65536])
+def test_e8dp_ragged_and_frozen(K):
+    """15 queries (the last wave of four rows of the forward-backward kernel is
+    partly empty) and a frozen row (infinite precision: the cavity passes
+    through with variance 0) between two live ones; K = 2401 ends in an
+    integer point, 65536 in a half-integer one."""
+    import post_quantization_solver_amd as mpq
+    E = S.e8_codebook(K)
+    g = np.random.default_rng(17)
+    m, n = 3, 40
+    a = (0.5 + g.random(m)).astype(np.float32)
+    o = (0.1 * g.standard_normal(m)).astype(np.float32)
+    R1 = (g.standard_normal((m, n)) * 1.2 * a[:, None] + o[:, None]).astype(np.float32)
+    g1 = (np.array([0.7, 1.0, 4.0]) / a.astype(np.float64) ** 2).astype(np.float32)
+    g1[1] = np.inf
+    xh, vt = mpq.denoise(dev(R1), dev(g1), E, dev(a), dev(o))
+    xh, vt = host(xh), host(vt)
+    assert np.array_equal(xh[1], R1[1]) and np.all(vt[1] == 0)
+    live = [0, 2]
+    xr, vr = oracle_denoise(R1[live], g1[live], E, a[live], o[live])
+    for t, k in enumerate(live):
+        assert rel_vec(xh[k], xr[t]) < SOFT_RTOL
+        assert rel_scalar(vt[k].astype(np.float64).sum(), vr[t].sum()) < SOFT_RTOL
