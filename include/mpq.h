@@ -110,7 +110,8 @@ typedef struct {
 #define MPQ_PROF_CD_SEARCH 8  /* CD candidate search and moves */
 #define MPQ_PROF_OTHER     9  /* traces, copies, factor preparation */
 #define MPQ_PROF_DENOISE_EXACT 10  /* lattice denoiser: exact pass over the queries the fast pass flagged */
-#define MPQ_PROF_COUNT    11
+#define MPQ_PROF_CD_SCORE 11  /* lattice CD: the codebook scoring kernel alone (MPQ_PROF_CD_SEARCH keeps the rest) */
+#define MPQ_PROF_COUNT    12
 
 /* Bytes of device workspace needed by every entry point for these shapes. */
 size_t mpq_workspace_bytes(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d);

@@ -43,7 +43,7 @@ class MPQError(RuntimeError):
 F_PROFILE = 2
 F_NO_E8DP = 4
 PROF_NAMES = ("prologue", "denoise", "extrinsic", "linear1", "beta", "linear2", "map", "cd_gemm", "cd_search",
-              "other", "denoise_exact")
+              "other", "denoise_exact", "cd_score")
 PROF_COUNT = len(PROF_NAMES)
 
 

@@ -89,7 +89,7 @@ struct Layout {
 enum Region {
   R_VS, R_VST, R_YTIL, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI,
   R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_SPLIT, R_TKEY, R_QF, R_VSP, R_VSTP, R_R2P, R_ZP, R_ANCH,
-  R_LAM, R_CTMP, R_GDIAG, R_COUNT
+  R_LAM, R_CTMP, R_GDIAG, R_MROWS, R_COUNT
 };
 
 static_assert(R_COUNT <= (int)(sizeof(Layout::off) / sizeof(size_t)), "Layout::off holds every region");
@@ -146,6 +146,8 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, bool g
   sz[R_LAM] = greedy ? (size_t)n * n * f64 : 0;
   sz[R_CTMP] = greedy ? chol_tmp_doubles(n) * f64 : 0;
   sz[R_GDIAG] = greedy ? (size_t)KD * KD * f64 : 0;
+  // per CD row group: the rows that moved in the current tile, and their count
+  sz[R_MROWS] = (size_t)CD_GROUPS_MAX * ((m + CD_GROUPS_MAX - 1) / CD_GROUPS_MAX + 64) * sizeof(int32_t);
   size_t o = 0;
   for (int k = 0; k < R_COUNT; ++k) {
     L.off[k] = o;
@@ -557,7 +559,7 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
   struct Group {
     int64_t r0, mg;
     double *Gt, *Dl, *U, *part;
-    int32_t *codes, *chg, *changes, *pi;
+    int32_t *codes, *chg, *changes, *pi, *mrows, *nmoved;
     float* ps;
     const float *a, *o;
     uint32_t *qf, *tk;
@@ -579,6 +581,8 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
     q.o = o + q.r0 * c.cb.G;
     q.qf = reinterpret_cast<uint32_t*>(c.p(R_QF)) + q.r0 * 16;
     q.tk = reinterpret_cast<uint32_t*>(c.p(R_TKEY)) + (int64_t)g * (KD / 8) * L.Kpad * 4;
+    q.nmoved = c.pi(R_MROWS) + (int64_t)g * (mg_max + 64);
+    q.mrows = q.nmoved + 64;
   }
   int rc = MPQ_OK;
   auto body = [&]() -> int {
@@ -619,19 +623,29 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
               const Group& q = grp[g];
               if (q.mg == 0) continue;
               c.st = gs[g];
+              const int64_t b = j0 / 8 + bl;
+              if (bl == 0)
+                TIMED(c, MPQ_PROF_CD_SEARCH,
+                      launch_cd_lattice_query(q.mg, L.n, b, bl, kw, q.Gt, Ht, c.cb, q.a, q.codes, q.qf, c.st));
+              TIMED(c, MPQ_PROF_CD_SCORE, launch_cd_lattice_score(q.mg, bl, q.tk, c.cb, q.qf, q.ps, q.pi, c.st));
               TIMED(c, MPQ_PROF_CD_SEARCH,
-                    launch_cd_lattice_block(q.mg, L.n, j0 / 8 + bl, bl, kw, q.Gt, Ht, q.tk, c.cb, q.a, q.codes, q.Dl,
-                                            q.chg, q.ps, q.pi, q.qf, c.st));
+                    launch_cd_lattice_update(q.mg, L.n, b, bl, kw, q.Gt, Ht, c.cb, q.a, q.codes, q.Dl, q.chg, q.ps,
+                                             q.pi, q.qf, c.st));
             }
           }
         }
+        // U -= Delta VS_tile^T over the rows that moved in the tile (the other
+        // rows of Delta are zero)
         for (int g = 0; g < G; ++g) {
           const Group& q = grp[g];
           if (q.mg == 0) continue;
           c.st = gs[g];
-          TIMED(c, MPQ_PROF_CD_GEMM,
-                launch_gemm64(EPI_SUB_INPLACE, true,
-                              gemm64((int)q.mg, (int)L.r, kw, q.Dl, kw, c.p(R_VST) + j0, L.n, q.U, L.r), c.st));
+          TIMED(c, MPQ_PROF_CD_GEMM, launch_fill_i32(q.nmoved, 1, 0, c.st));
+          TIMED(c, MPQ_PROF_CD_GEMM, launch_collect_nonzero_rows(q.Dl, q.mg, kw, q.mrows, q.nmoved, c.st));
+          Gemm64Args gu = gemm64((int)q.mg, (int)L.r, kw, q.Dl, kw, c.p(R_VST) + j0, L.n, q.U, L.r);
+          gu.rows = q.mrows;
+          gu.nrows = q.nmoved;
+          TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_SUB_INPLACE, true, gu, c.st));
         }
       }
       for (int g = 0; g < G; ++g) {
@@ -696,7 +710,7 @@ int run_greedy(Ctx& c, const float* W, const float* a, const float* o, int32_t* 
       TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_lattice_tkeys(kw / 8, kw, Gd, c.cb, tk, c.st));
       TIMED(c, MPQ_PROF_CD_SEARCH, launch_greedy_query(L.m, L.n, j0, P, Lam, W, a, o, qf, c.st));
       for (int bl = 0; bl < kw / 8; ++bl) {
-        TIMED(c, MPQ_PROF_CD_SEARCH,
+        TIMED(c, MPQ_PROF_CD_SCORE,
               launch_cd_lattice_score(L.m, bl, tk, c.cb, qf, c.p(R_PS), c.pi(R_PI), c.st));
         TIMED(c, MPQ_PROF_CD_SEARCH,
               launch_greedy_update(L.m, L.n, j0, j0 / 8 + bl, bl, kw, P, Lam, Rtile, W, c.cb, a, o, c.p(R_PS),

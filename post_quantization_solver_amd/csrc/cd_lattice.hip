@@ -357,30 +357,26 @@ hipError_t launch_cd_lattice_tkeys(int nb, int kd, const double* Ht, const CbTab
   return hipGetLastError();
 }
 
-hipError_t launch_cd_lattice_block(int64_t m, int64_t n, int64_t b, int bl, int kd, double* Gt, const double* Ht,
-                                   const uint32_t* tk, const CbTables& cb, const float* a, int32_t* codes,
-                                   double* Delta, int32_t* changes, float* part_s, int32_t* part_i, uint32_t* qf,
-                                   hipStream_t st) {
+int cd_lattice_slices(int Kpad) { return (Kpad + CDL_CW_WG - 1) / CDL_CW_WG; }
+
+hipError_t launch_cd_lattice_query(int64_t m, int64_t n, int64_t b, int bl, int kd, const double* Gt,
+                                   const double* Ht, const CbTables& cb, const float* a, const int32_t* codes,
+                                   uint32_t* qf, hipStream_t st) {
   if (m <= 0) return hipSuccess;
-  const dim3 rows_grid((unsigned)((m + 3) / 4));
-  if (bl == 0) {
-    hipLaunchKernelGGL(cd_query_kernel, rows_grid, dim3(256), 0, st, m, n, b, bl, kd, Gt, Ht, cb.e32, cb.K, a, codes,
-                       qf);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int nslices = (cb.Kpad + CDL_CW_WG - 1) / CDL_CW_WG;
-  dim3 g1((unsigned)nslices, (unsigned)((m + CDL_ROWS_WG - 1) / CDL_ROWS_WG));
-  hipLaunchKernelGGL(cd_score_kernel, g1, dim3(256), 0, st, m, bl, cb.qk_keys, reinterpret_cast<const v4u*>(tk),
-                     cb.Kpad, reinterpret_cast<const v4u*>(qf), part_s, part_i);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(cd_update_kernel, rows_grid, dim3(256), 0, st, m, n, b, bl, kd, nslices, Gt, Ht, cb.e32, cb.K,
-                     a, part_s, part_i, codes, Delta, changes, qf);
+  hipLaunchKernelGGL(cd_query_kernel, dim3((unsigned)((m + 3) / 4)), dim3(256), 0, st, m, n, b, bl, kd, Gt, Ht, cb.e32,
+                     cb.K, a, codes, qf);
   return hipGetLastError();
 }
 
-int cd_lattice_slices(int Kpad) { return (Kpad + CDL_CW_WG - 1) / CDL_CW_WG; }
+hipError_t launch_cd_lattice_update(int64_t m, int64_t n, int64_t b, int bl, int kd, double* Gt, const double* Ht,
+                                    const CbTables& cb, const float* a, int32_t* codes, double* Delta,
+                                    int32_t* changes, const float* part_s, const int32_t* part_i, uint32_t* qf,
+                                    hipStream_t st) {
+  if (m <= 0) return hipSuccess;
+  hipLaunchKernelGGL(cd_update_kernel, dim3((unsigned)((m + 3) / 4)), dim3(256), 0, st, m, n, b, bl, kd,
+                     cd_lattice_slices(cb.Kpad), Gt, Ht, cb.e32, cb.K, a, part_s, part_i, codes, Delta, changes, qf);
+  return hipGetLastError();
+}
 
 hipError_t launch_cd_lattice_score(int64_t m, int bl, const uint32_t* tk, const CbTables& cb, const uint32_t* qf,
                                    float* part_s, int32_t* part_i, hipStream_t st) {

@@ -23,12 +23,13 @@ constexpr int LDS64 = BK64 + 2;  // doubles per LDS row
 
 template <typename T, bool VEC>
 __device__ __forceinline__ void load_tile64(const T* __restrict__ P, int64_t ld, int rows, int K, int row0, int k0,
-                                            int t, double (&reg)[2][4]) {
+                                            int t, double (&reg)[2][4], const int32_t* __restrict__ rmap = nullptr) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     int rr = row0 + (t >> 2) + h * 64;
     int kk = k0 + (t & 3) * 4;
-    const T* src = P + (int64_t)rr * ld + kk;
+    const int64_t pr = rmap && rr < rows ? (int64_t)rmap[rr] : (int64_t)rr;   // physical row
+    const T* src = P + pr * ld + kk;
     if (VEC && rr < rows && kk < K) {
       if (sizeof(T) == 8) {
         const double2* s2 = reinterpret_cast<const double2*>(src);
@@ -69,6 +70,8 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
   const int row0 = blockIdx.y * GEMM_BM;
   const int col0 = blockIdx.x * GEMM_BN;
   if (g.lower && col0 >= row0 + GEMM_BM) return;   // whole tile above the diagonal
+  const int M = g.rows ? min(g.M, *g.nrows) : g.M;   // logical rows
+  if (row0 >= M) return;
   const int z = blockIdx.z;
   // split K: chunk z covers k in [z * kchunk, min(K, (z+1) * kchunk)) and
   // writes its partial product to slice z of C (stride sC); otherwise z is the batch
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
 
   const int nk = (Kz + BK64 - 1) / BK64;
   double ra[2][4], rb[2][4];
-  load_tile64<TA, VEC>(A, g.lda, g.M, Kz, row0, 0, t, ra);
+  load_tile64<TA, VEC>(A, g.lda, M, Kz, row0, 0, t, ra, g.rows);
   load_tile64<TB, VEC>(B, g.ldb, g.N, Kz, col0, 0, t, rb);
   store_tile64(As[0], t, ra);
   store_tile64(Bs[0], t, rb);
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) {
-      load_tile64<TA, VEC>(A, g.lda, g.M, Kz, row0, (kt + 1) * BK64, t, ra);
+      load_tile64<TA, VEC>(A, g.lda, M, Kz, row0, (kt + 1) * BK64, t, ra, g.rows);
       load_tile64<TB, VEC>(B, g.ldb, g.N, Kz, col0, (kt + 1) * BK64, t, rb);
     }
 #pragma unroll
@@ -125,12 +128,13 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
     for (int v = 0; v < 4; ++v) {
       // v_mfma_f64_16x16x4_f64 output: lane l holds rows l/16 + 4 v of column l % 16
       const int row = row0 + wr + si * 16 + lg + 4 * v;
-      if (row >= g.M) continue;
+      if (row >= M) continue;
+      const int64_t prow = g.rows ? (int64_t)g.rows[row] : (int64_t)row;
 #pragma unroll
       for (int sj = 0; sj < 4; ++sj) {
         const int col = col0 + wc + sj * 16 + li;
         if (col >= g.N) continue;
-        double* cp = C + (int64_t)row * g.ldc + col;
+        double* cp = C + prow * g.ldc + col;
         if (EPI == EPI_STORE)
           *cp = acc[si][sj][v];
         else
@@ -196,8 +200,29 @@ hipError_t launch_gemm64_splitk(int epi, const Gemm64Args& g0, int splits, doubl
   return hipGetLastError();
 }
 
+// One wave per row: any nonzero among its kd entries appends the row.
+__global__ __launch_bounds__(256) void collect_nonzero_rows_kernel(const double* __restrict__ X, int64_t m, int kd,
+                                                                   int32_t* __restrict__ list,
+                                                                   int32_t* __restrict__ count) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= m) return;
+  bool nz = false;
+  for (int j = lane; j < kd; j += 64) nz = nz || X[i * kd + j] != 0.0;
+  if (__any(nz) && lane == 0) list[atomicAdd(count, 1)] = (int32_t)i;
+}
+
+hipError_t launch_collect_nonzero_rows(const double* X, int64_t m, int kd, int32_t* list, int32_t* count,
+                                       hipStream_t st) {
+  if (m <= 0) return hipSuccess;
+  hipLaunchKernelGGL(collect_nonzero_rows_kernel, dim3((unsigned)((m + 3) / 4)), dim3(256), 0, st, X, m, kd, list,
+                     count);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm64(int epi, bool a_is_f64, const Gemm64Args& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.rows && (!g.nrows || g.ksplit > 1 || g.batch > 1)) return hipErrorInvalidValue;
   if (g.B64) {
     if (!a_is_f64 || g.ksplit > 1) return hipErrorInvalidValue;
     if (epi == EPI_STORE) return launch64<double, EPI_STORE, double>(g, st);

@@ -53,10 +53,18 @@ struct Gemm64Args {
   int ksplit, kchunk;   // split-K (set by launch_gemm64_splitk)
   const double* B64;    // float64 B (with a float64 A) in place of B
   int lower;            // only tiles with some col <= row (the rest of C untouched)
+  // optional row map: logical rows 0 .. *nrows - 1 of A and C are the rows
+  // rows[0 ..] (M bounds *nrows; tiles past it exit); not with split K
+  const int32_t* rows;
+  const int32_t* nrows;
 };
 hipError_t launch_gemm64(int epi, bool a_is_f64, const Gemm64Args& g, hipStream_t st);
 // A float64, split K into `splits` chunks through `part` (splits * M * N doubles).
 hipError_t launch_gemm64_splitk(int epi, const Gemm64Args& g, int splits, double* part, hipStream_t st);
+// Rows (of an m x kd float64 matrix) with some nonzero entry, appended to
+// list in no particular order, their number added to *count.
+hipError_t launch_collect_nonzero_rows(const double* X, int64_t m, int kd, int32_t* list, int32_t* count,
+                                       hipStream_t st);
 
 // ------------------------------------------------------------ codebook ----
 // Device tables derived from the host codebook.
@@ -120,10 +128,16 @@ hipError_t launch_cd_scalar_tile(int64_t m, int64_t n, int64_t j0, int kd, const
 // fragments, passed from each block's update to the next block's scoring.
 hipError_t launch_cd_lattice_tkeys(int nb, int kd, const double* Ht, const CbTables& cb, uint32_t* tk,
                                    hipStream_t st);
-hipError_t launch_cd_lattice_block(int64_t m, int64_t n, int64_t b, int bl, int kd, double* Gt, const double* Ht,
-                                   const uint32_t* tk, const CbTables& cb, const float* a, int32_t* codes,
-                                   double* Delta, int32_t* changes, float* part_s, int32_t* part_i, uint32_t* qf,
-                                   hipStream_t st);
+// One block of a tile: the first block's query fragments (bl = 0 only), then
+// launch_cd_lattice_score, then the update (merge, exact re-scoring, move,
+// gradient update, next block's query).
+hipError_t launch_cd_lattice_query(int64_t m, int64_t n, int64_t b, int bl, int kd, const double* Gt,
+                                   const double* Ht, const CbTables& cb, const float* a, const int32_t* codes,
+                                   uint32_t* qf, hipStream_t st);
+hipError_t launch_cd_lattice_update(int64_t m, int64_t n, int64_t b, int bl, int kd, double* Gt, const double* Ht,
+                                    const CbTables& cb, const float* a, int32_t* codes, double* Delta,
+                                    int32_t* changes, const float* part_s, const int32_t* part_i, uint32_t* qf,
+                                    hipStream_t st);
 int cd_lattice_slices(int Kpad);
 // The scoring pass alone (codeword slices x row groups -> part_s / part_i).
 hipError_t launch_cd_lattice_score(int64_t m, int bl, const uint32_t* tk, const CbTables& cb, const uint32_t* qf,
