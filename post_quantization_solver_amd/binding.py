@@ -360,8 +360,10 @@ def vamp_step(R1, gamma1, beta, ytil, s, V, cb, row_scale, row_offset, damping=0
     return dict(xhat1=xhat, eta1=eta1, gamma2=gamma2, r2=r2, fallback=fb)
 
 
-def map_codes(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=None, W=None, group=None):
-    """Marginal MAP codes (mpq_map)."""
+def map_codes(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=None, W=None, group=None,
+              scan_denoiser=False):
+    """Marginal MAP codes (mpq_map); scan_denoiser keeps the codebook scan for
+    E8 prefix codebooks too."""
     import torch
     m, n = R1.shape
     E = _host_codebook(cb)
@@ -373,7 +375,7 @@ def map_codes(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=
         _dev(W, torch.float32, "W", (m, n))
     codes = torch.empty((m, n // d), dtype=torch.int32, device=R1.device)
     ws = workspace if workspace is not None else _workspace(m, n, n, K, d, R1.device)
-    op, _keep = _opts(anchor_tau=anchor_tau, anchor_w=W, group=group)
+    op, _keep = _opts(anchor_tau=anchor_tau, anchor_w=W, group=group, scan_denoiser=scan_denoiser)
     rc = load_library().mpq_map(_ptr(R1), _ptr(gamma1), m, n, E.ctypes.data_as(ctypes.c_void_p), K, d,
                                 _ptr(row_scale), _ptr(row_offset), op, _ptr(codes), _ptr(ws), ws.numel(), _stream())
     _check(rc, "mpq_map")

@@ -29,6 +29,10 @@ hipError_t launch_beta_lin(int64_t, const float*, const float*, float*, float*, 
 hipError_t launch_fill_i32(int32_t*, int64_t, int32_t, hipStream_t);
 bool e8_prefix_detect(const float* cb, int64_t K, E8Prefix& P);
 int64_t e8_transitions(const E8Prefix& P);
+void e8_key_table(const float* cb, int64_t K, uint32_t* keys, int32_t* idx);
+hipError_t launch_nearest_e8(const float* R, int64_t m, int64_t n, const E8Prefix& P, const uint32_t* keys,
+                             const int32_t* kidx, int K, const float* a, const float* o, int32_t* codes,
+                             hipStream_t st);
 hipError_t launch_denoise_e8dp(const float* R1, const float* gamma1, int64_t m, int64_t n, const E8Prefix& P,
                                const float* a, const float* o, float* xhat, float* vblk, int32_t* flag,
                                hipStream_t st);
@@ -89,7 +93,7 @@ struct Layout {
 enum Region {
   R_VS, R_VST, R_YTIL, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI,
   R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_SPLIT, R_TKEY, R_QF, R_VSP, R_VSTP, R_R2P, R_ZP, R_ANCH,
-  R_LAM, R_CTMP, R_GDIAG, R_MROWS, R_COUNT
+  R_LAM, R_CTMP, R_GDIAG, R_MROWS, R_E8KEY, R_COUNT
 };
 
 static_assert(R_COUNT <= (int)(sizeof(Layout::off) / sizeof(size_t)), "Layout::off holds every region");
@@ -146,6 +150,8 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, bool g
   sz[R_LAM] = greedy ? (size_t)n * n * f64 : 0;
   sz[R_CTMP] = greedy ? chol_tmp_doubles(n) * f64 : 0;
   sz[R_GDIAG] = greedy ? (size_t)KD * KD * f64 : 0;
+  // d = 8: codebook keys in lexicographic order and their indices (E8 prefix codebooks)
+  sz[R_E8KEY] = d == 8 ? (size_t)2 * K * sizeof(uint32_t) : 0;
   // per CD row group: the rows that moved in the current tile, and their count
   sz[R_MROWS] = (size_t)CD_GROUPS_MAX * ((m + CD_GROUPS_MAX - 1) / CD_GROUPS_MAX + 64) * sizeof(int32_t);
   size_t o = 0;
@@ -352,6 +358,12 @@ int upload_codebook(Ctx& c, const float* cb) {
   MPQ_TRY(hipMemcpyAsync(c.p(R_E32), e32.data(), e32.size() * sizeof(float), hipMemcpyHostToDevice, c.st));
   MPQ_TRY(hipMemcpyAsync(c.p(R_QK), qk.data(), qk.size() * sizeof(uint16_t), hipMemcpyHostToDevice, c.st));
   MPQ_TRY(hipMemcpyAsync(c.p(R_PV), pv.data(), pv.size() * sizeof(uint16_t), hipMemcpyHostToDevice, c.st));
+  std::vector<uint32_t> e8k;
+  if (c.e8dp) {
+    e8k.resize((size_t)2 * L.K);
+    e8_key_table(cb, L.K, e8k.data(), reinterpret_cast<int32_t*>(e8k.data() + L.K));
+    MPQ_TRY(hipMemcpyAsync(c.p(R_E8KEY), e8k.data(), e8k.size() * sizeof(uint32_t), hipMemcpyHostToDevice, c.st));
+  }
   MPQ_TRY(hipStreamSynchronize(c.st));
   return MPQ_OK;
 }
@@ -369,6 +381,11 @@ GemmArgs gemm(int M, int N, int K, const float* A, int64_t lda, const float* B, 
 
 hipError_t nearest(const Ctx& c, const float* R, int32_t* codes, const float* a, const float* o) {
   if (c.L.d == 1) return launch_nearest_scalar(R, c.L.m, c.L.n, c.cb, a, o, codes, c.st);
+  if (c.e8dp) {
+    const uint32_t* keys = reinterpret_cast<const uint32_t*>(c.p(R_E8KEY));
+    return launch_nearest_e8(R, c.L.m, c.L.n, c.e8p, keys, reinterpret_cast<const int32_t*>(keys + c.L.K),
+                             (int)c.L.K, a, o, codes, c.st);
+  }
   return launch_nearest_lattice(R, c.L.m, c.L.n, c.cb, a, o, codes, c.st);
 }
 

@@ -113,6 +113,26 @@ int64_t e8_transitions(const E8Prefix& P) {
   return t;
 }
 
+// Lexicographic key of an E8 point: the nibbles 2 x_j + 6 (j = 1 .. 8, the
+// first in the top nibble), so that unsigned order is lexicographic order.
+uint32_t e8_key(const float* x) {
+  uint32_t k = 0;
+  for (int j = 0; j < 8; ++j) k = k * 16u + (uint32_t)((int)lrintf(2.f * x[j]) + 6);
+  return k;
+}
+
+// The codebook's keys in ascending order (keys[0 .. K)) and the codeword
+// index of each (idx[0 .. K)), for the nearest-codeword pass to name its winner.
+void e8_key_table(const float* cb, int64_t K, uint32_t* keys, int32_t* idx) {
+  std::vector<std::pair<uint32_t, int32_t>> kv((size_t)K);
+  for (int64_t k = 0; k < K; ++k) kv[(size_t)k] = {e8_key(cb + k * 8), (int32_t)k};
+  std::sort(kv.begin(), kv.end());
+  for (int64_t k = 0; k < K; ++k) {
+    keys[k] = kv[(size_t)k].first;
+    idx[k] = kv[(size_t)k].second;
+  }
+}
+
 // ------------------------------------------------------------ device side
 
 constexpr int E8DP_WAVES = 4;   // waves per workgroup, four queries per wave
@@ -375,6 +395,189 @@ hipError_t launch_denoise_e8dp(const float* R1, const float* gamma1, int64_t m, 
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(e8dp_kernel, dim3((unsigned)wgs), dim3(64 * E8DP_WAVES), 0, st, R1, gamma1, m, n, a, o, P, xhat,
                      vblk, flag + 64, flag);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ nearest codeword
+
+// Like row_read, but lanes whose source is outside the row keep `old`.
+template <int CTRL>
+__device__ __forceinline__ double row_read_or(double v, double old) {
+  if constexpr (CTRL < 0) {
+    return v;
+  } else {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v), ob = __builtin_bit_cast(uint64_t, old);
+    const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)ob, (int)(uint32_t)b, CTRL, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(ob >> 32), (int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, false);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+  }
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t row_read_or_u(uint32_t v, uint32_t old) {
+  if constexpr (CTRL < 0) {
+    return v;
+  } else {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, 0xf, 0xf, false);
+  }
+}
+
+// (score, key) kept if larger, or equal with a smaller (lexicographically earlier) key.
+__device__ __forceinline__ void keep_best(double v, uint32_t kv, double& bs, uint32_t& bk) {
+  const bool b = v > bs || (v == bs && kv < bk);
+  bs = b ? v : bs;
+  bk = b ? kv : bk;
+}
+// Across final states: score, then the smaller norm, then the smaller key
+// (codebook order is (norm, lexicographic)).
+__device__ __forceinline__ void keep_best3(double v, int nv, uint32_t kv, double& bs, int& bn, uint32_t& bk) {
+  const bool b = v > bs || (v == bs && (nv < bn || (nv == bn && kv < bk)));
+  bs = b ? v : bs;
+  bn = b ? nv : bn;
+  bk = b ? kv : bk;
+}
+
+// Max-sum pass of one class: the best prefix score sum_j f_j(x_j) into each
+// state and its key (the prefix's nibbles); merges keep the lexicographically
+// earlier prefix on ties, which is the earlier codeword since the merged paths
+// share every later coordinate.  Folds the accepting states into (bs, bn, bk).
+template <bool HALF, bool LCLASS>
+__device__ __forceinline__ void e8_nearest_pass(const int j, const E8RowCoef& cf, const E8Prefix& P, double& bs,
+                                                int& bn, uint32_t& bk) {
+  constexpr int NK = HALF ? 6 : 7;
+  constexpr int KO = HALF ? 7 : 0;
+  const int qi = j & 7;
+  // half class: a source below Qi = 0 of the lane's s block is no state
+  const double m1 = qi >= 1 ? 0.0 : -INFINITY, m3 = qi >= 3 ? 0.0 : -INFINITY;
+  double sl = -INFINITY, se = j == 0 ? 0.0 : -INFINITY, sg = -INFINITY;
+  uint32_t kl = ~0u, ke = j == 0 ? 0u : ~0u, kg = ~0u;
+  static_for<1, 9>([&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = decltype(pc)::value, c = p - 1;
+    constexpr bool live = LCLASS || p == 1;
+    int l2 = P.L2[c];
+    asm volatile("" : "+s"(l2));
+    double nl = -INFINITY, ne = -INFINITY, ng = -INFINITY;
+    uint32_t ql = ~0u, qe = ~0u, qg = ~0u;
+    static_for<0, NK>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int CT = e8_ctrl(HALF, p, k, true);
+      constexpr uint32_t nib = (uint32_t)(e8_twice_value(HALF, k) + 6);
+      double f = cf.c[c][KO + k];
+      if constexpr (HALF && e8_qi_step(k) == 1) f += m1;
+      if constexpr (HALF && e8_qi_step(k) == 3) f += m3;
+      keep_best(row_read_or<CT>(sl, -INFINITY) + f, row_read_or_u<CT>(kl, ~0u) * 16u + nib, nl, ql);
+      keep_best(row_read_or<CT>(sg, -INFINITY) + f, row_read_or_u<CT>(kg, ~0u) * 16u + nib, ng, qg);
+      if constexpr (live) {
+        const int ck = e8_cmp(e8_twice_value(HALF, k), l2);
+        const double v = row_read_or<CT>(se, -INFINITY) + f;
+        const uint32_t kv = row_read_or_u<CT>(ke, ~0u) * 16u + nib;
+        if (ck == 0)
+          keep_best(v, kv, nl, ql);
+        else if (ck == 1)
+          keep_best(v, kv, ne, qe);
+        else
+          keep_best(v, kv, ng, qg);
+      }
+    });
+    sl = nl;
+    se = ne;
+    sg = ng;
+    kl = ql;
+    ke = qe;
+    kg = qg;
+  });
+  const int norm = HALF ? 2 * qi + 2 : j;
+  const bool valid = HALF ? (qi <= 5 && j < 8) : ((j & 1) == 0 && j <= 12);
+  if (valid && norm <= P.qlast) {
+    keep_best3(sl, norm, kl, bs, bn, bk);
+    keep_best3(se, norm, ke, bs, bn, bk);
+    if (norm < P.qlast) keep_best3(sg, norm, kg, bs, bn, bk);
+  }
+}
+
+// Nearest codeword of every block (argmin ||r - (a e + o)||^2 = argmax of
+// sum_j e_j r'_j - e_j^2 / 2, ties to the lowest index), four blocks per wave.
+__global__ __launch_bounds__(256) void e8_nearest_kernel(const float* __restrict__ R, int64_t m, int64_t n,
+                                                         const float* __restrict__ a, const float* __restrict__ o,
+                                                         E8Prefix P, const uint32_t* __restrict__ keys,
+                                                         const int32_t* __restrict__ kidx, int K,
+                                                         int32_t* __restrict__ codes) {
+  __shared__ E8RowCoef coef[E8DP_WAVES * 4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row = lane >> 4, j = lane & 15;
+  E8RowCoef& cf = coef[wave * 4 + row];
+  const int64_t B = n / 8;
+  const int64_t total = m * B;
+  const bool lhalf = (P.L2[0] & 1) != 0;
+  const double xj = j < 7 ? (double)(j - 3) : (double)(j - 7) - 2.5;
+  const int64_t q = ((int64_t)blockIdx.x * E8DP_WAVES + wave) * 4 + row;
+  const bool active = q < total;
+  int64_t i = 0, b = 0;
+  double ai = 1.0, oi = 0.0;
+  if (active) {
+    i = q / B;
+    b = q - i * B;
+    ai = (double)a[i];
+    oi = (double)o[i];
+  }
+  const float rv = active && j < 8 ? R[i * n + b * 8 + j] : 0.f;
+  if (j < 8) cf.c[j][13] = ((double)rv - oi) / ai;
+  wave_sync();
+  if (j < 13) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) cf.c[c][j] = xj * fma(-0.5, xj, cf.c[c][13]);   // x r' - x^2 / 2
+  }
+  wave_sync();
+  double bs = -INFINITY;
+  int bn = 1 << 30;
+  uint32_t bk = ~0u;
+  if (lhalf) {
+    e8_nearest_pass<false, false>(j, cf, P, bs, bn, bk);
+    reload_barrier();
+    e8_nearest_pass<true, true>(j, cf, P, bs, bn, bk);
+  } else {
+    e8_nearest_pass<false, true>(j, cf, P, bs, bn, bk);
+    reload_barrier();
+    e8_nearest_pass<true, false>(j, cf, P, bs, bn, bk);
+  }
+#pragma unroll
+  for (int r = 8; r >= 1; r >>= 1) {
+    const double os = r == 8 ? row_read<DPP_ROW_ROR + 8>(bs)
+                             : (r == 4 ? row_read<DPP_ROW_ROR + 4>(bs)
+                                       : (r == 2 ? row_read<DPP_ROW_ROR + 2>(bs) : row_read<DPP_ROW_ROR + 1>(bs)));
+    const int on = r == 8 ? __builtin_amdgcn_update_dpp(0, bn, DPP_ROW_ROR + 8, 0xf, 0xf, true)
+                          : (r == 4 ? __builtin_amdgcn_update_dpp(0, bn, DPP_ROW_ROR + 4, 0xf, 0xf, true)
+                                    : (r == 2 ? __builtin_amdgcn_update_dpp(0, bn, DPP_ROW_ROR + 2, 0xf, 0xf, true)
+                                              : __builtin_amdgcn_update_dpp(0, bn, DPP_ROW_ROR + 1, 0xf, 0xf, true)));
+    const uint32_t ok = r == 8 ? row_read_or_u<DPP_ROW_ROR + 8>(bk, 0u)
+                               : (r == 4 ? row_read_or_u<DPP_ROW_ROR + 4>(bk, 0u)
+                                         : (r == 2 ? row_read_or_u<DPP_ROW_ROR + 2>(bk, 0u)
+                                                   : row_read_or_u<DPP_ROW_ROR + 1>(bk, 0u)));
+    keep_best3(os, on, ok, bs, bn, bk);
+  }
+  if (!active || j != 0) return;
+  // the winner's codebook index: lower bound of its key in the sorted keys
+  int lo = 0, hi = K;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (keys[mid] < bk)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  codes[i * B + b] = lo < K && keys[lo] == bk ? kidx[lo] : -1;
+}
+
+hipError_t launch_nearest_e8(const float* R, int64_t m, int64_t n, const E8Prefix& P, const uint32_t* keys,
+                             const int32_t* kidx, int K, const float* a, const float* o, int32_t* codes,
+                             hipStream_t st) {
+  const int64_t total = m * (n / 8);
+  if (total <= 0) return hipSuccess;
+  const int64_t per_wg = (int64_t)E8DP_WAVES * 4;
+  const int64_t wgs = (total + per_wg - 1) / per_wg;
+  if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(e8_nearest_kernel, dim3((unsigned)wgs), dim3(64 * E8DP_WAVES), 0, st, R, m, n, a, o, P, keys,
+                     kidx, K, codes);
   return hipGetLastError();
 }
 

@@ -131,3 +131,49 @@ def test_e8dp_ragged_and_frozen(K):
     for t, k in enumerate(live):
         assert rel_vec(xh[k], xr[t]) < SOFT_RTOL
         assert rel_scalar(vt[k].astype(np.float64).sum(), vr[t].sum()) < SOFT_RTOL
+
+
+def _e8_map(R1, E, a, o, scan=False):
+    import post_quantization_solver_amd as mpq
+    g1 = np.ones(R1.shape[0], np.float32)
+    return host(mpq.map_codes(dev(R1), dev(g1), E, dev(a), dev(o), scan_denoiser=scan)).astype(np.int64)
+
+
+def _oracle_nearest(R1, E, a, o):
+    return np.stack([O.nearest_codeword(R1[k].astype(np.float64), O.row_codewords(E, a[k], o[k]), 8)
+                     for k in range(R1.shape[0])])
+
+
+@pytest.mark.parametrize("K", [1, 240, 1000, 2401, 65536])
+def test_e8_nearest_matches_oracle(K):
+    """The max-sum pass over the E8 automaton (round to nearest and the
+    marginal MAP) names the oracle's nearest codeword, ties to the lowest
+    index, on 15 blocks per row (a partly empty last wave) at several scales."""
+    E = S.e8_codebook(K)
+    g = np.random.default_rng(K)
+    m, n = 4, 120
+    a = (0.4 + g.random(m)).astype(np.float32)
+    o = (0.1 * g.standard_normal(m)).astype(np.float32)
+    scale = np.array([0.6, 1.3, 3.0, 8.0])[:, None]
+    R1 = (g.standard_normal((m, n)) * scale * a[:, None] + o[:, None]).astype(np.float32)
+    got = _e8_map(R1, E, a, o)
+    ref = _oracle_nearest(R1, E, a, o)
+    print(f"[e8 nearest] K={K}: {np.mean(got == ref):.4f} agree", flush=True)
+    assert np.array_equal(got, ref)
+    scan = _e8_map(R1, E, a, o, scan=True)
+    assert np.mean(scan == ref) >= 0.99
+
+
+def test_e8_nearest_exact_ties():
+    """Points equidistant from several codewords: the lowest codebook index
+    wins, as in the oracle (a = 1, o = 0, dyadic coordinates, exact in float64)."""
+    E = S.e8_codebook(65536)
+    rows = [np.zeros(8), [0.5, 0.5, 0, 0, 0, 0, 0, 0], [0.25] * 8, [-0.5, 0.5, 0, 0, 0, 0, 0, 0],
+            [0.75, 0.25, 0.25, 0.25, 0.25, 0.25, 0.25, 0.25], [1, 0, 0, 0, 0, 0, 0, 0], [0.5] * 8,
+            [-1.5, 0, 0.5, 0, 0, 0, 0, 0]]
+    R1 = np.asarray(rows, np.float32).reshape(1, -1)
+    a = np.ones(1, np.float32)
+    o = np.zeros(1, np.float32)
+    got = _e8_map(R1, E, a, o)
+    ref = _oracle_nearest(R1, E, a, o)
+    assert np.array_equal(got, ref), (got, ref)
