@@ -23,7 +23,9 @@
 namespace mpq {
 
 constexpr int CDL_ROWS_WAVE = 64;            // 4 row subtiles per wave
-constexpr int CDL_ROWS_WG = 4 * CDL_ROWS_WAVE;
+constexpr int CDL_WAVES = 4;                 // waves per scoring workgroup (they share its key slice)
+constexpr int CDL_ROWS_WG = CDL_WAVES * CDL_ROWS_WAVE;
+constexpr int CDU_WAVES = 4;                 // rows (one per wave) per query / update workgroup
 constexpr int CDL_CW_WG = 512;               // codewords per workgroup slice
 
 // t fragments of one CD tile: for block bl of the tile and codeword cw, the
@@ -84,30 +86,30 @@ __device__ __forceinline__ void cd_query_row(int lane, int64_t i, int bl, int kd
 
 // Query fragments for the first block of a tile (later blocks get theirs from
 // the previous block's update).  One wave per row.
-__global__ __launch_bounds__(256) void cd_query_kernel(int64_t m, int64_t n, int64_t b, int bl, int kd,
+__global__ __launch_bounds__(64 * CDU_WAVES) void cd_query_kernel(int64_t m, int64_t n, int64_t b, int bl, int kd,
                                                        const double* __restrict__ Gt, const double* __restrict__ Ht,
                                                        const float* __restrict__ e32, int K,
                                                        const float* __restrict__ a,
                                                        const int32_t* __restrict__ codes,
                                                        uint32_t* __restrict__ qf) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t i = (int64_t)blockIdx.x * CDU_WAVES + (threadIdx.x >> 6);
   if (i >= m) return;
   const double gp = Gt[i * kd + 8 * bl + (lane & 7)];
   cd_query_row(lane, i, bl, kd, gp, Ht, e32 + (int64_t)safe_code(codes[i * (n / 8) + b], K) * 8, (double)a[i], qf);
 }
 
-// A score with its 2 low mantissa bits replaced by the codeword's position v
-// in the lane's group of 4 (a change of at most 3 ulp): one minimum then
-// ranks the lane's candidates and names the winner's position.
-__device__ __forceinline__ float tag2(float x, uint32_t v) {
-  return __uint_as_float((__float_as_uint(x) & 0xfffffffcu) | v);
+// A score with its 3 low mantissa bits replaced by the codeword's position
+// (step parity, v) in the lane's 8 candidates of a step pair (a change of at
+// most 7 ulp): one minimum then ranks them and names the winner's position.
+__device__ __forceinline__ float tag3(float x, uint32_t v) {
+  return __uint_as_float((__float_as_uint(x) & 0xfffffff8u) | v);
 }
 
 // grid: (slices, row groups).  part_s / part_i: [m][slices][2] (best, second).
 // The float32 scores only rank candidates; the update kernel re-evaluates the
 // two best of every slice exactly in float64.
-__global__ __launch_bounds__(256) void cd_score_kernel(int64_t m, int bl, const uint32_t* __restrict__ keys,
+__global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int bl, const uint32_t* __restrict__ keys,
                                                        const v4u* __restrict__ tk, int Kpad,
                                                        const v4u* __restrict__ qf, float* __restrict__ part_s,
                                                        int32_t* __restrict__ part_i) {
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void cd_score_kernel(int64_t m, int bl, const 
   // key fragments of this slice: lanes g < 3 carry e, lanes g = 3 the t(e) terms
   const v4u* kv = reinterpret_cast<const v4u*>(keys);
   const v4u* tkb = tk + (int64_t)bl * Kpad + cw_base;
-  for (int f = t; f < (ncw / 16) * 64; f += 256) {
+  for (int f = t; f < (ncw / 16) * 64; f += 64 * CDL_WAVES) {
     const int st = f >> 6, ln = f & 63;
     v4u w = (ln >> 4) < 3 ? kv[(int64_t)(cw_base / 16 + st) * 64 + ln] : tkb[st * 16 + (ln & 15)];
     reinterpret_cast<v4u*>(lds_key)[f] = w;
@@ -143,31 +145,34 @@ __global__ __launch_bounds__(256) void cd_score_kernel(int64_t m, int bl, const 
     best[q] = INFINITY;
     bst[q] = 0;
   }
-  // lane (j, g) sees codewords 16 st + 4 g + v of the slice for row j; it keeps
-  // the least tagged score and the step where it last strictly improved, so
-  // ties go to the earliest step and then to the lowest v
+  // lane (j, g) sees codewords 16 st + 4 g + v of the slice for row j, two
+  // steps at a time (ncw / 16 is even: Kpad is a multiple of 128); it keeps
+  // the least tagged score and the pair where it last strictly improved, so
+  // ties go to the earliest pair, then step, then the lowest v
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
   const v4u* kq = reinterpret_cast<const v4u*>(lds_key);
-#pragma unroll 2
-  for (int st = 0; st < ncw / 16; ++st) {
-    const v4u k0 = kq[st * 64 + lane];
+  for (int sp = 0; sp < ncw / 32; ++sp) {
+    const v4u k0 = kq[(2 * sp) * 64 + lane];
+    const v4u k1 = kq[(2 * sp + 1) * 64 + lane];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      v4f sc = mfma_bf16_16x16x32(k0, qop[q], zero4);
-      // IEEE minimum (v_minimum3_f32): the scores are finite, so it needs no
-      // NaN quieting of its operands
-      const float m4 = __builtin_elementwise_minimum(
-          __builtin_elementwise_minimum(__builtin_elementwise_minimum(tag2(sc[0], 0u), tag2(sc[1], 1u)),
-                                        tag2(sc[2], 2u)),
-          tag2(sc[3], 3u));
-      bst[q] = m4 < best[q] ? st : bst[q];
-      best[q] = __builtin_elementwise_minimum(best[q], m4);
+      const v4f s0 = mfma_bf16_16x16x32(k0, qop[q], zero4);
+      const v4f s1 = mfma_bf16_16x16x32(k1, qop[q], zero4);
+      // IEEE minimum, four v_minimum3_f32 with the running best (the scores are finite)
+      float mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(tag3(s0[0], 0u), tag3(s0[1], 1u)),
+                                               tag3(s0[2], 2u));
+      mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, tag3(s0[3], 3u)), tag3(s1[0], 4u));
+      mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, tag3(s1[1], 5u)), tag3(s1[2], 6u));
+      const float nb = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, tag3(s1[3], 7u)), best[q]);
+      bst[q] = nb < best[q] ? sp : bst[q];
+      best[q] = nb;
     }
   }
   // top 2 of the row's four lane-bests (lanes j, j+16, j+32, j+48)
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int idx = isfinite(best[q]) ? cw_base + bst[q] * 16 + 4 * g + (int)(__float_as_uint(best[q]) & 3u)
+    const uint32_t tg = __float_as_uint(best[q]) & 7u;
+    const int idx = isfinite(best[q]) ? cw_base + (2 * bst[q] + (int)(tg >> 2)) * 16 + 4 * g + (int)(tg & 3u)
                                       : 0x7fffffff;
     Cand c1 = {best[q], idx};
     Cand c2 = {INFINITY, 0x7fffffff};
@@ -195,7 +200,7 @@ __global__ __launch_bounds__(256) void cd_score_kernel(int64_t m, int bl, const 
 //   dF(c) = 1/2 d^T G d - d^T g,   d = a (e_c - e_x)
 // is one product per lane and a wave sum.
 constexpr int CD_COLS_LANE = 4;   // tile columns per lane in the gradient update (tile width <= 256)
-__global__ __launch_bounds__(256) void cd_update_kernel(int64_t m, int64_t n, int64_t b, int bl, int kd, int nslices,
+__global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, int64_t n, int64_t b, int bl, int kd, int nslices,
                                                         double* __restrict__ Gt, const double* __restrict__ Ht,
                                                         const float* __restrict__ e32, int K,
                                                         const float* __restrict__ a,
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(256) void cd_update_kernel(int64_t m, int64_t n, in
                                                         int32_t* __restrict__ codes, double* __restrict__ Delta,
                                                         int32_t* __restrict__ changes, uint32_t* __restrict__ qf) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t i = (int64_t)blockIdx.x * CDU_WAVES + (threadIdx.x >> 6);
   if (i >= m) return;
   const int64_t B = n / 8;
   const int p = lane >> 3, k = lane & 7;
@@ -363,7 +368,7 @@ hipError_t launch_cd_lattice_query(int64_t m, int64_t n, int64_t b, int bl, int 
                                    const double* Ht, const CbTables& cb, const float* a, const int32_t* codes,
                                    uint32_t* qf, hipStream_t st) {
   if (m <= 0) return hipSuccess;
-  hipLaunchKernelGGL(cd_query_kernel, dim3((unsigned)((m + 3) / 4)), dim3(256), 0, st, m, n, b, bl, kd, Gt, Ht, cb.e32,
+  hipLaunchKernelGGL(cd_query_kernel, dim3((unsigned)((m + CDU_WAVES - 1) / CDU_WAVES)), dim3(64 * CDU_WAVES), 0, st, m, n, b, bl, kd, Gt, Ht, cb.e32,
                      cb.K, a, codes, qf);
   return hipGetLastError();
 }
@@ -373,7 +378,7 @@ hipError_t launch_cd_lattice_update(int64_t m, int64_t n, int64_t b, int bl, int
                                     int32_t* changes, const float* part_s, const int32_t* part_i, uint32_t* qf,
                                     hipStream_t st) {
   if (m <= 0) return hipSuccess;
-  hipLaunchKernelGGL(cd_update_kernel, dim3((unsigned)((m + 3) / 4)), dim3(256), 0, st, m, n, b, bl, kd,
+  hipLaunchKernelGGL(cd_update_kernel, dim3((unsigned)((m + CDU_WAVES - 1) / CDU_WAVES)), dim3(64 * CDU_WAVES), 0, st, m, n, b, bl, kd,
                      cd_lattice_slices(cb.Kpad), Gt, Ht, cb.e32, cb.K, a, part_s, part_i, codes, Delta, changes, qf);
   return hipGetLastError();
 }
@@ -383,7 +388,7 @@ hipError_t launch_cd_lattice_score(int64_t m, int bl, const uint32_t* tk, const 
   if (m <= 0) return hipSuccess;
   const int nslices = cd_lattice_slices(cb.Kpad);
   dim3 g1((unsigned)nslices, (unsigned)((m + CDL_ROWS_WG - 1) / CDL_ROWS_WG));
-  hipLaunchKernelGGL(cd_score_kernel, g1, dim3(256), 0, st, m, bl, cb.qk_keys, reinterpret_cast<const v4u*>(tk),
+  hipLaunchKernelGGL(cd_score_kernel, g1, dim3(64 * CDL_WAVES), 0, st, m, bl, cb.qk_keys, reinterpret_cast<const v4u*>(tk),
                      cb.Kpad, reinterpret_cast<const v4u*>(qf), part_s, part_i);
   return hipGetLastError();
 }
