@@ -63,6 +63,25 @@ thread_local hipError_t g_last_hip_error = hipSuccess;
     }                                    \
   } while (0)
 
+// Launcher fn(args..., t0, t1) of a single kernel that takes its start and
+// end events itself (hipExtLaunchKernel: the kernel's own begin and end, free
+// of the launch gap that stream-recorded events include).
+#define TIMED_KERNEL(c, cat, fn, ...)                               \
+  do {                                                              \
+    if ((c).timed(cat)) {                                           \
+      Prof::Ev ev_{nullptr, nullptr, (cat)};                        \
+      MPQ_TRY(hipEventCreate(&ev_.a));                              \
+      if (hipEventCreate(&ev_.b) != hipSuccess) {                   \
+        (void)hipEventDestroy(ev_.a);                               \
+        return MPQ_EHIP;                                            \
+      }                                                             \
+      (c).prof.evs.push_back(ev_);                                  \
+      MPQ_TRY(fn(__VA_ARGS__, ev_.a, ev_.b));                       \
+    } else {                                                        \
+      MPQ_TRY(fn(__VA_ARGS__, nullptr, nullptr));                   \
+    }                                                               \
+  } while (0)
+
 // Run a launch expression; with profiling on for `cat`, bracket it with
 // events recorded on the call's stream.
 #define TIMED(c, cat, expr)                                         \
@@ -644,7 +663,8 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
               if (bl == 0)
                 TIMED(c, MPQ_PROF_CD_SEARCH,
                       launch_cd_lattice_query(q.mg, L.n, b, bl, kw, q.Gt, Ht, c.cb, q.a, q.codes, q.qf, c.st));
-              TIMED(c, MPQ_PROF_CD_SCORE, launch_cd_lattice_score(q.mg, bl, q.tk, c.cb, q.qf, q.ps, q.pi, c.st));
+              TIMED_KERNEL(c, MPQ_PROF_CD_SCORE, launch_cd_lattice_score, q.mg, bl, q.tk, c.cb, q.qf, q.ps, q.pi,
+                           c.st);
               TIMED(c, MPQ_PROF_CD_SEARCH,
                     launch_cd_lattice_update(q.mg, L.n, b, bl, kw, q.Gt, Ht, c.cb, q.a, q.codes, q.Dl, q.chg, q.ps,
                                              q.pi, q.qf, c.st));
@@ -727,8 +747,8 @@ int run_greedy(Ctx& c, const float* W, const float* a, const float* o, int32_t* 
       TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_lattice_tkeys(kw / 8, kw, Gd, c.cb, tk, c.st));
       TIMED(c, MPQ_PROF_CD_SEARCH, launch_greedy_query(L.m, L.n, j0, P, Lam, W, a, o, qf, c.st));
       for (int bl = 0; bl < kw / 8; ++bl) {
-        TIMED(c, MPQ_PROF_CD_SCORE,
-              launch_cd_lattice_score(L.m, bl, tk, c.cb, qf, c.p(R_PS), c.pi(R_PI), c.st));
+        TIMED_KERNEL(c, MPQ_PROF_CD_SCORE, launch_cd_lattice_score, L.m, bl, tk, c.cb, qf, c.p(R_PS), c.pi(R_PI),
+                     c.st);
         TIMED(c, MPQ_PROF_CD_SEARCH,
               launch_greedy_update(L.m, L.n, j0, j0 / 8 + bl, bl, kw, P, Lam, Rtile, W, c.cb, a, o, c.p(R_PS),
                                    c.pi(R_PI), codes, En, qf, c.st));

@@ -16,6 +16,7 @@
 // H and the residual are float64) and moves the block only on a strict
 // decrease.
 #include <math.h>
+#include <hip/hip_ext.h>
 #include "mpq_device.h"
 #include "internal.h"
 #include "lattice_search.h"
@@ -384,12 +385,13 @@ hipError_t launch_cd_lattice_update(int64_t m, int64_t n, int64_t b, int bl, int
 }
 
 hipError_t launch_cd_lattice_score(int64_t m, int bl, const uint32_t* tk, const CbTables& cb, const uint32_t* qf,
-                                   float* part_s, int32_t* part_i, hipStream_t st) {
+                                   float* part_s, int32_t* part_i, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
   if (m <= 0) return hipSuccess;
   const int nslices = cd_lattice_slices(cb.Kpad);
   dim3 g1((unsigned)nslices, (unsigned)((m + CDL_ROWS_WG - 1) / CDL_ROWS_WG));
-  hipLaunchKernelGGL(cd_score_kernel, g1, dim3(64 * CDL_WAVES), 0, st, m, bl, cb.qk_keys, reinterpret_cast<const v4u*>(tk),
-                     cb.Kpad, reinterpret_cast<const v4u*>(qf), part_s, part_i);
+  // t0 / t1 (optional) take the kernel's own start and end times
+  hipExtLaunchKernelGGL(cd_score_kernel, g1, dim3(64 * CDL_WAVES), 0, st, t0, t1, 0u, m, bl, cb.qk_keys,
+                        reinterpret_cast<const v4u*>(tk), cb.Kpad, reinterpret_cast<const v4u*>(qf), part_s, part_i);
   return hipGetLastError();
 }
 

@@ -141,7 +141,8 @@ hipError_t launch_cd_lattice_update(int64_t m, int64_t n, int64_t b, int bl, int
 int cd_lattice_slices(int Kpad);
 // The scoring pass alone (codeword slices x row groups -> part_s / part_i).
 hipError_t launch_cd_lattice_score(int64_t m, int bl, const uint32_t* tk, const CbTables& cb, const uint32_t* qf,
-                                   float* part_s, int32_t* part_i, hipStream_t st);
+                                   float* part_s, int32_t* part_i, hipStream_t st, hipEvent_t t0 = nullptr,
+                                   hipEvent_t t1 = nullptr);
 
 // ------------------------------------------------ sequential greedy (G3) ----
 // Lam (n x n float64, lower) with H + delta I = Lam^T Lam from VS (n x r),
