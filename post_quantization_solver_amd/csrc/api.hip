@@ -44,7 +44,6 @@ using namespace mpq;
 namespace {
 
 constexpr int KD = 256;          // CD tile width (columns)
-constexpr int MAX_SPLITK = 16;   // K chunks for the CD tile-gradient GEMM
 constexpr int CD_GROUPS_MAX = 2; // CD row groups run on streams of their own
 // row groups for the CD sweeps: two for layers of at least 1024 rows
 int cd_groups(int64_t m) { return m >= 1024 ? CD_GROUPS_MAX : 1; }
@@ -111,8 +110,8 @@ struct Layout {
 
 enum Region {
   R_VS, R_VST, R_YTIL, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI,
-  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_U64, R_D64, R_SPLIT, R_TKEY, R_QF, R_VSP, R_VSTP, R_R2P, R_ZP, R_ANCH,
-  R_LAM, R_CTMP, R_GDIAG, R_MROWS, R_E8KEY, R_COUNT
+  R_CHG, R_CODES, R_LEVELS, R_QK, R_PV, R_E32, R_FLAG, R_D64, R_TKEY, R_QF, R_VSP, R_VSTP, R_R2P, R_ZP, R_ANCH,
+  R_LAM, R_CTMP, R_GDIAG, R_MROWS, R_E8KEY, R_HFULL, R_G64, R_COUNT
 };
 
 static_assert(R_COUNT <= (int)(sizeof(Layout::off) / sizeof(size_t)), "Layout::off holds every region");
@@ -154,10 +153,8 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, bool g
   sz[R_PV] = d == 8 ? (size_t)L.Kpad * 8 * sizeof(uint32_t) : 0;
   sz[R_E32] = (size_t)(d == 8 ? L.Kpad : 64) * 8 * f;
   sz[R_FLAG] = d == 8 ? (size_t)(64 + m * L.B) * sizeof(int32_t) : 0;
-  sz[R_U64] = (size_t)m * r * f64;
   sz[R_D64] = (size_t)m * n * f64;
   const int G = cd_groups(m);
-  sz[R_SPLIT] = (size_t)MAX_SPLITK * G * ((m + G - 1) / G) * KD * f64;
   sz[R_TKEY] = d == 8 ? (size_t)G * (KD / 8) * L.Kpad * 4 * sizeof(uint32_t) : 0;
   sz[R_QF] = d == 8 ? (size_t)m * 16 * sizeof(uint32_t) : 0;
   // pre-split GEMM operands of the linear module (bf16 term tiles)
@@ -169,6 +166,9 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, bool g
   sz[R_LAM] = greedy ? (size_t)n * n * f64 : 0;
   sz[R_CTMP] = greedy ? chol_tmp_doubles(n) * f64 : 0;
   sz[R_GDIAG] = greedy ? (size_t)KD * KD * f64 : 0;
+  // CD: H = VS VS^T (n x n) and the gradient G = (W - X) H (m x n), float64
+  sz[R_HFULL] = (size_t)n * n * f64;
+  sz[R_G64] = (size_t)m * n * f64;
   // d = 8: codebook keys in lexicographic order and their indices (E8 prefix codebooks)
   sz[R_E8KEY] = d == 8 ? (size_t)2 * K * sizeof(uint32_t) : 0;
   // per CD row group: the rows that moved in the current tile, and their count
@@ -534,20 +534,33 @@ Gemm64Args gemm64(int M, int N, int K, const void* A, int64_t lda, const float* 
 }
 
 // n_cd sweeps of exact block CD from `codes` (workspace or caller buffer).
-// The residual U = (W - X) V diag(s), the tile gradients, the diagonal tiles
-// of H and the moves are float64.
+// The gradient G = (W - X) H of every row over all n columns is kept current
+// (H = VS VS^T): a tile reads its gradient from G, the blocks' moves update
+// the tile's copy in place, and after the tile G -= Delta H[tile, :] over the
+// rows that moved.  G, H, the tile gradients, the diagonal tiles of H and the
+// moves are float64.
 int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int32_t* codes, int32_t* cd_changes) {
   const Layout& L = c.L;
   if (n_cd <= 0 || L.m == 0) return MPQ_OK;
   double* D = reinterpret_cast<double*>(c.p(R_D64));   // W - X
-  double* U = reinterpret_cast<double*>(c.p(R_U64));   // rank-space residual
+  double* H = reinterpret_cast<double*>(c.p(R_HFULL));
+  double* Gf = reinterpret_cast<double*>(c.p(R_G64));
   double* Gt = reinterpret_cast<double*>(c.p(R_GT));
   double* Dl = reinterpret_cast<double*>(c.p(R_DELTA));
   double* Hd = reinterpret_cast<double*>(c.p(R_HD));
   int32_t* chg = c.pi(R_CHG);
   TIMED(c, MPQ_PROF_CD_GEMM, launch_gather(codes, L.m, L.n, c.cb, a, o, W, nullptr, nullptr, nullptr, c.st, D));
-  TIMED(c, MPQ_PROF_CD_GEMM,
-        launch_gemm64(EPI_STORE, true, gemm64((int)L.m, (int)L.r, (int)L.n, D, L.n, c.p(R_VST), L.n, U, L.r), c.st));
+  {
+    // H = VS VS^T on the tiles that touch the lower triangle, then mirrored
+    Gemm64Args h = gemm64((int)L.n, (int)L.n, (int)L.r, c.p(R_VS), L.r, c.p(R_VS), L.r, H, L.n);
+    h.lower = 1;
+    TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_STORE, false, h, c.st));
+    TIMED(c, MPQ_PROF_CD_GEMM, launch_mirror_lower(H, L.n, c.st));
+    // G = (W - X) H
+    Gemm64Args gd = gemm64((int)L.m, (int)L.n, (int)L.n, D, L.n, nullptr, L.n, Gf, L.n);
+    gd.B64 = H;
+    TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_STORE, true, gd, c.st));
+  }
   // diagonal tiles of H = VS VS^T
   const int full = (int)(L.n / KD);
   if (full > 0) {
@@ -594,7 +607,7 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
   }
   struct Group {
     int64_t r0, mg;
-    double *Gt, *Dl, *U, *part;
+    double *Gt, *Dl, *G;
     int32_t *codes, *chg, *changes, *pi, *mrows, *nmoved;
     float* ps;
     const float *a, *o;
@@ -606,8 +619,7 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
     q.mg = std::max<int64_t>(0, std::min<int64_t>(mg_max, L.m - q.r0));
     q.Gt = Gt + q.r0 * KD;
     q.Dl = Dl + q.r0 * KD;
-    q.U = U + q.r0 * L.r;
-    q.part = reinterpret_cast<double*>(c.p(R_SPLIT)) + (int64_t)g * MAX_SPLITK * mg_max * KD;
+    q.G = Gf + q.r0 * L.n;
     q.codes = codes + q.r0 * L.B;
     q.chg = chg + q.r0;
     q.changes = cd_changes ? cd_changes + q.r0 * n_cd : nullptr;
@@ -635,17 +647,10 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
           const Group& q = grp[g];
           if (q.mg == 0) continue;
           c.st = gs[g];
-          // the tile gradient has few output tiles and a long K (= r): split K
-          // until the launch has about 512 workgroups
-          const int64_t out_tiles = (int64_t)gemm_col_tiles(kw) * ((q.mg + GEMM_BM - 1) / GEMM_BM);
-          int splits = (int)std::min<int64_t>(MAX_SPLITK, std::max<int64_t>(1, 512 / std::max<int64_t>(out_tiles, 1)));
-          splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, L.r / 256));
-          Gemm64Args gg = gemm64((int)q.mg, kw, (int)L.r, q.U, L.r, c.p(R_VS) + j0 * L.r, L.r, q.Gt, kw);
-          if (splits > 1) {
-            TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64_splitk(EPI_STORE, gg, splits, q.part, c.st));
-          } else {
-            TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_STORE, true, gg, c.st));
-          }
+          // the tile's gradient, from G
+          TIMED(c, MPQ_PROF_CD_GEMM,
+                hipMemcpy2DAsync(q.Gt, (size_t)kw * sizeof(double), q.G + j0, (size_t)L.n * sizeof(double),
+                                 (size_t)kw * sizeof(double), (size_t)q.mg, hipMemcpyDeviceToDevice, c.st));
           if (L.d == 1) {
             TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_scalar_tile(q.mg, L.n, j0, kw, q.Gt, Ht, c.cb, q.a, q.o, q.codes,
                                                                nullptr, q.Dl, q.chg, c.st));
@@ -671,15 +676,17 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
             }
           }
         }
-        // U -= Delta VS_tile^T over the rows that moved in the tile (the other
-        // rows of Delta are zero)
+        // G -= Delta H[tile, :] over the rows that moved in the tile (the other
+        // rows of Delta are zero); H is symmetric, so row j of the GEMM's B
+        // operand is H[j][tile]
         for (int g = 0; g < G; ++g) {
           const Group& q = grp[g];
           if (q.mg == 0) continue;
           c.st = gs[g];
           TIMED(c, MPQ_PROF_CD_GEMM, launch_fill_i32(q.nmoved, 1, 0, c.st));
           TIMED(c, MPQ_PROF_CD_GEMM, launch_collect_nonzero_rows(q.Dl, q.mg, kw, q.mrows, q.nmoved, c.st));
-          Gemm64Args gu = gemm64((int)q.mg, (int)L.r, kw, q.Dl, kw, c.p(R_VST) + j0, L.n, q.U, L.r);
+          Gemm64Args gu = gemm64((int)q.mg, (int)L.n, kw, q.Dl, kw, nullptr, L.n, q.G, L.n);
+          gu.B64 = H + j0;
           gu.rows = q.mrows;
           gu.nrows = q.nmoved;
           TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_SUB_INPLACE, true, gu, c.st));
@@ -711,7 +718,7 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
 int run_objective(Ctx& c, const float* W, const float* a, const float* o, const int32_t* codes, double* f) {
   const Layout& L = c.L;
   double* D = reinterpret_cast<double*>(c.p(R_D64));
-  double* U = reinterpret_cast<double*>(c.p(R_U64));
+  double* U = reinterpret_cast<double*>(c.p(R_G64));   // m x r <= m x n
   TIMED(c, MPQ_PROF_OTHER, launch_gather(codes, L.m, L.n, c.cb, a, o, W, nullptr, nullptr, nullptr, c.st, D));
   TIMED(c, MPQ_PROF_OTHER,
         launch_gemm64(EPI_STORE, true, gemm64((int)L.m, (int)L.r, (int)L.n, D, L.n, c.p(R_VST), L.n, U, L.r), c.st));

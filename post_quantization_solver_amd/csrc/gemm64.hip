@@ -200,6 +200,35 @@ hipError_t launch_gemm64_splitk(int epi, const Gemm64Args& g0, int splits, doubl
   return hipGetLastError();
 }
 
+// H[j][i] = H[i][j] for every i > j (n x n, row-major): 32 x 32 tiles through
+// LDS so that both the reads and the transposed writes are coalesced.
+__global__ __launch_bounds__(256) void mirror_lower_kernel(double* __restrict__ H, int64_t n) {
+  __shared__ double tile[32][33];
+  const int64_t ti = blockIdx.y, tj = blockIdx.x;   // source tile (rows ti, columns tj), ti >= tj
+  if (tj > ti) return;
+  const int c = threadIdx.x & 31, r0 = threadIdx.x >> 5;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = r0 + 8 * k;
+    const int64_t i = ti * 32 + r, j = tj * 32 + c;
+    tile[r][c] = i < n && j < n ? H[i * n + j] : 0.0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int cc = r0 + 8 * k;                 // source column within the tile
+    const int64_t i = ti * 32 + c, j = tj * 32 + cc;   // source element (i, j), written to (j, i)
+    if (i < n && j < n && i > j) H[j * n + i] = tile[c][cc];
+  }
+}
+
+hipError_t launch_mirror_lower(double* H, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const unsigned t = (unsigned)((n + 31) / 32);
+  hipLaunchKernelGGL(mirror_lower_kernel, dim3(t, t), dim3(256), 0, st, H, n);
+  return hipGetLastError();
+}
+
 // One wave per row: any nonzero among its kd entries appends the row.
 __global__ __launch_bounds__(256) void collect_nonzero_rows_kernel(const double* __restrict__ X, int64_t m, int kd,
                                                                    int32_t* __restrict__ list,

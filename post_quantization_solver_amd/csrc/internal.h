@@ -61,6 +61,8 @@ struct Gemm64Args {
 hipError_t launch_gemm64(int epi, bool a_is_f64, const Gemm64Args& g, hipStream_t st);
 // A float64, split K into `splits` chunks through `part` (splits * M * N doubles).
 hipError_t launch_gemm64_splitk(int epi, const Gemm64Args& g, int splits, double* part, hipStream_t st);
+// Copies the lower triangle of an n x n float64 matrix onto the upper one.
+hipError_t launch_mirror_lower(double* H, int64_t n, hipStream_t st);
 // Rows (of an m x kd float64 matrix) with some nonzero entry, appended to
 // list in no particular order, their number added to *count.
 hipError_t launch_collect_nonzero_rows(const double* X, int64_t m, int kd, int32_t* list, int32_t* count,

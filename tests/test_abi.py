@@ -38,7 +38,7 @@ def test_header_symbols_exported(lib):
 def test_workspace_sizes(lib):
     assert mpq.workspace_bytes(64, 256, 256, 8, 1) > 0
     big = mpq.workspace_bytes(4096, 14336, 14336, 65536, 8)
-    assert 2e9 < big < 8e9
+    assert 2e9 < big < 12e9
     assert mpq.workspace_bytes(4, 10, 11, 8, 1) == 0       # r > n
     assert mpq.workspace_bytes(4, 12, 12, 8, 8) == 0       # n % d
     assert mpq.workspace_bytes(4, 16, 16, 8, 3) == 0       # d unsupported
