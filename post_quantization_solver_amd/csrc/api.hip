@@ -533,6 +533,18 @@ Gemm64Args gemm64(int M, int N, int K, const void* A, int64_t lda, const float* 
   return g;
 }
 
+// H = VS VS^T (float64, n x n) on the tiles that touch the lower triangle,
+// then mirrored.
+int compute_h(Ctx& c) {
+  const Layout& L = c.L;
+  double* H = reinterpret_cast<double*>(c.p(R_HFULL));
+  Gemm64Args h = gemm64((int)L.n, (int)L.n, (int)L.r, c.p(R_VS), L.r, c.p(R_VS), L.r, H, L.n);
+  h.lower = 1;
+  TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_STORE, false, h, c.st));
+  TIMED(c, MPQ_PROF_CD_GEMM, launch_mirror_lower(H, L.n, c.st));
+  return MPQ_OK;
+}
+
 // n_cd sweeps of exact block CD from `codes` (workspace or caller buffer).
 // The gradient G = (W - X) H of every row over all n columns is kept current
 // (H = VS VS^T): a tile reads its gradient from G, the blocks' moves update
@@ -551,11 +563,8 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
   int32_t* chg = c.pi(R_CHG);
   TIMED(c, MPQ_PROF_CD_GEMM, launch_gather(codes, L.m, L.n, c.cb, a, o, W, nullptr, nullptr, nullptr, c.st, D));
   {
-    // H = VS VS^T on the tiles that touch the lower triangle, then mirrored
-    Gemm64Args h = gemm64((int)L.n, (int)L.n, (int)L.r, c.p(R_VS), L.r, c.p(R_VS), L.r, H, L.n);
-    h.lower = 1;
-    TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_STORE, false, h, c.st));
-    TIMED(c, MPQ_PROF_CD_GEMM, launch_mirror_lower(H, L.n, c.st));
+    const int rc = compute_h(c);
+    if (rc) return rc;
     // G = (W - X) H
     Gemm64Args gd = gemm64((int)L.m, (int)L.n, (int)L.n, D, L.n, nullptr, L.n, Gf, L.n);
     gd.B64 = H;
@@ -648,9 +657,7 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
           if (q.mg == 0) continue;
           c.st = gs[g];
           // the tile's gradient, from G
-          TIMED(c, MPQ_PROF_CD_GEMM,
-                hipMemcpy2DAsync(q.Gt, (size_t)kw * sizeof(double), q.G + j0, (size_t)L.n * sizeof(double),
-                                 (size_t)kw * sizeof(double), (size_t)q.mg, hipMemcpyDeviceToDevice, c.st));
+          TIMED(c, MPQ_PROF_CD_GEMM, launch_copy_cols_f64(q.G + j0, L.n, q.Gt, kw, q.mg, kw, c.st));
           if (L.d == 1) {
             TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_scalar_tile(q.mg, L.n, j0, kw, q.Gt, Ht, c.cb, q.a, q.o, q.codes,
                                                                nullptr, q.Dl, q.chg, c.st));

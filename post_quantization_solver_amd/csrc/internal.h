@@ -174,6 +174,8 @@ int64_t factor_solver_bytes(int64_t n);
 int run_factor(double* H, int64_t n, int64_t r, float* s, float* V, double* D, double* E, int* info, void* scratch,
                size_t scratch_bytes, hipStream_t st);
 hipError_t launch_fill_f64(double* dst, int64_t count, double v, hipStream_t st);
+hipError_t launch_copy_cols_f64(const double* src, int64_t lds, double* dst, int64_t ldd, int64_t rows, int cols,
+                                hipStream_t st);
 hipError_t launch_fill_i32(int32_t* dst, int64_t count, int32_t v, hipStream_t st);
 
 }  // namespace mpq

@@ -302,6 +302,27 @@ hipError_t launch_half_sumsq64(const double* U, int64_t m, int64_t r, double* f,
   return hipGetLastError();
 }
 
+// dst[i][0 .. cols) = src[i][0 .. cols) for rows i < rows (row strides lds, ldd).
+__global__ void copy_cols_f64_kernel(const double* __restrict__ src, int64_t lds, double* __restrict__ dst,
+                                     int64_t ldd, int64_t rows, int cols) {
+  const int64_t total = rows * cols;
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; k < total; k += stride) {
+    const int64_t i = k / cols, j = k - i * cols;
+    dst[i * ldd + j] = src[i * lds + j];
+  }
+}
+
+hipError_t launch_copy_cols_f64(const double* src, int64_t lds, double* dst, int64_t ldd, int64_t rows, int cols,
+                                hipStream_t st) {
+  const int64_t total = rows * cols;
+  if (total <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
+  hipLaunchKernelGGL(copy_cols_f64_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, lds, dst, ldd, rows, cols);
+  return hipGetLastError();
+}
+
 __global__ void fill_f64_kernel(double* __restrict__ dst, int64_t count, double v) {
   int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t stride = (int64_t)gridDim.x * blockDim.x;
