@@ -97,6 +97,9 @@ typedef struct {
 #define MPQ_F_FIXED_BETA 1u
 #define MPQ_F_PROFILE    2u
 #define MPQ_F_NO_E8DP    4u   /* d = 8: always use the codebook-scan denoiser (for A/B checks) */
+#define MPQ_F_PROFILE_SAMPLED 8u  /* with MPQ_F_PROFILE: time one launch in 32 of the many-launch categories
+                                     (MPQ_PROF_CD_SCORE) and scale their milliseconds to all launches, so
+                                     that event creation does not slow the call being measured */
 
 /* Profiling categories (kernel groups). */
 #define MPQ_PROF_PROLOGUE  0  /* rank-space projection, RTN, beta^0 */

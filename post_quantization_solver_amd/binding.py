@@ -42,6 +42,7 @@ class MPQError(RuntimeError):
 
 F_PROFILE = 2
 F_NO_E8DP = 4
+F_PROFILE_SAMPLED = 8
 PROF_NAMES = ("prologue", "denoise", "extrinsic", "linear1", "beta", "linear2", "map", "cd_gemm", "cd_search",
               "other", "denoise_exact", "cd_score")
 PROF_COUNT = len(PROF_NAMES)
@@ -55,9 +56,12 @@ class Options(ctypes.Structure):
 
 
 class Profile:
-    """Host accumulators for the library's per-category event timing."""
+    """Host accumulators for the library's per-category event timing.
+    sampled: time one CD scoring launch in 32 and scale to all of them
+    (MPQ_F_PROFILE_SAMPLED), which keeps event creation from slowing the call."""
 
-    def __init__(self, categories=PROF_NAMES):
+    def __init__(self, categories=PROF_NAMES, sampled=False):
+        self.sampled = bool(sampled)
         self.ms = (ctypes.c_double * PROF_COUNT)()
         self.launches = (ctypes.c_int64 * PROF_COUNT)()
         self.mask = 0
@@ -210,6 +214,7 @@ def _workspace(m, n, r, K, d, device):
 def _opts(beta0=None, fixed_beta=False, profile=None, anchor_tau=None, anchor_w=None, group=None, map_codes=None,
           objective=None, scan_denoiser=False):
     flags = ((F_FIXED_BETA if fixed_beta else 0) | (F_PROFILE if profile is not None else 0) |
+             (F_PROFILE_SAMPLED if profile is not None and profile.sampled else 0) |
              (F_NO_E8DP if scan_denoiser else 0))
     o = Options(float(beta0) if beta0 else 0.0, flags, profile.mask if profile is not None else 0,
                 profile.ms if profile is not None else None, profile.launches if profile is not None else None,

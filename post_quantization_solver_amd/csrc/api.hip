@@ -67,7 +67,7 @@ thread_local hipError_t g_last_hip_error = hipSuccess;
 // of the launch gap that stream-recorded events include).
 #define TIMED_KERNEL(c, cat, fn, ...)                               \
   do {                                                              \
-    if ((c).timed(cat)) {                                           \
+    if ((c).timed(cat) && (c).prof.take(cat)) {                     \
       Prof::Ev ev_{nullptr, nullptr, (cat)};                        \
       MPQ_TRY(hipEventCreate(&ev_.a));                              \
       if (hipEventCreate(&ev_.b) != hipSuccess) {                   \
@@ -193,6 +193,17 @@ struct Prof {
   double* ms = nullptr;
   int64_t* launches = nullptr;
   std::vector<Ev> evs;
+  // sampled categories: one launch in SAMPLE_EVERY gets events
+  static constexpr int SAMPLE_EVERY = 32;
+  bool sampled = false;
+  int64_t calls[MPQ_PROF_COUNT] = {};
+  int64_t taken[MPQ_PROF_COUNT] = {};
+  bool take(int cat) {
+    const bool t = !sampled || cat != MPQ_PROF_CD_SCORE || calls[cat] % SAMPLE_EVERY == 0;
+    ++calls[cat];
+    taken[cat] += t;
+    return t;
+  }
   ~Prof() {
     for (auto& e : evs) {
       (void)hipEventDestroy(e.a);
@@ -441,12 +452,21 @@ int prepare_factors(Ctx& c, const float* V, const float* s, bool split = false) 
 // Collect profiling results (waits for the call's last event).
 int finish(Ctx& c, int rc) {
   if (rc != MPQ_OK || !c.prof.on || c.prof.evs.empty()) return rc;
+  double ms_cat[MPQ_PROF_COUNT] = {};
+  int64_t n_cat[MPQ_PROF_COUNT] = {};
   for (auto& e : c.prof.evs) {
     float ms = 0.f;
     MPQ_TRY(hipEventSynchronize(e.b));   // events may sit on several streams
     MPQ_TRY(hipEventElapsedTime(&ms, e.a, e.b));
-    if (c.prof.ms) c.prof.ms[e.cat] += ms;
-    if (c.prof.launches) c.prof.launches[e.cat] += 1;
+    ms_cat[e.cat] += ms;
+    n_cat[e.cat] += 1;
+  }
+  for (int k = 0; k < MPQ_PROF_COUNT; ++k) {
+    if (n_cat[k] == 0) continue;
+    // a sampled category reports its mean over the timed launches times all of them
+    const int64_t all = c.prof.taken[k] > 0 && c.prof.calls[k] > n_cat[k] ? c.prof.calls[k] : n_cat[k];
+    if (c.prof.ms) c.prof.ms[k] += ms_cat[k] * (double)all / (double)n_cat[k];
+    if (c.prof.launches) c.prof.launches[k] += all;
   }
   return rc;
 }
@@ -825,6 +845,7 @@ int begin(Ctx& c, int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, const f
     c.prof.mask = opt->prof_mask;
     c.prof.ms = opt->prof_ms;
     c.prof.launches = opt->prof_launches;
+    c.prof.sampled = (opt->flags & MPQ_F_PROFILE_SAMPLED) != 0;
   }
   if (opt && opt->anchor_tau > 0.f && std::isfinite(opt->anchor_tau)) {
     c.anchor_tau = opt->anchor_tau;

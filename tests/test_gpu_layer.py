@@ -128,3 +128,26 @@ def test_cd_row_groups_on_streams():
             for k in ("codes", "cd_changes", "beta_tr", "gamma1_tr"):
                 assert np.array_equal(part[k], full[k][lo:hi]), (d, lo, k)
         assert full["cd_changes"].sum() > 0
+
+
+def test_sampled_profile_counts_every_launch():
+    """With MPQ_F_PROFILE_SAMPLED the CD scoring category times one launch in
+    32 but reports every launch, and its milliseconds scale to all of them;
+    the codes do not depend on profiling."""
+    import torch
+    import post_quantization_solver_amd as mpq
+    L = S.make_layer("prof", 1024, 128, seed=36, d=8, K=1000, r=96, power=0.6, T_vamp=2)
+    T = layer_tensors(L)
+    runs = {}
+    for sampled in (False, True):
+        prof = mpq.Profile(("cd_score",), sampled=sampled)
+        out = mpq.quantize_layer(T["W"], T["s"], T["V"], L.E, T["a"], T["o"], T_vamp=L.T_vamp, n_cd=L.n_cd,
+                                 damping=L.damping, profile=prof)
+        torch.cuda.synchronize()
+        runs[sampled] = (prof.as_dict()["cd_score"], host(out["codes"]))
+    (ms_full, n_full), codes_full = runs[False]
+    (ms_s, n_s), codes_s = runs[True]
+    # two row groups x 16 blocks x n_cd sweeps
+    assert n_full == n_s == 2 * (128 // 8) * L.n_cd
+    assert ms_full > 0 and 0.2 < ms_s / ms_full < 5.0
+    assert np.array_equal(codes_full, codes_s)
