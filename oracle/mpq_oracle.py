@@ -19,7 +19,7 @@ page:
   inverse temperature beta updated by the empirical-Bayes M-step with damping,
   then marginal MAP and exact block coordinate descent.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   R1  extrinsic updates use scalar per-row precisions (standard VAMP):
       gamma_out = eta - gamma_in,
       r_out = (eta x_hat - gamma_in r_in) / gamma_out.

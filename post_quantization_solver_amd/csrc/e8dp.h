@@ -1,6 +1,7 @@
 // The first K points of the E8 lattice in (norm, lexicographic) order as a
-// finite automaton over the 8 coordinates, shared by the host (recognition,
-// counting) and the forward-backward denoiser (e8dp.hip).
+// finite automaton over the 8 coordinates: the host uses it to recognise such
+// codebooks and to count the automaton's transitions; the lane-parallel passes
+// of e8dp.hip run the same automaton with the states laid out over lanes.
 //
 // E8 = {x in Z^8 : sum x even} u {x in (Z + 1/2)^8 : sum x even}.  A point is
 // in the codebook iff ||x||^2 < N, or ||x||^2 = N and (x_1 .. x_8) <= L in
