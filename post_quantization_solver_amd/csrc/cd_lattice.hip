@@ -26,7 +26,7 @@ namespace mpq {
 constexpr int CDL_ROWS_WAVE = 64;            // 4 row subtiles per wave
 constexpr int CDL_WAVES = 4;                 // waves per scoring workgroup (they share its key slice)
 constexpr int CDL_ROWS_WG = CDL_WAVES * CDL_ROWS_WAVE;
-constexpr int CDU_WAVES = 4;                 // rows (one per wave) per query / update workgroup
+constexpr int CDU_WAVES = 8;                 // rows (one per wave) per query / update workgroup
 constexpr int CDL_CW_WG = 512;               // codewords per workgroup slice
 
 // t fragments of one CD tile: for block bl of the tile and codeword cw, the
