@@ -24,10 +24,10 @@
 namespace mpq {
 
 constexpr int CDL_ROWS_WAVE = 64;            // 4 row subtiles per wave
-constexpr int CDL_WAVES = 4;                 // waves per scoring workgroup (they share its key slice)
+constexpr int CDL_WAVES = 8;                 // waves per scoring workgroup (they share its key slice)
 constexpr int CDL_ROWS_WG = CDL_WAVES * CDL_ROWS_WAVE;
 constexpr int CDU_WAVES = 8;                 // rows (one per wave) per query / update workgroup
-constexpr int CDL_CW_WG = 512;               // codewords per workgroup slice
+constexpr int CDL_CW_WG = 1024;              // codewords per workgroup slice
 
 // t fragments of one CD tile: for block bl of the tile and codeword cw, the
 // K-slots 24..31 of the score key, [t hi, mid, lo, hi, mid, hi, 0, 0] with
