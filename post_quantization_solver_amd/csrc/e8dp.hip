@@ -302,7 +302,7 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // Four queries per wave, one per 16-lane row.
-__global__ __launch_bounds__(256) void e8dp_kernel(const float* __restrict__ R1, const float* __restrict__ gamma1,
+__global__ __launch_bounds__(64 * E8DP_WAVES) void e8dp_kernel(const float* __restrict__ R1, const float* __restrict__ gamma1,
                                                    int64_t m, int64_t n, const float* __restrict__ a,
                                                    const float* __restrict__ o, E8Prefix P, float* __restrict__ xhat,
                                                    float* __restrict__ vblk, int32_t* __restrict__ flag_list,
@@ -496,7 +496,7 @@ __device__ __forceinline__ void e8_nearest_pass(const int j, const E8RowCoef& cf
 
 // Nearest codeword of every block (argmin ||r - (a e + o)||^2 = argmax of
 // sum_j e_j r'_j - e_j^2 / 2, ties to the lowest index), four blocks per wave.
-__global__ __launch_bounds__(256) void e8_nearest_kernel(const float* __restrict__ R, int64_t m, int64_t n,
+__global__ __launch_bounds__(64 * E8DP_WAVES) void e8_nearest_kernel(const float* __restrict__ R, int64_t m, int64_t n,
                                                          const float* __restrict__ a, const float* __restrict__ o,
                                                          E8Prefix P, const uint32_t* __restrict__ keys,
                                                          const int32_t* __restrict__ kidx, int K,
