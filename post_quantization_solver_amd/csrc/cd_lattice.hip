@@ -125,17 +125,8 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
   const int64_t row_base = (int64_t)blockIdx.y * CDL_ROWS_WG + wave * CDL_ROWS_WAVE;
   const int nsl = gridDim.x;
 
-  // key fragments of this slice: lanes g < 3 carry e, lanes g = 3 the t(e) terms
-  const v4u* kv = reinterpret_cast<const v4u*>(keys);
-  const v4u* tkb = tk + (int64_t)bl * Kpad + cw_base;
-  for (int f = t; f < (ncw / 16) * 64; f += 64 * CDL_WAVES) {
-    const int st = f >> 6, ln = f & 63;
-    v4u w = (ln >> 4) < 3 ? kv[(int64_t)(cw_base / 16 + st) * 64 + ln] : tkb[st * 16 + (ln & 15)];
-    reinterpret_cast<v4u*>(lds_key)[f] = w;
-  }
-  __syncthreads();
-
   // row queries: lane (j, g) of subtile q serves row row_base + 16 q + j
+  // (loaded first, so that they arrive while the keys are staged)
   v4u qop[4];
   float best[4];
   int bst[4];
@@ -146,6 +137,28 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
     best[q] = INFINITY;
     bst[q] = 0;
   }
+
+  // key fragments of this slice: lanes g < 3 carry e, lanes g = 3 the t(e)
+  // terms; every load is issued before the first LDS write, so the staging
+  // costs one memory round trip
+  const v4u* kv = reinterpret_cast<const v4u*>(keys);
+  const v4u* tkb = tk + (int64_t)bl * Kpad + cw_base;
+  constexpr int NF = (CDL_CW_WG / 16) * 64 / (64 * CDL_WAVES);   // fragments per thread
+  const int nf = (ncw / 16) * 64;
+  v4u kbuf[NF];
+#pragma unroll
+  for (int u = 0; u < NF; ++u) {
+    // past the slice's end (a short last slice; nf >= 512 > t) reload fragment t
+    const int f = t + u * 64 * CDL_WAVES < nf ? t + u * 64 * CDL_WAVES : t;
+    const int st = f >> 6, ln = f & 63;
+    kbuf[u] = (ln >> 4) < 3 ? kv[(int64_t)(cw_base / 16 + st) * 64 + ln] : tkb[st * 16 + (ln & 15)];
+  }
+#pragma unroll
+  for (int u = 0; u < NF; ++u) {
+    const int f = t + u * 64 * CDL_WAVES;
+    if (f < nf) reinterpret_cast<v4u*>(lds_key)[f] = kbuf[u];
+  }
+  __syncthreads();
   // lane (j, g) sees codewords 16 st + 4 g + v of the slice for row j, two
   // steps at a time (ncw / 16 is even: Kpad is a multiple of 128); it keeps
   // the least tagged score and the pair where it last strictly improved, so

@@ -32,6 +32,7 @@
 namespace mpq {
 
 constexpr int BK = 16;
+constexpr int GEMM_GROUP_M = 8;   // tile rows per group of the XCD-aware tile order
 
 template <bool VEC>
 __device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t ld, int rows, int K,
@@ -154,8 +155,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
   const int li = lane & 15;
   const int lg = lane >> 4;
 
-  const int tile_n = blockIdx.x;
-  const int tile_m = blockIdx.y;
+  // Workgroups are dispatched to the 8 XCDs in turn (linear id mod 8), and
+  // each XCD has an L2 of its own.  Renumber so that XCD x runs the x-th
+  // contiguous eighth of the tiles, in groups of GEMM_GROUP_M tile rows walked
+  // column by column: the tiles resident on one XCD at a time then share a
+  // few A and B panels in its L2.
+  int tile_n, tile_m;
+  {
+    const int gx = gridDim.x, gy = gridDim.y;
+    const int T = gx * gy;
+    const int L = blockIdx.x + gx * blockIdx.y;
+    const int per = T / 8, rem = T % 8, x = L % 8;
+    const int P = x * per + min(x, rem) + L / 8;   // a bijection of [0, T)
+    const int npg = GEMM_GROUP_M * gx;
+    const int first = (P / npg) * GEMM_GROUP_M;
+    const int gsz = min(gy - first, GEMM_GROUP_M);
+    const int w = P % npg;
+    tile_m = first + w % gsz;
+    tile_n = w / gsz;
+  }
   const int row0 = tile_m * GEMM_BM;
   const int col0 = tile_n * GEMM_BN;
   const int z = blockIdx.z;
