@@ -165,7 +165,7 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
   // ties go to the earliest pair, then step, then the lowest v
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
   const v4u* kq = reinterpret_cast<const v4u*>(lds_key);
-  for (int sp = 0; sp < ncw / 32; ++sp) {
+  auto pair_step = [&](int sp) {
     const v4u k0 = kq[(2 * sp) * 64 + lane];
     const v4u k1 = kq[(2 * sp + 1) * 64 + lane];
 #pragma unroll
@@ -181,6 +181,12 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
       bst[q] = nb < best[q] ? sp : bst[q];
       best[q] = nb;
     }
+  };
+  // ncw / 32 is a multiple of 4: two pairs per iteration (the unrolled
+  // body lets the running bests change registers instead of being copied)
+  for (int sp = 0; sp < ncw / 32; sp += 2) {
+    pair_step(sp);
+    pair_step(sp + 1);
   }
   // top 2 of the row's four lane-bests (lanes j, j+16, j+32, j+48)
 #pragma unroll
