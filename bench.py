@@ -1,6 +1,6 @@
 """Benchmark: one MPQ layer solve per step on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config c5] [--group G] [--cpu-rows R | --no-cpu]
+    python bench.py [--steps K] [--warmup W] [--config c5] [--group G] [--cpu-rows R | --no-cpu] [--no-probe]
 
 A step is one full mpq_quantize_layer call (prologue, T_vamp VAMP
 iterations, marginal MAP, 3 CD sweeps) on a seeded synthetic layer whose
@@ -9,8 +9,11 @@ lattice layer 4096 x 14336 (Llama-3-8B MLP-down shape), T_vamp = 16.
 
 Prints ONE JSON line: throughput in weights quantized per second, the
 roofline of the dominant kernel (timed with HIP events on the library's
-stream inside the timed region) and the float64 oracle's throughput on a
-bounded sample of rows of the same layer, run on the host cores.
+stream inside the timed region) against the vendor's peak and against the
+rate this GPU reaches on the same instruction (mpq_probe_rate, run after the
+timed region; all probed rates are in `measured_peaks`), and the float64
+oracle's throughput on a bounded sample of rows of the same layer, run on
+the host cores.
 """
 from __future__ import annotations
 
@@ -117,6 +120,20 @@ def dominant_roofline(L, prof, steps, n_cd):
     return dict(base, bound="alu", achieved=None, peak=None, unit="TFLOP/s", frac=None)
 
 
+def measured_peak(roof, probes):
+    """The probed counterpart of roof["peak"] (same unit), or None."""
+    if roof["peak"] is None:
+        return None
+    if roof["bound"] == "mfma":
+        return probes["mfma_bf16_tflops"]
+    if roof.get("path", "").startswith("E8 forward-backward"):
+        return probes["valu_f64_tflops"]
+    if roof["kernel"] == "denoise":
+        # exponential-bound scan: the vendor-derived peak scales with the exp rate
+        return roof["peak"] * probes["exp_f32_tops"] * 1e12 / EXP_RATE
+    return None
+
+
 def measured_traffic(config, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or
@@ -192,6 +209,7 @@ def main():
     ap.add_argument("--n-cd", type=int, default=None,
                     help="CD sweeps (default: the workload's 3); 0 runs only the prologue, VAMP and MAP, e.g. for "
                          "counter passes over the VAMP kernels")
+    ap.add_argument("--no-probe", action="store_true", help="skip the achievable-rate probes")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), the reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -268,6 +286,20 @@ def main():
     roof["traffic"] = measured_traffic(args.config, roof["kernel"])
     codes = out["codes"].cpu().numpy()
 
+    # achievable rates of the instructions the kernels are bound by, probed on
+    # this GPU (outside the timed region; the solver workspace is the scratch)
+    probes = None
+    if not args.no_probe:
+        rates = {k: mpq.probe_rate(k, ws) for k in mpq.binding.PROBE_KINDS}
+        probes = dict(mfma_bf16_tflops=rates["mfma_bf16"] / 1e12, mfma_f64_tflops=rates["mfma_f64"] / 1e12,
+                      valu_f64_tflops=rates["valu_f64"] / 1e12, exp_f32_tops=rates["exp_f32"] / 1e12,
+                      hbm_copy_gbs=rates["hbm_copy"] / 1e9)
+        log(f"[bench] probed rates: " + ", ".join(f"{k} {v:.1f}" for k, v in probes.items()))
+        measured = measured_peak(roof, probes)
+        if measured and roof["achieved"] is not None:
+            roof["measured_peak"] = measured
+            roof["frac_of_measured"] = roof["achieved"] / measured
+
     cpu = None
     if not args.no_cpu:
         rows = args.cpu_rows or max(1, min(16, os.cpu_count() or 1))
@@ -286,8 +318,10 @@ def main():
                               frac=roof["frac"], traffic=roof["traffic"], kernel=roof["kernel"],
                               avg_launch_ms=roof["avg_ms"], launches=roof["launches"],
                               **({"path": roof["path"]} if "path" in roof else {}),
+                              **({"measured_peak": roof["measured_peak"], "frac_of_measured": roof["frac_of_measured"]}
+                                 if "measured_peak" in roof else {}),
                               **({"secondary": roof["secondary"]} if "secondary" in roof else {})),
-                kernel_ms_per_step=split, cpu_baseline=cpu)
+                measured_peaks=probes, kernel_ms_per_step=split, cpu_baseline=cpu)
     print(json.dumps(line), flush=True)
 
 

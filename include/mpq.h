@@ -136,6 +136,24 @@ int mpq_codebook_kind(const float* cb, int64_t K, int64_t d);
  * forward-backward denoiser (8 flops each per block); 0 for other codebooks. */
 int64_t mpq_e8dp_transitions(const float* cb, int64_t K);
 
+/* Achievable-rate probes, for reading kernel measurements against what this
+ * GPU reaches on the instructions the solver's kernels are bound by (as well
+ * as against the vendor's peak figures).  Runs the probe of `kind` on
+ * `stream` four times (the first as a warm-up), waits for it, and stores the
+ * best rate in *rate: flop/s for the MFMA and float64 FMA probes (2 flops per
+ * multiply-add), instructions/s x 64 lanes for v_exp_f32, and bytes read plus
+ * written per second for the copy.  `scratch` (device, 256-byte aligned,
+ * caller-owned; contents overwritten) needs 8 MiB for the instruction probes
+ * and 256 MiB for the copy, which uses up to 2 GiB of it (reads one half,
+ * writes the other; give it well over twice the 256 MB last-level cache).  Returns MPQ_OK, MPQ_ENULL, MPQ_EPARAM (unknown kind),
+ * MPQ_EWORKSPACE (scratch too small or misaligned) or MPQ_EHIP. */
+#define MPQ_PROBE_MFMA_BF16 0  /* v_mfma_f32_16x16x32_bf16, 16 independent accumulators per wave */
+#define MPQ_PROBE_MFMA_F64  1  /* v_mfma_f64_16x16x4_f64, 8 independent accumulators per wave */
+#define MPQ_PROBE_VALU_F64  2  /* v_fma_f64, 8 independent chains per lane */
+#define MPQ_PROBE_EXP_F32   3  /* v_exp_f32, 8 independent chains per lane */
+#define MPQ_PROBE_HBM_COPY  4  /* 16-byte loads and stores streaming through HBM */
+int mpq_probe_rate(int kind, void* scratch, size_t scratch_bytes, double* rate, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* mpq_strerror(int status);
 

@@ -7,6 +7,6 @@ C ABI of include/mpq.h (libmpq.so).  This package is the thin binding.
 """
 from .binding import (  # noqa: F401
     EXPORTS, LIB_PATH, MPQError, PROF_NAMES, Profile, STATUS, cd, codebook_kind, denoise, factor, frontend, gram, greedy,
-    greedy_workspace_bytes, load_library, map_codes, objective, prologue, quantize_layer, rht, vamp_step,
+    greedy_workspace_bytes, load_library, map_codes, objective, probe_rate, prologue, quantize_layer, rht, vamp_step,
     workspace_bytes,
 )

@@ -25,7 +25,7 @@ F_FIXED_BETA = 1
 EXPORTS = ("mpq_workspace_bytes", "mpq_strerror", "mpq_quantize_layer", "mpq_prologue", "mpq_denoise",
            "mpq_vamp_step", "mpq_map", "mpq_cd", "mpq_objective", "mpq_greedy", "mpq_greedy_workspace_bytes",
            "mpq_gram_workspace_bytes", "mpq_gram", "mpq_rht", "mpq_factor_workspace_bytes", "mpq_factor",
-           "mpq_codebook_kind", "mpq_hip_error_name", "mpq_e8dp_transitions")
+           "mpq_codebook_kind", "mpq_hip_error_name", "mpq_e8dp_transitions", "mpq_probe_rate")
 
 
 class MPQError(RuntimeError):
@@ -128,6 +128,7 @@ def load_library(path: str = LIB_PATH):
     lib.mpq_e8dp_transitions.restype = I64
     lib.mpq_hip_error_name.argtypes = []
     lib.mpq_hip_error_name.restype = ctypes.c_char_p
+    lib.mpq_probe_rate.argtypes = [I, P, SZ, ctypes.POINTER(ctypes.c_double), P]
     for name in EXPORTS[2:]:
         if name.endswith("_bytes") or name in ("mpq_hip_error_name", "mpq_e8dp_transitions"):
             continue
@@ -159,6 +160,27 @@ def e8dp_transitions(cb) -> int:
     if E.shape[1] != 8:
         return 0
     return int(load_library().mpq_e8dp_transitions(E.ctypes.data_as(ctypes.c_void_p), E.shape[0]))
+
+
+PROBE_KINDS = {"mfma_bf16": 0, "mfma_f64": 1, "valu_f64": 2, "exp_f32": 3, "hbm_copy": 4}
+
+
+def probe_rate(kind: str, scratch=None) -> float:
+    """Achievable rate of one instruction or of an HBM copy on this GPU
+    (mpq_probe_rate): flop/s for "mfma_bf16", "mfma_f64" and "valu_f64",
+    lane operations/s for "exp_f32", bytes read + written per second for
+    "hbm_copy".  `scratch` (a device tensor, contents overwritten) defaults
+    to a fresh 2 GiB buffer."""
+    import torch
+    if kind not in PROBE_KINDS:
+        raise ValueError(f"unknown probe {kind!r}; one of {sorted(PROBE_KINDS)}")
+    if scratch is None:
+        scratch = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    out = ctypes.c_double(0.0)
+    rc = load_library().mpq_probe_rate(PROBE_KINDS[kind], _ptr(scratch), scratch.numel() * scratch.element_size(),
+                                       ctypes.byref(out), _stream())
+    _check(rc, "mpq_probe_rate")
+    return float(out.value)
 
 
 def workspace_bytes(m, n, r, K, d) -> int:

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmpq.so")
 SOURCES = ["api.hip", "gemm.hip", "gemm64.hip", "rowops.hip", "scalar.hip", "lattice.hip", "cd.hip", "cd_lattice.hip",
-           "chol.hip", "greedy.hip", "frontend.hip", "e8dp.hip"]
+           "chol.hip", "greedy.hip", "frontend.hip", "e8dp.hip", "probe.hip"]
 ARCH = os.environ.get("MPQ_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

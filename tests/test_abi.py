@@ -130,3 +130,19 @@ def test_strerror(lib):
         assert lib.mpq_strerror(code).decode()
     with pytest.raises(mpq.MPQError):
         mpq.binding._check(-3, "x")
+
+
+def test_probe_argument_validation(lib):
+    import ctypes as C
+    out = C.c_double(0.0)
+    # rejected before anything reaches the GPU
+    assert lib.mpq_probe_rate(0, None, 1 << 30, C.byref(out), None) == -1          # MPQ_ENULL
+    fake = C.c_void_p(1 << 20)                                                   # never dereferenced
+    assert lib.mpq_probe_rate(0, fake, 1 << 30, None, None) == -1
+    assert lib.mpq_probe_rate(5, fake, 1 << 30, C.byref(out), None) == -3        # MPQ_EPARAM
+    assert lib.mpq_probe_rate(-1, fake, 1 << 30, C.byref(out), None) == -3
+    assert lib.mpq_probe_rate(0, fake, 1 << 20, C.byref(out), None) == -5        # MPQ_EWORKSPACE: < 8 MiB
+    assert lib.mpq_probe_rate(4, fake, 128 << 20, C.byref(out), None) == -5      # copy needs 256 MiB
+    assert lib.mpq_probe_rate(0, C.c_void_p((1 << 20) + 16), 1 << 30, C.byref(out), None) == -5   # misaligned
+    with pytest.raises(ValueError):
+        mpq.probe_rate("no_such_probe")
