@@ -234,6 +234,8 @@ struct Ctx {
   float anchor_tau = 0.f;
   const float* anchor_w = nullptr;
   bool anchored() const { return anchor_tau > 0.f; }
+  // VS and VSᵀ are also held as bf16-term tiles (R_VSP, R_VSTP)
+  bool vs_packed = false;
   // d = 8 codebooks that are the first K points of E8 in (norm, lex) order:
   // the denoiser runs the forward-backward pass over coordinates
   bool e8dp = false;
@@ -446,6 +448,7 @@ int prepare_factors(Ctx& c, const float* V, const float* s, bool split = false) 
     TIMED(c, MPQ_PROF_OTHER, launch_pack_split(c.p(R_VS), c.L.n, c.L.r, c.L.r, packed(c, R_VSP), c.st));
     TIMED(c, MPQ_PROF_OTHER, launch_pack_split(c.p(R_VST), c.L.r, c.L.n, c.L.n, packed(c, R_VSTP), c.st));
   }
+  c.vs_packed = split;
   return MPQ_OK;
 }
 
@@ -475,13 +478,26 @@ int finish(Ctx& c, int rc) {
 int run_prologue(Ctx& c, const float* W, const float* a, const float* o, const mpq_options* opt, float* ytil,
                  int32_t* rtn, float* gamma1, float* beta) {
   const Layout& L = c.L;
-  TIMED(c, MPQ_PROF_PROLOGUE,
-        launch_gemm(EPI_STORE, gemm((int)L.m, (int)L.r, (int)L.n, W, L.n, c.p(R_VST), L.n, ytil, L.r), c.st));
+  // with VSᵀ already in bf16-term tiles, the A operands are split once
+  // (into the R₂ tile region, free before the first iteration) so that both
+  // products take the pre-split GEMM path; the terms and sums are the same
+  GemmArgs gy = gemm((int)L.m, (int)L.r, (int)L.n, W, L.n, c.p(R_VST), L.n, ytil, L.r);
+  if (c.vs_packed) {
+    TIMED(c, MPQ_PROF_PROLOGUE, launch_pack_split(W, L.m, L.n, L.n, packed(c, R_R2P), c.st));
+    gy.Ap = packed(c, R_R2P);
+    gy.Bp = packed(c, R_VSTP);
+  }
+  TIMED(c, MPQ_PROF_PROLOGUE, launch_gemm(EPI_STORE, gy, c.st));
   TIMED(c, MPQ_PROF_PROLOGUE, nearest(c, W, rtn, a, o));
   TIMED(c, MPQ_PROF_PROLOGUE, launch_gather(rtn, L.m, L.n, c.cb, a, o, W, nullptr, c.p(R_X1), c.rowsq(), c.st));
   GemmArgs g = gemm((int)L.m, (int)L.r, (int)L.n, c.p(R_X1), L.n, c.p(R_VST), L.n, nullptr, 0);
   g.partial = c.p(R_PART);
   g.ldp = gemm_col_tiles((int)L.r);
+  if (c.vs_packed) {
+    TIMED(c, MPQ_PROF_PROLOGUE, launch_pack_split(c.p(R_X1), L.m, L.n, L.n, packed(c, R_R2P), c.st));
+    g.Ap = packed(c, R_R2P);
+    g.Bp = packed(c, R_VSTP);
+  }
   TIMED(c, MPQ_PROF_PROLOGUE, launch_gemm(EPI_ROWSUMSQ, g, c.st));
   float b0 = (opt && opt->beta0 > 0.f) ? opt->beta0 : 0.f;
   TIMED(c, MPQ_PROF_PROLOGUE, launch_prologue_finish(L.m, L.n, L.r, c.rowsq(), c.p(R_PART), gemm_col_tiles((int)L.r), b0, gamma1, beta,
