@@ -236,47 +236,59 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
   const int c0 = 8 * (bl + 1);          // the next block's first column in the tile
   const bool has_next = c0 < kd;
 
-  // ---- loads that do not depend on the merge
+  // ---- the codes first (loads return in order, so waiting for them does not
+  // wait for the rest), then every load that depends neither on the merge nor
+  // on the codes, with clamped indices and selects instead of branches; the
+  // codewords follow as soon as the codes arrive.  Without a next block the
+  // "next" code is this block's, its codeword unused.
   const int cx = codes[i * B + b];
-  const int cn = has_next ? safe_code(codes[i * B + b + 1], K) : 0;
-  const int cxs = safe_code(cx, K);
+  const int cn = safe_code(codes[i * B + b + (has_next ? 1 : 0)], K);
+  const int cnc = has_next ? c0 : 8 * bl;   // the next block's first column (a valid one without it)
+  Cand o[2][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int sl = 64 * r + lane;
+    const int slc = min(sl, nslices - 1);
+    const float2 sv = reinterpret_cast<const float2*>(part_s)[i * nslices + slc];
+    const int2 iv = reinterpret_cast<const int2*>(part_i)[i * nslices + slc];
+    o[r][0] = sl < nslices ? Cand{sv.x, iv.x} : Cand{INFINITY, 0x7fffffff};
+    o[r][1] = sl < nslices ? Cand{sv.y, iv.y} : Cand{INFINITY, 0x7fffffff};
+  }
   const double ai = a[i];
   const double hpk = Ht[(int64_t)(8 * bl + p) * kd + 8 * bl + k];
   const double gpp = Gt[i * kd + 8 * bl + p];
-  const double gnext = has_next ? Gt[i * kd + c0 + k] : 0.0;
-  const float exp_ = e32[(int64_t)cxs * 8 + p], exk = e32[(int64_t)cxs * 8 + k];
-  float exq[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) exq[q] = e32[(int64_t)cxs * 8 + q];
+  const double gnext_v = Gt[i * kd + cnc + k];
   // gradient update operands: column jc = lane + 64 u of the tile, rows 8 bl + q of
   // H's diagonal tile (symmetric, read as H[8 bl + q][jc] so the loads coalesce)
   double gcol[CD_COLS_LANE], hcol[CD_COLS_LANE][8];
 #pragma unroll
   for (int u = 0; u < CD_COLS_LANE; ++u) {
     const int jc = lane + 64 * u;
-    gcol[u] = jc < kd ? Gt[i * kd + jc] : 0.0;
+    const int jcc = min(jc, kd - 1);
+    const double gv = Gt[i * kd + jcc];
+    gcol[u] = jc < kd ? gv : 0.0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) hcol[u][q] = jc < kd ? Ht[(int64_t)(8 * bl + q) * kd + jc] : 0.0;
+    for (int q = 0; q < 8; ++q) {
+      const double hv = Ht[(int64_t)(8 * bl + q) * kd + jcc];
+      hcol[u][q] = jc < kd ? hv : 0.0;
+    }
   }
   // next block's query operands (lane k of each group of 8 builds q[k])
   double hnext[8];
-  float exn[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    hnext[q] = has_next ? Ht[(int64_t)(c0 + k) * kd + c0 + q] : 0.0;
-    exn[q] = e32[(int64_t)cn * 8 + q];
+    const double hv = Ht[(int64_t)(cnc + k) * kd + cnc + q];
+    hnext[q] = has_next ? hv : 0.0;
   }
-  Cand o[2][2];
+  const double gnext = has_next ? gnext_v : 0.0;
+  // ---- the current and next codewords
+  const int cxs = safe_code(cx, K);
+  const float exp_ = e32[(int64_t)cxs * 8 + p], exk = e32[(int64_t)cxs * 8 + k];
+  float exq[8], exn[8];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int sl = 64 * r + lane;
-    o[r][0] = o[r][1] = Cand{INFINITY, 0x7fffffff};
-    if (sl < nslices) {
-      const float2 sv = reinterpret_cast<const float2*>(part_s)[i * nslices + sl];
-      const int2 iv = reinterpret_cast<const int2*>(part_i)[i * nslices + sl];
-      o[r][0] = {sv.x, iv.x};
-      o[r][1] = {sv.y, iv.y};
-    }
+  for (int q = 0; q < 8; ++q) {
+    exq[q] = e32[(int64_t)cxs * 8 + q];
+    exn[q] = e32[(int64_t)cn * 8 + q];
   }
 
   // ---- top 2 over all slices (lane butterfly; the top two of a totally
