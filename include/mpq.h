@@ -100,6 +100,9 @@ typedef struct {
 #define MPQ_F_PROFILE_SAMPLED 8u  /* with MPQ_F_PROFILE: time one launch in 32 of the many-launch categories
                                      (MPQ_PROF_CD_SCORE) and scale their milliseconds to all launches, so
                                      that event creation does not slow the call being measured */
+#define MPQ_F_NO_E8_DECODE 16u  /* d = 8, E8-prefix codebooks: find every block's nearest codeword with the
+                                   automaton, without the lattice decoder's fast path (for A/B checks; the
+                                   codes are equal) */
 
 /* Profiling categories (kernel groups). */
 #define MPQ_PROF_PROLOGUE  0  /* rank-space projection, RTN, beta^0 */

@@ -42,6 +42,7 @@ class MPQError(RuntimeError):
 
 F_PROFILE = 2
 F_NO_E8DP = 4
+F_NO_E8_DECODE = 16
 F_PROFILE_SAMPLED = 8
 PROF_NAMES = ("prologue", "denoise", "extrinsic", "linear1", "beta", "linear2", "map", "cd_gemm", "cd_search",
               "other", "denoise_exact", "cd_score")
@@ -234,10 +235,10 @@ def _workspace(m, n, r, K, d, device):
 
 
 def _opts(beta0=None, fixed_beta=False, profile=None, anchor_tau=None, anchor_w=None, group=None, map_codes=None,
-          objective=None, scan_denoiser=False):
+          objective=None, scan_denoiser=False, e8_decode=True):
     flags = ((F_FIXED_BETA if fixed_beta else 0) | (F_PROFILE if profile is not None else 0) |
              (F_PROFILE_SAMPLED if profile is not None and profile.sampled else 0) |
-             (F_NO_E8DP if scan_denoiser else 0))
+             (F_NO_E8DP if scan_denoiser else 0) | (0 if e8_decode else F_NO_E8_DECODE))
     o = Options(float(beta0) if beta0 else 0.0, flags, profile.mask if profile is not None else 0,
                 profile.ms if profile is not None else None, profile.launches if profile is not None else None,
                 float(anchor_tau) if anchor_tau else 0.0, anchor_w.data_ptr() if anchor_w is not None else None,
@@ -388,9 +389,10 @@ def vamp_step(R1, gamma1, beta, ytil, s, V, cb, row_scale, row_offset, damping=0
 
 
 def map_codes(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=None, W=None, group=None,
-              scan_denoiser=False):
+              scan_denoiser=False, e8_decode=True):
     """Marginal MAP codes (mpq_map); scan_denoiser keeps the codebook scan for
-    E8 prefix codebooks too."""
+    E8 prefix codebooks too; e8_decode=False finds an E8 prefix codebook's
+    nearest codewords with the automaton alone (no lattice-decoder fast path)."""
     import torch
     m, n = R1.shape
     E = _host_codebook(cb)
@@ -402,7 +404,8 @@ def map_codes(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=
         _dev(W, torch.float32, "W", (m, n))
     codes = torch.empty((m, n // d), dtype=torch.int32, device=R1.device)
     ws = workspace if workspace is not None else _workspace(m, n, n, K, d, R1.device)
-    op, _keep = _opts(anchor_tau=anchor_tau, anchor_w=W, group=group, scan_denoiser=scan_denoiser)
+    op, _keep = _opts(anchor_tau=anchor_tau, anchor_w=W, group=group, scan_denoiser=scan_denoiser,
+                      e8_decode=e8_decode)
     rc = load_library().mpq_map(_ptr(R1), _ptr(gamma1), m, n, E.ctypes.data_as(ctypes.c_void_p), K, d,
                                 _ptr(row_scale), _ptr(row_offset), op, _ptr(codes), _ptr(ws), ws.numel(), _stream())
     _check(rc, "mpq_map")

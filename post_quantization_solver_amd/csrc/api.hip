@@ -30,9 +30,11 @@ hipError_t launch_fill_i32(int32_t*, int64_t, int32_t, hipStream_t);
 bool e8_prefix_detect(const float* cb, int64_t K, E8Prefix& P);
 int64_t e8_transitions(const E8Prefix& P);
 void e8_key_table(const float* cb, int64_t K, uint32_t* keys, int32_t* idx);
+// flag (count at [0], list from [64]; room for every block) enables the decoder
+// fast path; nullptr runs the automaton for every block
 hipError_t launch_nearest_e8(const float* R, int64_t m, int64_t n, const E8Prefix& P, const uint32_t* keys,
                              const int32_t* kidx, int K, const float* a, const float* o, int32_t* codes,
-                             hipStream_t st);
+                             int32_t* flag, hipStream_t st);
 hipError_t launch_denoise_e8dp(const float* R1, const float* gamma1, int64_t m, int64_t n, const E8Prefix& P,
                                const float* a, const float* o, float* xhat, float* vblk, int32_t* flag,
                                hipStream_t st);
@@ -236,6 +238,9 @@ struct Ctx {
   bool anchored() const { return anchor_tau > 0.f; }
   // VS and VSᵀ are also held as bf16-term tiles (R_VSP, R_VSTP)
   bool vs_packed = false;
+  // E8-prefix nearest codeword: the lattice decoder first, the automaton for
+  // the blocks it cannot settle (else the automaton for every block)
+  bool e8_decode = true;
   // d = 8 codebooks that are the first K points of E8 in (norm, lex) order:
   // the denoiser runs the forward-backward pass over coordinates
   bool e8dp = false;
@@ -416,7 +421,7 @@ hipError_t nearest(const Ctx& c, const float* R, int32_t* codes, const float* a,
   if (c.e8dp) {
     const uint32_t* keys = reinterpret_cast<const uint32_t*>(c.p(R_E8KEY));
     return launch_nearest_e8(R, c.L.m, c.L.n, c.e8p, keys, reinterpret_cast<const int32_t*>(keys + c.L.K),
-                             (int)c.L.K, a, o, codes, c.st);
+                             (int)c.L.K, a, o, codes, c.e8_decode ? c.pi(R_FLAG) : nullptr, c.st);
   }
   return launch_nearest_lattice(R, c.L.m, c.L.n, c.cb, a, o, codes, c.st);
 }
@@ -868,6 +873,7 @@ int begin(Ctx& c, int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, const f
     c.anchor_w = opt->anchor_w;
   }
   c.e8dp_allowed = !(opt && (opt->flags & MPQ_F_NO_E8DP));
+  c.e8_decode = !(opt && (opt->flags & MPQ_F_NO_E8_DECODE));
   int rc = check_shapes(m, n, r, K, d);
   if (rc) return rc;
   if (!cb) return MPQ_ENULL;

@@ -496,22 +496,16 @@ __device__ __forceinline__ void e8_nearest_pass(const int j, const E8RowCoef& cf
 
 // Nearest codeword of every block (argmin ||r - (a e + o)||^2 = argmax of
 // sum_j e_j r'_j - e_j^2 / 2, ties to the lowest index), four blocks per wave.
-__global__ __launch_bounds__(64 * E8DP_WAVES) void e8_nearest_kernel(const float* __restrict__ R, int64_t m, int64_t n,
-                                                         const float* __restrict__ a, const float* __restrict__ o,
-                                                         E8Prefix P, const uint32_t* __restrict__ keys,
-                                                         const int32_t* __restrict__ kidx, int K,
-                                                         int32_t* __restrict__ codes) {
-  __shared__ E8RowCoef coef[E8DP_WAVES * 4];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int row = lane >> 4, j = lane & 15;
-  E8RowCoef& cf = coef[wave * 4 + row];
+// One block per 16-lane row (q, when `active`); every lane of the wave calls it.
+__device__ __forceinline__ void e8_nearest_block(E8RowCoef& cf, int j, int64_t q, bool active,
+                                                 const float* __restrict__ R, int64_t n,
+                                                 const float* __restrict__ a, const float* __restrict__ o,
+                                                 const E8Prefix& P, const uint32_t* __restrict__ keys,
+                                                 const int32_t* __restrict__ kidx, int K,
+                                                 int32_t* __restrict__ codes) {
   const int64_t B = n / 8;
-  const int64_t total = m * B;
   const bool lhalf = (P.L2[0] & 1) != 0;
   const double xj = j < 7 ? (double)(j - 3) : (double)(j - 7) - 2.5;
-  const int64_t q = ((int64_t)blockIdx.x * E8DP_WAVES + wave) * 4 + row;
-  const bool active = q < total;
   int64_t i = 0, b = 0;
   double ai = 1.0, oi = 0.0;
   if (active) {
@@ -568,16 +562,168 @@ __global__ __launch_bounds__(64 * E8DP_WAVES) void e8_nearest_kernel(const float
   codes[i * B + b] = lo < K && keys[lo] == bk ? kidx[lo] : -1;
 }
 
+__global__ __launch_bounds__(64 * E8DP_WAVES) void e8_nearest_kernel(const float* __restrict__ R, int64_t m, int64_t n,
+                                                         const float* __restrict__ a, const float* __restrict__ o,
+                                                         E8Prefix P, const uint32_t* __restrict__ keys,
+                                                         const int32_t* __restrict__ kidx, int K,
+                                                         int32_t* __restrict__ codes) {
+  __shared__ E8RowCoef coef[E8DP_WAVES * 4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row = lane >> 4, j = lane & 15;
+  const int64_t q = ((int64_t)blockIdx.x * E8DP_WAVES + wave) * 4 + row;
+  e8_nearest_block(coef[wave * 4 + row], j, q, q < m * (n / 8), R, n, a, o, P, keys, kidx, K, codes);
+}
+
+// The same for the blocks listed in list[0 .. *count), a grid of workgroups
+// striding over the list.
+__global__ __launch_bounds__(64 * E8DP_WAVES) void e8_nearest_list_kernel(const float* __restrict__ R, int64_t n,
+                                                              const float* __restrict__ a, const float* __restrict__ o,
+                                                              E8Prefix P, const uint32_t* __restrict__ keys,
+                                                              const int32_t* __restrict__ kidx, int K,
+                                                              const int32_t* __restrict__ list,
+                                                              const int32_t* __restrict__ count,
+                                                              int32_t* __restrict__ codes) {
+  __shared__ E8RowCoef coef[E8DP_WAVES * 4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row = lane >> 4, j = lane & 15;
+  const int64_t cnt = *count;
+  for (int64_t base = (int64_t)blockIdx.x * E8DP_WAVES * 4; base < cnt; base += (int64_t)gridDim.x * E8DP_WAVES * 4) {
+    const int64_t idx = base + wave * 4 + row;
+    const bool active = idx < cnt;
+    const int64_t q = active ? (int64_t)list[idx] : 0;
+    e8_nearest_block(coef[wave * 4 + row], j, q, active, R, n, a, o, P, keys, kidx, K, codes);
+    wave_sync();
+  }
+}
+
+// Fast path of the nearest codeword: E8 is D8 ∪ (D8 + ½), and the nearest
+// point of D8 rounds every coordinate and, if the rounded sum is odd, moves
+// the coordinate with the largest rounding error to its other neighbour
+// (the decoder for D_n and its cosets in Conway and Sloane's "Sphere
+// Packings, Lattices and Groups", ch. 20).  When that point is the unique
+// nearest lattice point by a margin (no rounding error within E8_DEC_EPS of
+// 1/2, a unique largest error, the two cosets' squared distances apart) and it
+// is a codeword (its key is in the table), it is the nearest codeword, and the
+// block is done.  Every other block -- near ties, points outside the codebook,
+// non-finite rows -- is listed for the exact automaton pass.
+constexpr double E8_DEC_EPS = 1e-9;
+
+__device__ __forceinline__ bool d8_nearest(const double (&x)[8], double (&u)[8]) {
+  double err[8];
+  int par = 0;
+  bool ok = true;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    u[t] = rint(x[t]);
+    err[t] = x[t] - u[t];
+    ok = ok && fabs(err[t]) < 0.5 - E8_DEC_EPS;
+    par += (int)u[t];
+  }
+  if (!ok) return false;
+  if (par & 1) {
+    int k = 0;
+    double e1 = -1.0, e2 = -1.0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const double ae = fabs(err[t]);
+      if (ae > e1) {
+        e2 = e1;
+        e1 = ae;
+        k = t;
+      } else if (ae > e2) {
+        e2 = ae;
+      }
+    }
+    if (e1 - e2 < E8_DEC_EPS || e1 < E8_DEC_EPS) return false;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (t == k) u[t] += err[t] > 0.0 ? 1.0 : -1.0;
+  }
+  return true;
+}
+
+__global__ __launch_bounds__(256) void e8_decode_kernel(const float* __restrict__ R, int64_t m, int64_t n,
+                                                        const float* __restrict__ a, const float* __restrict__ o,
+                                                        const uint32_t* __restrict__ keys,
+                                                        const int32_t* __restrict__ kidx, int K,
+                                                        int32_t* __restrict__ codes, int32_t* __restrict__ list,
+                                                        int32_t* __restrict__ count) {
+  const int64_t B = n / 8;
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= m * B) return;
+  const int64_t i = q / B, b = q - i * B;
+  const double ai = (double)a[i], oi = (double)o[i];
+  const float4* rp = reinterpret_cast<const float4*>(R + i * n + b * 8);
+  const float4 r0 = rp[0], r1 = rp[1];
+  const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  double x[8], y[8], u[8], w[8];
+  bool ok = true;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    x[t] = ((double)rv[t] - oi) / ai;   // as the automaton pass forms r'
+    ok = ok && isfinite(x[t]) && fabs(x[t]) < 1e6;
+    y[t] = x[t] - 0.5;
+  }
+  ok = ok && d8_nearest(x, u) && d8_nearest(y, w);
+  double du = 0.0, dw = 0.0;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    w[t] += 0.5;
+    du = fma(x[t] - u[t], x[t] - u[t], du);
+    dw = fma(x[t] - w[t], x[t] - w[t], dw);
+  }
+  ok = ok && fabs(du - dw) > E8_DEC_EPS;
+  uint32_t key = 0;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int c2 = (int)(2.0 * (du < dw ? u[t] : w[t]));
+    ok = ok && c2 >= -6 && c2 <= 6;
+    key = key * 16u + (uint32_t)(c2 + 6);
+  }
+  int32_t code = -1;
+  if (ok) {
+    int lo = 0, hi = K;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (keys[mid] < key)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    if (lo < K && keys[lo] == key) code = kidx[lo];
+  }
+  if (code >= 0)
+    codes[i * B + b] = code;
+  else
+    list[atomicAdd(count, 1)] = (int32_t)q;
+}
+
 hipError_t launch_nearest_e8(const float* R, int64_t m, int64_t n, const E8Prefix& P, const uint32_t* keys,
                              const int32_t* kidx, int K, const float* a, const float* o, int32_t* codes,
-                             hipStream_t st) {
+                             int32_t* flag, hipStream_t st) {
   const int64_t total = m * (n / 8);
   if (total <= 0) return hipSuccess;
   const int64_t per_wg = (int64_t)E8DP_WAVES * 4;
   const int64_t wgs = (total + per_wg - 1) / per_wg;
-  if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(e8_nearest_kernel, dim3((unsigned)wgs), dim3(64 * E8DP_WAVES), 0, st, R, m, n, a, o, P, keys,
-                     kidx, K, codes);
+  if (wgs > INT32_MAX || total > INT32_MAX) return hipErrorInvalidValue;
+  if (!flag || (reinterpret_cast<uintptr_t>(R) & 15) != 0) {
+    // the automaton for every block
+    hipLaunchKernelGGL(e8_nearest_kernel, dim3((unsigned)wgs), dim3(64 * E8DP_WAVES), 0, st, R, m, n, a, o, P, keys,
+                       kidx, K, codes);
+    return hipGetLastError();
+  }
+  // the decoder for every block, then the automaton for the blocks it lists
+  int32_t* count = flag;
+  int32_t* list = flag + 64;
+  hipError_t e = launch_fill_i32(count, 1, 0, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(e8_decode_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, R, m, n, a, o, keys,
+                     kidx, K, codes, list, count);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(e8_nearest_list_kernel, dim3((unsigned)std::min<int64_t>(wgs, 4096)), dim3(64 * E8DP_WAVES), 0, st,
+                     R, n, a, o, P, keys, kidx, K, list, count, codes);
   return hipGetLastError();
 }
 

@@ -177,3 +177,33 @@ def test_e8_nearest_exact_ties():
     got = _e8_map(R1, E, a, o)
     ref = _oracle_nearest(R1, E, a, o)
     assert np.array_equal(got, ref), (got, ref)
+
+
+@pytest.mark.parametrize("K", [2401, 65536])
+def test_e8_decoder_equals_automaton(K):
+    """The lattice decoder's fast path (blocks whose nearest E8 point is unique
+    by a margin and a codeword) and the automaton alone name the same codeword
+    for every block: 8192 blocks from well inside the codebook to far outside
+    it (scales 0.3 to 12 codeword units), plus exact ties and non-finite
+    rows, which the decoder hands to the automaton."""
+    import post_quantization_solver_amd as mpq
+    E = S.e8_codebook(K)
+    g = np.random.default_rng(K + 7)
+    m, n = 64, 1024
+    a = (0.2 + g.random(m)).astype(np.float32)
+    o = (0.05 * g.standard_normal(m)).astype(np.float32)
+    scale = np.array([0.3, 0.8, 1.5, 3.0, 6.0, 12.0, 1.0, 2.0] * 8)[:, None]
+    R1 = (g.standard_normal((m, n)) * scale * a[:, None] + o[:, None]).astype(np.float32)
+    # exact ties (a = 1, o = 0 rows) and a non-finite block
+    a[:2] = 1.0
+    o[:2] = 0.0
+    R1[0, :16] = [0.5, 0.5, 0, 0, 0, 0, 0, 0] + [0.25] * 8
+    R1[1, :8] = np.inf
+    T = {k: dev(v) for k, v in (("a", a), ("o", o), ("R1", R1))}
+    g1 = dev(np.ones(m, np.float32))
+    fast = host(mpq.map_codes(T["R1"], g1, E, T["a"], T["o"]))
+    slow = host(mpq.map_codes(T["R1"], g1, E, T["a"], T["o"], e8_decode=False))
+    print(f"[e8 decoder] K={K}: {np.mean(fast == slow):.6f} agree", flush=True)
+    assert np.array_equal(fast, slow)
+    ref = _oracle_nearest(R1[2:8], E, a[2:8], o[2:8])
+    assert np.array_equal(fast[2:8], ref)
