@@ -25,6 +25,8 @@ Readings where the pages are silent:
       r_out = (eta x_hat - gamma_in r_in) / gamma_out.
   R2  if eta1 <= gamma1 the denoiser's posterior is passed through
       (r2 = x_hat1, gamma2 = eta1); the number of such events is counted.
+      A safeguard threshold eps >= 0 widens the rule to eta1 <= gamma1 (1 + eps)
+      (eps = 0, the default, is R2 itself).
   R3  beta^0 = r / ||T (w - w_rtn)||^2 (the M-step at the RTN point with
       zero posterior variance).
   R4  damping acts on beta itself: beta' = (1 - rho) beta + rho beta_EM.
@@ -212,11 +214,12 @@ def denoise(r1, gamma1, C, d, log_prior=None, return_q=False, anchor=None):
     return xhat.reshape(-1), v, q_all
 
 
-def extrinsic_denoiser_to_linear(r1, gamma1, xhat1, eta1):
-    """Self-feedback removal on the denoiser side (readings R1, R2).
+def extrinsic_denoiser_to_linear(r1, gamma1, xhat1, eta1, eps=0.0):
+    """Self-feedback removal on the denoiser side (readings R1, R2; eps: the
+    safeguard threshold of R2).
 
     Returns (r2, gamma2, fell_back)."""
-    if eta1 > gamma1:
+    if eta1 > gamma1 * (1.0 + eps):
         gamma2 = eta1 - gamma1
         r2 = (eta1 * xhat1 - gamma1 * r1) / gamma2
         return r2, gamma2, False
@@ -284,7 +287,7 @@ def vamp_init(w, s, V, C, d):
 
 
 def vamp(w, s, V, C, d, T_vamp, damping, a_scale, beta0=None, denoiser=None,
-         fixed_beta=False, record=False, anchor_tau=None):
+         fixed_beta=False, record=False, anchor_tau=None, safeguard_eps=0.0):
     """T_vamp iterations of rank-space VAMP with the beta M-step.
 
     `denoiser(r1, gamma1) -> (x_hat1, v_blocks)` defaults to the discrete
@@ -311,7 +314,7 @@ def vamp(w, s, V, C, d, T_vamp, damping, a_scale, beta0=None, denoiser=None,
             hist.append(dict(r1=r1.copy(), gamma1=gamma1, beta=beta))
         xhat1, v = denoiser(r1, gamma1)
         eta1 = n / max(float(np.sum(v)), floor)
-        r2, gamma2, fb = extrinsic_denoiser_to_linear(r1, gamma1, xhat1, eta1)
+        r2, gamma2, fb = extrinsic_denoiser_to_linear(r1, gamma1, xhat1, eta1, safeguard_eps)
         fallbacks += int(fb)
         lin = linear_module(r2, gamma2, beta, ytil, s, V)
         if not fixed_beta:
@@ -465,10 +468,12 @@ def codes_objective(w, codes, C, d, s, V):
 # the whole row
 # ----------------------------------------------------------------------------
 
-def solve_row(w, s, V, E, a, o, d, T_vamp, n_cd, damping, beta0=None, record=False, anchor_tau=None, group=0):
+def solve_row(w, s, V, E, a, o, d, T_vamp, n_cd, damping, beta0=None, record=False, anchor_tau=None, group=0,
+              safeguard_eps=0.0):
     """MPQ on one row: VAMP (T_vamp iterations) -> marginal MAP -> block CD.
     anchor_tau: the anchored prior of reading A1 (None: uniform prior).
     group > 0: group-wise grids of reading A2 (a, o hold one value per group).
+    safeguard_eps: the pass-through threshold of reading R2 (0: R2 itself).
 
     Returns dict(codes, objective, beta_tr, gamma1_tr, gamma2_tr, eta1_tr,
     cd_changes, fallbacks, map_codes, rtn_codes, frozen[, history]).
@@ -489,7 +494,8 @@ def solve_row(w, s, V, E, a, o, d, T_vamp, n_cd, damping, beta0=None, record=Fal
                     gamma1_tr=np.full(T_vamp + 1, inf), gamma2_tr=np.full(T_vamp, inf),
                     eta1_tr=np.full(T_vamp, inf), cd_changes=[0] * n_cd, fallbacks=0,
                     map_codes=rtn, rtn_codes=rtn, frozen=True, history=[])
-    st = vamp(w, s, V, C, d, T_vamp, damping, a, beta0=beta0, record=record, anchor_tau=anchor_tau)
+    st = vamp(w, s, V, C, d, T_vamp, damping, a, beta0=beta0, record=record, anchor_tau=anchor_tau,
+              safeguard_eps=safeguard_eps)
     mc = map_codes(st["r1"], st["gamma1"], C, d, anchor=(w, anchor_lambda(anchor_tau, a)))
     codes, changes = block_cd(mc, w, s, V, C, d, n_cd)
     changes = list(changes) + [0] * (n_cd - len(changes))

@@ -8,7 +8,7 @@ import test_oracle_pins as P
 
 _orig = {k: getattr(O, k) for k in ("denoise", "extrinsic_denoiser_to_linear", "linear_module",
                                      "beta_em", "block_cd", "rank_target", "block_logits", "anchor_log_prior",
-                                     "greedy_hessian")}
+                                     "greedy_hessian", "vamp_init")}
 
 
 def denoise_var_about_r(r1, gamma1, C, d, log_prior=None, return_q=False, anchor=None):
@@ -26,15 +26,45 @@ def logits_wrong_sign(r1b, gamma1, C, log_prior=None):
     return 0.5 * gamma1 * O.sq_dist(r1b, C)
 
 
-def extr_sign(r1, gamma1, xhat1, eta1):
+def extr_sign(r1, gamma1, xhat1, eta1, eps=0.0):
     if eta1 > gamma1:
         g2 = eta1 - gamma1
         return (eta1 * xhat1 + gamma1 * r1) / g2, g2, False
     return xhat1.copy(), eta1, True
 
 
-def extr_no_subtract(r1, gamma1, xhat1, eta1):
+def extr_no_subtract(r1, gamma1, xhat1, eta1, eps=0.0):
     return (eta1 * xhat1 - gamma1 * r1) / eta1, eta1, False
+
+
+def extr_pass_gamma1(r1, gamma1, xhat1, eta1, eps=0.0):
+    """R2 slip: the pass-through hands on gamma1 instead of eta1."""
+    r2, g2, fb = _orig["extrinsic_denoiser_to_linear"](r1, gamma1, xhat1, eta1, eps)
+    return (r2, gamma1, fb) if fb else (r2, g2, fb)
+
+
+def extr_pass_r1(r1, gamma1, xhat1, eta1, eps=0.0):
+    """R2 slip: the pass-through keeps the cavity mean r1."""
+    r2, g2, fb = _orig["extrinsic_denoiser_to_linear"](r1, gamma1, xhat1, eta1, eps)
+    return (np.array(r1, dtype=float), g2, fb) if fb else (r2, g2, fb)
+
+
+def init_gamma_sum(w, s, V, C, d):
+    """gamma1^0 = 1 / sum instead of 1 / mean."""
+    codes, g1, b0, mse, nrm2 = _orig["vamp_init"](w, s, V, C, d)
+    return codes, 1.0 / (mse * len(w)), b0, mse, nrm2
+
+
+def init_beta_no_r(w, s, V, C, d):
+    """beta^0 without the factor r."""
+    codes, g1, b0, mse, nrm2 = _orig["vamp_init"](w, s, V, C, d)
+    return codes, g1, 1.0 / nrm2, mse, nrm2
+
+
+def init_beta_n(w, s, V, C, d):
+    """beta^0 with n in place of r."""
+    codes, g1, b0, mse, nrm2 = _orig["vamp_init"](w, s, V, C, d)
+    return codes, g1, len(w) / nrm2, mse, nrm2
 
 
 def lin_wrong_D(r2, gamma2, beta, ytil, s, V):
@@ -161,6 +191,11 @@ MUTATIONS = [
     ("block_logits", logits_wrong_sign, [P.check_denoiser_limits]),
     ("extrinsic_denoiser_to_linear", extr_sign, [P.check_gaussian_prior_fixed_point]),
     ("extrinsic_denoiser_to_linear", extr_no_subtract, [P.check_gaussian_prior_fixed_point]),
+    ("extrinsic_denoiser_to_linear", extr_pass_gamma1, [P.check_r2_branch_hand, P.check_r2_in_vamp]),
+    ("extrinsic_denoiser_to_linear", extr_pass_r1, [P.check_r2_branch_hand, P.check_r2_in_vamp]),
+    ("vamp_init", init_gamma_sum, [P.check_vamp_init_hand]),
+    ("vamp_init", init_beta_no_r, [P.check_vamp_init_hand]),
+    ("vamp_init", init_beta_n, [P.check_vamp_init_hand]),
     ("linear_module", lin_wrong_D, [P.check_gaussian_prior_fixed_point, P.check_linear_module_dense]),
     ("linear_module", lin_no_null_term, [lambda: P.check_linear_module_dense(12, 9)]),
     ("linear_module", lin_no_extrinsic, [P.check_gaussian_prior_fixed_point, P.check_linear_module_dense]),

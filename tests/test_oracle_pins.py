@@ -471,6 +471,92 @@ def test_frozen_row():
 
 
 # ----------------------------------------------------------------------------
+# initialisation (hyper-parameter paragraph: r1^0 = w, gamma1^0 = 1 / MSE(w,
+# w_rtn); reading R3: beta^0 = r / ||T (w - w_rtn)||^2) and the pass-through
+# rule of reading R2, pinned on hand-computed numbers
+# ----------------------------------------------------------------------------
+
+def init_instance():
+    """w = (0.3, -0.7, 1.2, 0.1) on the levels {-1, 0, 1} (base {0, 1, 2},
+    scale 1, offset -1): round to nearest gives (0, -1, 1, 0), errors
+    (0.3, 0.3, 0.2, 0.1), squares summing to 0.23 (mean 0.0575).  Rank r = 2 < n = 4:
+    V = the first two unit vectors, s = (2, 0.5), so T (w - w_rtn) =
+    (2 * 0.3, 0.5 * 0.3) = (0.6, 0.15), squared norm 0.3825."""
+    w = np.array([0.3, -0.7, 1.2, 0.1])
+    E = np.array([[0.0], [1.0], [2.0]])
+    C = O.row_codewords(E, 1.0, -1.0)
+    V = np.eye(4)[:, :2]
+    s = np.array([2.0, 0.5])
+    return w, E, C, V, s
+
+
+def check_vamp_init_hand():
+    w, E, C, V, s = init_instance()
+    codes, g1, b0, mse, nrm2 = O.vamp_init(w, s, V, C, 1)
+    assert list(codes) == [1, 0, 2, 1]
+    assert mse == pytest.approx(0.0575, rel=1e-14)
+    assert g1 == pytest.approx(1.0 / 0.0575, rel=1e-12)          # 17.391304...
+    assert nrm2 == pytest.approx(0.3825, rel=1e-14)
+    assert b0 == pytest.approx(2.0 / 0.3825, rel=1e-12)          # r / ||T e||^2 with r = 2 (not n = 4)
+    # and as the whole-row solve records them
+    res = O.solve_row(w, s, V, E, 1.0, -1.0, 1, 1, 0, 0.5)
+    assert res["gamma1_tr"][0] == pytest.approx(1.0 / 0.0575, rel=1e-12)
+    assert res["beta_tr"][0] == pytest.approx(2.0 / 0.3825, rel=1e-12)
+
+
+def test_vamp_init_hand_computed():
+    check_vamp_init_hand()
+
+
+def check_r2_branch_hand():
+    """eta1 <= gamma1: pass the posterior through (r2 = xhat1, gamma2 = eta1);
+    eta1 > gamma1: gamma2 = eta1 - gamma1 and r2 = (eta1 xhat1 - gamma1 r1) /
+    gamma2, here with r1 = (0.2, 0.4), xhat1 = (0.1, 0.5), gamma1 = 5."""
+    r1 = np.array([0.2, 0.4])
+    x1 = np.array([0.1, 0.5])
+    r2, g2, fb = O.extrinsic_denoiser_to_linear(r1, 5.0, x1, 4.0)
+    assert fb and g2 == 4.0 and np.array_equal(r2, x1)
+    r2, g2, fb = O.extrinsic_denoiser_to_linear(r1, 5.0, x1, 5.0)      # boundary: not positive -> pass through
+    assert fb and g2 == 5.0 and np.array_equal(r2, x1)
+    r2, g2, fb = O.extrinsic_denoiser_to_linear(r1, 5.0, x1, 6.0)
+    assert not fb and g2 == pytest.approx(1.0)
+    assert np.allclose(r2, [6 * 0.1 - 5 * 0.2, 6 * 0.5 - 5 * 0.4], rtol=1e-12)   # (-0.4, 1.0)
+    # the safeguard threshold widens the rule: 5.2 <= 5 (1 + 0.05)
+    r2, g2, fb = O.extrinsic_denoiser_to_linear(r1, 5.0, x1, 5.2, eps=0.05)
+    assert fb and g2 == 5.2 and np.array_equal(r2, x1)
+    r2, g2, fb = O.extrinsic_denoiser_to_linear(r1, 5.0, x1, 5.2)
+    assert not fb and g2 == pytest.approx(0.2)
+
+
+def check_r2_in_vamp():
+    """On the 64 x 256 toy layer the rule fires; every iteration that took it
+    carries r2 = xhat1 and gamma2 = eta1 into the linear module, and every
+    other one gamma2 = eta1 - gamma1 > 0."""
+    L = S.make_config("c1")
+    fired = 0
+    for i in range(6):
+        C = O.row_codewords(L.E, L.a[i], L.o[i])
+        st = O.vamp(L.W[i], L.s, L.V, C, 1, L.T_vamp, L.damping, L.a[i], record=True)
+        for h in st["history"]:
+            if h["fell_back"]:
+                fired += 1
+                assert h["gamma2"] == h["eta1"] and h["eta1"] <= h["gamma1"]
+                assert np.array_equal(h["r2"], h["xhat1"])
+            else:
+                assert h["gamma2"] == pytest.approx(h["eta1"] - h["gamma1"], rel=1e-12) and h["gamma2"] > 0
+        assert st["fallbacks"] == sum(h["fell_back"] for h in st["history"])
+    assert fired > 0
+
+
+def test_r2_branch_hand_computed():
+    check_r2_branch_hand()
+
+
+def test_r2_branch_inside_vamp():
+    check_r2_in_vamp()
+
+
+# ----------------------------------------------------------------------------
 # anchored prior (reading A1: hyper-parameter paragraph, tau = 0.2; tau -> inf
 # is the unanchored limit)
 # ----------------------------------------------------------------------------
