@@ -8,12 +8,13 @@ inputs are already resident in HBM.  The default workload is the 2-bit E8
 lattice layer 4096 x 14336 (Llama-3-8B MLP-down shape), T_vamp = 16.
 
 Prints ONE JSON line: throughput in weights quantized per second, the
-roofline of the dominant kernel (timed with HIP events on the library's
-stream inside the timed region) against the vendor's peak and against the
-rate this GPU reaches on the same instruction (mpq_probe_rate, run after the
-timed region; all probed rates are in `measured_peaks`), and the float64
-oracle's throughput on a bounded sample of rows of the same layer, run on
-the host cores.
+roofline of the dominant kernel (the method's algorithmic work over the time
+measured with HIP events on the library's stream inside the timed region)
+against the vendor's peak of the dtype it issues and against the rate this
+GPU reaches on the same instruction (mpq_probe_rate, run after the timed
+region; all probed rates are in `measured_peaks`), the same for the denoiser
+and the linear module together, and the float64 oracle's throughput on a
+bounded sample of rows of the same layer, run on the host cores.
 """
 from __future__ import annotations
 
@@ -32,16 +33,15 @@ METRIC = "weights quantized/sec per layer (T_vamp=16 + 3 CD sweeps), % of MFMA/H
 # MI355X published peaks
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_BF16_MFMA_TFLOPS = 2500.0
+PEAK_FP64_TFLOPS = 78.6        # float64 matrix and vector alike on MI355X
 PEAK_HBM_GBS = 8000.0
-PEAK_FP64_VALU_TFLOPS = 78.6   # float64 vector and matrix alike on MI355X
-CD_MFMA_FLOP_PER_EVAL = 64
+CD_MFMA_FLOP_PER_EVAL = 64     # bf16 MFMA flops the CD scoring issues per (row, block, codeword)
 # Transcendental issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz at half
 # the fp32 VALU rate on gfx950 -> 19.66e12 exp/s (a throughput probe reads 18.4e12).
 EXP_RATE = 256 * 4 * 16 * 2.4e9 / 2
 LATTICE_FLOP_PER_EVAL = 36     # 2*8 (distance contraction) + 2*10 (weighted moments)
-LATTICE_MFMA_FLOP_PER_EVAL = 128   # bf16 MFMA flops the lattice denoiser issues per eval
 SCALAR_FLOP_PER_EVAL = 8       # distance, scaled logit, three moment updates
-SPLIT_BF16_PRODUCTS = 6        # linear GEMMs: bf16 cross products per float32 product (hh hm mh hl lh mm)
+NORTH_STAR_EVAL_FLOPS = 32     # the target's count of denoiser work per (block, codeword) eval
 
 WORKLOADS = {
     "c1": "3-bit scalar toy layer 64x256, T_vamp=8, 3 CD sweeps",
@@ -61,72 +61,87 @@ def mpq_e8dp_transitions(E):
     return mpq.binding.e8dp_transitions(E)
 
 
-def dominant_roofline(L, prof, steps, n_cd):
-    """Roofline entry for the kernel group with the largest time."""
+def group_work(L, kernel, launches, steps, n_cd):
+    """Algorithmic work of `launches` launches of a kernel group and the peak
+    of the dtype it issues: (flops, peak TFLOP/s, bound, basis)."""
     m, n, r, K, d = L.m, L.n, L.r, L.K, L.d
+    if kernel == "denoise" and d == 8 and mpq_e8dp_transitions(L.E) > 0:
+        # forward-backward pass over the trimmed E8 automaton: 8 flops per
+        # transition per block, float64 on the vector units
+        return (launches * m * (n // d) * 8.0 * mpq_e8dp_transitions(L.E), PEAK_FP64_TFLOPS, "alu",
+                "E8 forward-backward, 8 flops per automaton transition per block, float64 vector")
+    if kernel == "denoise":
+        per = LATTICE_FLOP_PER_EVAL if d == 8 else SCALAR_FLOP_PER_EVAL
+        return (launches * m * (n // d) * K * per, per * EXP_RATE / 1e12, "alu",
+                f"{per} flops and one exponential per (block, codeword)")
+    if kernel in ("linear1", "linear2"):
+        # one m x n x r product per launch on the fp64 matrix cores
+        return launches * 2.0 * m * n * r, PEAK_FP64_TFLOPS, "mfma", "2mnr flops per launch, float64 MFMA"
+    if kernel == "cd_score" and d == 8:
+        # every sweep scores every codeword for every (row, block): the
+        # method's own work is 2d flops per eval (e . q); it issues bf16 MFMAs
+        evals = float(steps) * n_cd * m * (n // d) * K
+        return evals * 2.0 * d, PEAK_BF16_MFMA_TFLOPS, "mfma", "2d flops per (row, block, codeword), bf16 MFMA"
+    return None
+
+
+def dominant_roofline(L, prof, steps, n_cd):
+    """Roofline entry for the kernel group with the largest time: the
+    method's algorithmic work over the measured time, against the peak of the
+    dtype the kernel issues."""
     best = max(prof, key=lambda k: prof[k][0])
     ms, launches = prof[best]
-    per_launch_s = ms / max(launches, 1) / 1e3
     base = dict(kernel=best, traffic=None, launches=launches, avg_ms=ms / max(launches, 1))
-    if best == "denoise" and d == 8 and mpq_e8dp_transitions(L.E) > 0:
-        # forward-backward pass over the trimmed E8 automaton: 8 flops per
-        # transition per block, on the float64 vector units
-        flops = m * (n // d) * 8.0 * mpq_e8dp_transitions(L.E)
-        achieved = flops / per_launch_s / 1e12
-        return dict(base, bound="alu", achieved=achieved, peak=PEAK_FP64_VALU_TFLOPS, unit="TFLOP/s",
-                    frac=achieved / PEAK_FP64_VALU_TFLOPS, path="E8 forward-backward (float64)")
-    if best == "denoise":
-        evals = m * (n // d) * K
-        if d == 8:
-            flops = evals * LATTICE_FLOP_PER_EVAL
-            peak = LATTICE_FLOP_PER_EVAL * EXP_RATE / 1e12
-        else:
-            flops = evals * SCALAR_FLOP_PER_EVAL
-            peak = SCALAR_FLOP_PER_EVAL * EXP_RATE / 1e12
-        achieved = flops / per_launch_s / 1e12
-        out = dict(base, bound="alu", achieved=achieved, peak=peak, unit="TFLOP/s", frac=achieved / peak)
-        if d == 8:
-            # the same launch against the bf16 matrix cores: per 16 queries x 32 codewords
-            # it issues two score and two weighted-sum 16x16x32 MFMAs (128 flops per eval)
-            mf = evals * LATTICE_MFMA_FLOP_PER_EVAL / per_launch_s / 1e12
-            out["secondary"] = dict(bound="mfma", achieved=mf, peak=PEAK_BF16_MFMA_TFLOPS, unit="TFLOP/s",
-                                    frac=mf / PEAK_BF16_MFMA_TFLOPS)
-        return out
-    if best in ("linear1", "linear2"):
-        # float32-accurate m x n x r product issued as split-bf16 MFMAs: six
-        # bf16 cross products per float32 product, priced at the bf16 peak
-        flops = 2.0 * m * n * r
-        fp32_equiv = flops / per_launch_s / 1e12
-        achieved = SPLIT_BF16_PRODUCTS * fp32_equiv
-        return dict(base, bound="mfma", achieved=achieved, peak=PEAK_BF16_MFMA_TFLOPS, unit="TFLOP/s",
-                    frac=achieved / PEAK_BF16_MFMA_TFLOPS,
-                    secondary=dict(bound="mfma", achieved=fp32_equiv, peak=PEAK_FP32_MFMA_TFLOPS, unit="TFLOP/s",
-                                   frac=fp32_equiv / PEAK_FP32_MFMA_TFLOPS,
-                                   basis="float32-equivalent vs the fp32 MFMA peak"))
-    if best == "cd_score" and d == 8:
-        # every sweep scores every codeword for every (row, block): one bf16
-        # 16x16x32 MFMA per 16 rows x 16 codewords issues 64 flops per eval
-        # (the three-way split of q, the t terms); the method's own work is 2d
-        # flops per eval (e . q)
-        evals = float(steps) * n_cd * m * (n // d) * K
-        secs = ms / 1e3
-        issued = evals * CD_MFMA_FLOP_PER_EVAL / secs / 1e12
-        algo = evals * 2.0 * d / secs / 1e12
-        return dict(base, bound="mfma", achieved=issued, peak=PEAK_BF16_MFMA_TFLOPS, unit="TFLOP/s",
-                    frac=issued / PEAK_BF16_MFMA_TFLOPS,
-                    secondary=dict(bound="mfma", achieved=algo, peak=PEAK_FP32_MFMA_TFLOPS, unit="TFLOP/s",
-                                   frac=algo / PEAK_FP32_MFMA_TFLOPS,
-                                   basis="2d flops per eval (float32-equivalent) vs the fp32 MFMA peak"))
-    return dict(base, bound="alu", achieved=None, peak=None, unit="TFLOP/s", frac=None)
+    w = group_work(L, best, launches if best != "cd_score" else 0, steps, n_cd)
+    if w is None:
+        return dict(base, bound="alu", achieved=None, peak=None, unit="TFLOP/s", frac=None)
+    flops, peak, bound, basis = w
+    achieved = flops / (ms / 1e3) / 1e12
+    out = dict(base, bound=bound, achieved=achieved, peak=peak, unit="TFLOP/s", frac=achieved / peak, basis=basis)
+    if best == "cd_score":
+        issued = flops / (2.0 * L.d) * CD_MFMA_FLOP_PER_EVAL / (ms / 1e3) / 1e12
+        out["secondary"] = dict(bound="mfma", achieved=issued, peak=PEAK_BF16_MFMA_TFLOPS, unit="TFLOP/s",
+                                frac=issued / PEAK_BF16_MFMA_TFLOPS,
+                                basis=f"bf16 MFMA flops as issued ({CD_MFMA_FLOP_PER_EVAL} per eval: split query "
+                                      "terms and the quadratic key), not the method's work")
+    return out
+
+
+def denoise_linear_fraction(L, prof, steps):
+    """mpq_denoise + mpq_linear together: (a) the fraction of their measured
+    time the issuing units would need at peak for the method's algorithmic
+    work (sum of work / peak over the sum of times); (b) the work as the
+    target counts it (32 flops per block x codeword eval, 4mnr per iteration)
+    over the same time, against the fp32 MFMA peak."""
+    keys = [k for k in ("denoise", "linear1", "linear2") if k in prof]
+    secs = sum(prof[k][0] for k in keys) / 1e3
+    if secs <= 0:
+        return None
+    need = 0.0
+    for k in keys:
+        w = group_work(L, k, prof[k][1], steps, L.n_cd)
+        if w is None:
+            return None
+        need += w[0] / (w[1] * 1e12)
+    T = L.T_vamp * steps
+    target_flops = T * (L.m * (L.n // L.d) * L.K * NORTH_STAR_EVAL_FLOPS + 4.0 * L.m * L.n * L.r)
+    return dict(seconds=secs, frac_of_issuing_peaks=need / secs,
+                target_count_tflops=target_flops / secs / 1e12,
+                target_count_frac_fp32=target_flops / secs / 1e12 / PEAK_FP32_MFMA_TFLOPS,
+                basis="(a) sum over denoise, linear 1, linear 2 of algorithmic work / peak of the issued dtype, "
+                      "over their summed time; (b) 32 flops per (block, codeword) eval + 4mnr per iteration over "
+                      "the same time, against the fp32 MFMA peak (the E8 path does far less work than that count)")
 
 
 def measured_peak(roof, probes):
     """The probed counterpart of roof["peak"] (same unit), or None."""
     if roof["peak"] is None:
         return None
+    if roof["kernel"] in ("linear1", "linear2"):
+        return probes["mfma_f64_tflops"]
     if roof["bound"] == "mfma":
         return probes["mfma_bf16_tflops"]
-    if roof.get("path", "").startswith("E8 forward-backward"):
+    if roof.get("basis", "").startswith("E8 forward-backward"):
         return probes["valu_f64_tflops"]
     if roof["kernel"] == "denoise":
         # exponential-bound scan: the vendor-derived peak scales with the exp rate
@@ -162,6 +177,13 @@ def cpu_baseline(L, rows_count, gpu_codes):
     t0 = time.perf_counter()
     res = solve_rows(L, rows, max_workers=len(rows))
     wall = time.perf_counter() - t0
+    model = ""
+    try:
+        import subprocess
+        txt = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        model = next((ln.split(":", 1)[1].strip() for ln in txt.splitlines() if ln.startswith("Model name")), "")
+    except Exception:  # noqa: BLE001 - the CPU model is informational
+        pass
     agree = float(np.mean([np.mean(gpu_codes[i] == r["codes"]) for i, r in zip(rows, res)]))
     def codebook(i):
         if L.group:
@@ -170,9 +192,11 @@ def cpu_baseline(L, rows_count, gpu_codes):
     obj_rel = max(abs(O.codes_objective(L.W[i], gpu_codes[i], codebook(i), L.d, L.s, L.V)
                       - r["objective"]) / r["objective"] for i, r in zip(rows, res))
     value = len(rows) * L.n / wall
-    return dict(value=value, unit="weights/s", cores=len(rows), kind="oracle",
+    return dict(value=value, unit="weights/s", cores=min(len(rows), os.cpu_count() or 1), kind="oracle",
+                host_cpus=os.cpu_count(), cpu_model=model, workers=len(rows),
                 sample=f"{len(rows)} rows (every {max(L.m // len(rows), 1)}-th) of the same layer through the "
-                       f"whole pipeline, one single-threaded float64 NumPy worker per row; wall {wall:.1f} s",
+                       f"whole pipeline, one single-threaded float64 NumPy worker process per row on "
+                       f"{os.cpu_count()} host CPUs; wall {wall:.1f} s",
                 parity=dict(rows=len(rows), code_agreement=agree, obj_rel_max=obj_rel))
 
 
@@ -252,19 +276,21 @@ def main():
     W, s, V, a, o = t(L.W), t(L.s), t(L.V), t(L.a), t(L.o)
     ws = torch.empty(mpq.workspace_bytes(L.m, L.n, L.r, L.K, L.d), dtype=torch.uint8, device=dev)
     kw = dict(T_vamp=L.T_vamp, n_cd=L.n_cd, damping=L.damping, workspace=ws, group=L.group)
+    cb = mpq.prepare_codebook(L.E, dev)   # the codebook's device tables, once per layer
     out = None
     for k in range(args.warmup):
-        out = mpq.quantize_layer(W, s, V, L.E, a, o, outputs=out, **kw)
+        out = mpq.quantize_layer(W, s, V, cb, a, o, outputs=out, **kw)
         torch.cuda.synchronize()
         log(f"[bench] warmup {k + 1}/{args.warmup} done")
 
     # timed region: K steps; the single-kernel groups are event-timed on the
-    # library's streams (the CD scoring launches one in 32, scaled to all)
-    prof = mpq.Profile(("denoise", "linear1", "linear2", "cd_score"), sampled=True)
+    # library's stream (the CD scoring launches one in 32, priced at their mean)
+    prof = mpq.Profile(("denoise", "linear1", "linear2", "cd_score"), sampled=True, capacity=4096)
+    full = mpq.Profile(capacity=32768)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
-        out = mpq.quantize_layer(W, s, V, L.E, a, o, outputs=out, profile=prof, **kw)
+        out = mpq.quantize_layer(W, s, V, cb, a, o, outputs=out, profile=prof, **kw)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = elapsed * 1e3 / args.steps
@@ -273,8 +299,7 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_per_step:.1f} ms/step, {value / 1e6:.3f} M weights/s")
 
     # one extra profiled step with every kernel group for the time split
-    full = mpq.Profile()
-    out = mpq.quantize_layer(W, s, V, L.E, a, o, outputs=out, profile=full, **kw)
+    out = mpq.quantize_layer(W, s, V, cb, a, o, outputs=out, profile=full, **kw)
     torch.cuda.synchronize()
     split = {k: round(v[0], 3) for k, v in full.as_dict().items()}
     log(f"[bench] kernel ms per step: {split}")
@@ -284,6 +309,7 @@ def main():
                                  if k in ("denoise", "linear1", "linear2", "cd_score")},
                              args.steps, L.n_cd)
     roof["traffic"] = measured_traffic(args.config, roof["kernel"])
+    dl = denoise_linear_fraction(L, timed_prof, args.steps)
     codes = out["codes"].cpu().numpy()
 
     # achievable rates of the instructions the kernels are bound by, probed on
@@ -308,7 +334,7 @@ def main():
         log(f"[bench] oracle {cpu['value']:.1f} weights/s; parity on its rows {cpu['parity']}")
 
     line = dict(metric=METRIC, value=value, unit="weights/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
-                ms_per_step=ms_per_step, higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
+                ms_per_step=ms_per_step, higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f64",
                 data="synthetic",
                 config=dict(workload=f"{args.config}: {WORKLOADS[args.config]}" +
                             (f", group-wise grids of {L.group} columns" if L.group else ""), m=L.m, n=L.n, r=L.r,
@@ -317,11 +343,11 @@ def main():
                 roofline=dict(bound=roof["bound"], achieved=roof["achieved"], peak=roof["peak"], unit=roof["unit"],
                               frac=roof["frac"], traffic=roof["traffic"], kernel=roof["kernel"],
                               avg_launch_ms=roof["avg_ms"], launches=roof["launches"],
-                              **({"path": roof["path"]} if "path" in roof else {}),
+                              **({"basis": roof["basis"]} if "basis" in roof else {}),
                               **({"measured_peak": roof["measured_peak"], "frac_of_measured": roof["frac_of_measured"]}
                                  if "measured_peak" in roof else {}),
                               **({"secondary": roof["secondary"]} if "secondary" in roof else {})),
-                measured_peaks=probes, kernel_ms_per_step=split, cpu_baseline=cpu)
+                denoise_linear=dl, measured_peaks=probes, kernel_ms_per_step=split, cpu_baseline=cpu)
     print(json.dumps(line), flush=True)
 
 

@@ -1,10 +1,12 @@
 """ctypes binding of libmpq.so (the C ABI in include/mpq.h).
 
 Argument marshalling only: every step of the solve runs in the library's HIP
-kernels.  Tensors are torch tensors on the GPU (float32 / int32, contiguous);
-the base codebook is a CPU float32 tensor or numpy array.  Work is enqueued on
-torch's current stream.  If the library is missing or fails to load, every
-call raises -- there is no CPU fallback.
+kernels.  Tensors are torch tensors on the GPU (float32 inputs, float64 VAMP
+state, int32 codes; contiguous); a base codebook is a CPU float32 tensor or
+numpy array, prepared once into device tables by `prepare_codebook` (the entry
+points also accept the raw codebook and prepare it on the spot).  Work is
+enqueued on torch's current stream.  If the library is missing or fails to
+load, every call raises -- there is no CPU fallback.
 """
 from __future__ import annotations
 
@@ -19,13 +21,15 @@ LIB_PATH = os.path.join(HERE, "libmpq.so")
 STATUS = {
     0: "MPQ_OK", -1: "MPQ_ENULL", -2: "MPQ_ESHAPE", -3: "MPQ_EPARAM",
     -4: "MPQ_EUNSUPPORTED", -5: "MPQ_EWORKSPACE", -6: "MPQ_EHIP", -7: "MPQ_ESOLVER",
+    -8: "MPQ_ENONFINITE", -9: "MPQ_EHOST",
 }
-F_FIXED_BETA = 1
 
-EXPORTS = ("mpq_workspace_bytes", "mpq_strerror", "mpq_quantize_layer", "mpq_prologue", "mpq_denoise",
-           "mpq_vamp_step", "mpq_map", "mpq_cd", "mpq_objective", "mpq_greedy", "mpq_greedy_workspace_bytes",
-           "mpq_gram_workspace_bytes", "mpq_gram", "mpq_rht", "mpq_factor_workspace_bytes", "mpq_factor",
-           "mpq_codebook_kind", "mpq_hip_error_name", "mpq_e8dp_transitions", "mpq_probe_rate")
+EXPORTS = ("mpq_workspace_bytes", "mpq_strerror", "mpq_codebook_bytes", "mpq_codebook_prepare",
+           "mpq_profiler_create", "mpq_profiler_destroy", "mpq_quantize_layer", "mpq_prologue", "mpq_denoise",
+           "mpq_vamp_step", "mpq_linear_step", "mpq_map", "mpq_cd", "mpq_objective", "mpq_greedy",
+           "mpq_greedy_workspace_bytes", "mpq_gram_workspace_bytes", "mpq_gram", "mpq_rht",
+           "mpq_factor_workspace_bytes", "mpq_factor", "mpq_codebook_kind", "mpq_hip_error_name",
+           "mpq_e8dp_transitions", "mpq_probe_rate")
 
 
 class MPQError(RuntimeError):
@@ -40,38 +44,94 @@ class MPQError(RuntimeError):
         super().__init__(f"{what} failed: {STATUS.get(status, status)} ({detail})")
 
 
+F_FIXED_BETA = 1
 F_PROFILE = 2
 F_NO_E8DP = 4
-F_NO_E8_DECODE = 16
 F_PROFILE_SAMPLED = 8
+F_NO_E8_DECODE = 16
+F_CHECK_FINITE = 32
 PROF_NAMES = ("prologue", "denoise", "extrinsic", "linear1", "beta", "linear2", "map", "cd_gemm", "cd_search",
               "other", "denoise_exact", "cd_score")
 PROF_COUNT = len(PROF_NAMES)
 
 
+class Codebook(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int64), ("d", ctypes.c_int64), ("kind", ctypes.c_int32),
+                ("e8_qlast", ctypes.c_int32), ("e8_last2", ctypes.c_int32 * 8), ("tables", ctypes.c_void_p),
+                ("magic", ctypes.c_uint64)]
+
+
 class Options(ctypes.Structure):
-    _fields_ = [("beta0", ctypes.c_float), ("flags", ctypes.c_uint32), ("prof_mask", ctypes.c_uint32),
-                ("prof_ms", ctypes.POINTER(ctypes.c_double)), ("prof_launches", ctypes.POINTER(ctypes.c_int64)),
+    _fields_ = [("beta0", ctypes.c_float), ("flags", ctypes.c_uint32), ("safeguard_eps", ctypes.c_float),
                 ("anchor_tau", ctypes.c_float), ("anchor_w", ctypes.c_void_p), ("group", ctypes.c_int64),
-                ("map_codes", ctypes.c_void_p), ("objective", ctypes.c_void_p)]
+                ("profiler", ctypes.c_void_p), ("prof_mask", ctypes.c_uint32),
+                ("prof_ms", ctypes.POINTER(ctypes.c_double)), ("prof_launches", ctypes.POINTER(ctypes.c_int64)),
+                ("map_codes", ctypes.c_void_p), ("objective", ctypes.c_void_p), ("fallbacks", ctypes.c_void_p),
+                ("sweeps", ctypes.c_void_p)]
+
+
+class PreparedCodebook:
+    """A codebook's device tables (mpq_codebook_prepare) and its host copy."""
+
+    def __init__(self, cb, device="cuda"):
+        import torch
+        E = _host_codebook(cb)
+        self.E = E
+        self.K, self.d = E.shape
+        lib = load_library()
+        nb = int(lib.mpq_codebook_bytes(self.K, self.d))
+        if nb == 0:
+            raise MPQError(-2, "mpq_codebook_bytes")
+        self.tables = torch.empty(nb, dtype=torch.uint8, device=device)
+        self.struct = Codebook()
+        rc = lib.mpq_codebook_prepare(E.ctypes.data_as(ctypes.c_void_p), self.K, self.d, _ptr(self.tables), nb,
+                                      _stream(), ctypes.byref(self.struct))
+        _check(rc, "mpq_codebook_prepare")
+
+    @property
+    def kind(self) -> str:
+        return "e8_prefix" if self.struct.kind == 1 else "generic"
+
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def prepare_codebook(cb, device="cuda") -> PreparedCodebook:
+    """Prepare a base codebook (K x d, host) once into device tables."""
+    return cb if isinstance(cb, PreparedCodebook) else PreparedCodebook(cb, device)
 
 
 class Profile:
-    """Host accumulators for the library's per-category event timing.
-    sampled: time one CD scoring launch in 32 and scale to all of them
-    (MPQ_F_PROFILE_SAMPLED), which keeps event creation from slowing the call."""
+    """Host accumulators for the library's per-category event timing, with
+    the event pairs (an mpq_profiler) created once.  sampled: time one CD
+    scoring launch in 32 and price the rest at their mean
+    (MPQ_F_PROFILE_SAMPLED)."""
 
-    def __init__(self, categories=PROF_NAMES, sampled=False):
+    def __init__(self, categories=PROF_NAMES, sampled=False, capacity=4096):
         self.sampled = bool(sampled)
         self.ms = (ctypes.c_double * PROF_COUNT)()
         self.launches = (ctypes.c_int64 * PROF_COUNT)()
         self.mask = 0
         for c in categories:
             self.mask |= 1 << PROF_NAMES.index(c)
+        self._lib = load_library()
+        self.handle = ctypes.c_void_p()
+        _check(self._lib.mpq_profiler_create(int(capacity), ctypes.byref(self.handle)), "mpq_profiler_create")
+
+    def reset(self):
+        for k in range(PROF_COUNT):
+            self.ms[k] = 0.0
+            self.launches[k] = 0
 
     def as_dict(self):
         return {nm: (float(self.ms[k]), int(self.launches[k])) for k, nm in enumerate(PROF_NAMES)
                 if self.mask >> k & 1}
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            self._lib.mpq_profiler_destroy(h)
+            self.handle = ctypes.c_void_p()
 
 
 _lib = None
@@ -101,20 +161,26 @@ def load_library(path: str = LIB_PATH):
     F = ctypes.c_float
     SZ = ctypes.c_size_t
     OPT = ctypes.POINTER(Options)
+    CB = ctypes.POINTER(Codebook)
     lib.mpq_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
     lib.mpq_workspace_bytes.restype = SZ
     lib.mpq_strerror.argtypes = [I]
     lib.mpq_strerror.restype = ctypes.c_char_p
-    lib.mpq_quantize_layer.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, I, I, F, OPT,
-                                       P, P, P, P, P, P, SZ, P]
-    lib.mpq_prologue.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, OPT, P, P, P, P, P, SZ, P]
-    lib.mpq_denoise.argtypes = [P, P, I64, I64, P, I64, I64, P, P, OPT, P, P, P, SZ, P]
-    lib.mpq_vamp_step.argtypes = [P, P, P, P, I64, I64, P, P, I64, P, I64, I64, P, P, F, OPT,
-                                  P, P, P, P, P, P, SZ, P]
-    lib.mpq_map.argtypes = [P, P, I64, I64, P, I64, I64, P, P, OPT, P, P, SZ, P]
-    lib.mpq_cd.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, I, OPT, P, P, P, SZ, P]
-    lib.mpq_objective.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, OPT, P, P, P, SZ, P]
-    lib.mpq_greedy.argtypes = [P, I64, I64, P, P, I64, P, I64, I64, P, P, OPT, P, P, SZ, P]
+    lib.mpq_codebook_bytes.argtypes = [I64, I64]
+    lib.mpq_codebook_bytes.restype = SZ
+    lib.mpq_codebook_prepare.argtypes = [P, I64, I64, P, SZ, P, CB]
+    lib.mpq_profiler_create.argtypes = [I, ctypes.POINTER(ctypes.c_void_p)]
+    lib.mpq_profiler_destroy.argtypes = [P]
+    lib.mpq_profiler_destroy.restype = None
+    lib.mpq_quantize_layer.argtypes = [P, I64, I64, P, P, I64, CB, P, P, I, I, F, OPT, P, P, P, P, P, P, SZ, P]
+    lib.mpq_prologue.argtypes = [P, I64, I64, P, P, I64, CB, P, P, OPT, P, P, P, P, SZ, P]
+    lib.mpq_denoise.argtypes = [P, P, I64, I64, CB, P, P, OPT, P, P, P, SZ, P]
+    lib.mpq_vamp_step.argtypes = [P, P, P, P, I64, I64, P, P, I64, CB, P, P, F, OPT, P, P, P, P, P, P, SZ, P]
+    lib.mpq_linear_step.argtypes = [P, P, P, P, I64, I64, P, P, I64, F, OPT, P, P, P, SZ, P]
+    lib.mpq_map.argtypes = [P, P, I64, I64, CB, P, P, OPT, P, P, SZ, P]
+    lib.mpq_cd.argtypes = [P, I64, I64, P, P, I64, CB, P, P, I, OPT, P, P, P, SZ, P]
+    lib.mpq_objective.argtypes = [P, I64, I64, P, P, I64, CB, P, P, OPT, P, P, P, SZ, P]
+    lib.mpq_greedy.argtypes = [P, I64, I64, P, P, I64, CB, P, P, OPT, P, P, SZ, P]
     lib.mpq_greedy_workspace_bytes.argtypes = [I64, I64, I64, I64, I64]
     lib.mpq_greedy_workspace_bytes.restype = SZ
     lib.mpq_gram_workspace_bytes.argtypes = [I64]
@@ -131,7 +197,7 @@ def load_library(path: str = LIB_PATH):
     lib.mpq_hip_error_name.restype = ctypes.c_char_p
     lib.mpq_probe_rate.argtypes = [I, P, SZ, ctypes.POINTER(ctypes.c_double), P]
     for name in EXPORTS[2:]:
-        if name.endswith("_bytes") or name in ("mpq_hip_error_name", "mpq_e8dp_transitions"):
+        if name.endswith("_bytes") or name in ("mpq_hip_error_name", "mpq_e8dp_transitions", "mpq_profiler_destroy"):
             continue
         getattr(lib, name).restype = I
     _lib = lib
@@ -148,7 +214,7 @@ def _strerror(status: int) -> str:
 def codebook_kind(cb) -> str:
     """'e8_prefix' if the codebook is the first K points of E8 in (norm, lex)
     order (the forward-backward denoiser applies), else 'generic'."""
-    E = _host_codebook(cb)
+    E = _host_codebook(cb.E if isinstance(cb, PreparedCodebook) else cb)
     rc = load_library().mpq_codebook_kind(E.ctypes.data_as(ctypes.c_void_p), E.shape[0], E.shape[1])
     if rc < 0:
         raise MPQError(rc, "mpq_codebook_kind")
@@ -157,7 +223,7 @@ def codebook_kind(cb) -> str:
 
 def e8dp_transitions(cb) -> int:
     """Valid transitions of an E8-prefix codebook's automaton (0 otherwise)."""
-    E = _host_codebook(cb)
+    E = _host_codebook(cb.E if isinstance(cb, PreparedCodebook) else cb)
     if E.shape[1] != 8:
         return 0
     return int(load_library().mpq_e8dp_transitions(E.ctypes.data_as(ctypes.c_void_p), E.shape[0]))
@@ -235,15 +301,28 @@ def _workspace(m, n, r, K, d, device):
 
 
 def _opts(beta0=None, fixed_beta=False, profile=None, anchor_tau=None, anchor_w=None, group=None, map_codes=None,
-          objective=None, scan_denoiser=False, e8_decode=True):
+          objective=None, scan_denoiser=False, e8_decode=True, safeguard_eps=0.0, fallbacks=None, sweeps=None,
+          check_finite=False):
     flags = ((F_FIXED_BETA if fixed_beta else 0) | (F_PROFILE if profile is not None else 0) |
              (F_PROFILE_SAMPLED if profile is not None and profile.sampled else 0) |
-             (F_NO_E8DP if scan_denoiser else 0) | (0 if e8_decode else F_NO_E8_DECODE))
-    o = Options(float(beta0) if beta0 else 0.0, flags, profile.mask if profile is not None else 0,
-                profile.ms if profile is not None else None, profile.launches if profile is not None else None,
-                float(anchor_tau) if anchor_tau else 0.0, anchor_w.data_ptr() if anchor_w is not None else None,
-                int(group) if group else 0, map_codes.data_ptr() if map_codes is not None else None,
-                objective.data_ptr() if objective is not None else None)
+             (F_NO_E8DP if scan_denoiser else 0) | (0 if e8_decode else F_NO_E8_DECODE) |
+             (F_CHECK_FINITE if check_finite else 0))
+    o = Options()
+    o.beta0 = float(beta0) if beta0 else 0.0
+    o.flags = flags
+    o.safeguard_eps = float(safeguard_eps or 0.0)
+    o.anchor_tau = float(anchor_tau) if anchor_tau else 0.0
+    o.anchor_w = anchor_w.data_ptr() if anchor_w is not None else None
+    o.group = int(group) if group else 0
+    if profile is not None:
+        o.profiler = profile.handle
+        o.prof_mask = profile.mask
+        o.prof_ms = profile.ms
+        o.prof_launches = profile.launches
+    o.map_codes = map_codes.data_ptr() if map_codes is not None else None
+    o.objective = objective.data_ptr() if objective is not None else None
+    o.fallbacks = fallbacks.data_ptr() if fallbacks is not None else None
+    o.sweeps = sweeps.data_ptr() if sweeps is not None else None
     return ctypes.byref(o), o
 
 
@@ -267,23 +346,25 @@ def _check(rc, what):
 
 def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, damping=0.5, beta0=None,
                    fixed_beta=False, workspace=None, traces=True, profile=None, outputs=None, anchor_tau=None,
-                   group=None, diagnostics=False, scan_denoiser=False):
+                   group=None, diagnostics=False, scan_denoiser=False, safeguard_eps=0.0, check_finite=False):
     """Full MPQ solve of one layer (mpq_quantize_layer).
 
+    `cb`: a PreparedCodebook (prepare_codebook) or a raw K x d codebook.
     Returns dict(codes, beta_tr, gamma1_tr, gamma2_tr, cd_changes) of device
     tensors.  `profile` (a Profile) turns on the library's event timing;
     `outputs` (a dict from a previous call) reuses its output tensors;
     `anchor_tau` > 0 selects the anchored codebook prior (None: uniform);
     `group` > 0 gives every `group` consecutive columns their own affine
     (row_scale and row_offset then m x ceil(n / group)); `diagnostics` adds
-    map_codes (the marginal-MAP codes CD starts from) and objective (float64,
-    per row) to the result.
+    map_codes (the marginal-MAP codes CD starts from), objective (float64,
+    per row), fallbacks (pass-through events per row) and sweeps (CD sweeps
+    run per row) to the result.
     """
     import torch
     m, n = W.shape
     r = s.shape[0]
-    E = _host_codebook(cb)
-    K, d = E.shape
+    P = prepare_codebook(cb, W.device)
+    K, d = P.K, P.d
     dev = W.device
     _dev(W, torch.float32, "W")
     _dev(s, torch.float32, "s", (r,))
@@ -300,105 +381,130 @@ def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, dampin
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
     mc = torch.empty((m, n // d), dtype=torch.int32, device=dev) if diagnostics else None
     obj = torch.empty(m, dtype=torch.float64, device=dev) if diagnostics else None
-    op, _keep = _opts(beta0, fixed_beta, profile, anchor_tau, None, group, mc, obj, scan_denoiser)
+    fb = torch.empty(m, dtype=torch.int32, device=dev) if diagnostics else None
+    sw = torch.empty(m, dtype=torch.int32, device=dev) if diagnostics else None
+    op, _keep = _opts(beta0, fixed_beta, profile, anchor_tau, None, group, mc, obj, scan_denoiser,
+                      safeguard_eps=safeguard_eps, fallbacks=fb, sweeps=sw, check_finite=check_finite)
     rc = load_library().mpq_quantize_layer(
-        _ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d, _ptr(row_scale),
-        _ptr(row_offset), int(T_vamp), int(n_cd), float(damping), op, _ptr(codes), _ptr(bt), _ptr(g1), _ptr(g2),
-        _ptr(ch), _ptr(ws), ws.numel(), _stream())
+        _ptr(W), m, n, _ptr(s), _ptr(V), r, P.ref(), _ptr(row_scale), _ptr(row_offset), int(T_vamp), int(n_cd),
+        float(damping), op, _ptr(codes), _ptr(bt), _ptr(g1), _ptr(g2), _ptr(ch), _ptr(ws), ws.numel(), _stream())
     _check(rc, "mpq_quantize_layer")
     out = dict(codes=codes, beta_tr=bt, gamma1_tr=g1, gamma2_tr=g2, cd_changes=ch)
     if diagnostics:
-        out.update(map_codes=mc, objective=obj)
+        out.update(map_codes=mc, objective=obj, fallbacks=fb, sweeps=sw)
     return out
 
 
 def prologue(W, s, V, cb, row_scale, row_offset, beta0=None, workspace=None, group=None):
+    """RTN codes, gamma1^0 and beta^0 of every row (mpq_prologue); float64 scalars."""
     import torch
     m, n = W.shape
     r = s.shape[0]
-    E = _host_codebook(cb)
-    K, d = E.shape
+    P = prepare_codebook(cb, W.device)
+    K, d = P.K, P.d
     dev = W.device
-    ytil = torch.empty((m, r), dtype=torch.float32, device=dev)
     rtn = torch.empty((m, n // d), dtype=torch.int32, device=dev)
-    gamma1 = torch.empty(m, dtype=torch.float32, device=dev)
-    beta = torch.empty(m, dtype=torch.float32, device=dev)
+    gamma1 = torch.empty(m, dtype=torch.float64, device=dev)
+    beta = torch.empty(m, dtype=torch.float64, device=dev)
     _affine(row_scale, row_offset, m, n, group)
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
     op, _keep = _opts(beta0, group=group)
-    rc = load_library().mpq_prologue(_ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d,
-                                     _ptr(row_scale), _ptr(row_offset), op, _ptr(ytil), _ptr(rtn), _ptr(gamma1),
-                                     _ptr(beta), _ptr(ws), ws.numel(), _stream())
+    rc = load_library().mpq_prologue(_ptr(W), m, n, _ptr(s), _ptr(V), r, P.ref(), _ptr(row_scale),
+                                     _ptr(row_offset), op, _ptr(rtn), _ptr(gamma1), _ptr(beta), _ptr(ws), ws.numel(),
+                                     _stream())
     _check(rc, "mpq_prologue")
-    return dict(ytil=ytil, rtn_codes=rtn, gamma1=gamma1, beta=beta)
+    return dict(rtn_codes=rtn, gamma1=gamma1, beta=beta)
 
 
 def denoise(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=None, W=None, group=None,
             scan_denoiser=False):
-    """Blockwise denoiser (mpq_denoise): (xhat1, per-block variance trace).
+    """Blockwise denoiser (mpq_denoise): (xhat1, per-block variance trace), float64.
     `scan_denoiser` forces the codebook-scan kernel for E8-prefix codebooks."""
     import torch
     m, n = R1.shape
-    E = _host_codebook(cb)
-    K, d = E.shape
+    P = prepare_codebook(cb, R1.device)
+    K, d = P.K, P.d
     dev = R1.device
-    _dev(R1, torch.float32, "R1")
-    _dev(gamma1, torch.float32, "gamma1", (m,))
+    _dev(R1, torch.float64, "R1")
+    _dev(gamma1, torch.float64, "gamma1", (m,))
     _affine(row_scale, row_offset, m, n, group)
     if anchor_tau:
         _dev(W, torch.float32, "W", (m, n))
     xhat = torch.empty_like(R1)
-    vtr = torch.empty((m, n // d), dtype=torch.float32, device=dev)
+    vtr = torch.empty((m, n // d), dtype=torch.float64, device=dev)
     ws = workspace if workspace is not None else _workspace(m, n, n, K, d, dev)
     op, _keep = _opts(anchor_tau=anchor_tau, anchor_w=W, group=group, scan_denoiser=scan_denoiser)
-    rc = load_library().mpq_denoise(_ptr(R1), _ptr(gamma1), m, n, E.ctypes.data_as(ctypes.c_void_p), K, d,
-                                    _ptr(row_scale), _ptr(row_offset), op, _ptr(xhat), _ptr(vtr), _ptr(ws),
-                                    ws.numel(), _stream())
+    rc = load_library().mpq_denoise(_ptr(R1), _ptr(gamma1), m, n, P.ref(), _ptr(row_scale), _ptr(row_offset), op,
+                                    _ptr(xhat), _ptr(vtr), _ptr(ws), ws.numel(), _stream())
     _check(rc, "mpq_denoise")
     return xhat, vtr
 
 
-def vamp_step(R1, gamma1, beta, ytil, s, V, cb, row_scale, row_offset, damping=0.5, fixed_beta=False,
-              workspace=None, anchor_tau=None, W=None, group=None):
-    """One VAMP iteration in place on (R1, gamma1, beta); returns the diagnostics.
-    With `anchor_tau` > 0 the prior is anchored at the weights `W`."""
+def vamp_step(R1, gamma1, beta, W, s, V, cb, row_scale, row_offset, damping=0.5, fixed_beta=False,
+              workspace=None, anchor_tau=None, group=None, safeguard_eps=0.0):
+    """One VAMP iteration in place on (R1, gamma1, beta) (float64); returns the
+    diagnostics.  W: the layer's weights (float32); with `anchor_tau` > 0 the
+    prior is anchored at W."""
     import torch
     m, n = R1.shape
     r = s.shape[0]
-    E = _host_codebook(cb)
-    K, d = E.shape
+    P = prepare_codebook(cb, R1.device)
+    K, d = P.K, P.d
     dev = R1.device
-    for t, nm in ((R1, "R1"), (gamma1, "gamma1"), (beta, "beta"), (ytil, "ytil")):
-        _dev(t, torch.float32, nm)
+    for t, nm in ((R1, "R1"), (gamma1, "gamma1"), (beta, "beta")):
+        _dev(t, torch.float64, nm)
+    _dev(W, torch.float32, "W", (m, n))
     xhat = torch.empty_like(R1)
     r2 = torch.empty_like(R1)
-    eta1 = torch.empty(m, dtype=torch.float32, device=dev)
-    gamma2 = torch.empty(m, dtype=torch.float32, device=dev)
+    eta1 = torch.empty(m, dtype=torch.float64, device=dev)
+    gamma2 = torch.empty(m, dtype=torch.float64, device=dev)
     fb = torch.empty(m, dtype=torch.int32, device=dev)
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
     _affine(row_scale, row_offset, m, n, group)
-    if anchor_tau:
-        _dev(W, torch.float32, "W", (m, n))
-    op, _keep = _opts(None, fixed_beta, None, anchor_tau, W, group)
-    rc = load_library().mpq_vamp_step(_ptr(R1), _ptr(gamma1), _ptr(beta), _ptr(ytil), m, n, _ptr(s), _ptr(V), r,
-                                      E.ctypes.data_as(ctypes.c_void_p), K, d, _ptr(row_scale), _ptr(row_offset),
-                                      float(damping), op, _ptr(xhat), _ptr(eta1), _ptr(gamma2), _ptr(r2), _ptr(fb),
-                                      _ptr(ws), ws.numel(), _stream())
+    op, _keep = _opts(None, fixed_beta, None, anchor_tau, W if anchor_tau else None, group,
+                      safeguard_eps=safeguard_eps)
+    rc = load_library().mpq_vamp_step(_ptr(R1), _ptr(gamma1), _ptr(beta), _ptr(W), m, n, _ptr(s), _ptr(V), r,
+                                      P.ref(), _ptr(row_scale), _ptr(row_offset), float(damping), op, _ptr(xhat),
+                                      _ptr(eta1), _ptr(gamma2), _ptr(r2), _ptr(fb), _ptr(ws), ws.numel(), _stream())
     _check(rc, "mpq_vamp_step")
     return dict(xhat1=xhat, eta1=eta1, gamma2=gamma2, r2=r2, fallback=fb)
 
 
+def linear_step(R2, gamma2, beta, W, s, V, damping=0.5, fixed_beta=False, workspace=None):
+    """The Gaussian linear module + beta M-step (mpq_linear_step): from the
+    extrinsic message (R2, gamma2) and beta (updated in place), returns
+    (R1, gamma1), the message back to the denoiser (float64)."""
+    import torch
+    m, n = R2.shape
+    r = s.shape[0]
+    _dev(R2, torch.float64, "R2")
+    _dev(gamma2, torch.float64, "gamma2", (m,))
+    _dev(beta, torch.float64, "beta", (m,))
+    _dev(W, torch.float32, "W", (m, n))
+    _dev(s, torch.float32, "s", (r,))
+    _dev(V, torch.float32, "V", (n, r))
+    R1 = torch.empty_like(R2)
+    gamma1 = torch.empty_like(gamma2)
+    ws = workspace if workspace is not None else _workspace(m, n, r, 2, 1, R2.device)
+    op, _keep = _opts(None, fixed_beta)
+    rc = load_library().mpq_linear_step(_ptr(R2), _ptr(gamma2), _ptr(beta), _ptr(W), m, n, _ptr(s), _ptr(V), r,
+                                        float(damping), op, _ptr(R1), _ptr(gamma1), _ptr(ws), ws.numel(), _stream())
+    _check(rc, "mpq_linear_step")
+    return R1, gamma1
+
+
 def map_codes(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=None, W=None, group=None,
               scan_denoiser=False, e8_decode=True):
-    """Marginal MAP codes (mpq_map); scan_denoiser keeps the codebook scan for
-    E8 prefix codebooks too; e8_decode=False finds an E8 prefix codebook's
-    nearest codewords with the automaton alone (no lattice-decoder fast path)."""
+    """Marginal MAP codes (mpq_map) at float64 (R1, gamma1); scan_denoiser keeps
+    the codebook scan for E8 prefix codebooks too; e8_decode=False finds an E8
+    prefix codebook's nearest codewords with the automaton alone (no
+    lattice-decoder fast path)."""
     import torch
     m, n = R1.shape
-    E = _host_codebook(cb)
-    K, d = E.shape
-    _dev(R1, torch.float32, "R1")
-    _dev(gamma1, torch.float32, "gamma1", (m,))
+    P = prepare_codebook(cb, R1.device)
+    K, d = P.K, P.d
+    _dev(R1, torch.float64, "R1")
+    _dev(gamma1, torch.float64, "gamma1", (m,))
     _affine(row_scale, row_offset, m, n, group)
     if anchor_tau:
         _dev(W, torch.float32, "W", (m, n))
@@ -406,27 +512,28 @@ def map_codes(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=
     ws = workspace if workspace is not None else _workspace(m, n, n, K, d, R1.device)
     op, _keep = _opts(anchor_tau=anchor_tau, anchor_w=W, group=group, scan_denoiser=scan_denoiser,
                       e8_decode=e8_decode)
-    rc = load_library().mpq_map(_ptr(R1), _ptr(gamma1), m, n, E.ctypes.data_as(ctypes.c_void_p), K, d,
-                                _ptr(row_scale), _ptr(row_offset), op, _ptr(codes), _ptr(ws), ws.numel(), _stream())
+    rc = load_library().mpq_map(_ptr(R1), _ptr(gamma1), m, n, P.ref(), _ptr(row_scale), _ptr(row_offset), op,
+                                _ptr(codes), _ptr(ws), ws.numel(), _stream())
     _check(rc, "mpq_map")
     return codes
 
 
-def cd(W, s, V, cb, row_scale, row_offset, codes, n_cd=3, workspace=None, group=None):
-    """Block CD from `codes` (a device int32 tensor, updated in place)."""
+def cd(W, s, V, cb, row_scale, row_offset, codes, n_cd=3, workspace=None, group=None, sweeps=None):
+    """Block CD from `codes` (a device int32 tensor, updated in place); returns
+    (codes, changes per sweep).  `sweeps` (device int32, m) receives the
+    sweeps run per row."""
     import torch
     m, n = W.shape
     r = s.shape[0]
-    E = _host_codebook(cb)
-    K, d = E.shape
+    P = prepare_codebook(cb, W.device)
+    K, d = P.K, P.d
     _dev(codes, torch.int32, "codes", (m, n // d))
     _affine(row_scale, row_offset, m, n, group)
     ch = torch.zeros((m, max(n_cd, 1)), dtype=torch.int32, device=W.device)
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, W.device)
-    op, _keep = _opts(group=group)
-    rc = load_library().mpq_cd(_ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d,
-                               _ptr(row_scale), _ptr(row_offset), int(n_cd), op, _ptr(codes), _ptr(ch), _ptr(ws),
-                               ws.numel(), _stream())
+    op, _keep = _opts(group=group, sweeps=sweeps)
+    rc = load_library().mpq_cd(_ptr(W), m, n, _ptr(s), _ptr(V), r, P.ref(), _ptr(row_scale), _ptr(row_offset),
+                               int(n_cd), op, _ptr(codes), _ptr(ch), _ptr(ws), ws.numel(), _stream())
     _check(rc, "mpq_cd")
     return codes, ch[:, :n_cd]
 
@@ -436,8 +543,8 @@ def objective(W, s, V, cb, row_scale, row_offset, codes, workspace=None, group=N
     import torch
     m, n = W.shape
     r = s.shape[0]
-    E = _host_codebook(cb)
-    K, d = E.shape
+    P = prepare_codebook(cb, W.device)
+    K, d = P.K, P.d
     _dev(W, torch.float32, "W")
     _dev(s, torch.float32, "s", (r,))
     _dev(V, torch.float32, "V", (n, r))
@@ -446,9 +553,8 @@ def objective(W, s, V, cb, row_scale, row_offset, codes, workspace=None, group=N
     f = torch.empty(m, dtype=torch.float64, device=W.device)
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, W.device)
     op, _keep = _opts(group=group)
-    rc = load_library().mpq_objective(_ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d,
-                                      _ptr(row_scale), _ptr(row_offset), op, _ptr(codes), _ptr(f), _ptr(ws),
-                                      ws.numel(), _stream())
+    rc = load_library().mpq_objective(_ptr(W), m, n, _ptr(s), _ptr(V), r, P.ref(), _ptr(row_scale),
+                                      _ptr(row_offset), op, _ptr(codes), _ptr(f), _ptr(ws), ws.numel(), _stream())
     _check(rc, "mpq_objective")
     return f
 
@@ -459,8 +565,8 @@ def greedy(W, s, V, cb, row_scale, row_offset, workspace=None, group=None, profi
     import torch
     m, n = W.shape
     r = s.shape[0]
-    E = _host_codebook(cb)
-    K, d = E.shape
+    P = prepare_codebook(cb, W.device)
+    K, d = P.K, P.d
     _dev(W, torch.float32, "W")
     _dev(s, torch.float32, "s", (r,))
     _dev(V, torch.float32, "V", (n, r))
@@ -472,9 +578,8 @@ def greedy(W, s, V, cb, row_scale, row_offset, workspace=None, group=None, profi
             raise MPQError(-2, "mpq_greedy_workspace_bytes")
         workspace = torch.empty(nb, dtype=torch.uint8, device=W.device)
     op, _keep = _opts(profile=profile, group=group)
-    rc = load_library().mpq_greedy(_ptr(W), m, n, _ptr(s), _ptr(V), r, E.ctypes.data_as(ctypes.c_void_p), K, d,
-                                   _ptr(row_scale), _ptr(row_offset), op, _ptr(codes), _ptr(workspace),
-                                   workspace.numel(), _stream())
+    rc = load_library().mpq_greedy(_ptr(W), m, n, _ptr(s), _ptr(V), r, P.ref(), _ptr(row_scale), _ptr(row_offset),
+                                   op, _ptr(codes), _ptr(workspace), workspace.numel(), _stream())
     _check(rc, "mpq_greedy")
     return codes
 

@@ -123,7 +123,7 @@ __global__ void chol_antitranspose_kernel(double* __restrict__ A, int64_t n) {
 
 size_t chol_tmp_doubles(int64_t n) { return (size_t)n * CH_NB + (size_t)CH_NB * CH_NB; }
 
-hipError_t launch_greedy_factor(const float* VS, int64_t n, int64_t r, double damp, double* A, double* tmp,
+hipError_t launch_greedy_factor(const double* VS, int64_t n, int64_t r, double damp, double* A, double* tmp,
                                 hipStream_t st) {
   if (n <= 0) return hipSuccess;
   // H' = VS' VS'^T, VS' = VS with its rows in reverse order (negative stride)
@@ -131,11 +131,11 @@ hipError_t launch_greedy_factor(const float* VS, int64_t n, int64_t r, double da
   memset(&h, 0, sizeof(h));
   h.M = (int)n; h.N = (int)n; h.K = (int)r;
   h.A = VS + (n - 1) * r; h.lda = -r;
-  h.B = VS + (n - 1) * r; h.ldb = -r;
+  h.B64 = VS + (n - 1) * r; h.ldb = -r;
   h.C = A; h.ldc = n;
   h.batch = 1;
   h.lower = 1;
-  hipError_t e = launch_gemm64(EPI_STORE, false, h, st);
+  hipError_t e = launch_gemm64(EPI_STORE, true, h, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(chol_damp_kernel, dim3(1), dim3(256), 0, st, A, n, damp);
   if ((e = hipGetLastError()) != hipSuccess) return e;

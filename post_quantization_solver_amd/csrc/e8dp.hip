@@ -302,10 +302,11 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // Four queries per wave, one per 16-lane row.
-__global__ __launch_bounds__(64 * E8DP_WAVES) void e8dp_kernel(const float* __restrict__ R1, const float* __restrict__ gamma1,
-                                                   int64_t m, int64_t n, const float* __restrict__ a,
-                                                   const float* __restrict__ o, E8Prefix P, float* __restrict__ xhat,
-                                                   float* __restrict__ vblk, int32_t* __restrict__ flag_list,
+__global__ __launch_bounds__(64 * E8DP_WAVES) void e8dp_kernel(const double* __restrict__ R1,
+                                                   const double* __restrict__ gamma1, int64_t m, int64_t n,
+                                                   const float* __restrict__ a, const float* __restrict__ o,
+                                                   E8Prefix P, double* __restrict__ xhat,
+                                                   double* __restrict__ vblk, int32_t* __restrict__ flag_list,
                                                    int32_t* __restrict__ flag_count) {
   __shared__ E8RowCoef coef[E8DP_WAVES * 4];
   const int lane = threadIdx.x & 63;
@@ -324,15 +325,15 @@ __global__ __launch_bounds__(64 * E8DP_WAVES) void e8dp_kernel(const float* __re
     if (active) {
       i = q / B;
       b = q - i * B;
-      gm = (double)gamma1[i];
+      gm = gamma1[i];
       ai = (double)a[i];
       oi = (double)o[i];
     }
     const bool frozen = active && !isfinite(gm);   // frozen row: the cavity passes through
     const double kap = active && !frozen ? gm * ai * ai : 0.0;
-    const float* rq = R1 + i * n + b * 8;
-    const float rv = active && j < 8 ? rq[j] : 0.f;
-    if (j < 8) cf.c[j][13] = ((double)rv - oi) / ai;
+    const double* rq = R1 + i * n + b * 8;
+    const double rv = active && j < 8 ? rq[j] : 0.0;
+    if (j < 8) cf.c[j][13] = (rv - oi) / ai;
     wave_sync();
     if (j < 13) {
 #pragma unroll
@@ -367,10 +368,10 @@ __global__ __launch_bounds__(64 * E8DP_WAVES) void e8dp_kernel(const float* __re
       sq = fma(dl, dl, sq);
     }
     if (!active) return;
-    float* xo = xhat + i * n + b * 8;
+    double* xo = xhat + i * n + b * 8;
     if (frozen) {
       if (j < 8) xo[j] = rv;
-      if (j == 0) vblk[i * B + b] = 0.f;
+      if (j == 0) vblk[i * B + b] = 0.0;
       return;
     }
     if (!(Z > 1e-280) || !isfinite(Z)) {
@@ -378,13 +379,13 @@ __global__ __launch_bounds__(64 * E8DP_WAVES) void e8dp_kernel(const float* __re
       return;
     }
     const double iz = 1.0 / Z;
-    if (j < 8) xo[j] = (float)fma(ai, mj * iz, oi);
-    if (j == 0) vblk[i * B + b] = (float)(fmax(M2 * iz - sq, 0.0) * ai * ai);
+    if (j < 8) xo[j] = fma(ai, mj * iz, oi);
+    if (j == 0) vblk[i * B + b] = fmax(M2 * iz - sq, 0.0) * ai * ai;
   }
 }
 
-hipError_t launch_denoise_e8dp(const float* R1, const float* gamma1, int64_t m, int64_t n, const E8Prefix& P,
-                               const float* a, const float* o, float* xhat, float* vblk, int32_t* flag,
+hipError_t launch_denoise_e8dp(const double* R1, const double* gamma1, int64_t m, int64_t n, const E8Prefix& P,
+                               const float* a, const float* o, double* xhat, double* vblk, int32_t* flag,
                                hipStream_t st) {
   const int64_t total = m * (n / 8);
   if (total <= 0) return hipSuccess;
@@ -497,8 +498,9 @@ __device__ __forceinline__ void e8_nearest_pass(const int j, const E8RowCoef& cf
 // Nearest codeword of every block (argmin ||r - (a e + o)||^2 = argmax of
 // sum_j e_j r'_j - e_j^2 / 2, ties to the lowest index), four blocks per wave.
 // One block per 16-lane row (q, when `active`); every lane of the wave calls it.
+template <typename TR>
 __device__ __forceinline__ void e8_nearest_block(E8RowCoef& cf, int j, int64_t q, bool active,
-                                                 const float* __restrict__ R, int64_t n,
+                                                 const TR* __restrict__ R, int64_t n,
                                                  const float* __restrict__ a, const float* __restrict__ o,
                                                  const E8Prefix& P, const uint32_t* __restrict__ keys,
                                                  const int32_t* __restrict__ kidx, int K,
@@ -514,8 +516,8 @@ __device__ __forceinline__ void e8_nearest_block(E8RowCoef& cf, int j, int64_t q
     ai = (double)a[i];
     oi = (double)o[i];
   }
-  const float rv = active && j < 8 ? R[i * n + b * 8 + j] : 0.f;
-  if (j < 8) cf.c[j][13] = ((double)rv - oi) / ai;
+  const double rv = active && j < 8 ? (double)R[i * n + b * 8 + j] : 0.0;
+  if (j < 8) cf.c[j][13] = (rv - oi) / ai;
   wave_sync();
   if (j < 13) {
 #pragma unroll
@@ -562,7 +564,8 @@ __device__ __forceinline__ void e8_nearest_block(E8RowCoef& cf, int j, int64_t q
   codes[i * B + b] = lo < K && keys[lo] == bk ? kidx[lo] : -1;
 }
 
-__global__ __launch_bounds__(64 * E8DP_WAVES) void e8_nearest_kernel(const float* __restrict__ R, int64_t m, int64_t n,
+template <typename TR>
+__global__ __launch_bounds__(64 * E8DP_WAVES) void e8_nearest_kernel(const TR* __restrict__ R, int64_t m, int64_t n,
                                                          const float* __restrict__ a, const float* __restrict__ o,
                                                          E8Prefix P, const uint32_t* __restrict__ keys,
                                                          const int32_t* __restrict__ kidx, int K,
@@ -577,7 +580,8 @@ __global__ __launch_bounds__(64 * E8DP_WAVES) void e8_nearest_kernel(const float
 
 // The same for the blocks listed in list[0 .. *count), a grid of workgroups
 // striding over the list.
-__global__ __launch_bounds__(64 * E8DP_WAVES) void e8_nearest_list_kernel(const float* __restrict__ R, int64_t n,
+template <typename TR>
+__global__ __launch_bounds__(64 * E8DP_WAVES) void e8_nearest_list_kernel(const TR* __restrict__ R, int64_t n,
                                                               const float* __restrict__ a, const float* __restrict__ o,
                                                               E8Prefix P, const uint32_t* __restrict__ keys,
                                                               const int32_t* __restrict__ kidx, int K,
@@ -644,7 +648,8 @@ __device__ __forceinline__ bool d8_nearest(const double (&x)[8], double (&u)[8])
   return true;
 }
 
-__global__ __launch_bounds__(256) void e8_decode_kernel(const float* __restrict__ R, int64_t m, int64_t n,
+template <typename TR>
+__global__ __launch_bounds__(256) void e8_decode_kernel(const TR* __restrict__ R, int64_t m, int64_t n,
                                                         const float* __restrict__ a, const float* __restrict__ o,
                                                         const uint32_t* __restrict__ keys,
                                                         const int32_t* __restrict__ kidx, int K,
@@ -655,14 +660,26 @@ __global__ __launch_bounds__(256) void e8_decode_kernel(const float* __restrict_
   if (q >= m * B) return;
   const int64_t i = q / B, b = q - i * B;
   const double ai = (double)a[i], oi = (double)o[i];
-  const float4* rp = reinterpret_cast<const float4*>(R + i * n + b * 8);
-  const float4 r0 = rp[0], r1 = rp[1];
-  const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  double rv[8];
+  if constexpr (sizeof(TR) == 4) {
+    const float4* rp = reinterpret_cast<const float4*>(R + i * n + b * 8);
+    const float4 r0 = rp[0], r1 = rp[1];
+    rv[0] = r0.x; rv[1] = r0.y; rv[2] = r0.z; rv[3] = r0.w;
+    rv[4] = r1.x; rv[5] = r1.y; rv[6] = r1.z; rv[7] = r1.w;
+  } else {
+    const double2* rp = reinterpret_cast<const double2*>(R + i * n + b * 8);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const double2 v = rp[h];
+      rv[2 * h] = v.x;
+      rv[2 * h + 1] = v.y;
+    }
+  }
   double x[8], y[8], u[8], w[8];
   bool ok = true;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    x[t] = ((double)rv[t] - oi) / ai;   // as the automaton pass forms r'
+    x[t] = (rv[t] - oi) / ai;   // as the automaton pass forms r'
     ok = ok && isfinite(x[t]) && fabs(x[t]) < 1e6;
     y[t] = x[t] - 0.5;
   }
@@ -700,7 +717,8 @@ __global__ __launch_bounds__(256) void e8_decode_kernel(const float* __restrict_
     list[atomicAdd(count, 1)] = (int32_t)q;
 }
 
-hipError_t launch_nearest_e8(const float* R, int64_t m, int64_t n, const E8Prefix& P, const uint32_t* keys,
+template <typename TR>
+hipError_t launch_nearest_e8(const TR* R, int64_t m, int64_t n, const E8Prefix& P, const uint32_t* keys,
                              const int32_t* kidx, int K, const float* a, const float* o, int32_t* codes,
                              int32_t* flag, hipStream_t st) {
   const int64_t total = m * (n / 8);
@@ -710,7 +728,7 @@ hipError_t launch_nearest_e8(const float* R, int64_t m, int64_t n, const E8Prefi
   if (wgs > INT32_MAX || total > INT32_MAX) return hipErrorInvalidValue;
   if (!flag || (reinterpret_cast<uintptr_t>(R) & 15) != 0) {
     // the automaton for every block
-    hipLaunchKernelGGL(e8_nearest_kernel, dim3((unsigned)wgs), dim3(64 * E8DP_WAVES), 0, st, R, m, n, a, o, P, keys,
+    hipLaunchKernelGGL(e8_nearest_kernel<TR>, dim3((unsigned)wgs), dim3(64 * E8DP_WAVES), 0, st, R, m, n, a, o, P, keys,
                        kidx, K, codes);
     return hipGetLastError();
   }
@@ -719,12 +737,19 @@ hipError_t launch_nearest_e8(const float* R, int64_t m, int64_t n, const E8Prefi
   int32_t* list = flag + 64;
   hipError_t e = launch_fill_i32(count, 1, 0, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(e8_decode_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, R, m, n, a, o, keys,
+  hipLaunchKernelGGL(e8_decode_kernel<TR>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, R, m, n, a, o, keys,
                      kidx, K, codes, list, count);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(e8_nearest_list_kernel, dim3((unsigned)std::min<int64_t>(wgs, 4096)), dim3(64 * E8DP_WAVES), 0, st,
+  hipLaunchKernelGGL(e8_nearest_list_kernel<TR>, dim3((unsigned)std::min<int64_t>(wgs, 4096)), dim3(64 * E8DP_WAVES), 0, st,
                      R, n, a, o, P, keys, kidx, K, list, count, codes);
   return hipGetLastError();
 }
+
+template hipError_t launch_nearest_e8<float>(const float*, int64_t, int64_t, const E8Prefix&, const uint32_t*,
+                                             const int32_t*, int, const float*, const float*, int32_t*, int32_t*,
+                                             hipStream_t);
+template hipError_t launch_nearest_e8<double>(const double*, int64_t, int64_t, const E8Prefix&, const uint32_t*,
+                                              const int32_t*, int, const float*, const float*, int32_t*, int32_t*,
+                                              hipStream_t);
 
 }  // namespace mpq

@@ -1,16 +1,20 @@
-// Float64 GEMM on the CDNA4 fp64 matrix cores, for the coordinate-descent
-// state (rank-space residual, tile gradients and the diagonal tiles of H):
+// Float64 GEMM on the CDNA4 fp64 matrix cores:
 //
 //   C[M x N] (=, -=) A[M x K] * B[N x K]^T,   A and B float64, or A float64
 //   and B float32, or both float32 (float32 widened exactly on load), C float64;
-//   optionally only the tiles that touch the lower triangle (col <= row).
+//   optionally only the tiles that touch the lower triangle (col <= row);
+//   optionally with the linear module's epilogues (EPI_ROWSUMSQ_S,
+//   EPI_LINEAR1, EPI_AXPY_W).
 //
-// CD decides integer codes from small differences of these quantities, so
-// they are kept in float64.  Same tiling as the float32 kernel: 256 threads
-// per 128 x 128 tile, K in LDS slices of 16 (double-buffered), each wave a
-// 64 x 64 block of 4 x 4 v_mfma_f64_16x16x4_f64 accumulators; lane (i, g)
-// feeds k = 4g + kk to MFMA step kk.  Unlike the float32 form, this MFMA
-// returns rows g + 4v (v = 0..3) of column i in lane (i, g).
+// It carries every product whose result feeds a decision or an amplifying
+// update: the linear module's rank-space products (u = s (V^T (w - r2)) and
+// V z, where the extrinsic update multiplies their rounding error by
+// eta2 / gamma1', which reaches tens), and the coordinate-descent state
+// (H = VS VS^T, the gradient G = (W - X) H and its updates).  Tiling: 256
+// threads per 128 x 128 tile, K in LDS slices of 16 (double-buffered), each
+// wave a 64 x 64 block of 4 x 4 v_mfma_f64_16x16x4_f64 accumulators; lane
+// (i, g) feeds k = 4g + kk to MFMA step kk.  This MFMA returns rows g + 4v
+// (v = 0..3) of column i in lane (i, g).
 #include "mpq_device.h"
 #include "internal.h"
 
@@ -122,6 +126,57 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
     }
     __syncthreads();
   }
+  if constexpr (EPI == EPI_ROWSUMSQ_S || EPI == EPI_LINEAR1) {
+    // per-row sums over the tile's columns: lanes of one 16-lane group share
+    // rows, the two column waves combine through LDS (fixed order)
+    __shared__ double red[2][GEMM_BM];
+    double rs[4][4];
+#pragma unroll
+    for (int si = 0; si < 4; ++si)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = row0 + wr + si * 16 + lg + 4 * v;
+        double beta = 0.0, gam = 1.0;
+        if (EPI == EPI_LINEAR1 && row < M) {
+          beta = g.rowa[row];
+          gam = g.rowb[row];
+        }
+        double acc_r = 0.0;
+#pragma unroll
+        for (int sj = 0; sj < 4; ++sj) {
+          const int col = col0 + wc + sj * 16 + li;
+          if (row < M && col < g.N) {
+            const double sl = (double)g.s[col];
+            const double u = sl * acc[si][sj][v];
+            if (EPI == EPI_ROWSUMSQ_S) {
+              acc_r = fma(u, u, acc_r);
+            } else {
+              const double den = fma(beta * sl, sl, gam);
+              C[(int64_t)row * g.ldc + col] = beta * sl * u / den;
+              const double e = gam * u / den;
+              acc_r = fma(e, e, acc_r);
+            }
+          }
+        }
+        acc_r += __shfl_xor(acc_r, 1, 64);
+        acc_r += __shfl_xor(acc_r, 2, 64);
+        acc_r += __shfl_xor(acc_r, 4, 64);
+        acc_r += __shfl_xor(acc_r, 8, 64);
+        rs[si][v] = acc_r;
+      }
+    if (li == 0) {
+#pragma unroll
+      for (int si = 0; si < 4; ++si)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[wave & 1][wr + si * 16 + lg + 4 * v] = rs[si][v];
+    }
+    __syncthreads();
+    if (t < GEMM_BM) {
+      const int row = row0 + t;
+      if (row < M) g.partial[(int64_t)row * g.ldp + blockIdx.x] = red[0][t] + red[1][t];
+    }
+    return;
+  }
 #pragma unroll
   for (int si = 0; si < 4; ++si)
 #pragma unroll
@@ -130,6 +185,7 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
       const int row = row0 + wr + si * 16 + lg + 4 * v;
       if (row >= M) continue;
       const int64_t prow = g.rows ? (int64_t)g.rows[row] : (int64_t)row;
+      const double coef = EPI == EPI_AXPY_W ? g.rowa[row] : 0.0;
 #pragma unroll
       for (int sj = 0; sj < 4; ++sj) {
         const int col = col0 + wc + sj * 16 + li;
@@ -137,8 +193,10 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
         double* cp = C + prow * g.ldc + col;
         if (EPI == EPI_STORE)
           *cp = acc[si][sj][v];
-        else
+        else if (EPI == EPI_SUB_INPLACE)
           *cp = *cp - acc[si][sj][v];
+        else   // EPI_AXPY_W: r2 + coef acc with r2 = W - X
+          *cp = fma(coef, acc[si][sj][v], (double)g.W[prow * g.ldw + col] - g.X[prow * g.ldx + col]);
       }
     }
 }
@@ -252,6 +310,14 @@ hipError_t launch_collect_nonzero_rows(const double* X, int64_t m, int kd, int32
 hipError_t launch_gemm64(int epi, bool a_is_f64, const Gemm64Args& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (g.rows && (!g.nrows || g.ksplit > 1 || g.batch > 1)) return hipErrorInvalidValue;
+  if (epi == EPI_ROWSUMSQ_S || epi == EPI_LINEAR1 || epi == EPI_AXPY_W) {
+    // linear module: float64 A, float32 B, one batch, no row map
+    if (!a_is_f64 || g.B64 || g.rows || g.ksplit > 1 || g.batch > 1 || !g.s && epi != EPI_AXPY_W)
+      return hipErrorInvalidValue;
+    if (epi == EPI_ROWSUMSQ_S) return launch64<double, EPI_ROWSUMSQ_S>(g, st);
+    if (epi == EPI_LINEAR1) return launch64<double, EPI_LINEAR1>(g, st);
+    return launch64<double, EPI_AXPY_W>(g, st);
+  }
   if (g.B64) {
     if (!a_is_f64 || g.ksplit > 1) return hipErrorInvalidValue;
     if (epi == EPI_STORE) return launch64<double, EPI_STORE, double>(g, st);

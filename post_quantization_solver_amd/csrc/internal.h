@@ -7,43 +7,23 @@
 namespace mpq {
 
 // ---------------------------------------------------------------- GEMM ----
-// C[M x N] (+)= A[M x K] * B[N x K]^T in float32 on the fp32 MFMA units.
+// C[M x N] (=, -=) A[M x K] * B[N x K]^T on the fp64 matrix cores (both
+// operands K-contiguous, float32 widened exactly on load), with the fused
+// epilogues of the linear module.
 enum GemmEpi : int {
   EPI_STORE = 0,        // C = acc
-  EPI_ROWSUMSQ = 1,     // partial[i][tile] = sum over the tile's columns of acc^2
-  EPI_LINEAR1 = 2,      // u = X - acc; C = beta u / (beta s^2 + gamma2);
-                        // partial[i][tile] = sum (gamma2 u / (beta s^2 + gamma2))^2
-  EPI_AXPY_ROW = 3,     // C = X + rowa[i] * acc
   EPI_SUB_INPLACE = 4,  // C -= acc
-};
-
-struct GemmArgs {
-  int M, N, K;
-  const float* A; int64_t lda; int64_t sA;   // sA/sB/sC: batch strides (blockIdx.z)
-  const float* B; int64_t ldb; int64_t sB;
-  float* C; int64_t ldc; int64_t sC;
-  const float* X; int64_t ldx;
-  const float* s;
-  const float* rowa;
-  const float* rowb;
-  float* partial; int64_t ldp;
-  int batch;
-  // optional pre-split operands (launch_pack_split layout, same M/N/K); when
-  // both are set they replace A and B
-  const uint32_t* Ap;
-  const uint32_t* Bp;
+  // linear module (acc = V^T d for a row's d, or V z): s, rowa, rowb, X, W
+  EPI_ROWSUMSQ_S = 5,   // partial[i][tile] = sum over the tile's columns of (s_l acc)^2
+  EPI_LINEAR1 = 6,      // u = s_l acc; C = beta s_l u / (beta s_l^2 + gamma2);
+                        // partial[i][tile] = sum (gamma2 u / (beta s_l^2 + gamma2))^2
+                        // (beta = rowa[i], gamma2 = rowb[i])
+  EPI_AXPY_W = 7,       // C = (W - X) + rowa[i] acc   (X = W - r2, so C = r2 + coef acc)
 };
 
 constexpr int GEMM_BM = 128, GEMM_BN = 128;
 inline int gemm_col_tiles(int N) { return (N + GEMM_BN - 1) / GEMM_BN; }
-hipError_t launch_gemm(int epi, const GemmArgs& g, hipStream_t st);
-// X (rows x K, leading dimension ld) -> its three bf16 terms in the GEMM's
-// packed tile layout (packed_split_words(rows, K) uint32 words).
-size_t packed_split_words(int64_t rows, int64_t K);
-hipError_t launch_pack_split(const float* X, int64_t rows, int64_t K, int64_t ld, uint32_t* out, hipStream_t st);
 
-// Float64 variant for the CD state: C (float64) = / -= A (float64 or float32)
-// * B (float32)^T on the fp64 matrix cores.  Epilogues EPI_STORE, EPI_SUB_INPLACE.
 struct Gemm64Args {
   int M, N, K;
   const void* A; int64_t lda; int64_t sA;
@@ -57,6 +37,13 @@ struct Gemm64Args {
   // rows[0 ..] (M bounds *nrows; tiles past it exit); not with split K
   const int32_t* rows;
   const int32_t* nrows;
+  // linear-module epilogues
+  const float* s;                  // N column scales
+  const double* rowa;              // per row
+  const double* rowb;              // per row
+  double* partial; int64_t ldp;    // per (row, column tile)
+  const double* X; int64_t ldx;
+  const float* W; int64_t ldw;
 };
 hipError_t launch_gemm64(int epi, bool a_is_f64, const Gemm64Args& g, hipStream_t st);
 // A float64, split K into `splits` chunks through `part` (splits * M * N doubles).
@@ -69,7 +56,7 @@ hipError_t launch_collect_nonzero_rows(const double* X, int64_t m, int kd, int32
                                        hipStream_t st);
 
 // ------------------------------------------------------------ codebook ----
-// Device tables derived from the host codebook.
+// Device tables of a prepared codebook (mpq_codebook_prepare).
 struct CbTables {
   int K, d;
   int Kpad;                 // K rounded up to the lattice chunk size (d = 8)
@@ -77,6 +64,7 @@ struct CbTables {
   const uint32_t* qk_keys;  // d = 8: QK operand fragments, Kpad/16 subtiles x 64 lanes x 4 words
   const uint32_t* pv_ops;   // d = 8: PV operand fragments, Kpad/32 steps x 64 lanes x 4 words
   const float* e32;         // d = 8: base codewords as float32, Kpad x 8
+  const uint32_t* e8keys;   // d = 8, E8-prefix codebooks: sorted lexicographic keys (K), then their indices (K)
   // Per-row affine layout: column j of row i uses a[i * G + j / gs],
   // o[i * G + j / gs] (one affine per row: gs = n, G = 1; column groups of
   // gs weights only with d = 1).
@@ -84,41 +72,67 @@ struct CbTables {
 };
 
 // ----------------------------------------------------------- kernels ----
-hipError_t launch_scale_columns(const float* V, const float* s, int64_t n, int64_t r, float* VS, float* VSt, hipStream_t st);
+// Vt = V^T (r x n, float32) and VS = V diag(s) (n x r, float64: each entry is
+// the exact product of two float32 values).
+hipError_t launch_prepare_v(const float* V, const float* s, int64_t n, int64_t r, float* Vt, double* VS,
+                            hipStream_t st);
 
-// X = codewords of codes; optionally D = W - X (float32 and/or float64) and
-// the per-row sum of D^2.
-hipError_t launch_gather(const int32_t* codes, int64_t m, int64_t n, const CbTables& cb,
-                         const float* a, const float* o, const float* W, float* X, float* D,
-                         float* rowsq, hipStream_t st, double* D64 = nullptr);
+// D64 = W - X in float64 for the codewords X of `codes`; optionally X
+// (float32) and the per-row sum of D64^2 (float64).
+hipError_t launch_gather(const int32_t* codes, int64_t m, int64_t n, const CbTables& cb, const float* a,
+                         const float* o, const float* W, float* X, double* rowsq, hipStream_t st, double* D64);
 
-// Prologue per-row finish: gamma1 = 1/mse, beta0 from partial sums, frozen flags.
-hipError_t launch_prologue_finish(int64_t m, int64_t n, int64_t r, const float* rowsq, const float* partial,
-                                  int nparts, float beta0_override, float* gamma1, float* beta,
-                                  float* beta_work, hipStream_t st);
+// Prologue per-row finish: gamma1 = n / sum (w - w_rtn)^2, beta0 = r / sum of
+// the partials (or the override), frozen rows +inf.
+hipError_t launch_prologue_finish(int64_t m, int64_t n, int64_t r, const double* rowsq, const double* partial,
+                                  int nparts, double beta0_override, double* gamma1, double* beta, hipStream_t st);
 
-// Extrinsic denoiser -> linear: eta1 from the block variances, gamma2, r2.
-// The variance floor uses the row's largest scale over its G affine groups.
-hipError_t launch_extrinsic(const float* R1, const float* xhat, const float* vblk, int64_t m, int64_t n, int64_t B,
-                            const float* a, int G, const float* gamma1, float* R2, float* gamma2, float* eta1,
-                            int32_t* fallback, hipStream_t st);
+// Extrinsic denoiser -> linear: eta1 from the block variances, gamma2 and
+// D2 = W - r2.  The variance floor uses the row's largest scale over its G
+// affine groups; eta1 <= gamma1 (1 + eps) takes the pass-through rule.
+// fb_count (optional) accumulates the pass-through events per row.
+hipError_t launch_extrinsic(const double* R1, const double* xhat, const double* vblk, const float* W, int64_t m,
+                            int64_t n, int64_t B, const float* a, int G, const double* gamma1, double eps,
+                            double* D2, double* gamma2, double* eta1, int32_t* fallback, int32_t* fb_count,
+                            hipStream_t st);
 
 // beta M-step + linear-side extrinsic precision.
-hipError_t launch_beta(int64_t m, int64_t n, int64_t r, const float* s, const float* partial, int nparts,
-                       const float* gamma2, float damping, int fixed_beta, float* beta, float* gamma1,
-                       float* coef, hipStream_t st);
+hipError_t launch_beta(int64_t m, int64_t n, int64_t r, const float* s, const double* partial, int nparts,
+                       const double* gamma2, double damping, int fixed_beta, double* beta, double* gamma1,
+                       double* coef, hipStream_t st);
+hipError_t launch_beta_lin(int64_t m, const double* gamma1, const double* beta, double* out, double* gamma2,
+                           hipStream_t st);
 
 // Anchored prior: Reff = (gamma R + lam W) / (gamma + lam), geff = gamma + lam
 // per row, lam = 1 / (tau a_i)^2.
-hipError_t launch_anchor(const float* R, const float* W, const float* gamma, const float* a, float tau, int64_t m,
-                         int64_t n, float* Reff, float* geff, hipStream_t st);
+hipError_t launch_anchor(const double* R, const float* W, const double* gamma, const float* a, double tau,
+                         int64_t m, int64_t n, double* Reff, double* geff, hipStream_t st);
 
 // Trace / state bookkeeping.
-hipError_t launch_record(const float* src, int64_t m, float* dst, int64_t ld, int64_t col, hipStream_t st);
-hipError_t launch_copy_rows_f(const float* src, float* dst, int64_t count, hipStream_t st);
+hipError_t launch_record(const double* src, int64_t m, float* dst, int64_t ld, int64_t col, hipStream_t st);
+hipError_t launch_copy_f64(const double* src, double* dst, int64_t count, hipStream_t st);
+hipError_t launch_widen(const float* src, double* dst, int64_t count, hipStream_t st);
+// dst = W - D (float64)
+hipError_t launch_w_minus(const float* W, const double* D, double* dst, int64_t count, hipStream_t st);
 hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t count, hipStream_t st);
-// f[i] = 1/2 sum_l U[i][l]^2 (float64), U m x r.
-hipError_t launch_half_sumsq64(const double* U, int64_t m, int64_t r, double* f, hipStream_t st);
+// f[i] = 1/2 sum_l (s_l U[i][l])^2 (float64), U m x r.
+hipError_t launch_half_sumsq64(const double* U, const float* s, int64_t m, int64_t r, double* f, hipStream_t st);
+
+// Denoisers and nearest codeword.  TR: float (the weights) or double (VAMP state).
+hipError_t launch_denoise_scalar(const double* R1, const double* gamma1, int64_t m, int64_t n, const CbTables& cb,
+                                 const float* a, const float* o, double* xhat, double* vblk, hipStream_t st);
+template <typename TR>
+hipError_t launch_nearest_scalar(const TR* R, int64_t m, int64_t n, const CbTables& cb, const float* a,
+                                 const float* o, int32_t* codes, hipStream_t st);
+hipError_t launch_denoise_lattice(const double* R1, const double* gamma1, int64_t m, int64_t n, const CbTables& cb,
+                                  const float* a, const float* o, double* xhat, double* vblk, int32_t* flag,
+                                  hipStream_t st);
+hipError_t launch_denoise_lattice_exact(const double* R1, const double* gamma1, int64_t m, int64_t n,
+                                        const CbTables& cb, const float* a, const float* o, double* xhat,
+                                        double* vblk, int32_t* flag, hipStream_t st);
+template <typename TR>
+hipError_t launch_nearest_lattice(const TR* R, int64_t m, int64_t n, const CbTables& cb, const float* a,
+                                  const float* o, int32_t* codes, hipStream_t st);
 
 // CD (scalar grids): one tile of kd columns starting at column j0.
 hipError_t launch_cd_scalar_tile(int64_t m, int64_t n, int64_t j0, int kd, const double* G, const double* Ht,
@@ -147,10 +161,10 @@ hipError_t launch_cd_lattice_score(int64_t m, int bl, const uint32_t* tk, const 
                                    hipEvent_t t1 = nullptr);
 
 // ------------------------------------------------ sequential greedy (G3) ----
-// Lam (n x n float64, lower) with H + delta I = Lam^T Lam from VS (n x r),
-// delta = damp * mean(diag H); tmp: chol_tmp_doubles(n) doubles.
+// Lam (n x n float64, lower) with H + delta I = Lam^T Lam from VS (n x r,
+// float64), delta = damp * mean(diag H); tmp: chol_tmp_doubles(n) doubles.
 size_t chol_tmp_doubles(int64_t n);
-hipError_t launch_greedy_factor(const float* VS, int64_t n, int64_t r, double damp, double* Lam, double* tmp,
+hipError_t launch_greedy_factor(const double* VS, int64_t n, int64_t r, double damp, double* Lam, double* tmp,
                                 hipStream_t st);
 // Transposed diagonal tiles of Lam (tile t at Rt + t kd kd, row stride = its width).
 hipError_t launch_greedy_rtiles(const double* Lam, int64_t n, int kd, double* Rt, hipStream_t st);

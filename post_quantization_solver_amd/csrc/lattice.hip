@@ -143,12 +143,12 @@ __device__ __forceinline__ void split_p(float p0, float p1, const DotMasks& dm, 
 //    online maximum described above; exact for any query.
 // Each query's result depends only on its own inputs, so the order of the
 // list does not change any output bit.
-template <bool ONLINE>
+template <bool ONLINE, typename TR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 : 5))) void denoise_lattice_kernel(
-    const float* __restrict__ R1, const float* __restrict__ gamma1, int64_t m, int64_t n,
+    const TR* __restrict__ R1, const TR* __restrict__ gamma1, int64_t m, int64_t n,
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ pvops, const float* __restrict__ e32,
-    int Kpad, const float* __restrict__ a, const float* __restrict__ o, float* __restrict__ xhat,
-    float* __restrict__ vblk, int32_t* __restrict__ flag_list, int32_t* __restrict__ flag_count) {
+    int Kpad, const float* __restrict__ a, const float* __restrict__ o, TR* __restrict__ xhat,
+    TR* __restrict__ vblk, int32_t* __restrict__ flag_list, int32_t* __restrict__ flag_count) {
   // codebook chunks (double-buffered) while scoring; per-query sums after
   union Smem {
     struct {
@@ -206,13 +206,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
 #pragma unroll
     for (int k = 0; k < 8; ++k) rp[k] = 0.f;
     if (qi.valid) {
-      float gm = gamma1[qi.i];
+      float gm = (float)gamma1[qi.i];
       if (isfinite(gm)) {
         float ai = a[qi.i], oi = o[qi.i];
-        const float* rr = R1 + qi.i * n + qi.b * 8;
+        const TR* rr = R1 + qi.i * n + qi.b * 8;
         float inva = 1.f / ai;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) rp[k] = (rr[k] - oi) * inva;
+        for (int k = 0; k < 8; ++k) rp[k] = ((float)rr[k] - oi) * inva;
         k2 = gm * ai * ai * LOG2E;
       }
     }
@@ -331,14 +331,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
     const int64_t slot = vb * QWG + ql;
     QueryInfo qi = resolve(slot);
     if (qi.valid) {
-      float gm = gamma1[qi.i];
-      float* xo = xhat + qi.i * n + qi.b * 8;
+      float gm = (float)gamma1[qi.i];
+      TR* xo = xhat + qi.i * n + qi.b * 8;
       float z = fin[ql][11];
       if (!isfinite(gm)) {
-        const float* rr = R1 + qi.i * n + qi.b * 8;
+        const TR* rr = R1 + qi.i * n + qi.b * 8;
 #pragma unroll
         for (int k = 0; k < 8; ++k) xo[k] = rr[k];
-        vblk[qi.i * B + qi.b] = 0.f;
+        vblk[qi.i * B + qi.b] = 0;
       } else if (!ONLINE && !(z >= 0x1p-90f)) {
         int pos = atomicAdd(flag_count, 1);
         flag_list[pos] = (int32_t)slot;
@@ -351,9 +351,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
         for (int k = 0; k < 8; ++k) {
           float mk = fin[ql][k] * invz;
           nx = fmaf(mk, mk, nx);
-          xo[k] = fmaf(ai, mk, oi);
+          xo[k] = (TR)fmaf(ai, mk, oi);
         }
-        vblk[qi.i * B + qi.b] = fmaxf(m2 - nx, 0.f) * ai * ai;
+        vblk[qi.i * B + qi.b] = (TR)(fmaxf(m2 - nx, 0.f) * ai * ai);
       }
     }
   }
@@ -372,7 +372,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONLINE ? 1 
 
 // Nearest codeword per block (argmax of e . r' - ||e||^2/2; ties to the
 // lowest index), used for round-to-nearest and for the marginal MAP.
-__global__ __launch_bounds__(256) void nearest_lattice_kernel(const float* __restrict__ R, int64_t m, int64_t n,
+template <typename TR>
+__global__ __launch_bounds__(256) void nearest_lattice_kernel(const TR* __restrict__ R, int64_t m, int64_t n,
                                                               const uint32_t* __restrict__ keys, int Kpad,
                                                               const float* __restrict__ a,
                                                               const float* __restrict__ o,
@@ -396,10 +397,10 @@ __global__ __launch_bounds__(256) void nearest_lattice_kernel(const float* __res
     for (int k = 0; k < 8; ++k) rp[k] = 0.f;
     if (qi.valid) {
       float ai = a[qi.i], oi = o[qi.i];
-      const float* rr = R + qi.i * n + qi.b * 8;
+      const TR* rr = R + qi.i * n + qi.b * 8;
       float inva = 1.f / ai;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) rp[k] = (rr[k] - oi) * inva;
+      for (int k = 0; k < 8; ++k) rp[k] = ((float)rr[k] - oi) * inva;
     }
     qop[q] = make_query(rp, 1.f, 0.f, g);
   }
@@ -449,8 +450,11 @@ __global__ __launch_bounds__(256) void nearest_lattice_kernel(const float* __res
 // flag: 64 int32 words of scratch (count first) followed by room for
 // m * n / 8 query indices.  The fast pass scores every query and lists those
 // it cannot resolve; launch_denoise_lattice_exact redoes the listed ones.
-hipError_t launch_denoise_lattice(const float* R1, const float* gamma1, int64_t m, int64_t n, const CbTables& cb,
-                                  const float* a, const float* o, float* xhat, float* vblk, int32_t* flag,
+// The state is float64; this scan works in float32 (bf16 products made exact
+// by operand splits), so for codebooks that are not an E8 prefix the
+// denoiser's outputs carry float32 rounding.
+hipError_t launch_denoise_lattice(const double* R1, const double* gamma1, int64_t m, int64_t n, const CbTables& cb,
+                                  const float* a, const float* o, double* xhat, double* vblk, int32_t* flag,
                                   hipStream_t st) {
   int64_t total = m * (n / 8);
   if (total <= 0) return hipSuccess;
@@ -459,33 +463,38 @@ hipError_t launch_denoise_lattice(const float* R1, const float* gamma1, int64_t 
   hipError_t e = launch_fill_i32(count, 1, 0, st);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)((total + LAT_QWG - 1) / LAT_QWG));
-  hipLaunchKernelGGL((denoise_lattice_kernel<false>), grid, dim3(256), 0, st, R1, gamma1, m, n, cb.qk_keys, cb.pv_ops,
-                     cb.e32, cb.Kpad, a, o, xhat, vblk, list, count);
+  hipLaunchKernelGGL((denoise_lattice_kernel<false, double>), grid, dim3(256), 0, st, R1, gamma1, m, n, cb.qk_keys,
+                     cb.pv_ops, cb.e32, cb.Kpad, a, o, xhat, vblk, list, count);
   return hipGetLastError();
 }
 
 // The flagged queries with the exact online-maximum pass: a grid of at most
 // LAT_EXACT_WGS workgroups strides over the list (surplus ones exit at once).
 constexpr int64_t LAT_EXACT_WGS = 1024;
-hipError_t launch_denoise_lattice_exact(const float* R1, const float* gamma1, int64_t m, int64_t n,
-                                        const CbTables& cb, const float* a, const float* o, float* xhat, float* vblk,
-                                        int32_t* flag, hipStream_t st) {
+hipError_t launch_denoise_lattice_exact(const double* R1, const double* gamma1, int64_t m, int64_t n,
+                                        const CbTables& cb, const float* a, const float* o, double* xhat,
+                                        double* vblk, int32_t* flag, hipStream_t st) {
   int64_t total = m * (n / 8);
   if (total <= 0) return hipSuccess;
   const int64_t qwg = 16 * LAT_WAVES;   // queries per workgroup of the exact pass
   dim3 grid((unsigned)std::min<int64_t>((total + qwg - 1) / qwg, LAT_EXACT_WGS));
-  hipLaunchKernelGGL((denoise_lattice_kernel<true>), grid, dim3(256), 0, st, R1, gamma1, m, n, cb.qk_keys, cb.pv_ops,
-                     cb.e32, cb.Kpad, a, o, xhat, vblk, flag + 64, flag);
+  hipLaunchKernelGGL((denoise_lattice_kernel<true, double>), grid, dim3(256), 0, st, R1, gamma1, m, n, cb.qk_keys,
+                     cb.pv_ops, cb.e32, cb.Kpad, a, o, xhat, vblk, flag + 64, flag);
   return hipGetLastError();
 }
 
-hipError_t launch_nearest_lattice(const float* R, int64_t m, int64_t n, const CbTables& cb, const float* a,
+template <typename TR>
+hipError_t launch_nearest_lattice(const TR* R, int64_t m, int64_t n, const CbTables& cb, const float* a,
                                   const float* o, int32_t* codes, hipStream_t st) {
   int64_t total = m * (n / 8);
   if (total <= 0) return hipSuccess;
   dim3 grid((unsigned)((total + LAT_QWG - 1) / LAT_QWG));
-  hipLaunchKernelGGL(nearest_lattice_kernel, grid, dim3(256), 0, st, R, m, n, cb.qk_keys, cb.Kpad, a, o, codes);
+  hipLaunchKernelGGL(nearest_lattice_kernel<TR>, grid, dim3(256), 0, st, R, m, n, cb.qk_keys, cb.Kpad, a, o, codes);
   return hipGetLastError();
 }
+template hipError_t launch_nearest_lattice<float>(const float*, int64_t, int64_t, const CbTables&, const float*,
+                                                  const float*, int32_t*, hipStream_t);
+template hipError_t launch_nearest_lattice<double>(const double*, int64_t, int64_t, const CbTables&, const float*,
+                                                   const float*, int32_t*, hipStream_t);
 
 }  // namespace mpq

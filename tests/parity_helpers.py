@@ -72,11 +72,6 @@ def compare_layer(L, rows, gpu, refs, report_only_traces=False):
             g = gpu[key][rows]
             o = np.stack([r[key] for r in refs])
             scale = np.abs(o)
-            if key == "gamma2_tr":
-                # gamma2 = eta1 - gamma1: errors relative to the operands
-                # (eta1 <= gamma1 + gamma2 bounds both)
-                g1 = np.stack([r["gamma1_tr"][:-1] for r in refs])
-                scale = np.abs(o) + np.abs(g1)
             with np.errstate(invalid="ignore", divide="ignore"):
                 rel = np.where(np.isinf(o) & np.isinf(g), 0.0, np.abs(g - o) / scale)
             tr[key] = rel

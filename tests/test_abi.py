@@ -46,14 +46,25 @@ def test_workspace_sizes(lib):
 
 
 FAKE = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+# the marker mpq_codebook_prepare sets in a filled mpq_codebook (library-internal)
+CB_MAGIC = 0x4d50514342763200
+
+
+def fake_codebook(K=8, d=1, kind=0, magic=CB_MAGIC, tables=FAKE):
+    """A mpq_codebook as mpq_codebook_prepare would fill it, with tables at a
+    fake device address: enough for the host-side validation paths."""
+    cb = mpq.binding.Codebook()
+    cb.K, cb.d, cb.kind, cb.magic = K, d, kind, magic
+    cb.tables = tables
+    return cb
 
 
 def call_layer(lib, m=4, n=16, r=16, K=8, d=1, T=2, ncd=1, rho=0.5, cb=None, ws_bytes=1 << 30, W=FAKE, ws=FAKE,
                opt=None):
-    E = np.arange(K * d, dtype=np.float32).reshape(K, d) if cb is None else cb
+    cbs = fake_codebook(K, d) if cb is None else cb
     op = ctypes.byref(opt) if opt is not None else None
-    return lib.mpq_quantize_layer(W, m, n, FAKE, FAKE, r, E.ctypes.data_as(ctypes.c_void_p), K, d, FAKE, FAKE, T,
-                                  ncd, rho, op, FAKE, None, None, None, None, ws, ws_bytes, None)
+    return lib.mpq_quantize_layer(W, m, n, FAKE, FAKE, r, ctypes.byref(cbs), FAKE, FAKE, T, ncd, rho, op, FAKE,
+                                  None, None, None, None, ws, ws_bytes, None)
 
 
 def test_argument_validation(lib):
@@ -63,31 +74,78 @@ def test_argument_validation(lib):
     assert call_layer(lib, rho=1.5) == -3
     assert call_layer(lib, rho=float("nan")) == -3
     assert call_layer(lib, d=3, n=18, r=18) == -4
-    assert call_layer(lib, d=8, n=12, r=12) == -2
+    assert call_layer(lib, d=8, K=256, n=12, r=12) == -2
     assert call_layer(lib, r=17) == -2
     assert call_layer(lib, m=-1) == -2
+    assert call_layer(lib, n=65536 + 8, r=8) == -2            # longer rows than the solver takes
     assert call_layer(lib, W=None) == -1
-    assert call_layer(lib, m=0) == 0                       # nothing to do
-    # d = 8 codebook not exact in bfloat16
-    bad = S.e8_codebook(256) * np.float32(1.1)
-    assert call_layer(lib, d=8, K=256, cb=bad) == -4
+    assert call_layer(lib, m=0) == 0                          # nothing to do
+    # an unprepared codebook, or none
+    assert call_layer(lib, cb=fake_codebook(magic=0)) == -3
+    assert call_layer(lib, cb=fake_codebook(tables=None)) == -1
+    assert lib.mpq_quantize_layer(FAKE, 4, 16, FAKE, FAKE, 16, None, FAKE, FAKE, 2, 1, 0.5, None, FAKE, None, None,
+                                  None, None, FAKE, 1 << 30, None) == -1
     # workspace too small or misaligned
+    assert call_layer(lib, d=8, K=256, ws_bytes=1024) == -5
+    assert call_layer(lib, d=8, K=256, ws=ctypes.c_void_p((1 << 20) + 4)) == -5
+    assert call_layer(lib, d=8, K=256, ws=None) == -5
+
+
+def test_codebook_prepare_validation(lib):
+    def prep(E, K=None, d=None, tables=FAKE, nbytes=1 << 30, out=True):
+        E = np.ascontiguousarray(E, dtype=np.float32)
+        K = E.shape[0] if K is None else K
+        d = E.shape[1] if d is None else d
+        cb = mpq.binding.Codebook()
+        return lib.mpq_codebook_prepare(E.ctypes.data_as(ctypes.c_void_p), K, d, tables, nbytes, None,
+                                        ctypes.byref(cb) if out else None)
     good = S.e8_codebook(256)
-    assert call_layer(lib, d=8, K=256, cb=good, ws_bytes=1024) == -5
-    assert call_layer(lib, d=8, K=256, cb=good, ws=ctypes.c_void_p((1 << 20) + 4)) == -5
-    assert call_layer(lib, d=8, K=256, cb=good, ws=None) == -5
+    assert prep(good * np.float32(1.1)) == -4                  # d = 8 codebook not exact in bfloat16
+    assert prep(np.zeros((4, 3))) == -4                        # d unsupported
+    assert prep(np.zeros((65, 1))) == -2                       # K > 64 for scalar grids
+    assert prep(np.array([[0.0], [np.nan]])) == -3             # non-finite level
+    assert prep(good, tables=None) == -1
+    assert prep(good, out=False) == -1
+    assert prep(good, nbytes=1024) == -5                       # table buffer too small
+    assert prep(good, tables=ctypes.c_void_p((1 << 20) + 8)) == -5   # misaligned
+    assert lib.mpq_codebook_bytes(8, 1) > 0 and lib.mpq_codebook_bytes(65536, 8) > 8 << 20
+    assert lib.mpq_codebook_bytes(65, 1) == 0 and lib.mpq_codebook_bytes(8, 3) == 0
 
 
 def test_group_option_validation(lib):
     Opt = mpq.binding.Options
     assert call_layer(lib, opt=Opt(group=-1)) == -3
-    good = S.e8_codebook(256)
-    assert call_layer(lib, d=8, K=256, cb=good, opt=Opt(group=8)) == -4          # groups need d = 1
+    assert call_layer(lib, d=8, K=256, opt=Opt(group=8)) == -4                   # groups need d = 1
     assert call_layer(lib, opt=Opt(group=8, anchor_tau=0.2)) == -4                # and the uniform prior
     # an accepted group option reaches the workspace check
     assert call_layer(lib, opt=Opt(group=8), ws_bytes=1024) == -5
     assert call_layer(lib, opt=Opt(group=64), ws_bytes=1024) == -5                # group >= n: one per row
     assert call_layer(lib, opt=Opt(group=0, anchor_tau=0.2), ws_bytes=1024) == -5
+
+
+def test_option_validation(lib):
+    Opt = mpq.binding.Options
+    assert call_layer(lib, opt=Opt(safeguard_eps=-0.1)) == -3
+    assert call_layer(lib, opt=Opt(safeguard_eps=float("nan"))) == -3
+    assert call_layer(lib, opt=Opt(safeguard_eps=0.5), ws_bytes=1024) == -5       # accepted
+    assert call_layer(lib, opt=Opt(flags=mpq.binding.F_PROFILE)) == -1            # profiling needs a profiler
+    h = ctypes.c_void_p()
+    assert lib.mpq_profiler_create(0, ctypes.byref(h)) == -3
+    assert lib.mpq_profiler_create(4, None) == -1
+    lib.mpq_profiler_destroy(None)                                                # no-op
+
+
+def test_linear_step_validation(lib):
+    def call(m=4, n=16, r=16, rho=0.5, R2=FAKE, ws_bytes=1 << 30, opt=None):
+        return lib.mpq_linear_step(R2, FAKE, FAKE, FAKE, m, n, FAKE, FAKE, r, rho,
+                                   ctypes.byref(opt) if opt is not None else None, FAKE, FAKE, FAKE, ws_bytes, None)
+    assert call(rho=0.0) == -3
+    assert call(r=17) == -2
+    assert call(m=-1) == -2
+    assert call(m=0) == 0
+    assert call(R2=None) == -1
+    assert call(ws_bytes=1024) == -5
+    assert call(opt=mpq.binding.Options(flags=mpq.binding.F_PROFILE)) == -4
 
 
 def test_frontend_argument_validation(lib):
@@ -104,20 +162,21 @@ def test_frontend_argument_validation(lib):
     assert lib.mpq_gram_workspace_bytes(0) == 0 and lib.mpq_gram_workspace_bytes(256) > 0
 
 
-def test_options_layout_matches_header(tmp_path):
-    """The ctypes mirror of mpq_options has the header's field offsets and size
-    (compiled with the host C compiler)."""
+@pytest.mark.parametrize("struct_name,cls", [("mpq_options", "Options"), ("mpq_codebook", "Codebook")])
+def test_struct_layout_matches_header(tmp_path, struct_name, cls):
+    """The ctypes mirrors of the header's structs have its field offsets and
+    sizes (compiled with the host C compiler)."""
     import shutil
     import subprocess
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no host C compiler")
-    Opt = mpq.binding.Options
+    Opt = getattr(mpq.binding, cls)
     names = [f[0] for f in Opt._fields_]
     src = tmp_path / "layout.c"
     src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"mpq.h\"\nint main(void) {\n" +
-                   "".join(f'  printf("%zu\\n", offsetof(mpq_options, {nm}));\n' for nm in names) +
-                   '  printf("%zu\\n", sizeof(mpq_options));\n  return 0;\n}\n')
+                   "".join(f'  printf("%zu\\n", offsetof({struct_name}, {nm}));\n' for nm in names) +
+                   f'  printf("%zu\\n", sizeof({struct_name}));\n  return 0;\n}}\n')
     exe = tmp_path / "layout"
     subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
@@ -126,7 +185,7 @@ def test_options_layout_matches_header(tmp_path):
 
 
 def test_strerror(lib):
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert lib.mpq_strerror(code).decode()
     with pytest.raises(mpq.MPQError):
         mpq.binding._check(-3, "x")

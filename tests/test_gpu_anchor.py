@@ -32,26 +32,22 @@ def test_anchored_vamp_step(name):
     rows = np.arange(L.m)
     refs = solve_rows(L, rows, record=True, anchor_tau=TAU)
     T = layer_tensors(L)
-    ytil = dev(np.stack([O.rank_target(L.W[i], L.s, L.V) for i in rows]).astype(np.float32))
     worst = {}
     for t in range(L.T_vamp):
         h = [r["history"][t] for r in refs]
-        R1 = dev(np.stack([x["r1"] for x in h]).astype(np.float32))
-        g1 = dev(np.array([x["gamma1"] for x in h], dtype=np.float32))
-        bt = dev(np.array([x["beta"] for x in h], dtype=np.float32))
+        R1 = dev(np.stack([x["r1"] for x in h]))
+        g1 = dev(np.array([x["gamma1"] for x in h]))
+        bt = dev(np.array([x["beta"] for x in h]))
         print(f"[anchor step] {name} t={t}", flush=True)
-        out = mpq.vamp_step(R1, g1, bt, ytil, T["s"], T["V"], L.E, T["a"], T["o"], damping=L.damping,
-                            anchor_tau=TAU, W=T["W"])
+        out = mpq.vamp_step(R1, g1, bt, T["W"], T["s"], T["V"], L.E, T["a"], T["o"], damping=L.damping,
+                            anchor_tau=TAU)
         r1n, g1n = host(R1), host(g1)
         xh, eta1, g2, fb = (host(out[k]) for k in ("xhat1", "eta1", "gamma2", "fallback"))
         for k in range(len(rows)):
             nxt = refs[k]["history"][t + 1]["r1"] if t + 1 < L.T_vamp else refs[k]["r1_final"]
-            cond = max(1.0, h[k]["eta1"] / h[k]["gamma2"])
             g1_ref = refs[k]["gamma1_tr"][t + 1]
-            cond2 = max(1.0, h[k]["eta2"] / g1_ref * np.linalg.norm(h[k]["xhat2"] - h[k]["r2"]) /
-                        max(np.linalg.norm(nxt), 1e-300))
             e = dict(xhat1=rel_vec(xh[k], h[k]["xhat1"]), eta1=rel_scalar(eta1[k], h[k]["eta1"]),
-                     gamma2=rel_scalar(g2[k], h[k]["gamma2"]) / cond, r1=rel_vec(r1n[k], nxt) / cond2,
+                     gamma2=rel_scalar(g2[k], h[k]["gamma2"]), r1=rel_vec(r1n[k], nxt),
                      gamma1=rel_scalar(g1n[k], g1_ref), fallback=float(bool(fb[k]) != bool(h[k]["fell_back"])))
             for key, v in e.items():
                 worst[key] = max(worst.get(key, 0.0), v)

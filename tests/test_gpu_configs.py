@@ -6,21 +6,20 @@ The GPU solves the whole layer in the configuration bench.py times; the
 float64 oracle solves a fixed sample of rows (every m/k-th row).  Rows are
 independent problems, so a sampled row's GPU result is compared exactly.
 
-Checks per sampled row:
-  (a) teacher-forced VAMP steps (the GPU step starts from the oracle's own
-      state): soft quantities within 1e-4 relative; gamma2, r2 and r1 are
-      measured relative to the operands of the extrinsic differences they
-      come from (gamma2 = eta1 - gamma1, r1' = r2 + (eta2/gamma1')(x2 - r2)).
-  (b) decision chain on the GPU's own trajectory: the GPU's marginal MAP
+Asserted per workload (the target specification's bar):
+  (a) end to end against the oracle's own trajectory: codes equal on
+      >= 99.9 % of the sampled blocks, every sampled row's objective
+      1/2 ||T (w - w_hat)||^2 within 1e-5 relative, the beta / gamma1 /
+      gamma2 traces within 1e-4 relative (each entry), pass-through counts and
+      CD sweeps equal;
+  (b) teacher-forced VAMP steps (the GPU step starts from the oracle's own
+      state): soft quantities within 1e-4 relative (raw, no conditioning);
+  (c) decision chain on the GPU's own trajectory: the GPU's marginal MAP
       equals the oracle's MAP of the GPU's r1^T, and the GPU's CD equals the
-      oracle's CD from the GPU's MAP codes (>= 99.9 % of blocks, objectives
-      within 1e-5 relative).
-  (c) end to end against the oracle's own trajectory: beta / gamma1 / gamma2
-      drift below 1e-3 relative; code agreement and objective differences
-      are reported.  A float32 trajectory differs from the float64 one by
-      ~1e-5..1e-4, which can move a near-tied MAP decision and send CD to a
-      different local minimum; (b) shows each such row is still exactly what
-      the method computes from the GPU's state.
+      oracle's CD from the GPU's MAP codes.
+The VAMP state and the linear module's products are float64 on the GPU: with
+float32 state the trajectory drifted by 1e-6..1e-4 and moved near-tied MAP
+decisions on the 2048 x 8192 and 4096 x 14336 workloads.
 """
 import numpy as np
 import pytest
@@ -31,12 +30,11 @@ from oracle.pool import solve_rows, map_rows, cd_rows
 from parity_helpers import (SOFT_RTOL, OBJ_RTOL, CODE_FRAC, dev, host, layer_tensors, compare_layer, rel_vec,
                             rel_scalar, row_codebook)
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
-SAMPLE = {"c1": 64, "c2": 16, "c3": 16, "c4": 8, "c5": 4, "c3_g128": 16}
+SAMPLE = {"c1": 64, "c2": 16, "c3": 16, "c4": 16, "c5": 16, "c3_g128": 16}
 CASES = {"c1": ("c1", 0), "c2": ("c2", 0), "c3": ("c3", 0), "c4": ("c4", 0), "c5": ("c5", 0),
          "c3_g128": ("c3", 128)}
-E2E_TRACE_TOL = 1e-3
 
 
 def sublayer(L, rows):
@@ -44,27 +42,22 @@ def sublayer(L, rows):
                    np.ascontiguousarray(L.o[rows]), L.d, L.T_vamp, L.n_cd, L.damping, group=L.group)
 
 
-def teacher_forced_steps(mpq, L, Ts, refs, k_rows):
-    ytil = dev(np.stack([O.rank_target(Ts["W_np"][k], L.s, L.V) for k in range(k_rows)]).astype(np.float32))
+def teacher_forced_steps(mpq, L, Ts, refs, k_rows, cb):
     worst = {}
     for t in sorted({0, L.T_vamp // 2, L.T_vamp - 1}):
         h = [r["history"][t] for r in refs]
-        R1 = dev(np.stack([x["r1"] for x in h]).astype(np.float32))
-        g1 = dev(np.array([x["gamma1"] for x in h], dtype=np.float32))
-        bt = dev(np.array([x["beta"] for x in h], dtype=np.float32))
-        o = mpq.vamp_step(R1, g1, bt, ytil, Ts["s"], Ts["V"], L.E, Ts["a"], Ts["o"], damping=L.damping,
+        R1 = dev(np.stack([x["r1"] for x in h]))
+        g1 = dev(np.array([x["gamma1"] for x in h]))
+        bt = dev(np.array([x["beta"] for x in h]))
+        o = mpq.vamp_step(R1, g1, bt, Ts["W"], Ts["s"], Ts["V"], cb, Ts["a"], Ts["o"], damping=L.damping,
                           group=L.group)
         r1n, g1n, btn = host(R1), host(g1), host(bt)
         xh, eta1, g2, r2, fb = (host(o[k]) for k in ("xhat1", "eta1", "gamma2", "r2", "fallback"))
         for k in range(k_rows):
             nxt = refs[k]["history"][t + 1]["r1"] if t + 1 < L.T_vamp else refs[k]["r1_final"]
-            cond1 = max(1.0, h[k]["eta1"] / h[k]["gamma2"])
-            g1_next = refs[k]["gamma1_tr"][t + 1]
-            cond2 = max(1.0, h[k]["eta2"] / g1_next * np.linalg.norm(h[k]["xhat2"] - h[k]["r2"]) /
-                        max(np.linalg.norm(nxt), 1e-300))
             e = dict(xhat1=rel_vec(xh[k], h[k]["xhat1"]), eta1=rel_scalar(eta1[k], h[k]["eta1"]),
-                     gamma2=rel_scalar(g2[k], h[k]["gamma2"]) / cond1, r2=rel_vec(r2[k], h[k]["r2"]) / cond1,
-                     r1=rel_vec(r1n[k], nxt) / cond2, gamma1=rel_scalar(g1n[k], g1_next),
+                     gamma2=rel_scalar(g2[k], h[k]["gamma2"]), r2=rel_vec(r2[k], h[k]["r2"]),
+                     r1=rel_vec(r1n[k], nxt), gamma1=rel_scalar(g1n[k], refs[k]["gamma1_tr"][t + 1]),
                      beta=rel_scalar(btn[k], refs[k]["beta_tr"][t + 1]),
                      fallback=float(bool(fb[k]) != bool(h[k]["fell_back"])))
             for key, v in e.items():
@@ -80,9 +73,10 @@ def test_config_parity(name):
     L = S.make_config(CASES[name][0], device="cuda", group=CASES[name][1])
     g = L.group
     T = layer_tensors(L)
+    cb = mpq.prepare_codebook(L.E)
     print(f"[config] {name}: m={L.m} n={L.n} r={L.r} K={L.K} d={L.d} T={L.T_vamp} full solve on GPU", flush=True)
-    out = mpq.quantize_layer(T["W"], T["s"], T["V"], L.E, T["a"], T["o"], T_vamp=L.T_vamp, n_cd=L.n_cd,
-                             damping=L.damping, group=g)
+    out = mpq.quantize_layer(T["W"], T["s"], T["V"], cb, T["a"], T["o"], T_vamp=L.T_vamp, n_cd=L.n_cd,
+                             damping=L.damping, group=g, diagnostics=True)
     torch.cuda.synchronize()
     gpu = {k: (host(v) if v is not None else None) for k, v in out.items()}
     del T, out
@@ -91,17 +85,16 @@ def test_config_parity(name):
     k_rows = len(rows)
     Ls = sublayer(L, rows)
     Ts = layer_tensors(Ls)
-    Ts["W_np"] = Ls.W
 
     # GPU stages on the sampled rows alone (bitwise the same as in the full solve)
     print(f"[config] {name}: GPU stages on {k_rows} sampled rows", flush=True)
-    pro = mpq.prologue(Ts["W"], Ts["s"], Ts["V"], L.E, Ts["a"], Ts["o"], group=g)
-    R1 = Ts["W"].clone()
+    pro = mpq.prologue(Ts["W"], Ts["s"], Ts["V"], cb, Ts["a"], Ts["o"], group=g)
+    R1 = Ts["W"].double()
     g1, bt = pro["gamma1"], pro["beta"]
     for _ in range(L.T_vamp):
-        mpq.vamp_step(R1, g1, bt, pro["ytil"], Ts["s"], Ts["V"], L.E, Ts["a"], Ts["o"], damping=L.damping, group=g)
-    map_gpu = mpq.map_codes(R1, g1, L.E, Ts["a"], Ts["o"], group=g)
-    cd_gpu, _ = mpq.cd(Ts["W"], Ts["s"], Ts["V"], L.E, Ts["a"], Ts["o"], map_gpu.clone(), n_cd=L.n_cd, group=g)
+        mpq.vamp_step(R1, g1, bt, Ts["W"], Ts["s"], Ts["V"], cb, Ts["a"], Ts["o"], damping=L.damping, group=g)
+    map_gpu = mpq.map_codes(R1, g1, cb, Ts["a"], Ts["o"], group=g)
+    cd_gpu, _ = mpq.cd(Ts["W"], Ts["s"], Ts["V"], cb, Ts["a"], Ts["o"], map_gpu.clone(), n_cd=L.n_cd, group=g)
     torch.cuda.synchronize()
     r1_gpu, g1_gpu, map_gpu, cd_gpu = host(R1), host(g1), host(map_gpu), host(cd_gpu)
     same_as_full = bool(np.array_equal(cd_gpu, gpu["codes"][rows]))
@@ -111,38 +104,44 @@ def test_config_parity(name):
     map_ref = np.stack(map_rows(L, rows, r1_gpu, g1_gpu))
     cdr = cd_rows(L, rows, map_gpu)
     cd_ref = np.stack([r["codes"] for r in cdr])
-    f_cd_ref = np.array([r["objective"] for r in cdr])
-    f_cd_gpu = np.array([O.codes_objective(Ls.W[k], cd_gpu[k], row_codebook(Ls, k), L.d, L.s, L.V)
-                         for k in range(k_rows)])
 
     report = {}
-    report["step"] = {k: float(f"{v:.3g}") for k, v in teacher_forced_steps(mpq, L, Ts, refs, k_rows).items()}
+    report["step"] = {k: float(f"{v:.3g}") for k, v in teacher_forced_steps(mpq, L, Ts, refs, k_rows, cb).items()}
     report["rows_match_full_solve"] = same_as_full
     report["map_agree"] = float((map_gpu == map_ref).mean())
     report["cd_agree"] = float((cd_gpu == cd_ref).mean())
-    report["cd_obj_rel"] = float(np.max(np.abs(f_cd_gpu - f_cd_ref) / f_cd_ref))
     summ = compare_layer(L, rows, gpu, refs)
     report["e2e_traces"] = {k: float(f"{v:.3g}") for k, v in summ["trace_rel_max"].items()}
     report["e2e_code_agree"] = summ["code_agreement"]
     report["e2e_rows_equal"] = f"{summ['rows_codes_equal']}/{k_rows}"
     report["e2e_obj_rel_max"] = summ["obj_rel_max"]
-    report["e2e_obj_gpu_minus_oracle_mean"] = float(np.mean(
-        (np.array([O.codes_objective(L.W[i], gpu["codes"][i], row_codebook(L, i), L.d, L.s, L.V)
-                   for i in rows]) - np.array([r["objective"] for r in refs])) /
-        np.array([r["objective"] for r in refs])))
-    report["fallbacks"] = int(sum(r["fallbacks"] for r in refs))
+    fb_ref = np.array([r["fallbacks"] for r in refs])
+    sw_ref = np.array([next((j + 1 for j, c in enumerate(r["cd_changes"]) if c == 0), L.n_cd) for r in refs])
+    report["fallbacks"] = f"{int(gpu['fallbacks'][rows].sum())}/{int(fb_ref.sum())}"
+    report["sweeps_equal"] = bool((gpu["sweeps"][rows] == sw_ref).all())
+    # the library's float64 objective of its own codes against the oracle's recomputation
+    f_lib = gpu["objective"][rows]
+    f_re = np.array([O.codes_objective(L.W[i], gpu["codes"][i], row_codebook(L, i), L.d, L.s, L.V) for i in rows])
+    report["objective_output_rel"] = float(np.max(np.abs(f_lib - f_re) / np.maximum(f_re, 1e-300)))
     print(f"  {name}: " + ", ".join(f"{k}={v}" for k, v in report.items()), flush=True)
 
+    # (a) the end-to-end bar
+    assert summ["code_agreement"] >= CODE_FRAC, summ["code_agreement"]
+    assert summ["obj_rel_max"] < OBJ_RTOL, summ["obj_rel_max"]
+    for key, v in summ["trace_rel_max"].items():
+        assert v < SOFT_RTOL, ("end-to-end trace", key, v)
+    assert (gpu["fallbacks"][rows] == fb_ref).all()
+    assert report["sweeps_equal"]
+    assert report["objective_output_rel"] < 1e-10
+    # (b) teacher-forced steps
     st = report["step"]
     for key in ("xhat1", "eta1", "gamma2", "r2", "r1", "gamma1", "beta"):
         assert st[key] < SOFT_RTOL, ("teacher-forced step", key, st[key])
     assert st["fallback"] == 0.0
+    # (c) decision chain
     assert same_as_full
     assert report["map_agree"] >= CODE_FRAC
     assert report["cd_agree"] >= CODE_FRAC
-    assert report["cd_obj_rel"] < OBJ_RTOL
-    for key, v in summ["trace_rel_max"].items():
-        assert v < E2E_TRACE_TOL, ("end-to-end trace drift", key, v)
 
 
 GREEDY_SAMPLE = {"c2": (4, 8), "c4": (2, 4)}   # rows, blocks per row
@@ -159,7 +158,7 @@ def test_config_greedy(name):
     L = S.make_config(name, device="cuda")
     T = layer_tensors(L)
     print(f"[greedy config] {name}: m={L.m} n={L.n} K={L.K} d={L.d}", flush=True)
-    codes = host(mpq.greedy(T["W"], T["s"], T["V"], L.E, T["a"], T["o"]))
+    codes = host(mpq.greedy(T["W"], T["s"], T["V"], mpq.prepare_codebook(L.E), T["a"], T["o"]))
     torch.cuda.synchronize()
     del T
     torch.cuda.empty_cache()

@@ -58,16 +58,16 @@ def test_grouped_denoise(name, t):
     import post_quantization_solver_amd as mpq
     L, rows, refs = oracle_runs(name)
     T = layer_tensors(L)
-    R1 = np.stack([r["history"][t]["r1"] for r in refs]).astype(np.float32)
-    g1 = np.array([r["history"][t]["gamma1"] for r in refs], dtype=np.float32)
+    R1 = np.stack([r["history"][t]["r1"] for r in refs])
+    g1 = np.array([r["history"][t]["gamma1"] for r in refs])
     print(f"[group denoise] {name} t={t}", flush=True)
     xh, vt = mpq.denoise(dev(R1), dev(g1), L.E, T["a"], T["o"], group=L.group)
     xh, vt = host(xh), host(vt)
     wx, wv = 0.0, 0.0
     for k, i in enumerate(rows):
-        xr, vr, _ = O.denoise(R1[k].astype(np.float64), float(g1[k]), row_codebook(L, i), L.d)
+        xr, vr, _ = O.denoise(R1[k], float(g1[k]), row_codebook(L, i), L.d)
         wx = max(wx, rel_vec(xh[k], xr))
-        wv = max(wv, rel_scalar(vt[k].astype(np.float64).sum(), vr.sum()))
+        wv = max(wv, rel_scalar(vt[k].sum(), vr.sum()))
     print(f"  xhat1 {wx:.2e}  sum v {wv:.2e}", flush=True)
     assert wx < SOFT_RTOL and wv < SOFT_RTOL
 
@@ -77,26 +77,22 @@ def test_grouped_vamp_step(name):
     import post_quantization_solver_amd as mpq
     L, rows, refs = oracle_runs(name)
     T = layer_tensors(L)
-    ytil = dev(np.stack([O.rank_target(L.W[i], L.s, L.V) for i in rows]).astype(np.float32))
     worst = {}
     for t in range(L.T_vamp):
         h = [r["history"][t] for r in refs]
-        R1 = dev(np.stack([x["r1"] for x in h]).astype(np.float32))
-        g1 = dev(np.array([x["gamma1"] for x in h], dtype=np.float32))
-        bt = dev(np.array([x["beta"] for x in h], dtype=np.float32))
+        R1 = dev(np.stack([x["r1"] for x in h]))
+        g1 = dev(np.array([x["gamma1"] for x in h]))
+        bt = dev(np.array([x["beta"] for x in h]))
         print(f"[group vamp_step] {name} t={t}", flush=True)
-        out = mpq.vamp_step(R1, g1, bt, ytil, T["s"], T["V"], L.E, T["a"], T["o"], damping=L.damping,
+        out = mpq.vamp_step(R1, g1, bt, T["W"], T["s"], T["V"], L.E, T["a"], T["o"], damping=L.damping,
                             group=L.group)
         r1n, g1n, btn = host(R1), host(g1), host(bt)
         xh, eta1, g2, fb = (host(out[k]) for k in ("xhat1", "eta1", "gamma2", "fallback"))
         for k in range(len(rows)):
             nxt = refs[k]["history"][t + 1]["r1"] if t + 1 < L.T_vamp else refs[k]["r1_final"]
-            cond = max(1.0, h[k]["eta1"] / h[k]["gamma2"])
             g1_ref = refs[k]["gamma1_tr"][t + 1]
-            cond2 = max(1.0, h[k]["eta2"] / g1_ref * np.linalg.norm(h[k]["xhat2"] - h[k]["r2"]) /
-                        max(np.linalg.norm(nxt), 1e-300))
             e = dict(xhat1=rel_vec(xh[k], h[k]["xhat1"]), eta1=rel_scalar(eta1[k], h[k]["eta1"]),
-                     gamma2=rel_scalar(g2[k], h[k]["gamma2"]) / cond, r1=rel_vec(r1n[k], nxt) / cond2,
+                     gamma2=rel_scalar(g2[k], h[k]["gamma2"]), r1=rel_vec(r1n[k], nxt),
                      gamma1=rel_scalar(g1n[k], g1_ref), beta=rel_scalar(btn[k], refs[k]["beta_tr"][t + 1]),
                      fallback=float(bool(fb[k]) != bool(h[k]["fell_back"])))
             for key, v in e.items():
@@ -113,10 +109,10 @@ def test_grouped_map_and_cd(name):
     import post_quantization_solver_amd as mpq
     L, rows, refs = oracle_runs(name)
     T = layer_tensors(L)
-    R1 = np.stack([r["r1_final"] for r in refs]).astype(np.float32)
-    g1 = np.array([r["gamma1_tr"][-1] for r in refs], dtype=np.float32)
+    R1 = np.stack([r["r1_final"] for r in refs])
+    g1 = np.array([r["gamma1_tr"][-1] for r in refs])
     mc = host(mpq.map_codes(dev(R1), dev(g1), L.E, T["a"], T["o"], group=L.group))
-    ref = np.stack([O.map_codes(R1[k].astype(np.float64), float(g1[k]), row_codebook(L, i), L.d)
+    ref = np.stack([O.map_codes(R1[k], float(g1[k]), row_codebook(L, i), L.d)
                     for k, i in enumerate(rows)])
     map_agree = float((mc == ref).mean())
     start = dev(np.stack([r["map_codes"] for r in refs]).astype(np.int32))

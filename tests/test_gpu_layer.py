@@ -12,13 +12,13 @@ from oracle.pool import solve_rows
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(L, T_vamp=None, n_cd=None):
+def run_gpu(L, T_vamp=None, n_cd=None, **kw):
     import torch
     import post_quantization_solver_amd as mpq
     T = layer_tensors(L)
     out = mpq.quantize_layer(T["W"], T["s"], T["V"], L.E, T["a"], T["o"],
                              T_vamp=L.T_vamp if T_vamp is None else T_vamp,
-                             n_cd=L.n_cd if n_cd is None else n_cd, damping=L.damping)
+                             n_cd=L.n_cd if n_cd is None else n_cd, damping=L.damping, diagnostics=True, **kw)
     torch.cuda.synchronize()
     return {k: (host(v) if v is not None else None) for k, v in out.items()}
 
@@ -48,6 +48,33 @@ def test_layer_parity(name):
     assert summ["obj_rel_max"] < OBJ_RTOL
     for key, v in summ["trace_rel_max"].items():
         assert v < SOFT_RTOL, (key, v)
+    check_counts(L, gpu, refs)
+
+
+def check_counts(L, gpu, refs):
+    """Pass-through events and CD sweeps per row, as the oracle counts them."""
+    fb = np.array([r["fallbacks"] for r in refs])
+    sw = np.array([next((j + 1 for j, c in enumerate(r["cd_changes"]) if c == 0), L.n_cd) for r in refs])
+    assert np.array_equal(gpu["fallbacks"], fb), (gpu["fallbacks"], fb)
+    assert np.array_equal(gpu["sweeps"], sw), (gpu["sweeps"], sw)
+
+
+@pytest.mark.parametrize("eps", [0.05, 0.5])
+def test_safeguard_eps(eps):
+    """A positive safeguard threshold widens the pass-through rule: more rows
+    pass through, and the whole solve still matches the oracle run with the
+    same threshold."""
+    L = S.make_layer("eps", 24, 96, seed=37, d=1, bits=3, power=0.5, T_vamp=6)
+    rows = np.arange(L.m)
+    gpu = run_gpu(L, safeguard_eps=eps)
+    refs = solve_rows(L, rows, safeguard_eps=eps)
+    summ = compare_layer(L, rows, gpu, refs)
+    base = solve_rows(L, rows)
+    print(f"[safeguard {eps}] codes {summ['code_agreement']:.5f} obj {summ['obj_rel_max']:.2e} pass-through "
+          f"{int(gpu['fallbacks'].sum())} (eps 0: {sum(r['fallbacks'] for r in base)})", flush=True)
+    assert summ["code_agreement"] >= CODE_FRAC and summ["obj_rel_max"] < OBJ_RTOL
+    check_counts(L, gpu, refs)
+    assert gpu["fallbacks"].sum() > sum(r["fallbacks"] for r in base)
 
 
 def test_special_cases():
@@ -62,6 +89,7 @@ def test_special_cases():
     r1 = solve_rows(L, rows, n_cd=0)
     assert (g1["codes"] == np.stack([r["map_codes"] for r in r1])).mean() >= CODE_FRAC
     assert g1["cd_changes"] is None
+    assert np.all(g1["sweeps"] == 0)
 
 
 def test_frozen_rows_and_empty():
@@ -113,11 +141,11 @@ def test_scale_metamorphic():
     assert np.allclose(gs["gamma1_tr"], g["gamma1_tr"] / 16, rtol=1e-5)
 
 
-def test_cd_row_groups_on_streams():
-    """Layers of >= 1024 rows run their CD sweeps as two row groups on streams
-    of their own; each row's result must equal solving its group alone (both
-    halves use the same kernels and split counts), for the lattice and the
-    scalar CD."""
+def test_halves_equal_full_solve():
+    """Rows are independent problems: solving each half of a 1024-row layer
+    alone gives bitwise the rows of the whole layer, for the lattice and the
+    scalar CD (the row-compacted gradient updates and the per-row moves see
+    different row counts)."""
     for d, extra in ((8, dict(K=1000, r=60)), (1, dict(bits=3))):
         L = S.make_layer("grp", 1024, 64, seed=35, d=d, power=0.6, T_vamp=3, **extra)
         full = run_gpu(L)
@@ -147,7 +175,7 @@ def test_sampled_profile_counts_every_launch():
         runs[sampled] = (prof.as_dict()["cd_score"], host(out["codes"]))
     (ms_full, n_full), codes_full = runs[False]
     (ms_s, n_s), codes_s = runs[True]
-    # two row groups x 16 blocks x n_cd sweeps
-    assert n_full == n_s == 2 * (128 // 8) * L.n_cd
+    # 16 blocks x n_cd sweeps
+    assert n_full == n_s == (128 // 8) * L.n_cd
     assert ms_full > 0 and 0.2 < ms_s / ms_full < 5.0
     assert np.array_equal(codes_full, codes_s)

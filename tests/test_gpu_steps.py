@@ -2,7 +2,10 @@
 the oracle's own state and its outputs are compared with the oracle's.
 
 Tolerances: soft quantities 1e-4 relative (per row vector, per scalar), codes
->= 99.9 % of blocks, objectives 1e-5 relative.
+>= 99.9 % of blocks, objectives 1e-5 relative.  The VAMP state and its
+products are float64 on the GPU, so the teacher-forced steps are also held to
+F64_RTOL wherever the denoiser is exact in float64 (scalar grids and
+E8-prefix codebooks; the codebook scan for other lattices is float32).
 """
 import numpy as np
 import pytest
@@ -13,6 +16,9 @@ from parity_helpers import SOFT_RTOL, OBJ_RTOL, CODE_FRAC, dev, host, layer_tens
 from oracle.pool import solve_rows
 
 pytestmark = pytest.mark.gpu
+
+F64_RTOL = 1e-9
+SCAN = {"lattice_shuffled"}   # generic codebook: float32 scan denoiser
 
 
 def layers():
@@ -47,18 +53,15 @@ def test_prologue(name):
     T = layer_tensors(L)
     print(f"[prologue] {name} m={L.m} n={L.n} r={L.r} K={L.K} d={L.d}", flush=True)
     out = mpq.prologue(T["W"], T["s"], T["V"], L.E, T["a"], T["o"])
-    ytil = host(out["ytil"])
     rtn = host(out["rtn_codes"])
     g1 = host(out["gamma1"])
     b0 = host(out["beta"])
-    worst_y = max(rel_vec(ytil[i], O.rank_target(L.W[i], L.s, L.V)) for i in rows)
     agree = float(np.mean([np.mean(rtn[i] == refs[k]["rtn_codes"]) for k, i in enumerate(rows)]))
     wg = max(rel_scalar(g1[i], refs[k]["gamma1_tr"][0]) for k, i in enumerate(rows))
     wb = max(rel_scalar(b0[i], refs[k]["beta_tr"][0]) for k, i in enumerate(rows))
-    print(f"  ytil {worst_y:.2e} rtn agree {agree:.5f} gamma1 {wg:.2e} beta {wb:.2e}", flush=True)
-    assert worst_y < 1e-5
-    assert agree >= CODE_FRAC
-    assert wg < SOFT_RTOL and wb < SOFT_RTOL
+    print(f"  rtn agree {agree:.5f} gamma1 {wg:.2e} beta {wb:.2e}", flush=True)
+    assert agree == 1.0   # integer decisions on the same float32 weights, in float64 on both sides
+    assert wg < F64_RTOL and wb < F64_RTOL
 
 
 @pytest.mark.parametrize("name", NAMES)
@@ -67,19 +70,20 @@ def test_denoise(name, t):
     import post_quantization_solver_amd as mpq
     L, rows, refs = oracle_runs(name)
     T = layer_tensors(L)
-    R1 = np.stack([r["history"][t]["r1"] for r in refs]).astype(np.float32)
-    g1 = np.array([r["history"][t]["gamma1"] for r in refs], dtype=np.float32)
+    R1 = np.stack([r["history"][t]["r1"] for r in refs])
+    g1 = np.array([r["history"][t]["gamma1"] for r in refs])
     print(f"[denoise] {name} t={t}", flush=True)
     xh, vt = mpq.denoise(dev(R1), dev(g1), L.E, T["a"], T["o"])
     xh, vt = host(xh), host(vt)
     wx, wv = 0.0, 0.0
     for k, i in enumerate(rows):
         C = O.row_codewords(L.E, L.a[i], L.o[i])
-        xr, vr, _ = O.denoise(R1[k].astype(np.float64), float(g1[k]), C, L.d)
+        xr, vr, _ = O.denoise(R1[k], float(g1[k]), C, L.d)
         wx = max(wx, rel_vec(xh[k], xr))
-        wv = max(wv, rel_scalar(vt[k].astype(np.float64).sum(), vr.sum()))
+        wv = max(wv, rel_scalar(vt[k].sum(), vr.sum()))
     print(f"  xhat1 {wx:.2e}  sum v {wv:.2e}", flush=True)
-    assert wx < SOFT_RTOL and wv < SOFT_RTOL
+    tol = SOFT_RTOL if name in SCAN else F64_RTOL
+    assert wx < tol and wv < tol
 
 
 @pytest.mark.parametrize("name", NAMES)
@@ -87,15 +91,14 @@ def test_vamp_step(name):
     import post_quantization_solver_amd as mpq
     L, rows, refs = oracle_runs(name)
     T = layer_tensors(L)
-    ytil = np.stack([O.rank_target(L.W[i], L.s, L.V) for i in rows]).astype(np.float32)
     worst = {}
     for t in range(L.T_vamp):
         h = [r["history"][t] for r in refs]
-        R1 = dev(np.stack([x["r1"] for x in h]).astype(np.float32))
-        g1 = dev(np.array([x["gamma1"] for x in h], dtype=np.float32))
-        bt = dev(np.array([x["beta"] for x in h], dtype=np.float32))
+        R1 = dev(np.stack([x["r1"] for x in h]))
+        g1 = dev(np.array([x["gamma1"] for x in h]))
+        bt = dev(np.array([x["beta"] for x in h]))
         print(f"[vamp_step] {name} t={t}", flush=True)
-        out = mpq.vamp_step(R1, g1, bt, dev(ytil), T["s"], T["V"], L.E, T["a"], T["o"], damping=L.damping)
+        out = mpq.vamp_step(R1, g1, bt, T["W"], T["s"], T["V"], L.E, T["a"], T["o"], damping=L.damping)
         r1n, g1n, btn = host(R1), host(g1), host(bt)
         eta1, g2, fb = host(out["eta1"]), host(out["gamma2"]), host(out["fallback"])
         xh, r2 = host(out["xhat1"]), host(out["r2"])
@@ -104,25 +107,44 @@ def test_vamp_step(name):
             r1_ref = nxt["r1"] if nxt else refs[k]["r1_final"]
             g1_ref = refs[k]["gamma1_tr"][t + 1]
             b_ref = refs[k]["beta_tr"][t + 1]
-            # gamma2 = eta1 - gamma1 and r2 (which divides by gamma2) are
-            # compared relative to the subtraction's operands: errors scaled
-            # by cond = eta1 / gamma2 (1 when the posterior is passed through)
-            cond = max(1.0, h[k]["eta1"] / h[k]["gamma2"])
-            # r1' = r2 + (eta2/gamma1')(xhat2 - r2): relative to its largest operand
-            cond2 = max(1.0, h[k]["eta2"] / g1_ref * np.linalg.norm(h[k]["xhat2"] - h[k]["r2"]) /
-                        max(np.linalg.norm(r1_ref), 1e-300))
             errs = dict(xhat1=rel_vec(xh[k], h[k]["xhat1"]), eta1=rel_scalar(eta1[k], h[k]["eta1"]),
-                        gamma2=rel_scalar(g2[k], h[k]["gamma2"]) / cond, r2=rel_vec(r2[k], h[k]["r2"]) / cond,
-                        gamma2_raw=rel_scalar(g2[k], h[k]["gamma2"]), r2_raw=rel_vec(r2[k], h[k]["r2"]),
-                        r1=rel_vec(r1n[k], r1_ref) / cond2, r1_raw=rel_vec(r1n[k], r1_ref),
-                        gamma1=rel_scalar(g1n[k], g1_ref), beta=rel_scalar(btn[k], b_ref),
-                        fallback=float(bool(fb[k]) != bool(h[k]["fell_back"])))
+                        gamma2=rel_scalar(g2[k], h[k]["gamma2"]), r2=rel_vec(r2[k], h[k]["r2"]),
+                        r1=rel_vec(r1n[k], r1_ref), gamma1=rel_scalar(g1n[k], g1_ref),
+                        beta=rel_scalar(btn[k], b_ref), fallback=float(bool(fb[k]) != bool(h[k]["fell_back"])))
             for key, v in errs.items():
                 worst[key] = max(worst.get(key, 0.0), v)
     print("  worst:", {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
     assert worst["fallback"] == 0.0
+    tol = SOFT_RTOL if name in SCAN else F64_RTOL
     for key in ("xhat1", "eta1", "gamma2", "r2", "r1", "gamma1", "beta"):
-        assert worst[key] < SOFT_RTOL, (key, worst[key])
+        assert worst[key] < tol, (key, worst[key])
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_linear_step(name):
+    """The linear module + M-step alone, from the oracle's extrinsic message."""
+    import post_quantization_solver_amd as mpq
+    L, rows, refs = oracle_runs(name)
+    T = layer_tensors(L)
+    worst = {}
+    for t in range(L.T_vamp):
+        h = [r["history"][t] for r in refs]
+        R2 = dev(np.stack([x["r2"] for x in h]))
+        g2 = dev(np.array([x["gamma2"] for x in h]))
+        bt = dev(np.array([x["beta"] for x in h]))
+        print(f"[linear_step] {name} t={t}", flush=True)
+        R1, g1 = mpq.linear_step(R2, g2, bt, T["W"], T["s"], T["V"], damping=L.damping)
+        r1n, g1n, btn = host(R1), host(g1), host(bt)
+        for k in range(len(rows)):
+            nxt = refs[k]["history"][t + 1] if t + 1 < L.T_vamp else None
+            r1_ref = nxt["r1"] if nxt else refs[k]["r1_final"]
+            errs = dict(r1=rel_vec(r1n[k], r1_ref), gamma1=rel_scalar(g1n[k], refs[k]["gamma1_tr"][t + 1]),
+                        beta=rel_scalar(btn[k], refs[k]["beta_tr"][t + 1]))
+            for key, v in errs.items():
+                worst[key] = max(worst.get(key, 0.0), v)
+    print("  worst:", {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
+    for key, v in worst.items():
+        assert v < F64_RTOL, (key, v)
 
 
 @pytest.mark.parametrize("name", NAMES)
@@ -130,14 +152,17 @@ def test_map(name):
     import post_quantization_solver_amd as mpq
     L, rows, refs = oracle_runs(name)
     T = layer_tensors(L)
-    R1 = np.stack([r["r1_final"] for r in refs]).astype(np.float32)
-    g1 = np.array([r["gamma1_tr"][-1] for r in refs], dtype=np.float32)
+    R1 = np.stack([r["r1_final"] for r in refs])
+    g1 = np.array([r["gamma1_tr"][-1] for r in refs])
     codes = host(mpq.map_codes(dev(R1), dev(g1), L.E, T["a"], T["o"]))
-    ref = np.stack([O.map_codes(R1[k].astype(np.float64), float(g1[k]), O.row_codewords(L.E, L.a[i], L.o[i]), L.d)
+    ref = np.stack([O.map_codes(R1[k], float(g1[k]), O.row_codewords(L.E, L.a[i], L.o[i]), L.d)
                     for k, i in enumerate(rows)])
     agree = float((codes == ref).mean())
     print(f"[map] {name} agreement {agree:.5f}", flush=True)
-    assert agree >= CODE_FRAC
+    if name in SCAN:
+        assert agree >= CODE_FRAC
+    else:
+        assert agree == 1.0
 
 
 @pytest.mark.parametrize("name", NAMES)
@@ -148,9 +173,10 @@ def test_cd(name):
     T = layer_tensors(L)
     start = np.stack([r["map_codes"] for r in refs]).astype(np.int32)
     codes = dev(start)
-    codes, ch = mpq.cd(T["W"], T["s"], T["V"], L.E, T["a"], T["o"], codes, n_cd=L.n_cd)
+    sweeps = torch.zeros(L.m, dtype=torch.int32, device="cuda")
+    codes, ch = mpq.cd(T["W"], T["s"], T["V"], L.E, T["a"], T["o"], codes, n_cd=L.n_cd, sweeps=sweeps)
     torch.cuda.synchronize()
-    codes, ch = host(codes), host(ch)
+    codes, ch, sweeps = host(codes), host(ch), host(sweeps)
     ref = np.stack([r["codes"] for r in refs])
     agree = float((codes == ref).mean())
     f_gpu = np.array([O.codes_objective(L.W[i], codes[k], O.row_codewords(L.E, L.a[i], L.o[i]), L.d, L.s, L.V)
@@ -162,3 +188,6 @@ def test_cd(name):
           flush=True)
     assert agree >= CODE_FRAC
     assert obj < OBJ_RTOL
+    # sweeps run: up to and including the first sweep without a change
+    want = np.array([next((j + 1 for j, c in enumerate(r["cd_changes"]) if c == 0), L.n_cd) for r in refs])
+    assert (sweeps == want).all(), (sweeps, want)
