@@ -34,6 +34,8 @@ METRIC = "weights quantized/sec per layer (T_vamp=16 + 3 CD sweeps), % of MFMA/H
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_FP64_TFLOPS = 78.6        # float64 matrix and vector alike on MI355X
+PEAK_INT8_TOPS = 5000.0        # dense int8 MFMA
+DIGIT_PRODUCTS = 15            # int8 digit products per float64-accurate multiply-add (linear module)
 PEAK_HBM_GBS = 8000.0
 CD_MFMA_FLOP_PER_EVAL = 64     # bf16 MFMA flops the CD scoring issues per (row, block, codeword)
 # Transcendental issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz at half
@@ -75,8 +77,9 @@ def group_work(L, kernel, launches, steps, n_cd):
         return (launches * m * (n // d) * K * per, per * EXP_RATE / 1e12, "alu",
                 f"{per} flops and one exponential per (block, codeword)")
     if kernel in ("linear1", "linear2"):
-        # one m x n x r product per launch on the fp64 matrix cores
-        return launches * 2.0 * m * n * r, PEAK_FP64_TFLOPS, "mfma", "2mnr flops per launch, float64 MFMA"
+        # one m x n x r product per launch, float64-accurate, issued as exact
+        # int8 digit products on the int8 matrix cores
+        return launches * 2.0 * m * n * r, PEAK_INT8_TOPS, "mfma", "2mnr flops per launch, int8 digit MFMA"
     if kernel == "cd_score" and d == 8:
         # every sweep scores every codeword for every (row, block): the
         # method's own work is 2d flops per eval (e . q); it issues bf16 MFMAs
@@ -98,6 +101,14 @@ def dominant_roofline(L, prof, steps, n_cd):
     flops, peak, bound, basis = w
     achieved = flops / (ms / 1e3) / 1e12
     out = dict(base, bound=bound, achieved=achieved, peak=peak, unit="TFLOP/s", frac=achieved / peak, basis=basis)
+    if best in ("linear1", "linear2"):
+        issued = DIGIT_PRODUCTS * achieved
+        out["secondary"] = dict(bound="mfma", achieved=issued, peak=PEAK_INT8_TOPS, unit="TOP/s",
+                                frac=issued / PEAK_INT8_TOPS,
+                                basis=f"int8 MFMA operations as issued ({DIGIT_PRODUCTS} digit products per "
+                                      "float64-accurate multiply-add), not the method's work",
+                                fp64_equivalent=dict(achieved=achieved, peak=PEAK_FP64_TFLOPS,
+                                                     frac=achieved / PEAK_FP64_TFLOPS))
     if best == "cd_score":
         issued = flops / (2.0 * L.d) * CD_MFMA_FLOP_PER_EVAL / (ms / 1e3) / 1e12
         out["secondary"] = dict(bound="mfma", achieved=issued, peak=PEAK_BF16_MFMA_TFLOPS, unit="TFLOP/s",
@@ -110,27 +121,31 @@ def dominant_roofline(L, prof, steps, n_cd):
 def denoise_linear_fraction(L, prof, steps):
     """mpq_denoise + mpq_linear together: (a) the fraction of their measured
     time the issuing units would need at peak for the method's algorithmic
-    work (sum of work / peak over the sum of times); (b) the work as the
-    target counts it (32 flops per block x codeword eval, 4mnr per iteration)
-    over the same time, against the fp32 MFMA peak."""
+    work (sum of work / peak over the sum of times; the linear module's 2mnr
+    against the int8 peak it issues on); (a') the same with the linear
+    module's work counted as the int8 operations it issues; (b) the work as
+    the target counts it (32 flops per block x codeword eval, 4mnr per
+    iteration) over the same time, against the fp32 MFMA peak."""
     keys = [k for k in ("denoise", "linear1", "linear2") if k in prof]
     secs = sum(prof[k][0] for k in keys) / 1e3
     if secs <= 0:
         return None
-    need = 0.0
+    need = need_issued = 0.0
     for k in keys:
         w = group_work(L, k, prof[k][1], steps, L.n_cd)
         if w is None:
             return None
         need += w[0] / (w[1] * 1e12)
+        need_issued += w[0] * (DIGIT_PRODUCTS if k.startswith("linear") else 1) / (w[1] * 1e12)
     T = L.T_vamp * steps
     target_flops = T * (L.m * (L.n // L.d) * L.K * NORTH_STAR_EVAL_FLOPS + 4.0 * L.m * L.n * L.r)
-    return dict(seconds=secs, frac_of_issuing_peaks=need / secs,
+    return dict(seconds=secs, frac_of_issuing_peaks=need / secs, frac_of_issuing_peaks_as_issued=need_issued / secs,
                 target_count_tflops=target_flops / secs / 1e12,
                 target_count_frac_fp32=target_flops / secs / 1e12 / PEAK_FP32_MFMA_TFLOPS,
                 basis="(a) sum over denoise, linear 1, linear 2 of algorithmic work / peak of the issued dtype, "
-                      "over their summed time; (b) 32 flops per (block, codeword) eval + 4mnr per iteration over "
-                      "the same time, against the fp32 MFMA peak (the E8 path does far less work than that count)")
+                      "over their summed time; (a') the same with the linear products counted as the int8 digit "
+                      "products they issue; (b) 32 flops per (block, codeword) eval + 4mnr per iteration over the "
+                      "same time, against the fp32 MFMA peak (the E8 path does far less work than that count)")
 
 
 def measured_peak(roof, probes):
@@ -138,7 +153,7 @@ def measured_peak(roof, probes):
     if roof["peak"] is None:
         return None
     if roof["kernel"] in ("linear1", "linear2"):
-        return probes["mfma_f64_tflops"]
+        return None   # no int8 MFMA probe
     if roof["bound"] == "mfma":
         return probes["mfma_bf16_tflops"]
     if roof.get("basis", "").startswith("E8 forward-backward"):
@@ -162,7 +177,10 @@ def measured_traffic(config, kernel):
         return None
     h = hashlib.sha256()
     for f in rec["sources"]:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        path = os.path.join(ROOT, f)
+        if not os.path.exists(path):
+            return None
+        h.update(open(path, "rb").read())
     return rec["hbm_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
 
 

@@ -136,7 +136,8 @@ void mpq_profiler_destroy(mpq_profiler* p);
 #define MPQ_PROF_OTHER     9  /* traces, copies, factor preparation */
 #define MPQ_PROF_DENOISE_EXACT 10  /* lattice denoiser: exact pass over the queries the fast pass flagged */
 #define MPQ_PROF_CD_SCORE 11  /* lattice CD: the codebook scoring kernel alone (MPQ_PROF_CD_SEARCH keeps the rest) */
-#define MPQ_PROF_COUNT    12
+#define MPQ_PROF_SPLIT    12  /* digit split of the linear module's operands (int8 digit GEMM) */
+#define MPQ_PROF_COUNT    13
 
 /* ------------------------------------------------------------------ options */
 
@@ -202,6 +203,9 @@ typedef struct {
                                       return MPQ_ENONFINITE, having run nothing else, if any entry is
                                       NaN or infinite or a row scale is <= 0; the call waits for the
                                       scan's verdict */
+#define MPQ_F_LINEAR_F64     64u   /* run the linear module's rank-space products on the fp64 matrix
+                                      cores instead of the int8 digit GEMM (for A/B checks; the digit
+                                      GEMM also gives way by itself when n or r exceeds 32767) */
 
 /* ------------------------------------------------------------------ sizes, status */
 
@@ -226,7 +230,10 @@ const char* mpq_hip_error_name(void);
  * designs 1 (denoiser, rank-space linear module), 2 (beta M-step, damping),
  * 3 (marginal MAP, exact block CD) and the hyper-parameter paragraph
  * (gamma1^0 = 1 / MSE(w, w_rtn), S_CD sweeps with early stop).  The VAMP
- * state and all its products are float64; CD decides in float64.
+ * state is float64; the linear module's rank-space products are float64
+ * accurate (exact int8 digit products summed in int32 on the matrix cores,
+ * about 1e-10 relative, or fp64 MFMA with MPQ_F_LINEAR_F64); CD decides in
+ * float64.
  *
  * Inputs: W, s, V, row_scale, row_offset as in the conventions; T_vamp >= 0;
  * n_cd >= 0; damping in (0, 1] (the weight of the new beta).

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmpq.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "gemm64.hip", "rowops.hip", "scalar.hip", "lattice.hip", "cd.hip", "cd_lattice.hip",
-           "chol.hip", "greedy.hip", "frontend.hip", "e8dp.hip", "probe.hip"]
+           "chol.hip", "greedy.hip", "frontend.hip", "e8dp.hip", "probe.hip", "digitgemm.hip"]
 ARCH = os.environ.get("MPQ_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

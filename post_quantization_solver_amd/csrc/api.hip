@@ -133,8 +133,13 @@ struct Layout {
 
 enum Region {
   R_VT, R_VS64, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI, R_CHG, R_CODES,
-  R_FLAG, R_D64, R_TKEY, R_QF, R_ANCH, R_LAM, R_CTMP, R_GDIAG, R_MROWS, R_HFULL, R_G64, R_ACTIVE, R_CHECK, R_COUNT
+  R_FLAG, R_D64, R_TKEY, R_QF, R_ANCH, R_LAM, R_CTMP, R_GDIAG, R_MROWS, R_HFULL, R_G64, R_ACTIVE, R_CHECK,
+  R_DPA, R_DPVT, R_DPV, R_DEA, R_DEVT, R_DEV, R_COUNT
 };
+
+// The linear module's products take the int8 digit GEMM when both of its
+// inner dimensions fit it.
+bool digits_fit(int64_t n, int64_t r) { return n <= DG_MAX_K && r <= DG_MAX_K; }
 
 static_assert(R_COUNT <= (int)(sizeof(Layout::off) / sizeof(size_t)), "Layout::off holds every region");
 
@@ -185,6 +190,15 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, bool g
   sz[R_MROWS] = (size_t)(m + 64) * i32;
   sz[R_ACTIVE] = (size_t)m * i32;   // rows still sweeping (for the sweeps output)
   sz[R_CHECK] = 64;                 // MPQ_F_CHECK_FINITE flag
+  // digit planes of the linear module's operands: W - r2 or z (per call), and
+  // V^T and V (once per call), with their row exponents
+  const bool dg = digits_fit(n, r);
+  sz[R_DPA] = dg ? std::max(digit_plane_bytes(m, n), digit_plane_bytes(m, r)) : 0;
+  sz[R_DPVT] = dg ? digit_plane_bytes(r, n) : 0;
+  sz[R_DPV] = dg ? digit_plane_bytes(n, r) : 0;
+  sz[R_DEA] = dg ? (size_t)m * i32 : 0;
+  sz[R_DEVT] = dg ? (size_t)r * i32 : 0;
+  sz[R_DEV] = dg ? (size_t)n * i32 : 0;
   size_t o = 0;
   for (int k = 0; k < R_COUNT; ++k) {
     L.off[k] = o;
@@ -373,6 +387,10 @@ struct Ctx {
   // E8-prefix nearest codeword: the lattice decoder first, the automaton for
   // the blocks it cannot settle (else the automaton for every block)
   bool e8_decode = true;
+  // the linear module's products on the int8 digit GEMM (else on the fp64
+  // matrix cores)
+  bool digits = false;
+  uint8_t* dp(Region k) const { return reinterpret_cast<uint8_t*>(ws + L.off[k]); }
   // d = 8 codebooks that are the first K points of E8 in (norm, lex) order:
   // the denoiser runs the forward-backward pass over coordinates
   bool e8dp = false;
@@ -431,10 +449,27 @@ int denoise(Ctx& c, const double* R1, const double* gamma1, const float* a, cons
 }
 
 // Vt = V^T (float32) for the products with V; with `vs`, also the exact
-// float64 VS = V diag(s) for H and the objective.
+// float64 VS = V diag(s) for H and the objective; with the digit GEMM, the
+// digit planes of V^T and V.
 int prepare_factors(Ctx& c, const float* V, const float* s, bool vs) {
-  TIMED(c, MPQ_PROF_OTHER, launch_prepare_v(V, s, c.L.n, c.L.r, c.f(R_VT), vs ? c.d(R_VS64) : nullptr, c.st));
+  const Layout& L = c.L;
+  TIMED(c, MPQ_PROF_OTHER, launch_prepare_v(V, s, L.n, L.r, c.f(R_VT), vs ? c.d(R_VS64) : nullptr, c.st));
+  if (c.digits) {
+    TIMED(c, MPQ_PROF_SPLIT, launch_digit_split_f32(c.f(R_VT), L.r, L.n, L.n, c.pi(R_DEVT), c.dp(R_DPVT), c.st));
+    TIMED(c, MPQ_PROF_SPLIT, launch_digit_split_f32(V, L.n, L.r, L.r, c.pi(R_DEV), c.dp(R_DPV), c.st));
+  }
   return MPQ_OK;
+}
+
+DigitGemmArgs digit_args(const Ctx& c, int M, int N, int K, Region bplanes, Region bexp) {
+  DigitGemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.M = M; g.N = N; g.K = K;
+  g.Ap = c.dp(R_DPA);
+  g.EA = c.pi(R_DEA);
+  g.Bp = c.dp(bplanes);
+  g.EB = c.pi(bexp);
+  return g;
 }
 
 // Collect profiling results (waits for the call's last event).
@@ -481,11 +516,20 @@ int run_prologue(Ctx& c, const float* W, const float* s, const float* a, const f
   double* D = c.d(R_D64);
   TIMED(c, MPQ_PROF_PROLOGUE, nearest_f(c, W, rtn, a, o));
   TIMED(c, MPQ_PROF_PROLOGUE, launch_gather(rtn, L.m, L.n, c.cb, a, o, W, nullptr, c.rowsq(), c.st, D));
-  Gemm64Args g = gemm64((int)L.m, (int)L.r, (int)L.n, D, L.n, c.f(R_VT), L.n, nullptr, 0);
-  g.s = s;
-  g.partial = c.d(R_PART);
-  g.ldp = gemm_col_tiles((int)L.r);
-  TIMED(c, MPQ_PROF_PROLOGUE, launch_gemm64(EPI_ROWSUMSQ_S, true, g, c.st));
+  if (c.digits) {
+    TIMED(c, MPQ_PROF_PROLOGUE, launch_digit_split(D, L.m, L.n, L.n, c.pi(R_DEA), c.dp(R_DPA), c.st));
+    DigitGemmArgs g = digit_args(c, (int)L.m, (int)L.r, (int)L.n, R_DPVT, R_DEVT);
+    g.s = s;
+    g.partial = c.d(R_PART);
+    g.ldp = gemm_col_tiles((int)L.r);
+    TIMED(c, MPQ_PROF_PROLOGUE, launch_digit_gemm(EPI_ROWSUMSQ_S, g, c.st));
+  } else {
+    Gemm64Args g = gemm64((int)L.m, (int)L.r, (int)L.n, D, L.n, c.f(R_VT), L.n, nullptr, 0);
+    g.s = s;
+    g.partial = c.d(R_PART);
+    g.ldp = gemm_col_tiles((int)L.r);
+    TIMED(c, MPQ_PROF_PROLOGUE, launch_gemm64(EPI_ROWSUMSQ_S, true, g, c.st));
+  }
   TIMED(c, MPQ_PROF_PROLOGUE, launch_prologue_finish(L.m, L.n, L.r, c.rowsq(), c.d(R_PART), gemm_col_tiles((int)L.r),
                                                      beta0, gamma1, beta, c.st));
   return MPQ_OK;
@@ -502,20 +546,42 @@ int run_linear(Ctx& c, const float* W, const float* s, const float* V, double* R
   const Layout& L = c.L;
   double* D2 = c.d(R_R2);
   TIMED(c, MPQ_PROF_EXTRINSIC, launch_beta_lin(L.m, gamma1, beta, c.betalin(), c.gamma2(), c.st));
-  Gemm64Args g1 = gemm64((int)L.m, (int)L.r, (int)L.n, D2, L.n, c.f(R_VT), L.n, c.d(R_Z), L.r);
-  g1.s = s;
-  g1.rowa = c.betalin();
-  g1.rowb = c.gamma2();
-  g1.partial = c.d(R_PART);
-  g1.ldp = gemm_col_tiles((int)L.r);
-  TIMED(c, MPQ_PROF_LINEAR1, launch_gemm64(EPI_LINEAR1, true, g1, c.st));
+  if (c.digits) {
+    TIMED(c, MPQ_PROF_SPLIT, launch_digit_split(D2, L.m, L.n, L.n, c.pi(R_DEA), c.dp(R_DPA), c.st));
+    DigitGemmArgs g1 = digit_args(c, (int)L.m, (int)L.r, (int)L.n, R_DPVT, R_DEVT);
+    g1.C = c.d(R_Z); g1.ldc = L.r;
+    g1.s = s;
+    g1.rowa = c.betalin();
+    g1.rowb = c.gamma2();
+    g1.partial = c.d(R_PART);
+    g1.ldp = gemm_col_tiles((int)L.r);
+    TIMED(c, MPQ_PROF_LINEAR1, launch_digit_gemm(EPI_LINEAR1, g1, c.st));
+  } else {
+    Gemm64Args g1 = gemm64((int)L.m, (int)L.r, (int)L.n, D2, L.n, c.f(R_VT), L.n, c.d(R_Z), L.r);
+    g1.s = s;
+    g1.rowa = c.betalin();
+    g1.rowb = c.gamma2();
+    g1.partial = c.d(R_PART);
+    g1.ldp = gemm_col_tiles((int)L.r);
+    TIMED(c, MPQ_PROF_LINEAR1, launch_gemm64(EPI_LINEAR1, true, g1, c.st));
+  }
   TIMED(c, MPQ_PROF_BETA, launch_beta(L.m, L.n, L.r, s, c.d(R_PART), gemm_col_tiles((int)L.r), c.gamma2(), damping,
                                       fixed_beta, beta, gamma1, c.coef(), c.st));
-  Gemm64Args g2 = gemm64((int)L.m, (int)L.n, (int)L.r, c.d(R_Z), L.r, V, L.r, R1, L.n);
-  g2.rowa = c.coef();
-  g2.X = D2; g2.ldx = L.n;
-  g2.W = W; g2.ldw = L.n;
-  TIMED(c, MPQ_PROF_LINEAR2, launch_gemm64(EPI_AXPY_W, true, g2, c.st));
+  if (c.digits) {
+    TIMED(c, MPQ_PROF_SPLIT, launch_digit_split(c.d(R_Z), L.m, L.r, L.r, c.pi(R_DEA), c.dp(R_DPA), c.st));
+    DigitGemmArgs g2 = digit_args(c, (int)L.m, (int)L.n, (int)L.r, R_DPV, R_DEV);
+    g2.C = R1; g2.ldc = L.n;
+    g2.rowa = c.coef();
+    g2.X = D2; g2.ldx = L.n;
+    g2.W = W; g2.ldw = L.n;
+    TIMED(c, MPQ_PROF_LINEAR2, launch_digit_gemm(EPI_AXPY_W, g2, c.st));
+  } else {
+    Gemm64Args g2 = gemm64((int)L.m, (int)L.n, (int)L.r, c.d(R_Z), L.r, V, L.r, R1, L.n);
+    g2.rowa = c.coef();
+    g2.X = D2; g2.ldx = L.n;
+    g2.W = W; g2.ldw = L.n;
+    TIMED(c, MPQ_PROF_LINEAR2, launch_gemm64(EPI_AXPY_W, true, g2, c.st));
+  }
   return MPQ_OK;
 }
 
@@ -862,6 +928,7 @@ int begin(Ctx& c, int64_t m, int64_t n, int64_t r, const mpq_codebook* cb, void*
     c.eps = (double)opt->safeguard_eps;
   }
   c.e8_decode = !(opt && (opt->flags & MPQ_F_NO_E8_DECODE));
+  c.digits = digits_fit(n, r) && !(opt && (opt->flags & MPQ_F_LINEAR_F64));
   // codebook tables
   const TableLayout T = table_layout(cb->K, cb->d);
   const char* tb = static_cast<const char*>(cb->tables);
@@ -1106,6 +1173,7 @@ int mpq_linear_step(const double* R2, const double* gamma2, double* beta, const 
     if (m < 0 || n < 1 || r < 1 || r > n || n > MPQ_MAX_N || m > ((int64_t)1 << 23)) return MPQ_ESHAPE;
     Ctx c;
     c.L = make_layout(m, n, r, 2, 1);
+    c.digits = digits_fit(n, r) && !(opt && (opt->flags & MPQ_F_LINEAR_F64));
     int rc = check_ws(c.L, workspace, ws_bytes);
     if (rc) return rc;
     if (m == 0) return MPQ_OK;

@@ -1,0 +1,354 @@
+// The linear module's rank-space products in float64 accuracy on the int8
+// matrix cores (v_mfma_i32_16x16x64_i8), for K <= DG_MAX_K:
+//
+//   C[M x N] = A[M x K] * B[N x K]^T,  A float64 (w - r2, or z), B float32 (V^T or V).
+//
+// Digit split (an exact integer form of each operand).  Row i of A is scaled
+// by its own power of two 2^E_i > max_k |A_ik| and rounded to the integer
+// N_ik = rint(A_ik 2^(38 - E_i)), |N_ik| <= 2^38, which is written in balanced
+// base-256 digits N = sum_p d_p 256^(4 - p), p = 0..4: the low four in
+// [-128, 127], the top one in [-64, 64].  B's rows likewise (F_j).  Then
+//
+//   sum_k A_ik B_jk ~= 2^(E_i + F_j - 12) sum_{l=0..4} 2^(-8 l) I_l,
+//   I_l = sum_{p+q=l} sum_k d_p(A_ik) d_q(B_jk),
+//
+// each I_l an exact int32 sum of int8 x int8 products (|I_l| <= 65536 K <
+// 2^31 for K < 32768), converted to float64 once after the K loop.  The
+// pairs with p + q > 4 (below 2^-38 of max|A_ik| max|B_jk| per term) are
+// dropped: 15 int8 products per output and k, against the 53-bit float64
+// product; the rank-space output is accurate to about 1e-10 relative (the
+// split itself is exact to 2^-39 of each row's largest entry).
+//
+// Layout.  The digits live in "fragment order": for every 16-row x 64-k
+// chunk of one digit plane, 64 lanes x 16 bytes exactly as lane (i, g) of an
+// MFMA operand holds them (row i, k = 16 g .. 16 g + 15), chunks ordered
+// [row tile of 16][k tile of 64][plane].  A chunk reaches LDS with one
+// global_load_lds_dwordx4 per wave (lane l's 16 bytes land at 16 l) and an
+// operand fragment is then one conflict-free 16-byte LDS read per lane.
+//
+// Tiling: 512 threads (8 waves) per 128 x 128 output tile, K in steps of 64
+// through two LDS stages of 80 KB (5 planes x (128 + 128) rows x 64 bytes;
+// the next step's chunks stream in while this one is multiplied).  Each
+// wave owns 32 x 64 outputs: 2 x 4 sub-tiles of 16 x 16, 5 int32
+// accumulators each.  Tiles go to the XCDs in contiguous runs and, within a
+// run, in groups of 8 tile rows column by column, so the tiles resident on one
+// XCD share their A and B panels in its L2.
+#include <math.h>
+#include <limits.h>
+#include "mpq_device.h"
+#include "internal.h"
+
+namespace mpq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int DG_S = 5;             // digits per operand entry
+constexpr int DG_CHUNK = 1024;      // bytes of one 16-row x 64-k chunk of one plane
+constexpr int DG_TILE = 128;        // output tile (rows and columns)
+constexpr int DG_RT = DG_TILE / 16; // row tiles per output tile side
+constexpr int DG_CHUNKS = 2 * DG_RT * DG_S;   // chunks per K step (A and B)
+constexpr int DG_WAVES = 8;
+constexpr int DG_GROUP_M = 8;       // tile rows per group of the tile order
+constexpr int DG_EXP_NONFINITE = INT_MAX;     // row exponent of a row holding NaN or inf
+
+// Bytes of the digit planes of a rows x K operand (row tiles padded to whole
+// output tiles, K to whole steps).
+size_t digit_plane_bytes(int64_t rows, int64_t K) {
+  const int64_t rt = (rows + DG_TILE - 1) / DG_TILE * DG_RT;
+  const int64_t kt = (K + 63) / 64;
+  return (size_t)(rt * kt * DG_S) * DG_CHUNK;
+}
+
+// --------------------------------------------------------------- digit split
+
+// E[i] with max_k |X_ik| < 2^E[i] (0 for a zero row, DG_EXP_NONFINITE for a
+// row holding NaN or inf); one wave per row.
+template <typename T>
+__global__ __launch_bounds__(256) void digit_exp_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t ld,
+                                                        int32_t* __restrict__ E) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= rows) return;
+  double mx = 0.0;
+  bool bad = false;
+  for (int64_t k = lane; k < K; k += 64) {
+    const double v = (double)X[i * ld + k];
+    bad = bad || !isfinite(v);
+    mx = fmax(mx, fabs(v));
+  }
+#pragma unroll
+  for (int msk = 32; msk >= 1; msk >>= 1) mx = fmax(mx, __shfl_xor(mx, msk, 64));
+  bad = __any(bad);
+  if (lane == 0) {
+    int e = 0;
+    if (mx > 0.0) (void)frexp(mx, &e);   // mx = f 2^e, f in [0.5, 1)
+    E[i] = bad ? DG_EXP_NONFINITE : e;
+  }
+}
+
+// The digit planes, one wave per 16-row x 64-k chunk position: lane (i, g)
+// splits X[row i][k = 16 g .. 16 g + 15] (zero outside the matrix) and writes
+// its 16 bytes of each of the five planes.
+template <typename T>
+__global__ __launch_bounds__(256) void digit_split_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t ld,
+                                                          const int32_t* __restrict__ E, int64_t nrt, int64_t nkt,
+                                                          uint8_t* __restrict__ planes) {
+  const int lane = threadIdx.x & 63;
+  const int64_t pos = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // chunk position = rt * nkt + kt
+  if (pos >= nrt * nkt) return;
+  const int64_t rt = pos / nkt, kt = pos - rt * nkt;
+  const int i = lane & 15, g = lane >> 4;
+  const int64_t row = rt * 16 + i;
+  const int64_t k0 = kt * 64 + 16 * g;
+  const bool live = row < rows;
+  const int e = live ? E[row] : 0;
+  const bool ok = live && e != DG_EXP_NONFINITE;
+  uint32_t w[DG_S][4];
+#pragma unroll
+  for (int p = 0; p < DG_S; ++p)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[p][q] = 0u;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int64_t k = k0 + t;
+    const double v = ok && k < K ? (double)X[row * ld + k] : 0.0;
+    long long N = llrint(ldexp(v, 38 - e));   // |N| <= 2^38
+    int d[DG_S];
+#pragma unroll
+    for (int p = DG_S - 1; p >= 1; --p) {
+      const int r = (int)(N & 255);
+      d[p] = r >= 128 ? r - 256 : r;
+      N = (N - d[p]) >> 8;
+    }
+    d[0] = (int)N;   // in [-64, 64]
+#pragma unroll
+    for (int p = 0; p < DG_S; ++p) w[p][t >> 2] |= ((uint32_t)d[p] & 255u) << (8 * (t & 3));
+  }
+#pragma unroll
+  for (int p = 0; p < DG_S; ++p) {
+    uint4* dst = reinterpret_cast<uint4*>(planes + ((size_t)pos * DG_S + p) * DG_CHUNK) + lane;
+    *dst = make_uint4(w[p][0], w[p][1], w[p][2], w[p][3]);
+  }
+}
+
+template <typename T>
+static hipError_t split(const T* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes, hipStream_t st) {
+  if (rows <= 0 || K <= 0) return hipSuccess;
+  hipLaunchKernelGGL(digit_exp_kernel<T>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, X, rows, K, ld, E);
+  const int64_t nrt = (rows + DG_TILE - 1) / DG_TILE * DG_RT;
+  const int64_t nkt = (K + 63) / 64;
+  hipLaunchKernelGGL(digit_split_kernel<T>, dim3((unsigned)((nrt * nkt + 3) / 4)), dim3(256), 0, st, X, rows, K, ld,
+                     E, nrt, nkt, planes);
+  return hipGetLastError();
+}
+
+hipError_t launch_digit_split(const double* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes,
+                              hipStream_t st) {
+  return split<double>(X, rows, K, ld, E, planes, st);
+}
+hipError_t launch_digit_split_f32(const float* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes,
+                                  hipStream_t st) {
+  return split<float>(X, rows, K, ld, E, planes, st);
+}
+
+// ------------------------------------------------------------------ the GEMM
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// This wave's share of one K step's chunks, straight into LDS stage `buf`.
+__device__ __forceinline__ void fetch_step(uint8_t (*stage)[DG_CHUNK], const uint8_t* __restrict__ Ap,
+                                           const uint8_t* __restrict__ Bp, int64_t rt0, int64_t ct0, int64_t nkt,
+                                           int64_t kt, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < DG_CHUNKS / DG_WAVES; ++j) {
+    const int c = wave * (DG_CHUNKS / DG_WAVES) + j;   // wave-uniform
+    const uint8_t* src;
+    if (c < DG_RT * DG_S) {
+      const int rt = c / DG_S, p = c - rt * DG_S;
+      src = Ap + (((rt0 + rt) * nkt + kt) * DG_S + p) * DG_CHUNK;
+    } else {
+      const int cc = c - DG_RT * DG_S;
+      const int ct = cc / DG_S, q = cc - ct * DG_S;
+      src = Bp + (((ct0 + ct) * nkt + kt) * DG_S + q) * DG_CHUNK;
+    }
+    __builtin_amdgcn_global_load_lds(src + 16 * lane, (lds_ptr_t)stage[c], 16, 0, 0);
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][DG_CHUNKS][DG_CHUNK];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wm = wave >> 1;   // 4 wave rows of 32
+  const int wn = wave & 1;    // 2 wave columns of 64
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+  // tile order: contiguous runs per XCD (workgroups go to the 8 XCDs in
+  // turn), groups of DG_GROUP_M tile rows column by column within a run
+  const int tm = (g.M + DG_TILE - 1) / DG_TILE, tn = (g.N + DG_TILE - 1) / DG_TILE;
+  const int T = tm * tn;
+  const int per = (T + 7) / 8;
+  const int tile = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (tile >= T) return;
+  const int group = tile / (DG_GROUP_M * tn);
+  const int first = group * DG_GROUP_M;
+  const int gm = min(tm - first, DG_GROUP_M);
+  const int in = tile - group * DG_GROUP_M * tn;
+  const int tr = first + in % gm, tc = in / gm;
+  const int row0 = tr * DG_TILE, col0 = tc * DG_TILE;
+  const int64_t rt0 = (int64_t)tr * DG_RT, ct0 = (int64_t)tc * DG_RT;
+  const int64_t nkt = (g.K + 63) / 64;
+
+  v4i acc[DG_S][2][4];
+#pragma unroll
+  for (int l = 0; l < DG_S; ++l)
+#pragma unroll
+    for (int si = 0; si < 2; ++si)
+#pragma unroll
+      for (int sj = 0; sj < 4; ++sj) acc[l][si][sj] = (v4i){0, 0, 0, 0};
+
+  fetch_step(lds[0], g.Ap, g.Bp, rt0, ct0, nkt, 0, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nkt; ++kt) {
+    const int cur = (int)(kt & 1);
+    if (kt + 1 < nkt) fetch_step(lds[cur ^ 1], g.Ap, g.Bp, rt0, ct0, nkt, kt + 1, wave, lane);
+    const v4i* Ast = reinterpret_cast<const v4i*>(lds[cur][0]);
+    const v4i* Bst = reinterpret_cast<const v4i*>(lds[cur][DG_RT * DG_S]);
+    v4i af[2][DG_S];
+#pragma unroll
+    for (int si = 0; si < 2; ++si)
+#pragma unroll
+      for (int p = 0; p < DG_S; ++p) af[si][p] = Ast[((wm * 2 + si) * DG_S + p) * 64 + lane];
+#pragma unroll
+    for (int q = 0; q < DG_S; ++q) {
+      v4i bf[4];
+#pragma unroll
+      for (int sj = 0; sj < 4; ++sj) bf[sj] = Bst[((wn * 4 + sj) * DG_S + q) * 64 + lane];
+#pragma unroll
+      for (int p = 0; p + q < DG_S; ++p)
+#pragma unroll
+        for (int si = 0; si < 2; ++si)
+#pragma unroll
+          for (int sj = 0; sj < 4; ++sj) acc[p + q][si][sj] = mfma_i8(af[si][p], bf[sj], acc[p + q][si][sj]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's chunks of the next step have landed
+    __syncthreads();                 // everyone's have, and everyone is done with this stage
+  }
+
+  // ---- epilogue: lane (li, lg) of sub-tile (si, sj) holds rows 4 lg + v of column li
+  double val[2][4][4];
+#pragma unroll
+  for (int si = 0; si < 2; ++si)
+#pragma unroll
+    for (int sj = 0; sj < 4; ++sj)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        double x = (double)acc[DG_S - 1][si][sj][v];
+#pragma unroll
+        for (int l = DG_S - 2; l >= 0; --l) x = fma(x, 0x1p-8, (double)acc[l][si][sj][v]);
+        val[si][sj][v] = x;
+      }
+  int fe[4];
+#pragma unroll
+  for (int sj = 0; sj < 4; ++sj) {
+    const int col = col0 + wn * 64 + sj * 16 + li;
+    fe[sj] = col < g.N ? g.EB[col] : 0;
+  }
+  if constexpr (EPI == EPI_ROWSUMSQ_S || EPI == EPI_LINEAR1) {
+    double* red = reinterpret_cast<double*>(lds[0][0]);   // the operand stages are free now
+    double rs[2][4];
+#pragma unroll
+    for (int si = 0; si < 2; ++si)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = row0 + wm * 32 + si * 16 + 4 * lg + v;
+        const int ea = row < g.M ? g.EA[row] : 0;
+        double beta = 0.0, gam = 1.0;
+        if (EPI == EPI_LINEAR1 && row < g.M) {
+          beta = g.rowa[row];
+          gam = g.rowb[row];
+        }
+        double acc_r = 0.0;
+#pragma unroll
+        for (int sj = 0; sj < 4; ++sj) {
+          const int col = col0 + wn * 64 + sj * 16 + li;
+          if (row < g.M && col < g.N) {
+            const bool bad = ea == DG_EXP_NONFINITE || fe[sj] == DG_EXP_NONFINITE;
+            const double prod = bad ? __builtin_nan("") : ldexp(val[si][sj][v], ea + fe[sj] - 12);
+            const double sl = (double)g.s[col];
+            const double u = sl * prod;
+            if (EPI == EPI_ROWSUMSQ_S) {
+              acc_r = fma(u, u, acc_r);
+            } else {
+              const double den = fma(beta * sl, sl, gam);
+              g.C[(int64_t)row * g.ldc + col] = beta * sl * u / den;
+              const double e = gam * u / den;
+              acc_r = fma(e, e, acc_r);
+            }
+          }
+        }
+        acc_r += __shfl_xor(acc_r, 1, 64);
+        acc_r += __shfl_xor(acc_r, 2, 64);
+        acc_r += __shfl_xor(acc_r, 4, 64);
+        acc_r += __shfl_xor(acc_r, 8, 64);
+        rs[si][v] = acc_r;
+      }
+    if (li == 0) {
+#pragma unroll
+      for (int si = 0; si < 2; ++si)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[wn * DG_TILE + wm * 32 + si * 16 + 4 * lg + v] = rs[si][v];
+    }
+    __syncthreads();
+    if (t < DG_TILE) {
+      const int row = row0 + t;
+      if (row < g.M) g.partial[(int64_t)row * g.ldp + tc] = red[t] + red[DG_TILE + t];
+    }
+    return;
+  }
+#pragma unroll
+  for (int si = 0; si < 2; ++si)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = row0 + wm * 32 + si * 16 + 4 * lg + v;
+      if (row >= g.M) continue;
+      const int ea = g.EA[row];
+      const double coef = EPI == EPI_AXPY_W ? g.rowa[row] : 0.0;
+#pragma unroll
+      for (int sj = 0; sj < 4; ++sj) {
+        const int col = col0 + wn * 64 + sj * 16 + li;
+        if (col >= g.N) continue;
+        const bool bad = ea == DG_EXP_NONFINITE || fe[sj] == DG_EXP_NONFINITE;
+        const double prod = bad ? __builtin_nan("") : ldexp(val[si][sj][v], ea + fe[sj] - 12);
+        double* cp = g.C + (int64_t)row * g.ldc + col;
+        if (EPI == EPI_STORE)
+          *cp = prod;
+        else   // EPI_AXPY_W: r2 + coef acc with r2 = W - X
+          *cp = fma(coef, prod, (double)g.W[(int64_t)row * g.ldw + col] - g.X[(int64_t)row * g.ldx + col]);
+      }
+    }
+}
+
+hipError_t launch_digit_gemm(int epi, const DigitGemmArgs& g, hipStream_t st) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.K <= 0 || g.K > DG_MAX_K) return hipErrorInvalidValue;
+  const int T = ((g.M + DG_TILE - 1) / DG_TILE) * ((g.N + DG_TILE - 1) / DG_TILE);
+  const dim3 grid((unsigned)(8 * ((T + 7) / 8))), block(64 * DG_WAVES);
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL(digit_gemm_kernel<EPI_STORE>, grid, block, 0, st, g); break;
+    case EPI_ROWSUMSQ_S: hipLaunchKernelGGL(digit_gemm_kernel<EPI_ROWSUMSQ_S>, grid, block, 0, st, g); break;
+    case EPI_LINEAR1: hipLaunchKernelGGL(digit_gemm_kernel<EPI_LINEAR1>, grid, block, 0, st, g); break;
+    case EPI_AXPY_W: hipLaunchKernelGGL(digit_gemm_kernel<EPI_AXPY_W>, grid, block, 0, st, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mpq

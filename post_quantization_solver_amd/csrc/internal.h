@@ -55,6 +55,30 @@ hipError_t launch_mirror_lower(double* H, int64_t n, hipStream_t st);
 hipError_t launch_collect_nonzero_rows(const double* X, int64_t m, int kd, int32_t* list, int32_t* count,
                                        hipStream_t st);
 
+// The same products in float64 accuracy on the int8 matrix cores (exact
+// integer digit products, int32 sums; digitgemm.hip) for K <= DG_MAX_K.
+// Operands are split once into digit planes (launch_digit_split*), then
+// multiplied with the linear-module epilogues of launch_gemm64.
+constexpr int DG_MAX_K = 32767;
+struct DigitGemmArgs {
+  int M, N, K;
+  const uint8_t* Ap; const uint8_t* Bp;   // digit planes of A (M x K) and B (N x K)
+  const int32_t* EA; const int32_t* EB;   // their row exponents
+  double* C; int64_t ldc;
+  const float* s;
+  const double* rowa;
+  const double* rowb;
+  double* partial; int64_t ldp;
+  const double* X; int64_t ldx;
+  const float* W; int64_t ldw;
+};
+size_t digit_plane_bytes(int64_t rows, int64_t K);
+hipError_t launch_digit_split(const double* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes,
+                              hipStream_t st);
+hipError_t launch_digit_split_f32(const float* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes,
+                                  hipStream_t st);
+hipError_t launch_digit_gemm(int epi, const DigitGemmArgs& g, hipStream_t st);
+
 // ------------------------------------------------------------ codebook ----
 // Device tables of a prepared codebook (mpq_codebook_prepare).
 struct CbTables {

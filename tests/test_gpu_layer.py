@@ -77,6 +77,45 @@ def test_safeguard_eps(eps):
     assert gpu["fallbacks"].sum() > sum(r["fallbacks"] for r in base)
 
 
+def test_linear_paths_agree_and_digits_run():
+    """The int8 digit GEMM is what the default solve runs (its split kernels
+    appear in the profile), the fp64-MFMA path gives way to it only on request,
+    and both paths give the same codes and matching traces."""
+    import torch
+    import post_quantization_solver_amd as mpq
+    L = S.make_layer("paths", 48, 320, seed=38, d=1, bits=4, power=0.5, T_vamp=8)
+    T = layer_tensors(L)
+    outs = {}
+    for f64 in (False, True):
+        prof = mpq.Profile(("linear1", "linear2", "split"))
+        out = mpq.quantize_layer(T["W"], T["s"], T["V"], L.E, T["a"], T["o"], T_vamp=L.T_vamp, n_cd=L.n_cd,
+                                 damping=L.damping, profile=prof, linear_f64=f64)
+        torch.cuda.synchronize()
+        outs[f64] = ({k: host(v) for k, v in out.items() if v is not None}, prof.as_dict())
+    (dg, pd), (fp, pf) = outs[False], outs[True]
+    assert pd["split"][1] > 0 and pf["split"][1] == 0
+    assert pd["linear1"][1] == pf["linear1"][1] == L.T_vamp
+    assert np.array_equal(dg["codes"], fp["codes"])
+    # beta and gamma1 follow the products directly; gamma2 = eta1 - gamma1 is
+    # an ill-conditioned difference, held to the soft-quantity bar
+    for k, tol in (("beta_tr", 1e-6), ("gamma1_tr", 1e-6), ("gamma2_tr", SOFT_RTOL)):
+        assert np.allclose(dg[k], fp[k], rtol=tol, atol=0), k
+
+
+def test_long_rows_take_fp64_products():
+    """Rows longer than the digit GEMM's inner dimension (n > 32767) run the
+    linear module on the fp64 matrix cores and still match the oracle."""
+    L = S.make_layer("long", 3, 32776, seed=39, d=1, bits=3, power=0.5, r=24, T_vamp=3)
+    rows = np.arange(L.m)
+    gpu = run_gpu(L)
+    refs = solve_rows(L, rows)
+    summ = compare_layer(L, rows, gpu, refs)
+    print(f"[long rows] codes {summ['code_agreement']:.5f} obj {summ['obj_rel_max']:.2e}", flush=True)
+    assert summ["code_agreement"] >= CODE_FRAC and summ["obj_rel_max"] < OBJ_RTOL
+    for key, v in summ["trace_rel_max"].items():
+        assert v < SOFT_RTOL, (key, v)
+
+
 def test_special_cases():
     L = S.make_layer("sp", 12, 48, seed=31, d=1, bits=3, T_vamp=4)
     rows = np.arange(L.m)

@@ -18,6 +18,9 @@ from oracle.pool import solve_rows
 pytestmark = pytest.mark.gpu
 
 F64_RTOL = 1e-9
+# the int8 digit GEMM of the linear module keeps its products to about 1e-10
+# relative; the extrinsic update multiplies that by eta2 / gamma1' in r1'
+DIGIT_RTOL = 1e-8
 SCAN = {"lattice_shuffled"}   # generic codebook: float32 scan denoiser
 
 
@@ -116,13 +119,17 @@ def test_vamp_step(name):
     print("  worst:", {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
     assert worst["fallback"] == 0.0
     tol = SOFT_RTOL if name in SCAN else F64_RTOL
-    for key in ("xhat1", "eta1", "gamma2", "r2", "r1", "gamma1", "beta"):
+    for key in ("xhat1", "eta1", "gamma2", "r2"):
         assert worst[key] < tol, (key, worst[key])
+    for key in ("r1", "gamma1", "beta"):
+        assert worst[key] < max(tol, DIGIT_RTOL), (key, worst[key])
 
 
 @pytest.mark.parametrize("name", NAMES)
-def test_linear_step(name):
-    """The linear module + M-step alone, from the oracle's extrinsic message."""
+@pytest.mark.parametrize("linear_f64", [False, True], ids=["digit", "f64"])
+def test_linear_step(name, linear_f64):
+    """The linear module + M-step alone, from the oracle's extrinsic message,
+    on the int8 digit GEMM and on the fp64 matrix cores."""
     import post_quantization_solver_amd as mpq
     L, rows, refs = oracle_runs(name)
     T = layer_tensors(L)
@@ -133,7 +140,7 @@ def test_linear_step(name):
         g2 = dev(np.array([x["gamma2"] for x in h]))
         bt = dev(np.array([x["beta"] for x in h]))
         print(f"[linear_step] {name} t={t}", flush=True)
-        R1, g1 = mpq.linear_step(R2, g2, bt, T["W"], T["s"], T["V"], damping=L.damping)
+        R1, g1 = mpq.linear_step(R2, g2, bt, T["W"], T["s"], T["V"], damping=L.damping, linear_f64=linear_f64)
         r1n, g1n, btn = host(R1), host(g1), host(bt)
         for k in range(len(rows)):
             nxt = refs[k]["history"][t + 1] if t + 1 < L.T_vamp else None
@@ -144,7 +151,7 @@ def test_linear_step(name):
                 worst[key] = max(worst.get(key, 0.0), v)
     print("  worst:", {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
     for key, v in worst.items():
-        assert v < F64_RTOL, (key, v)
+        assert v < (F64_RTOL if linear_f64 else DIGIT_RTOL), (key, v)
 
 
 @pytest.mark.parametrize("name", NAMES)
