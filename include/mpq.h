@@ -254,6 +254,29 @@ int mpq_quantize_layer(const float* W, int64_t m, int64_t n,
                        int32_t* cd_changes, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * mpq_quantize_layer for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same solve, arguments and outputs, with no workspace
+ * argument.  Its workspace is a library-owned static device array of
+ * MPQ_STATIC_WORKSPACE_BYTES per GPU (allocated when the library is loaded
+ * on that GPU, held until the process ends), so it serves layers with
+ * mpq_workspace_bytes(m, n, r, K, d) <= MPQ_STATIC_WORKSPACE_BYTES (for
+ * example 256 x 512 scalar or 128 x 512 E8 layers); larger ones return
+ * MPQ_EWORKSPACE.  The call allocates nothing and never waits:
+ * MPQ_F_PROFILE and MPQ_F_CHECK_FINITE return MPQ_EUNSUPPORTED.  All calls
+ * on one GPU share its array and leave their data in it; calls that overlap
+ * on one GPU (another stream, another thread) race and must be ordered by
+ * the caller.
+ */
+#define MPQ_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+int mpq_quantize_layer_static(const float* W, int64_t m, int64_t n,
+                              const float* s, const float* V, int64_t r,
+                              const mpq_codebook* cb, const float* row_scale, const float* row_offset,
+                              int T_vamp, int n_cd, float damping, const mpq_options* opt,
+                              int32_t* codes, float* beta_tr, float* gamma1_tr, float* gamma2_tr,
+                              int32_t* cd_changes, void* stream);
+
+/*
  * Step-level entry points.  They expose each stage of the solve on caller
  * state so that a single stage can be compared with the oracle on the
  * oracle's own inputs.  State vectors are float64 device buffers.

@@ -25,7 +25,8 @@ STATUS = {
 }
 
 EXPORTS = ("mpq_workspace_bytes", "mpq_strerror", "mpq_codebook_bytes", "mpq_codebook_prepare",
-           "mpq_profiler_create", "mpq_profiler_destroy", "mpq_quantize_layer", "mpq_prologue", "mpq_denoise",
+           "mpq_profiler_create", "mpq_profiler_destroy", "mpq_quantize_layer", "mpq_quantize_layer_static",
+           "mpq_prologue", "mpq_denoise",
            "mpq_vamp_step", "mpq_linear_step", "mpq_map", "mpq_cd", "mpq_objective", "mpq_greedy",
            "mpq_greedy_workspace_bytes", "mpq_gram_workspace_bytes", "mpq_gram", "mpq_rht",
            "mpq_factor_workspace_bytes", "mpq_factor", "mpq_codebook_kind", "mpq_hip_error_name",
@@ -174,6 +175,7 @@ def load_library(path: str = LIB_PATH):
     lib.mpq_profiler_destroy.argtypes = [P]
     lib.mpq_profiler_destroy.restype = None
     lib.mpq_quantize_layer.argtypes = [P, I64, I64, P, P, I64, CB, P, P, I, I, F, OPT, P, P, P, P, P, P, SZ, P]
+    lib.mpq_quantize_layer_static.argtypes = [P, I64, I64, P, P, I64, CB, P, P, I, I, F, OPT, P, P, P, P, P, P]
     lib.mpq_prologue.argtypes = [P, I64, I64, P, P, I64, CB, P, P, OPT, P, P, P, P, SZ, P]
     lib.mpq_denoise.argtypes = [P, P, I64, I64, CB, P, P, OPT, P, P, P, SZ, P]
     lib.mpq_vamp_step.argtypes = [P, P, P, P, I64, I64, P, P, I64, CB, P, P, F, OPT, P, P, P, P, P, P, SZ, P]
@@ -396,6 +398,42 @@ def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, dampin
     if diagnostics:
         out.update(map_codes=mc, objective=obj, fallbacks=fb, sweeps=sw)
     return out
+
+
+STATIC_WORKSPACE_BYTES = 64 << 20   # MPQ_STATIC_WORKSPACE_BYTES
+
+
+def quantize_layer_static(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, damping=0.5, beta0=None,
+                          group=None, outputs=None):
+    """mpq_quantize_layer_static: the full solve in the library's static
+    per-GPU workspace (no workspace argument; layers whose workspace exceeds
+    STATIC_WORKSPACE_BYTES raise MPQ_EWORKSPACE).  `outputs` (a dict from a
+    previous call of the same shape) reuses its output tensors.  Returns the
+    dict of quantize_layer (codes and traces)."""
+    import torch
+    m, n = W.shape
+    r = s.shape[0]
+    P = prepare_codebook(cb, W.device)
+    d = P.d
+    dev = W.device
+    _dev(W, torch.float32, "W")
+    _dev(s, torch.float32, "s", (r,))
+    _dev(V, torch.float32, "V", (n, r))
+    _affine(row_scale, row_offset, m, n, group)
+    if outputs is not None:
+        codes, bt, g1, g2, ch = (outputs[k] for k in ("codes", "beta_tr", "gamma1_tr", "gamma2_tr", "cd_changes"))
+    else:
+        codes = torch.empty((m, n // d), dtype=torch.int32, device=dev)
+        bt = torch.empty((m, T_vamp + 1), dtype=torch.float32, device=dev)
+        g1 = torch.empty((m, T_vamp + 1), dtype=torch.float32, device=dev)
+        g2 = torch.empty((m, T_vamp), dtype=torch.float32, device=dev) if T_vamp > 0 else None
+        ch = torch.zeros((m, n_cd), dtype=torch.int32, device=dev) if n_cd > 0 else None
+    op, _keep = _opts(beta0, group=group)
+    rc = load_library().mpq_quantize_layer_static(
+        _ptr(W), m, n, _ptr(s), _ptr(V), r, P.ref(), _ptr(row_scale), _ptr(row_offset), int(T_vamp), int(n_cd),
+        float(damping), op, _ptr(codes), _ptr(bt), _ptr(g1), _ptr(g2), _ptr(ch), _stream())
+    _check(rc, "mpq_quantize_layer_static")
+    return dict(codes=codes, beta_tr=bt, gamma1_tr=g1, gamma2_tr=g2, cd_changes=ch)
 
 
 def prologue(W, s, V, cb, row_scale, row_offset, beta0=None, workspace=None, group=None, linear_f64=False):

@@ -10,6 +10,7 @@
 #include <math.h>
 #include <string.h>
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -964,6 +965,33 @@ int begin(Ctx& c, int64_t m, int64_t n, int64_t r, const mpq_codebook* cb, void*
 
 bool check_finite_requested(const mpq_options* opt) { return opt && (opt->flags & MPQ_F_CHECK_FINITE); }
 
+// Workspace of mpq_quantize_layer_static: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel or copy (in host code it only names a host-side stand-in):
+// its device address is looked up once per device with hipGetSymbolAddress,
+// with that device current, and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[MPQ_STATIC_WORKSPACE_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's copy of `scratch` (looked up at the first call on it).
+int static_workspace(void** out) {
+  int dev = -1;
+  MPQ_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES) return MPQ_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    MPQ_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || (reinterpret_cast<uintptr_t>(p) % ALIGN) != 0) return MPQ_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MPQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1106,6 +1134,30 @@ int mpq_quantize_layer(const float* W, int64_t m, int64_t n, const float* s, con
     if (check_finite_requested(opt) && (rc = check_inputs(c, W, s, V, row_scale, row_offset))) return rc;
     return finish(c, solve_layer(c, W, s, V, row_scale, row_offset, T_vamp, n_cd, (double)damping, opt, codes,
                                  beta_tr, gamma1_tr, gamma2_tr, cd_changes));
+  });
+}
+
+int mpq_quantize_layer_static(const float* W, int64_t m, int64_t n, const float* s, const float* V, int64_t r,
+                              const mpq_codebook* cb, const float* row_scale, const float* row_offset, int T_vamp,
+                              int n_cd, float damping, const mpq_options* opt, int32_t* codes, float* beta_tr,
+                              float* gamma1_tr, float* gamma2_tr, int32_t* cd_changes, void* stream) {
+  return guarded([&]() -> int {
+    if (T_vamp < 0 || n_cd < 0 || !(damping > 0.f && damping <= 1.f)) return MPQ_EPARAM;
+    // nothing that waits for the stream: no profiling, no finiteness verdict
+    if (opt && (opt->flags & (MPQ_F_PROFILE | MPQ_F_CHECK_FINITE))) return MPQ_EUNSUPPORTED;
+    int rc = check_prepared(cb);
+    if (rc) return rc;
+    if ((rc = check_shapes(m, n, r, cb->K, cb->d))) return rc;
+    if (m == 0) return MPQ_OK;
+    if (make_layout(m, n, r, cb->K, cb->d).total > MPQ_STATIC_WORKSPACE_BYTES) return MPQ_EWORKSPACE;
+    void* ws = nullptr;
+    if ((rc = static_workspace(&ws))) return rc;
+    Ctx c;
+    rc = begin(c, m, n, r, cb, ws, MPQ_STATIC_WORKSPACE_BYTES, stream, opt);
+    if (rc) return rc;
+    if (!W || !s || !V || !row_scale || !row_offset || !codes) return MPQ_ENULL;
+    return solve_layer(c, W, s, V, row_scale, row_offset, T_vamp, n_cd, (double)damping, opt, codes, beta_tr,
+                       gamma1_tr, gamma2_tr, cd_changes);
   });
 }
 
