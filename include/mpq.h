@@ -54,8 +54,9 @@ extern "C" {
 #define MPQ_EPARAM          -3   /* T_vamp < 0, n_cd < 0, damping not in (0, 1], group < 0,
                                     safeguard_eps < 0, a non-finite codebook entry, or a
                                     mpq_codebook that mpq_codebook_prepare did not fill */
-#define MPQ_EUNSUPPORTED    -4   /* d not in {1, 8}, a d = 8 codebook not exact in bfloat16, or
-                                    column groups with d = 8 or the anchored prior */
+#define MPQ_EUNSUPPORTED    -4   /* d not in {1, 8}, a d = 8 codebook not exact in bfloat16,
+                                    column groups with d = 8 or the anchored prior, a log-prior
+                                    with d = 8, or an option an entry point does not take */
 #define MPQ_EWORKSPACE      -5   /* workspace (or codebook table buffer) NULL, misaligned or too small */
 #define MPQ_EHIP            -6   /* a HIP runtime call failed (mpq_hip_error_name names it) */
 #define MPQ_ESOLVER         -7   /* mpq_factor: rocSOLVER not loadable, or its eigensolver failed */
@@ -162,6 +163,12 @@ typedef struct {
                              for mpq_vamp_step, mpq_denoise and mpq_map
                              (mpq_quantize_layer anchors at its W; mpq_cd has no
                              prior) */
+  const float* log_prior; /* device, K floats: log rho(c) of every base codeword, the
+                             prior of key design 1's block posterior
+                             q_b(c) ~ rho(c) exp(-gamma1/2 ||c - r1_b||^2), used by the
+                             denoiser and the marginal MAP (CD minimises the objective
+                             alone); NULL: uniform.  Scalar grids (d = 1) only, else
+                             MPQ_EUNSUPPORTED */
   int64_t group;          /* > 0: group-wise scalar grids (the hyper-parameter
                              paragraph's scalar runs use groups of 128): each run of
                              g = group consecutive columns of a row has its own

@@ -287,7 +287,7 @@ def vamp_init(w, s, V, C, d):
 
 
 def vamp(w, s, V, C, d, T_vamp, damping, a_scale, beta0=None, denoiser=None,
-         fixed_beta=False, record=False, anchor_tau=None, safeguard_eps=0.0):
+         fixed_beta=False, record=False, anchor_tau=None, safeguard_eps=0.0, log_prior=None):
     """T_vamp iterations of rank-space VAMP with the beta M-step.
 
     `denoiser(r1, gamma1) -> (x_hat1, v_blocks)` defaults to the discrete
@@ -303,7 +303,7 @@ def vamp(w, s, V, C, d, T_vamp, damping, a_scale, beta0=None, denoiser=None,
         beta = float(beta0)
     if denoiser is None:
         anchor = (w, anchor_lambda(anchor_tau, a_scale))
-        denoiser = lambda r, g: denoise(r, g, C, d, anchor=anchor)[:2]  # noqa: E731
+        denoiser = lambda r, g: denoise(r, g, C, d, log_prior=log_prior, anchor=anchor)[:2]  # noqa: E731
     r1 = w.copy()
     tr_beta, tr_g1, tr_g2, tr_eta1 = [beta], [gamma1], [], []
     hist = []
@@ -469,11 +469,14 @@ def codes_objective(w, codes, C, d, s, V):
 # ----------------------------------------------------------------------------
 
 def solve_row(w, s, V, E, a, o, d, T_vamp, n_cd, damping, beta0=None, record=False, anchor_tau=None, group=0,
-              safeguard_eps=0.0):
+              safeguard_eps=0.0, log_prior=None):
     """MPQ on one row: VAMP (T_vamp iterations) -> marginal MAP -> block CD.
     anchor_tau: the anchored prior of reading A1 (None: uniform prior).
     group > 0: group-wise grids of reading A2 (a, o hold one value per group).
     safeguard_eps: the pass-through threshold of reading R2 (0: R2 itself).
+    log_prior: log rho(c), one value per base codeword (key design 1's prior
+    of the block posterior; None: uniform), used by the denoiser and the
+    marginal MAP; CD minimises the objective alone.
 
     Returns dict(codes, objective, beta_tr, gamma1_tr, gamma2_tr, eta1_tr,
     cd_changes, fallbacks, map_codes, rtn_codes, frozen[, history]).
@@ -495,8 +498,8 @@ def solve_row(w, s, V, E, a, o, d, T_vamp, n_cd, damping, beta0=None, record=Fal
                     eta1_tr=np.full(T_vamp, inf), cd_changes=[0] * n_cd, fallbacks=0,
                     map_codes=rtn, rtn_codes=rtn, frozen=True, history=[])
     st = vamp(w, s, V, C, d, T_vamp, damping, a, beta0=beta0, record=record, anchor_tau=anchor_tau,
-              safeguard_eps=safeguard_eps)
-    mc = map_codes(st["r1"], st["gamma1"], C, d, anchor=(w, anchor_lambda(anchor_tau, a)))
+              safeguard_eps=safeguard_eps, log_prior=log_prior)
+    mc = map_codes(st["r1"], st["gamma1"], C, d, log_prior=log_prior, anchor=(w, anchor_lambda(anchor_tau, a)))
     codes, changes = block_cd(mc, w, s, V, C, d, n_cd)
     changes = list(changes) + [0] * (n_cd - len(changes))
     out = dict(codes=codes, objective=codes_objective(w, codes, C, d, s, V),

@@ -60,7 +60,7 @@ def _solve(job):
     if _ROOT not in sys.path:
         sys.path.insert(0, _ROOT)
     from oracle import mpq_oracle as O
-    path, i, d, T, S, rho, record, tau, group, eps = job
+    path, i, d, T, S, rho, record, tau, group, eps, lp = job
     A = _load(path)
     w = np.asarray(A["W"][i], np.float64)
     if group:
@@ -70,7 +70,7 @@ def _solve(job):
         a, o = float(A["a"][i]), float(A["o"][i])
         C = O.row_codewords(A["E"], a, o)
     res = O.solve_row(w, A["s"], A["V"], A["E"], a, o, d, T, S, rho, record=record, anchor_tau=tau, group=group,
-                      safeguard_eps=eps)
+                      safeguard_eps=eps, log_prior=lp)
     res["map_objective"] = O.codes_objective(w, res["map_codes"], C, d, A["s"], A["V"])
     res["rtn_objective"] = O.codes_objective(w, res["rtn_codes"], C, d, A["s"], A["V"])
     res["row"] = int(i)
@@ -104,15 +104,18 @@ def _run(L, fn, make_jobs, max_workers):
         shutil.rmtree(tmp, ignore_errors=True)
 
 
-def solve_rows(L, rows, T_vamp=None, n_cd=None, record=False, max_workers=None, anchor_tau=None, safeguard_eps=0.0):
+def solve_rows(L, rows, T_vamp=None, n_cd=None, record=False, max_workers=None, anchor_tau=None, safeguard_eps=0.0,
+               log_prior=None):
     """Oracle results for the given rows of a layer (attributes W, s, V, E, a,
     o, d, T_vamp, n_cd, damping), in row order; anchor_tau: the anchored prior;
-    safeguard_eps: the pass-through threshold."""
+    safeguard_eps: the pass-through threshold; log_prior: one log-prior value
+    per base codeword."""
     T = L.T_vamp if T_vamp is None else T_vamp
     S = L.n_cd if n_cd is None else n_cd
     rows = [int(i) for i in rows]
     group = getattr(L, "group", 0)
-    return _run(L, _solve, lambda tmp: [(tmp, i, L.d, T, S, L.damping, record, anchor_tau, group, safeguard_eps)
+    lp = None if log_prior is None else np.asarray(log_prior, np.float64)
+    return _run(L, _solve, lambda tmp: [(tmp, i, L.d, T, S, L.damping, record, anchor_tau, group, safeguard_eps, lp)
                                         for i in rows], max_workers)
 
 

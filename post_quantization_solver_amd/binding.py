@@ -65,7 +65,8 @@ class Codebook(ctypes.Structure):
 
 class Options(ctypes.Structure):
     _fields_ = [("beta0", ctypes.c_float), ("flags", ctypes.c_uint32), ("safeguard_eps", ctypes.c_float),
-                ("anchor_tau", ctypes.c_float), ("anchor_w", ctypes.c_void_p), ("group", ctypes.c_int64),
+                ("anchor_tau", ctypes.c_float), ("anchor_w", ctypes.c_void_p), ("log_prior", ctypes.c_void_p),
+                ("group", ctypes.c_int64),
                 ("profiler", ctypes.c_void_p), ("prof_mask", ctypes.c_uint32),
                 ("prof_ms", ctypes.POINTER(ctypes.c_double)), ("prof_launches", ctypes.POINTER(ctypes.c_int64)),
                 ("map_codes", ctypes.c_void_p), ("objective", ctypes.c_void_p), ("fallbacks", ctypes.c_void_p),
@@ -305,7 +306,7 @@ def _workspace(m, n, r, K, d, device):
 
 def _opts(beta0=None, fixed_beta=False, profile=None, anchor_tau=None, anchor_w=None, group=None, map_codes=None,
           objective=None, scan_denoiser=False, e8_decode=True, safeguard_eps=0.0, fallbacks=None, sweeps=None,
-          check_finite=False, linear_f64=False):
+          check_finite=False, linear_f64=False, log_prior=None):
     flags = ((F_FIXED_BETA if fixed_beta else 0) | (F_PROFILE if profile is not None else 0) |
              (F_PROFILE_SAMPLED if profile is not None and profile.sampled else 0) |
              (F_NO_E8DP if scan_denoiser else 0) | (0 if e8_decode else F_NO_E8_DECODE) |
@@ -317,6 +318,7 @@ def _opts(beta0=None, fixed_beta=False, profile=None, anchor_tau=None, anchor_w=
     o.anchor_tau = float(anchor_tau) if anchor_tau else 0.0
     o.anchor_w = anchor_w.data_ptr() if anchor_w is not None else None
     o.group = int(group) if group else 0
+    o.log_prior = log_prior.data_ptr() if log_prior is not None else None
     if profile is not None:
         o.profiler = profile.handle
         o.prof_mask = profile.mask
@@ -350,7 +352,7 @@ def _check(rc, what):
 def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, damping=0.5, beta0=None,
                    fixed_beta=False, workspace=None, traces=True, profile=None, outputs=None, anchor_tau=None,
                    group=None, diagnostics=False, scan_denoiser=False, safeguard_eps=0.0, check_finite=False,
-                   linear_f64=False):
+                   linear_f64=False, log_prior=None):
     """Full MPQ solve of one layer (mpq_quantize_layer).
 
     `cb`: a PreparedCodebook (prepare_codebook) or a raw K x d codebook.
@@ -358,6 +360,7 @@ def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, dampin
     tensors.  `profile` (a Profile) turns on the library's event timing;
     `outputs` (a dict from a previous call) reuses its output tensors;
     `anchor_tau` > 0 selects the anchored codebook prior (None: uniform);
+    `log_prior` (device float32, K) is log rho of every base codeword (d = 1);
     `group` > 0 gives every `group` consecutive columns their own affine
     (row_scale and row_offset then m x ceil(n / group)); `diagnostics` adds
     map_codes (the marginal-MAP codes CD starts from), objective (float64,
@@ -389,7 +392,7 @@ def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, dampin
     sw = torch.empty(m, dtype=torch.int32, device=dev) if diagnostics else None
     op, _keep = _opts(beta0, fixed_beta, profile, anchor_tau, None, group, mc, obj, scan_denoiser,
                       safeguard_eps=safeguard_eps, fallbacks=fb, sweeps=sw, check_finite=check_finite,
-                      linear_f64=linear_f64)
+                      linear_f64=linear_f64, log_prior=log_prior)
     rc = load_library().mpq_quantize_layer(
         _ptr(W), m, n, _ptr(s), _ptr(V), r, P.ref(), _ptr(row_scale), _ptr(row_offset), int(T_vamp), int(n_cd),
         float(damping), op, _ptr(codes), _ptr(bt), _ptr(g1), _ptr(g2), _ptr(ch), _ptr(ws), ws.numel(), _stream())

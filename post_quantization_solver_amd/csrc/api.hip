@@ -384,6 +384,8 @@ struct Ctx {
   bool anchored() const { return anchor_tau > 0.0; }
   // pass-through rule threshold (mpq_options.safeguard_eps)
   double eps = 0.0;
+  // log-prior per base codeword (mpq_options.log_prior; d = 1), nullptr: uniform
+  const float* log_prior = nullptr;
   int32_t* fb_count = nullptr;   // optional per-row pass-through counts
   // E8-prefix nearest codeword: the lattice decoder first, the automaton for
   // the blocks it cannot settle (else the automaton for every block)
@@ -431,10 +433,18 @@ hipError_t nearest_d(const Ctx& c, const double* R, int32_t* codes, const float*
   return launch_nearest_lattice<double>(R, c.L.m, c.L.n, c.cb, a, o, codes, c.st);
 }
 
+// Marginal MAP at (R, gamma): the nearest codeword, or under a log-prior the
+// argmax of log rho - gamma/2 ||c - r||^2.
+hipError_t map_d(const Ctx& c, const double* R, const double* gamma, int32_t* codes, const float* a, const float* o) {
+  if (c.log_prior) return launch_map_scalar_prior(R, gamma, c.L.m, c.L.n, c.cb, a, o, c.log_prior, codes, c.st);
+  return nearest_d(c, R, codes, a, o);
+}
+
 int denoise(Ctx& c, const double* R1, const double* gamma1, const float* a, const float* o, double* xhat,
             double* vblk) {
   if (c.L.d == 1) {
-    TIMED(c, MPQ_PROF_DENOISE, launch_denoise_scalar(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, xhat, vblk, c.st));
+    TIMED(c, MPQ_PROF_DENOISE,
+          launch_denoise_scalar(R1, gamma1, c.L.m, c.L.n, c.cb, a, o, c.log_prior, xhat, vblk, c.st));
     return MPQ_OK;
   }
   if (c.e8dp) {
@@ -890,12 +900,14 @@ int solve_layer(Ctx& c, const float* W, const float* s, const float* V, const fl
   // marginal MAP at (r1^T, gamma1^T); frozen rows keep r1 = w, i.e. their RTN
   // codes.  With the anchored prior the argmax is the codeword nearest r_eff.
   const double* Rm = R1;
+  const double* gm = c.gamma1();
   if (c.anchored()) {
     TIMED(c, MPQ_PROF_MAP, launch_anchor(R1, W, c.gamma1(), row_scale, c.anchor_tau, L.m, L.n, c.d(R_ANCH),
                                          c.gamma_anchor(), c.st));
     Rm = c.d(R_ANCH);
+    gm = c.gamma_anchor();
   }
-  TIMED(c, MPQ_PROF_MAP, nearest_d(c, Rm, codes, row_scale, row_offset));
+  TIMED(c, MPQ_PROF_MAP, map_d(c, Rm, gm, codes, row_scale, row_offset));
   if (opt && opt->map_codes) TIMED(c, MPQ_PROF_OTHER, launch_copy_i32(codes, opt->map_codes, L.m * L.B, c.st));
   rc = run_cd(c, W, row_scale, row_offset, n_cd, codes, cd_changes, opt ? opt->sweeps : nullptr);
   if (rc) return rc;
@@ -927,6 +939,10 @@ int begin(Ctx& c, int64_t m, int64_t n, int64_t r, const mpq_codebook* cb, void*
   if (opt) {
     if (!(opt->safeguard_eps >= 0.f) || !std::isfinite(opt->safeguard_eps)) return MPQ_EPARAM;
     c.eps = (double)opt->safeguard_eps;
+    if (opt->log_prior) {
+      if (cb->d != 1) return MPQ_EUNSUPPORTED;
+      c.log_prior = opt->log_prior;
+    }
   }
   c.e8_decode = !(opt && (opt->flags & MPQ_F_NO_E8_DECODE));
   c.digits = digits_fit(n, r) && !(opt && (opt->flags & MPQ_F_LINEAR_F64));
@@ -1255,12 +1271,14 @@ int mpq_map(const double* R1, const double* gamma1, int64_t m, int64_t n, const 
     if (!R1 || !gamma1 || !row_scale || !row_offset || !codes) return MPQ_ENULL;
     if (c.anchored() && !c.anchor_w) return MPQ_ENULL;
     const double* Rm = R1;
+    const double* gm = gamma1;
     if (c.anchored()) {
       TIMED(c, MPQ_PROF_MAP, launch_anchor(R1, c.anchor_w, gamma1, row_scale, c.anchor_tau, m, n, c.d(R_ANCH),
                                            c.gamma_anchor(), c.st));
       Rm = c.d(R_ANCH);
+      gm = c.gamma_anchor();
     }
-    TIMED(c, MPQ_PROF_MAP, nearest_d(c, Rm, codes, row_scale, row_offset));
+    TIMED(c, MPQ_PROF_MAP, map_d(c, Rm, gm, codes, row_scale, row_offset));
     return finish(c, MPQ_OK);
   });
 }

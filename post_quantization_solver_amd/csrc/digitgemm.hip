@@ -86,48 +86,75 @@ __global__ __launch_bounds__(256) void digit_exp_kernel(const T* __restrict__ X,
   }
 }
 
-// The digit planes, one wave per 16-row x 64-k chunk position: lane (i, g)
-// splits X[row i][k = 16 g .. 16 g + 15] (zero outside the matrix) and writes
-// its 16 bytes of each of the five planes.
+// Digits of one value (five int8, top first) given its row exponent e.
+__device__ __forceinline__ void digits5(double v, int e, int (&d)[DG_S]) {
+  long long N = llrint(ldexp(v, 38 - e));   // |N| <= 2^38
+#pragma unroll
+  for (int p = DG_S - 1; p >= 1; --p) {
+    const int r = (int)(N & 255);
+    d[p] = r >= 128 ? r - 256 : r;
+    N = (N - d[p]) >> 8;
+  }
+  d[0] = (int)N;   // in [-64, 64]
+}
+
+// The digit planes, one wave per 16-row x 64-k chunk position.  The wave
+// reads its chunk row by row (two rows of 64 values per instruction, lanes on
+// consecutive elements) into LDS, then lane (i, g) takes row i, k = 16 g ..
+// 16 g + 15 from there (zero outside the matrix), splits them and writes its
+// 16 bytes of each of the five planes (1 KB contiguous per plane and wave).
+constexpr int DG_SPLIT_PITCH = 65;   // doubles per LDS row (one of padding)
 template <typename T>
 __global__ __launch_bounds__(256) void digit_split_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t ld,
                                                           const int32_t* __restrict__ E, int64_t nrt, int64_t nkt,
                                                           uint8_t* __restrict__ planes) {
+  __shared__ double tile[4][16 * DG_SPLIT_PITCH];
   const int lane = threadIdx.x & 63;
-  const int64_t pos = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // chunk position = rt * nkt + kt
-  if (pos >= nrt * nkt) return;
+  const int w = threadIdx.x >> 6;
+  const int64_t pos = (int64_t)blockIdx.x * 4 + w;   // chunk position = rt * nkt + kt
+  if (pos >= nrt * nkt) return;                       // uniform per wave; no block-wide barrier below
   const int64_t rt = pos / nkt, kt = pos - rt * nkt;
+  double* tl = tile[w];
+  // coalesced loads: lanes 0..31 take one row, 32..63 the next, two consecutive values each
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int rl = 2 * q + (lane >> 5);
+    const int64_t row = rt * 16 + rl;
+    const int c0 = 2 * (lane & 31);
+    const int64_t k = kt * 64 + c0;
+    double v0 = 0.0, v1 = 0.0;
+    if (row < rows) {
+      const T* src = X + row * ld + k;
+      if (k < K) v0 = (double)src[0];
+      if (k + 1 < K) v1 = (double)src[1];
+    }
+    tl[rl * DG_SPLIT_PITCH + c0] = v0;
+    tl[rl * DG_SPLIT_PITCH + c0 + 1] = v1;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int i = lane & 15, g = lane >> 4;
   const int64_t row = rt * 16 + i;
-  const int64_t k0 = kt * 64 + 16 * g;
-  const bool live = row < rows;
-  const int e = live ? E[row] : 0;
-  const bool ok = live && e != DG_EXP_NONFINITE;
-  uint32_t w[DG_S][4];
+  const int e = row < rows ? E[row] : 0;
+  const bool ok = row < rows && e != DG_EXP_NONFINITE;
+  uint32_t wd[DG_S][4];
 #pragma unroll
   for (int p = 0; p < DG_S; ++p)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) w[p][q] = 0u;
+    for (int q = 0; q < 4; ++q) wd[p][q] = 0u;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
-    const int64_t k = k0 + t;
-    const double v = ok && k < K ? (double)X[row * ld + k] : 0.0;
-    long long N = llrint(ldexp(v, 38 - e));   // |N| <= 2^38
+    const double v = ok ? tl[i * DG_SPLIT_PITCH + 16 * g + t] : 0.0;
     int d[DG_S];
+    digits5(v, e, d);
 #pragma unroll
-    for (int p = DG_S - 1; p >= 1; --p) {
-      const int r = (int)(N & 255);
-      d[p] = r >= 128 ? r - 256 : r;
-      N = (N - d[p]) >> 8;
-    }
-    d[0] = (int)N;   // in [-64, 64]
-#pragma unroll
-    for (int p = 0; p < DG_S; ++p) w[p][t >> 2] |= ((uint32_t)d[p] & 255u) << (8 * (t & 3));
+    for (int p = 0; p < DG_S; ++p) wd[p][t >> 2] |= ((uint32_t)d[p] & 255u) << (8 * (t & 3));
   }
 #pragma unroll
   for (int p = 0; p < DG_S; ++p) {
     uint4* dst = reinterpret_cast<uint4*>(planes + ((size_t)pos * DG_S + p) * DG_CHUNK) + lane;
-    *dst = make_uint4(w[p][0], w[p][1], w[p][2], w[p][3]);
+    *dst = make_uint4(wd[p][0], wd[p][1], wd[p][2], wd[p][3]);
   }
 }
 

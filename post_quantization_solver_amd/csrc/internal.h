@@ -143,8 +143,12 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int64_t count, hipS
 hipError_t launch_half_sumsq64(const double* U, const float* s, int64_t m, int64_t r, double* f, hipStream_t st);
 
 // Denoisers and nearest codeword.  TR: float (the weights) or double (VAMP state).
+// lp: log-prior per base level (nullptr: uniform).
 hipError_t launch_denoise_scalar(const double* R1, const double* gamma1, int64_t m, int64_t n, const CbTables& cb,
-                                 const float* a, const float* o, double* xhat, double* vblk, hipStream_t st);
+                                 const float* a, const float* o, const float* lp, double* xhat, double* vblk,
+                                 hipStream_t st);
+hipError_t launch_map_scalar_prior(const double* R, const double* gamma, int64_t m, int64_t n, const CbTables& cb,
+                                   const float* a, const float* o, const float* lp, int32_t* codes, hipStream_t st);
 template <typename TR>
 hipError_t launch_nearest_scalar(const TR* R, int64_t m, int64_t n, const CbTables& cb, const float* a,
                                  const float* o, int32_t* codes, hipStream_t st);

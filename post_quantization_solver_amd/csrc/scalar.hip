@@ -12,18 +12,24 @@ namespace mpq {
 constexpr int MAXK_SCALAR = 64;
 
 // Denoiser for one weight (key design 1, d = 1), float64:
-//   q(c_k) ~ exp(-gamma/2 (c_k - r)^2),  c_k = a e_k + o.
-// Logits are taken relative to the nearest level c*, in the product form
+//   q(c_k) ~ rho_k exp(-gamma/2 (c_k - r)^2),  c_k = a e_k + o,
+// with log rho_k = lp[k] (nullptr: uniform prior).  Logits are taken relative
+// to the nearest level c*, in the product form
 //   -gamma/2 [(c_k - r)^2 - (c* - r)^2] = -gamma/2 (c_k - c*)(c_k + c* - 2 r),
-// which stays accurate when gamma is large; moments are centred at c*.
+// which stays accurate when gamma is large, plus lp[k], then shifted by their
+// maximum (0 under the uniform prior); moments are centred at c*.
 __global__ __launch_bounds__(256) void denoise_scalar_kernel(const double* __restrict__ R1,
                                                              const double* __restrict__ gamma1, int64_t m, int64_t n,
                                                              const float* __restrict__ levels, int K,
                                                              const float* __restrict__ a, const float* __restrict__ o,
-                                                             int gs, int G, double* __restrict__ xhat,
-                                                             double* __restrict__ vblk) {
+                                                             int gs, int G, const float* __restrict__ lp,
+                                                             double* __restrict__ xhat, double* __restrict__ vblk) {
   __shared__ float lv[MAXK_SCALAR];
-  if (threadIdx.x < K) lv[threadIdx.x] = levels[threadIdx.x];
+  __shared__ float lps[MAXK_SCALAR];
+  if (threadIdx.x < K) {
+    lv[threadIdx.x] = levels[threadIdx.x];
+    lps[threadIdx.x] = lp ? lp[threadIdx.x] : 0.f;
+  }
   __syncthreads();
   const int64_t k0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (k0 >= m * n) return;
@@ -46,11 +52,19 @@ __global__ __launch_bounds__(256) void denoise_scalar_kernel(const double* __res
   }
   const double hg = -0.5 * g;
   const double tr = cs - 2.0 * r;
+  double shift = 0.0;
+  if (lp) {
+    shift = -INFINITY;
+    for (int k = 0; k < K; ++k) {
+      const double c = fma(ai, (double)lv[k], oi);
+      shift = fmax(shift, fma(hg * (c - cs), c + tr, (double)lps[k]));
+    }
+  }
   double m0 = 0.0, m1 = 0.0, m2 = 0.0;
   for (int k = 0; k < K; ++k) {
     const double c = fma(ai, (double)lv[k], oi);
     const double dc = c - cs;
-    const double p = exp(hg * dc * (c + tr));
+    const double p = exp(fma(hg * dc, c + tr, (double)lps[k]) - shift);
     m0 += p;
     m1 = fma(p, dc, m1);
     m2 = fma(p * dc, dc, m2);
@@ -88,10 +102,54 @@ __global__ __launch_bounds__(256) void nearest_scalar_kernel(const TR* __restric
 }
 
 hipError_t launch_denoise_scalar(const double* R1, const double* gamma1, int64_t m, int64_t n, const CbTables& cb,
-                                 const float* a, const float* o, double* xhat, double* vblk, hipStream_t st) {
+                                 const float* a, const float* o, const float* lp, double* xhat, double* vblk,
+                                 hipStream_t st) {
   dim3 grid((unsigned)((m * n + 255) / 256));
   hipLaunchKernelGGL(denoise_scalar_kernel, grid, dim3(256), 0, st, R1, gamma1, m, n, cb.levels, cb.K, a, o, cb.gs,
-                     cb.G, xhat, vblk);
+                     cb.G, lp, xhat, vblk);
+  return hipGetLastError();
+}
+
+// Marginal MAP under a log-prior (d = 1): argmax_k lp[k] - gamma/2 (c_k - r)^2
+// in float64, ties to the lowest index; rows with infinite precision (frozen)
+// take the nearest level.
+__global__ __launch_bounds__(256) void map_scalar_prior_kernel(const double* __restrict__ R,
+                                                               const double* __restrict__ gamma, int64_t m, int64_t n,
+                                                               const float* __restrict__ levels, int K,
+                                                               const float* __restrict__ a,
+                                                               const float* __restrict__ o, int gs, int G,
+                                                               const float* __restrict__ lp,
+                                                               int32_t* __restrict__ codes) {
+  __shared__ float lv[MAXK_SCALAR];
+  __shared__ float lps[MAXK_SCALAR];
+  if (threadIdx.x < K) {
+    lv[threadIdx.x] = levels[threadIdx.x];
+    lps[threadIdx.x] = lp[threadIdx.x];
+  }
+  __syncthreads();
+  const int64_t k0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k0 >= m * n) return;
+  const int64_t i = k0 / n, j = k0 - i * n;
+  const double r = R[i * n + j];
+  const double g = gamma[i];
+  const bool hard = !isfinite(g);
+  const int64_t ag = i * G + (int)j / gs;
+  const double ai = (double)a[ag], oi = (double)o[ag];
+  double best = -INFINITY;
+  int bk = 0;
+  for (int k = 0; k < K; ++k) {
+    const double dd = fma(ai, (double)lv[k], oi) - r;
+    const double sc = hard ? -dd * dd : fma(-0.5 * g * dd, dd, (double)lps[k]);
+    if (sc > best) { best = sc; bk = k; }
+  }
+  codes[i * n + j] = bk;
+}
+
+hipError_t launch_map_scalar_prior(const double* R, const double* gamma, int64_t m, int64_t n, const CbTables& cb,
+                                   const float* a, const float* o, const float* lp, int32_t* codes, hipStream_t st) {
+  dim3 grid((unsigned)((m * n + 255) / 256));
+  hipLaunchKernelGGL(map_scalar_prior_kernel, grid, dim3(256), 0, st, R, gamma, m, n, cb.levels, cb.K, a, o, cb.gs,
+                     cb.G, lp, codes);
   return hipGetLastError();
 }
 

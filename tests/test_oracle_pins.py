@@ -556,6 +556,29 @@ def test_r2_branch_inside_vamp():
     check_r2_in_vamp()
 
 
+def test_log_prior_pins():
+    """Key design 1's prior rho(c): a constant log-prior is the uniform prior;
+    a prior that leaves two levels the others' probability e^-200 confines the
+    posterior mean to between them and the MAP to one of them, while the
+    prologue (RTN) and CD ignore it."""
+    L = S.make_layer("lp", 4, 48, seed=17, d=1, bits=3, power=0.5, T_vamp=5)
+    i = 2
+    base = O.solve_row(L.W[i], L.s, L.V, L.E, L.a[i], L.o[i], 1, 5, 3, 0.5, record=True)
+    const = O.solve_row(L.W[i], L.s, L.V, L.E, L.a[i], L.o[i], 1, 5, 3, 0.5, record=True,
+                        log_prior=np.full(L.K, 3.7))
+    assert list(base["codes"]) == list(const["codes"])
+    assert np.allclose(base["beta_tr"], const["beta_tr"], rtol=1e-12)
+    lp = np.full(L.K, -200.0)
+    lp[[2, 5]] = 0.0
+    res = O.solve_row(L.W[i], L.s, L.V, L.E, L.a[i], L.o[i], 1, 5, 0, 0.5, record=True, log_prior=lp)
+    C = O.row_codewords(L.E, L.a[i], L.o[i])
+    lo, hi = sorted((C[2, 0], C[5, 0]))
+    for h in res["history"]:
+        assert np.all(h["xhat1"] >= lo - 1e-9) and np.all(h["xhat1"] <= hi + 1e-9)
+    assert set(np.unique(res["map_codes"])) <= {2, 5}
+    assert list(res["rtn_codes"]) == list(base["rtn_codes"])
+
+
 # ----------------------------------------------------------------------------
 # anchored prior (reading A1: hyper-parameter paragraph, tau = 0.2; tau -> inf
 # is the unanchored limit)
