@@ -252,6 +252,10 @@ def main():
                     help="CD sweeps (default: the workload's 3); 0 runs only the prologue, VAMP and MAP, e.g. for "
                          "counter passes over the VAMP kernels")
     ap.add_argument("--no-probe", action="store_true", help="skip the achievable-rate probes")
+    ap.add_argument("--host-qr", action="store_true",
+                    help="draw the orthogonal factor V with NumPy's QR on the host instead of rocSOLVER's (e.g. "
+                         "under counter collection, where rocSOLVER's QR has crashed the profiled process); "
+                         "V is then another orthogonal draw of the same distribution")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), the reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -285,7 +289,7 @@ def main():
     if args.group and S.configs._SPECS[args.config]["d"] != 1:
         print("--group applies to the scalar workloads (c1, c2, c3)", file=sys.stderr)
         sys.exit(2)
-    L = load_or_make(S, args.config, dev, args.cache, args.group)
+    L = load_or_make(S, args.config, None if args.host_qr else dev, args.cache, args.group)
     if args.n_cd is not None:
         L.n_cd = args.n_cd
     log(f"[bench] {args.config}: m={L.m} n={L.n} r={L.r} K={L.K} d={L.d} T={L.T_vamp} S={L.n_cd} "

@@ -9,12 +9,19 @@
 //     score(e) = a^2 t(e) - e . q,   t(e) = e^T G e / 2,   q = a (a G e_x + g_b).
 // cd_score_kernel evaluates score(e) for every codeword with one bf16 MFMA per
 // 16 x 16 (codeword x row) tile -- key slots [e | e | e | t terms], query
-// slots [-q hi | -q mid | -q lo | a^2 terms], all products exact -- and keeps
-// the per-row argmin (ties: lowest index) of its codeword slice.
-// cd_update_kernel merges the slices' two best candidates in order,
-// re-evaluates dF of both finalists exactly in float64 (the tile gradient,
-// H and the residual are float64) and moves the block only on a strict
-// decrease.
+// slots [-q hi | -q mid | -q lo | a^2 terms], all products exact, the sums
+// in float32 -- and reports two candidates per (row, codeword slice): the
+// slice's least tagged score (the float32 score with its 3 low mantissa bits
+// replaced by the codeword's position in a group of 8, so ranks can move by
+// up to 7 ulp) and the least of the other three lane-bests of that row (a
+// near-best codeword, not necessarily the slice's second-smallest score).  cd_update_kernel takes the top two of all
+// slices' candidates by (float32 score, index), re-evaluates dF of both
+// finalists exactly in float64 (the tile gradient, H and the residual are
+// float64) and moves the block to the lesser one (ties: lower index) only on
+// a strict decrease.  The float32 scores therefore only choose which two
+// codewords are compared exactly; a codeword whose float32 score lies within
+// the float32 rounding of the row's minimum but is not a finalist is not
+// considered.
 #include <math.h>
 #include <hip/hip_ext.h>
 #include "mpq_device.h"
@@ -220,6 +227,9 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
 //   dF(c) = 1/2 d^T G d - d^T g,   d = a (e_c - e_x)
 // is one product per lane and a wave sum.
 constexpr int CD_COLS_LANE = 4;   // tile columns per lane in the gradient update (tile width <= 256)
+constexpr int CD_KD_MAX = 64 * CD_COLS_LANE;
+constexpr int CD_SLAB_PER_THREAD = 8 * CD_KD_MAX / (64 * CDU_WAVES);
+static_assert(CD_SLAB_PER_THREAD * 64 * CDU_WAVES == 8 * CD_KD_MAX, "slab staging covers 8 x CD_KD_MAX");
 __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, int64_t n, int64_t b, int bl, int kd, int nslices,
                                                         double* __restrict__ Gt, const double* __restrict__ Ht,
                                                         const float* __restrict__ e32, int K,
@@ -228,9 +238,21 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
                                                         const int32_t* __restrict__ part_i,
                                                         int32_t* __restrict__ codes, double* __restrict__ Delta,
                                                         int32_t* __restrict__ changes, uint32_t* __restrict__ qf) {
+  // H[8 bl + q][jc] (q < 8, jc < kd), the rows of the gradient update, staged
+  // once per workgroup (every row's update reads the same 8 x kd slab)
+  __shared__ double hslab[8 * CD_KD_MAX];
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * CDU_WAVES + (threadIdx.x >> 6);
-  if (i >= m) return;
+  const int64_t i_w = (int64_t)blockIdx.x * CDU_WAVES + (threadIdx.x >> 6);
+  const bool live = i_w < m;               // waves past the last row only help stage the slab
+  const int64_t i = live ? i_w : m - 1;
+  double hs[CD_SLAB_PER_THREAD];
+#pragma unroll
+  for (int u = 0; u < CD_SLAB_PER_THREAD; ++u) {
+    const int e = (int)threadIdx.x + 64 * CDU_WAVES * u;
+    const int q = e / CD_KD_MAX, jc = e % CD_KD_MAX;
+    const double hv = Ht[(int64_t)(8 * bl + q) * kd + min(jc, kd - 1)];
+    hs[u] = jc < kd ? hv : 0.0;
+  }
   const int64_t B = n / 8;
   const int p = lane >> 3, k = lane & 7;
   const int c0 = 8 * (bl + 1);          // the next block's first column in the tile
@@ -258,20 +280,13 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
   const double hpk = Ht[(int64_t)(8 * bl + p) * kd + 8 * bl + k];
   const double gpp = Gt[i * kd + 8 * bl + p];
   const double gnext_v = Gt[i * kd + cnc + k];
-  // gradient update operands: column jc = lane + 64 u of the tile, rows 8 bl + q of
-  // H's diagonal tile (symmetric, read as H[8 bl + q][jc] so the loads coalesce)
-  double gcol[CD_COLS_LANE], hcol[CD_COLS_LANE][8];
+  // the row's gradient at column jc = lane + 64 u of the tile
+  double gcol[CD_COLS_LANE];
 #pragma unroll
   for (int u = 0; u < CD_COLS_LANE; ++u) {
     const int jc = lane + 64 * u;
-    const int jcc = min(jc, kd - 1);
-    const double gv = Gt[i * kd + jcc];
+    const double gv = Gt[i * kd + min(jc, kd - 1)];
     gcol[u] = jc < kd ? gv : 0.0;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const double hv = Ht[(int64_t)(8 * bl + q) * kd + jcc];
-      hcol[u][q] = jc < kd ? hv : 0.0;
-    }
   }
   // next block's query operands (lane k of each group of 8 builds q[k])
   double hnext[8];
@@ -290,6 +305,11 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
     exq[q] = e32[(int64_t)cxs * 8 + q];
     exn[q] = e32[(int64_t)cn * 8 + q];
   }
+
+#pragma unroll
+  for (int u = 0; u < CD_SLAB_PER_THREAD; ++u) hslab[threadIdx.x + 64 * CDU_WAVES * u] = hs[u];
+  __syncthreads();
+  if (!live) return;
 
   // ---- top 2 over all slices (lane butterfly; the top two of a totally
   // ordered set do not depend on the merge order)
@@ -368,7 +388,7 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
       if (jc < kd) {
         double sacc = 0.0;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) sacc = fma(hcol[u][q], dl[q], sacc);
+        for (int q = 0; q < 8; ++q) sacc = fma(hslab[q * CD_KD_MAX + jc], dl[q], sacc);
         const double nv = gcol[u] - sacc;
         Gt[i * kd + jc] = nv;
         if (jc >= c0 && jc < c0 + 8) gk = nv;
