@@ -252,6 +252,10 @@ def main():
                     help="CD sweeps (default: the workload's 3); 0 runs only the prologue, VAMP and MAP, e.g. for "
                          "counter passes over the VAMP kernels")
     ap.add_argument("--no-probe", action="store_true", help="skip the achievable-rate probes")
+    ap.add_argument("--no-split", action="store_true",
+                    help="skip the extra profiled step that gives the per-group time split (keeps a counter pass "
+                         "to one solve's dispatches: rocprofv3 --pmc has crashed in its dispatch interception after "
+                         "about 20 000 dispatches in one process)")
     ap.add_argument("--host-qr", action="store_true",
                     help="draw the orthogonal factor V with NumPy's QR on the host instead of rocSOLVER's (e.g. "
                          "under counter collection, where rocSOLVER's QR has crashed the profiled process); "
@@ -321,10 +325,12 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_per_step:.1f} ms/step, {value / 1e6:.3f} M weights/s")
 
     # one extra profiled step with every kernel group for the time split
-    out = mpq.quantize_layer(W, s, V, cb, a, o, outputs=out, profile=full, **kw)
-    torch.cuda.synchronize()
-    split = {k: round(v[0], 3) for k, v in full.as_dict().items()}
-    log(f"[bench] kernel ms per step: {split}")
+    split = None
+    if not args.no_split:
+        out = mpq.quantize_layer(W, s, V, cb, a, o, outputs=out, profile=full, **kw)
+        torch.cuda.synchronize()
+        split = {k: round(v[0], 3) for k, v in full.as_dict().items()}
+        log(f"[bench] kernel ms per step: {split}")
     # candidates are the single-kernel groups (the CD GEMM and update groups
     # each span several kernels and are reported in the split only)
     roof = dominant_roofline(L, {k: v for k, v in timed_prof.items()

@@ -179,7 +179,7 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, bool g
   sz[R_FLAG] = d == 8 ? (size_t)(64 + m * L.B) * i32 : 0;
   sz[R_D64] = (size_t)m * n * f64;
   sz[R_TKEY] = d == 8 ? (size_t)(KD / 8) * L.Kpad * 4 * sizeof(uint32_t) : 0;
-  sz[R_QF] = d == 8 ? (size_t)m * 16 * sizeof(uint32_t) : 0;
+  sz[R_QF] = d == 8 ? (size_t)m * 17 * sizeof(uint32_t) : 0;   // query fragments, then the CD bounds
   sz[R_ANCH] = (size_t)m * n * f64;   // anchored-prior cavity mean
   sz[R_LAM] = greedy ? (size_t)n * n * f64 : 0;
   sz[R_CTMP] = greedy ? chol_tmp_doubles(n) * f64 : 0;
@@ -211,7 +211,8 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, bool g
 
 // ------------------------------------------------------- codebook tables
 
-// Device table layout of a prepared codebook: levels (64 floats), float32
+// Device table layout of a prepared codebook: levels (64 floats; with d = 8
+// the first is a bound on the codeword norms), float32
 // codewords (Kpad x 8), QK and PV operand fragments, sorted E8 keys + indices.
 struct TableLayout {
   size_t levels, e32, qk, pv, e8k, total;
@@ -771,7 +772,7 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
           if (bl == 0)
             TIMED(c, MPQ_PROF_CD_SEARCH,
                   launch_cd_lattice_query(L.m, L.n, b, bl, kw, Gt, Ht, c.cb, a, codes, qf, c.st));
-          TIMED_KERNEL(c, MPQ_PROF_CD_SCORE, launch_cd_lattice_score, L.m, bl, tk, c.cb, qf, ps, pi, c.st);
+          TIMED_KERNEL(c, MPQ_PROF_CD_SCORE, launch_cd_lattice_score, L.m, bl, tk, c.cb, qf, true, ps, pi, c.st);
           TIMED(c, MPQ_PROF_CD_SEARCH,
                 launch_cd_lattice_update(L.m, L.n, b, bl, kw, Gt, Ht, c.cb, a, codes, Dl, chg, ps, pi, qf, c.st));
         }
@@ -835,7 +836,7 @@ int run_greedy(Ctx& c, const float* W, const float* a, const float* o, int32_t* 
       TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_lattice_tkeys(kw / 8, kw, Gd, c.cb, tk, c.st));
       TIMED(c, MPQ_PROF_CD_SEARCH, launch_greedy_query(L.m, L.n, j0, P, Lam, W, a, o, qf, c.st));
       for (int bl = 0; bl < kw / 8; ++bl) {
-        TIMED_KERNEL(c, MPQ_PROF_CD_SCORE, launch_cd_lattice_score, L.m, bl, tk, c.cb, qf, c.f(R_PS), c.pi(R_PI),
+        TIMED_KERNEL(c, MPQ_PROF_CD_SCORE, launch_cd_lattice_score, L.m, bl, tk, c.cb, qf, false, c.f(R_PS), c.pi(R_PI),
                      c.st);
         TIMED(c, MPQ_PROF_CD_SEARCH,
               launch_greedy_update(L.m, L.n, j0, j0 / 8 + bl, bl, kw, P, Lam, Rtile, W, c.cb, a, o, c.f(R_PS),
@@ -1081,6 +1082,16 @@ int mpq_codebook_prepare(const float* cb, int64_t K, int64_t d, void* tables, si
       for (int64_t k = 0; k < K; ++k) lv[k] = cb[k];
       MPQ_TRY(hipMemcpyAsync(tb + T.levels, lv.data(), 64 * sizeof(float), hipMemcpyHostToDevice, st));
     } else {
+      // levels[0] of a d = 8 codebook: an upper bound on the codeword norms
+      // (the block coordinate descent's score-error bound scales with it)
+      double r2 = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        double h2 = 0.0;
+        for (int q = 0; q < 8; ++q) h2 += (double)cb[k * 8 + q] * cb[k * 8 + q];
+        r2 = std::max(r2, h2);
+      }
+      lv[0] = (float)(std::sqrt(r2) * (1.0 + 1e-6));
+      MPQ_TRY(hipMemcpyAsync(tb + T.levels, lv.data(), 64 * sizeof(float), hipMemcpyHostToDevice, st));
       build_lattice_tables(cb, K, padded_k(K, d), e32, qk, pv);
       MPQ_TRY(hipMemcpyAsync(tb + T.e32, e32.data(), e32.size() * sizeof(float), hipMemcpyHostToDevice, st));
       MPQ_TRY(hipMemcpyAsync(tb + T.qk, qk.data(), qk.size() * sizeof(uint16_t), hipMemcpyHostToDevice, st));

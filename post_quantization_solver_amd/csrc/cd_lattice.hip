@@ -74,22 +74,55 @@ __global__ __launch_bounds__(256) void cd_tkeys_kernel(int kd, const double* __r
 
 // CD's query for block b: q = -a (a G e_x + g) (G the block's 8 x 8 diagonal
 // of H, e_x the current codeword, g the block's gradient), so the score is
-// dF(e) up to a per-row constant.  Lane p (= lane & 7) passes ge = (G e_x)[p]
-// and g[p].
-__device__ __forceinline__ void cd_query_write(int lane, int64_t i, double ge, double gp, double ai,
-                                               uint32_t* __restrict__ qf) {
-  query_write(lane, i, (float)(-ai * fma(ai, ge, gp)), ai, qf);
+// dF(e) up to a per-row constant.  Lane p (= lane & 7) passes ge = (G e_x)[p],
+// g[p], e_x[p] and the absolute row sum of G's row p.
+//
+// It also writes the row's acceptance bound tau = S(e_x) + eps: S(e_x) =
+// -sum_p e_x[p] a (a (G e_x)[p] / 2 + g[p]) is the current codeword's score
+// in float64 and eps bounds, for every codeword e of norm <= R, the gap
+// between the float32 score the MFMA computes (fp32 rounding of a^2, of t(e)
+// as computed from the float32 G, of q, the float32 sum of the 30 exact
+// products, and the 3-bit position tag) and the exact score:
+//   eps = CD_TAU_ULPS 2^-24 (a^2 R^2 max_p sum_q |G_pq| / 2 + R ||q||) + 1e-30.
+// A codeword with exact score below S(e_x) (a strict decrease of F) thus has
+// a tagged float32 score below tau; the score kernel reports only such
+// codewords, and a row with none keeps its codeword.
+constexpr double CD_TAU_ULPS = 128.0;
+__device__ __forceinline__ void cd_query_write(int lane, int64_t i, double ge, double gp, double exp_, double grow,
+                                               double ai, float rmax, uint32_t* __restrict__ qf,
+                                               float* __restrict__ tau) {
+  const double qv = -ai * fma(ai, ge, gp);
+  query_write(lane, i, (float)qv, ai, qf);
+  double sx = -exp_ * ai * fma(0.5 * ai, ge, gp);
+  double q2 = qv * qv;
+  double gm = grow;
+#pragma unroll
+  for (int msk = 1; msk < 8; msk <<= 1) {
+    sx += __shfl_xor(sx, msk, 64);
+    q2 += __shfl_xor(q2, msk, 64);
+    gm = fmax(gm, __shfl_xor(gm, msk, 64));
+  }
+  const double R = (double)rmax;
+  const double eps = CD_TAU_ULPS * 0x1p-24 * (0.5 * ai * ai * R * R * gm + R * sqrt(q2)) + 1e-30;
+  const double tv = sx + eps;
+  float tf = (float)tv;
+  if ((double)tf < tv) tf = nextafterf(tf, INFINITY);
+  if (lane == 0) tau[i] = tf;
 }
 
 __device__ __forceinline__ void cd_query_row(int lane, int64_t i, int bl, int kd, double gp,
                                              const double* __restrict__ Ht, const float* __restrict__ ex,
-                                             double ai, uint32_t* __restrict__ qf) {
+                                             double ai, float rmax, uint32_t* __restrict__ qf,
+                                             float* __restrict__ tau) {
   const int p = lane & 7;
   const double* hr = Ht + (int64_t)(8 * bl + p) * kd + 8 * bl;
-  double ge = 0.0;
+  double ge = 0.0, grow = 0.0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) ge = fma(hr[k], (double)ex[k], ge);
-  cd_query_write(lane, i, ge, gp, ai, qf);
+  for (int k = 0; k < 8; ++k) {
+    ge = fma(hr[k], (double)ex[k], ge);
+    grow += fabs(hr[k]);
+  }
+  cd_query_write(lane, i, ge, gp, (double)ex[p], grow, ai, rmax, qf, tau);
 }
 
 // Query fragments for the first block of a tile (later blocks get theirs from
@@ -98,13 +131,14 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_query_kernel(int64_t m, int
                                                        const double* __restrict__ Gt, const double* __restrict__ Ht,
                                                        const float* __restrict__ e32, int K,
                                                        const float* __restrict__ a,
-                                                       const int32_t* __restrict__ codes,
-                                                       uint32_t* __restrict__ qf) {
+                                                       const int32_t* __restrict__ codes, const float* __restrict__ rmaxp,
+                                                       uint32_t* __restrict__ qf, float* __restrict__ tau) {
   const int lane = threadIdx.x & 63;
   const int64_t i = (int64_t)blockIdx.x * CDU_WAVES + (threadIdx.x >> 6);
   if (i >= m) return;
   const double gp = Gt[i * kd + 8 * bl + (lane & 7)];
-  cd_query_row(lane, i, bl, kd, gp, Ht, e32 + (int64_t)safe_code(codes[i * (n / 8) + b], K) * 8, (double)a[i], qf);
+  cd_query_row(lane, i, bl, kd, gp, Ht, e32 + (int64_t)safe_code(codes[i * (n / 8) + b], K) * 8, (double)a[i],
+               rmaxp[0], qf, tau);
 }
 
 // A score with its 3 low mantissa bits replaced by the codeword's position
@@ -114,13 +148,13 @@ __device__ __forceinline__ float tag3(float x, uint32_t v) {
   return __uint_as_float((__float_as_uint(x) & 0xfffffff8u) | v);
 }
 
-// grid: (slices, row groups).  part_s / part_i: [m][slices][2] (best, second).
+// grid: (slices, row groups).  part_s / part_i: [slices][m][2] (best, second).
 // The float32 scores only rank candidates; the update kernel re-evaluates the
 // two best of every slice exactly in float64.
 __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int bl, const uint32_t* __restrict__ keys,
                                                        const v4u* __restrict__ tk, int Kpad,
-                                                       const v4u* __restrict__ qf, float* __restrict__ part_s,
-                                                       int32_t* __restrict__ part_i) {
+                                                       const v4u* __restrict__ qf, const float* __restrict__ tau,
+                                                       float* __restrict__ part_s, int32_t* __restrict__ part_i) {
   __shared__ __attribute__((aligned(16))) uint32_t lds_key[(CDL_CW_WG / 16) * 64 * 4];
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -141,8 +175,9 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
   for (int q = 0; q < 4; ++q) {
     const int64_t i = row_base + q * 16 + j;
     qop[q] = i < m ? qf[i * 4 + g] : (v4u){0u, 0u, 0u, 0u};
-    best[q] = INFINITY;
-    bst[q] = 0;
+    // only scores below the row's bound are candidates (no bound: every score)
+    best[q] = i < m ? (tau ? tau[i] : INFINITY) : -INFINITY;
+    bst[q] = -1;
   }
 
   // key fragments of this slice: lanes g < 3 carry e, lanes g = 3 the t(e)
@@ -166,10 +201,15 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
     if (f < nf) reinterpret_cast<v4u*>(lds_key)[f] = kbuf[u];
   }
   __syncthreads();
-  // lane (j, g) sees codewords 16 st + 4 g + v of the slice for row j, two
-  // steps at a time (ncw / 16 is even: Kpad is a multiple of 128); it keeps
-  // the least tagged score and the pair where it last strictly improved, so
-  // ties go to the earliest pair, then step, then the lowest v
+  // lane (j, g) sees codewords 16 st + 4 g + v (v = 0..3) of the slice for
+  // row j, two steps st = 2 sp, 2 sp + 1 at a time (ncw / 16 is even: Kpad is
+  // a multiple of 128).  The running best starts at the row's bound tau, so
+  // a pair's eight scores usually all lie above it: the common path is their
+  // minimum (v_minimum3_f32 x 3) and one compare.  Only when a lane of the
+  // wave sees a score below its running best does the wave tag the pair's
+  // scores (3 low mantissa bits := position, a change of at most 7 ulp, so
+  // one minimum ranks them and names the winner) and record the pair where
+  // the lane's best strictly decreased.
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
   const v4u* kq = reinterpret_cast<const v4u*>(lds_key);
   auto pair_step = [&](int sp) {
@@ -179,29 +219,37 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
     for (int q = 0; q < 4; ++q) {
       const v4f s0 = mfma_bf16_16x16x32(k0, qop[q], zero4);
       const v4f s1 = mfma_bf16_16x16x32(k1, qop[q], zero4);
-      // IEEE minimum, four v_minimum3_f32 with the running best (the scores are finite)
-      float mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(tag3(s0[0], 0u), tag3(s0[1], 1u)),
-                                               tag3(s0[2], 2u));
-      mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, tag3(s0[3], 3u)), tag3(s1[0], 4u));
-      mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, tag3(s1[1], 5u)), tag3(s1[2], 6u));
-      const float nb = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, tag3(s1[3], 7u)), best[q]);
-      bst[q] = nb < best[q] ? sp : bst[q];
-      best[q] = nb;
+      float mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(s0[0], s0[1]), s0[2]);
+      mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, s0[3]), s1[0]);
+      mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, s1[1]), s1[2]);
+      mn = __builtin_elementwise_minimum(mn, s1[3]);
+      if (__builtin_amdgcn_ballot_w64(mn < best[q]) != 0) {
+        float tm = __builtin_elementwise_minimum(__builtin_elementwise_minimum(tag3(s0[0], 0u), tag3(s0[1], 1u)),
+                                                 tag3(s0[2], 2u));
+        tm = __builtin_elementwise_minimum(__builtin_elementwise_minimum(tm, tag3(s0[3], 3u)), tag3(s1[0], 4u));
+        tm = __builtin_elementwise_minimum(__builtin_elementwise_minimum(tm, tag3(s1[1], 5u)), tag3(s1[2], 6u));
+        tm = __builtin_elementwise_minimum(tm, tag3(s1[3], 7u));
+        const bool better = tm < best[q];
+        bst[q] = better ? sp : bst[q];
+        best[q] = better ? tm : best[q];
+      }
     }
   };
-  // ncw / 32 is a multiple of 4: two pairs per iteration (the unrolled
-  // body lets the running bests change registers instead of being copied)
+  // ncw / 32 is a multiple of 4: two pairs per iteration
   for (int sp = 0; sp < ncw / 32; sp += 2) {
     pair_step(sp);
     pair_step(sp + 1);
   }
-  // top 2 of the row's four lane-bests (lanes j, j+16, j+32, j+48)
+  // top 2 of the row's four lane-bests (lanes j, j+16, j+32, j+48), ordered
+  // by (tagged score, index); a lane without a score below tau has none.
+  // part_s / part_i are [slice][m] so that the 16 rows of a subtile store
+  // one contiguous segment.
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t tg = __float_as_uint(best[q]) & 7u;
-    const int idx = isfinite(best[q]) ? cw_base + (2 * bst[q] + (int)(tg >> 2)) * 16 + 4 * g + (int)(tg & 3u)
-                                      : 0x7fffffff;
-    Cand c1 = {best[q], idx};
+    const bool found = bst[q] >= 0;
+    const int idx = found ? cw_base + (2 * bst[q] + (int)(tg >> 2)) * 16 + 4 * g + (int)(tg & 3u) : 0x7fffffff;
+    Cand c1 = {found ? best[q] : INFINITY, idx};
     Cand c2 = {INFINITY, 0x7fffffff};
 #pragma unroll
     for (int msk = 16; msk <= 32; msk <<= 1) {
@@ -210,8 +258,8 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
     }
     const int64_t i = row_base + q * 16 + j;
     if (g == 0 && i < m) {
-      reinterpret_cast<float2*>(part_s)[i * nsl + blockIdx.x] = make_float2(c1.v, c2.v);
-      reinterpret_cast<int2*>(part_i)[i * nsl + blockIdx.x] = make_int2(c1.i, c2.i);
+      reinterpret_cast<float2*>(part_s)[(int64_t)blockIdx.x * m + i] = make_float2(c1.v, c2.v);
+      reinterpret_cast<int2*>(part_i)[(int64_t)blockIdx.x * m + i] = make_int2(c1.i, c2.i);
     }
   }
 }
@@ -237,7 +285,8 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
                                                         const float* __restrict__ part_s,
                                                         const int32_t* __restrict__ part_i,
                                                         int32_t* __restrict__ codes, double* __restrict__ Delta,
-                                                        int32_t* __restrict__ changes, uint32_t* __restrict__ qf) {
+                                                        int32_t* __restrict__ changes, const float* __restrict__ rmaxp,
+                                                        uint32_t* __restrict__ qf, float* __restrict__ tau) {
   // H[8 bl + q][jc] (q < 8, jc < kd), the rows of the gradient update, staged
   // once per workgroup (every row's update reads the same 8 x kd slab)
   __shared__ double hslab[8 * CD_KD_MAX];
@@ -271,12 +320,13 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
   for (int r = 0; r < 2; ++r) {
     const int sl = 64 * r + lane;
     const int slc = min(sl, nslices - 1);
-    const float2 sv = reinterpret_cast<const float2*>(part_s)[i * nslices + slc];
-    const int2 iv = reinterpret_cast<const int2*>(part_i)[i * nslices + slc];
+    const float2 sv = reinterpret_cast<const float2*>(part_s)[(int64_t)slc * m + i];
+    const int2 iv = reinterpret_cast<const int2*>(part_i)[(int64_t)slc * m + i];
     o[r][0] = sl < nslices ? Cand{sv.x, iv.x} : Cand{INFINITY, 0x7fffffff};
     o[r][1] = sl < nslices ? Cand{sv.y, iv.y} : Cand{INFINITY, 0x7fffffff};
   }
   const double ai = a[i];
+  const float rmax = rmaxp[0];
   const double hpk = Ht[(int64_t)(8 * bl + p) * kd + 8 * bl + k];
   const double gpp = Gt[i * kd + 8 * bl + p];
   const double gnext_v = Gt[i * kd + cnc + k];
@@ -323,8 +373,8 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
       const int sl = base + lane;
       o1 = o2 = Cand{INFINITY, 0x7fffffff};
       if (sl < nslices) {
-        const float2 sv = reinterpret_cast<const float2*>(part_s)[i * nslices + sl];
-        const int2 iv = reinterpret_cast<const int2*>(part_i)[i * nslices + sl];
+        const float2 sv = reinterpret_cast<const float2*>(part_s)[(int64_t)sl * m + i];
+        const int2 iv = reinterpret_cast<const int2*>(part_i)[(int64_t)sl * m + i];
         o1 = {sv.x, iv.x};
         o2 = {sv.y, iv.y};
       }
@@ -398,12 +448,18 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
   // ---- the next block's query fragments
   if (has_next) {
     const double gp = moved ? shfl_d(gk, (c0 & 63) + k) : gnext;
-    double ge = 0.0;
+    double ge = 0.0, grow = 0.0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) ge = fma(hnext[q], (double)exn[q], ge);
-    cd_query_write(lane, i, ge, gp, ai, qf);
+    for (int q = 0; q < 8; ++q) {
+      ge = fma(hnext[q], (double)exn[q], ge);
+      grow += fabs(hnext[q]);
+    }
+    cd_query_write(lane, i, ge, gp, (double)exn[k], grow, ai, rmax, qf, tau);
   }
 }
+
+// The rows' acceptance bounds follow their query fragments (16 words per row).
+float* cd_tau(const uint32_t* qf, int64_t m) { return reinterpret_cast<float*>(const_cast<uint32_t*>(qf) + 16 * m); }
 
 hipError_t launch_cd_lattice_tkeys(int nb, int kd, const double* Ht, const CbTables& cb, uint32_t* tk,
                                    hipStream_t st) {
@@ -421,7 +477,7 @@ hipError_t launch_cd_lattice_query(int64_t m, int64_t n, int64_t b, int bl, int 
                                    uint32_t* qf, hipStream_t st) {
   if (m <= 0) return hipSuccess;
   hipLaunchKernelGGL(cd_query_kernel, dim3((unsigned)((m + CDU_WAVES - 1) / CDU_WAVES)), dim3(64 * CDU_WAVES), 0, st, m, n, b, bl, kd, Gt, Ht, cb.e32,
-                     cb.K, a, codes, qf);
+                     cb.K, a, codes, cb.levels, qf, cd_tau(qf, m));
   return hipGetLastError();
 }
 
@@ -431,18 +487,21 @@ hipError_t launch_cd_lattice_update(int64_t m, int64_t n, int64_t b, int bl, int
                                     hipStream_t st) {
   if (m <= 0) return hipSuccess;
   hipLaunchKernelGGL(cd_update_kernel, dim3((unsigned)((m + CDU_WAVES - 1) / CDU_WAVES)), dim3(64 * CDU_WAVES), 0, st, m, n, b, bl, kd,
-                     cd_lattice_slices(cb.Kpad), Gt, Ht, cb.e32, cb.K, a, part_s, part_i, codes, Delta, changes, qf);
+                     cd_lattice_slices(cb.Kpad), Gt, Ht, cb.e32, cb.K, a, part_s, part_i, codes, Delta, changes,
+                     cb.levels, qf, cd_tau(qf, m));
   return hipGetLastError();
 }
 
 hipError_t launch_cd_lattice_score(int64_t m, int bl, const uint32_t* tk, const CbTables& cb, const uint32_t* qf,
-                                   float* part_s, int32_t* part_i, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
+                                   bool bounded, float* part_s, int32_t* part_i, hipStream_t st, hipEvent_t t0,
+                                   hipEvent_t t1) {
   if (m <= 0) return hipSuccess;
   const int nslices = cd_lattice_slices(cb.Kpad);
   dim3 g1((unsigned)nslices, (unsigned)((m + CDL_ROWS_WG - 1) / CDL_ROWS_WG));
   // t0 / t1 (optional) take the kernel's own start and end times
   hipExtLaunchKernelGGL(cd_score_kernel, g1, dim3(64 * CDL_WAVES), 0, st, t0, t1, 0u, m, bl, cb.qk_keys,
-                        reinterpret_cast<const v4u*>(tk), cb.Kpad, reinterpret_cast<const v4u*>(qf), part_s, part_i);
+                        reinterpret_cast<const v4u*>(tk), cb.Kpad, reinterpret_cast<const v4u*>(qf),
+                        bounded ? static_cast<const float*>(cd_tau(qf, m)) : nullptr, part_s, part_i);
   return hipGetLastError();
 }
 

@@ -238,8 +238,8 @@ __global__ __launch_bounds__(256) void greedy_update_kernel(int64_t m, int64_t n
     const int sl = 64 * r + lane;
     o2[r][0] = o2[r][1] = Cand{INFINITY, 0x7fffffff};
     if (sl < nslices) {
-      const float2 sv = reinterpret_cast<const float2*>(part_s)[i * nslices + sl];
-      const int2 iv = reinterpret_cast<const int2*>(part_i)[i * nslices + sl];
+      const float2 sv = reinterpret_cast<const float2*>(part_s)[(int64_t)sl * m + i];
+      const int2 iv = reinterpret_cast<const int2*>(part_i)[(int64_t)sl * m + i];
       o2[r][0] = {sv.x, iv.x};
       o2[r][1] = {sv.y, iv.y};
     }
@@ -256,8 +256,8 @@ __global__ __launch_bounds__(256) void greedy_update_kernel(int64_t m, int64_t n
       const int sl = base + lane;
       x1 = x2 = Cand{INFINITY, 0x7fffffff};
       if (sl < nslices) {
-        const float2 sv = reinterpret_cast<const float2*>(part_s)[i * nslices + sl];
-        const int2 iv = reinterpret_cast<const int2*>(part_i)[i * nslices + sl];
+        const float2 sv = reinterpret_cast<const float2*>(part_s)[(int64_t)sl * m + i];
+        const int2 iv = reinterpret_cast<const int2*>(part_i)[(int64_t)sl * m + i];
         x1 = {sv.x, iv.x};
         x2 = {sv.y, iv.y};
       }

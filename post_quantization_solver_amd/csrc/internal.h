@@ -84,7 +84,7 @@ hipError_t launch_digit_gemm(int epi, const DigitGemmArgs& g, hipStream_t st);
 struct CbTables {
   int K, d;
   int Kpad;                 // K rounded up to the lattice chunk size (d = 8)
-  const float* levels;      // d = 1: K base levels
+  const float* levels;      // d = 1: K base levels; d = 8: levels[0] bounds the codeword norms
   const uint32_t* qk_keys;  // d = 8: QK operand fragments, Kpad/16 subtiles x 64 lanes x 4 words
   const uint32_t* pv_ops;   // d = 8: PV operand fragments, Kpad/32 steps x 64 lanes x 4 words
   const float* e32;         // d = 8: base codewords as float32, Kpad x 8
@@ -169,7 +169,9 @@ hipError_t launch_cd_scalar_tile(int64_t m, int64_t n, int64_t j0, int kd, const
 // CD (d = 8): one block of a tile (scoring over codeword slices, then the move).
 // tk: the tile's score-key table, nb blocks x Kpad x 4 words (written by
 // launch_cd_lattice_tkeys once per tile); qf: m x 16 words of per-row query
-// fragments, passed from each block's update to the next block's scoring.
+// fragments followed by m float32 acceptance bounds (scores at or above a
+// row's bound cannot decrease F), passed from each block's update to the
+// next block's scoring.
 hipError_t launch_cd_lattice_tkeys(int nb, int kd, const double* Ht, const CbTables& cb, uint32_t* tk,
                                    hipStream_t st);
 // One block of a tile: the first block's query fragments (bl = 0 only), then
@@ -183,10 +185,13 @@ hipError_t launch_cd_lattice_update(int64_t m, int64_t n, int64_t b, int bl, int
                                     int32_t* changes, const float* part_s, const int32_t* part_i, uint32_t* qf,
                                     hipStream_t st);
 int cd_lattice_slices(int Kpad);
-// The scoring pass alone (codeword slices x row groups -> part_s / part_i).
+// The scoring pass alone (codeword slices x row groups -> part_s / part_i,
+// both [slices][m][2]).  bounded: only scores below the rows' acceptance
+// bounds (after the query fragments in qf) are candidates; otherwise every
+// codeword is (the greedy comparator's queries carry no bound).
 hipError_t launch_cd_lattice_score(int64_t m, int bl, const uint32_t* tk, const CbTables& cb, const uint32_t* qf,
-                                   float* part_s, int32_t* part_i, hipStream_t st, hipEvent_t t0 = nullptr,
-                                   hipEvent_t t1 = nullptr);
+                                   bool bounded, float* part_s, int32_t* part_i, hipStream_t st,
+                                   hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 // ------------------------------------------------ sequential greedy (G3) ----
 // Lam (n x n float64, lower) with H + delta I = Lam^T Lam from VS (n x r,
