@@ -215,20 +215,31 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
   auto pair_step = [&](int sp) {
     const v4u k0 = kq[(2 * sp) * 64 + lane];
     const v4u k1 = kq[(2 * sp + 1) * 64 + lane];
+    // the four row subtiles' tiles first (eight MFMAs back to back), then
+    // their minima and one wave-uniform branch for all four
+    v4f s0[4], s1[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const v4f s0 = mfma_bf16_16x16x32(k0, qop[q], zero4);
-      const v4f s1 = mfma_bf16_16x16x32(k1, qop[q], zero4);
-      float mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(s0[0], s0[1]), s0[2]);
-      mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, s0[3]), s1[0]);
-      mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, s1[1]), s1[2]);
-      mn = __builtin_elementwise_minimum(mn, s1[3]);
-      if (__builtin_amdgcn_ballot_w64(mn < best[q]) != 0) {
-        float tm = __builtin_elementwise_minimum(__builtin_elementwise_minimum(tag3(s0[0], 0u), tag3(s0[1], 1u)),
-                                                 tag3(s0[2], 2u));
-        tm = __builtin_elementwise_minimum(__builtin_elementwise_minimum(tm, tag3(s0[3], 3u)), tag3(s1[0], 4u));
-        tm = __builtin_elementwise_minimum(__builtin_elementwise_minimum(tm, tag3(s1[1], 5u)), tag3(s1[2], 6u));
-        tm = __builtin_elementwise_minimum(tm, tag3(s1[3], 7u));
+      s0[q] = mfma_bf16_16x16x32(k0, qop[q], zero4);
+      s1[q] = mfma_bf16_16x16x32(k1, qop[q], zero4);
+    }
+    uint32_t any = 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(s0[q][0], s0[q][1]), s0[q][2]);
+      mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, s0[q][3]), s1[q][0]);
+      mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, s1[q][1]), s1[q][2]);
+      mn = __builtin_elementwise_minimum(mn, s1[q][3]);
+      any |= (uint32_t)(mn < best[q]);   // no short circuit: one compare per subtile
+    }
+    if (__builtin_amdgcn_ballot_w64(any != 0u) != 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float tm = __builtin_elementwise_minimum(
+            __builtin_elementwise_minimum(tag3(s0[q][0], 0u), tag3(s0[q][1], 1u)), tag3(s0[q][2], 2u));
+        tm = __builtin_elementwise_minimum(__builtin_elementwise_minimum(tm, tag3(s0[q][3], 3u)), tag3(s1[q][0], 4u));
+        tm = __builtin_elementwise_minimum(__builtin_elementwise_minimum(tm, tag3(s1[q][1], 5u)), tag3(s1[q][2], 6u));
+        tm = __builtin_elementwise_minimum(tm, tag3(s1[q][3], 7u));
         const bool better = tm < best[q];
         bst[q] = better ? sp : bst[q];
         best[q] = better ? tm : best[q];
