@@ -210,9 +210,10 @@ typedef struct {
                                       return MPQ_ENONFINITE, having run nothing else, if any entry is
                                       NaN or infinite or a row scale is <= 0; the call waits for the
                                       scan's verdict */
-#define MPQ_F_LINEAR_F64     64u   /* run the linear module's rank-space products on the fp64 matrix
-                                      cores instead of the int8 digit GEMM (for A/B checks; the digit
-                                      GEMM also gives way by itself when n or r exceeds 32767) */
+#define MPQ_F_LINEAR_F64     64u   /* run the float64 products (the linear module's rank-space products
+                                      and CD's H = VS VS^T and G = (W - X) H) on the fp64 matrix cores
+                                      instead of the int8 digit GEMM (for A/B checks; the digit GEMM
+                                      also gives way by itself when n or r exceeds 32767) */
 
 /* ------------------------------------------------------------------ sizes, status */
 
@@ -240,7 +241,7 @@ const char* mpq_hip_error_name(void);
  * state is float64; the linear module's rank-space products are float64
  * accurate (exact int8 digit products summed in int32 on the matrix cores,
  * about 1e-10 relative, or fp64 MFMA with MPQ_F_LINEAR_F64); CD decides in
- * float64.
+ * float64, on H and its gradient formed the same way.
  *
  * Inputs: W, s, V, row_scale, row_offset as in the conventions; T_vamp >= 0;
  * n_cd >= 0; damping in (0, 1] (the weight of the new beta).

@@ -135,7 +135,7 @@ struct Layout {
 enum Region {
   R_VT, R_VS64, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI, R_CHG, R_CODES,
   R_FLAG, R_D64, R_TKEY, R_QF, R_ANCH, R_LAM, R_CTMP, R_GDIAG, R_MROWS, R_HFULL, R_G64, R_ACTIVE, R_CHECK,
-  R_DPA, R_DPVT, R_DPV, R_DEA, R_DEVT, R_DEV, R_COUNT
+  R_DPA, R_DPVT, R_DPV, R_DEA, R_DEVT, R_DEV, R_DPN, R_DEN, R_COUNT
 };
 
 // The linear module's products take the int8 digit GEMM when both of its
@@ -200,6 +200,9 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, bool g
   sz[R_DEA] = dg ? (size_t)m * i32 : 0;
   sz[R_DEVT] = dg ? (size_t)r * i32 : 0;
   sz[R_DEV] = dg ? (size_t)n * i32 : 0;
+  // CD's float64 products: the digits of VS (n x r), then of H (n x n)
+  sz[R_DPN] = dg ? digit_plane_bytes(n, std::max(n, r)) : 0;
+  sz[R_DEN] = dg ? (size_t)n * i32 : 0;
   size_t o = 0;
   for (int k = 0; k < R_COUNT; ++k) {
     L.off[k] = o;
@@ -629,14 +632,26 @@ int run_iteration(Ctx& c, const float* W, double* R1, double* gamma1, double* be
 }
 
 // H = VS VS^T (float64, n x n) on the tiles that touch the lower triangle,
-// then mirrored.
+// then mirrored.  With the digit products VS is split once and serves as both
+// operands (the digit pairs are symmetric, so H is exactly symmetric).
 int compute_h(Ctx& c) {
   const Layout& L = c.L;
   double* H = c.d(R_HFULL);
-  Gemm64Args h = gemm64((int)L.n, (int)L.n, (int)L.r, c.d(R_VS64), L.r, nullptr, L.r, H, L.n);
-  h.B64 = c.d(R_VS64);
-  h.lower = 1;
-  TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_STORE, true, h, c.st));
+  if (c.digits) {
+    TIMED(c, MPQ_PROF_CD_GEMM, launch_digit_split(c.d(R_VS64), L.n, L.r, L.r, c.pi(R_DEN), c.dp(R_DPN), c.st));
+    DigitGemmArgs h = digit_args(c, (int)L.n, (int)L.n, (int)L.r, R_DPN, R_DEN);
+    h.Ap = c.dp(R_DPN);
+    h.EA = c.pi(R_DEN);
+    h.C = H;
+    h.ldc = L.n;
+    h.lower = 1;
+    TIMED(c, MPQ_PROF_CD_GEMM, launch_digit_gemm(EPI_STORE, h, c.st));
+  } else {
+    Gemm64Args h = gemm64((int)L.n, (int)L.n, (int)L.r, c.d(R_VS64), L.r, nullptr, L.r, H, L.n);
+    h.B64 = c.d(R_VS64);
+    h.lower = 1;
+    TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_STORE, true, h, c.st));
+  }
   TIMED(c, MPQ_PROF_CD_GEMM, launch_mirror_lower(H, L.n, c.st));
   return MPQ_OK;
 }
@@ -728,9 +743,18 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
     const int rc = compute_h(c);
     if (rc) return rc;
     // G = (W - X) H
-    Gemm64Args gd = gemm64((int)L.m, (int)L.n, (int)L.n, D, L.n, nullptr, L.n, Gf, L.n);
-    gd.B64 = H;
-    TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_STORE, true, gd, c.st));
+    if (c.digits) {
+      TIMED(c, MPQ_PROF_CD_GEMM, launch_digit_split(D, L.m, L.n, L.n, c.pi(R_DEA), c.dp(R_DPA), c.st));
+      TIMED(c, MPQ_PROF_CD_GEMM, launch_digit_split(H, L.n, L.n, L.n, c.pi(R_DEN), c.dp(R_DPN), c.st));
+      DigitGemmArgs gd = digit_args(c, (int)L.m, (int)L.n, (int)L.n, R_DPN, R_DEN);
+      gd.C = Gf;
+      gd.ldc = L.n;
+      TIMED(c, MPQ_PROF_CD_GEMM, launch_digit_gemm(EPI_STORE, gd, c.st));
+    } else {
+      Gemm64Args gd = gemm64((int)L.m, (int)L.n, (int)L.n, D, L.n, nullptr, L.n, Gf, L.n);
+      gd.B64 = H;
+      TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_STORE, true, gd, c.st));
+    }
   }
   // diagonal tiles of H = VS VS^T
   const int full = (int)(L.n / KD);

@@ -228,6 +228,7 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
   const int gm = min(tm - first, DG_GROUP_M);
   const int in = tile - group * DG_GROUP_M * tn;
   const int tr = first + in % gm, tc = in / gm;
+  if (g.lower && tc > tr) return;   // whole tile above the diagonal
   const int row0 = tr * DG_TILE, col0 = tc * DG_TILE;
   const int64_t rt0 = (int64_t)tr * DG_RT, ct0 = (int64_t)tc * DG_RT;
   const int64_t nkt = (g.K + 63) / 64;

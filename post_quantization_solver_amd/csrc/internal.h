@@ -71,6 +71,7 @@ struct DigitGemmArgs {
   double* partial; int64_t ldp;
   const double* X; int64_t ldx;
   const float* W; int64_t ldw;
+  int lower;                              // only the tiles that touch the lower triangle (M == N)
 };
 size_t digit_plane_bytes(int64_t rows, int64_t K);
 hipError_t launch_digit_split(const double* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes,
