@@ -135,7 +135,7 @@ struct Layout {
 enum Region {
   R_VT, R_VS64, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI, R_CHG, R_CODES,
   R_FLAG, R_D64, R_TKEY, R_QF, R_ANCH, R_LAM, R_CTMP, R_GDIAG, R_MROWS, R_HFULL, R_G64, R_ACTIVE, R_CHECK,
-  R_DPA, R_DPVT, R_DPV, R_DEA, R_DEVT, R_DEV, R_DPN, R_DEN, R_COUNT
+  R_DPA, R_DPVT, R_DPV, R_DEA, R_DEVT, R_DEV, R_DPN, R_DEN, R_LASTMV, R_CDROWS, R_COUNT
 };
 
 // The linear module's products take the int8 digit GEMM when both of its
@@ -190,6 +190,8 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, bool g
   // CD: the rows that moved in the current tile, and their count
   sz[R_MROWS] = (size_t)(m + 64) * i32;
   sz[R_ACTIVE] = (size_t)m * i32;   // rows still sweeping (for the sweeps output)
+  sz[R_LASTMV] = d == 8 ? (size_t)m * i32 : 0;          // CD: step of each row's last move
+  sz[R_CDROWS] = d == 8 ? (size_t)(m + 64) * i32 : 0;   // CD: a tile's rows, then their count
   sz[R_CHECK] = 64;                 // MPQ_F_CHECK_FINITE flag
   // digit planes of the linear module's operands: W - r2 or z (per call), and
   // V^T and V (once per call), with their row exponents
@@ -778,6 +780,9 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
   uint32_t* tk = reinterpret_cast<uint32_t*>(c.pi(R_TKEY));
   float* ps = c.f(R_PS);
   int32_t* pi = c.pi(R_PI);
+  int32_t* lastmv = c.pi(R_LASTMV);
+  int32_t* cdrows = c.pi(R_CDROWS);
+  if (L.d == 8) TIMED(c, MPQ_PROF_OTHER, launch_fill_i32(lastmv, L.m, -1, c.st));
   for (int sw = 0; sw < n_cd; ++sw) {
     TIMED(c, MPQ_PROF_OTHER, launch_fill_i32(chg, L.m, 0, c.st));
     for (int tl = 0; tl < L.ntiles; ++tl) {
@@ -791,14 +796,26 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
               launch_cd_scalar_tile(L.m, L.n, j0, kw, Gt, Ht, c.cb, a, o, codes, nullptr, Dl, chg, c.st));
       } else {
         TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_lattice_tkeys(kw / 8, kw, Ht, c.cb, tk, c.st));
+        // after the first sweep only the rows that moved within the last B
+        // steps run the tile (a block with no move of its row since its last
+        // evaluation keeps its codeword)
+        const int64_t B = L.n / 8;
+        const int64_t t0 = (int64_t)sw * B + j0 / 8;
+        const int32_t* rows = nullptr;
+        if (sw > 0) {
+          TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_tile_rows(lastmv, L.m, t0 - B, kw, cdrows, cdrows + L.m, Dl, c.st));
+          rows = cdrows;
+        }
         for (int bl = 0; bl < kw / 8; ++bl) {
           const int64_t b = j0 / 8 + bl;
           if (bl == 0)
             TIMED(c, MPQ_PROF_CD_SEARCH,
                   launch_cd_lattice_query(L.m, L.n, b, bl, kw, Gt, Ht, c.cb, a, codes, qf, c.st));
-          TIMED_KERNEL(c, MPQ_PROF_CD_SCORE, launch_cd_lattice_score, L.m, bl, tk, c.cb, qf, true, ps, pi, c.st);
+          TIMED_KERNEL(c, MPQ_PROF_CD_SCORE, launch_cd_lattice_score, L.m, bl, tk, c.cb, qf, true, rows,
+                       cdrows + L.m, ps, pi, c.st);
           TIMED(c, MPQ_PROF_CD_SEARCH,
-                launch_cd_lattice_update(L.m, L.n, b, bl, kw, Gt, Ht, c.cb, a, codes, Dl, chg, ps, pi, qf, c.st));
+                launch_cd_lattice_update(L.m, L.n, b, bl, kw, Gt, Ht, c.cb, a, codes, Dl, chg, ps, pi, qf, rows,
+                                         cdrows + L.m, lastmv, (int32_t)(t0 + bl), c.st));
         }
       }
       // G -= Delta H[tile, :] over the rows that moved in the tile (the other
@@ -860,7 +877,8 @@ int run_greedy(Ctx& c, const float* W, const float* a, const float* o, int32_t* 
       TIMED(c, MPQ_PROF_CD_SEARCH, launch_cd_lattice_tkeys(kw / 8, kw, Gd, c.cb, tk, c.st));
       TIMED(c, MPQ_PROF_CD_SEARCH, launch_greedy_query(L.m, L.n, j0, P, Lam, W, a, o, qf, c.st));
       for (int bl = 0; bl < kw / 8; ++bl) {
-        TIMED_KERNEL(c, MPQ_PROF_CD_SCORE, launch_cd_lattice_score, L.m, bl, tk, c.cb, qf, false, c.f(R_PS), c.pi(R_PI),
+        TIMED_KERNEL(c, MPQ_PROF_CD_SCORE, launch_cd_lattice_score, L.m, bl, tk, c.cb, qf, false, nullptr, nullptr,
+                     c.f(R_PS), c.pi(R_PI),
                      c.st);
         TIMED(c, MPQ_PROF_CD_SEARCH,
               launch_greedy_update(L.m, L.n, j0, j0 / 8 + bl, bl, kw, P, Lam, Rtile, W, c.cb, a, o, c.f(R_PS),

@@ -148,14 +148,20 @@ __device__ __forceinline__ float tag3(float x, uint32_t v) {
   return __uint_as_float((__float_as_uint(x) & 0xfffffff8u) | v);
 }
 
-// grid: (slices, row groups).  part_s / part_i: [slices][m][2] (best, second).
+// grid: (slices, row groups).  part_s / part_i: [slices][list position][2] (best, second).
 // The float32 scores only rank candidates; the update kernel re-evaluates the
 // two best of every slice exactly in float64.
 __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int bl, const uint32_t* __restrict__ keys,
                                                        const v4u* __restrict__ tk, int Kpad,
                                                        const v4u* __restrict__ qf, const float* __restrict__ tau,
+                                                       const int32_t* __restrict__ rows,
+                                                       const int32_t* __restrict__ rcount,
                                                        float* __restrict__ part_s, int32_t* __restrict__ part_i) {
   __shared__ __attribute__((aligned(16))) uint32_t lds_key[(CDL_CW_WG / 16) * 64 * 4];
+  // rows: the rows this block scores, by list position (nullptr: all m rows
+  // in order); workgroups past the list's end have nothing to do
+  const int64_t cnt = rows ? (int64_t)rcount[0] : m;
+  if ((int64_t)blockIdx.y * CDL_ROWS_WG >= cnt) return;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -173,10 +179,12 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
   int bst[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int64_t i = row_base + q * 16 + j;
-    qop[q] = i < m ? qf[i * 4 + g] : (v4u){0u, 0u, 0u, 0u};
+    const int64_t x = row_base + q * 16 + j;   // list position
+    const bool valid = x < cnt;
+    const int64_t i = valid ? (rows ? (int64_t)rows[x] : x) : 0;
+    qop[q] = valid ? qf[i * 4 + g] : (v4u){0u, 0u, 0u, 0u};
     // only scores below the row's bound are candidates (no bound: every score)
-    best[q] = i < m ? (tau ? tau[i] : INFINITY) : -INFINITY;
+    best[q] = valid ? (tau ? tau[i] : INFINITY) : -INFINITY;
     bst[q] = -1;
   }
 
@@ -267,10 +275,10 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
       Cand o1 = shfl_cand(c1, msk), o2 = shfl_cand(c2, msk);
       merge_top2(c1, c2, o1, o2);
     }
-    const int64_t i = row_base + q * 16 + j;
-    if (g == 0 && i < m) {
-      reinterpret_cast<float2*>(part_s)[(int64_t)blockIdx.x * m + i] = make_float2(c1.v, c2.v);
-      reinterpret_cast<int2*>(part_i)[(int64_t)blockIdx.x * m + i] = make_int2(c1.i, c2.i);
+    const int64_t x = row_base + q * 16 + j;
+    if (g == 0 && x < cnt) {   // candidates by list position
+      reinterpret_cast<float2*>(part_s)[(int64_t)blockIdx.x * m + x] = make_float2(c1.v, c2.v);
+      reinterpret_cast<int2*>(part_i)[(int64_t)blockIdx.x * m + x] = make_int2(c1.i, c2.i);
     }
   }
 }
@@ -297,14 +305,20 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
                                                         const int32_t* __restrict__ part_i,
                                                         int32_t* __restrict__ codes, double* __restrict__ Delta,
                                                         int32_t* __restrict__ changes, const float* __restrict__ rmaxp,
-                                                        uint32_t* __restrict__ qf, float* __restrict__ tau) {
+                                                        uint32_t* __restrict__ qf, float* __restrict__ tau,
+                                                        const int32_t* __restrict__ rows,
+                                                        const int32_t* __restrict__ rcount,
+                                                        int32_t* __restrict__ lastmv, int32_t step) {
   // H[8 bl + q][jc] (q < 8, jc < kd), the rows of the gradient update, staged
   // once per workgroup (every row's update reads the same 8 x kd slab)
   __shared__ double hslab[8 * CD_KD_MAX];
+  const int64_t cnt = rows ? (int64_t)rcount[0] : m;
+  if ((int64_t)blockIdx.x * CDU_WAVES >= cnt) return;
   const int lane = threadIdx.x & 63;
-  const int64_t i_w = (int64_t)blockIdx.x * CDU_WAVES + (threadIdx.x >> 6);
-  const bool live = i_w < m;               // waves past the last row only help stage the slab
-  const int64_t i = live ? i_w : m - 1;
+  const int64_t x_w = (int64_t)blockIdx.x * CDU_WAVES + (threadIdx.x >> 6);   // list position
+  const bool live = x_w < cnt;             // waves past the list's end only help stage the slab
+  const int64_t x = live ? x_w : cnt - 1;
+  const int64_t i = rows ? (int64_t)rows[x] : x;
   double hs[CD_SLAB_PER_THREAD];
 #pragma unroll
   for (int u = 0; u < CD_SLAB_PER_THREAD; ++u) {
@@ -331,8 +345,8 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
   for (int r = 0; r < 2; ++r) {
     const int sl = 64 * r + lane;
     const int slc = min(sl, nslices - 1);
-    const float2 sv = reinterpret_cast<const float2*>(part_s)[(int64_t)slc * m + i];
-    const int2 iv = reinterpret_cast<const int2*>(part_i)[(int64_t)slc * m + i];
+    const float2 sv = reinterpret_cast<const float2*>(part_s)[(int64_t)slc * m + x];
+    const int2 iv = reinterpret_cast<const int2*>(part_i)[(int64_t)slc * m + x];
     o[r][0] = sl < nslices ? Cand{sv.x, iv.x} : Cand{INFINITY, 0x7fffffff};
     o[r][1] = sl < nslices ? Cand{sv.y, iv.y} : Cand{INFINITY, 0x7fffffff};
   }
@@ -384,8 +398,8 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
       const int sl = base + lane;
       o1 = o2 = Cand{INFINITY, 0x7fffffff};
       if (sl < nslices) {
-        const float2 sv = reinterpret_cast<const float2*>(part_s)[(int64_t)sl * m + i];
-        const int2 iv = reinterpret_cast<const int2*>(part_i)[(int64_t)sl * m + i];
+        const float2 sv = reinterpret_cast<const float2*>(part_s)[(int64_t)sl * m + x];
+        const int2 iv = reinterpret_cast<const int2*>(part_i)[(int64_t)sl * m + x];
         o1 = {sv.x, iv.x};
         o2 = {sv.y, iv.y};
       }
@@ -438,6 +452,7 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
   if (moved && lane == 0) {
     codes[i * B + b] = bestk;
     changes[i] += 1;
+    lastmv[i] = step;
   }
   // g_j -= sum_q H[j][8 bl + q] delta_q for every column j of the tile; the
   // lanes owning the next block's columns keep their new values
@@ -469,6 +484,51 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
   }
 }
 
+// Rows that need a tile of a later sweep.  A block's decision depends on the
+// row only through its gradient, which changes only when the row moves; a
+// block that was evaluated (and moved to its best, or kept its codeword) at
+// step t - B, with no move of the row since, keeps its codeword at step t.
+// lastmv[i] is the step (sweep * B + block) of row i's last move (-1: none),
+// so the row needs step t only if lastmv[i] > t - B; with no moves that
+// stays false, so over a tile starting at step t0 the row needs evaluation
+// only if lastmv[i] > t0 - B.  Each wave ballots 64 rows and appends the
+// needed ones with one atomic (the list's order does not affect any row).
+__global__ __launch_bounds__(256) void cd_tile_rows_kernel(const int32_t* __restrict__ lastmv, int64_t m,
+                                                           int64_t thresh, int32_t* __restrict__ rows,
+                                                           int32_t* __restrict__ count) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool need = i < m && (int64_t)lastmv[i] > thresh;
+  const uint64_t bal = __builtin_amdgcn_ballot_w64(need);
+  if (bal == 0) return;
+  int base = 0;
+  if (lane == 0) base = atomicAdd(count, (int)__builtin_popcountll(bal));
+  base = __shfl(base, 0, 64);
+  if (need) rows[base + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] = (int32_t)i;
+}
+
+// The tile's moves of the rows that skip it: zero (their update kernels do not
+// run, and the tile's gradient update reads every row's moves).
+__global__ __launch_bounds__(256) void cd_clear_skipped_kernel(const int32_t* __restrict__ lastmv, int64_t m,
+                                                               int64_t thresh, int kd, double* __restrict__ Delta) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = e / kd;
+  if (i >= m) return;
+  if ((int64_t)lastmv[i] <= thresh) Delta[e] = 0.0;
+}
+
+hipError_t launch_cd_tile_rows(const int32_t* lastmv, int64_t m, int64_t thresh, int kd, int32_t* rows,
+                               int32_t* count, double* Delta, hipStream_t st) {
+  if (m <= 0) return hipSuccess;
+  hipError_t e = launch_fill_i32(count, 1, 0, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(cd_tile_rows_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, lastmv, m, thresh,
+                     rows, count);
+  hipLaunchKernelGGL(cd_clear_skipped_kernel, dim3((unsigned)((m * kd + 255) / 256)), dim3(256), 0, st, lastmv, m,
+                     thresh, kd, Delta);
+  return hipGetLastError();
+}
+
 // The rows' acceptance bounds follow their query fragments (16 words per row).
 float* cd_tau(const uint32_t* qf, int64_t m) { return reinterpret_cast<float*>(const_cast<uint32_t*>(qf) + 16 * m); }
 
@@ -495,24 +555,25 @@ hipError_t launch_cd_lattice_query(int64_t m, int64_t n, int64_t b, int bl, int 
 hipError_t launch_cd_lattice_update(int64_t m, int64_t n, int64_t b, int bl, int kd, double* Gt, const double* Ht,
                                     const CbTables& cb, const float* a, int32_t* codes, double* Delta,
                                     int32_t* changes, const float* part_s, const int32_t* part_i, uint32_t* qf,
+                                    const int32_t* rows, const int32_t* rcount, int32_t* lastmv, int32_t step,
                                     hipStream_t st) {
   if (m <= 0) return hipSuccess;
   hipLaunchKernelGGL(cd_update_kernel, dim3((unsigned)((m + CDU_WAVES - 1) / CDU_WAVES)), dim3(64 * CDU_WAVES), 0, st, m, n, b, bl, kd,
                      cd_lattice_slices(cb.Kpad), Gt, Ht, cb.e32, cb.K, a, part_s, part_i, codes, Delta, changes,
-                     cb.levels, qf, cd_tau(qf, m));
+                     cb.levels, qf, cd_tau(qf, m), rows, rcount, lastmv, step);
   return hipGetLastError();
 }
 
 hipError_t launch_cd_lattice_score(int64_t m, int bl, const uint32_t* tk, const CbTables& cb, const uint32_t* qf,
-                                   bool bounded, float* part_s, int32_t* part_i, hipStream_t st, hipEvent_t t0,
-                                   hipEvent_t t1) {
+                                   bool bounded, const int32_t* rows, const int32_t* rcount, float* part_s,
+                                   int32_t* part_i, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
   if (m <= 0) return hipSuccess;
   const int nslices = cd_lattice_slices(cb.Kpad);
   dim3 g1((unsigned)nslices, (unsigned)((m + CDL_ROWS_WG - 1) / CDL_ROWS_WG));
   // t0 / t1 (optional) take the kernel's own start and end times
   hipExtLaunchKernelGGL(cd_score_kernel, g1, dim3(64 * CDL_WAVES), 0, st, t0, t1, 0u, m, bl, cb.qk_keys,
                         reinterpret_cast<const v4u*>(tk), cb.Kpad, reinterpret_cast<const v4u*>(qf),
-                        bounded ? static_cast<const float*>(cd_tau(qf, m)) : nullptr, part_s, part_i);
+                        bounded ? static_cast<const float*>(cd_tau(qf, m)) : nullptr, rows, rcount, part_s, part_i);
   return hipGetLastError();
 }
 

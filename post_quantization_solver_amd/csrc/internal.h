@@ -181,18 +181,26 @@ hipError_t launch_cd_lattice_tkeys(int nb, int kd, const double* Ht, const CbTab
 hipError_t launch_cd_lattice_query(int64_t m, int64_t n, int64_t b, int bl, int kd, const double* Gt,
                                    const double* Ht, const CbTables& cb, const float* a, const int32_t* codes,
                                    uint32_t* qf, hipStream_t st);
+// rows / rcount: the rows to run, by list position (nullptr: all m rows);
+// lastmv[i] receives `step` (sweep * B + block) when row i moves.
 hipError_t launch_cd_lattice_update(int64_t m, int64_t n, int64_t b, int bl, int kd, double* Gt, const double* Ht,
                                     const CbTables& cb, const float* a, int32_t* codes, double* Delta,
                                     int32_t* changes, const float* part_s, const int32_t* part_i, uint32_t* qf,
+                                    const int32_t* rows, const int32_t* rcount, int32_t* lastmv, int32_t step,
                                     hipStream_t st);
+// The rows with lastmv > thresh (the rows a tile starting at step thresh + B
+// must run) into rows / count; the others' tile moves (Delta, m x kd) zeroed.
+hipError_t launch_cd_tile_rows(const int32_t* lastmv, int64_t m, int64_t thresh, int kd, int32_t* rows,
+                               int32_t* count, double* Delta, hipStream_t st);
 int cd_lattice_slices(int Kpad);
 // The scoring pass alone (codeword slices x row groups -> part_s / part_i,
 // both [slices][m][2]).  bounded: only scores below the rows' acceptance
 // bounds (after the query fragments in qf) are candidates; otherwise every
 // codeword is (the greedy comparator's queries carry no bound).
 hipError_t launch_cd_lattice_score(int64_t m, int bl, const uint32_t* tk, const CbTables& cb, const uint32_t* qf,
-                                   bool bounded, float* part_s, int32_t* part_i, hipStream_t st,
-                                   hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+                                   bool bounded, const int32_t* rows, const int32_t* rcount, float* part_s,
+                                   int32_t* part_i, hipStream_t st, hipEvent_t t0 = nullptr,
+                                   hipEvent_t t1 = nullptr);
 
 // ------------------------------------------------ sequential greedy (G3) ----
 // Lam (n x n float64, lower) with H + delta I = Lam^T Lam from VS (n x r,
