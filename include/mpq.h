@@ -399,6 +399,9 @@ int mpq_objective(const float* W, int64_t m, int64_t n, const float* s, const fl
 #define MPQ_PROBE_VALU_F64  2  /* v_fma_f64, 8 independent chains per lane */
 #define MPQ_PROBE_EXP_F32   3  /* v_exp_f32, 8 independent chains per lane */
 #define MPQ_PROBE_HBM_COPY  4  /* 16-byte loads and stores streaming through HBM */
+#define MPQ_PROBE_MFMA_I8   5  /* v_mfma_i32_16x16x64_i8, 16 independent accumulators per wave, on
+                                  uniformly random operand bytes that change every instruction
+                                  (operations = 2 x 16 x 16 x 64 per instruction) */
 int mpq_probe_rate(int kind, void* scratch, size_t scratch_bytes, double* rate, void* stream);
 
 /*

@@ -233,14 +233,14 @@ def e8dp_transitions(cb) -> int:
     return int(load_library().mpq_e8dp_transitions(E.ctypes.data_as(ctypes.c_void_p), E.shape[0]))
 
 
-PROBE_KINDS = {"mfma_bf16": 0, "mfma_f64": 1, "valu_f64": 2, "exp_f32": 3, "hbm_copy": 4}
+PROBE_KINDS = {"mfma_bf16": 0, "mfma_f64": 1, "valu_f64": 2, "exp_f32": 3, "hbm_copy": 4, "mfma_i8": 5}
 
 
 def probe_rate(kind: str, scratch=None) -> float:
     """Achievable rate of one instruction or of an HBM copy on this GPU
     (mpq_probe_rate): flop/s for "mfma_bf16", "mfma_f64" and "valu_f64",
-    lane operations/s for "exp_f32", bytes read + written per second for
-    "hbm_copy".  `scratch` (a device tensor, contents overwritten) defaults
+    int8 operations/s for "mfma_i8" (random operand bytes), lane operations/s
+    for "exp_f32", bytes read + written per second for "hbm_copy".  `scratch` (a device tensor, contents overwritten) defaults
     to a fresh 2 GiB buffer."""
     import torch
     if kind not in PROBE_KINDS:

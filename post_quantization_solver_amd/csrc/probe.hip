@@ -12,12 +12,13 @@
 namespace mpq {
 
 typedef double v4d __attribute__((ext_vector_type(4)));
+typedef int v4i_t __attribute__((ext_vector_type(4)));
 
 constexpr int PROBE_WG = 256;        // threads per workgroup
 constexpr int PROBE_GRID = 2048;     // workgroups: 8 per CU on 256 CUs
 constexpr size_t PROBE_SINK = (size_t)PROBE_GRID * PROBE_WG * sizeof(double);
 constexpr size_t PROBE_MIN_SCRATCH = (size_t)8 << 20;   // >= 4 KiB of operands + PROBE_SINK
-static_assert(PROBE_MIN_SCRATCH >= PROBE_SINK + 4096, "probe scratch");
+static_assert(PROBE_MIN_SCRATCH >= PROBE_SINK + 4096 + 8192, "probe scratch");
 constexpr size_t PROBE_MIN_COPY = (size_t)256 << 20;
 constexpr size_t PROBE_MAX_COPY = (size_t)2 << 30;
 
@@ -44,6 +45,47 @@ __global__ __launch_bounds__(PROBE_WG) void probe_mfma_bf16_kernel(const v4u* __
     for (int i = 0; i < 16; ++i) acc[i] = mfma_bf16_16x16x32(a, b, acc[i]);
   }
   float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+  sink[blockIdx.x * PROBE_WG + threadIdx.x] = s;
+}
+
+// Uniformly random bytes (the int8 probe's operands: the digit planes of the
+// float64-accurate products are balanced base-256 digits, i.e. close to
+// uniform bytes), 1024 words.
+__global__ void probe_init_i8_kernel(uint32_t* w) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t x = i * 2654435761u + 0x9e3779b9u;
+  x ^= x >> 15;
+  x *= 0x2c1b3c6du;
+  x ^= x >> 12;
+  x *= 0x297a2d39u;
+  x ^= x >> 15;
+  w[i] = x;
+}
+
+// v_mfma_i32_16x16x64_i8 (the float64-accurate digit products): 16
+// independent accumulators per wave, the operands cycling through 4 x 4
+// random register pairs so that every instruction sees new bytes (the MFMA
+// draws more power, and on this GPU runs slower, on changing random bytes
+// than on repeated ones).
+__global__ __launch_bounds__(PROBE_WG) void probe_mfma_i8_kernel(const v4i_t* __restrict__ src, int* __restrict__ sink,
+                                                               int iters) {
+  const int lane = threadIdx.x & 63;
+  v4i_t a[4], b[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    a[k] = src[k * 64 + lane];
+    b[k] = src[256 + k * 64 + lane];
+  }
+  v4i_t acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = (v4i_t){0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i & 3], b[i >> 2], acc[i], 0, 0, 0);
+  }
+  int s = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
   sink[blockIdx.x * PROBE_WG + threadIdx.x] = s;
@@ -117,7 +159,7 @@ using namespace mpq;
 
 extern "C" int mpq_probe_rate(int kind, void* scratch, size_t scratch_bytes, double* rate, void* stream) {
   if (!scratch || !rate) return MPQ_ENULL;
-  if (kind < MPQ_PROBE_MFMA_BF16 || kind > MPQ_PROBE_HBM_COPY) return MPQ_EPARAM;
+  if (kind < MPQ_PROBE_MFMA_BF16 || kind > MPQ_PROBE_MFMA_I8) return MPQ_EPARAM;
   const size_t need = kind == MPQ_PROBE_HBM_COPY ? PROBE_MIN_COPY : PROBE_MIN_SCRATCH;
   if (scratch_bytes < need || (reinterpret_cast<uintptr_t>(scratch) & 255u) != 0) return MPQ_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -135,6 +177,9 @@ extern "C" int mpq_probe_rate(int kind, void* scratch, size_t scratch_bytes, dou
   float best_ms = INFINITY;
   const size_t half = std::min(scratch_bytes / 2, PROBE_MAX_COPY / 2) & ~(size_t)255;
   hipLaunchKernelGGL(probe_init_kernel, dim3(1), dim3(1024), 0, st, ops);
+  // the int8 probe's random operands (512 v4i = 8 KiB) follow the sink
+  uint32_t* ops_i8 = reinterpret_cast<uint32_t*>(base + 4096 + PROBE_SINK);
+  if (kind == MPQ_PROBE_MFMA_I8) hipLaunchKernelGGL(probe_init_i8_kernel, dim3(2), dim3(1024), 0, st, ops_i8);
   for (int rep = 0; rep < 4 && rc == MPQ_OK; ++rep) {
     if (hipEventRecord(e0, st) != hipSuccess) { rc = MPQ_EHIP; break; }
     switch (kind) {
@@ -164,6 +209,13 @@ extern "C" int mpq_probe_rate(int kind, void* scratch, size_t scratch_bytes, dou
         hipLaunchKernelGGL(probe_exp_f32_kernel, dim3(PROBE_GRID), dim3(PROBE_WG), 0, st,
                            reinterpret_cast<const float*>(ops), static_cast<float*>(sink), iters);
         work = (double)PROBE_GRID * PROBE_WG * iters * 8;
+        break;
+      }
+      case MPQ_PROBE_MFMA_I8: {
+        const int iters = 2048;
+        hipLaunchKernelGGL(probe_mfma_i8_kernel, dim3(PROBE_GRID), dim3(PROBE_WG), 0, st,
+                           reinterpret_cast<const v4i_t*>(ops_i8), static_cast<int*>(sink), iters);
+        work = (double)PROBE_GRID * (PROBE_WG / 64) * iters * 16 * (16.0 * 16.0 * 64.0 * 2.0);
         break;
       }
       default: {   // MPQ_PROBE_HBM_COPY

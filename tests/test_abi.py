@@ -198,7 +198,7 @@ def test_probe_argument_validation(lib):
     assert lib.mpq_probe_rate(0, None, 1 << 30, C.byref(out), None) == -1          # MPQ_ENULL
     fake = C.c_void_p(1 << 20)                                                   # never dereferenced
     assert lib.mpq_probe_rate(0, fake, 1 << 30, None, None) == -1
-    assert lib.mpq_probe_rate(5, fake, 1 << 30, C.byref(out), None) == -3        # MPQ_EPARAM
+    assert lib.mpq_probe_rate(6, fake, 1 << 30, C.byref(out), None) == -3        # MPQ_EPARAM
     assert lib.mpq_probe_rate(-1, fake, 1 << 30, C.byref(out), None) == -3
     assert lib.mpq_probe_rate(0, fake, 1 << 20, C.byref(out), None) == -5        # MPQ_EWORKSPACE: < 8 MiB
     assert lib.mpq_probe_rate(4, fake, 128 << 20, C.byref(out), None) == -5      # copy needs 256 MiB

@@ -6,7 +6,7 @@ import pytest
 pytestmark = pytest.mark.gpu
 
 VENDOR = {"mfma_bf16": 2.5e15, "mfma_f64": 78.6e12, "valu_f64": 78.6e12, "exp_f32": 256 * 4 * 16 * 2.4e9,
-          "hbm_copy": 8.0e12}
+          "hbm_copy": 8.0e12, "mfma_i8": 5.0e15}
 
 
 @pytest.mark.parametrize("kind", sorted(VENDOR))
