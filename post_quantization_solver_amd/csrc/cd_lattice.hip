@@ -10,18 +10,19 @@
 // cd_score_kernel evaluates score(e) for every codeword with one bf16 MFMA per
 // 16 x 16 (codeword x row) tile -- key slots [e | e | e | t terms], query
 // slots [-q hi | -q mid | -q lo | a^2 terms], all products exact, the sums
-// in float32 -- and reports two candidates per (row, codeword slice): the
-// slice's least tagged score (the float32 score with its 3 low mantissa bits
-// replaced by the codeword's position in a group of 8, so ranks can move by
-// up to 7 ulp) and the least of the other three lane-bests of that row (a
-// near-best codeword, not necessarily the slice's second-smallest score).  cd_update_kernel takes the top two of all
-// slices' candidates by (float32 score, index), re-evaluates dF of both
-// finalists exactly in float64 (the tile gradient, H and the residual are
-// float64) and moves the block to the lesser one (ties: lower index) only on
-// a strict decrease.  The float32 scores therefore only choose which two
-// codewords are compared exactly; a codeword whose float32 score lies within
-// the float32 rounding of the row's minimum but is not a finalist is not
-// considered.
+// in float32 -- and reports two candidates per (row, codeword slice) among
+// the codewords whose score lies below the row's acceptance bound (see
+// cd_query_write): the slice's float32 argmin (ties: lowest index) and the
+// least of the row's other three lane-bests (a near-best codeword, not
+// necessarily the slice's second-smallest score).  cd_update_kernel takes the
+// top two of all slices' candidates by (float32 score, index), re-evaluates
+// dF of both finalists exactly in float64 (the tile gradient, H and the
+// residual are float64) and moves the block to the lesser one (ties: lower
+// index) only on a strict decrease.  The float32 scores therefore only choose
+// which two codewords are compared exactly: the float32 argmin is always a
+// finalist (so exact ties go to the lowest index), while a codeword whose
+// float32 score lies within the float32 rounding of the minimum but is not a
+// finalist is not considered.
 #include <math.h>
 #include <hip/hip_ext.h>
 #include "mpq_device.h"
@@ -81,12 +82,12 @@ __global__ __launch_bounds__(256) void cd_tkeys_kernel(int kd, const double* __r
 // -sum_p e_x[p] a (a (G e_x)[p] / 2 + g[p]) is the current codeword's score
 // in float64 and eps bounds, for every codeword e of norm <= R, the gap
 // between the float32 score the MFMA computes (fp32 rounding of a^2, of t(e)
-// as computed from the float32 G, of q, the float32 sum of the 30 exact
-// products, and the 3-bit position tag) and the exact score:
+// as computed from the float32 G, of q, and the float32 sum of the 30 exact
+// products) and the exact score:
 //   eps = CD_TAU_ULPS 2^-24 (a^2 R^2 max_p sum_q |G_pq| / 2 + R ||q||) + 1e-30.
 // A codeword with exact score below S(e_x) (a strict decrease of F) thus has
-// a tagged float32 score below tau; the score kernel reports only such
-// codewords, and a row with none keeps its codeword.
+// a float32 score below tau; the score kernel reports only such codewords,
+// and a row with none keeps its codeword.
 constexpr double CD_TAU_ULPS = 128.0;
 __device__ __forceinline__ void cd_query_write(int lane, int64_t i, double ge, double gp, double exp_, double grow,
                                                double ai, float rmax, uint32_t* __restrict__ qf,
@@ -141,13 +142,6 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_query_kernel(int64_t m, int
                rmaxp[0], qf, tau);
 }
 
-// A score with its 3 low mantissa bits replaced by the codeword's position
-// (step parity, v) in the lane's 8 candidates of a step pair (a change of at
-// most 7 ulp): one minimum then ranks them and names the winner's position.
-__device__ __forceinline__ float tag3(float x, uint32_t v) {
-  return __uint_as_float((__float_as_uint(x) & 0xfffffff8u) | v);
-}
-
 // grid: (slices, row groups).  part_s / part_i: [slices][list position][2] (best, second).
 // The float32 scores only rank candidates; the update kernel re-evaluates the
 // two best of every slice exactly in float64.
@@ -176,7 +170,7 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
   // (loaded first, so that they arrive while the keys are staged)
   v4u qop[4];
   float best[4];
-  int bst[4];
+  int bpos[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t x = row_base + q * 16 + j;   // list position
@@ -185,7 +179,7 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
     qop[q] = valid ? qf[i * 4 + g] : (v4u){0u, 0u, 0u, 0u};
     // only scores below the row's bound are candidates (no bound: every score)
     best[q] = valid ? (tau ? tau[i] : INFINITY) : -INFINITY;
-    bst[q] = -1;
+    bpos[q] = -1;
   }
 
   // key fragments of this slice: lanes g < 3 carry e, lanes g = 3 the t(e)
@@ -213,44 +207,40 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
   // row j, two steps st = 2 sp, 2 sp + 1 at a time (ncw / 16 is even: Kpad is
   // a multiple of 128).  The running best starts at the row's bound tau, so
   // a pair's eight scores usually all lie above it: the common path is their
-  // minimum (v_minimum3_f32 x 3) and one compare.  Only when a lane of the
-  // wave sees a score below its running best does the wave tag the pair's
-  // scores (3 low mantissa bits := position, a change of at most 7 ulp, so
-  // one minimum ranks them and names the winner) and record the pair where
-  // the lane's best strictly decreased.
+  // minimum (v_minimum3_f32 x 3) and one compare per row subtile.  Only when
+  // a lane of the wave sees a score below its running best does the wave walk
+  // that subtile's eight scores in codeword order, keeping a score and its
+  // position only when strictly below the running best: the lane's candidate
+  // is its least float32 score, ties to the lowest index.
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
   const v4u* kq = reinterpret_cast<const v4u*>(lds_key);
   auto pair_step = [&](int sp) {
     const v4u k0 = kq[(2 * sp) * 64 + lane];
     const v4u k1 = kq[(2 * sp + 1) * 64 + lane];
     // the four row subtiles' tiles first (eight MFMAs back to back), then
-    // their minima and one wave-uniform branch for all four
+    // each subtile's minimum and its wave-uniform branch
     v4f s0[4], s1[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       s0[q] = mfma_bf16_16x16x32(k0, qop[q], zero4);
       s1[q] = mfma_bf16_16x16x32(k1, qop[q], zero4);
     }
-    uint32_t any = 0u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(s0[q][0], s0[q][1]), s0[q][2]);
       mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, s0[q][3]), s1[q][0]);
       mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, s1[q][1]), s1[q][2]);
       mn = __builtin_elementwise_minimum(mn, s1[q][3]);
-      any |= (uint32_t)(mn < best[q]);   // no short circuit: one compare per subtile
-    }
-    if (__builtin_amdgcn_ballot_w64(any != 0u) != 0) {
+      if (__builtin_amdgcn_ballot_w64(mn < best[q]) != 0) {
+        // positions within the slice, relative to this lane's 4 g (wave-uniform)
+        const int p0 = 32 * sp;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float tm = __builtin_elementwise_minimum(
-            __builtin_elementwise_minimum(tag3(s0[q][0], 0u), tag3(s0[q][1], 1u)), tag3(s0[q][2], 2u));
-        tm = __builtin_elementwise_minimum(__builtin_elementwise_minimum(tm, tag3(s0[q][3], 3u)), tag3(s1[q][0], 4u));
-        tm = __builtin_elementwise_minimum(__builtin_elementwise_minimum(tm, tag3(s1[q][1], 5u)), tag3(s1[q][2], 6u));
-        tm = __builtin_elementwise_minimum(tm, tag3(s1[q][3], 7u));
-        const bool better = tm < best[q];
-        bst[q] = better ? sp : bst[q];
-        best[q] = better ? tm : best[q];
+        for (int v = 0; v < 8; ++v) {
+          const float sv = v < 4 ? s0[q][v] : s1[q][v - 4];
+          const bool lt = sv < best[q];
+          best[q] = lt ? sv : best[q];
+          bpos[q] = lt ? p0 + (v >> 2) * 16 + (v & 3) : bpos[q];
+        }
       }
     }
   };
@@ -260,15 +250,13 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
     pair_step(sp + 1);
   }
   // top 2 of the row's four lane-bests (lanes j, j+16, j+32, j+48), ordered
-  // by (tagged score, index); a lane without a score below tau has none.
-  // part_s / part_i are [slice][m] so that the 16 rows of a subtile store
-  // one contiguous segment.
+  // by (score, index); a lane without a score below tau has none.
+  // part_s / part_i are [slice][list position] so that the 16 rows of a
+  // subtile store one contiguous segment.
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t tg = __float_as_uint(best[q]) & 7u;
-    const bool found = bst[q] >= 0;
-    const int idx = found ? cw_base + (2 * bst[q] + (int)(tg >> 2)) * 16 + 4 * g + (int)(tg & 3u) : 0x7fffffff;
-    Cand c1 = {found ? best[q] : INFINITY, idx};
+    const bool found = bpos[q] >= 0;
+    Cand c1 = {found ? best[q] : INFINITY, found ? cw_base + 4 * g + bpos[q] : 0x7fffffff};
     Cand c2 = {INFINITY, 0x7fffffff};
 #pragma unroll
     for (int msk = 16; msk <= 32; msk <<= 1) {
