@@ -27,7 +27,7 @@ struct E8Prefix {
   int L2[8];     // 2 L (integers)
 };
 
-__host__ __device__ inline int e8_cmp(int u2, int l2) { return u2 < l2 ? 0 : (u2 == l2 ? 1 : 2); }
+__host__ __device__ constexpr int e8_cmp(int u2, int l2) { return u2 < l2 ? 0 : (u2 == l2 ? 1 : 2); }
 
 // Successor of state st after coordinate p (1-based) takes value index k, or -1.
 __host__ __device__ inline int e8_succ(int st, int p, int k, const E8Prefix& P) {

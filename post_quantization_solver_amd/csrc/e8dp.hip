@@ -203,11 +203,27 @@ constexpr int e8_ctrl(bool half, int p, int k, bool fwd) {
 // Keeps the factors of a pass from being held in registers until the next one.
 __device__ __forceinline__ void reload_barrier() { asm volatile("" ::: "memory"); }
 
+// The last point of the 2^16-point prefix (twice its coordinates; norm 12):
+// the codebook size of the pages' lattice codebook.  When a prefix's last
+// point is this one (checked on the host), the passes below take it as a
+// compile-time constant, so every comparison of a value with it is decided
+// at compile time and the "equal" chain's moves cost no selects.
+constexpr int E8_FIX_QLAST = 12;
+constexpr int E8_FIX_L2[8] = {-3, 1, 3, -5, -1, 1, -1, 1};
+static_assert((E8_FIX_L2[0] & 1) != 0, "e8dp_kernel<true> runs the half class as the last point's class");
+bool e8_prefix_is_fixed(const E8Prefix& P) {
+  if (P.qlast != E8_FIX_QLAST) return false;
+  for (int j = 0; j < 8; ++j)
+    if (P.L2[j] != E8_FIX_L2[j]) return false;
+  return true;
+}
+
 // One class: forward pass storing F_0..F_7, then the backward pass with the
 // moments of every coordinate accumulated per lane.  LCLASS: the codebook's
 // last point is in this class, so the lexicographic "equal" chain runs the
-// whole length (otherwise it ends after the first coordinate).
-template <bool HALF, bool LCLASS>
+// whole length (otherwise it ends after the first coordinate).  FIX: the
+// last point is E8_FIX_L2 (compile-time comparisons).
+template <bool HALF, bool LCLASS, bool FIX = false>
 __device__ __forceinline__ void e8_class_pass(const int j, const E8RowCoef& cf, const E8Prefix& P, double (&m1)[8],
                                               double& m2, double& z) {
   constexpr int NK = HALF ? 6 : 7;
@@ -234,7 +250,15 @@ __device__ __forceinline__ void e8_class_pass(const int j, const E8RowCoef& cf, 
       if constexpr (HALF && e8_qi_step(k) == 3) g *= mf3;
       nl = fma(g, row_read<CT>(Fl[c]), nl);
       ng = fma(g, row_read<CT>(Fg[c]), ng);
-      if constexpr (live) {
+      if constexpr (live && FIX) {
+        constexpr int ck = e8_cmp(e8_twice_value(HALF, k), E8_FIX_L2[c]);
+        if constexpr (ck == 0)
+          nl = fma(g, row_read<CT>(Fe[c]), nl);
+        else if constexpr (ck == 1)
+          ne = fma(g, row_read<CT>(Fe[c]), ne);
+        else
+          ng = fma(g, row_read<CT>(Fe[c]), ng);
+      } else if constexpr (live) {
         const int ck = e8_cmp(e8_twice_value(HALF, k), l2);
         const double w = g * row_read<CT>(Fe[c]);
         nl = fma(w, ck == 0 ? 1.0 : 0.0, nl);
@@ -273,7 +297,18 @@ __device__ __forceinline__ void e8_class_pass(const int j, const E8RowCoef& cf, 
       nl = fma(g, sl, nl);
       ng = fma(g, sg, ng);
       double pk = fma(Fl[c], sl, Fg[c] * sg);
-      if constexpr (live) {
+      if constexpr (live && FIX) {
+        constexpr int ck = e8_cmp(e8_twice_value(HALF, k), E8_FIX_L2[c]);
+        double sel;
+        if constexpr (ck == 0)
+          sel = sl;
+        else if constexpr (ck == 1)
+          sel = row_read<CT>(Be);
+        else
+          sel = sg;
+        pk = fma(Fe[c], sel, pk);
+        ne = fma(g, sel, ne);
+      } else if constexpr (live) {
         const int ck = e8_cmp(e8_twice_value(HALF, k), l2);
         const double se = row_read<CT>(Be);
         const double sel = fma(se, ck == 1 ? 1.0 : 0.0, fma(sg, ck == 2 ? 1.0 : 0.0, sl * (ck == 0 ? 1.0 : 0.0)));
@@ -302,6 +337,7 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // Four queries per wave, one per 16-lane row.
+template <bool FIX>
 __global__ __launch_bounds__(64 * E8DP_WAVES) void e8dp_kernel(const double* __restrict__ R1,
                                                    const double* __restrict__ gamma1, int64_t m, int64_t n,
                                                    const float* __restrict__ a, const float* __restrict__ o,
@@ -347,7 +383,11 @@ __global__ __launch_bounds__(64 * E8DP_WAVES) void e8dp_kernel(const double* __r
     wave_sync();
     double m1[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
     double m2 = 0.0, z = 0.0;
-    if (lhalf) {
+    if constexpr (FIX) {   // the fixed last point is a half-integer point
+      e8_class_pass<false, false, true>(j, cf, P, m1, m2, z);
+      reload_barrier();
+      e8_class_pass<true, true, true>(j, cf, P, m1, m2, z);
+    } else if (lhalf) {
       e8_class_pass<false, false>(j, cf, P, m1, m2, z);
       reload_barrier();
       e8_class_pass<true, true>(j, cf, P, m1, m2, z);
@@ -394,8 +434,12 @@ hipError_t launch_denoise_e8dp(const double* R1, const double* gamma1, int64_t m
   const int64_t per_wg = (int64_t)E8DP_WAVES * 4;
   const int64_t wgs = (total + per_wg - 1) / per_wg;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(e8dp_kernel, dim3((unsigned)wgs), dim3(64 * E8DP_WAVES), 0, st, R1, gamma1, m, n, a, o, P, xhat,
-                     vblk, flag + 64, flag);
+  if (e8_prefix_is_fixed(P))
+    hipLaunchKernelGGL(e8dp_kernel<true>, dim3((unsigned)wgs), dim3(64 * E8DP_WAVES), 0, st, R1, gamma1, m, n, a, o, P,
+                       xhat, vblk, flag + 64, flag);
+  else
+    hipLaunchKernelGGL(e8dp_kernel<false>, dim3((unsigned)wgs), dim3(64 * E8DP_WAVES), 0, st, R1, gamma1, m, n, a, o, P,
+                       xhat, vblk, flag + 64, flag);
   return hipGetLastError();
 }
 
