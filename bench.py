@@ -256,6 +256,9 @@ def main():
                     help="skip the extra profiled step that gives the per-group time split (keeps a counter pass "
                          "to one solve's dispatches: rocprofv3 --pmc has crashed in its dispatch interception after "
                          "about 20 000 dispatches in one process)")
+    ap.add_argument("--only", choices=["linear"], default=None,
+                    help="run only two calls of the linear module (mpq_linear_step) on the workload's shapes and "
+                         "exit: a short program with few dispatches for counter passes over the dominant kernels")
     ap.add_argument("--host-qr", action="store_true",
                     help="draw the orthogonal factor V with NumPy's QR on the host instead of rocSOLVER's (e.g. "
                          "under counter collection, where rocSOLVER's QR has crashed the profiled process); "
@@ -300,6 +303,17 @@ def main():
         f"inputs in {time.perf_counter() - t0:.1f} s")
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
     W, s, V, a, o = t(L.W), t(L.s), t(L.V), t(L.a), t(L.o)
+    if args.only == "linear":
+        # the linear module alone on a synthetic extrinsic message (r2 near w)
+        gen = torch.Generator(device=dev).manual_seed(7)
+        R2 = W.double() + 0.01 * torch.randn(W.shape, dtype=torch.float64, device=dev, generator=gen)
+        g2 = torch.full((L.m,), 10.0, dtype=torch.float64, device=dev)
+        beta = torch.ones(L.m, dtype=torch.float64, device=dev)
+        for k in range(2):
+            mpq.linear_step(R2, g2, beta, W, s, V, damping=L.damping)
+            torch.cuda.synchronize()
+            log(f"[bench] linear module call {k + 1}/2 done")
+        return
     ws = torch.empty(mpq.workspace_bytes(L.m, L.n, L.r, L.K, L.d), dtype=torch.uint8, device=dev)
     kw = dict(T_vamp=L.T_vamp, n_cd=L.n_cd, damping=L.damping, workspace=ws, group=L.group)
     cb = mpq.prepare_codebook(L.E, dev)   # the codebook's device tables, once per layer
