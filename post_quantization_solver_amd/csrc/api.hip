@@ -559,12 +559,15 @@ int run_prologue(Ctx& c, const float* W, const float* s, const float* a, const f
 //   r1' = r2 + coef V z                                         (GEMM 2)
 // gamma1 is read for the frozen-row test (+inf) and overwritten with gamma1'.
 int run_linear(Ctx& c, const float* W, const float* s, const float* V, double* R1, double* gamma1, double* beta,
-               double damping, int fixed_beta) {
+               double damping, int fixed_beta, bool d2_exp_ready = false) {
   const Layout& L = c.L;
   double* D2 = c.d(R_R2);
   TIMED(c, MPQ_PROF_EXTRINSIC, launch_beta_lin(L.m, gamma1, beta, c.betalin(), c.gamma2(), c.st));
   if (c.digits) {
-    TIMED(c, MPQ_PROF_SPLIT, launch_digit_split(D2, L.m, L.n, L.n, c.pi(R_DEA), c.dp(R_DPA), c.st));
+    if (d2_exp_ready)   // the extrinsic kernel wrote D2's row exponents
+      TIMED(c, MPQ_PROF_SPLIT, launch_digit_split_planes(D2, L.m, L.n, L.n, c.pi(R_DEA), c.dp(R_DPA), c.st));
+    else
+      TIMED(c, MPQ_PROF_SPLIT, launch_digit_split(D2, L.m, L.n, L.n, c.pi(R_DEA), c.dp(R_DPA), c.st));
     DigitGemmArgs g1 = digit_args(c, (int)L.m, (int)L.r, (int)L.n, R_DPVT, R_DEVT);
     g1.C = c.d(R_Z); g1.ldc = L.r;
     g1.s = s;
@@ -626,11 +629,12 @@ int run_iteration(Ctx& c, const float* W, double* R1, double* gamma1, double* be
   if (xhat_out) TIMED(c, MPQ_PROF_OTHER, launch_copy_f64(X1, xhat_out, L.m * L.n, c.st));
   TIMED(c, MPQ_PROF_EXTRINSIC,
         launch_extrinsic(R1, X1, c.d(R_VBLK), W, L.m, L.n, L.B, a, c.cb.G, gamma1, c.eps, c.d(R_R2), c.gamma2(),
-                         eta1_out ? eta1_out : c.eta1(), fallback_out, c.fb_count, c.st));
+                         eta1_out ? eta1_out : c.eta1(), fallback_out, c.fb_count,
+                         c.digits ? c.pi(R_DEA) : nullptr, c.st));
   if (gamma2_out) TIMED(c, MPQ_PROF_OTHER, launch_copy_f64(c.gamma2(), gamma2_out, L.m, c.st));
   if (trace_g2) TIMED(c, MPQ_PROF_OTHER, launch_record(c.gamma2(), L.m, trace_g2, ld_g2, col, c.st));
   if (r2_out) TIMED(c, MPQ_PROF_OTHER, launch_w_minus(W, c.d(R_R2), r2_out, L.m * L.n, c.st));
-  return run_linear(c, W, s, V, R1, gamma1, beta, damping, fixed_beta);
+  return run_linear(c, W, s, V, R1, gamma1, beta, damping, fixed_beta, c.digits);
 }
 
 // H = VS VS^T (float64, n x n) on the tiles that touch the lower triangle,

@@ -405,12 +405,16 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
   float ec[2][8], ecp[2], eck[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const bool ok = cands[c] != 0x7fffffff;
-    const int64_t base_c = ok ? (int64_t)cands[c] * 8 : 0;
-    ecp[c] = e32[base_c + p];
-    eck[c] = e32[base_c + k];
+    ecp[c] = eck[c] = 0.f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) ec[c][q] = e32[base_c + q];
+    for (int q = 0; q < 8; ++q) ec[c][q] = 0.f;
+    if (cands[c] != 0x7fffffff) {   // uniform over the wave; a row without candidates loads nothing
+      const int64_t base_c = (int64_t)cands[c] * 8;
+      ecp[c] = e32[base_c + p];
+      eck[c] = e32[base_c + k];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ec[c][q] = e32[base_c + q];
+    }
   }
   double bestF = 0.0;
   int bestk = cx, bestc = -1;

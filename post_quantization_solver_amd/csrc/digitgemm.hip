@@ -49,7 +49,6 @@ constexpr int DG_RT = DG_TILE / 16; // row tiles per output tile side
 constexpr int DG_CHUNKS = 2 * DG_RT * DG_S;   // chunks per K step (A and B)
 constexpr int DG_WAVES = 8;
 constexpr int DG_GROUP_M = 8;       // tile rows per group of the tile order
-constexpr int DG_EXP_NONFINITE = INT_MAX;     // row exponent of a row holding NaN or inf
 
 // Bytes of the digit planes of a rows x K operand (row tiles padded to whole
 // output tiles, K to whole steps).
@@ -172,6 +171,15 @@ static hipError_t split(const T* X, int64_t rows, int64_t K, int64_t ld, int32_t
 hipError_t launch_digit_split(const double* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes,
                               hipStream_t st) {
   return split<double>(X, rows, K, ld, E, planes, st);
+}
+hipError_t launch_digit_split_planes(const double* X, int64_t rows, int64_t K, int64_t ld, const int32_t* E,
+                                     uint8_t* planes, hipStream_t st) {
+  if (rows <= 0 || K <= 0) return hipSuccess;
+  const int64_t nrt = (rows + DG_TILE - 1) / DG_TILE * DG_RT;
+  const int64_t nkt = (K + 63) / 64;
+  hipLaunchKernelGGL(digit_split_kernel<double>, dim3((unsigned)((nrt * nkt + 3) / 4)), dim3(256), 0, st, X, rows, K,
+                     ld, E, nrt, nkt, planes);
+  return hipGetLastError();
 }
 hipError_t launch_digit_split_f32(const float* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes,
                                   hipStream_t st) {

@@ -78,7 +78,13 @@ hipError_t launch_digit_split(const double* X, int64_t rows, int64_t K, int64_t 
                               hipStream_t st);
 hipError_t launch_digit_split_f32(const float* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes,
                                   hipStream_t st);
+// The split alone, given the row exponents E (as the split computes them:
+// max_k |X_ik| < 2^E[i], 0 for a zero row, DG_EXP_NONFINITE for a row holding
+// NaN or inf).
+hipError_t launch_digit_split_planes(const double* X, int64_t rows, int64_t K, int64_t ld, const int32_t* E,
+                                     uint8_t* planes, hipStream_t st);
 hipError_t launch_digit_gemm(int epi, const DigitGemmArgs& g, hipStream_t st);
+constexpr int DG_EXP_NONFINITE = 0x7fffffff;   // row exponent of a row holding NaN or inf
 
 // ------------------------------------------------------------ codebook ----
 // Device tables of a prepared codebook (mpq_codebook_prepare).
@@ -119,6 +125,7 @@ hipError_t launch_prologue_finish(int64_t m, int64_t n, int64_t r, const double*
 hipError_t launch_extrinsic(const double* R1, const double* xhat, const double* vblk, const float* W, int64_t m,
                             int64_t n, int64_t B, const float* a, int G, const double* gamma1, double eps,
                             double* D2, double* gamma2, double* eta1, int32_t* fallback, int32_t* fb_count,
+                            int32_t* dexp,
                             hipStream_t st);
 
 // beta M-step + linear-side extrinsic precision.

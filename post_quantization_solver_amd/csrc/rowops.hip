@@ -109,7 +109,7 @@ __global__ __launch_bounds__(ROW_THREADS) void extrinsic_kernel(
     const double* __restrict__ R1, const double* xhat, const double* __restrict__ vblk, const float* __restrict__ W,
     int64_t n, int64_t B, const float* __restrict__ a, int G, const double* __restrict__ gamma1, double eps,
     double* D2, double* __restrict__ gamma2, double* __restrict__ eta1_out, int32_t* __restrict__ fallback,
-    int32_t* __restrict__ fb_count) {
+    int32_t* __restrict__ fb_count, int32_t* __restrict__ dexp) {
   __shared__ double sh[ROW_THREADS];
   const int64_t i = blockIdx.x;
   const int t = threadIdx.x;
@@ -118,46 +118,65 @@ __global__ __launch_bounds__(ROW_THREADS) void extrinsic_kernel(
   const double* xh = xhat + i * n;
   const float* w = W + i * n;
   double* d2 = D2 + i * n;
+  double mx = 0.0;   // max |d2| and whether any entry is not finite (the digit split's row exponent)
+  int bad = 0;
   if (!isfinite(g1)) {
-    for (int64_t j = t; j < n; j += ROW_THREADS) d2[j] = (double)w[j] - r1[j];
+    for (int64_t j = t; j < n; j += ROW_THREADS) {
+      const double v = (double)w[j] - r1[j];
+      d2[j] = v;
+      mx = fmax(mx, fabs(v));
+      bad |= !isfinite(v);
+    }
     if (t == 0) {
       gamma2[i] = INFINITY;
       if (eta1_out) eta1_out[i] = INFINITY;
       if (fallback) fallback[i] = 0;
     }
-    return;
+  } else {
+    double part = 0.0;
+    for (int64_t b = t; b < B; b += ROW_THREADS) part += vblk[i * B + b];
+    const double vs = block_sum(part, sh);
+    double amax = 0.0;
+    for (int g = t; g < G; g += ROW_THREADS) amax = fmax(amax, (double)a[i * G + g]);
+    const double ai = G == 1 ? (double)a[i] : block_max(amax, sh);
+    const double floor_v = (double)n * 1e-24 * ai * ai;
+    const double eta1 = (double)n / fmax(vs, floor_v);
+    const bool pass = eta1 > g1 * (1.0 + eps);
+    const double g2 = pass ? eta1 - g1 : eta1;
+    const double ratio = eta1 / g2;
+    for (int64_t j = t; j < n; j += ROW_THREADS) {
+      const double x = xh[j];
+      const double rr = r1[j];
+      const double v = (double)w[j] - (pass ? fma(ratio, x - rr, rr) : x);
+      d2[j] = v;
+      mx = fmax(mx, fabs(v));
+      bad |= !isfinite(v);
+    }
+    if (t == 0) {
+      gamma2[i] = g2;
+      if (eta1_out) eta1_out[i] = eta1;
+      if (fallback) fallback[i] = pass ? 0 : 1;
+      if (fb_count && !pass) fb_count[i] += 1;
+    }
   }
-  double part = 0.0;
-  for (int64_t b = t; b < B; b += ROW_THREADS) part += vblk[i * B + b];
-  const double vs = block_sum(part, sh);
-  double amax = 0.0;
-  for (int g = t; g < G; g += ROW_THREADS) amax = fmax(amax, (double)a[i * G + g]);
-  const double ai = G == 1 ? (double)a[i] : block_max(amax, sh);
-  const double floor_v = (double)n * 1e-24 * ai * ai;
-  const double eta1 = (double)n / fmax(vs, floor_v);
-  const bool pass = eta1 > g1 * (1.0 + eps);
-  const double g2 = pass ? eta1 - g1 : eta1;
-  const double ratio = eta1 / g2;
-  for (int64_t j = t; j < n; j += ROW_THREADS) {
-    const double x = xh[j];
-    const double rr = r1[j];
-    d2[j] = (double)w[j] - (pass ? fma(ratio, x - rr, rr) : x);
-  }
-  if (t == 0) {
-    gamma2[i] = g2;
-    if (eta1_out) eta1_out[i] = eta1;
-    if (fallback) fallback[i] = pass ? 0 : 1;
-    if (fb_count && !pass) fb_count[i] += 1;
+  if (dexp) {   // uniform: every thread reaches the reductions
+    const double M = block_max(mx, sh);
+    const int anybad = __syncthreads_or(bad);
+    if (t == 0) {
+      int e = 0;
+      if (M > 0.0) (void)frexp(M, &e);   // M = f 2^e, f in [0.5, 1)
+      dexp[i] = anybad ? DG_EXP_NONFINITE : e;
+    }
   }
 }
 
 hipError_t launch_extrinsic(const double* R1, const double* xhat, const double* vblk, const float* W, int64_t m,
                             int64_t n, int64_t B, const float* a, int G, const double* gamma1, double eps,
                             double* D2, double* gamma2, double* eta1, int32_t* fallback, int32_t* fb_count,
-                            hipStream_t st) {
+                            int32_t* dexp, hipStream_t st) {
   if (m <= 0) return hipSuccess;
   hipLaunchKernelGGL(extrinsic_kernel, dim3((unsigned)m), dim3(ROW_THREADS), 0, st, R1, xhat, vblk, W, n, B, a, G,
-                     gamma1, eps, D2, gamma2, eta1, fallback, fb_count);
+                     gamma1, eps, D2, gamma2, eta1, fallback, fb_count, dexp);
   return hipGetLastError();
 }
 
