@@ -329,6 +329,217 @@ __device__ __forceinline__ void e8_class_pass(const int j, const E8RowCoef& cf, 
   });
 }
 
+// DPP control of a transition whose target is moved `extra` further along the
+// partial norm (Q + extra lanes in the integer class, Qi + extra in the half
+// class, same s): row shifts by x^2 + extra, or the flips' rotations by
+// 8 +- (d + extra).  Only for extra >= 1, where no shift is the identity.
+constexpr int e8_ctrl_ext(bool half, int p, int k, bool fwd, int extra) {
+  if (!half) {
+    const int a2 = (k - 3) * (k - 3) + extra;
+    return (fwd ? DPP_ROW_SHR : DPP_ROW_SHL) + a2;
+  }
+  const int u = 2 * k - 5, d = e8_qi_step(k) + extra;
+  const bool flip = (p & 1) ? ((u & 3) == 3) : ((u & 3) == 1);
+  if (!flip) return (fwd ? DPP_ROW_SHR : DPP_ROW_SHL) + d;
+  return DPP_ROW_ROR + ((fwd ? 8 + d : 8 - d) & 15);
+}
+
+// Per-query table of the fixed-prefix kernel, 32 words per coordinate c:
+//   [0, 7)    integer class; c = 0: the factors g of x = k - 3; c >= 1:
+//             [0, 4) gs_x = g(x) + g(-x) (gs_0 = g(0)) and [4, 7)
+//             gx_x = x (g(x) - g(-x)), x = 1, 2, 3
+//   [7, 13)   half class: the factors g of x = k - 5/2
+//   13        r'_c
+//   [14, 18)  integer class, c >= 1: gq_x = g(x) (x - r')^2 + g(-x) (x + r')^2
+//   [18, 24)  half class: g x;  [24, 30) half class: g (x - r')^2
+// The padding puts the four rows of a wave in different banks.
+struct E8FixCoef {
+  double c[8][32];
+  double pad[2];
+};
+
+// The passes below regroup the sums of the three-chain pass (e8_class_pass)
+// for the fixed last point (E8_FIX_L2, a half-integer point of norm 12):
+//  * "below" and "above" chains merged: a prefix above L's is accepted iff
+//    its final norm is below 12, i.e. exactly the below chain's acceptance
+//    from a partial norm one step larger (Q + 2, or Qi + 1; s unchanged).  The
+//    transitions do not depend on the partial norm, so storing every "above"
+//    prefix one step up turns both into one chain with the below chain's
+//    acceptance: F' (q) = F_below(q) + F_above(q - step) forward and the below
+//    chain's B backward (B_above(q) = B(q + step)).  Only the "equal" chain
+//    (one lane per position) stays separate; its moves into the above chain
+//    land one step up.
+//  * moments per lane: coordinate c's terms at a lane are F_c (or the equal
+//    chain's F) times sums over the values of g, g x and g (x - r')^2 against
+//    the shifted B, so one sum per factor table replaces per-value products.
+
+// The merge needs "norm < N" to equal "norm + step <= N" on valid prefixes,
+// also at the largest partial norm a lane holds (12): N even and at most 12.
+static_assert(E8_FIX_QLAST % 2 == 0 && E8_FIX_QLAST <= 12, "merged chains need an even last norm of at most 12");
+
+// Integer class.  No integer prefix equals L's (a half-integer point) past
+// the empty one, so the equal chain lives only at the first coordinate, and
+// from the second on the merged chain is all there is.  Values x and -x move Q
+// by the same x^2: a step is four row shifts (0, 1, 4, 9) with pair sums.
+__device__ __forceinline__ void e8_int_pass_fix(const int j, const E8FixCoef& cf, double (&m1)[8], double& m2,
+                                                double& z) {
+  const double e0 = j == 0 ? 1.0 : 0.0;   // the empty prefix, equal to L's
+  double F[8];
+  F[0] = 0.0;
+  {   // first coordinate: below L's (x <= -2) in place, above it one step up
+    double nf = 0.0;
+    static_for<0, 7>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int ck = e8_cmp(e8_twice_value(false, k), E8_FIX_L2[0]);
+      static_assert(ck != 1, "an integer value never equals a half-integer one");
+      constexpr int CT = ck == 0 ? e8_ctrl(false, 1, k, true) : e8_ctrl_ext(false, 1, k, true, 2);
+      nf = fma(cf.c[0][k], row_read<CT>(e0), nf);
+    });
+    F[1] = nf;
+  }
+  static_for<2, 8>([&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = decltype(pc)::value, c = p - 1;
+    const double* t = cf.c[c];
+    const double f = F[c];
+    F[p] = fma(t[3], row_read<DPP_ROW_SHR + 9>(f),
+               fma(t[2], row_read<DPP_ROW_SHR + 4>(f), fma(t[1], row_read<DPP_ROW_SHR + 1>(f), t[0] * f)));
+  });
+  reload_barrier();
+  // accepted: an even Q (the coordinate sum is even) of at most the last norm
+  double Bm = (j & 1) == 0 && j <= E8_FIX_QLAST ? 1.0 : 0.0;
+  static_for<0, 7>([&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = 8 - decltype(pc)::value, c = p - 1;
+    const double* t = cf.c[c];
+    const double s1 = row_read<DPP_ROW_SHL + 1>(Bm), s4 = row_read<DPP_ROW_SHL + 4>(Bm),
+                 s9 = row_read<DPP_ROW_SHL + 9>(Bm);
+    const double nb = fma(t[3], s9, fma(t[2], s4, fma(t[1], s1, t[0] * Bm)));
+    const double n1 = fma(t[6], s9, fma(t[5], s4, t[4] * s1));
+    const double n2 = fma(t[17], s9, fma(t[16], s4, fma(t[15], s1, t[14] * Bm)));
+    m1[c] = fma(F[c], n1, m1[c]);
+    m2 = fma(F[c], n2, m2);
+    Bm = nb;
+  });
+  {   // first coordinate: F_0 is the equal chain's start alone
+    const double r = cf.c[0][13];
+    double ne = 0.0, ne1 = 0.0, ne2 = 0.0;
+    static_for<0, 7>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int ck = e8_cmp(e8_twice_value(false, k), E8_FIX_L2[0]);
+      constexpr int CT = ck == 0 ? e8_ctrl(false, 1, k, false) : e8_ctrl_ext(false, 1, k, false, 2);
+      constexpr double x = (double)(k - 3);
+      const double w = cf.c[0][k] * row_read<CT>(Bm), dx = x - r;
+      ne += w;
+      ne1 = fma(x, w, ne1);
+      ne2 = fma(dx * dx, w, ne2);
+    });
+    m1[0] = fma(e0, ne1, m1[0]);
+    m2 = fma(e0, ne2, m2);
+    z = fma(e0, ne, z);
+  }
+}
+
+// Half class, L's class: merged chain plus the equal chain at every step.
+__device__ __forceinline__ void e8_half_pass_fix(const int j, const E8FixCoef& cf, double (&m1)[8], double& m2,
+                                                 double& z) {
+  const int qi = j & 7;
+  // a move of Qi by d stays inside the 6 valid slots of the lane's s block:
+  // backward reads need qi + d <= 5, forward reads qi >= d, and forward reads
+  // one step up qi >= d + 1
+  const double mb1 = qi <= 4 ? 1.0 : 0.0, mb3 = qi <= 2 ? 1.0 : 0.0;
+  const double mf1 = qi >= 1 ? 1.0 : 0.0, mf3 = qi >= 3 ? 1.0 : 0.0;
+  const double mu0 = qi >= 1 ? 1.0 : 0.0, mu1 = qi >= 2 ? 1.0 : 0.0, mu3 = qi >= 4 ? 1.0 : 0.0;
+  double F[8], Fe[8];
+  F[0] = 0.0;
+  Fe[0] = j == 0 ? 1.0 : 0.0;
+  static_for<1, 8>([&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = decltype(pc)::value, c = p - 1;
+    const double* t = cf.c[c];
+    const double fs = p == 1 ? Fe[c] : F[c] + Fe[c];   // the sources of values below L's
+    double nf = 0.0, ne = 0.0;
+    static_for<0, 6>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int d = e8_qi_step(k);
+      constexpr int CT = e8_ctrl(true, p, k, true);
+      constexpr int ck = e8_cmp(e8_twice_value(true, k), E8_FIX_L2[c]);
+      const double g0 = t[7 + k];
+      double g = g0;
+      if constexpr (d == 1) g *= mf1;
+      if constexpr (d == 3) g *= mf3;
+      if constexpr (ck == 0) {
+        nf = fma(g, row_read<CT>(fs), nf);
+      } else {
+        if constexpr (p > 1) nf = fma(g, row_read<CT>(F[c]), nf);
+        if constexpr (ck == 1) {
+          ne = fma(g, row_read<CT>(Fe[c]), ne);
+        } else {
+          double gu = g0;
+          if constexpr (d == 0) gu *= mu0;
+          if constexpr (d == 1) gu *= mu1;
+          if constexpr (d == 3) gu *= mu3;
+          nf = fma(gu, row_read<e8_ctrl_ext(true, p, k, true, 1)>(Fe[c]), nf);
+        }
+      }
+    });
+    F[p] = nf;
+    Fe[p] = ne;
+  });
+  reload_barrier();
+  // accepted: s = 0 (the coordinate sum is even) and norm 2 Qi + 2 of at most the last norm
+  double Bm = j < 8 && qi <= 5 && 2 * qi + 2 <= E8_FIX_QLAST ? 1.0 : 0.0;
+  double Be = Bm;
+  static_for<0, 8>([&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = 8 - decltype(pc)::value, c = p - 1;
+    const double* t = cf.c[c];
+    // values below L's first: their sums are also the equal chain's
+    double nb = 0.0, n1 = 0.0, n2 = 0.0;
+    static_for<0, 6>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int d = e8_qi_step(k);
+      if constexpr (e8_cmp(e8_twice_value(true, k), E8_FIX_L2[c]) == 0) {
+        double sb = row_read<e8_ctrl(true, p, k, false)>(Bm);
+        if constexpr (d == 1) sb *= mb1;
+        if constexpr (d == 3) sb *= mb3;
+        nb = fma(t[7 + k], sb, nb);
+        n1 = fma(t[18 + k], sb, n1);
+        n2 = fma(t[24 + k], sb, n2);
+      }
+    });
+    double ne = nb, ne1 = n1, ne2 = n2;
+    static_for<0, 6>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int d = e8_qi_step(k);
+      constexpr int CT = e8_ctrl(true, p, k, false);
+      constexpr int ck = e8_cmp(e8_twice_value(true, k), E8_FIX_L2[c]);
+      if constexpr (ck != 0) {
+        if constexpr (p > 1) {   // F_0 = 0: the merged chain's first step carries no weight
+          double sb = row_read<CT>(Bm);
+          if constexpr (d == 1) sb *= mb1;
+          if constexpr (d == 3) sb *= mb3;
+          nb = fma(t[7 + k], sb, nb);
+          n1 = fma(t[18 + k], sb, n1);
+          n2 = fma(t[24 + k], sb, n2);
+        }
+        double se = ck == 1 ? row_read<CT>(Be) : row_read<e8_ctrl_ext(true, p, k, false, 1)>(Bm);
+        if constexpr (d == 1) se *= mb1;
+        if constexpr (d == 3) se *= mb3;
+        ne = fma(t[7 + k], se, ne);
+        ne1 = fma(t[18 + k], se, ne1);
+        ne2 = fma(t[24 + k], se, ne2);
+      }
+    });
+    if constexpr (p > 1) {
+      m1[c] = fma(F[c], n1, fma(Fe[c], ne1, m1[c]));
+      m2 = fma(F[c], n2, fma(Fe[c], ne2, m2));
+    } else {
+      m1[0] = fma(Fe[0], ne1, m1[0]);
+      m2 = fma(Fe[0], ne2, m2);
+      z = fma(Fe[0], ne, z);
+    }
+    Bm = nb;
+    Be = ne;
+  });
+}
+
 // Wave-local ordering of LDS writes before other lanes of the wave read them.
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -344,11 +555,12 @@ __global__ __launch_bounds__(64 * E8DP_WAVES) void e8dp_kernel(const double* __r
                                                    E8Prefix P, double* __restrict__ xhat,
                                                    double* __restrict__ vblk, int32_t* __restrict__ flag_list,
                                                    int32_t* __restrict__ flag_count) {
-  __shared__ E8RowCoef coef[E8DP_WAVES * 4];
+  using Coef = std::conditional_t<FIX, E8FixCoef, E8RowCoef>;
+  __shared__ Coef coef[E8DP_WAVES * 4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int row = lane >> 4, j = lane & 15;
-  E8RowCoef& cf = coef[wave * 4 + row];
+  Coef& cf = coef[wave * 4 + row];
   const int64_t B = n / 8;
   const int64_t total = m * B;
   const bool lhalf = (P.L2[0] & 1) != 0;
@@ -371,22 +583,45 @@ __global__ __launch_bounds__(64 * E8DP_WAVES) void e8dp_kernel(const double* __r
     const double rv = active && j < 8 ? rq[j] : 0.0;
     if (j < 8) cf.c[j][13] = (rv - oi) / ai;
     wave_sync();
+    double gk[8];
     if (j < 13) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const double r = cf.c[c][13];
         const double xb = fmin(fmax(rint(2.0 * r) * 0.5, -3.0), 3.0);   // nearest of the 13 values
         const double d = xj - r, db = xb - r;
-        cf.c[c][j] = exp(-0.5 * kap * (d * d - db * db));
+        gk[c] = exp(-0.5 * kap * (d * d - db * db));
+        cf.c[c][j] = gk[c];
       }
     }
     wave_sync();
+    if constexpr (FIX) {   // the combined factors of E8FixCoef
+      double gm[8];   // integer lanes x = 1..3: the factor of -x
+#pragma unroll
+      for (int c = 1; c < 8; ++c) gm[c] = j >= 4 && j < 7 ? cf.c[c][6 - j] : 0.0;
+      wave_sync();   // every raw factor read before the pair sums overwrite them
+      // one formula for both classes (a half lane's partner factor is 0):
+      // integer lanes x = 0..3 write gs, gx, gq from c = 1, half lanes g x and
+      // g (x - r')^2 from c = 0
+      const bool il = j >= 3 && j < 7, hl = j >= 7 && j < 13;
+      const int sx = il ? j : 11 + j, sq = il ? 11 + j : 17 + j;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const double r = cf.c[c][13], g = gk[c], h = c > 0 ? gm[c] : 0.0;
+        const double dm = xj - r, dp = xj + r;
+        const bool w = hl || (il && c > 0);
+        if (w && il) cf.c[c][j - 3] = g + h;
+        if (w && j != 3) cf.c[c][sx] = xj * (g - h);
+        if (w) cf.c[c][sq] = fma(g * dm, dm, h * dp * dp);
+      }
+      wave_sync();
+    }
     double m1[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
     double m2 = 0.0, z = 0.0;
     if constexpr (FIX) {   // the fixed last point is a half-integer point
-      e8_class_pass<false, false, true>(j, cf, P, m1, m2, z);
+      e8_int_pass_fix(j, cf, m1, m2, z);
       reload_barrier();
-      e8_class_pass<true, true, true>(j, cf, P, m1, m2, z);
+      e8_half_pass_fix(j, cf, m1, m2, z);
     } else if (lhalf) {
       e8_class_pass<false, false>(j, cf, P, m1, m2, z);
       reload_barrier();
@@ -399,12 +634,13 @@ __global__ __launch_bounds__(64 * E8DP_WAVES) void e8dp_kernel(const double* __r
     reload_barrier();
     const double Z = row_sum(z);
     const double M2 = row_sum(m2);
+    const double iz = 1.0 / Z;
     double mj = 0.0, sq = 0.0;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const double mc = row_sum(m1[c]);
       mj = j == c ? mc : mj;
-      const double dl = mc / Z - cf.c[c][13];
+      const double dl = fma(mc, iz, -cf.c[c][13]);
       sq = fma(dl, dl, sq);
     }
     if (!active) return;
@@ -418,7 +654,6 @@ __global__ __launch_bounds__(64 * E8DP_WAVES) void e8dp_kernel(const double* __r
       if (j == 0) flag_list[atomicAdd(flag_count, 1)] = (int32_t)q;
       return;
     }
-    const double iz = 1.0 / Z;
     if (j < 8) xo[j] = fma(ai, mj * iz, oi);
     if (j == 0) vblk[i * B + b] = fmax(M2 * iz - sq, 0.0) * ai * ai;
   }
