@@ -50,6 +50,39 @@ constexpr int DG_CHUNKS = 2 * DG_RT * DG_S;   // chunks per K step (A and B)
 constexpr int DG_WAVES = 8;
 constexpr int DG_GROUP_M = 8;       // tile rows per group of the tile order
 
+// Lower-triangle tile order (tc <= tr, square M = N): the same groups of
+// DG_GROUP_M tile rows column by column, but each column of a group starts at
+// the diagonal and the columns end at the group's last row, so only tiles
+// that touch the lower triangle are enumerated and the contiguous runs of the
+// XCDs carry equal work.  Tiles of group q before it: GM^2 q (q - 1) / 2 +
+// q GM (GM + 1) / 2.
+__host__ __device__ inline int dg_lower_before(int q) {
+  return DG_GROUP_M * DG_GROUP_M * q * (q - 1) / 2 + q * DG_GROUP_M * (DG_GROUP_M + 1) / 2;
+}
+__host__ __device__ inline int dg_lower_tiles(int tm) {
+  const int full = tm / DG_GROUP_M, gm = tm - full * DG_GROUP_M;
+  return dg_lower_before(full) + full * DG_GROUP_M * gm + gm * (gm + 1) / 2;
+}
+__host__ __device__ inline void dg_lower_tile(int t, int tm, int& tr, int& tc) {
+  int q = 0;
+  while ((q + 1) * DG_GROUP_M < tm && dg_lower_before(q + 1) <= t) ++q;
+  const int first = q * DG_GROUP_M, gm = min(tm - first, DG_GROUP_M);
+  int l = t - dg_lower_before(q);
+  if (l < first * gm) {   // columns left of the group's diagonal block: gm tiles each
+    tc = l / gm;
+    tr = first + l % gm;
+    return;
+  }
+  l -= first * gm;   // diagonal block: column first + u holds gm - u tiles
+  int u = 0;
+  while (l >= gm - u) {
+    l -= gm - u;
+    ++u;
+  }
+  tc = first + u;
+  tr = first + u + l;
+}
+
 // Bytes of the digit planes of a rows x K operand (row tiles padded to whole
 // output tiles, K to whole steps).
 size_t digit_plane_bytes(int64_t rows, int64_t K) {
@@ -227,16 +260,21 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
   // tile order: contiguous runs per XCD (workgroups go to the 8 XCDs in
   // turn), groups of DG_GROUP_M tile rows column by column within a run
   const int tm = (g.M + DG_TILE - 1) / DG_TILE, tn = (g.N + DG_TILE - 1) / DG_TILE;
-  const int T = tm * tn;
+  const int T = g.lower ? dg_lower_tiles(tm) : tm * tn;
   const int per = (T + 7) / 8;
   const int tile = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (tile >= T) return;
-  const int group = tile / (DG_GROUP_M * tn);
-  const int first = group * DG_GROUP_M;
-  const int gm = min(tm - first, DG_GROUP_M);
-  const int in = tile - group * DG_GROUP_M * tn;
-  const int tr = first + in % gm, tc = in / gm;
-  if (g.lower && tc > tr) return;   // whole tile above the diagonal
+  int tr, tc;
+  if (g.lower) {
+    dg_lower_tile(tile, tm, tr, tc);
+  } else {
+    const int group = tile / (DG_GROUP_M * tn);
+    const int first = group * DG_GROUP_M;
+    const int gm = min(tm - first, DG_GROUP_M);
+    const int in = tile - group * DG_GROUP_M * tn;
+    tr = first + in % gm;
+    tc = in / gm;
+  }
   const int row0 = tr * DG_TILE, col0 = tc * DG_TILE;
   const int64_t rt0 = (int64_t)tr * DG_RT, ct0 = (int64_t)tc * DG_RT;
   const int64_t nkt = (g.K + 63) / 64;
@@ -375,7 +413,9 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
 hipError_t launch_digit_gemm(int epi, const DigitGemmArgs& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (g.K <= 0 || g.K > DG_MAX_K) return hipErrorInvalidValue;
-  const int T = ((g.M + DG_TILE - 1) / DG_TILE) * ((g.N + DG_TILE - 1) / DG_TILE);
+  if (g.lower && g.M != g.N) return hipErrorInvalidValue;
+  const int tm = (g.M + DG_TILE - 1) / DG_TILE;
+  const int T = g.lower ? dg_lower_tiles(tm) : tm * ((g.N + DG_TILE - 1) / DG_TILE);
   const dim3 grid((unsigned)(8 * ((T + 7) / 8))), block(64 * DG_WAVES);
   switch (epi) {
     case EPI_STORE: hipLaunchKernelGGL(digit_gemm_kernel<EPI_STORE>, grid, block, 0, st, g); break;
