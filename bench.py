@@ -35,7 +35,13 @@ PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_FP64_TFLOPS = 78.6        # float64 matrix and vector alike on MI355X
 PEAK_INT8_TOPS = 5000.0        # dense int8 MFMA
-DIGIT_PRODUCTS = 15            # int8 digit products per float64-accurate multiply-add (linear module)
+DIGITS = 5                     # base-256 digits per operand entry of the digit products (set from --digits)
+# Digits a workload runs with unless --digits says otherwise (the library
+# default elsewhere).  4 digits split each operand row exact to 2^-31 of its
+# largest entry; on the 4096 x 14336 lattice workload that keeps every sampled
+# code and trace within the parity bar (tests/test_gpu_configs.py, case c5).
+WORKLOAD_DIGITS = {"c5": 4}
+DIGIT_PRODUCTS = 15            # int8 digit products per multiply-add of the linear module: DIGITS (DIGITS + 1) / 2
 PEAK_HBM_GBS = 8000.0
 CD_MFMA_FLOP_PER_EVAL = 64     # bf16 MFMA flops the CD scoring issues per (row, block, codeword)
 # Transcendental issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz at half
@@ -58,6 +64,11 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def mpq_digits_default():
+    import post_quantization_solver_amd as mpq
+    return mpq.binding.DIGITS_DEFAULT
+
+
 def mpq_e8dp_transitions(E):
     import post_quantization_solver_amd as mpq
     return mpq.binding.e8dp_transitions(E)
@@ -77,8 +88,8 @@ def group_work(L, kernel, launches, steps, n_cd):
         return (launches * m * (n // d) * K * per, per * EXP_RATE / 1e12, "alu",
                 f"{per} flops and one exponential per (block, codeword)")
     if kernel in ("linear1", "linear2"):
-        # one m x n x r product per launch, float64-accurate, issued as exact
-        # int8 digit products on the int8 matrix cores
+        # one m x n x r product per launch, issued as exact int8 digit
+        # products on the int8 matrix cores
         return launches * 2.0 * m * n * r, PEAK_INT8_TOPS, "mfma", "2mnr flops per launch, int8 digit MFMA"
     if kernel == "cd_score" and d == 8:
         # every sweep scores every codeword for every (row, block): the
@@ -106,7 +117,8 @@ def dominant_roofline(L, prof, steps, n_cd):
         out["secondary"] = dict(bound="mfma", achieved=issued, peak=PEAK_INT8_TOPS, unit="TOP/s",
                                 frac=issued / PEAK_INT8_TOPS,
                                 basis=f"int8 MFMA operations as issued ({DIGIT_PRODUCTS} digit products per "
-                                      "float64-accurate multiply-add), not the method's work",
+                                      f"multiply-add, {DIGITS} base-256 digits per operand entry), not the "
+                                      "method's work",
                                 fp64_equivalent=dict(achieved=achieved, peak=PEAK_FP64_TFLOPS,
                                                      frac=achieved / PEAK_FP64_TFLOPS))
     if best == "cd_score":
@@ -252,6 +264,9 @@ def main():
                     help="CD sweeps (default: the workload's 3); 0 runs only the prologue, VAMP and MAP, e.g. for "
                          "counter passes over the VAMP kernels")
     ap.add_argument("--no-probe", action="store_true", help="skip the achievable-rate probes")
+    ap.add_argument("--digits", type=int, default=None, choices=[0, 4, 5],
+                    help="base-256 digits per operand entry of the int8 digit products (0: the library default; "
+                         "unset: the workload's setting, 4 for c5 as its parity test runs it, else the default)")
     ap.add_argument("--no-split", action="store_true",
                     help="skip the extra profiled step that gives the per-group time split (keeps a counter pass "
                          "to one solve's dispatches: rocprofv3 --pmc has crashed in its dispatch interception after "
@@ -267,6 +282,9 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB (5 times), the reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    global DIGITS, DIGIT_PRODUCTS
+    DIGITS = (args.digits if args.digits is not None else WORKLOAD_DIGITS.get(args.config, 0)) or mpq_digits_default()
+    DIGIT_PRODUCTS = DIGITS * (DIGITS + 1) // 2
     if args.copy_calibration:
         import torch
         nbytes = args.copy_calibration << 20
@@ -310,12 +328,12 @@ def main():
         g2 = torch.full((L.m,), 10.0, dtype=torch.float64, device=dev)
         beta = torch.ones(L.m, dtype=torch.float64, device=dev)
         for k in range(2):
-            mpq.linear_step(R2, g2, beta, W, s, V, damping=L.damping)
+            mpq.linear_step(R2, g2, beta, W, s, V, damping=L.damping, digits=DIGITS)
             torch.cuda.synchronize()
             log(f"[bench] linear module call {k + 1}/2 done")
         return
     ws = torch.empty(mpq.workspace_bytes(L.m, L.n, L.r, L.K, L.d), dtype=torch.uint8, device=dev)
-    kw = dict(T_vamp=L.T_vamp, n_cd=L.n_cd, damping=L.damping, workspace=ws, group=L.group)
+    kw = dict(T_vamp=L.T_vamp, n_cd=L.n_cd, damping=L.damping, workspace=ws, group=L.group, digits=DIGITS)
     cb = mpq.prepare_codebook(L.E, dev)   # the codebook's device tables, once per layer
     out = None
     for k in range(args.warmup):
@@ -385,7 +403,7 @@ def main():
                 data="synthetic",
                 config=dict(workload=f"{args.config}: {WORKLOADS[args.config]}" +
                             (f", group-wise grids of {L.group} columns" if L.group else ""), m=L.m, n=L.n, r=L.r,
-                            K=L.K, d=L.d, T_vamp=L.T_vamp, n_cd=L.n_cd, damping=L.damping,
+                            K=L.K, d=L.d, T_vamp=L.T_vamp, n_cd=L.n_cd, damping=L.damping, digits=DIGITS,
                             **({"group": L.group} if L.group else {})),
                 roofline=dict(bound=roof["bound"], achieved=roof["achieved"], peak=roof["peak"], unit=roof["unit"],
                               frac=roof["frac"], traffic=roof["traffic"], kernel=roof["kernel"],
@@ -394,6 +412,9 @@ def main():
                               **({"measured_peak": roof["measured_peak"], "frac_of_measured": roof["frac_of_measured"]}
                                  if "measured_peak" in roof else {}),
                               **({"secondary": roof["secondary"]} if "secondary" in roof else {})),
+                products=f"int8 digit products, {DIGITS} base-256 digits per operand entry "
+                         f"({DIGIT_PRODUCTS} per multiply-add, split exact to 2^-{8 * DIGITS - 1} of each row's "
+                         "largest entry); float64 VAMP state",
                 denoise_linear=dl, measured_peaks=probes, kernel_ms_per_step=split, cpu_baseline=cpu)
     print(json.dumps(line), flush=True)
 

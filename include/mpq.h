@@ -196,7 +196,21 @@ typedef struct {
   int32_t* sweeps;        /* m: CD sweeps run (a row stops after a sweep without a
                              change, the hyper-parameter paragraph's early stop);
                              also filled by mpq_cd */
+  int32_t digits;         /* base-256 digits per operand entry of the int8 digit
+                             products (the linear module's rank-space products,
+                             the prologue's ||T (w - w_rtn)||^2, CD's H and G):
+                             5 (15 int8 products per output and k, each row split
+                             exact to 2^-39 of its largest entry: float64-class)
+                             or 4 (10 products, 2^-31; about 1.2 x faster
+                             products, soft quantities still well inside 1e-4
+                             relative, but trajectories that pass close to the
+                             pass-through rule amplify the difference);
+                             0: MPQ_DIGITS_DEFAULT; else MPQ_EPARAM.
+                             Ignored where the fp64 products run (MPQ_F_LINEAR_F64,
+                             or n or r above 32767). */
 } mpq_options;
+
+#define MPQ_DIGITS_DEFAULT    5    /* mpq_options.digits = 0 */
 
 #define MPQ_F_FIXED_BETA      1u   /* skip the beta M-step (beta stays beta^0) */
 #define MPQ_F_PROFILE         2u   /* time kernel groups (see mpq_options.profiler) */

@@ -52,6 +52,7 @@ F_PROFILE_SAMPLED = 8
 F_NO_E8_DECODE = 16
 F_CHECK_FINITE = 32
 F_LINEAR_F64 = 64
+DIGITS_DEFAULT = 5   # MPQ_DIGITS_DEFAULT: digits per operand entry of the int8 digit products
 PROF_NAMES = ("prologue", "denoise", "extrinsic", "linear1", "beta", "linear2", "map", "cd_gemm", "cd_search",
               "other", "denoise_exact", "cd_score", "split")
 PROF_COUNT = len(PROF_NAMES)
@@ -70,7 +71,7 @@ class Options(ctypes.Structure):
                 ("profiler", ctypes.c_void_p), ("prof_mask", ctypes.c_uint32),
                 ("prof_ms", ctypes.POINTER(ctypes.c_double)), ("prof_launches", ctypes.POINTER(ctypes.c_int64)),
                 ("map_codes", ctypes.c_void_p), ("objective", ctypes.c_void_p), ("fallbacks", ctypes.c_void_p),
-                ("sweeps", ctypes.c_void_p)]
+                ("sweeps", ctypes.c_void_p), ("digits", ctypes.c_int32)]
 
 
 class PreparedCodebook:
@@ -306,7 +307,7 @@ def _workspace(m, n, r, K, d, device):
 
 def _opts(beta0=None, fixed_beta=False, profile=None, anchor_tau=None, anchor_w=None, group=None, map_codes=None,
           objective=None, scan_denoiser=False, e8_decode=True, safeguard_eps=0.0, fallbacks=None, sweeps=None,
-          check_finite=False, linear_f64=False, log_prior=None):
+          check_finite=False, linear_f64=False, log_prior=None, digits=None):
     flags = ((F_FIXED_BETA if fixed_beta else 0) | (F_PROFILE if profile is not None else 0) |
              (F_PROFILE_SAMPLED if profile is not None and profile.sampled else 0) |
              (F_NO_E8DP if scan_denoiser else 0) | (0 if e8_decode else F_NO_E8_DECODE) |
@@ -328,6 +329,7 @@ def _opts(beta0=None, fixed_beta=False, profile=None, anchor_tau=None, anchor_w=
     o.objective = objective.data_ptr() if objective is not None else None
     o.fallbacks = fallbacks.data_ptr() if fallbacks is not None else None
     o.sweeps = sweeps.data_ptr() if sweeps is not None else None
+    o.digits = int(digits or 0)
     return ctypes.byref(o), o
 
 
@@ -352,7 +354,7 @@ def _check(rc, what):
 def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, damping=0.5, beta0=None,
                    fixed_beta=False, workspace=None, traces=True, profile=None, outputs=None, anchor_tau=None,
                    group=None, diagnostics=False, scan_denoiser=False, safeguard_eps=0.0, check_finite=False,
-                   linear_f64=False, log_prior=None):
+                   linear_f64=False, log_prior=None, digits=None):
     """Full MPQ solve of one layer (mpq_quantize_layer).
 
     `cb`: a PreparedCodebook (prepare_codebook) or a raw K x d codebook.
@@ -392,7 +394,7 @@ def quantize_layer(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3, dampin
     sw = torch.empty(m, dtype=torch.int32, device=dev) if diagnostics else None
     op, _keep = _opts(beta0, fixed_beta, profile, anchor_tau, None, group, mc, obj, scan_denoiser,
                       safeguard_eps=safeguard_eps, fallbacks=fb, sweeps=sw, check_finite=check_finite,
-                      linear_f64=linear_f64, log_prior=log_prior)
+                      linear_f64=linear_f64, log_prior=log_prior, digits=digits)
     rc = load_library().mpq_quantize_layer(
         _ptr(W), m, n, _ptr(s), _ptr(V), r, P.ref(), _ptr(row_scale), _ptr(row_offset), int(T_vamp), int(n_cd),
         float(damping), op, _ptr(codes), _ptr(bt), _ptr(g1), _ptr(g2), _ptr(ch), _ptr(ws), ws.numel(), _stream())
@@ -439,7 +441,8 @@ def quantize_layer_static(W, s, V, cb, row_scale, row_offset, T_vamp=16, n_cd=3,
     return dict(codes=codes, beta_tr=bt, gamma1_tr=g1, gamma2_tr=g2, cd_changes=ch)
 
 
-def prologue(W, s, V, cb, row_scale, row_offset, beta0=None, workspace=None, group=None, linear_f64=False):
+def prologue(W, s, V, cb, row_scale, row_offset, beta0=None, workspace=None, group=None, linear_f64=False,
+             digits=None):
     """RTN codes, gamma1^0 and beta^0 of every row (mpq_prologue); float64 scalars."""
     import torch
     m, n = W.shape
@@ -452,7 +455,7 @@ def prologue(W, s, V, cb, row_scale, row_offset, beta0=None, workspace=None, gro
     beta = torch.empty(m, dtype=torch.float64, device=dev)
     _affine(row_scale, row_offset, m, n, group)
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
-    op, _keep = _opts(beta0, group=group, linear_f64=linear_f64)
+    op, _keep = _opts(beta0, group=group, linear_f64=linear_f64, digits=digits)
     rc = load_library().mpq_prologue(_ptr(W), m, n, _ptr(s), _ptr(V), r, P.ref(), _ptr(row_scale),
                                      _ptr(row_offset), op, _ptr(rtn), _ptr(gamma1), _ptr(beta), _ptr(ws), ws.numel(),
                                      _stream())
@@ -485,7 +488,7 @@ def denoise(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=No
 
 
 def vamp_step(R1, gamma1, beta, W, s, V, cb, row_scale, row_offset, damping=0.5, fixed_beta=False,
-              workspace=None, anchor_tau=None, group=None, safeguard_eps=0.0, linear_f64=False):
+              workspace=None, anchor_tau=None, group=None, safeguard_eps=0.0, linear_f64=False, digits=None):
     """One VAMP iteration in place on (R1, gamma1, beta) (float64); returns the
     diagnostics.  W: the layer's weights (float32); with `anchor_tau` > 0 the
     prior is anchored at W."""
@@ -506,7 +509,7 @@ def vamp_step(R1, gamma1, beta, W, s, V, cb, row_scale, row_offset, damping=0.5,
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, dev)
     _affine(row_scale, row_offset, m, n, group)
     op, _keep = _opts(None, fixed_beta, None, anchor_tau, W if anchor_tau else None, group,
-                      safeguard_eps=safeguard_eps, linear_f64=linear_f64)
+                      safeguard_eps=safeguard_eps, linear_f64=linear_f64, digits=digits)
     rc = load_library().mpq_vamp_step(_ptr(R1), _ptr(gamma1), _ptr(beta), _ptr(W), m, n, _ptr(s), _ptr(V), r,
                                       P.ref(), _ptr(row_scale), _ptr(row_offset), float(damping), op, _ptr(xhat),
                                       _ptr(eta1), _ptr(gamma2), _ptr(r2), _ptr(fb), _ptr(ws), ws.numel(), _stream())
@@ -514,7 +517,8 @@ def vamp_step(R1, gamma1, beta, W, s, V, cb, row_scale, row_offset, damping=0.5,
     return dict(xhat1=xhat, eta1=eta1, gamma2=gamma2, r2=r2, fallback=fb)
 
 
-def linear_step(R2, gamma2, beta, W, s, V, damping=0.5, fixed_beta=False, workspace=None, linear_f64=False):
+def linear_step(R2, gamma2, beta, W, s, V, damping=0.5, fixed_beta=False, workspace=None, linear_f64=False,
+                digits=None):
     """The Gaussian linear module + beta M-step (mpq_linear_step): from the
     extrinsic message (R2, gamma2) and beta (updated in place), returns
     (R1, gamma1), the message back to the denoiser (float64)."""
@@ -530,7 +534,7 @@ def linear_step(R2, gamma2, beta, W, s, V, damping=0.5, fixed_beta=False, worksp
     R1 = torch.empty_like(R2)
     gamma1 = torch.empty_like(gamma2)
     ws = workspace if workspace is not None else _workspace(m, n, r, 2, 1, R2.device)
-    op, _keep = _opts(None, fixed_beta, linear_f64=linear_f64)
+    op, _keep = _opts(None, fixed_beta, linear_f64=linear_f64, digits=digits)
     rc = load_library().mpq_linear_step(_ptr(R2), _ptr(gamma2), _ptr(beta), _ptr(W), m, n, _ptr(s), _ptr(V), r,
                                         float(damping), op, _ptr(R1), _ptr(gamma1), _ptr(ws), ws.numel(), _stream())
     _check(rc, "mpq_linear_step")
@@ -562,7 +566,7 @@ def map_codes(R1, gamma1, cb, row_scale, row_offset, workspace=None, anchor_tau=
     return codes
 
 
-def cd(W, s, V, cb, row_scale, row_offset, codes, n_cd=3, workspace=None, group=None, sweeps=None):
+def cd(W, s, V, cb, row_scale, row_offset, codes, n_cd=3, workspace=None, group=None, sweeps=None, digits=None):
     """Block CD from `codes` (a device int32 tensor, updated in place); returns
     (codes, changes per sweep).  `sweeps` (device int32, m) receives the
     sweeps run per row."""
@@ -575,7 +579,7 @@ def cd(W, s, V, cb, row_scale, row_offset, codes, n_cd=3, workspace=None, group=
     _affine(row_scale, row_offset, m, n, group)
     ch = torch.zeros((m, max(n_cd, 1)), dtype=torch.int32, device=W.device)
     ws = workspace if workspace is not None else _workspace(m, n, r, K, d, W.device)
-    op, _keep = _opts(group=group, sweeps=sweeps)
+    op, _keep = _opts(group=group, sweeps=sweeps, digits=digits)
     rc = load_library().mpq_cd(_ptr(W), m, n, _ptr(s), _ptr(V), r, P.ref(), _ptr(row_scale), _ptr(row_offset),
                                int(n_cd), op, _ptr(codes), _ptr(ch), _ptr(ws), ws.numel(), _stream())
     _check(rc, "mpq_cd")

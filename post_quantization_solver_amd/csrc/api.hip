@@ -142,6 +142,12 @@ enum Region {
 // inner dimensions fit it.
 bool digits_fit(int64_t n, int64_t r) { return n <= DG_MAX_K && r <= DG_MAX_K; }
 
+// Digits per operand entry of the digit products (mpq_options.digits, 0: the default).
+int digit_count(const mpq_options* opt, int& S) {
+  S = opt && opt->digits ? opt->digits : MPQ_DIGITS_DEFAULT;
+  return digit_count_ok(S) ? MPQ_OK : MPQ_EPARAM;
+}
+
 static_assert(R_COUNT <= (int)(sizeof(Layout::off) / sizeof(size_t)), "Layout::off holds every region");
 
 size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -399,6 +405,7 @@ struct Ctx {
   // the linear module's products on the int8 digit GEMM (else on the fp64
   // matrix cores)
   bool digits = false;
+  int dg_s = 5;   // digits per operand entry of the digit products
   uint8_t* dp(Region k) const { return reinterpret_cast<uint8_t*>(ws + L.off[k]); }
   // d = 8 codebooks that are the first K points of E8 in (norm, lex) order:
   // the denoiser runs the forward-backward pass over coordinates
@@ -472,8 +479,8 @@ int prepare_factors(Ctx& c, const float* V, const float* s, bool vs) {
   const Layout& L = c.L;
   TIMED(c, MPQ_PROF_OTHER, launch_prepare_v(V, s, L.n, L.r, c.f(R_VT), vs ? c.d(R_VS64) : nullptr, c.st));
   if (c.digits) {
-    TIMED(c, MPQ_PROF_SPLIT, launch_digit_split_f32(c.f(R_VT), L.r, L.n, L.n, c.pi(R_DEVT), c.dp(R_DPVT), c.st));
-    TIMED(c, MPQ_PROF_SPLIT, launch_digit_split_f32(V, L.n, L.r, L.r, c.pi(R_DEV), c.dp(R_DPV), c.st));
+    TIMED(c, MPQ_PROF_SPLIT, launch_digit_split_f32(c.f(R_VT), L.r, L.n, L.n, c.pi(R_DEVT), c.dp(R_DPVT), c.dg_s, c.st));
+    TIMED(c, MPQ_PROF_SPLIT, launch_digit_split_f32(V, L.n, L.r, L.r, c.pi(R_DEV), c.dp(R_DPV), c.dg_s, c.st));
   }
   return MPQ_OK;
 }
@@ -486,6 +493,7 @@ DigitGemmArgs digit_args(const Ctx& c, int M, int N, int K, Region bplanes, Regi
   g.EA = c.pi(R_DEA);
   g.Bp = c.dp(bplanes);
   g.EB = c.pi(bexp);
+  g.S = c.dg_s;
   return g;
 }
 
@@ -534,7 +542,7 @@ int run_prologue(Ctx& c, const float* W, const float* s, const float* a, const f
   TIMED(c, MPQ_PROF_PROLOGUE, nearest_f(c, W, rtn, a, o));
   TIMED(c, MPQ_PROF_PROLOGUE, launch_gather(rtn, L.m, L.n, c.cb, a, o, W, nullptr, c.rowsq(), c.st, D));
   if (c.digits) {
-    TIMED(c, MPQ_PROF_PROLOGUE, launch_digit_split(D, L.m, L.n, L.n, c.pi(R_DEA), c.dp(R_DPA), c.st));
+    TIMED(c, MPQ_PROF_PROLOGUE, launch_digit_split(D, L.m, L.n, L.n, c.pi(R_DEA), c.dp(R_DPA), c.dg_s, c.st));
     DigitGemmArgs g = digit_args(c, (int)L.m, (int)L.r, (int)L.n, R_DPVT, R_DEVT);
     g.s = s;
     g.partial = c.d(R_PART);
@@ -565,9 +573,9 @@ int run_linear(Ctx& c, const float* W, const float* s, const float* V, double* R
   TIMED(c, MPQ_PROF_EXTRINSIC, launch_beta_lin(L.m, gamma1, beta, c.betalin(), c.gamma2(), c.st));
   if (c.digits) {
     if (d2_exp_ready)   // the extrinsic kernel wrote D2's row exponents
-      TIMED(c, MPQ_PROF_SPLIT, launch_digit_split_planes(D2, L.m, L.n, L.n, c.pi(R_DEA), c.dp(R_DPA), c.st));
+      TIMED(c, MPQ_PROF_SPLIT, launch_digit_split_planes(D2, L.m, L.n, L.n, c.pi(R_DEA), c.dp(R_DPA), c.dg_s, c.st));
     else
-      TIMED(c, MPQ_PROF_SPLIT, launch_digit_split(D2, L.m, L.n, L.n, c.pi(R_DEA), c.dp(R_DPA), c.st));
+      TIMED(c, MPQ_PROF_SPLIT, launch_digit_split(D2, L.m, L.n, L.n, c.pi(R_DEA), c.dp(R_DPA), c.dg_s, c.st));
     DigitGemmArgs g1 = digit_args(c, (int)L.m, (int)L.r, (int)L.n, R_DPVT, R_DEVT);
     g1.C = c.d(R_Z); g1.ldc = L.r;
     g1.s = s;
@@ -588,7 +596,7 @@ int run_linear(Ctx& c, const float* W, const float* s, const float* V, double* R
   TIMED(c, MPQ_PROF_BETA, launch_beta(L.m, L.n, L.r, s, c.d(R_PART), gemm_col_tiles((int)L.r), c.gamma2(), damping,
                                       fixed_beta, beta, gamma1, c.coef(), c.st));
   if (c.digits) {
-    TIMED(c, MPQ_PROF_SPLIT, launch_digit_split(c.d(R_Z), L.m, L.r, L.r, c.pi(R_DEA), c.dp(R_DPA), c.st));
+    TIMED(c, MPQ_PROF_SPLIT, launch_digit_split(c.d(R_Z), L.m, L.r, L.r, c.pi(R_DEA), c.dp(R_DPA), c.dg_s, c.st));
     DigitGemmArgs g2 = digit_args(c, (int)L.m, (int)L.n, (int)L.r, R_DPV, R_DEV);
     g2.C = R1; g2.ldc = L.n;
     g2.rowa = c.coef();
@@ -644,7 +652,7 @@ int compute_h(Ctx& c) {
   const Layout& L = c.L;
   double* H = c.d(R_HFULL);
   if (c.digits) {
-    TIMED(c, MPQ_PROF_CD_GEMM, launch_digit_split(c.d(R_VS64), L.n, L.r, L.r, c.pi(R_DEN), c.dp(R_DPN), c.st));
+    TIMED(c, MPQ_PROF_CD_GEMM, launch_digit_split(c.d(R_VS64), L.n, L.r, L.r, c.pi(R_DEN), c.dp(R_DPN), c.dg_s, c.st));
     DigitGemmArgs h = digit_args(c, (int)L.n, (int)L.n, (int)L.r, R_DPN, R_DEN);
     h.Ap = c.dp(R_DPN);
     h.EA = c.pi(R_DEN);
@@ -750,8 +758,8 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
     if (rc) return rc;
     // G = (W - X) H
     if (c.digits) {
-      TIMED(c, MPQ_PROF_CD_GEMM, launch_digit_split(D, L.m, L.n, L.n, c.pi(R_DEA), c.dp(R_DPA), c.st));
-      TIMED(c, MPQ_PROF_CD_GEMM, launch_digit_split(H, L.n, L.n, L.n, c.pi(R_DEN), c.dp(R_DPN), c.st));
+      TIMED(c, MPQ_PROF_CD_GEMM, launch_digit_split(D, L.m, L.n, L.n, c.pi(R_DEA), c.dp(R_DPA), c.dg_s, c.st));
+      TIMED(c, MPQ_PROF_CD_GEMM, launch_digit_split(H, L.n, L.n, L.n, c.pi(R_DEN), c.dp(R_DPN), c.dg_s, c.st));
       DigitGemmArgs gd = digit_args(c, (int)L.m, (int)L.n, (int)L.n, R_DPN, R_DEN);
       gd.C = Gf;
       gd.ldc = L.n;
@@ -993,6 +1001,7 @@ int begin(Ctx& c, int64_t m, int64_t n, int64_t r, const mpq_codebook* cb, void*
   }
   c.e8_decode = !(opt && (opt->flags & MPQ_F_NO_E8_DECODE));
   c.digits = digits_fit(n, r) && !(opt && (opt->flags & MPQ_F_LINEAR_F64));
+  if ((rc = digit_count(opt, c.dg_s))) return rc;
   // codebook tables
   const TableLayout T = table_layout(cb->K, cb->d);
   const char* tb = static_cast<const char*>(cb->tables);
@@ -1299,7 +1308,9 @@ int mpq_linear_step(const double* R2, const double* gamma2, double* beta, const 
     Ctx c;
     c.L = make_layout(m, n, r, 2, 1);
     c.digits = digits_fit(n, r) && !(opt && (opt->flags & MPQ_F_LINEAR_F64));
-    int rc = check_ws(c.L, workspace, ws_bytes);
+    int rc = digit_count(opt, c.dg_s);
+    if (rc) return rc;
+    rc = check_ws(c.L, workspace, ws_bytes);
     if (rc) return rc;
     if (m == 0) return MPQ_OK;
     if (!R2 || !gamma2 || !beta || !W || !s || !V || !R1 || !gamma1) return MPQ_ENULL;

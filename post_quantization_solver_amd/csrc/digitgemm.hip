@@ -1,23 +1,25 @@
-// The linear module's rank-space products in float64 accuracy on the int8
+// The linear module's rank-space products (and CD's H and G) on the int8
 // matrix cores (v_mfma_i32_16x16x64_i8), for K <= DG_MAX_K:
 //
 //   C[M x N] = A[M x K] * B[N x K]^T,  A float64 (w - r2, or z), B float32 (V^T or V).
 //
-// Digit split (an exact integer form of each operand).  Row i of A is scaled
-// by its own power of two 2^E_i > max_k |A_ik| and rounded to the integer
-// N_ik = rint(A_ik 2^(38 - E_i)), |N_ik| <= 2^38, which is written in balanced
-// base-256 digits N = sum_p d_p 256^(4 - p), p = 0..4: the low four in
-// [-128, 127], the top one in [-64, 64].  B's rows likewise (F_j).  Then
+// Digit split (an exact integer form of each operand), S = 4 or 5 digits.
+// Row i of A is scaled by its own power of two 2^E_i > max_k |A_ik| and
+// rounded to the integer N_ik = rint(A_ik 2^(8S - 2 - E_i)), |N_ik| <=
+// 2^(8S - 2), which is written in balanced base-256 digits
+// N = sum_p d_p 256^(S - 1 - p), p = 0..S-1: the low S - 1 in [-128, 127], the
+// top one in [-64, 64].  B's rows likewise (F_j).  Then, for every S,
 //
-//   sum_k A_ik B_jk ~= 2^(E_i + F_j - 12) sum_{l=0..4} 2^(-8 l) I_l,
+//   sum_k A_ik B_jk ~= 2^(E_i + F_j - 12) sum_{l=0..S-1} 2^(-8 l) I_l,
 //   I_l = sum_{p+q=l} sum_k d_p(A_ik) d_q(B_jk),
 //
 // each I_l an exact int32 sum of int8 x int8 products (|I_l| <= 65536 K <
 // 2^31 for K < 32768), converted to float64 once after the K loop.  The
-// pairs with p + q > 4 (below 2^-38 of max|A_ik| max|B_jk| per term) are
-// dropped: 15 int8 products per output and k, against the 53-bit float64
-// product; the rank-space output is accurate to about 1e-10 relative (the
-// split itself is exact to 2^-39 of each row's largest entry).
+// pairs with p + q >= S (below 2^-(8S - 2) of max|A_ik| max|B_jk| per term)
+// are dropped: S (S + 1) / 2 int8 products per output and k.  The split is
+// exact to 2^-(8S - 1) of each row's largest entry: 2^-39 for S = 5 (15
+// products; float64-class, the rank-space output accurate to about 1e-10
+// relative) or 2^-31 for S = 4 (10 products).
 //
 // Layout.  The digits live in "fragment order": for every 16-row x 64-k
 // chunk of one digit plane, 64 lanes x 16 bytes exactly as lane (i, g) of an
@@ -27,9 +29,9 @@
 // operand fragment is then one conflict-free 16-byte LDS read per lane.
 //
 // Tiling: 512 threads (8 waves) per 128 x 128 output tile, K in steps of 64
-// through two LDS stages of 80 KB (5 planes x (128 + 128) rows x 64 bytes;
+// through two LDS stages of 16 S KB (S planes x (128 + 128) rows x 64 bytes;
 // the next step's chunks stream in while this one is multiplied).  Each
-// wave owns 32 x 64 outputs: 2 x 4 sub-tiles of 16 x 16, 5 int32
+// wave owns 32 x 64 outputs: 2 x 4 sub-tiles of 16 x 16, S int32
 // accumulators each.  Tiles go to the XCDs in contiguous runs and, within a
 // run, in groups of 8 tile rows column by column, so the tiles resident on one
 // XCD share their A and B panels in its L2.
@@ -42,12 +44,13 @@ namespace mpq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int DG_S = 5;             // digits per operand entry
+constexpr int DG_S_MAX = 5;         // most digits per operand entry (the planes' allocation)
 constexpr int DG_CHUNK = 1024;      // bytes of one 16-row x 64-k chunk of one plane
 constexpr int DG_TILE = 128;        // output tile (rows and columns)
 constexpr int DG_RT = DG_TILE / 16; // row tiles per output tile side
-constexpr int DG_CHUNKS = 2 * DG_RT * DG_S;   // chunks per K step (A and B)
 constexpr int DG_WAVES = 8;
+template <int S>
+constexpr int dg_chunks() { return 2 * DG_RT * S; }   // chunks per K step (A and B)
 constexpr int DG_GROUP_M = 8;       // tile rows per group of the tile order
 
 // Lower-triangle tile order (tc <= tr, square M = N): the same groups of
@@ -84,12 +87,13 @@ __host__ __device__ inline void dg_lower_tile(int t, int tm, int& tr, int& tc) {
 }
 
 // Bytes of the digit planes of a rows x K operand (row tiles padded to whole
-// output tiles, K to whole steps).
+// output tiles, K to whole steps), for up to DG_S_MAX digits.
 size_t digit_plane_bytes(int64_t rows, int64_t K) {
   const int64_t rt = (rows + DG_TILE - 1) / DG_TILE * DG_RT;
   const int64_t kt = (K + 63) / 64;
-  return (size_t)(rt * kt * DG_S) * DG_CHUNK;
+  return (size_t)(rt * kt * DG_S_MAX) * DG_CHUNK;
 }
+bool digit_count_ok(int S) { return S == 4 || S == 5; }
 
 // --------------------------------------------------------------- digit split
 
@@ -118,11 +122,12 @@ __global__ __launch_bounds__(256) void digit_exp_kernel(const T* __restrict__ X,
   }
 }
 
-// Digits of one value (five int8, top first) given its row exponent e.
-__device__ __forceinline__ void digits5(double v, int e, int (&d)[DG_S]) {
-  long long N = llrint(ldexp(v, 38 - e));   // |N| <= 2^38
+// Digits of one value (S int8, top first) given its row exponent e.
+template <int S>
+__device__ __forceinline__ void digits_of(double v, int e, int (&d)[S]) {
+  long long N = llrint(ldexp(v, 8 * S - 2 - e));   // |N| <= 2^(8S - 2)
 #pragma unroll
-  for (int p = DG_S - 1; p >= 1; --p) {
+  for (int p = S - 1; p >= 1; --p) {
     const int r = (int)(N & 255);
     d[p] = r >= 128 ? r - 256 : r;
     N = (N - d[p]) >> 8;
@@ -134,9 +139,9 @@ __device__ __forceinline__ void digits5(double v, int e, int (&d)[DG_S]) {
 // reads its chunk row by row (two rows of 64 values per instruction, lanes on
 // consecutive elements) into LDS, then lane (i, g) takes row i, k = 16 g ..
 // 16 g + 15 from there (zero outside the matrix), splits them and writes its
-// 16 bytes of each of the five planes (1 KB contiguous per plane and wave).
+// 16 bytes of each of the S planes (1 KB contiguous per plane and wave).
 constexpr int DG_SPLIT_PITCH = 65;   // doubles per LDS row (one of padding)
-template <typename T>
+template <typename T, int S>
 __global__ __launch_bounds__(256) void digit_split_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t ld,
                                                           const int32_t* __restrict__ E, int64_t nrt, int64_t nkt,
                                                           uint8_t* __restrict__ planes) {
@@ -170,53 +175,62 @@ __global__ __launch_bounds__(256) void digit_split_kernel(const T* __restrict__ 
   const int64_t row = rt * 16 + i;
   const int e = row < rows ? E[row] : 0;
   const bool ok = row < rows && e != DG_EXP_NONFINITE;
-  uint32_t wd[DG_S][4];
+  uint32_t wd[S][4];
 #pragma unroll
-  for (int p = 0; p < DG_S; ++p)
+  for (int p = 0; p < S; ++p)
 #pragma unroll
     for (int q = 0; q < 4; ++q) wd[p][q] = 0u;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     const double v = ok ? tl[i * DG_SPLIT_PITCH + 16 * g + t] : 0.0;
-    int d[DG_S];
-    digits5(v, e, d);
+    int d[S];
+    digits_of<S>(v, e, d);
 #pragma unroll
-    for (int p = 0; p < DG_S; ++p) wd[p][t >> 2] |= ((uint32_t)d[p] & 255u) << (8 * (t & 3));
+    for (int p = 0; p < S; ++p) wd[p][t >> 2] |= ((uint32_t)d[p] & 255u) << (8 * (t & 3));
   }
 #pragma unroll
-  for (int p = 0; p < DG_S; ++p) {
-    uint4* dst = reinterpret_cast<uint4*>(planes + ((size_t)pos * DG_S + p) * DG_CHUNK) + lane;
+  for (int p = 0; p < S; ++p) {
+    uint4* dst = reinterpret_cast<uint4*>(planes + ((size_t)pos * S + p) * DG_CHUNK) + lane;
     *dst = make_uint4(wd[p][0], wd[p][1], wd[p][2], wd[p][3]);
   }
 }
 
+// The planes from given row exponents.
 template <typename T>
-static hipError_t split(const T* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes, hipStream_t st) {
+static hipError_t split_planes(const T* X, int64_t rows, int64_t K, int64_t ld, const int32_t* E, uint8_t* planes,
+                               int S, hipStream_t st) {
   if (rows <= 0 || K <= 0) return hipSuccess;
-  hipLaunchKernelGGL(digit_exp_kernel<T>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, X, rows, K, ld, E);
   const int64_t nrt = (rows + DG_TILE - 1) / DG_TILE * DG_RT;
   const int64_t nkt = (K + 63) / 64;
-  hipLaunchKernelGGL(digit_split_kernel<T>, dim3((unsigned)((nrt * nkt + 3) / 4)), dim3(256), 0, st, X, rows, K, ld,
-                     E, nrt, nkt, planes);
+  const dim3 grid((unsigned)((nrt * nkt + 3) / 4)), block(256);
+  switch (S) {
+    case 4: hipLaunchKernelGGL((digit_split_kernel<T, 4>), grid, block, 0, st, X, rows, K, ld, E, nrt, nkt, planes); break;
+    case 5: hipLaunchKernelGGL((digit_split_kernel<T, 5>), grid, block, 0, st, X, rows, K, ld, E, nrt, nkt, planes); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t split(const T* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes, int S,
+                        hipStream_t st) {
+  if (rows <= 0 || K <= 0) return hipSuccess;
+  if (!digit_count_ok(S)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(digit_exp_kernel<T>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, X, rows, K, ld, E);
+  return split_planes<T>(X, rows, K, ld, E, planes, S, st);
+}
+
 hipError_t launch_digit_split(const double* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes,
-                              hipStream_t st) {
-  return split<double>(X, rows, K, ld, E, planes, st);
+                              int S, hipStream_t st) {
+  return split<double>(X, rows, K, ld, E, planes, S, st);
 }
 hipError_t launch_digit_split_planes(const double* X, int64_t rows, int64_t K, int64_t ld, const int32_t* E,
-                                     uint8_t* planes, hipStream_t st) {
-  if (rows <= 0 || K <= 0) return hipSuccess;
-  const int64_t nrt = (rows + DG_TILE - 1) / DG_TILE * DG_RT;
-  const int64_t nkt = (K + 63) / 64;
-  hipLaunchKernelGGL(digit_split_kernel<double>, dim3((unsigned)((nrt * nkt + 3) / 4)), dim3(256), 0, st, X, rows, K,
-                     ld, E, nrt, nkt, planes);
-  return hipGetLastError();
+                                     uint8_t* planes, int S, hipStream_t st) {
+  return split_planes<double>(X, rows, K, ld, E, planes, S, st);
 }
 hipError_t launch_digit_split_f32(const float* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes,
-                                  hipStream_t st) {
-  return split<float>(X, rows, K, ld, E, planes, st);
+                                  int S, hipStream_t st) {
+  return split<float>(X, rows, K, ld, E, planes, S, st);
 }
 
 // ------------------------------------------------------------------ the GEMM
@@ -228,28 +242,31 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
 }
 
 // This wave's share of one K step's chunks, straight into LDS stage `buf`.
+template <int S>
 __device__ __forceinline__ void fetch_step(uint8_t (*stage)[DG_CHUNK], const uint8_t* __restrict__ Ap,
                                            const uint8_t* __restrict__ Bp, int64_t rt0, int64_t ct0, int64_t nkt,
                                            int64_t kt, int wave, int lane) {
+  constexpr int CH = dg_chunks<S>();
+  static_assert(CH % DG_WAVES == 0, "every wave fetches the same number of chunks");
 #pragma unroll
-  for (int j = 0; j < DG_CHUNKS / DG_WAVES; ++j) {
-    const int c = wave * (DG_CHUNKS / DG_WAVES) + j;   // wave-uniform
+  for (int j = 0; j < CH / DG_WAVES; ++j) {
+    const int c = wave * (CH / DG_WAVES) + j;   // wave-uniform
     const uint8_t* src;
-    if (c < DG_RT * DG_S) {
-      const int rt = c / DG_S, p = c - rt * DG_S;
-      src = Ap + (((rt0 + rt) * nkt + kt) * DG_S + p) * DG_CHUNK;
+    if (c < DG_RT * S) {
+      const int rt = c / S, p = c - rt * S;
+      src = Ap + (((rt0 + rt) * nkt + kt) * S + p) * DG_CHUNK;
     } else {
-      const int cc = c - DG_RT * DG_S;
-      const int ct = cc / DG_S, q = cc - ct * DG_S;
-      src = Bp + (((ct0 + ct) * nkt + kt) * DG_S + q) * DG_CHUNK;
+      const int cc = c - DG_RT * S;
+      const int ct = cc / S, q = cc - ct * S;
+      src = Bp + (((ct0 + ct) * nkt + kt) * S + q) * DG_CHUNK;
     }
     __builtin_amdgcn_global_load_lds(src + 16 * lane, (lds_ptr_t)stage[c], 16, 0, 0);
   }
 }
 
-template <int EPI>
+template <int EPI, int S>
 __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][DG_CHUNKS][DG_CHUNK];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][dg_chunks<S>()][DG_CHUNK];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -279,34 +296,34 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
   const int64_t rt0 = (int64_t)tr * DG_RT, ct0 = (int64_t)tc * DG_RT;
   const int64_t nkt = (g.K + 63) / 64;
 
-  v4i acc[DG_S][2][4];
+  v4i acc[S][2][4];
 #pragma unroll
-  for (int l = 0; l < DG_S; ++l)
+  for (int l = 0; l < S; ++l)
 #pragma unroll
     for (int si = 0; si < 2; ++si)
 #pragma unroll
       for (int sj = 0; sj < 4; ++sj) acc[l][si][sj] = (v4i){0, 0, 0, 0};
 
-  fetch_step(lds[0], g.Ap, g.Bp, rt0, ct0, nkt, 0, wave, lane);
+  fetch_step<S>(lds[0], g.Ap, g.Bp, rt0, ct0, nkt, 0, wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int64_t kt = 0; kt < nkt; ++kt) {
     const int cur = (int)(kt & 1);
-    if (kt + 1 < nkt) fetch_step(lds[cur ^ 1], g.Ap, g.Bp, rt0, ct0, nkt, kt + 1, wave, lane);
+    if (kt + 1 < nkt) fetch_step<S>(lds[cur ^ 1], g.Ap, g.Bp, rt0, ct0, nkt, kt + 1, wave, lane);
     const v4i* Ast = reinterpret_cast<const v4i*>(lds[cur][0]);
-    const v4i* Bst = reinterpret_cast<const v4i*>(lds[cur][DG_RT * DG_S]);
-    v4i af[2][DG_S];
+    const v4i* Bst = reinterpret_cast<const v4i*>(lds[cur][DG_RT * S]);
+    v4i af[2][S];
 #pragma unroll
     for (int si = 0; si < 2; ++si)
 #pragma unroll
-      for (int p = 0; p < DG_S; ++p) af[si][p] = Ast[((wm * 2 + si) * DG_S + p) * 64 + lane];
+      for (int p = 0; p < S; ++p) af[si][p] = Ast[((wm * 2 + si) * S + p) * 64 + lane];
 #pragma unroll
-    for (int q = 0; q < DG_S; ++q) {
+    for (int q = 0; q < S; ++q) {
       v4i bf[4];
 #pragma unroll
-      for (int sj = 0; sj < 4; ++sj) bf[sj] = Bst[((wn * 4 + sj) * DG_S + q) * 64 + lane];
+      for (int sj = 0; sj < 4; ++sj) bf[sj] = Bst[((wn * 4 + sj) * S + q) * 64 + lane];
 #pragma unroll
-      for (int p = 0; p + q < DG_S; ++p)
+      for (int p = 0; p + q < S; ++p)
 #pragma unroll
         for (int si = 0; si < 2; ++si)
 #pragma unroll
@@ -324,9 +341,9 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
     for (int sj = 0; sj < 4; ++sj)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        double x = (double)acc[DG_S - 1][si][sj][v];
+        double x = (double)acc[S - 1][si][sj][v];
 #pragma unroll
-        for (int l = DG_S - 2; l >= 0; --l) x = fma(x, 0x1p-8, (double)acc[l][si][sj][v]);
+        for (int l = S - 2; l >= 0; --l) x = fma(x, 0x1p-8, (double)acc[l][si][sj][v]);
         val[si][sj][v] = x;
       }
   int fe[4];
@@ -410,6 +427,18 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
     }
 }
 
+template <int S>
+static hipError_t launch_epi(int epi, dim3 grid, dim3 block, const DigitGemmArgs& g, hipStream_t st) {
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL((digit_gemm_kernel<EPI_STORE, S>), grid, block, 0, st, g); break;
+    case EPI_ROWSUMSQ_S: hipLaunchKernelGGL((digit_gemm_kernel<EPI_ROWSUMSQ_S, S>), grid, block, 0, st, g); break;
+    case EPI_LINEAR1: hipLaunchKernelGGL((digit_gemm_kernel<EPI_LINEAR1, S>), grid, block, 0, st, g); break;
+    case EPI_AXPY_W: hipLaunchKernelGGL((digit_gemm_kernel<EPI_AXPY_W, S>), grid, block, 0, st, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_digit_gemm(int epi, const DigitGemmArgs& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (g.K <= 0 || g.K > DG_MAX_K) return hipErrorInvalidValue;
@@ -417,14 +446,11 @@ hipError_t launch_digit_gemm(int epi, const DigitGemmArgs& g, hipStream_t st) {
   const int tm = (g.M + DG_TILE - 1) / DG_TILE;
   const int T = g.lower ? dg_lower_tiles(tm) : tm * ((g.N + DG_TILE - 1) / DG_TILE);
   const dim3 grid((unsigned)(8 * ((T + 7) / 8))), block(64 * DG_WAVES);
-  switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL(digit_gemm_kernel<EPI_STORE>, grid, block, 0, st, g); break;
-    case EPI_ROWSUMSQ_S: hipLaunchKernelGGL(digit_gemm_kernel<EPI_ROWSUMSQ_S>, grid, block, 0, st, g); break;
-    case EPI_LINEAR1: hipLaunchKernelGGL(digit_gemm_kernel<EPI_LINEAR1>, grid, block, 0, st, g); break;
-    case EPI_AXPY_W: hipLaunchKernelGGL(digit_gemm_kernel<EPI_AXPY_W>, grid, block, 0, st, g); break;
+  switch (g.S) {
+    case 4: return launch_epi<4>(epi, grid, block, g, st);
+    case 5: return launch_epi<5>(epi, grid, block, g, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace mpq

@@ -55,10 +55,11 @@ hipError_t launch_mirror_lower(double* H, int64_t n, hipStream_t st);
 hipError_t launch_collect_nonzero_rows(const double* X, int64_t m, int kd, int32_t* list, int32_t* count,
                                        hipStream_t st);
 
-// The same products in float64 accuracy on the int8 matrix cores (exact
-// integer digit products, int32 sums; digitgemm.hip) for K <= DG_MAX_K.
-// Operands are split once into digit planes (launch_digit_split*), then
-// multiplied with the linear-module epilogues of launch_gemm64.
+// The same products on the int8 matrix cores (exact integer products of S
+// base-256 digits per operand entry, int32 sums; digitgemm.hip) for K <=
+// DG_MAX_K: S = 5 (float64-class) or 4.  Operands are split
+// once into digit planes (launch_digit_split*, with the S of the product),
+// then multiplied with the linear-module epilogues of launch_gemm64.
 constexpr int DG_MAX_K = 32767;
 struct DigitGemmArgs {
   int M, N, K;
@@ -72,17 +73,19 @@ struct DigitGemmArgs {
   const double* X; int64_t ldx;
   const float* W; int64_t ldw;
   int lower;                              // only the tiles that touch the lower triangle (M == N)
+  int S;                                  // digits per entry of both operands' planes (4 or 5)
 };
-size_t digit_plane_bytes(int64_t rows, int64_t K);
+size_t digit_plane_bytes(int64_t rows, int64_t K);   // room for any S
+bool digit_count_ok(int S);
 hipError_t launch_digit_split(const double* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes,
-                              hipStream_t st);
+                              int S, hipStream_t st);
 hipError_t launch_digit_split_f32(const float* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes,
-                                  hipStream_t st);
+                                  int S, hipStream_t st);
 // The split alone, given the row exponents E (as the split computes them:
 // max_k |X_ik| < 2^E[i], 0 for a zero row, DG_EXP_NONFINITE for a row holding
 // NaN or inf).
 hipError_t launch_digit_split_planes(const double* X, int64_t rows, int64_t K, int64_t ld, const int32_t* E,
-                                     uint8_t* planes, hipStream_t st);
+                                     uint8_t* planes, int S, hipStream_t st);
 hipError_t launch_digit_gemm(int epi, const DigitGemmArgs& g, hipStream_t st);
 constexpr int DG_EXP_NONFINITE = 0x7fffffff;   // row exponent of a row holding NaN or inf
 

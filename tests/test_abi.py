@@ -129,6 +129,10 @@ def test_option_validation(lib):
     assert call_layer(lib, opt=Opt(safeguard_eps=float("nan"))) == -3
     assert call_layer(lib, opt=Opt(safeguard_eps=0.5), ws_bytes=1024) == -5       # accepted
     assert call_layer(lib, opt=Opt(flags=mpq.binding.F_PROFILE)) == -1            # profiling needs a profiler
+    for bad in (1, 3, 6, -1):                                                     # digits: 4, 5 or 0
+        assert call_layer(lib, opt=Opt(digits=bad)) == -3
+    for ok in (0, 4, 5):
+        assert call_layer(lib, opt=Opt(digits=ok), ws_bytes=1024) == -5
     h = ctypes.c_void_p()
     assert lib.mpq_profiler_create(0, ctypes.byref(h)) == -3
     assert lib.mpq_profiler_create(4, None) == -1
@@ -146,6 +150,8 @@ def test_linear_step_validation(lib):
     assert call(R2=None) == -1
     assert call(ws_bytes=1024) == -5
     assert call(opt=mpq.binding.Options(flags=mpq.binding.F_PROFILE)) == -4
+    assert call(opt=mpq.binding.Options(digits=2)) == -3
+    assert call(opt=mpq.binding.Options(digits=4), ws_bytes=1024) == -5
 
 
 def test_frontend_argument_validation(lib):
@@ -182,6 +188,22 @@ def test_struct_layout_matches_header(tmp_path, struct_name, cls):
     got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
     want = [getattr(Opt, nm).offset for nm in names] + [ctypes.sizeof(Opt)]
     assert got == want
+
+
+def test_digits_default_matches_header(tmp_path):
+    """The binding's DIGITS_DEFAULT is the header's MPQ_DIGITS_DEFAULT."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    src = tmp_path / "dd.c"
+    src.write_text('#include <stdio.h>\n#include "mpq.h"\nint main(void) { printf("%d\\n", MPQ_DIGITS_DEFAULT); '
+                   'return 0; }\n')
+    exe = tmp_path / "dd"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = int(subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout)
+    assert got == mpq.binding.DIGITS_DEFAULT
 
 
 def test_strerror(lib):

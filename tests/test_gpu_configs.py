@@ -17,9 +17,15 @@ Asserted per workload (the target specification's bar):
   (c) decision chain on the GPU's own trajectory: the GPU's marginal MAP
       equals the oracle's MAP of the GPU's r1^T, and the GPU's CD equals the
       oracle's CD from the GPU's MAP codes.
-The VAMP state and the linear module's products are float64 on the GPU: with
-float32 state the trajectory drifted by 1e-6..1e-4 and moved near-tied MAP
-decisions on the 2048 x 8192 and 4096 x 14336 workloads.
+The VAMP state is float64 on the GPU and the products run as int8 digit
+products: with float32 state the trajectory drifted by 1e-6..1e-4 and moved
+near-tied MAP decisions on the 2048 x 8192 and 4096 x 14336 workloads.  The
+4096 x 14336 lattice workload runs as bench.py times it, with 4 base-256
+digits per operand entry (c5), and also with the library default of 5
+(c5_d5).  4 digits keep every sampled code on every workload but take the
+1024 x 4096 scalar workload's gamma2 trace past the bar near its pass-through
+steps (gamma2 = eta1 - gamma1 cancels there); 3 digits (float32-class, not
+offered) moved codes on every workload.
 """
 import numpy as np
 import pytest
@@ -32,9 +38,10 @@ from parity_helpers import (SOFT_RTOL, OBJ_RTOL, CODE_FRAC, dev, host, layer_ten
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
-SAMPLE = {"c1": 64, "c2": 16, "c3": 16, "c4": 16, "c5": 16, "c3_g128": 16}
-CASES = {"c1": ("c1", 0), "c2": ("c2", 0), "c3": ("c3", 0), "c4": ("c4", 0), "c5": ("c5", 0),
-         "c3_g128": ("c3", 128)}
+SAMPLE = {"c1": 64, "c2": 16, "c3": 16, "c4": 16, "c5": 16, "c5_d5": 16, "c3_g128": 16}
+# name: (workload, group, digits per operand entry of the digit products; None: the library default)
+CASES = {"c1": ("c1", 0, None), "c2": ("c2", 0, None), "c3": ("c3", 0, None), "c4": ("c4", 0, None),
+         "c5": ("c5", 0, 4), "c5_d5": ("c5", 0, None), "c3_g128": ("c3", 128, None)}
 
 
 def sublayer(L, rows):
@@ -42,7 +49,7 @@ def sublayer(L, rows):
                    np.ascontiguousarray(L.o[rows]), L.d, L.T_vamp, L.n_cd, L.damping, group=L.group)
 
 
-def teacher_forced_steps(mpq, L, Ts, refs, k_rows, cb):
+def teacher_forced_steps(mpq, L, Ts, refs, k_rows, cb, digits=None):
     worst = {}
     for t in sorted({0, L.T_vamp // 2, L.T_vamp - 1}):
         h = [r["history"][t] for r in refs]
@@ -50,7 +57,7 @@ def teacher_forced_steps(mpq, L, Ts, refs, k_rows, cb):
         g1 = dev(np.array([x["gamma1"] for x in h]))
         bt = dev(np.array([x["beta"] for x in h]))
         o = mpq.vamp_step(R1, g1, bt, Ts["W"], Ts["s"], Ts["V"], cb, Ts["a"], Ts["o"], damping=L.damping,
-                          group=L.group)
+                          group=L.group, digits=digits)
         r1n, g1n, btn = host(R1), host(g1), host(bt)
         xh, eta1, g2, r2, fb = (host(o[k]) for k in ("xhat1", "eta1", "gamma2", "r2", "fallback"))
         for k in range(k_rows):
@@ -72,11 +79,13 @@ def test_config_parity(name):
     print(f"[config] {name}: generating inputs", flush=True)
     L = S.make_config(CASES[name][0], device="cuda", group=CASES[name][1])
     g = L.group
+    dg = CASES[name][2]
     T = layer_tensors(L)
     cb = mpq.prepare_codebook(L.E)
-    print(f"[config] {name}: m={L.m} n={L.n} r={L.r} K={L.K} d={L.d} T={L.T_vamp} full solve on GPU", flush=True)
+    print(f"[config] {name}: m={L.m} n={L.n} r={L.r} K={L.K} d={L.d} T={L.T_vamp} digits={dg or 'default'} "
+          "full solve on GPU", flush=True)
     out = mpq.quantize_layer(T["W"], T["s"], T["V"], cb, T["a"], T["o"], T_vamp=L.T_vamp, n_cd=L.n_cd,
-                             damping=L.damping, group=g, diagnostics=True)
+                             damping=L.damping, group=g, diagnostics=True, digits=dg)
     torch.cuda.synchronize()
     gpu = {k: (host(v) if v is not None else None) for k, v in out.items()}
     del T, out
@@ -88,13 +97,15 @@ def test_config_parity(name):
 
     # GPU stages on the sampled rows alone (bitwise the same as in the full solve)
     print(f"[config] {name}: GPU stages on {k_rows} sampled rows", flush=True)
-    pro = mpq.prologue(Ts["W"], Ts["s"], Ts["V"], cb, Ts["a"], Ts["o"], group=g)
+    pro = mpq.prologue(Ts["W"], Ts["s"], Ts["V"], cb, Ts["a"], Ts["o"], group=g, digits=dg)
     R1 = Ts["W"].double()
     g1, bt = pro["gamma1"], pro["beta"]
     for _ in range(L.T_vamp):
-        mpq.vamp_step(R1, g1, bt, Ts["W"], Ts["s"], Ts["V"], cb, Ts["a"], Ts["o"], damping=L.damping, group=g)
+        mpq.vamp_step(R1, g1, bt, Ts["W"], Ts["s"], Ts["V"], cb, Ts["a"], Ts["o"], damping=L.damping, group=g,
+                      digits=dg)
     map_gpu = mpq.map_codes(R1, g1, cb, Ts["a"], Ts["o"], group=g)
-    cd_gpu, _ = mpq.cd(Ts["W"], Ts["s"], Ts["V"], cb, Ts["a"], Ts["o"], map_gpu.clone(), n_cd=L.n_cd, group=g)
+    cd_gpu, _ = mpq.cd(Ts["W"], Ts["s"], Ts["V"], cb, Ts["a"], Ts["o"], map_gpu.clone(), n_cd=L.n_cd, group=g,
+                       digits=dg)
     torch.cuda.synchronize()
     r1_gpu, g1_gpu, map_gpu, cd_gpu = host(R1), host(g1), host(map_gpu), host(cd_gpu)
     same_as_full = bool(np.array_equal(cd_gpu, gpu["codes"][rows]))
@@ -106,7 +117,8 @@ def test_config_parity(name):
     cd_ref = np.stack([r["codes"] for r in cdr])
 
     report = {}
-    report["step"] = {k: float(f"{v:.3g}") for k, v in teacher_forced_steps(mpq, L, Ts, refs, k_rows, cb).items()}
+    report["step"] = {k: float(f"{v:.3g}") for k, v in
+                      teacher_forced_steps(mpq, L, Ts, refs, k_rows, cb, dg).items()}
     report["rows_match_full_solve"] = same_as_full
     report["map_agree"] = float((map_gpu == map_ref).mean())
     report["cd_agree"] = float((cd_gpu == cd_ref).mean())
