@@ -271,7 +271,7 @@ def main():
                     help="skip the extra profiled step that gives the per-group time split (keeps a counter pass "
                          "to one solve's dispatches: rocprofv3 --pmc has crashed in its dispatch interception after "
                          "about 20 000 dispatches in one process)")
-    ap.add_argument("--only", choices=["linear"], default=None,
+    ap.add_argument("--only", choices=["linear", "cd"], default=None,
                     help="run only two calls of the linear module (mpq_linear_step) on the workload's shapes and "
                          "exit: a short program with few dispatches for counter passes over the dominant kernels")
     ap.add_argument("--host-qr", action="store_true",
@@ -331,6 +331,17 @@ def main():
             mpq.linear_step(R2, g2, beta, W, s, V, damping=L.damping, digits=DIGITS)
             torch.cuda.synchronize()
             log(f"[bench] linear module call {k + 1}/2 done")
+        return
+    if args.only == "cd":
+        # one CD sweep alone, from the round-to-nearest codes of the prologue
+        cb = mpq.prepare_codebook(L.E, dev)
+        pro = mpq.prologue(W, s, V, cb, a, o, digits=DIGITS)
+        codes = pro["rtn_codes"].clone()
+        torch.cuda.synchronize()
+        log("[bench] prologue done")
+        mpq.cd(W, s, V, cb, a, o, codes, n_cd=1, digits=DIGITS)
+        torch.cuda.synchronize()
+        log("[bench] one CD sweep done")
         return
     ws = torch.empty(mpq.workspace_bytes(L.m, L.n, L.r, L.K, L.d), dtype=torch.uint8, device=dev)
     kw = dict(T_vamp=L.T_vamp, n_cd=L.n_cd, damping=L.damping, workspace=ws, group=L.group, digits=DIGITS)
