@@ -252,10 +252,11 @@ const char* mpq_hip_error_name(void);
  * designs 1 (denoiser, rank-space linear module), 2 (beta M-step, damping),
  * 3 (marginal MAP, exact block CD) and the hyper-parameter paragraph
  * (gamma1^0 = 1 / MSE(w, w_rtn), S_CD sweeps with early stop).  The VAMP
- * state is float64; the linear module's rank-space products are float64
- * accurate (exact int8 digit products summed in int32 on the matrix cores,
- * about 1e-10 relative, or fp64 MFMA with MPQ_F_LINEAR_F64); CD decides in
- * float64, on H and its gradient formed the same way.
+ * state is float64; the linear module's rank-space products are exact int8
+ * digit products summed in int32 on the matrix cores (mpq_options.digits:
+ * 5 digits by default, about 1e-10 relative; 4 digits, about 1e-8), or fp64
+ * MFMA with MPQ_F_LINEAR_F64; CD decides in float64, on H and its gradient
+ * formed the same way.
  *
  * Inputs: W, s, V, row_scale, row_offset as in the conventions; T_vamp >= 0;
  * n_cd >= 0; damping in (0, 1] (the weight of the new beta).

@@ -51,8 +51,8 @@ __global__ __launch_bounds__(PROBE_WG) void probe_mfma_bf16_kernel(const v4u* __
 }
 
 // Uniformly random bytes (the int8 probe's operands: the digit planes of the
-// float64-accurate products are balanced base-256 digits, i.e. close to
-// uniform bytes), 1024 words.
+// int8 digit products are balanced base-256 digits, i.e. close to uniform
+// bytes), 1024 words.
 __global__ void probe_init_i8_kernel(uint32_t* w) {
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   uint32_t x = i * 2654435761u + 0x9e3779b9u;
@@ -64,7 +64,7 @@ __global__ void probe_init_i8_kernel(uint32_t* w) {
   w[i] = x;
 }
 
-// v_mfma_i32_16x16x64_i8 (the float64-accurate digit products): 16
+// v_mfma_i32_16x16x64_i8 (the int8 digit products): 16
 // independent accumulators per wave, the operands cycling through 4 x 4
 // random register pairs so that every instruction sees new bytes (the MFMA
 // draws more power, and on this GPU runs slower, on changing random bytes
