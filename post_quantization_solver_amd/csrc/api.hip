@@ -835,11 +835,27 @@ int run_cd(Ctx& c, const float* W, const float* a, const float* o, int n_cd, int
       // operand is H[j][tile]
       TIMED(c, MPQ_PROF_CD_GEMM, launch_fill_i32(nmoved, 1, 0, c.st));
       TIMED(c, MPQ_PROF_CD_GEMM, launch_collect_nonzero_rows(Dl, L.m, kw, mrows, nmoved, c.st));
-      Gemm64Args gu = gemm64((int)L.m, (int)L.n, kw, Dl, kw, nullptr, L.n, Gf, L.n);
-      gu.B64 = H + j0;
-      gu.rows = mrows;
-      gu.nrows = nmoved;
-      TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_SUB_INPLACE, true, gu, c.st));
+      if (c.digits) {
+        // the moved rows' Delta split in list order, times the digits of H
+        // (split once for G) over the tile's k range, subtracted from their
+        // rows of G
+        TIMED(c, MPQ_PROF_CD_GEMM, launch_digit_split_rows(Dl, L.m, kw, kw, mrows, nmoved, c.pi(R_DEA),
+                                                           c.dp(R_DPA), c.dg_s, c.st));
+        DigitGemmArgs gu = digit_args(c, (int)L.m, (int)L.n, kw, R_DPN, R_DEN);
+        gu.C = Gf;
+        gu.ldc = L.n;
+        gu.rows = mrows;
+        gu.nrows = nmoved;
+        gu.ktB = (int)((L.n + 63) / 64);
+        gu.kt0B = (int)(j0 / 64);
+        TIMED(c, MPQ_PROF_CD_GEMM, launch_digit_gemm(EPI_SUB_INPLACE, gu, c.st));
+      } else {
+        Gemm64Args gu = gemm64((int)L.m, (int)L.n, kw, Dl, kw, nullptr, L.n, Gf, L.n);
+        gu.B64 = H + j0;
+        gu.rows = mrows;
+        gu.nrows = nmoved;
+        TIMED(c, MPQ_PROF_CD_GEMM, launch_gemm64(EPI_SUB_INPLACE, true, gu, c.st));
+      }
     }
     if (cd_changes) TIMED(c, MPQ_PROF_OTHER, launch_record_i32(chg, L.m, cd_changes, n_cd, sw, c.st));
     if (sweeps) TIMED(c, MPQ_PROF_OTHER, launch_sweep_count(chg, L.m, sw, c.pi(R_ACTIVE), sweeps, c.st));

@@ -101,14 +101,20 @@ bool digit_count_ok(int S) { return S == 4 || S == 5; }
 // row holding NaN or inf); one wave per row.
 template <typename T>
 __global__ __launch_bounds__(256) void digit_exp_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t ld,
-                                                        int32_t* __restrict__ E) {
+                                                        const int32_t* __restrict__ list,
+                                                        const int32_t* __restrict__ count, int32_t* __restrict__ E) {
   const int lane = threadIdx.x & 63;
   const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= rows) return;
+  if (list && i >= (int64_t)count[0]) {   // past the list: a zero row
+    if (lane == 0) E[i] = 0;
+    return;
+  }
+  const int64_t src = list ? (int64_t)list[i] : i;
   double mx = 0.0;
   bool bad = false;
   for (int64_t k = lane; k < K; k += 64) {
-    const double v = (double)X[i * ld + k];
+    const double v = (double)X[src * ld + k];
     bad = bad || !isfinite(v);
     mx = fmax(mx, fabs(v));
   }
@@ -143,6 +149,8 @@ __device__ __forceinline__ void digits_of(double v, int e, int (&d)[S]) {
 constexpr int DG_SPLIT_PITCH = 65;   // doubles per LDS row (one of padding)
 template <typename T, int S>
 __global__ __launch_bounds__(256) void digit_split_kernel(const T* __restrict__ X, int64_t rows, int64_t K, int64_t ld,
+                                                          const int32_t* __restrict__ list,
+                                                          const int32_t* __restrict__ count,
                                                           const int32_t* __restrict__ E, int64_t nrt, int64_t nkt,
                                                           uint8_t* __restrict__ planes) {
   __shared__ double tile[4][16 * DG_SPLIT_PITCH];
@@ -151,6 +159,8 @@ __global__ __launch_bounds__(256) void digit_split_kernel(const T* __restrict__ 
   const int64_t pos = (int64_t)blockIdx.x * 4 + w;   // chunk position = rt * nkt + kt
   if (pos >= nrt * nkt) return;                       // uniform per wave; no block-wide barrier below
   const int64_t rt = pos / nkt, kt = pos - rt * nkt;
+  // with a row list, logical row r is X's row list[r] (rows past the list are zero)
+  const int64_t live = list ? min(rows, (int64_t)count[0]) : rows;
   double* tl = tile[w];
   // coalesced loads: lanes 0..31 take one row, 32..63 the next, two consecutive values each
 #pragma unroll
@@ -160,8 +170,8 @@ __global__ __launch_bounds__(256) void digit_split_kernel(const T* __restrict__ 
     const int c0 = 2 * (lane & 31);
     const int64_t k = kt * 64 + c0;
     double v0 = 0.0, v1 = 0.0;
-    if (row < rows) {
-      const T* src = X + row * ld + k;
+    if (row < live) {
+      const T* src = X + (list ? (int64_t)list[row] : row) * ld + k;
       if (k < K) v0 = (double)src[0];
       if (k + 1 < K) v1 = (double)src[1];
     }
@@ -173,8 +183,8 @@ __global__ __launch_bounds__(256) void digit_split_kernel(const T* __restrict__ 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int i = lane & 15, g = lane >> 4;
   const int64_t row = rt * 16 + i;
-  const int e = row < rows ? E[row] : 0;
-  const bool ok = row < rows && e != DG_EXP_NONFINITE;
+  const int e = row < live ? E[row] : 0;
+  const bool ok = row < live && e != DG_EXP_NONFINITE;
   uint32_t wd[S][4];
 #pragma unroll
   for (int p = 0; p < S; ++p)
@@ -198,14 +208,20 @@ __global__ __launch_bounds__(256) void digit_split_kernel(const T* __restrict__ 
 // The planes from given row exponents.
 template <typename T>
 static hipError_t split_planes(const T* X, int64_t rows, int64_t K, int64_t ld, const int32_t* E, uint8_t* planes,
-                               int S, hipStream_t st) {
+                               int S, hipStream_t st, const int32_t* list = nullptr, const int32_t* count = nullptr) {
   if (rows <= 0 || K <= 0) return hipSuccess;
   const int64_t nrt = (rows + DG_TILE - 1) / DG_TILE * DG_RT;
   const int64_t nkt = (K + 63) / 64;
   const dim3 grid((unsigned)((nrt * nkt + 3) / 4)), block(256);
   switch (S) {
-    case 4: hipLaunchKernelGGL((digit_split_kernel<T, 4>), grid, block, 0, st, X, rows, K, ld, E, nrt, nkt, planes); break;
-    case 5: hipLaunchKernelGGL((digit_split_kernel<T, 5>), grid, block, 0, st, X, rows, K, ld, E, nrt, nkt, planes); break;
+    case 4:
+      hipLaunchKernelGGL((digit_split_kernel<T, 4>), grid, block, 0, st, X, rows, K, ld, list, count, E, nrt, nkt,
+                         planes);
+      break;
+    case 5:
+      hipLaunchKernelGGL((digit_split_kernel<T, 5>), grid, block, 0, st, X, rows, K, ld, list, count, E, nrt, nkt,
+                         planes);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -213,11 +229,18 @@ static hipError_t split_planes(const T* X, int64_t rows, int64_t K, int64_t ld, 
 
 template <typename T>
 static hipError_t split(const T* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes, int S,
-                        hipStream_t st) {
+                        hipStream_t st, const int32_t* list = nullptr, const int32_t* count = nullptr) {
   if (rows <= 0 || K <= 0) return hipSuccess;
   if (!digit_count_ok(S)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(digit_exp_kernel<T>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, X, rows, K, ld, E);
-  return split_planes<T>(X, rows, K, ld, E, planes, S, st);
+  hipLaunchKernelGGL(digit_exp_kernel<T>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, X, rows, K, ld, list,
+                     count, E);
+  return split_planes<T>(X, rows, K, ld, E, planes, S, st, list, count);
+}
+
+hipError_t launch_digit_split_rows(const double* X, int64_t rows_max, int64_t K, int64_t ld, const int32_t* list,
+                                   const int32_t* count, int32_t* E, uint8_t* planes, int S, hipStream_t st) {
+  if (!list || !count) return hipErrorInvalidValue;
+  return split<double>(X, rows_max, K, ld, E, planes, S, st, list, count);
 }
 
 hipError_t launch_digit_split(const double* X, int64_t rows, int64_t K, int64_t ld, int32_t* E, uint8_t* planes,
@@ -245,7 +268,7 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
 template <int S>
 __device__ __forceinline__ void fetch_step(uint8_t (*stage)[DG_CHUNK], const uint8_t* __restrict__ Ap,
                                            const uint8_t* __restrict__ Bp, int64_t rt0, int64_t ct0, int64_t nkt,
-                                           int64_t kt, int wave, int lane) {
+                                           int64_t nktB, int64_t kt0B, int64_t kt, int wave, int lane) {
   constexpr int CH = dg_chunks<S>();
   static_assert(CH % DG_WAVES == 0, "every wave fetches the same number of chunks");
 #pragma unroll
@@ -258,7 +281,7 @@ __device__ __forceinline__ void fetch_step(uint8_t (*stage)[DG_CHUNK], const uin
     } else {
       const int cc = c - DG_RT * S;
       const int ct = cc / S, q = cc - ct * S;
-      src = Bp + (((ct0 + ct) * nkt + kt) * S + q) * DG_CHUNK;
+      src = Bp + (((ct0 + ct) * nktB + kt0B + kt) * S + q) * DG_CHUNK;
     }
     __builtin_amdgcn_global_load_lds(src + 16 * lane, (lds_ptr_t)stage[c], 16, 0, 0);
   }
@@ -279,10 +302,18 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
   const int tm = (g.M + DG_TILE - 1) / DG_TILE, tn = (g.N + DG_TILE - 1) / DG_TILE;
   const int T = g.lower ? dg_lower_tiles(tm) : tm * tn;
   const int per = (T + 7) / 8;
-  const int tile = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  int tile = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  // a row map's live rows are known on the device only: tiles go out row
+  // tile by row tile, so the live ones spread over every XCD
+  const int Mlive = g.rows ? min(g.M, *g.nrows) : g.M;
+  if (g.rows) tile = (int)blockIdx.x;
   if (tile >= T) return;
   int tr, tc;
-  if (g.lower) {
+  if (g.rows) {
+    tr = tile / tn;
+    tc = tile - tr * tn;
+    if (tr * DG_TILE >= Mlive) return;
+  } else if (g.lower) {
     dg_lower_tile(tile, tm, tr, tc);
   } else {
     const int group = tile / (DG_GROUP_M * tn);
@@ -295,6 +326,7 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
   const int row0 = tr * DG_TILE, col0 = tc * DG_TILE;
   const int64_t rt0 = (int64_t)tr * DG_RT, ct0 = (int64_t)tc * DG_RT;
   const int64_t nkt = (g.K + 63) / 64;
+  const int64_t nktB = g.ktB > 0 ? g.ktB : nkt, kt0B = g.kt0B;
 
   v4i acc[S][2][4];
 #pragma unroll
@@ -304,12 +336,12 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
 #pragma unroll
       for (int sj = 0; sj < 4; ++sj) acc[l][si][sj] = (v4i){0, 0, 0, 0};
 
-  fetch_step<S>(lds[0], g.Ap, g.Bp, rt0, ct0, nkt, 0, wave, lane);
+  fetch_step<S>(lds[0], g.Ap, g.Bp, rt0, ct0, nkt, nktB, kt0B, 0, wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int64_t kt = 0; kt < nkt; ++kt) {
     const int cur = (int)(kt & 1);
-    if (kt + 1 < nkt) fetch_step<S>(lds[cur ^ 1], g.Ap, g.Bp, rt0, ct0, nkt, kt + 1, wave, lane);
+    if (kt + 1 < nkt) fetch_step<S>(lds[cur ^ 1], g.Ap, g.Bp, rt0, ct0, nkt, nktB, kt0B, kt + 1, wave, lane);
     const v4i* Ast = reinterpret_cast<const v4i*>(lds[cur][0]);
     const v4i* Bst = reinterpret_cast<const v4i*>(lds[cur][DG_RT * S]);
     v4i af[2][S];
@@ -409,18 +441,21 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int row = row0 + wm * 32 + si * 16 + 4 * lg + v;
-      if (row >= g.M) continue;
+      if (row >= Mlive) continue;
       const int ea = g.EA[row];
       const double coef = EPI == EPI_AXPY_W ? g.rowa[row] : 0.0;
+      const int64_t crow = g.rows ? (int64_t)g.rows[row] : (int64_t)row;
 #pragma unroll
       for (int sj = 0; sj < 4; ++sj) {
         const int col = col0 + wn * 64 + sj * 16 + li;
         if (col >= g.N) continue;
         const bool bad = ea == DG_EXP_NONFINITE || fe[sj] == DG_EXP_NONFINITE;
         const double prod = bad ? __builtin_nan("") : ldexp(val[si][sj][v], ea + fe[sj] - 12);
-        double* cp = g.C + (int64_t)row * g.ldc + col;
+        double* cp = g.C + crow * g.ldc + col;
         if (EPI == EPI_STORE)
           *cp = prod;
+        else if (EPI == EPI_SUB_INPLACE)
+          *cp -= prod;
         else   // EPI_AXPY_W: r2 + coef acc with r2 = W - X
           *cp = fma(coef, prod, (double)g.W[(int64_t)row * g.ldw + col] - g.X[(int64_t)row * g.ldx + col]);
       }
@@ -431,6 +466,7 @@ template <int S>
 static hipError_t launch_epi(int epi, dim3 grid, dim3 block, const DigitGemmArgs& g, hipStream_t st) {
   switch (epi) {
     case EPI_STORE: hipLaunchKernelGGL((digit_gemm_kernel<EPI_STORE, S>), grid, block, 0, st, g); break;
+    case EPI_SUB_INPLACE: hipLaunchKernelGGL((digit_gemm_kernel<EPI_SUB_INPLACE, S>), grid, block, 0, st, g); break;
     case EPI_ROWSUMSQ_S: hipLaunchKernelGGL((digit_gemm_kernel<EPI_ROWSUMSQ_S, S>), grid, block, 0, st, g); break;
     case EPI_LINEAR1: hipLaunchKernelGGL((digit_gemm_kernel<EPI_LINEAR1, S>), grid, block, 0, st, g); break;
     case EPI_AXPY_W: hipLaunchKernelGGL((digit_gemm_kernel<EPI_AXPY_W, S>), grid, block, 0, st, g); break;
@@ -443,6 +479,9 @@ hipError_t launch_digit_gemm(int epi, const DigitGemmArgs& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (g.K <= 0 || g.K > DG_MAX_K) return hipErrorInvalidValue;
   if (g.lower && g.M != g.N) return hipErrorInvalidValue;
+  if (g.rows && (!g.nrows || g.lower || epi != EPI_SUB_INPLACE)) return hipErrorInvalidValue;
+  if (g.ktB > 0 && g.kt0B + (g.K + 63) / 64 > g.ktB) return hipErrorInvalidValue;
+  if (g.ktB < 0 || g.kt0B < 0 || (g.kt0B > 0 && g.ktB <= 0)) return hipErrorInvalidValue;
   const int tm = (g.M + DG_TILE - 1) / DG_TILE;
   const int T = g.lower ? dg_lower_tiles(tm) : tm * ((g.N + DG_TILE - 1) / DG_TILE);
   const dim3 grid((unsigned)(8 * ((T + 7) / 8))), block(64 * DG_WAVES);

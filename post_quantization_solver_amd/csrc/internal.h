@@ -74,6 +74,14 @@ struct DigitGemmArgs {
   const float* W; int64_t ldw;
   int lower;                              // only the tiles that touch the lower triangle (M == N)
   int S;                                  // digits per entry of both operands' planes (4 or 5)
+  // optional row map (EPI_SUB_INPLACE only): logical rows 0 .. *nrows - 1 of
+  // A (its planes hold them in that order) are rows rows[0 ..] of C; tiles
+  // past *nrows exit, and the tiles go out row tile by row tile
+  const int32_t* rows;
+  const int32_t* nrows;
+  // B's planes may hold a longer K: ktB k-steps of 64 per row tile (0: K's),
+  // of which the product takes kt0B .. kt0B + ceil(K / 64) - 1
+  int ktB, kt0B;
 };
 size_t digit_plane_bytes(int64_t rows, int64_t K);   // room for any S
 bool digit_count_ok(int S);
@@ -86,6 +94,10 @@ hipError_t launch_digit_split_f32(const float* X, int64_t rows, int64_t K, int64
 // NaN or inf).
 hipError_t launch_digit_split_planes(const double* X, int64_t rows, int64_t K, int64_t ld, const int32_t* E,
                                      uint8_t* planes, int S, hipStream_t st);
+// The split of rows list[0 .. *count - 1] of X (rows_max rows of planes
+// and exponents, zero past *count): the A operand of a row-mapped product.
+hipError_t launch_digit_split_rows(const double* X, int64_t rows_max, int64_t K, int64_t ld, const int32_t* list,
+                                   const int32_t* count, int32_t* E, uint8_t* planes, int S, hipStream_t st);
 hipError_t launch_digit_gemm(int epi, const DigitGemmArgs& g, hipStream_t st);
 constexpr int DG_EXP_NONFINITE = 0x7fffffff;   // row exponent of a row holding NaN or inf
 
