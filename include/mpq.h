@@ -225,7 +225,8 @@ typedef struct {
                                       NaN or infinite or a row scale is <= 0; the call waits for the
                                       scan's verdict */
 #define MPQ_F_LINEAR_F64     64u   /* run the float64 products (the linear module's rank-space products
-                                      and CD's H = VS VS^T and G = (W - X) H) on the fp64 matrix cores
+                                      and CD's H = VS VS^T, G = (W - X) H and its row updates
+                                      G -= Delta H[tile, :]) on the fp64 matrix cores
                                       instead of the int8 digit GEMM (for A/B checks; the digit GEMM
                                       also gives way by itself when n or r exceeds 32767) */
 

@@ -405,7 +405,7 @@ struct Ctx {
   // the linear module's products on the int8 digit GEMM (else on the fp64
   // matrix cores)
   bool digits = false;
-  int dg_s = 5;   // digits per operand entry of the digit products
+  int dg_s = MPQ_DIGITS_DEFAULT;   // digits per operand entry of the digit products
   uint8_t* dp(Region k) const { return reinterpret_cast<uint8_t*>(ws + L.off[k]); }
   // d = 8 codebooks that are the first K points of E8 in (norm, lex) order:
   // the denoiser runs the forward-backward pass over coordinates

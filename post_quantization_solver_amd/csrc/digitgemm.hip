@@ -1,7 +1,10 @@
-// The linear module's rank-space products (and CD's H and G) on the int8
-// matrix cores (v_mfma_i32_16x16x64_i8), for K <= DG_MAX_K:
+// The solver's float64-class products on the int8 matrix cores
+// (v_mfma_i32_16x16x64_i8), for K <= DG_MAX_K: the linear module's
+// rank-space products, and CD's H = VS VS^T, G = (W - X) H and its row
+// updates G -= Delta H[tile, :]:
 //
-//   C[M x N] = A[M x K] * B[N x K]^T,  A float64 (w - r2, or z), B float32 (V^T or V).
+//   C[M x N] (=, -=) A[M x K] * B[N x K]^T,  A and B float64 (or B float32:
+//   V^T, V), each split once into digit planes.
 //
 // Digit split (an exact integer form of each operand), S = 4 or 5 digits.
 // Row i of A is scaled by its own power of two 2^E_i > max_k |A_ik| and
@@ -34,7 +37,9 @@
 // wave owns 32 x 64 outputs: 2 x 4 sub-tiles of 16 x 16, S int32
 // accumulators each.  Tiles go to the XCDs in contiguous runs and, within a
 // run, in groups of 8 tile rows column by column, so the tiles resident on one
-// XCD share their A and B panels in its L2.
+// XCD share their A and B panels in its L2.  A row-mapped product (the CD row
+// updates, whose live rows are counted on the device) takes its tiles row
+// tile by row tile instead, so that the few live ones spread over the XCDs.
 #include <math.h>
 #include <limits.h>
 #include "mpq_device.h"
