@@ -135,7 +135,7 @@ struct Layout {
 enum Region {
   R_VT, R_VS64, R_R1, R_R2, R_X1, R_Z, R_VBLK, R_ROWS, R_PART, R_GT, R_DELTA, R_HD, R_PS, R_PI, R_CHG, R_CODES,
   R_FLAG, R_D64, R_TKEY, R_QF, R_ANCH, R_LAM, R_CTMP, R_GDIAG, R_MROWS, R_HFULL, R_G64, R_ACTIVE, R_CHECK,
-  R_DPA, R_DPVT, R_DPV, R_DEA, R_DEVT, R_DEV, R_DPN, R_DEN, R_LASTMV, R_CDROWS, R_COUNT
+  R_DPA, R_DPVT, R_DPV, R_DEA, R_DEVT, R_DEV, R_DPN, R_DEN, R_LASTMV, R_CDROWS, R_PMAX, R_COUNT
 };
 
 // The linear module's products take the int8 digit GEMM when both of its
@@ -206,6 +206,7 @@ Layout make_layout(int64_t m, int64_t n, int64_t r, int64_t K, int64_t d, bool g
   sz[R_DPVT] = dg ? digit_plane_bytes(r, n) : 0;
   sz[R_DPV] = dg ? digit_plane_bytes(n, r) : 0;
   sz[R_DEA] = dg ? (size_t)m * i32 : 0;
+  sz[R_PMAX] = dg ? (size_t)m * L.ncoltiles * f64 : 0;   // the first product's per-tile max |z|
   sz[R_DEVT] = dg ? (size_t)r * i32 : 0;
   sz[R_DEV] = dg ? (size_t)n * i32 : 0;
   // CD's float64 products: the digits of VS (n x r), then of H (n x n)
@@ -583,6 +584,7 @@ int run_linear(Ctx& c, const float* W, const float* s, const float* V, double* R
     g1.rowb = c.gamma2();
     g1.partial = c.d(R_PART);
     g1.ldp = gemm_col_tiles((int)L.r);
+    g1.pmax = c.d(R_PMAX);
     TIMED(c, MPQ_PROF_LINEAR1, launch_digit_gemm(EPI_LINEAR1, g1, c.st));
   } else {
     Gemm64Args g1 = gemm64((int)L.m, (int)L.r, (int)L.n, D2, L.n, c.f(R_VT), L.n, c.d(R_Z), L.r);
@@ -593,10 +595,14 @@ int run_linear(Ctx& c, const float* W, const float* s, const float* V, double* R
     g1.ldp = gemm_col_tiles((int)L.r);
     TIMED(c, MPQ_PROF_LINEAR1, launch_gemm64(EPI_LINEAR1, true, g1, c.st));
   }
+  // with the digit products, the M-step kernel also turns the first
+  // product's per-tile max |z| into z's row exponents for its split
   TIMED(c, MPQ_PROF_BETA, launch_beta(L.m, L.n, L.r, s, c.d(R_PART), gemm_col_tiles((int)L.r), c.gamma2(), damping,
-                                      fixed_beta, beta, gamma1, c.coef(), c.st));
+                                      fixed_beta, beta, gamma1, c.coef(), c.st, c.digits ? c.d(R_PMAX) : nullptr,
+                                      c.digits ? c.pi(R_DEA) : nullptr));
   if (c.digits) {
-    TIMED(c, MPQ_PROF_SPLIT, launch_digit_split(c.d(R_Z), L.m, L.r, L.r, c.pi(R_DEA), c.dp(R_DPA), c.dg_s, c.st));
+    TIMED(c, MPQ_PROF_SPLIT, launch_digit_split_planes(c.d(R_Z), L.m, L.r, L.r, c.pi(R_DEA), c.dp(R_DPA), c.dg_s,
+                                                       c.st));
     DigitGemmArgs g2 = digit_args(c, (int)L.m, (int)L.n, (int)L.r, R_DPV, R_DEV);
     g2.C = R1; g2.ldc = L.n;
     g2.rowa = c.coef();

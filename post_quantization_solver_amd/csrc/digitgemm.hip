@@ -391,7 +391,8 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
   }
   if constexpr (EPI == EPI_ROWSUMSQ_S || EPI == EPI_LINEAR1) {
     double* red = reinterpret_cast<double*>(lds[0][0]);   // the operand stages are free now
-    double rs[2][4];
+    double* redm = red + 2 * DG_TILE;                      // EPI_LINEAR1: the rows' max |z|
+    double rs[2][4], rm[2][4];
 #pragma unroll
     for (int si = 0; si < 2; ++si)
 #pragma unroll
@@ -403,7 +404,7 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
           beta = g.rowa[row];
           gam = g.rowb[row];
         }
-        double acc_r = 0.0;
+        double acc_r = 0.0, max_r = 0.0;
 #pragma unroll
         for (int sj = 0; sj < 4; ++sj) {
           const int col = col0 + wn * 64 + sj * 16 + li;
@@ -416,7 +417,9 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
               acc_r = fma(u, u, acc_r);
             } else {
               const double den = fma(beta * sl, sl, gam);
-              g.C[(int64_t)row * g.ldc + col] = beta * sl * u / den;
+              const double zv = beta * sl * u / den;
+              g.C[(int64_t)row * g.ldc + col] = zv;
+              max_r = fmax(max_r, isfinite(zv) ? fabs(zv) : INFINITY);
               const double e = gam * u / den;
               acc_r = fma(e, e, acc_r);
             }
@@ -427,17 +430,28 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
         acc_r += __shfl_xor(acc_r, 4, 64);
         acc_r += __shfl_xor(acc_r, 8, 64);
         rs[si][v] = acc_r;
+        if (EPI == EPI_LINEAR1 && g.pmax) {
+#pragma unroll
+          for (int msk = 1; msk <= 8; msk <<= 1) max_r = fmax(max_r, __shfl_xor(max_r, msk, 64));
+        }
+        rm[si][v] = max_r;
       }
     if (li == 0) {
 #pragma unroll
       for (int si = 0; si < 2; ++si)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[wn * DG_TILE + wm * 32 + si * 16 + 4 * lg + v] = rs[si][v];
+        for (int v = 0; v < 4; ++v) {
+          red[wn * DG_TILE + wm * 32 + si * 16 + 4 * lg + v] = rs[si][v];
+          if (EPI == EPI_LINEAR1 && g.pmax) redm[wn * DG_TILE + wm * 32 + si * 16 + 4 * lg + v] = rm[si][v];
+        }
     }
     __syncthreads();
     if (t < DG_TILE) {
       const int row = row0 + t;
-      if (row < g.M) g.partial[(int64_t)row * g.ldp + tc] = red[t] + red[DG_TILE + t];
+      if (row < g.M) {
+        g.partial[(int64_t)row * g.ldp + tc] = red[t] + red[DG_TILE + t];
+        if (EPI == EPI_LINEAR1 && g.pmax) g.pmax[(int64_t)row * g.ldp + tc] = fmax(redm[t], redm[DG_TILE + t]);
+      }
     }
     return;
   }

@@ -70,6 +70,9 @@ struct DigitGemmArgs {
   const double* rowa;
   const double* rowb;
   double* partial; int64_t ldp;
+  // EPI_LINEAR1 (optional): per (row, column tile) max |C| (+inf for a
+  // non-finite entry), at the stride of `partial`, for C's digit exponents
+  double* pmax;
   const double* X; int64_t ldx;
   const float* W; int64_t ldw;
   int lower;                              // only the tiles that touch the lower triangle (M == N)
@@ -144,9 +147,12 @@ hipError_t launch_extrinsic(const double* R1, const double* xhat, const double* 
                             hipStream_t st);
 
 // beta M-step + linear-side extrinsic precision.
+// With pmax (the first product's per-tile max |z|, as `partial`), also
+// zexp[i]: the digit split's row exponent of z (DG_EXP_NONFINITE for a row
+// holding NaN or inf, 0 for a zero or frozen row).
 hipError_t launch_beta(int64_t m, int64_t n, int64_t r, const float* s, const double* partial, int nparts,
                        const double* gamma2, double damping, int fixed_beta, double* beta, double* gamma1,
-                       double* coef, hipStream_t st);
+                       double* coef, hipStream_t st, const double* pmax = nullptr, int32_t* zexp = nullptr);
 hipError_t launch_beta_lin(int64_t m, const double* gamma1, const double* beta, double* out, double* gamma2,
                            hipStream_t st);
 

@@ -194,13 +194,26 @@ __global__ __launch_bounds__(ROW_THREADS) void beta_kernel(int64_t n, int64_t r,
                                                           const double* __restrict__ partial, int nparts,
                                                           const double* __restrict__ gamma2, double damping,
                                                           int fixed_beta, double* __restrict__ beta,
-                                                          double* __restrict__ gamma1, double* __restrict__ coef) {
+                                                          double* __restrict__ gamma1, double* __restrict__ coef,
+                                                          const double* __restrict__ pmax,
+                                                          int32_t* __restrict__ zexp) {
   __shared__ double sh[ROW_THREADS];
   const int64_t i = blockIdx.x;
   const int t = threadIdx.x;
-  if (!isfinite(gamma1[i])) {
+  if (!isfinite(gamma1[i])) {   // frozen: z = 0 (the product ran with beta = 0)
     if (t == 0) coef[i] = 0.0;
+    if (t == 0 && zexp) zexp[i] = 0;
     return;
+  }
+  if (zexp) {   // the row exponent of z, as the digit split computes it: max |z| < 2^E
+    double mx = 0.0;
+    for (int p = t; p < nparts; p += ROW_THREADS) mx = fmax(mx, pmax[i * nparts + p]);
+    mx = block_max(mx, sh);
+    if (t == 0) {
+      int e = 0;
+      if (mx > 0.0 && mx != INFINITY) (void)frexp(mx, &e);
+      zexp[i] = mx == INFINITY ? DG_EXP_NONFINITE : e;
+    }
   }
   const double b = beta[i];
   const double g2 = gamma2[i];
@@ -233,10 +246,11 @@ __global__ __launch_bounds__(ROW_THREADS) void beta_kernel(int64_t n, int64_t r,
 
 hipError_t launch_beta(int64_t m, int64_t n, int64_t r, const float* s, const double* partial, int nparts,
                        const double* gamma2, double damping, int fixed_beta, double* beta, double* gamma1,
-                       double* coef, hipStream_t st) {
+                       double* coef, hipStream_t st, const double* pmax, int32_t* zexp) {
   if (m <= 0) return hipSuccess;
+  if (!pmax != !zexp) return hipErrorInvalidValue;
   hipLaunchKernelGGL(beta_kernel, dim3((unsigned)m), dim3(ROW_THREADS), 0, st, n, r, s, partial, nparts, gamma2,
-                     damping, fixed_beta, beta, gamma1, coef);
+                     damping, fixed_beta, beta, gamma1, coef, pmax, zexp);
   return hipGetLastError();
 }
 
