@@ -44,6 +44,7 @@
 #include <limits.h>
 #include "mpq_device.h"
 #include "internal.h"
+#include "tile_order.h"
 
 namespace mpq {
 
@@ -56,40 +57,6 @@ constexpr int DG_RT = DG_TILE / 16; // row tiles per output tile side
 constexpr int DG_WAVES = 8;
 template <int S>
 constexpr int dg_chunks() { return 2 * DG_RT * S; }   // chunks per K step (A and B)
-constexpr int DG_GROUP_M = 8;       // tile rows per group of the tile order
-
-// Lower-triangle tile order (tc <= tr, square M = N): the same groups of
-// DG_GROUP_M tile rows column by column, but each column of a group starts at
-// the diagonal and the columns end at the group's last row, so only tiles
-// that touch the lower triangle are enumerated and the contiguous runs of the
-// XCDs carry equal work.  Tiles of group q before it: GM^2 q (q - 1) / 2 +
-// q GM (GM + 1) / 2.
-__host__ __device__ inline int dg_lower_before(int q) {
-  return DG_GROUP_M * DG_GROUP_M * q * (q - 1) / 2 + q * DG_GROUP_M * (DG_GROUP_M + 1) / 2;
-}
-__host__ __device__ inline int dg_lower_tiles(int tm) {
-  const int full = tm / DG_GROUP_M, gm = tm - full * DG_GROUP_M;
-  return dg_lower_before(full) + full * DG_GROUP_M * gm + gm * (gm + 1) / 2;
-}
-__host__ __device__ inline void dg_lower_tile(int t, int tm, int& tr, int& tc) {
-  int q = 0;
-  while ((q + 1) * DG_GROUP_M < tm && dg_lower_before(q + 1) <= t) ++q;
-  const int first = q * DG_GROUP_M, gm = min(tm - first, DG_GROUP_M);
-  int l = t - dg_lower_before(q);
-  if (l < first * gm) {   // columns left of the group's diagonal block: gm tiles each
-    tc = l / gm;
-    tr = first + l % gm;
-    return;
-  }
-  l -= first * gm;   // diagonal block: column first + u holds gm - u tiles
-  int u = 0;
-  while (l >= gm - u) {
-    l -= gm - u;
-    ++u;
-  }
-  tc = first + u;
-  tr = first + u + l;
-}
 
 // Bytes of the digit planes of a rows x K operand (row tiles padded to whole
 // output tiles, K to whole steps), for up to DG_S_MAX digits.
