@@ -135,7 +135,7 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_query_kernel(int64_t m, int
                                                        const int32_t* __restrict__ codes, const float* __restrict__ rmaxp,
                                                        uint32_t* __restrict__ qf, float* __restrict__ tau) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * CDU_WAVES + (threadIdx.x >> 6);
+  const int64_t i = (int64_t)blockIdx.x * CDU_WAVES + wave_id();
   if (i >= m) return;
   const double gp = Gt[i * kd + 8 * bl + (lane & 7)];
   cd_query_row(lane, i, bl, kd, gp, Ht, e32 + (int64_t)safe_code(codes[i * (n / 8) + b], K) * 8, (double)a[i],
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
   if ((int64_t)blockIdx.y * CDL_ROWS_WG >= cnt) return;
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  const int wave = wave_id();
   const int j = lane & 15;
   const int g = lane >> 4;
   const int cw_base = blockIdx.x * CDL_CW_WG;
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
   const int64_t cnt = rows ? (int64_t)rcount[0] : m;
   if ((int64_t)blockIdx.x * CDU_WAVES >= cnt) return;
   const int lane = threadIdx.x & 63;
-  const int64_t x_w = (int64_t)blockIdx.x * CDU_WAVES + (threadIdx.x >> 6);   // list position
+  const int64_t x_w = (int64_t)blockIdx.x * CDU_WAVES + wave_id();   // list position
   const bool live = x_w < cnt;             // waves past the list's end only help stage the slab
   const int64_t x = live ? x_w : cnt - 1;
   const int64_t i = rows ? (int64_t)rows[x] : x;

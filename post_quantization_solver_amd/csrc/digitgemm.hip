@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void digit_exp_kernel(const T* __restrict__ X,
                                                         const int32_t* __restrict__ list,
                                                         const int32_t* __restrict__ count, int32_t* __restrict__ E) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t i = (int64_t)blockIdx.x * 4 + wave_id();
   if (i >= rows) return;
   if (list && i >= (int64_t)count[0]) {   // past the list: a zero row
     if (lane == 0) E[i] = 0;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void digit_split_kernel(const T* __restrict__ 
                                                           uint8_t* __restrict__ planes) {
   __shared__ double tile[4][16 * DG_SPLIT_PITCH];
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = wave_id();
   const int64_t pos = (int64_t)blockIdx.x * 4 + w;   // chunk position = rt * nkt + kt
   if (pos >= nrt * nkt) return;                       // uniform per wave; no block-wide barrier below
   const int64_t rt = pos / nkt, kt = pos - rt * nkt;
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(64 * DG_WAVES) void digit_gemm_kernel(DigitGemmArgs
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2][dg_chunks<S>()][DG_CHUNK];
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  const int wave = wave_id();
   const int wm = wave >> 1;   // 4 wave rows of 32
   const int wn = wave & 1;    // 2 wave columns of 64
   const int li = lane & 15;

@@ -558,7 +558,7 @@ __global__ __launch_bounds__(64 * E8DP_WAVES) void e8dp_kernel(const double* __r
   using Coef = std::conditional_t<FIX, E8FixCoef, E8RowCoef>;
   __shared__ Coef coef[E8DP_WAVES * 4];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int row = lane >> 4, j = lane & 15;
   Coef& cf = coef[wave * 4 + row];
   const int64_t B = n / 8;
@@ -851,7 +851,7 @@ __global__ __launch_bounds__(64 * E8DP_WAVES) void e8_nearest_kernel(const TR* _
                                                          int32_t* __restrict__ codes) {
   __shared__ E8RowCoef coef[E8DP_WAVES * 4];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int row = lane >> 4, j = lane & 15;
   const int64_t q = ((int64_t)blockIdx.x * E8DP_WAVES + wave) * 4 + row;
   e8_nearest_block(coef[wave * 4 + row], j, q, q < m * (n / 8), R, n, a, o, P, keys, kidx, K, codes);
@@ -869,7 +869,7 @@ __global__ __launch_bounds__(64 * E8DP_WAVES) void e8_nearest_list_kernel(const 
                                                               int32_t* __restrict__ codes) {
   __shared__ E8RowCoef coef[E8DP_WAVES * 4];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int row = lane >> 4, j = lane & 15;
   const int64_t cnt = *count;
   for (int64_t base = (int64_t)blockIdx.x * E8DP_WAVES * 4; base < cnt; base += (int64_t)gridDim.x * E8DP_WAVES * 4) {

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void gemm64_nt_kernel(Gemm64Args g) {
   __shared__ double Bs[2][GEMM_BN * LDS64];
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  const int wave = wave_id();
   const int wr = (wave >> 1) * 64;
   const int wc = (wave & 1) * 64;
   const int li = lane & 15;
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256) void collect_nonzero_rows_kernel(const double*
                                                                    int32_t* __restrict__ list,
                                                                    int32_t* __restrict__ count) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t i = (int64_t)blockIdx.x * 4 + wave_id();
   if (i >= m) return;
   bool nz = false;
   for (int j = lane; j < kd; j += 64) nz = nz || X[i * kd + j] != 0.0;

@@ -40,6 +40,10 @@ __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return
 // nothing is decided from the stand-in).
 __device__ __forceinline__ int safe_code(int c, int K) { return (unsigned)c < (unsigned)K ? c : 0; }
 
+// This thread's wave within the workgroup, as a wave-uniform (scalar) value:
+// the compiler then keeps the addresses derived from it in scalar registers.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // Cross-lane helpers (full wave64).
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 __device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, 64); }
