@@ -707,6 +707,15 @@ __device__ __forceinline__ void keep_best(double v, uint32_t kv, double& bs, uin
   bs = b ? v : bs;
   bk = b ? kv : bk;
 }
+// The same, only where `on` holds.  Choosing the destination with a predicate
+// on every candidate state (rather than branching to one of them) keeps the
+// states in registers: a branch between references let the compiler turn the
+// three states into a scratch-memory array.
+__device__ __forceinline__ void keep_best_if(bool on, double v, uint32_t kv, double& bs, uint32_t& bk) {
+  const bool b = on && (v > bs || (v == bs && kv < bk));
+  bs = b ? v : bs;
+  bk = b ? kv : bk;
+}
 // Across final states: score, then the smaller norm, then the smaller key
 // (codebook order is (norm, lexicographic)).
 __device__ __forceinline__ void keep_best3(double v, int nv, uint32_t kv, double& bs, int& bn, uint32_t& bk) {
@@ -750,12 +759,9 @@ __device__ __forceinline__ void e8_nearest_pass(const int j, const E8RowCoef& cf
         const int ck = e8_cmp(e8_twice_value(HALF, k), l2);
         const double v = row_read_or<CT>(se, -INFINITY) + f;
         const uint32_t kv = row_read_or_u<CT>(ke, ~0u) * 16u + nib;
-        if (ck == 0)
-          keep_best(v, kv, nl, ql);
-        else if (ck == 1)
-          keep_best(v, kv, ne, qe);
-        else
-          keep_best(v, kv, ng, qg);
+        keep_best_if(ck == 0, v, kv, nl, ql);
+        keep_best_if(ck == 1, v, kv, ne, qe);
+        keep_best_if(ck == 2, v, kv, ng, qg);
       }
     });
     sl = nl;
