@@ -151,7 +151,10 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
                                                        const int32_t* __restrict__ rows,
                                                        const int32_t* __restrict__ rcount,
                                                        float* __restrict__ part_s, int32_t* __restrict__ part_i) {
-  __shared__ __attribute__((aligned(16))) uint32_t lds_key[(CDL_CW_WG / 16) * 64 * 4];
+  // the slice's keys: every codeword's e (one 16-byte copy; the three key
+  // groups that hold e read it as a broadcast) and its t(e) slots
+  __shared__ __attribute__((aligned(16))) v4u lds_e[CDL_CW_WG];
+  __shared__ __attribute__((aligned(16))) v4u lds_t[CDL_CW_WG];
   // rows: the rows this block scores, by list position (nullptr: all m rows
   // in order); workgroups past the list's end have nothing to do
   const int64_t cnt = rows ? (int64_t)rcount[0] : m;
@@ -182,25 +185,29 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
     bpos[q] = -1;
   }
 
-  // key fragments of this slice: lanes g < 3 carry e, lanes g = 3 the t(e)
-  // terms; every load is issued before the first LDS write, so the staging
-  // costs one memory round trip
+  // the slice's e and t(e) entries (2 x 16 B per codeword); every load is
+  // issued before the first LDS write, so the staging costs one memory round
+  // trip.  A short last slice (ncw < CDL_CW_WG) reloads codeword 0 past its
+  // end and does not store it.
   const v4u* kv = reinterpret_cast<const v4u*>(keys);
   const v4u* tkb = tk + (int64_t)bl * Kpad + cw_base;
-  constexpr int NF = (CDL_CW_WG / 16) * 64 / (64 * CDL_WAVES);   // fragments per thread
-  const int nf = (ncw / 16) * 64;
-  v4u kbuf[NF];
+  constexpr int NH = CDL_CW_WG / (64 * CDL_WAVES);   // codewords per thread
+  static_assert(NH * 64 * CDL_WAVES == CDL_CW_WG, "the staging covers every codeword of the slice");
+  v4u kbuf[2 * NH];   // [0, NH): e entries, [NH, 2 NH): t entries
 #pragma unroll
-  for (int u = 0; u < NF; ++u) {
-    // past the slice's end (a short last slice; nf >= 512 > t) reload fragment t
-    const int f = t + u * 64 * CDL_WAVES < nf ? t + u * 64 * CDL_WAVES : t;
-    const int st = f >> 6, ln = f & 63;
-    kbuf[u] = (ln >> 4) < 3 ? kv[(int64_t)(cw_base / 16 + st) * 64 + ln] : tkb[st * 16 + (ln & 15)];
+  for (int u = 0; u < NH; ++u) {
+    const int c = t + u * 64 * CDL_WAVES;
+    const int cc = c < ncw ? c : 0;
+    kbuf[u] = kv[(int64_t)(cw_base / 16 + cc / 16) * 64 + (cc & 15)];
+    kbuf[NH + u] = tkb[cc];
   }
 #pragma unroll
-  for (int u = 0; u < NF; ++u) {
-    const int f = t + u * 64 * CDL_WAVES;
-    if (f < nf) reinterpret_cast<v4u*>(lds_key)[f] = kbuf[u];
+  for (int u = 0; u < NH; ++u) {
+    const int c = t + u * 64 * CDL_WAVES;
+    if (c < ncw) {
+      lds_e[c] = kbuf[u];
+      lds_t[c] = kbuf[NH + u];
+    }
   }
   __syncthreads();
   // lane (j, g) sees codewords 16 st + 4 g + v (v = 0..3) of the slice for
@@ -213,10 +220,11 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
   // position only when strictly below the running best: the lane's candidate
   // is its least float32 score, ties to the lowest index.
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-  const v4u* kq = reinterpret_cast<const v4u*>(lds_key);
+  // lane (j, g)'s key fragment of step st: e (g < 3) or t(e) (g = 3) of codeword 16 st + j
+  const v4u* kq = (g < 3 ? lds_e : lds_t) + j;
   auto pair_step = [&](int sp) {
-    const v4u k0 = kq[(2 * sp) * 64 + lane];
-    const v4u k1 = kq[(2 * sp + 1) * 64 + lane];
+    const v4u k0 = kq[(2 * sp) * 16];
+    const v4u k1 = kq[(2 * sp + 1) * 16];
     // the four row subtiles' tiles first (eight MFMAs back to back), then
     // each subtile's minimum and its wave-uniform branch
     v4f s0[4], s1[4];
