@@ -29,6 +29,15 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
 // CD decisions use float64 state (tile gradient g, tile of H, moves) and
 // float64 codeword values c = a e + o:
 // dF(c) = 1/2 H_jj (c - x_j)^2 - (c - x_j) g_j.
+//
+// The column loop's critical path holds no memory access: H's diagonal and
+// superdiagonal and every column's affine (a, o) are loaded with the row's
+// gradient before it.  A move at column j updates g_{j+1} at once (from the
+// superdiagonal) and loads H's row j, which is applied to the columns after
+// j + 1 one column later, after column j + 1's decision (which reads only
+// g_{j+1}); every g entry still receives the moves' updates in column order,
+// so the arithmetic is that of the plain sweep.  The argmin over the levels
+// takes log2 of K's next power of two butterfly steps.
 template <int SLOTS>
 __global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t n, int64_t j0, int kd,
                                                              const double* __restrict__ G,
@@ -41,58 +50,87 @@ __global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t 
   const int lane = threadIdx.x & 63;
   const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= m) return;
-  // lane k holds level k of the current column's affine group; the group
-  // changes along the tile only with column groups (uniform across the wave)
   const double lvk = lane < K ? (double)levels[lane] : 0.0;
-  int cur = (int)j0 / gs;
-  double cl = (double)a[i * ng + cur] * lvk + (double)o[i * ng + cur];
+  int kspan = 1;   // lanes of the argmin: the levels, rounded up to a power of two
+  while (kspan < K) kspan <<= 1;
 
-  double g[SLOTS], dl[SLOTS], x[SLOTS];
+  // lane l, slot s <-> column jj = s * 64 + l of the tile
+  double g[SLOTS], dl[SLOTS], x[SLOTS], hd[SLOTS], hs[SLOTS], ga[SLOTS], go[SLOTS];
   int cd[SLOTS];
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
-    int jj = s * 64 + lane;
-    bool in = jj < kd;
-    g[s] = in ? G[i * kd + jj] : 0.0;
-    cd[s] = in ? codes[i * n + j0 + jj] : 0;
-    const int64_t ag = i * ng + (in ? (int)(j0 + jj) / gs : 0);
-    x[s] = in ? (double)a[ag] * (double)levels[safe_code(cd[s], K)] + (double)o[ag] : 0.0;
+    const int jj = s * 64 + lane;
+    const bool in = jj < kd;
+    const int jc = in ? jj : kd - 1;   // clamped for the loads
+    const double gv = G[i * kd + jc];
+    const int cv = codes[i * n + j0 + jc];
+    const int64_t ag = i * ng + (int)(j0 + jc) / gs;
+    ga[s] = (double)a[ag];
+    go[s] = (double)o[ag];
+    const double lv = (double)levels[safe_code(cv, K)];
+    const double hdv = Ht[(int64_t)jc * kd + jc];
+    const double hsv = Ht[(int64_t)jc * kd + min(jc + 1, kd - 1)];
+    g[s] = in ? gv : 0.0;
+    cd[s] = in ? cv : 0;
+    x[s] = in ? ga[s] * lv + go[s] : 0.0;
+    hd[s] = in ? hdv : 0.0;
+    hs[s] = jj + 1 < kd ? hsv : 0.0;   // H[jj][jj + 1]
     dl[s] = 0.0;
   }
   int moved = 0;
+  bool pend = false;   // a move whose H row still has to reach the later columns (uniform)
+  double pd = 0.0;     // its step
+  int pj = 0;          // its column
+  double hp[SLOTS];    // its H row
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) hp[s] = 0.0;
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     for (int jl = 0; jl < 64; ++jl) {
       const int jj = s * 64 + jl;
       if (jj >= kd) break;
-      const int grp = (int)(j0 + jj) / gs;
-      if (grp != cur) {
-        cur = grp;
-        cl = (double)a[i * ng + cur] * lvk + (double)o[i * ng + cur];
-      }
       const double gj = readlane_d(g[s], jl);
       const double xj = readlane_d(x[s], jl);
-      const double hjj = Ht[(int64_t)jj * kd + jj];
+      const double hjj = readlane_d(hd[s], jl);
+      const double cl = readlane_d(ga[s], jl) * lvk + readlane_d(go[s], jl);
       const double dlt = cl - xj;
       double f = lane < K ? (0.5 * hjj * dlt - gj) * dlt : INFINITY;
       int k = lane;
-#pragma unroll
-      for (int msk = 1; msk < 64; msk <<= 1) {
+      for (int msk = 1; msk < kspan; msk <<= 1) {
         double fo = __shfl_xor(f, msk, 64);
         int ko = shfl_xor_i(k, msk);
         if (fo < f || (fo == f && ko < k)) { f = fo; k = ko; }
+      }
+      f = readlane_d(f, 0);
+      k = __builtin_amdgcn_readlane(k, 0);
+      // the previous column's move reaches the columns after this one
+      if (pend) {
+#pragma unroll
+        for (int s2 = 0; s2 < SLOTS; ++s2) {
+          const int jc = s2 * 64 + lane;
+          if (jc > pj + 1 && jc < kd) g[s2] -= hp[s2] * pd;
+        }
+        pend = false;
       }
       if (f < 0.0) {  // strict improvement only (uniform across the wave)
         const double cnew = readlane_d(cl, k);
         const double dstar = cnew - xj;
         if (lane == jl) { x[s] = cnew; cd[s] = k; dl[s] = dstar; }
         ++moved;
+        // the next column at once, from the superdiagonal; the rest of H's
+        // row after the next decision
+        const double hsd = readlane_d(hs[s], jl);
+        if (jl < 63) {
+          if (lane == jl + 1) g[s] -= hsd * dstar;
+        } else if (s + 1 < SLOTS) {
+          if (lane == 0) g[s + 1] -= hsd * dstar;
+        }
         const double* hrow = Ht + (int64_t)jj * kd;
 #pragma unroll
-        for (int s2 = 0; s2 < SLOTS; ++s2) {
-          int jc = s2 * 64 + lane;
-          if (jc < kd) g[s2] -= hrow[jc] * dstar;
-        }
+        for (int s2 = 0; s2 < SLOTS; ++s2) hp[s2] = hrow[min(s2 * 64 + lane, kd - 1)];
+        pend = true;
+        pd = dstar;
+        pj = jj;
       }
     }
   }
