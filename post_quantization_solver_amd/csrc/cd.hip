@@ -26,6 +26,24 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
   return __builtin_bit_cast(double, p);
 }
 
+// DPP read of a double from lane pattern CTRL within each 16-lane row
+// (quad_perm xor 1 = 0xB1, xor 2 = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140).
+template <int CTRL>
+__device__ __forceinline__ double row_dpp_d(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, true);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+}
+
+// One step of the (value, index) argmin: the lesser pair, ties to the lower index.
+template <int CTRL>
+__device__ __forceinline__ void argmin_dpp(double& f, int& k) {
+  const double fo = row_dpp_d<CTRL>(f);
+  const int ko = __builtin_amdgcn_update_dpp(0, k, CTRL, 0xf, 0xf, true);
+  if (fo < f || (fo == f && ko < k)) { f = fo; k = ko; }
+}
+
 // CD decisions use float64 state (tile gradient g, tile of H, moves) and
 // float64 codeword values c = a e + o:
 // dF(c) = 1/2 H_jj (c - x_j)^2 - (c - x_j) g_j.
@@ -37,7 +55,7 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
 // j + 1 one column later, after column j + 1's decision (which reads only
 // g_{j+1}); every g entry still receives the moves' updates in column order,
 // so the arithmetic is that of the plain sweep.  The argmin over the levels
-// takes log2 of K's next power of two butterfly steps.
+// takes log2 of K's next power of two steps, DPP moves within a 16-lane row.
 template <int SLOTS>
 __global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t n, int64_t j0, int kd,
                                                              const double* __restrict__ G,
@@ -96,7 +114,14 @@ __global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t 
       const double dlt = cl - xj;
       double f = lane < K ? (0.5 * hjj * dlt - gj) * dlt : INFINITY;
       int k = lane;
-      for (int msk = 1; msk < kspan; msk <<= 1) {
+      // within a 16-lane row by DPP (after the quad steps every quad holds
+      // its minimum; the mirrors join quads, then halves), across rows by
+      // lane shuffles
+      if (kspan > 1) argmin_dpp<0xB1>(f, k);
+      if (kspan > 2) argmin_dpp<0x4E>(f, k);
+      if (kspan > 4) argmin_dpp<0x141>(f, k);
+      if (kspan > 8) argmin_dpp<0x140>(f, k);
+      for (int msk = 16; msk < kspan; msk <<= 1) {
         double fo = __shfl_xor(f, msk, 64);
         int ko = shfl_xor_i(k, msk);
         if (fo < f || (fo == f && ko < k)) { f = fo; k = ko; }
