@@ -26,21 +26,11 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
   return __builtin_bit_cast(double, p);
 }
 
-// DPP read of a double from lane pattern CTRL within each 16-lane row
-// (quad_perm xor 1 = 0xB1, xor 2 = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140).
-template <int CTRL>
-__device__ __forceinline__ double row_dpp_d(double v) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xf, 0xf, true);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, true);
-  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
-}
-
 // One step of the (value, index) argmin: the lesser pair, ties to the lower index.
 template <int CTRL>
 __device__ __forceinline__ void argmin_dpp(double& f, int& k) {
-  const double fo = row_dpp_d<CTRL>(f);
-  const int ko = __builtin_amdgcn_update_dpp(0, k, CTRL, 0xf, 0xf, true);
+  const double fo = dpp_d<CTRL>(f);
+  const int ko = dpp_i<CTRL>(k);
   if (fo < f || (fo == f && ko < k)) { f = fo; k = ko; }
 }
 
@@ -117,10 +107,10 @@ __global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t 
       // within a 16-lane row by DPP (after the quad steps every quad holds
       // its minimum; the mirrors join quads, then halves), across rows by
       // lane shuffles
-      if (kspan > 1) argmin_dpp<0xB1>(f, k);
-      if (kspan > 2) argmin_dpp<0x4E>(f, k);
-      if (kspan > 4) argmin_dpp<0x141>(f, k);
-      if (kspan > 8) argmin_dpp<0x140>(f, k);
+      if (kspan > 1) argmin_dpp<DPP_XOR1>(f, k);
+      if (kspan > 2) argmin_dpp<DPP_XOR2>(f, k);
+      if (kspan > 4) argmin_dpp<DPP_HALF_MIRROR>(f, k);
+      if (kspan > 8) argmin_dpp<DPP_MIRROR>(f, k);
       for (int msk = 16; msk < kspan; msk <<= 1) {
         double fo = __shfl_xor(f, msk, 64);
         int ko = shfl_xor_i(k, msk);

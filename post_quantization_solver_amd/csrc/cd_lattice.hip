@@ -97,12 +97,16 @@ __device__ __forceinline__ void cd_query_write(int lane, int64_t i, double ge, d
   double sx = -exp_ * ai * fma(0.5 * ai, ge, gp);
   double q2 = qv * qv;
   double gm = grow;
-#pragma unroll
-  for (int msk = 1; msk < 8; msk <<= 1) {
-    sx += __shfl_xor(sx, msk, 64);
-    q2 += __shfl_xor(q2, msk, 64);
-    gm = fmax(gm, __shfl_xor(gm, msk, 64));
-  }
+  // sums over each 8-lane group (the row's coordinates): xor 1, 2, 4 as DPP moves
+  sx += dpp_d<DPP_XOR1>(sx);
+  q2 += dpp_d<DPP_XOR1>(q2);
+  gm = fmax(gm, dpp_d<DPP_XOR1>(gm));
+  sx += dpp_d<DPP_XOR2>(sx);
+  q2 += dpp_d<DPP_XOR2>(q2);
+  gm = fmax(gm, dpp_d<DPP_XOR2>(gm));
+  sx += dpp_d<DPP_HALF_MIRROR>(sx);
+  q2 += dpp_d<DPP_HALF_MIRROR>(q2);
+  gm = fmax(gm, dpp_d<DPP_HALF_MIRROR>(gm));
   const double R = (double)rmax;
   const double eps = CD_TAU_ULPS * 0x1p-24 * (0.5 * ai * ai * R * R * gm + R * sqrt(q2)) + 1e-30;
   const double tv = sx + eps;
@@ -400,11 +404,7 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_update_kernel(int64_t m, in
         o2 = {sv.y, iv.y};
       }
     }
-#pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) {
-      Cand p1 = shfl_cand(o1, msk), p2 = shfl_cand(o2, msk);
-      merge_top2(o1, o2, p1, p2);
-    }
+    wave_top2(o1, o2);
     merge_top2(c1, c2, o1, o2);
   }
 

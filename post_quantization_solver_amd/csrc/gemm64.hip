@@ -287,23 +287,37 @@ hipError_t launch_mirror_lower(double* H, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
-// One wave per row: any nonzero among its kd entries appends the row.
+// Eight rows per wave, eight lanes per row: a row with any nonzero among its
+// kd entries is appended, with one atomic per wave for all its rows (every
+// row moves in most tiles of a scalar grid, and one atomic per row serialised
+// on the counter).  The list's order does not matter to its users.
+constexpr int CNZ_ROWS_WAVE = 8;
 __global__ __launch_bounds__(256) void collect_nonzero_rows_kernel(const double* __restrict__ X, int64_t m, int kd,
                                                                    int32_t* __restrict__ list,
                                                                    int32_t* __restrict__ count) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * 4 + wave_id();
-  if (i >= m) return;
+  const int sub = lane & (CNZ_ROWS_WAVE - 1);
+  const int64_t i = ((int64_t)blockIdx.x * 4 + wave_id()) * CNZ_ROWS_WAVE + lane / CNZ_ROWS_WAVE;
   bool nz = false;
-  for (int j = lane; j < kd; j += 64) nz = nz || X[i * kd + j] != 0.0;
-  if (__any(nz) && lane == 0) list[atomicAdd(count, 1)] = (int32_t)i;
+  if (i < m)
+    for (int j = sub; j < kd; j += CNZ_ROWS_WAVE) nz |= X[i * kd + j] != 0.0;
+  const uint64_t any = __builtin_amdgcn_ballot_w64(nz);
+  const int first = lane & ~(CNZ_ROWS_WAVE - 1);   // the row's first lane
+  const bool lead = sub == 0 && ((any >> first) & 0xffull) != 0;
+  const uint64_t leads = __builtin_amdgcn_ballot_w64(lead);
+  if (leads == 0) return;
+  int base = 0;
+  if (lane == 0) base = atomicAdd(count, (int)__builtin_popcountll(leads));
+  base = __shfl(base, 0, 64);
+  if (lead) list[base + __builtin_popcountll(leads & ((1ull << lane) - 1ull))] = (int32_t)i;
 }
 
 hipError_t launch_collect_nonzero_rows(const double* X, int64_t m, int kd, int32_t* list, int32_t* count,
                                        hipStream_t st) {
   if (m <= 0) return hipSuccess;
-  hipLaunchKernelGGL(collect_nonzero_rows_kernel, dim3((unsigned)((m + 3) / 4)), dim3(256), 0, st, X, m, kd, list,
-                     count);
+  const int64_t rows_wg = 4 * CNZ_ROWS_WAVE;
+  hipLaunchKernelGGL(collect_nonzero_rows_kernel, dim3((unsigned)((m + rows_wg - 1) / rows_wg)), dim3(256), 0, st, X,
+                     m, kd, list, count);
   return hipGetLastError();
 }
 

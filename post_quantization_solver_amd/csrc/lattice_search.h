@@ -42,11 +42,36 @@ __device__ __forceinline__ Cand shfl_cand(Cand c, int mask) {
   return o;
 }
 
-// Sum over the wave, fixed butterfly order (the same value in every lane).
+template <int CTRL>
+__device__ __forceinline__ Cand dpp_cand(Cand c) {
+  return Cand{dpp_f<CTRL>(c.v), dpp_i<CTRL>(c.i)};
+}
+
+// Sum over the wave, fixed butterfly order (the same value in every lane):
+// the xor butterfly over 1, 2, 4, ..., 32, its steps within a 16-lane row as
+// DPP moves.
 __device__ __forceinline__ double wave_sum_d(double x) {
-#pragma unroll
-  for (int msk = 1; msk < 64; msk <<= 1) x += __shfl_xor(x, msk, 64);
+  x += dpp_d<DPP_XOR1>(x);
+  x += dpp_d<DPP_XOR2>(x);
+  x += dpp_d<DPP_HALF_MIRROR>(x);
+  x += dpp_d<DPP_MIRROR>(x);
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
   return x;
+}
+
+// The top 2 over every lane's sorted pair (c1 <= c2), in every lane; the
+// steps within a 16-lane row as DPP moves.
+__device__ __forceinline__ void wave_top2(Cand& c1, Cand& c2) {
+  merge_top2(c1, c2, dpp_cand<DPP_XOR1>(c1), dpp_cand<DPP_XOR1>(c2));
+  merge_top2(c1, c2, dpp_cand<DPP_XOR2>(c1), dpp_cand<DPP_XOR2>(c2));
+  merge_top2(c1, c2, dpp_cand<DPP_HALF_MIRROR>(c1), dpp_cand<DPP_HALF_MIRROR>(c2));
+  merge_top2(c1, c2, dpp_cand<DPP_MIRROR>(c1), dpp_cand<DPP_MIRROR>(c2));
+#pragma unroll
+  for (int msk = 16; msk <= 32; msk <<= 1) {
+    const Cand p1 = shfl_cand(c1, msk), p2 = shfl_cand(c2, msk);
+    merge_top2(c1, c2, p1, p2);
+  }
 }
 
 // Query fragments of row i: the K-slots of the score MFMA's query column,

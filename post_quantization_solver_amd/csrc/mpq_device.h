@@ -54,6 +54,28 @@ __device__ __forceinline__ double shfl_d(double v, int src) {
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
+// DPP lane patterns within a 16-lane row: quad_perm [1,0,3,2] (xor 1) and
+// [2,3,0,1] (xor 2), row_half_mirror (lane i <-> 7 - i of each 8) and
+// row_mirror (i <-> 15 - i).  In a reduction step whose lane quads (or halves)
+// already hold one value each, the mirrors pair the same quads (halves) as
+// xor 4 (xor 8), so a butterfly over them gives the xor butterfly's values.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const int lo = dpp_i<CTRL>((int)(uint32_t)b);
+  const int hi = dpp_i<CTRL>((int)(uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+}
+
 // MFMA wrappers.  16x16 output layout (all dtypes): lane l holds rows
 // 4*(l/16) + v (v = 0..3) of column l % 16.
 __device__ __forceinline__ v4f mfma_f32_16x16x4(float a, float b, v4f c) {
