@@ -51,6 +51,43 @@ def test_layer_parity(name):
     check_counts(L, gpu, refs)
 
 
+def levels_layer(name, m, n, K, seed, **kw):
+    """A scalar layer with a K-level Min-Max grid per row for any K in [2, 64]
+    (the synthetic workloads use powers of two): levels 0..K-1, scale
+    (max - min) / (K - 1), integer zero point rounded half to even."""
+    L = S.make_layer(name, m, n, seed=seed, d=1, bits=4, **kw)
+    W64 = np.asarray(L.W, np.float64)
+    lo, hi = W64.min(1), W64.max(1)
+    scale = (hi - lo) / (K - 1)
+    scale = np.where(scale > 0, scale, 1.0)
+    zero = np.round(-lo / scale)
+    E = np.arange(K, dtype=np.float32).reshape(K, 1)
+    return S.Layer(name, L.W, L.s, L.V, E, scale.astype(np.float32), (-scale * zero).astype(np.float32), 1,
+                   L.T_vamp, L.n_cd, L.damping)
+
+
+@pytest.mark.parametrize("K", [3, 5, 12, 33])
+def test_layer_parity_levels(K):
+    """Scalar grids whose level count is not a power of two: CD's argmin over
+    the levels runs over K's next power of two lanes (the lanes past K carry
+    no level), within a 16-lane row up to 16 levels and across rows above
+    (K = 33).  n = 300 spans a full and a ragged CD tile, r < n."""
+    L = levels_layer(f"levels_k{K}", 24, 300, K, seed=70 + K, power=0.6, r=260, T_vamp=5)
+    rows = np.arange(L.m)
+    print(f"[layer] levels K={K} m={L.m} n={L.n} r={L.r}", flush=True)
+    gpu = run_gpu(L)
+    refs = solve_rows(L, rows)
+    summ = compare_layer(L, rows, gpu, refs)
+    print(f"  codes {summ['code_agreement']:.5f} rows-equal {summ['rows_codes_equal']}/{summ['n_rows']} "
+          f"obj {summ['obj_rel_max']:.2e} traces {summ['trace_rel_max']}", flush=True)
+    assert int(gpu["codes"].max()) <= K - 1
+    assert summ["code_agreement"] >= CODE_FRAC
+    assert summ["obj_rel_max"] < OBJ_RTOL
+    for key, v in summ["trace_rel_max"].items():
+        assert v < SOFT_RTOL, (key, v)
+    check_counts(L, gpu, refs)
+
+
 def check_counts(L, gpu, refs):
     """Pass-through events and CD sweeps per row, as the oracle counts them."""
     fb = np.array([r["fallbacks"] for r in refs])
