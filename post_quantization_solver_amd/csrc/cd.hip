@@ -38,13 +38,14 @@ __device__ __forceinline__ void argmin_dpp(double& f, int& k) {
 // float64 codeword values c = a e + o:
 // dF(c) = 1/2 H_jj (c - x_j)^2 - (c - x_j) g_j.
 //
-// The column loop's critical path holds no memory access: H's diagonal and
+// A column's decision waits on no memory access: H's diagonal and
 // superdiagonal and every column's affine (a, o) are loaded with the row's
-// gradient before it.  A move at column j updates g_{j+1} at once (from the
-// superdiagonal) and loads H's row j, which is applied to the columns after
-// j + 1 one column later, after column j + 1's decision (which reads only
-// g_{j+1}); every g entry still receives the moves' updates in column order,
-// so the arithmetic is that of the plain sweep.  The argmin over the levels
+// gradient before the loop.  A move at column j updates g_{j+1} at once (from
+// the superdiagonal) and loads H's row j, which is applied to the columns
+// after j + 1 one column later, after column j + 1's decision (which reads
+// only g_{j+1}), so the row's load has a column's work to land in; every g
+// entry still receives the moves' updates in column order, so the arithmetic
+// is that of the plain sweep.  The argmin over the levels
 // takes log2 of K's next power of two steps, DPP moves within a 16-lane row.
 template <int SLOTS>
 __global__ __launch_bounds__(256) void cd_scalar_tile_kernel(int64_t m, int64_t n, int64_t j0, int kd,
