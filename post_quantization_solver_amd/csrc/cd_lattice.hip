@@ -31,9 +31,7 @@
 
 namespace mpq {
 
-constexpr int CDL_ROWS_WAVE = 64;            // 4 row subtiles per wave
 constexpr int CDL_WAVES = 8;                 // waves per scoring workgroup (they share its key slice)
-constexpr int CDL_ROWS_WG = CDL_WAVES * CDL_ROWS_WAVE;
 constexpr int CDU_WAVES = 8;                 // rows (one per wave) per query / update workgroup
 constexpr int CDL_CW_WG = 1024;              // codewords per workgroup slice
 
@@ -146,9 +144,12 @@ __global__ __launch_bounds__(64 * CDU_WAVES) void cd_query_kernel(int64_t m, int
                rmaxp[0], qf, tau);
 }
 
-// grid: (slices, row groups).  part_s / part_i: [slices][list position][2] (best, second).
+// grid: (slices, row groups of 8 x 16 RSUB rows).  part_s / part_i: [slices][list position][2] (best, second).
 // The float32 scores only rank candidates; the update kernel re-evaluates the
-// two best of every slice exactly in float64.
+// two best of every slice exactly in float64.  RSUB row subtiles of 16 rows
+// per wave: 4 when every row is scored; 2 over a row list (the later sweeps,
+// whose fewer rows would otherwise leave most CUs one workgroup of long waves).
+template <int RSUB>
 __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int bl, const uint32_t* __restrict__ keys,
                                                        const v4u* __restrict__ tk, int Kpad,
                                                        const v4u* __restrict__ qf, const float* __restrict__ tau,
@@ -161,8 +162,10 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
   __shared__ __attribute__((aligned(16))) v4u lds_t[CDL_CW_WG];
   // rows: the rows this block scores, by list position (nullptr: all m rows
   // in order); workgroups past the list's end have nothing to do
+  constexpr int ROWS_WAVE = 16 * RSUB;
+  constexpr int ROWS_WG = CDL_WAVES * ROWS_WAVE;
   const int64_t cnt = rows ? (int64_t)rcount[0] : m;
-  if ((int64_t)blockIdx.y * CDL_ROWS_WG >= cnt) return;
+  if ((int64_t)blockIdx.y * ROWS_WG >= cnt) return;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = wave_id();
@@ -170,16 +173,16 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
   const int g = lane >> 4;
   const int cw_base = blockIdx.x * CDL_CW_WG;
   const int ncw = min(CDL_CW_WG, Kpad - cw_base);
-  const int64_t row_base = (int64_t)blockIdx.y * CDL_ROWS_WG + wave * CDL_ROWS_WAVE;
+  const int64_t row_base = (int64_t)blockIdx.y * ROWS_WG + wave * ROWS_WAVE;
   const int nsl = gridDim.x;
 
   // row queries: lane (j, g) of subtile q serves row row_base + 16 q + j
   // (loaded first, so that they arrive while the keys are staged)
-  v4u qop[4];
-  float best[4];
-  int bpos[4];
+  v4u qop[RSUB];
+  float best[RSUB];
+  int bpos[RSUB];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < RSUB; ++q) {
     const int64_t x = row_base + q * 16 + j;   // list position
     const bool valid = x < cnt;
     const int64_t i = valid ? (rows ? (int64_t)rows[x] : x) : 0;
@@ -229,16 +232,16 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
   auto pair_step = [&](int sp) {
     const v4u k0 = kq[(2 * sp) * 16];
     const v4u k1 = kq[(2 * sp + 1) * 16];
-    // the four row subtiles' tiles first (eight MFMAs back to back), then
-    // each subtile's minimum and its wave-uniform branch
-    v4f s0[4], s1[4];
+    // the row subtiles' tiles first (2 RSUB MFMAs back to back), then each
+    // subtile's minimum and its wave-uniform branch
+    v4f s0[RSUB], s1[RSUB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < RSUB; ++q) {
       s0[q] = mfma_bf16_16x16x32(k0, qop[q], zero4);
       s1[q] = mfma_bf16_16x16x32(k1, qop[q], zero4);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < RSUB; ++q) {
       float mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(s0[q][0], s0[q][1]), s0[q][2]);
       mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, s0[q][3]), s1[q][0]);
       mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, s1[q][1]), s1[q][2]);
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(64 * CDL_WAVES) void cd_score_kernel(int64_t m, int
   // part_s / part_i are [slice][list position] so that the 16 rows of a
   // subtile store one contiguous segment.
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < RSUB; ++q) {
     const bool found = bpos[q] >= 0;
     Cand c1 = {found ? best[q] : INFINITY, found ? cw_base + 4 * g + bpos[q] : 0x7fffffff};
     Cand c2 = {INFINITY, 0x7fffffff};
@@ -569,11 +572,21 @@ hipError_t launch_cd_lattice_score(int64_t m, int bl, const uint32_t* tk, const 
                                    int32_t* part_i, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
   if (m <= 0) return hipSuccess;
   const int nslices = cd_lattice_slices(cb.Kpad);
-  dim3 g1((unsigned)nslices, (unsigned)((m + CDL_ROWS_WG - 1) / CDL_ROWS_WG));
+  const float* tau = bounded ? static_cast<const float*>(cd_tau(qf, m)) : nullptr;
+  const v4u* tkv = reinterpret_cast<const v4u*>(tk);
+  const v4u* qfv = reinterpret_cast<const v4u*>(qf);
   // t0 / t1 (optional) take the kernel's own start and end times
-  hipExtLaunchKernelGGL(cd_score_kernel, g1, dim3(64 * CDL_WAVES), 0, st, t0, t1, 0u, m, bl, cb.qk_keys,
-                        reinterpret_cast<const v4u*>(tk), cb.Kpad, reinterpret_cast<const v4u*>(qf),
-                        bounded ? static_cast<const float*>(cd_tau(qf, m)) : nullptr, rows, rcount, part_s, part_i);
+  if (rows) {   // a row list: half-height waves, twice the workgroups
+    constexpr int rows_wg = CDL_WAVES * 16 * 2;
+    const dim3 g1((unsigned)nslices, (unsigned)((m + rows_wg - 1) / rows_wg));
+    hipExtLaunchKernelGGL(cd_score_kernel<2>, g1, dim3(64 * CDL_WAVES), 0, st, t0, t1, 0u, m, bl, cb.qk_keys, tkv,
+                          cb.Kpad, qfv, tau, rows, rcount, part_s, part_i);
+  } else {
+    constexpr int rows_wg = CDL_WAVES * 16 * 4;
+    const dim3 g1((unsigned)nslices, (unsigned)((m + rows_wg - 1) / rows_wg));
+    hipExtLaunchKernelGGL(cd_score_kernel<4>, g1, dim3(64 * CDL_WAVES), 0, st, t0, t1, 0u, m, bl, cb.qk_keys, tkv,
+                          cb.Kpad, qfv, tau, rows, rcount, part_s, part_i);
+  }
   return hipGetLastError();
 }
 
